@@ -1,0 +1,183 @@
+/*
+ * hisa.h -- C ABI of the MI355X (gfx950) HiSA sparse-selection and sparse
+ * local+pooled attention library (libhisa.so).
+ *
+ * What it computes (the pages):
+ *   [HiSA issue]  GitHub lablup/mlxcel issue #549, "feat(deepseek-v4): implement
+ *                 HiSA hierarchical sparse attention": sections Conventions, The
+ *                 pooled stream and positions, The indexer query and per-head
+ *                 weights, Flat selection, HiSA decode path, HiSA batched path,
+ *                 Consuming the selection: sparse combine, Engagement thresholds.
+ *   [DSA issue]   GitHub lablup/mlxcel issue #509, "implement the DeepSeek Sparse
+ *                 Attention (DSA) indexer", What needs to be built, items 1 and 3.
+ *
+ * Conventions shared by every call
+ *   - All tensors are dense, row-major, in the axis order written at each call;
+ *     the caller allocates and owns every buffer (inputs, outputs, workspace).
+ *     Pointers are device pointers unless said otherwise; dims is a host pointer.
+ *   - t0 is a device int32[B]: the number of tokens the layer had consumed before
+ *     this step for sequence b.  Query row j sits at absolute position t0[b] + j.
+ *     After the step the pooled stream holds Np_b = floor((t0[b] + L) / ratio)
+ *     rows; row j sees the pooled rows p < V = min(Np_b, floor((t0[b]+j+1)/ratio)).
+ *   - Work is enqueued on `stream` (a hipStream_t, NULL = the null stream).  No
+ *     call allocates, synchronises, or copies between host and device, and none
+ *     keeps a pointer after it returns.  Calls on one workspace must not overlap.
+ *   - Sequences whose t0 breaks the buffer bounds (t0 < 0, Np_b > Np_cap, or a
+ *     local window longer than Wl_cap) are not computed: their index rows are -1,
+ *     their attention rows are 0, and path_out reports HISA_PATH_INVALID.
+ *   - Return value: HISA_OK or a negative HISA_ERR_*; on error nothing was
+ *     enqueued and hisa_last_error() (thread-local) says why.  Nothing throws.
+ *   - Which selection path a sequence takes (dense / flat / HiSA) is decided on
+ *     the device per sequence; it is not an error (see hisa_dims.mode).
+ */
+#ifndef HISA_H
+#define HISA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HISA_ABI_VERSION 1
+
+enum hisa_dtype { HISA_F32 = 0, HISA_BF16 = 1 };
+
+/* mode: HISA_MODE_AUTO runs the gate of the HiSA issue (dense when Np <= topk;
+ * HiSA when index_block > 0, Np >= index_block*index_keep and
+ * index_block*index_keep >= min(topk, Np); flat otherwise).
+ * HISA_MODE_FORCE_FLAT is the "force the flat scan" switch of the HiSA issue's
+ * implementation plan: it replaces the hierarchy by the flat scan (the dense
+ * case Np <= topk is kept). */
+enum hisa_mode { HISA_MODE_AUTO = 0, HISA_MODE_FORCE_FLAT = 1 };
+
+enum hisa_path { HISA_PATH_INVALID = -1, HISA_PATH_DENSE = 0, HISA_PATH_FLAT = 1, HISA_PATH_HISA = 2 };
+
+enum hisa_status {
+  HISA_OK = 0,
+  HISA_ERR_ARG = -1,       /* bad pointer, size or unsupported shape */
+  HISA_ERR_DTYPE = -2,     /* unsupported dtype combination */
+  HISA_ERR_WORKSPACE = -3, /* ws_bytes smaller than hisa_workspace_bytes() */
+  HISA_ERR_OVERFLOW = -4,  /* a size or offset overflows the kernels' int32 indexing */
+  HISA_ERR_LAUNCH = -5     /* a kernel launch failed (see hisa_last_error) */
+};
+
+enum hisa_op {
+  HISA_OP_BLOCK_SCORES = 0,
+  HISA_OP_SELECT_DECODE = 1,
+  HISA_OP_SELECT_PREFILL = 2,
+  HISA_OP_FLAT_TOPK = 3,
+  HISA_OP_ATTENTION = 4
+};
+
+/* Problem sizes (HiSA issue, Configuration table). */
+typedef struct {
+  int32_t B;           /* sequences */
+  int32_t L;           /* query rows per sequence in this step (1 = decode) */
+  int32_t ratio;       /* compress ratio r of the layer (4; 1 = per-token DSA keys) */
+  int32_t window;      /* sliding_window of the local stream (128); 0 = no local stream */
+  int32_t topk;        /* index_topk: pooled rows kept per query, k = min(topk, Np) */
+  int32_t index_block; /* HiSA block size b in pooled rows; 0 disables the hierarchy.
+                          Supported: 0 or a divisor of 64 */
+  int32_t index_keep;  /* HiSA blocks kept by the coarse stage (Kb upper bound) */
+  int32_t H_i, D_i;    /* indexer heads and head dim (64 x 128) */
+  int32_t H, Dk, Dv;   /* main attention heads, key width, value width (Dv <= Dk) */
+  int32_t Np_cap;      /* pooled rows allocated per sequence in keys / pooled_kv */
+  int32_t Wl_cap;      /* local rows allocated per sequence in local_kv */
+  int32_t kI;          /* width of the index rows I given to the attention call */
+  int32_t mode;        /* enum hisa_mode (selection calls) */
+  int32_t idx_dtype;   /* dtype of q_idx and keys: HISA_BF16 or HISA_F32 */
+  int32_t attn_dtype;  /* dtype of q, local_kv, pooled_kv and out: HISA_BF16 or HISA_F32 */
+} hisa_dims;
+
+/* Common selection inputs
+ *   q_idx (B, L, H_i, D_i) idx_dtype: the roped indexer query, one row per query.
+ *   w     (B, L, H_i) f32: the raw weights_proj(x) output.  The library applies
+ *         H_i^-1/2 * D_i^-1/2 (HiSA issue, The indexer query and per-head
+ *         weights; DSA issue, item 1, Score).
+ *   keys  (B, Np_cap, D_i) idx_dtype: the indexer's pooled keys (HiSA issue,
+ *         The pooled stream; for ratio 1, the per-token DSA keys).  Rows at or
+ *         past Np_b are never read.
+ * Scores are relu(q.k) per head, weighted and summed over heads, in f32
+ * (HiSA issue, Conventions).  Index outputs hold absolute pooled row ids in
+ * ascending order, padded with -1; exact score ties keep the lowest id.
+ */
+
+/* The coarse stage alone (HiSA issue, HiSA decode path "coarse" and HiSA
+ * batched path "coarse"): block means rep and block scores cscore, with the
+ * batched eligibility mask (a block is eligible iff its first row is visible,
+ * else -1e30).  nb_cap = Np_cap / index_block; index_block must be > 0.
+ *   cscore_out (B, L, nb_cap) f32: entries past nb_b = floor(Np_b / b) are -1e30.
+ *   rep_out    (B, nb_cap, D_i) f32 or NULL: entries past nb_b are 0. */
+int hisa_block_scores(const hisa_dims* d, const void* q_idx, const float* w, const void* keys,
+                      const int32_t* t0, float* cscore_out, float* rep_out, void* ws,
+                      size_t ws_bytes, void* stream);
+
+/* Single-token selection (HiSA issue, HiSA decode path; L must be 1).  The gate
+ * runs per sequence: dense -> I = 0..Np-1; flat -> the flat top-k; HiSA ->
+ * coarse top-Kb blocks then the fine top-k within them (the tail rows
+ * [nb*b, Np) are never selected).
+ *   I_out       (B, 1, topk) int32.
+ *   top_blk_out (B, 1, index_keep) int32 or NULL: the retained blocks (HiSA
+ *               path only, ascending; -1 elsewhere).
+ *   path_out    (B) int32 or NULL: enum hisa_path per sequence. */
+int hisa_select_decode(const hisa_dims* d, const void* q_idx, const float* w, const void* keys,
+                       const int32_t* t0, int32_t* I_out, int32_t* top_blk_out, int32_t* path_out,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Multi-row selection (HiSA issue, HiSA batched path: prefill chunks and
+ * multi-token verify; any L >= 1).  Per query row j: valid_len = V(t0+j);
+ * blocks with b*beta >= valid_len score -1e30; candidates at or past
+ * valid_len score -1e30.  Rows with fewer than k visible rows then carry
+ * masked ids, which the attention call re-masks.
+ *   I_out (B, L, topk), top_blk_out (B, L, index_keep) or NULL, path_out (B) or NULL. */
+int hisa_select_prefill(const hisa_dims* d, const void* q_idx, const float* w, const void* keys,
+                        const int32_t* t0, int32_t* I_out, int32_t* top_blk_out, int32_t* path_out,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* The flat top-k indexer (HiSA issue, Flat selection; DSA issue, item 1):
+ * score every visible row, -1e30 for p >= V(t0+j), keep the top
+ * k = min(topk, Np) ids.  Ignores mode and index_block.  ratio = 1 gives the
+ * per-token DSA indexer.
+ *   I_out (B, L, topk) int32. */
+int flat_topk_select(const hisa_dims* d, const void* q_idx, const float* w, const void* keys,
+                     const int32_t* t0, int32_t* I_out, void* ws, size_t ws_bytes, void* stream);
+
+/* The sparse local+pooled combine (HiSA issue, Consuming the selection:
+ * sparse combine; DSA issue, item 3: gather, not mask).  For query row j at
+ * t = t0 + j and each head h: one softmax over
+ *   - the local rows at positions s with t - window < s <= t, and
+ *   - the pooled rows I[b, j, kk] with 0 <= id < V(t) (others are masked),
+ * plus the sink logit sinks[h] in the normaliser (mass, no value); scores are
+ * (q * Dk^-1/2) . row; K = V with one shared KV head; the value of a row is its
+ * first Dv entries.  No visible key and no sink gives 0.
+ *   q         (B, L, H, Dk) attn_dtype, already roped.
+ *   local_kv  (B, Wl_cap, Dk) attn_dtype: row r holds absolute position
+ *             ls + r, ls = max(0, t0[b] - window + 1); rows run through
+ *             position t0[b] + L - 1.
+ *   pooled_kv (B, Np_cap, Dk) attn_dtype: the attention compressor's pooled rows.
+ *   I         (B, L, kI) int32: pooled ids from a selection call (or any ids;
+ *             dense attention over all pooled rows is I = 0..Np-1).
+ *   sinks     (H) f32 or NULL.
+ *   out       (B, L, H, Dv) attn_dtype. */
+int sparse_local_pooled_attention(const hisa_dims* d, const void* q, const void* local_kv,
+                                  const void* pooled_kv, const int32_t* I, const float* sinks,
+                                  const int32_t* t0, void* out, void* ws, size_t ws_bytes,
+                                  void* stream);
+
+/* Workspace bytes the call `op` (enum hisa_op) needs for dims d (>= 256-byte
+ * aligned offsets inside); 0 when it needs none.  Returns (size_t)-1 for
+ * invalid dims (see hisa_last_error). */
+size_t hisa_workspace_bytes(int op, const hisa_dims* d);
+
+/* Human-readable reason of the last error on this thread ("" if none). */
+const char* hisa_last_error(void);
+
+/* HISA_ABI_VERSION of the loaded library. */
+int hisa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HISA_H */

@@ -69,6 +69,7 @@ def lib():
         L.orc_select_row.argtypes = [dp, f32p, f32p, f32p, ctypes.c_int, ctypes.c_int, i32p,
                                      i32p, i32p, i32p]
         L.orc_select.argtypes = [dp, f32p, f32p, f32p, i32p, i32p, i32p, i32p]
+        L.orc_coarse_row.argtypes = [dp, f32p, f32p, f32p, ctypes.c_int, ctypes.c_int, f32p]
         L.orc_block_scores.argtypes = [dp, f32p, f32p, f32p, i32p, f32p, f32p]
         L.orc_scores_of.argtypes = [dp, f32p, f32p, f32p, ctypes.c_int, ctypes.c_int, i32p,
                                     ctypes.c_int, f32p]
@@ -170,6 +171,15 @@ def block_scores(d: Dims, q, w, keys, t0):
     rep = np.empty((d.B, nb_cap, d.D_i), np.float32)
     lib().orc_block_scores(ctypes.byref(dc), _fp(q), _fp(w), _fp(keys), _ip(t0), _fp(cs), _fp(rep))
     return cs, rep
+
+
+def coarse_row(d: Dims, q_row, w_row, keys_b, t0: int, j: int) -> np.ndarray:
+    """Coarse scores (nb_cap,) of one query row, batched mask applied."""
+    dc = d.c()
+    q_row, w_row, keys_b = _f32(q_row), _f32(w_row), _f32(keys_b)
+    out = np.empty(d.Np_cap // d.index_block, np.float32)
+    lib().orc_coarse_row(ctypes.byref(dc), _fp(q_row), _fp(w_row), _fp(keys_b), int(t0), int(j), _fp(out))
+    return out
 
 
 def scores_of(d: Dims, q_row, w_row, keys_b, t0: int, j: int, ids) -> np.ndarray:

@@ -232,9 +232,30 @@ void orc_select(const orc_dims* d, const float* q, const float* w, const float* 
   }
 }
 
+/* Coarse scores of one query row (b, j): cscore[beta] for beta < nb_cap,
+ * with the batched eligibility mask (beta * b >= valid_len -> -1e30) and -1e30
+ * past nb.  keys_b is sequence b's (Np_cap, D_i) keys. */
+void orc_coarse_row(const orc_dims* d, const float* q_row, const float* w_row, const float* keys_b,
+                    int t0, int j, float* cscore_row) {
+  const int b = d->index_block;
+  const int nb_cap = d->Np_cap / b;
+  const int Np = orc_num_pooled(t0, d->L, d->ratio);
+  const int nb = Np / b;
+  const int valid = orc_visible(t0 + j, d->ratio, Np);
+  double* tmp = (double*)malloc(sizeof(double) * (size_t)d->D_i);
+  for (int beta = 0; beta < nb_cap; beta++) {
+    float v = ORC_NEG;
+    if (beta < nb && beta * b < valid) {
+      orc_block_mean(d, keys_b, beta, tmp);
+      v = orc_score_rep(d, q_row, w_row, tmp);
+    }
+    cscore_row[beta] = v;
+  }
+  free(tmp);
+}
+
 /* The coarse stage alone: rep (B, nb_cap, D_i) rounded to float (zeros past
- * nb) and cscore (B, L, nb_cap) with the batched eligibility mask (-1e30 past
- * nb as well).  nb_cap = Np_cap / index_block. */
+ * nb) and cscore (B, L, nb_cap) from orc_coarse_row.  nb_cap = Np_cap / b. */
 void orc_block_scores(const orc_dims* d, const float* q, const float* w, const float* keys,
                       const int* t0, float* cscore, float* rep) {
   const int b = d->index_block;
@@ -260,20 +281,8 @@ void orc_block_scores(const orc_dims* d, const float* q, const float* w, const f
 #pragma omp parallel for schedule(dynamic, 1)
   for (long long r = 0; r < rows; r++) {
     const int bb = (int)(r / d->L), j = (int)(r % d->L);
-    const int Np = orc_num_pooled(t0[bb], d->L, d->ratio);
-    const int nb = Np / b;
-    const int valid = orc_visible(t0[bb] + j, d->ratio, Np);
-    const float* keys_b = keys + (long long)bb * d->Np_cap * d->D_i;
-    double* tmp = (double*)malloc(sizeof(double) * (size_t)d->D_i);
-    for (int beta = 0; beta < nb_cap; beta++) {
-      float v = ORC_NEG;
-      if (beta < nb && beta * b < valid) {
-        orc_block_mean(d, keys_b, beta, tmp);
-        v = orc_score_rep(d, q + r * d->H_i * d->D_i, w + r * d->H_i, tmp);
-      }
-      cscore[r * nb_cap + beta] = v;
-    }
-    free(tmp);
+    orc_coarse_row(d, q + r * d->H_i * d->D_i, w + r * d->H_i,
+                   keys + (long long)bb * d->Np_cap * d->D_i, t0[bb], j, cscore + r * nb_cap);
   }
 }
 

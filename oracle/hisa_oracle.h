@@ -57,6 +57,8 @@ void orc_select_row(const orc_dims* d, const float* q_row, const float* w_row,
                     int* I_row, int* blk_row, int* path);
 void orc_select(const orc_dims* d, const float* q, const float* w, const float* keys,
                 const int* t0, int* I, int* blk, int* path);
+void orc_coarse_row(const orc_dims* d, const float* q_row, const float* w_row, const float* keys_b,
+                    int t0, int j, float* cscore_row);
 void orc_block_scores(const orc_dims* d, const float* q, const float* w, const float* keys,
                       const int* t0, float* cscore, float* rep);
 void orc_scores_of(const orc_dims* d, const float* q_row, const float* w_row,

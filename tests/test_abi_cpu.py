@@ -1,0 +1,101 @@
+"""Host-side checks of libhisa.so that need no GPU: the library loads, exports
+every function include/hisa.h declares, sizes workspaces, and turns bad
+arguments into the documented error codes before anything is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from top_kv_indexer_amd import hisa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hisa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\**\s*([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(hisa.LIB_PATH):
+        from top_kv_indexer_amd import build
+        build.build()
+    return hisa.lib()
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert set(names) == set(hisa.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.hisa_abi_version() == 1
+
+
+def dims(**kw):
+    base = dict(B=1, L=1, ratio=4, window=128, topk=512, index_block=64, index_keep=16, H_i=64, D_i=128,
+                H=64, Dk=512, Dv=512, Np_cap=16384, Wl_cap=128, kI=512, mode=0, idx_dtype=hisa.BF16,
+                attn_dtype=hisa.BF16)
+    base.update(kw)
+    return hisa.hisa_dims(**base)
+
+
+def test_workspace_sizes(lib):
+    d = dims()
+    # decode: f32 scores of every pooled row + one coarse score per block
+    assert hisa.workspace_bytes(hisa.OP_SELECT_DECODE, d) == 16384 * 4 + 256 * 4
+    assert hisa.workspace_bytes(hisa.OP_FLAT_TOPK, dims(L=4, Np_cap=1000)) == ((4 * 1000 * 4 + 255) // 256) * 256
+    # single-row attention splits the 640 rows into 20 parts of 32
+    assert hisa.workspace_bytes(hisa.OP_ATTENTION, d) == 20 * 64 * 514 * 4
+    # many rows: no split, no workspace
+    assert hisa.workspace_bytes(hisa.OP_ATTENTION, dims(L=2048, Wl_cap=2175)) == 0
+    n = hisa.workspace_bytes(hisa.OP_SELECT_PREFILL, dims(L=2048))
+    assert n >= 2048 * 16384 * 4 + 2048 * 256 * 4
+
+
+@pytest.mark.parametrize("op,kw,code", [
+    (hisa.OP_SELECT_DECODE, dict(L=2), -1),
+    (hisa.OP_SELECT_DECODE, dict(index_block=48), -1),
+    (hisa.OP_SELECT_DECODE, dict(index_keep=0), -1),
+    (hisa.OP_SELECT_DECODE, dict(index_keep=2000), -1),
+    (hisa.OP_SELECT_DECODE, dict(idx_dtype=7), -2),
+    (hisa.OP_SELECT_DECODE, dict(topk=0), -1),
+    (hisa.OP_SELECT_DECODE, dict(B=0), -1),
+    (hisa.OP_SELECT_DECODE, dict(Np_cap=0), -1),
+    (hisa.OP_SELECT_DECODE, dict(ratio=4, Np_cap=600000000), -4),
+    (hisa.OP_BLOCK_SCORES, dict(index_block=0), -1),
+    (hisa.OP_ATTENTION, dict(Dv=600), -1),
+    (hisa.OP_ATTENTION, dict(attn_dtype=3), -2),
+    (hisa.OP_ATTENTION, dict(attn_dtype=hisa.F32, Dk=2048, Dv=2048), -1),
+    (hisa.OP_ATTENTION, dict(kI=-1), -1),
+])
+def test_bad_dims_are_rejected(lib, op, kw, code):
+    d = dims(**kw)
+    assert lib.hisa_workspace_bytes(op, ctypes.byref(d)) == ctypes.c_size_t(-1).value
+    assert hisa.last_error() != ""
+    fake = ctypes.c_void_p(256)  # never dereferenced: the checks fail first
+    if op == hisa.OP_SELECT_DECODE:
+        rc = lib.hisa_select_decode(ctypes.byref(d), fake, fake, fake, fake, fake, None, None, fake, 1 << 30, None)
+    elif op == hisa.OP_BLOCK_SCORES:
+        rc = lib.hisa_block_scores(ctypes.byref(d), fake, fake, fake, fake, fake, None, fake, 1 << 30, None)
+    else:
+        rc = lib.sparse_local_pooled_attention(ctypes.byref(d), fake, fake, fake, fake, None, fake, fake, fake,
+                                               1 << 30, None)
+    assert rc == code, hisa.last_error()
+
+
+def test_small_workspace_and_null_pointers(lib):
+    d = dims()
+    fake = ctypes.c_void_p(256)
+    rc = lib.hisa_select_decode(ctypes.byref(d), fake, fake, fake, fake, fake, None, None, fake, 16, None)
+    assert rc == -3 and "workspace" in hisa.last_error()
+    rc = lib.hisa_select_decode(ctypes.byref(d), fake, fake, fake, fake, None, None, None, fake, 1 << 30, None)
+    assert rc == -1 and "NULL" in hisa.last_error()
+    rc = lib.hisa_select_decode(ctypes.byref(d), fake, fake, fake, fake, fake, None, None, ctypes.c_void_p(257),
+                                1 << 30, None)
+    assert rc == -1 and "aligned" in hisa.last_error()
+    rc = lib.flat_topk_select(None, fake, fake, fake, fake, fake, fake, 1 << 30, None)
+    assert rc == -1

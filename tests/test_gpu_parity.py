@@ -1,0 +1,334 @@
+"""Parity of the HIP library (through its C ABI) with the CPU oracle on the
+same seeded inputs: the five workloads at full size (oracle on sampled rows
+where it is slow) plus edge cases (ragged batches mixing the dense / flat /
+HiSA / invalid paths, early prefill rows with fewer than k visible rows, tail
+blocks, window 0, no sinks, masked and -1 ids, the generic VALU kernels)."""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import parity
+from top_kv_indexer_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def hisa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from top_kv_indexer_amd import hisa as h
+    h.lib()  # fails loudly when the library is missing
+    return h
+
+
+_cache = {}
+
+
+def inputs(w, seed):
+    key = (repr(w), seed)
+    if key not in _cache:
+        say(f"[gen] {w.name} seed={seed}")
+        x = synth.make_inputs(w, seed)
+        dt = torch.bfloat16 if w.bf16 else torch.float32
+        g = {}
+        for k in ("q_idx", "keys", "q", "local_kv", "pooled_kv"):
+            g[k] = torch.from_numpy(x[k]).to("cuda").to(dt).contiguous()
+        g["w"] = torch.from_numpy(x["w"]).to("cuda")
+        g["sinks"] = None if x["sinks"] is None else torch.from_numpy(x["sinks"]).to("cuda")
+        g["t0"] = torch.from_numpy(x["t0"]).to("cuda")
+        _cache.clear()
+        _cache[key] = (x, g)
+    return _cache[key]
+
+
+def odims(w, x, kI=0, force_flat=0):
+    return oracle.Dims(B=w.B, L=w.L, ratio=w.ratio, window=w.window, topk=w.topk, index_block=w.index_block,
+                       index_keep=w.index_keep, H_i=w.H_i, D_i=w.D_i, H=w.H, Dk=w.Dk, Dv=w.Dv,
+                       Np_cap=int(x["Np_cap"]), force_flat=force_flat)
+
+
+def sel_kw(w, mode=0):
+    return dict(ratio=w.ratio, topk=w.topk, index_block=w.index_block, index_keep=w.index_keep, mode=mode)
+
+
+def rows_of(w, sample):
+    if sample is None or w.B * w.L <= sample:
+        return [(b, j) for b in range(w.B) for j in range(w.L)]
+    rng = np.random.default_rng(123)
+    picks = {(0, 0), (w.B - 1, w.L - 1), (0, w.L // 2)}
+    while len(picks) < sample:
+        picks.add((int(rng.integers(w.B)), int(rng.integers(w.L))))
+    return sorted(picks)
+
+
+def check_selection(w, x, I, blk, path, mode=0, sample=None):
+    d = odims(w, x, force_flat=mode)
+    I, blk, path = parity.to_np(I), parity.to_np(blk), parity.to_np(path)
+    for b, j in rows_of(w, sample):
+        Io, blko, po = oracle.select_row(d, x["q_idx"][b, j], x["w"][b, j], x["keys"][b], int(x["t0"][b]), j)
+        assert path[b] == po, (b, path[b], po)
+        parity.check_selection_row(d, x, b, j, I[b, j], blk[b, j] if blk is not None else None, po, Io, blko, po)
+
+
+def check_attention(w, x, I, out, sample=None, tol=None):
+    I = parity.to_np(I)
+    out = parity.to_np(out)
+    d = odims(w, x)
+    tol = tol if tol is not None else (2e-2 if w.bf16 else 1e-4)
+    worst = 0.0
+    for b, j in rows_of(w, sample):
+        ref = oracle.combine_row(d, x["q"][b, j], x["local_kv"][b], x["pooled_kv"][b], I[b, j], x["sinks"],
+                                 int(x["t0"][b]), j)
+        err = parity.max_abs(out[b, j], ref)
+        worst = max(worst, err)
+        assert err <= tol, (b, j, err)
+    return worst
+
+
+def run_attention(hisa, w, g, I):
+    return hisa.sparse_local_pooled_attention(g["q"], g["local_kv"], g["pooled_kv"], I, g["sinks"], g["t0"],
+                                              ratio=w.ratio, window=w.window)
+
+
+DECODE = [synth.TINY_DECODE, synth.FLASH_DECODE, synth.BATCHED_DECODE]
+
+
+@pytest.mark.parametrize("w", DECODE, ids=lambda w: w.name)
+def test_decode_selection_and_attention(hisa, w):
+    x, g = inputs(w, synth.SEEDS[w.name])
+    say(f"[run] hisa_select_decode {w.name}")
+    I, blk, path = hisa.hisa_select_decode(g["q_idx"], g["w"], g["keys"], g["t0"], **sel_kw(w))
+    torch.cuda.synchronize()
+    assert (parity.to_np(path) == hisa.PATH_HISA).all()
+    check_selection(w, x, I, blk, path)
+    say(f"[run] sparse_local_pooled_attention {w.name}")
+    out = run_attention(hisa, w, g, I)
+    torch.cuda.synchronize()
+    say(f"  max-abs {check_attention(w, x, I, out):.3g}")
+
+
+@pytest.mark.parametrize("w", [synth.TINY_DECODE, synth.FLASH_DECODE], ids=lambda w: w.name)
+def test_decode_force_flat_and_flat_indexer(hisa, w):
+    x, g = inputs(w, synth.SEEDS[w.name])
+    say(f"[run] hisa_select_decode force-flat {w.name}")
+    I, blk, path = hisa.hisa_select_decode(g["q_idx"], g["w"], g["keys"], g["t0"], **sel_kw(w, mode=1))
+    torch.cuda.synchronize()
+    assert (parity.to_np(path) == hisa.PATH_FLAT).all()
+    assert (parity.to_np(blk) == -1).all()
+    check_selection(w, x, I, blk, path, mode=1)
+    say(f"[run] flat_topk_select {w.name}")
+    If = hisa.flat_topk_select(g["q_idx"], g["w"], g["keys"], g["t0"], ratio=w.ratio, topk=w.topk)
+    torch.cuda.synchronize()
+    check_selection(w, x, If, None, path, mode=1)
+
+
+def test_prefill_selection_and_attention(hisa):
+    w = synth.PREFILL
+    x, g = inputs(w, synth.SEEDS[w.name])
+    say(f"[run] hisa_select_prefill {w.name}")
+    I, blk, path = hisa.hisa_select_prefill(g["q_idx"], g["w"], g["keys"], g["t0"], **sel_kw(w))
+    torch.cuda.synchronize()
+    assert (parity.to_np(path) == hisa.PATH_HISA).all()
+    check_selection(w, x, I, blk, path, sample=40)
+    # causality on every row: all selected ids are visible (>= k rows visible here)
+    In = parity.to_np(I)
+    V = (int(x["t0"][0]) + np.arange(w.L) + 1) // w.ratio
+    assert (In[0] < V[:, None]).all() and (In >= 0).all()
+    say(f"[run] sparse_local_pooled_attention {w.name}")
+    out = run_attention(hisa, w, g, I)
+    torch.cuda.synchronize()
+    say(f"  max-abs {check_attention(w, x, I, out, sample=24):.3g}")
+
+
+@pytest.mark.parametrize("w", [synth.DSA_DECODE, synth.DSA_PREFILL], ids=lambda w: w.name)
+def test_flat_dsa(hisa, w):
+    x, g = inputs(w, synth.SEEDS[w.name])
+    say(f"[run] flat_topk_select {w.name}")
+    I = hisa.flat_topk_select(g["q_idx"], g["w"], g["keys"], g["t0"], ratio=w.ratio, topk=w.topk)
+    torch.cuda.synchronize()
+    d = odims(w, x)
+    In = parity.to_np(I)
+    for b, j in rows_of(w, 5):
+        q, ww, kb, t0 = x["q_idx"][b, j], x["w"][b, j], x["keys"][b], int(x["t0"][b])
+        Io, _, _ = oracle.select_row(dataclasses.replace(d, index_block=0), q, ww, kb, t0, j)
+        parity.compare_sets(In[b, j], Io, lambda ids: oracle.scores_of(d, q, ww, kb, t0, j, ids), what=f"({b},{j})")
+    say(f"[run] sparse_local_pooled_attention {w.name}")
+    out = run_attention(hisa, w, g, I)
+    torch.cuda.synchronize()
+    say(f"  max-abs {check_attention(w, x, I, out, sample=3):.3g}")
+
+
+def test_block_scores(hisa):
+    for w in (synth.FLASH_DECODE, synth.TINY_DECODE, synth.PREFILL.with_(L=96)):
+        seed = 77
+        x, g = inputs(w, seed)
+        say(f"[run] hisa_block_scores {w.name}")
+        cs, rep = hisa.hisa_block_scores(g["q_idx"], g["w"], g["keys"], g["t0"], ratio=w.ratio,
+                                         index_block=w.index_block, want_rep=True)
+        torch.cuda.synchronize()
+        d = odims(w, x)
+        cso, repo = oracle.block_scores(d, x["q_idx"], x["w"], x["keys"], x["t0"])
+        np.testing.assert_allclose(parity.to_np(rep), repo, rtol=1e-6, atol=1e-7)
+        csg = parity.to_np(cs)
+        masked = cso == np.float32(-1e30)
+        assert (csg[masked] == np.float32(-1e30)).all()
+        scale = np.abs(cso[~masked]).max()
+        np.testing.assert_allclose(csg[~masked], cso[~masked], rtol=1e-4, atol=1e-5 * scale)
+
+
+# ------------------------------------------------------------------ edge cases
+
+MIXED = synth.Workload("mixed_paths_b6", B=6, L=1, ratio=4, window=128, topk=512, index_block=64, index_keep=16,
+                       H_i=64, D_i=128, H=64, Dk=512, Dv=512, bf16=True,
+                       # Np = 300 (dense), 700 (flat), 1024 (HiSA, no tail), 1500 (HiSA + tail),
+                       # 5000 and 4100 (HiSA)
+                       t0=[1200, 2800, 4096, 6000, 20000, 16400], planted=4, Np_cap=5000)
+
+
+def test_mixed_paths_decode(hisa):
+    w = MIXED
+    x, g = inputs(w, 5)
+    x = dict(x)
+    say("[run] mixed-path decode")
+    I, blk, path = hisa.hisa_select_decode(g["q_idx"], g["w"], g["keys"], g["t0"], **sel_kw(w))
+    torch.cuda.synchronize()
+    p = parity.to_np(path)
+    assert p.tolist() == [hisa.PATH_DENSE, hisa.PATH_FLAT, hisa.PATH_HISA, hisa.PATH_HISA, hisa.PATH_HISA,
+                          hisa.PATH_HISA], p
+    d = odims(w, x)
+    In, bn = parity.to_np(I), parity.to_np(blk)
+    for b in range(6):
+        parity.check_selection_row(d, x, b, 0, In[b, 0], bn[b, 0], p[b])
+    # tail exclusion where Np is not a multiple of the block
+    assert (In[3, 0] < (1500 // 64) * 64).all()
+    say("[run] mixed-path attention")
+    out = run_attention(hisa, w, g, I)
+    torch.cuda.synchronize()
+    o = parity.to_np(out)
+    dd = odims(w, x)
+    for b in range(6):
+        ref = oracle.combine_row(dd, x["q"][b, 0], x["local_kv"][b], x["pooled_kv"][b], In[b, 0], x["sinks"],
+                                 int(x["t0"][b]), 0)
+        assert parity.max_abs(o[b, 0], ref) <= 2e-2, b
+
+
+def test_invalid_sequence_outputs(hisa):
+    x, g = inputs(MIXED, 5)
+    w = MIXED
+    g = dict(g)
+    g["t0"] = g["t0"].clone()
+    g["t0"][5] = 30000  # Np = 7500 > Np_cap = 5000
+    say("[run] invalid t0 (Np > Np_cap)")
+    I, blk, path = hisa.hisa_select_decode(g["q_idx"], g["w"], g["keys"], g["t0"], **sel_kw(w))
+    Ip, _, pp = hisa.hisa_select_prefill(g["q_idx"], g["w"], g["keys"], g["t0"], **sel_kw(w))
+    If = hisa.flat_topk_select(g["q_idx"], g["w"], g["keys"], g["t0"], ratio=4, topk=512)
+    out = run_attention(hisa, w, g, I)
+    torch.cuda.synchronize()
+    assert parity.to_np(path)[5] == hisa.PATH_INVALID and parity.to_np(pp)[5] == hisa.PATH_INVALID
+    assert (parity.to_np(I)[5] == -1).all() and (parity.to_np(blk)[5] == -1).all()
+    assert (parity.to_np(Ip)[5] == -1).all() and (parity.to_np(If)[5] == -1).all()
+    assert (parity.to_np(out)[5] == 0).all()
+    # the valid sequences are unaffected and prefill at L = 1 equals decode
+    np.testing.assert_array_equal(np.sort(parity.to_np(I)[:5], -1), np.sort(parity.to_np(Ip)[:5], -1))
+
+
+EARLY = synth.Workload("early_rows_prefill", B=2, L=800, ratio=1, window=128, topk=512, index_block=64,
+                       index_keep=16, H_i=64, D_i=128, H=64, Dk=512, Dv=512, bf16=True, t0=[300, 70],
+                       planted=0, Np_cap=1100)
+
+
+def test_prefill_early_rows_and_small_t0(hisa):
+    # t0 = 300, ratio 1: Np = 1100 (HiSA) but row j sees only 301 + j rows, so
+    # rows j < 211 hold masked ids; t0 = 70 < window: short local streams and a
+    # flat sequence (Np = 870).
+    w = EARLY
+    x, g = inputs(w, 9)
+    say("[run] early-row prefill")
+    I, blk, path = hisa.hisa_select_prefill(g["q_idx"], g["w"], g["keys"], g["t0"], **sel_kw(w))
+    torch.cuda.synchronize()
+    assert parity.to_np(path).tolist() == [hisa.PATH_HISA, hisa.PATH_FLAT]
+    check_selection(w, x, I, blk, path, sample=60)
+    In = parity.to_np(I)
+    for j in (0, 100, 210, 211, 500):
+        V = 301 + j
+        vis = In[0, j][(In[0, j] >= 0) & (In[0, j] < V)]
+        assert len(vis) == min(V, 512), (j, len(vis))
+    say("[run] early-row attention")
+    out = run_attention(hisa, w, g, I)
+    torch.cuda.synchronize()
+    check_attention(w, x, I, out, sample=40)
+
+
+def test_attention_masks_window0_no_sinks(hisa):
+    w = synth.FLASH_DECODE.with_(name="flash_b3_window0", B=3, t0=[65536, 40000, 9000], window=0, sinks=False,
+                                 planted=0, Np_cap=16384)
+    x, g = inputs(w, 11)
+    rng = np.random.default_rng(3)
+    kI = 300
+    Iw = np.stack([rng.choice(int(n), kI, replace=False) for n in x["Np"]])[:, None, :].astype(np.int32)
+    Iw[:, :, :17] = -1
+    Iw[:, :, 17:30] = x["Np"][:, None, None] + 5      # invisible ids
+    Ig = torch.from_numpy(Iw).to("cuda")
+    say("[run] attention window 0, no sinks, masked ids")
+    out = hisa.sparse_local_pooled_attention(g["q"], None, g["pooled_kv"], Ig, None, g["t0"], ratio=4, window=0)
+    torch.cuda.synchronize()
+    d = odims(w, x)
+    o = parity.to_np(out)
+    for b in range(3):
+        ref = oracle.combine_row(d, x["q"][b, 0], np.zeros((1, w.Dk), np.float32), x["pooled_kv"][b], Iw[b, 0], None,
+                                 int(x["t0"][b]), 0)
+        assert parity.max_abs(o[b, 0], ref) <= 2e-2
+
+
+def test_generic_kernels_prefill_f32(hisa):
+    # f32 inputs take the VALU kernels; L > 1 with a tail block and ragged t0.
+    w = synth.TINY_DECODE.with_(name="tiny_prefill_f32", B=2, L=37, t0=[4000, 2500], Np_cap=1100, planted=3)
+    x, g = inputs(w, 13)
+    say("[run] generic prefill selection")
+    I, blk, path = hisa.hisa_select_prefill(g["q_idx"], g["w"], g["keys"], g["t0"], **sel_kw(w))
+    torch.cuda.synchronize()
+    check_selection(w, x, I, blk, path)
+    say("[run] generic attention")
+    out = run_attention(hisa, w, g, I)
+    torch.cuda.synchronize()
+    check_attention(w, x, I, out)
+    If = hisa.flat_topk_select(g["q_idx"], g["w"], g["keys"], g["t0"], ratio=w.ratio, topk=w.topk)
+    torch.cuda.synchronize()
+    d = odims(w, x, force_flat=1)
+    In = parity.to_np(If)
+    for b in range(2):
+        for j in (0, 17, 36):
+            Io, _, _ = oracle.select_row(d, x["q_idx"][b, j], x["w"][b, j], x["keys"][b], int(x["t0"][b]), j)
+            parity.compare_sets(In[b, j], Io, lambda ids: oracle.scores_of(d, x["q_idx"][b, j], x["w"][b, j],
+                                                                           x["keys"][b], int(x["t0"][b]), j, ids))
+
+
+def test_dense_equivalence(hisa):
+    # HiSA issue, Validation: with every pooled row selected (k == Np) the
+    # sparse combine equals dense local + pooled attention.
+    w = synth.FLASH_DECODE.with_(name="dense_np400", t0=[1600], planted=0, Np_cap=400)
+    x, g = inputs(w, 17)
+    I, _, path = hisa.hisa_select_decode(g["q_idx"], g["w"], g["keys"], g["t0"], **sel_kw(w))
+    torch.cuda.synchronize()
+    assert parity.to_np(path)[0] == hisa.PATH_DENSE
+    In = parity.to_np(I)
+    np.testing.assert_array_equal(In[0, 0, :400], np.arange(400))
+    assert (In[0, 0, 400:] == -1).all()
+    out = run_attention(hisa, w, g, I)
+    perm = torch.from_numpy(np.random.default_rng(0).permutation(400).astype(np.int32)[None, None]).to("cuda")
+    out2 = hisa.sparse_local_pooled_attention(g["q"], g["local_kv"], g["pooled_kv"], perm, g["sinks"], g["t0"],
+                                              ratio=4, window=128)
+    torch.cuda.synchronize()
+    check_attention(w, x, I, out)
+    assert parity.max_abs(parity.to_np(out2), parity.to_np(out)) <= 2e-2

@@ -1,0 +1,293 @@
+// hisa_abi.cpp -- the C ABI of libhisa.so: argument checks, workspace layout
+// and the kernel sequence of each call (declared in include/hisa.h).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <initializer_list>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "hisa.h"
+#include "hisa_internal.h"
+
+using hisa::KDims;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int launch_fail(hipError_t e, const char* what) {
+  return fail(HISA_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr long long kMaxElems = 1LL << 40;
+constexpr int kMaxKeep = 1024;
+constexpr int kMaxCandidates = 8192;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool is_sel(int op) { return op == HISA_OP_BLOCK_SCORES || op == HISA_OP_SELECT_DECODE || op == HISA_OP_SELECT_PREFILL || op == HISA_OP_FLAT_TOPK; }
+
+// Checks dims for `op` and fills the kernel-side description.
+int make_kdims(int op, const hisa_dims* d, KDims* k) {
+  if (!d) return fail(HISA_ERR_ARG, "dims is NULL");
+  if (op < HISA_OP_BLOCK_SCORES || op > HISA_OP_ATTENTION) return fail(HISA_ERR_ARG, "unknown op %d", op);
+  if (d->B < 1 || d->B > 65535) return fail(HISA_ERR_ARG, "B = %d must be in [1, 65535]", d->B);
+  if (d->L < 1 || d->L > 524280) return fail(HISA_ERR_ARG, "L = %d must be in [1, 524280]", d->L);
+  if (d->ratio < 1) return fail(HISA_ERR_ARG, "ratio = %d must be >= 1", d->ratio);
+  if (d->window < 0) return fail(HISA_ERR_ARG, "window = %d must be >= 0", d->window);
+  if (d->Np_cap < 1) return fail(HISA_ERR_ARG, "Np_cap = %d must be >= 1", d->Np_cap);
+  // Every visible position must fit int32: t0 + L <= ratio * (Np_cap + 1).
+  if ((long long)d->ratio * ((long long)d->Np_cap + 1) + d->L >= (1LL << 31))
+    return fail(HISA_ERR_OVERFLOW, "ratio * (Np_cap + 1) + L overflows int32");
+  KDims kd{};
+  kd.B = d->B; kd.L = d->L; kd.ratio = d->ratio; kd.window = d->window; kd.topk = d->topk;
+  kd.index_block = d->index_block; kd.index_keep = d->index_keep; kd.H_i = d->H_i; kd.D_i = d->D_i;
+  kd.H = d->H; kd.Dk = d->Dk; kd.Dv = d->Dv; kd.Np_cap = d->Np_cap; kd.Wl_cap = d->Wl_cap; kd.kI = d->kI;
+  kd.force_flat = d->mode == HISA_MODE_FORCE_FLAT;
+  kd.force_path = -1;
+  if (is_sel(op)) {
+    if (d->idx_dtype != HISA_F32 && d->idx_dtype != HISA_BF16) return fail(HISA_ERR_DTYPE, "idx_dtype %d", d->idx_dtype);
+    if (d->mode != HISA_MODE_AUTO && d->mode != HISA_MODE_FORCE_FLAT) return fail(HISA_ERR_ARG, "mode = %d", d->mode);
+    if (d->topk < 1) return fail(HISA_ERR_ARG, "topk = %d must be >= 1", d->topk);
+    if (d->H_i < 1 || d->D_i < 1 || d->D_i > 1024) return fail(HISA_ERR_ARG, "H_i = %d, D_i = %d (need D_i in [1, 1024])", d->H_i, d->D_i);
+    if (d->index_block < 0 || (d->index_block > 0 && 64 % d->index_block != 0))
+      return fail(HISA_ERR_ARG, "index_block = %d must be 0 or a divisor of 64", d->index_block);
+    if (d->index_keep < 1 || d->index_keep > kMaxKeep) return fail(HISA_ERR_ARG, "index_keep = %d must be in [1, %d]", d->index_keep, kMaxKeep);
+    if ((long long)d->index_keep * d->index_block > kMaxCandidates)
+      return fail(HISA_ERR_ARG, "index_keep * index_block = %lld exceeds %d", (long long)d->index_keep * d->index_block, kMaxCandidates);
+    if (op == HISA_OP_BLOCK_SCORES && d->index_block == 0) return fail(HISA_ERR_ARG, "hisa_block_scores needs index_block > 0");
+    if (op == HISA_OP_SELECT_DECODE && d->L != 1) return fail(HISA_ERR_ARG, "hisa_select_decode needs L == 1 (got %d)", d->L);
+    const long long rows = (long long)d->B * d->L;
+    if (rows * d->H_i * d->D_i > kMaxElems || (long long)d->B * d->Np_cap * d->D_i > kMaxElems ||
+        rows * d->Np_cap > kMaxElems || rows * d->topk > kMaxElems)
+      return fail(HISA_ERR_OVERFLOW, "selection tensors too large");
+    if (d->idx_dtype == HISA_BF16 && d->D_i % 8 != 0) return fail(HISA_ERR_ARG, "bf16 keys need D_i %% 8 == 0");
+    kd.nb_cap = d->index_block > 0 ? d->Np_cap / d->index_block : 0;
+    kd.w_scale = (float)(1.0 / std::sqrt((double)d->H_i * (double)d->D_i));
+  } else {
+    if (d->attn_dtype != HISA_F32 && d->attn_dtype != HISA_BF16) return fail(HISA_ERR_DTYPE, "attn_dtype %d", d->attn_dtype);
+    if (d->H < 1 || d->Dk < 1 || d->Dv < 1 || d->Dv > d->Dk) return fail(HISA_ERR_ARG, "H = %d, Dk = %d, Dv = %d (need 1 <= Dv <= Dk)", d->H, d->Dk, d->Dv);
+    if (d->kI < 0) return fail(HISA_ERR_ARG, "kI = %d must be >= 0", d->kI);
+    if (d->window > 0 && d->Wl_cap < 1) return fail(HISA_ERR_ARG, "Wl_cap = %d must be >= 1 when window > 0", d->Wl_cap);
+    const long long rows = (long long)d->B * d->L;
+    if (rows * d->H * d->Dk > kMaxElems || (long long)d->B * d->Np_cap * d->Dk > kMaxElems ||
+        (long long)d->B * d->Wl_cap * d->Dk > kMaxElems || rows * d->kI > kMaxElems)
+      return fail(HISA_ERR_OVERFLOW, "attention tensors too large");
+    if (rows > 2147483647LL) return fail(HISA_ERR_OVERFLOW, "B * L overflows the grid");
+    kd.attn_scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d->Dk));
+    const bool bf = d->attn_dtype == HISA_BF16;
+    if (!hisa::attn_mfma_ok(kd, bf) && !hisa::attn_generic_ok(kd))
+      return fail(HISA_ERR_ARG, "shape not supported: Dk = %d, window + kI = %lld (generic path needs Dk <= 1024 and window + kI <= 4096)",
+                  d->Dk, (long long)d->window + d->kI);
+  }
+  *k = kd;
+  return HISA_OK;
+}
+
+struct Layout {
+  size_t total = 0;
+  size_t rep = 0, rep3 = 0, cscore = 0, scores = 0, fscore = 0, partial = 0;
+  int splits = 1;
+};
+
+size_t take(Layout& l, size_t bytes) {
+  const size_t off = l.total;
+  l.total += align256(bytes);
+  return off;
+}
+
+Layout layout(int op, const hisa_dims* d, const KDims& k) {
+  Layout l;
+  const size_t B = (size_t)d->B, L = (size_t)d->L;
+  const bool bf = d->idx_dtype == HISA_BF16;
+  const size_t nb_cap = (size_t)k.nb_cap;
+  switch (op) {
+    case HISA_OP_BLOCK_SCORES:
+      l.rep = take(l, B * nb_cap * d->D_i * sizeof(float));
+      l.rep3 = hisa::idx_mfma_ok(k, bf) ? take(l, 3 * B * nb_cap * d->D_i * sizeof(uint16_t)) : 0;
+      break;
+    case HISA_OP_SELECT_DECODE:
+      l.fscore = take(l, B * d->Np_cap * sizeof(float));
+      l.cscore = take(l, B * std::max<size_t>(nb_cap, 1) * sizeof(float));
+      break;
+    case HISA_OP_SELECT_PREFILL:
+      if (nb_cap > 0) {
+        l.rep = take(l, B * nb_cap * d->D_i * sizeof(float));
+        l.rep3 = hisa::idx_mfma_ok(k, bf) ? take(l, 3 * B * nb_cap * d->D_i * sizeof(uint16_t)) : 0;
+        l.cscore = take(l, B * L * nb_cap * sizeof(float));
+      }
+      l.scores = take(l, B * L * d->Np_cap * sizeof(float));
+      break;
+    case HISA_OP_FLAT_TOPK:
+      l.scores = take(l, B * L * d->Np_cap * sizeof(float));
+      break;
+    case HISA_OP_ATTENTION:
+      l.splits = hisa::attn_splits(k, d->attn_dtype == HISA_BF16);
+      l.partial = take(l, hisa::attn_partial_bytes(k, l.splits));
+      break;
+  }
+  return l;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return (T*)((char*)ws + off);
+}
+
+int check_ws(const Layout& l, void* ws, size_t ws_bytes) {
+  if (l.total > ws_bytes) return fail(HISA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, l.total);
+  if (l.total > 0 && !ws) return fail(HISA_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", l.total);
+  if (ws && ((uintptr_t)ws & 255)) return fail(HISA_ERR_ARG, "workspace must be 256-byte aligned");
+  return HISA_OK;
+}
+
+int check_ptrs(std::initializer_list<const void*> ptrs, const char* names) {
+  for (const void* p : ptrs)
+    if (!p) return fail(HISA_ERR_ARG, "NULL pointer among (%s)", names);
+  return HISA_OK;
+}
+
+int prepare(int op, const hisa_dims* d, KDims* k, Layout* l, void* ws, size_t ws_bytes) {
+  int rc = make_kdims(op, d, k);
+  if (rc) return rc;
+  *l = layout(op, d, *k);
+  return check_ws(*l, ws, ws_bytes);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hisa_last_error(void) { return g_err.c_str(); }
+
+int hisa_abi_version(void) { return HISA_ABI_VERSION; }
+
+size_t hisa_workspace_bytes(int op, const hisa_dims* d) {
+  KDims k;
+  if (make_kdims(op, d, &k)) return (size_t)-1;
+  return layout(op, d, k).total;
+}
+
+int hisa_block_scores(const hisa_dims* d, const void* q_idx, const float* w, const void* keys, const int32_t* t0,
+                      float* cscore_out, float* rep_out, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  KDims k;
+  Layout l;
+  int rc = prepare(HISA_OP_BLOCK_SCORES, d, &k, &l, ws, ws_bytes);
+  if (rc) return rc;
+  if ((rc = check_ptrs({q_idx, w, keys, t0, cscore_out}, "q_idx, w, keys, t0, cscore_out"))) return rc;
+  const bool bf = d->idx_dtype == HISA_BF16;
+  hipStream_t st = (hipStream_t)stream;
+  float* rep = rep_out ? rep_out : at<float>(ws, l.rep);
+  uint16_t* rep3 = hisa::idx_mfma_ok(k, bf) ? at<uint16_t>(ws, l.rep3) : nullptr;
+  hipError_t e = hisa::launch_block_mean(k, bf, true, keys, t0, rep, rep3, st);
+  if (e != hipSuccess) return launch_fail(e, "block mean");
+  e = hisa::launch_coarse(k, bf, true, q_idx, w, rep, rep3, t0, cscore_out, st);
+  if (e != hipSuccess) return launch_fail(e, "coarse scores");
+  return HISA_OK;
+}
+
+int hisa_select_decode(const hisa_dims* d, const void* q_idx, const float* w, const void* keys, const int32_t* t0,
+                       int32_t* I_out, int32_t* top_blk_out, int32_t* path_out, void* ws, size_t ws_bytes,
+                       void* stream) {
+  g_err.clear();
+  KDims k;
+  Layout l;
+  int rc = prepare(HISA_OP_SELECT_DECODE, d, &k, &l, ws, ws_bytes);
+  if (rc) return rc;
+  if ((rc = check_ptrs({q_idx, w, keys, t0, I_out}, "q_idx, w, keys, t0, I_out"))) return rc;
+  const bool bf = d->idx_dtype == HISA_BF16;
+  hipStream_t st = (hipStream_t)stream;
+  float* fscore = at<float>(ws, l.fscore);
+  float* cscore = at<float>(ws, l.cscore);
+  hipError_t e = hisa::launch_decode_scan(k, bf, q_idx, w, keys, t0, fscore, cscore, st);
+  if (e != hipSuccess) return launch_fail(e, "decode scan");
+  e = hisa::launch_decode_select(k, fscore, cscore, t0, I_out, top_blk_out, path_out, st);
+  if (e != hipSuccess) return launch_fail(e, "decode select");
+  return HISA_OK;
+}
+
+int hisa_select_prefill(const hisa_dims* d, const void* q_idx, const float* w, const void* keys, const int32_t* t0,
+                        int32_t* I_out, int32_t* top_blk_out, int32_t* path_out, void* ws, size_t ws_bytes,
+                        void* stream) {
+  g_err.clear();
+  KDims k;
+  Layout l;
+  int rc = prepare(HISA_OP_SELECT_PREFILL, d, &k, &l, ws, ws_bytes);
+  if (rc) return rc;
+  if ((rc = check_ptrs({q_idx, w, keys, t0, I_out}, "q_idx, w, keys, t0, I_out"))) return rc;
+  const bool bf = d->idx_dtype == HISA_BF16;
+  hipStream_t st = (hipStream_t)stream;
+  float* cscore = nullptr;
+  hipError_t e;
+  if (k.nb_cap > 0) {
+    float* rep = at<float>(ws, l.rep);
+    uint16_t* rep3 = hisa::idx_mfma_ok(k, bf) ? at<uint16_t>(ws, l.rep3) : nullptr;
+    cscore = at<float>(ws, l.cscore);
+    e = hisa::launch_block_mean(k, bf, false, keys, t0, rep, rep3, st);
+    if (e != hipSuccess) return launch_fail(e, "block mean");
+    e = hisa::launch_coarse(k, bf, false, q_idx, w, rep, rep3, t0, cscore, st);
+    if (e != hipSuccess) return launch_fail(e, "coarse scores");
+  }
+  float* scores = at<float>(ws, l.scores);
+  e = hisa::launch_flat_scores(k, bf, q_idx, w, keys, t0, scores, st);
+  if (e != hipSuccess) return launch_fail(e, "flat scores");
+  e = hisa::launch_topk_rows(k, scores, t0, I_out, nullptr, st);
+  if (e != hipSuccess) return launch_fail(e, "flat top-k");
+  e = hisa::launch_fine(k, bf, q_idx, w, keys, cscore, t0, I_out, top_blk_out, path_out, st);
+  if (e != hipSuccess) return launch_fail(e, "fine selection");
+  return HISA_OK;
+}
+
+int flat_topk_select(const hisa_dims* d, const void* q_idx, const float* w, const void* keys, const int32_t* t0,
+                     int32_t* I_out, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  KDims k;
+  Layout l;
+  int rc = prepare(HISA_OP_FLAT_TOPK, d, &k, &l, ws, ws_bytes);
+  if (rc) return rc;
+  if ((rc = check_ptrs({q_idx, w, keys, t0, I_out}, "q_idx, w, keys, t0, I_out"))) return rc;
+  const bool bf = d->idx_dtype == HISA_BF16;
+  hipStream_t st = (hipStream_t)stream;
+  k.force_path = hisa::PATH_FLAT;
+  float* scores = at<float>(ws, l.scores);
+  hipError_t e = hisa::launch_flat_scores(k, bf, q_idx, w, keys, t0, scores, st);
+  if (e != hipSuccess) return launch_fail(e, "flat scores");
+  e = hisa::launch_topk_rows(k, scores, t0, I_out, nullptr, st);
+  if (e != hipSuccess) return launch_fail(e, "flat top-k");
+  return HISA_OK;
+}
+
+int sparse_local_pooled_attention(const hisa_dims* d, const void* q, const void* local_kv, const void* pooled_kv,
+                                  const int32_t* I, const float* sinks, const int32_t* t0, void* out, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  g_err.clear();
+  KDims k;
+  Layout l;
+  int rc = prepare(HISA_OP_ATTENTION, d, &k, &l, ws, ws_bytes);
+  if (rc) return rc;
+  if ((rc = check_ptrs({q, pooled_kv, t0, out}, "q, pooled_kv, t0, out"))) return rc;
+  if (d->window > 0 && !local_kv) return fail(HISA_ERR_ARG, "local_kv is NULL with window > 0");
+  if (d->kI > 0 && !I) return fail(HISA_ERR_ARG, "I is NULL with kI > 0");
+  const bool bf = d->attn_dtype == HISA_BF16;
+  hipError_t e = hisa::launch_attention(k, bf, q, local_kv, pooled_kv, I, sinks, t0, out,
+                                        l.splits > 1 ? at<float>(ws, l.partial) : nullptr, l.splits,
+                                        (hipStream_t)stream);
+  if (e != hipSuccess) return launch_fail(e, "attention");
+  return HISA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// hisa_internal.h -- kernel-side problem description and launcher entry points
+// shared by the host library (hisa_abi.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hisa {
+
+enum { PATH_INVALID = -1, PATH_DENSE = 0, PATH_FLAT = 1, PATH_HISA = 2 };
+
+// Plain-int copy of hisa_dims plus derived constants, passed to kernels by value.
+struct KDims {
+  int B, L, ratio, window, topk, index_block, index_keep;
+  int H_i, D_i, H, Dk, Dv, Np_cap, Wl_cap, kI;
+  int force_flat;  // HISA_MODE_FORCE_FLAT
+  int force_path;  // -1: run the gate; PATH_FLAT: flat for every valid sequence
+  int nb_cap;      // Np_cap / index_block (0 when index_block == 0)
+  float w_scale;   // (float)(1 / sqrt(H_i * D_i)), rounded once from double
+  float attn_scale_log2;  // (float)(log2(e) / sqrt(Dk))
+};
+
+// Launchers (kernel files).  Each returns hipSuccess or the launch error.
+// Pointers are device pointers; bf16 data is passed as uint16_t.
+hipError_t launch_decode_scan(const KDims& d, bool bf16, const void* q_idx, const float* w,
+                              const void* keys, const int* t0, float* fscore, float* cscore,
+                              hipStream_t st);
+hipError_t launch_decode_select(const KDims& d, const float* fscore, const float* cscore,
+                                const int* t0, int* I, int* top_blk, int* path, hipStream_t st);
+hipError_t launch_block_mean(const KDims& d, bool bf16, bool all_paths, const void* keys,
+                             const int* t0, float* rep, uint16_t* rep3, hipStream_t st);
+hipError_t launch_coarse(const KDims& d, bool bf16, bool all_paths, const void* q_idx,
+                         const float* w, const float* rep, const uint16_t* rep3, const int* t0,
+                         float* cscore, hipStream_t st);
+hipError_t launch_fine(const KDims& d, bool bf16, const void* q_idx, const float* w,
+                       const void* keys, const float* cscore, const int* t0, int* I,
+                       int* top_blk, int* path, hipStream_t st);
+hipError_t launch_flat_scores(const KDims& d, bool bf16, const void* q_idx, const float* w,
+                              const void* keys, const int* t0, float* scores, hipStream_t st);
+hipError_t launch_topk_rows(const KDims& d, const float* scores, const int* t0, int* I,
+                            int* path, hipStream_t st);
+
+// Attention.  splits > 1 writes partials to ws and merges them.
+int attn_splits(const KDims& d, bool bf16);
+bool attn_mfma_ok(const KDims& d, bool bf16);
+bool attn_generic_ok(const KDims& d);
+size_t attn_partial_bytes(const KDims& d, int splits);
+hipError_t launch_attention(const KDims& d, bool bf16, const void* q, const void* local_kv,
+                            const void* pooled_kv, const int* I, const float* sinks,
+                            const int* t0, void* out, float* partial, int splits,
+                            hipStream_t st);
+
+// Shapes with hand-tuned MFMA selection kernels.
+inline bool idx_mfma_ok(const KDims& d, bool bf16) { return bf16 && d.H_i == 64 && d.D_i == 128; }
+
+}  // namespace hisa

@@ -1,0 +1,726 @@
+// select_kernels.hip -- indexer scoring and top-k selection kernels for gfx950.
+//
+// Method (HiSA issue, lablup/mlxcel #549, sections "Flat selection", "HiSA decode
+// path", "HiSA batched path"; DSA issue, lablup/mlxcel #509, item 1):
+//   score(p) = sum_h relu(q[h] . key[p]) * w[h] * H_i^-1/2 * D_i^-1/2, in f32;
+//   flat: top-k over the visible rows; HiSA: top-Kb blocks by the score of the
+//   block mean, then the top-k rows inside those blocks.
+//
+// Kernels
+//   decode scan   one pass over the pooled keys of an L == 1 step: every 64-row
+//                 tile gets its rows' fine scores (MFMA) and its blocks' means
+//                 and coarse scores; the decode step's HBM traffic is this pass.
+//   decode select one workgroup per sequence: gate, coarse top-Kb, fine top-k.
+//   block mean / coarse / fine   the batched (L > 1) path: block means once,
+//                 coarse scores as a GEMM over (rows x heads) x blocks, then one
+//                 workgroup per query row for coarse top-Kb + fine scores + top-k.
+//   flat scores + topk rows      the flat scan for any L.
+// The MFMA kernels serve bf16 keys with 64 heads x 128 dims (the V4-Flash and
+// V3.2 indexer shapes); other shapes and f32 inputs take plain VALU kernels.
+#include "hisa_device.h"
+
+namespace hisa {
+
+namespace {
+
+constexpr int KP = 136;  // LDS row pitch (bf16) of 128-dim rows: 272 B, 4 banks of skew per row
+
+__device__ __forceinline__ bf16x8 lds8(const uint16_t* p) { return *(const bf16x8*)p; }
+__device__ __forceinline__ bf16x8 ldg8(const uint16_t* p) { return *(const bf16x8*)p; }
+
+// ------------------------------------------------------------------ decode scan
+
+// One 64-row tile of one sequence (bf16, H_i = 64, D_i = 128, index_block | 64).
+__global__ __launch_bounds__(256) void k_decode_scan_mfma(KDims d, const uint16_t* __restrict__ q_idx,
+                                                          const float* __restrict__ w,
+                                                          const uint16_t* __restrict__ keys,
+                                                          const int* __restrict__ t0,
+                                                          float* __restrict__ fscore,
+                                                          float* __restrict__ cscore) {
+  const int b = blockIdx.y;
+  const int row0 = blockIdx.x * 64;
+  const SeqInfo si = seq_info(d, t0[b]);
+  if (!si.ok || si.path == PATH_DENSE || row0 >= si.Np) return;
+  __shared__ __align__(16) uint16_t sk[64 * KP];
+  __shared__ __align__(16) uint16_t sq[64 * KP];
+  __shared__ float s_weff[64];
+  __shared__ float s_rep[128];
+  __shared__ float s_red[4];
+  const int tid = threadIdx.x;
+  const uint16_t* qb = q_idx + (size_t)b * d.L * 64 * 128;
+  const uint16_t* kb = keys + ((size_t)b * d.Np_cap + row0) * 128;
+  const int nrows = min(64, si.Np - row0);
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int ch = tid + it * 256;
+    const int r = ch >> 4, seg = (ch & 15) * 8;
+    const uint4 vq = *(const uint4*)(qb + r * 128 + seg);
+    uint4 vk = make_uint4(0, 0, 0, 0);
+    if (r < nrows) vk = *(const uint4*)(kb + (size_t)r * 128 + seg);
+    *(uint4*)(sq + r * KP + seg) = vq;
+    *(uint4*)(sk + r * KP + seg) = vk;
+  }
+  if (tid < 64) s_weff[tid] = w[(size_t)b * d.L * 64 + tid] * d.w_scale;
+  __syncthreads();
+
+  // Fine scores of the tile's rows: wave wv takes rows 16wv..16wv+15.
+  // A = q (rows = heads), B = keys^T (columns = rows); D[h][row].
+  const int lane = lane_id(), wv = wave_id(), g = lane >> 4, c = lane & 15;
+  f32x4 acc[4];
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const bf16x8 kf = lds8(sk + (wv * 16 + c) * KP + s * 32 + g * 8);
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) {
+      const bf16x8 qf = lds8(sq + (ht * 16 + c) * KP + s * 32 + g * 8);
+      acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf, kf, acc[ht], 0, 0, 0);
+    }
+  }
+  float v = 0.f;
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v += fmaxf(acc[ht][i], 0.f) * s_weff[ht * 16 + 4 * g + i];
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
+  if (g == 0 && wv * 16 + c < nrows) fscore[(size_t)b * d.Np_cap + row0 + wv * 16 + c] = v;
+
+  if (si.path != PATH_HISA) return;
+  // Block means and coarse scores of the blocks inside this tile.
+  const int bsz = d.index_block;
+  const int h = tid >> 2, part = tid & 3;
+  float qr[32];
+#pragma unroll
+  for (int e = 0; e < 32; ++e) qr[e] = bf2f(sq[h * KP + part * 32 + e]);
+  const float wh = s_weff[h];
+  for (int blk = 0; blk < 64 / bsz; ++blk) {
+    const int beta = row0 / bsz + blk;
+    if (beta >= si.nb) break;
+    if (tid < 128) {
+      float s = 0.f;
+      for (int r = 0; r < bsz; ++r) s += bf2f(sk[(blk * bsz + r) * KP + tid]);
+      s_rep[tid] = s / (float)bsz;
+    }
+    __syncthreads();
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) dot += qr[e] * s_rep[part * 32 + e];
+    dot += __shfl_xor(dot, 1, 64);
+    dot += __shfl_xor(dot, 2, 64);
+    float contrib = part == 0 ? fmaxf(dot, 0.f) * wh : 0.f;
+    contrib = wave_sum(contrib);
+    if (lane == 0) s_red[wv] = contrib;
+    __syncthreads();
+    if (tid == 0) cscore[(size_t)b * d.nb_cap + beta] = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+  }
+}
+
+// Any shape / dtype: 4 threads per row, VALU dot products.
+template <typename T>
+__global__ __launch_bounds__(256) void k_decode_scan_valu(KDims d, const T* __restrict__ q_idx,
+                                                          const float* __restrict__ w,
+                                                          const T* __restrict__ keys,
+                                                          const int* __restrict__ t0,
+                                                          float* __restrict__ fscore,
+                                                          float* __restrict__ cscore) {
+  const int b = blockIdx.y;
+  const int row0 = blockIdx.x * 64;
+  const SeqInfo si = seq_info(d, t0[b]);
+  if (!si.ok || si.path == PATH_DENSE || row0 >= si.Np) return;
+  __shared__ float s_rep[1024];
+  __shared__ float s_red[4];
+  const int tid = threadIdx.x, part = tid & 3, r = tid >> 2;
+  const T* qb = q_idx + (size_t)b * d.L * d.H_i * d.D_i;
+  const float* wb = w + (size_t)b * d.L * d.H_i;
+  const int p = row0 + r;
+  const bool live = p < si.Np;
+  const T* kp = keys + ((size_t)b * d.Np_cap + (live ? p : row0)) * d.D_i;
+  float tot = 0.f;
+  for (int h = 0; h < d.H_i; ++h) {
+    float dot = 0.f;
+    for (int e = part; e < d.D_i; e += 4) dot += ldf(qb + (size_t)h * d.D_i + e) * ldf(kp + e);
+    dot += __shfl_xor(dot, 1, 64);
+    dot += __shfl_xor(dot, 2, 64);
+    tot += fmaxf(dot, 0.f) * (wb[h] * d.w_scale);
+  }
+  if (live && part == 0) fscore[(size_t)b * d.Np_cap + p] = tot;
+  if (si.path != PATH_HISA) return;
+  const int bsz = d.index_block;
+  for (int blk = 0; blk < 64 / bsz; ++blk) {
+    const int beta = row0 / bsz + blk;
+    if (beta >= si.nb) break;
+    for (int e = tid; e < d.D_i; e += 256) {
+      float s = 0.f;
+      for (int rr = 0; rr < bsz; ++rr) s += ldf(keys + ((size_t)b * d.Np_cap + (size_t)beta * bsz + rr) * d.D_i + e);
+      s_rep[e] = s / (float)bsz;
+    }
+    __syncthreads();
+    float contrib = 0.f;
+    for (int h = tid; h < d.H_i; h += 256) {
+      float dot = 0.f;
+      for (int e = 0; e < d.D_i; ++e) dot += ldf(qb + (size_t)h * d.D_i + e) * s_rep[e];
+      contrib += fmaxf(dot, 0.f) * (wb[h] * d.w_scale);
+    }
+    contrib = wave_sum(contrib);
+    if (lane_id() == 0) s_red[wave_id()] = contrib;
+    __syncthreads();
+    if (tid == 0) cscore[(size_t)b * d.nb_cap + beta] = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+  }
+}
+
+// ------------------------------------------------------------------ decode select
+
+constexpr int kMaxKeep = 1024;
+
+__global__ __launch_bounds__(256) void k_decode_select(KDims d, const float* __restrict__ fscore,
+                                                       const float* __restrict__ cscore,
+                                                       const int* __restrict__ t0, int* __restrict__ I,
+                                                       int* __restrict__ top_blk, int* __restrict__ path) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const SeqInfo si = seq_info(d, t0[b]);
+  __shared__ TopkSmem sm;
+  __shared__ int s_blk[kMaxKeep];
+  int* Ib = I + (size_t)b * d.topk;
+  const bool dense = si.path == PATH_DENSE;
+  const int first_pad = (si.ok && !dense) ? si.k : 0;
+  for (int i = tid; i < d.topk; i += 256) {
+    if (dense && i < si.Np) Ib[i] = i;
+    else if (i >= first_pad) Ib[i] = -1;
+  }
+  if (top_blk)
+    for (int i = tid; i < d.index_keep; i += 256) top_blk[(size_t)b * d.index_keep + i] = -1;
+  if (path && tid == 0) path[b] = si.path;
+  if (!si.ok || dense) return;
+  const float* fs = fscore + (size_t)b * d.Np_cap;
+  if (si.path == PATH_FLAT) {
+    block_topk<256>(si.Np, si.k, [&](int i) { return score_key(fs[i]); },
+                    [&](int slot, int i) { Ib[slot] = i; }, sm);
+    return;
+  }
+  const float* cs = cscore + (size_t)b * d.nb_cap;
+  block_topk<256>(si.nb, si.Kb, [&](int i) { return score_key(cs[i]); },
+                  [&](int slot, int i) { s_blk[slot] = i; }, sm);
+  __syncthreads();
+  if (top_blk)
+    for (int i = tid; i < si.Kb; i += 256) top_blk[(size_t)b * d.index_keep + i] = s_blk[i];
+  const int bsz = d.index_block;
+  const int C = si.Kb * bsz;
+  block_topk<256>(C, si.k, [&](int c) { return score_key(fs[s_blk[c / bsz] * bsz + c % bsz]); },
+                  [&](int slot, int c) { Ib[slot] = s_blk[c / bsz] * bsz + c % bsz; }, sm);
+}
+
+// ------------------------------------------------------------------ batched path
+
+// Block means (f32) and their three-part bf16 split rep = hi + mid + lo, used by
+// the MFMA coarse kernel (each part times a bf16 query is exact in f32).
+template <typename T>
+__global__ __launch_bounds__(128) void k_block_mean(KDims d, int all_paths, const T* __restrict__ keys,
+                                                    const int* __restrict__ t0, float* __restrict__ rep,
+                                                    uint16_t* __restrict__ rep3) {
+  const int b = blockIdx.y, beta = blockIdx.x;
+  const SeqInfo si = seq_info(d, t0[b]);
+  if (!all_paths && si.path != PATH_HISA) return;
+  const bool live = si.ok && beta < si.nb;
+  const int bsz = d.index_block;
+  const size_t plane = (size_t)d.B * d.nb_cap * d.D_i;
+  for (int e = threadIdx.x; e < d.D_i; e += 128) {
+    float s = 0.f;
+    if (live) {
+      const T* kp = keys + ((size_t)b * d.Np_cap + (size_t)beta * bsz) * d.D_i + e;
+      for (int r = 0; r < bsz; ++r) s += ldf(kp + (size_t)r * d.D_i);
+      s = s / (float)bsz;
+    }
+    const size_t o = ((size_t)b * d.nb_cap + beta) * d.D_i + e;
+    rep[o] = s;
+    if (rep3) {
+      const uint16_t hi = f2bf(s);
+      const float r1 = s - bf2f(hi);
+      const uint16_t mid = f2bf(r1);
+      const uint16_t lo = f2bf(r1 - bf2f(mid));
+      rep3[o] = hi;
+      rep3[plane + o] = mid;
+      rep3[2 * plane + o] = lo;
+    }
+  }
+}
+
+// Coarse scores for 4 query rows per workgroup (one per wave), 16 blocks per
+// MFMA column tile, rep taken as hi + mid + lo bf16 parts.
+__global__ __launch_bounds__(256) void k_coarse_mfma(KDims d, int all_paths, const uint16_t* __restrict__ q_idx,
+                                                     const float* __restrict__ w,
+                                                     const uint16_t* __restrict__ rep3,
+                                                     const int* __restrict__ t0,
+                                                     float* __restrict__ cscore) {
+  const int b = blockIdx.y;
+  const int j = blockIdx.x * 4 + wave_id();
+  const SeqInfo si = seq_info(d, t0[b]);
+  if (!all_paths && si.path != PATH_HISA) return;
+  if (j >= d.L) return;
+  const int lane = lane_id(), g = lane >> 4, c = lane & 15;
+  float* out = cscore + ((size_t)b * d.L + j) * d.nb_cap;
+  if (!si.ok) {
+    for (int i = lane; i < d.nb_cap; i += 64) out[i] = kNeg;
+    return;
+  }
+  const int valid = visible(t0[b] + j, d.ratio, si.Np);
+  const uint16_t* qrow = q_idx + ((size_t)b * d.L + j) * 64 * 128;
+  bf16x8 qf[4][4];
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qf[ht][s] = ldg8(qrow + (ht * 16 + c) * 128 + s * 32 + g * 8);
+  float wl[4][4];
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wl[ht][i] = w[((size_t)b * d.L + j) * 64 + ht * 16 + 4 * g + i] * d.w_scale;
+  const size_t plane = (size_t)d.B * d.nb_cap * 128;
+  const int nt_live = (si.nb + 15) / 16;
+  for (int nt = 0; nt * 16 < d.nb_cap; ++nt) {
+    const int beta = nt * 16 + c;
+    float v = kNeg;
+    if (nt < nt_live) {
+      const int bl = min(beta, d.nb_cap - 1);
+      const uint16_t* rp = rep3 + ((size_t)b * d.nb_cap + bl) * 128 + g * 8;
+      f32x4 acc[4];
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int part = 0; part < 3; ++part)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8 bf = ldg8(rp + part * plane + s * 32);
+#pragma unroll
+          for (int ht = 0; ht < 4; ++ht)
+            acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ht][s], bf, acc[ht], 0, 0, 0);
+        }
+      float x = 0.f;
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x += fmaxf(acc[ht][i], 0.f) * wl[ht][i];
+      x += __shfl_xor(x, 16, 64);
+      x += __shfl_xor(x, 32, 64);
+      if (beta < si.nb && beta * d.index_block < valid) v = x;
+    }
+    if (g == 0 && beta < d.nb_cap) out[beta] = v;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_coarse_valu(KDims d, int all_paths, const T* __restrict__ q_idx,
+                                                     const float* __restrict__ w, const float* __restrict__ rep,
+                                                     const int* __restrict__ t0, float* __restrict__ cscore) {
+  const int b = blockIdx.y, j = blockIdx.x;
+  const SeqInfo si = seq_info(d, t0[b]);
+  if (!all_paths && si.path != PATH_HISA) return;
+  float* out = cscore + ((size_t)b * d.L + j) * d.nb_cap;
+  const int valid = si.ok ? visible(t0[b] + j, d.ratio, si.Np) : 0;
+  const T* qrow = q_idx + ((size_t)b * d.L + j) * d.H_i * d.D_i;
+  const float* wrow = w + ((size_t)b * d.L + j) * d.H_i;
+  for (int beta = threadIdx.x; beta < d.nb_cap; beta += 256) {
+    float v = kNeg;
+    if (si.ok && beta < si.nb && beta * d.index_block < valid) {
+      const float* rp = rep + ((size_t)b * d.nb_cap + beta) * d.D_i;
+      float tot = 0.f;
+      for (int h = 0; h < d.H_i; ++h) {
+        float dot = 0.f;
+        for (int e = 0; e < d.D_i; ++e) dot += ldf(qrow + (size_t)h * d.D_i + e) * rp[e];
+        tot += fmaxf(dot, 0.f) * (wrow[h] * d.w_scale);
+      }
+      v = tot;
+    }
+    out[beta] = v;
+  }
+}
+
+// Shared prologue of the fine kernels: writes the dense / invalid rows and the
+// padding; returns true when the row takes the HiSA path.
+__device__ __forceinline__ bool fine_prologue(const KDims& d, const SeqInfo& si, int b, int j, int* Irow,
+                                              int* blkrow, int* path) {
+  const bool dense = si.path == PATH_DENSE;
+  if (si.path == PATH_FLAT) {
+    if (blkrow)
+      for (int i = threadIdx.x; i < d.index_keep; i += blockDim.x) blkrow[i] = -1;
+    if (path && j == 0 && threadIdx.x == 0) path[b] = si.path;
+    return false;
+  }
+  const int first_pad = (si.ok && !dense) ? si.k : 0;
+  for (int i = threadIdx.x; i < d.topk; i += blockDim.x) {
+    if (dense && i < si.Np) Irow[i] = i;
+    else if (i >= first_pad) Irow[i] = -1;
+  }
+  if (blkrow)
+    for (int i = threadIdx.x; i < d.index_keep; i += blockDim.x) blkrow[i] = -1;
+  if (path && j == 0 && threadIdx.x == 0) path[b] = si.path;
+  return si.ok && si.path == PATH_HISA;
+}
+
+// One query row per workgroup: coarse top-Kb, fine scores of the C = Kb*b
+// candidates on MFMA (keys gathered straight from HBM/L2), fine top-k.
+__global__ __launch_bounds__(256) void k_fine_mfma(KDims d, const uint16_t* __restrict__ q_idx,
+                                                   const float* __restrict__ w, const uint16_t* __restrict__ keys,
+                                                   const float* __restrict__ cscore, const int* __restrict__ t0,
+                                                   int* __restrict__ I, int* __restrict__ top_blk,
+                                                   int* __restrict__ path) {
+  const int b = blockIdx.y, j = blockIdx.x;
+  const SeqInfo si = seq_info(d, t0[b]);
+  int* Irow = I + ((size_t)b * d.L + j) * d.topk;
+  int* blkrow = top_blk ? top_blk + ((size_t)b * d.L + j) * d.index_keep : nullptr;
+  if (!fine_prologue(d, si, b, j, Irow, blkrow, path)) return;
+  extern __shared__ float s_fs[];
+  __shared__ TopkSmem sm;
+  __shared__ int s_blk[kMaxKeep];
+  const int valid = visible(t0[b] + j, d.ratio, si.Np);
+  const float* cs = cscore + ((size_t)b * d.L + j) * d.nb_cap;
+  block_topk<256>(si.nb, si.Kb, [&](int i) { return score_key(cs[i]); },
+                  [&](int slot, int i) { s_blk[slot] = i; }, sm);
+  __syncthreads();
+  if (blkrow)
+    for (int i = threadIdx.x; i < si.Kb; i += 256) blkrow[i] = s_blk[i];
+
+  const int lane = lane_id(), wv = wave_id(), g = lane >> 4, c = lane & 15;
+  // q fragments with the contiguous-64-byte k order: lane group g holds dims
+  // [32g, 32g + 32); MFMA step s takes dims 32g + 8s .. 32g + 8s + 7.
+  const uint16_t* qrow = q_idx + ((size_t)b * d.L + j) * 64 * 128;
+  bf16x8 qf[4][4];
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qf[ht][s] = ldg8(qrow + (ht * 16 + c) * 128 + g * 32 + s * 8);
+  float wl[4][4];
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wl[ht][i] = w[((size_t)b * d.L + j) * 64 + ht * 16 + 4 * g + i] * d.w_scale;
+  const int bsz = d.index_block;
+  const int C = si.Kb * bsz;
+  const uint16_t* kb = keys + (size_t)b * d.Np_cap * 128;
+  for (int tile = wv; tile * 16 < C; tile += 4) {
+    const int cidx = tile * 16 + c;
+    const int cc = min(cidx, C - 1);
+    const int pos = s_blk[cc / bsz] * bsz + cc % bsz;
+    const uint16_t* kp = kb + (size_t)pos * 128 + g * 32;
+    bf16x8 kf[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) kf[s] = ldg8(kp + s * 8);
+    f32x4 acc[4];
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) {
+      acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ht][s], kf[s], acc[ht], 0, 0, 0);
+    }
+    float x = 0.f;
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x += fmaxf(acc[ht][i], 0.f) * wl[ht][i];
+    x += __shfl_xor(x, 16, 64);
+    x += __shfl_xor(x, 32, 64);
+    if (g == 0 && cidx < C) s_fs[cidx] = pos < valid ? x : kNeg;
+  }
+  __syncthreads();
+  block_topk<256>(C, si.k, [&](int cc) { return score_key(s_fs[cc]); },
+                  [&](int slot, int cc) { Irow[slot] = s_blk[cc / bsz] * bsz + cc % bsz; }, sm);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_fine_valu(KDims d, const T* __restrict__ q_idx, const float* __restrict__ w,
+                                                   const T* __restrict__ keys, const float* __restrict__ cscore,
+                                                   const int* __restrict__ t0, int* __restrict__ I,
+                                                   int* __restrict__ top_blk, int* __restrict__ path) {
+  const int b = blockIdx.y, j = blockIdx.x;
+  const SeqInfo si = seq_info(d, t0[b]);
+  int* Irow = I + ((size_t)b * d.L + j) * d.topk;
+  int* blkrow = top_blk ? top_blk + ((size_t)b * d.L + j) * d.index_keep : nullptr;
+  if (!fine_prologue(d, si, b, j, Irow, blkrow, path)) return;
+  extern __shared__ float s_fs[];
+  __shared__ TopkSmem sm;
+  __shared__ int s_blk[kMaxKeep];
+  const int valid = visible(t0[b] + j, d.ratio, si.Np);
+  const float* cs = cscore + ((size_t)b * d.L + j) * d.nb_cap;
+  block_topk<256>(si.nb, si.Kb, [&](int i) { return score_key(cs[i]); },
+                  [&](int slot, int i) { s_blk[slot] = i; }, sm);
+  __syncthreads();
+  if (blkrow)
+    for (int i = threadIdx.x; i < si.Kb; i += 256) blkrow[i] = s_blk[i];
+  const int bsz = d.index_block;
+  const int C = si.Kb * bsz;
+  const T* qrow = q_idx + ((size_t)b * d.L + j) * d.H_i * d.D_i;
+  const float* wrow = w + ((size_t)b * d.L + j) * d.H_i;
+  for (int cc = threadIdx.x; cc < C; cc += 256) {
+    const int pos = s_blk[cc / bsz] * bsz + cc % bsz;
+    const T* kp = keys + ((size_t)b * d.Np_cap + pos) * d.D_i;
+    float tot = 0.f;
+    for (int h = 0; h < d.H_i; ++h) {
+      float dot = 0.f;
+      for (int e = 0; e < d.D_i; ++e) dot += ldf(qrow + (size_t)h * d.D_i + e) * ldf(kp + e);
+      tot += fmaxf(dot, 0.f) * (wrow[h] * d.w_scale);
+    }
+    s_fs[cc] = pos < valid ? tot : kNeg;
+  }
+  __syncthreads();
+  block_topk<256>(C, si.k, [&](int cc) { return score_key(s_fs[cc]); },
+                  [&](int slot, int cc) { Irow[slot] = s_blk[cc / bsz] * bsz + cc % bsz; }, sm);
+}
+
+// ------------------------------------------------------------------ flat scan
+
+__device__ __forceinline__ bool flat_active(const KDims& d, const SeqInfo& si) {
+  return si.ok && (d.force_path == PATH_FLAT || si.path == PATH_FLAT);
+}
+
+// Scores of 8 query rows (2 per wave) against a chunk of kc keys, streamed
+// through LDS in 64-row tiles.  Masked entries (p >= V) are written as -1e30.
+__global__ __launch_bounds__(256) void k_flat_scores_mfma(KDims d, int kc, const uint16_t* __restrict__ q_idx,
+                                                          const float* __restrict__ w,
+                                                          const uint16_t* __restrict__ keys,
+                                                          const int* __restrict__ t0,
+                                                          float* __restrict__ scores) {
+  const int b = blockIdx.z;
+  const SeqInfo si = seq_info(d, t0[b]);
+  if (!flat_active(d, si)) return;
+  const int p_begin = blockIdx.x * kc;
+  if (p_begin >= si.Np) return;
+  const int p_end = min(si.Np, p_begin + kc);
+  const int j0 = blockIdx.y * 8;
+  const int lane = lane_id(), wv = wave_id(), g = lane >> 4, c = lane & 15, tid = threadIdx.x;
+  const int jlast = min(d.L - 1, j0 + 7);
+  const int Vmax = visible(t0[b] + jlast, d.ratio, si.Np);
+  int jr[2], Vr[2];
+  bool live[2];
+  bf16x8 qf[2][4][4];
+  float wl[2][4][4];
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    jr[rr] = j0 + wv * 2 + rr;
+    live[rr] = jr[rr] < d.L;
+    const int jj = live[rr] ? jr[rr] : 0;
+    Vr[rr] = live[rr] ? visible(t0[b] + jj, d.ratio, si.Np) : 0;
+    const uint16_t* qrow = q_idx + ((size_t)b * d.L + jj) * 64 * 128;
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) qf[rr][ht][s] = ldg8(qrow + (ht * 16 + c) * 128 + s * 32 + g * 8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wl[rr][ht][i] = w[((size_t)b * d.L + jj) * 64 + ht * 16 + 4 * g + i] * d.w_scale;
+    }
+  }
+  __shared__ __align__(16) uint16_t sk[64 * KP];
+  const uint16_t* kb = keys + (size_t)b * d.Np_cap * 128;
+  for (int p0 = p_begin; p0 < p_end; p0 += 64) {
+    const bool compute = p0 < Vmax;
+    __syncthreads();
+    if (compute) {
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int ch = tid + it * 256;
+        const int r = ch >> 4, seg = (ch & 15) * 8;
+        uint4 vk = make_uint4(0, 0, 0, 0);
+        if (p0 + r < p_end) vk = *(const uint4*)(kb + (size_t)(p0 + r) * 128 + seg);
+        *(uint4*)(sk + r * KP + seg) = vk;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      if (!live[rr]) continue;
+      float* srow = scores + ((size_t)b * d.L + jr[rr]) * d.Np_cap;
+      for (int sub = 0; sub < 4; ++sub) {
+        const int p = p0 + sub * 16 + c;
+        float x = kNeg;
+        if (p0 + sub * 16 < Vr[rr]) {
+          f32x4 acc[4];
+#pragma unroll
+          for (int ht = 0; ht < 4; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const bf16x8 kf = lds8(sk + (sub * 16 + c) * KP + s * 32 + g * 8);
+#pragma unroll
+            for (int ht = 0; ht < 4; ++ht)
+              acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[rr][ht][s], kf, acc[ht], 0, 0, 0);
+          }
+          float v = 0.f;
+#pragma unroll
+          for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v += fmaxf(acc[ht][i], 0.f) * wl[rr][ht][i];
+          v += __shfl_xor(v, 16, 64);
+          v += __shfl_xor(v, 32, 64);
+          if (p < Vr[rr]) x = v;
+        }
+        if (g == 0 && p < p_end) srow[p] = x;
+      }
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_flat_scores_valu(KDims d, const T* __restrict__ q_idx,
+                                                          const float* __restrict__ w, const T* __restrict__ keys,
+                                                          const int* __restrict__ t0, float* __restrict__ scores) {
+  const int b = blockIdx.z, j = blockIdx.y;
+  const SeqInfo si = seq_info(d, t0[b]);
+  if (!flat_active(d, si)) return;
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  if (p >= si.Np) return;
+  const int valid = visible(t0[b] + j, d.ratio, si.Np);
+  float v = kNeg;
+  if (p < valid) {
+    const T* qrow = q_idx + ((size_t)b * d.L + j) * d.H_i * d.D_i;
+    const float* wrow = w + ((size_t)b * d.L + j) * d.H_i;
+    const T* kp = keys + ((size_t)b * d.Np_cap + p) * d.D_i;
+    float tot = 0.f;
+    for (int h = 0; h < d.H_i; ++h) {
+      float dot = 0.f;
+      for (int e = 0; e < d.D_i; ++e) dot += ldf(qrow + (size_t)h * d.D_i + e) * ldf(kp + e);
+      tot += fmaxf(dot, 0.f) * (wrow[h] * d.w_scale);
+    }
+    v = tot;
+  }
+  scores[((size_t)b * d.L + j) * d.Np_cap + p] = v;
+}
+
+constexpr int kTopkRowsThreads = 512;
+
+// Flat top-k of one query row; the row's scores are staged in LDS when they fit.
+__global__ __launch_bounds__(kTopkRowsThreads) void k_topk_rows(KDims d, int lds_cap, const float* __restrict__ scores,
+                                                                const int* __restrict__ t0, int* __restrict__ I,
+                                                                int* __restrict__ path) {
+  const int b = blockIdx.y, j = blockIdx.x;
+  const SeqInfo si = seq_info(d, t0[b]);
+  int* Irow = I + ((size_t)b * d.L + j) * d.topk;
+  const bool act = flat_active(d, si);
+  if (d.force_path == PATH_FLAT) {
+    // flat_topk_select: this kernel owns the whole output row.
+    const int first_pad = act ? si.k : 0;
+    for (int i = threadIdx.x; i < d.topk; i += kTopkRowsThreads)
+      if (i >= first_pad) Irow[i] = -1;
+    if (path && j == 0 && threadIdx.x == 0) path[b] = si.ok ? PATH_FLAT : PATH_INVALID;
+  } else if (act) {
+    for (int i = threadIdx.x; i < d.topk; i += kTopkRowsThreads)
+      if (i >= si.k) Irow[i] = -1;
+  }
+  if (!act) return;
+  extern __shared__ uint32_t s_keys[];
+  __shared__ TopkSmem sm;
+  const float* srow = scores + ((size_t)b * d.L + j) * d.Np_cap;
+  if (si.Np <= lds_cap) {
+    for (int i = threadIdx.x; i < si.Np; i += kTopkRowsThreads) s_keys[i] = score_key(srow[i]);
+    __syncthreads();
+    block_topk<kTopkRowsThreads>(si.Np, si.k, [&](int i) { return s_keys[i]; },
+                                 [&](int slot, int i) { Irow[slot] = i; }, sm);
+  } else {
+    block_topk<kTopkRowsThreads>(si.Np, si.k, [&](int i) { return score_key(srow[i]); },
+                                 [&](int slot, int i) { Irow[slot] = i; }, sm);
+  }
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ launchers
+
+static inline unsigned cdiv(long long a, long long b) { return (unsigned)((a + b - 1) / b); }
+
+hipError_t launch_decode_scan(const KDims& d, bool bf16, const void* q_idx, const float* w, const void* keys,
+                              const int* t0, float* fscore, float* cscore, hipStream_t st) {
+  const dim3 grid(cdiv(d.Np_cap, 64), d.B);
+  if (idx_mfma_ok(d, bf16))
+    hipLaunchKernelGGL(k_decode_scan_mfma, grid, dim3(256), 0, st, d, (const uint16_t*)q_idx, w,
+                       (const uint16_t*)keys, t0, fscore, cscore);
+  else if (bf16)
+    hipLaunchKernelGGL(k_decode_scan_valu<uint16_t>, grid, dim3(256), 0, st, d, (const uint16_t*)q_idx, w,
+                       (const uint16_t*)keys, t0, fscore, cscore);
+  else
+    hipLaunchKernelGGL(k_decode_scan_valu<float>, grid, dim3(256), 0, st, d, (const float*)q_idx, w,
+                       (const float*)keys, t0, fscore, cscore);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_select(const KDims& d, const float* fscore, const float* cscore, const int* t0, int* I,
+                                int* top_blk, int* path, hipStream_t st) {
+  hipLaunchKernelGGL(k_decode_select, dim3(d.B), dim3(256), 0, st, d, fscore, cscore, t0, I, top_blk, path);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_mean(const KDims& d, bool bf16, bool all_paths, const void* keys, const int* t0,
+                             float* rep, uint16_t* rep3, hipStream_t st) {
+  if (d.nb_cap == 0) return hipSuccess;
+  const dim3 grid(d.nb_cap, d.B);
+  if (bf16)
+    hipLaunchKernelGGL(k_block_mean<uint16_t>, grid, dim3(128), 0, st, d, (int)all_paths, (const uint16_t*)keys, t0,
+                       rep, rep3);
+  else
+    hipLaunchKernelGGL(k_block_mean<float>, grid, dim3(128), 0, st, d, (int)all_paths, (const float*)keys, t0, rep,
+                       rep3);
+  return hipGetLastError();
+}
+
+hipError_t launch_coarse(const KDims& d, bool bf16, bool all_paths, const void* q_idx, const float* w,
+                         const float* rep, const uint16_t* rep3, const int* t0, float* cscore, hipStream_t st) {
+  if (d.nb_cap == 0) return hipSuccess;
+  if (idx_mfma_ok(d, bf16))
+    hipLaunchKernelGGL(k_coarse_mfma, dim3(cdiv(d.L, 4), d.B), dim3(256), 0, st, d, (int)all_paths,
+                       (const uint16_t*)q_idx, w, rep3, t0, cscore);
+  else if (bf16)
+    hipLaunchKernelGGL(k_coarse_valu<uint16_t>, dim3(d.L, d.B), dim3(256), 0, st, d, (int)all_paths,
+                       (const uint16_t*)q_idx, w, rep, t0, cscore);
+  else
+    hipLaunchKernelGGL(k_coarse_valu<float>, dim3(d.L, d.B), dim3(256), 0, st, d, (int)all_paths,
+                       (const float*)q_idx, w, rep, t0, cscore);
+  return hipGetLastError();
+}
+
+hipError_t launch_fine(const KDims& d, bool bf16, const void* q_idx, const float* w, const void* keys,
+                       const float* cscore, const int* t0, int* I, int* top_blk, int* path, hipStream_t st) {
+  const size_t lds = (size_t)d.index_keep * d.index_block * sizeof(float);
+  const dim3 grid(d.L, d.B);
+  if (idx_mfma_ok(d, bf16))
+    hipLaunchKernelGGL(k_fine_mfma, grid, dim3(256), lds, st, d, (const uint16_t*)q_idx, w, (const uint16_t*)keys,
+                       cscore, t0, I, top_blk, path);
+  else if (bf16)
+    hipLaunchKernelGGL(k_fine_valu<uint16_t>, grid, dim3(256), lds, st, d, (const uint16_t*)q_idx, w,
+                       (const uint16_t*)keys, cscore, t0, I, top_blk, path);
+  else
+    hipLaunchKernelGGL(k_fine_valu<float>, grid, dim3(256), lds, st, d, (const float*)q_idx, w, (const float*)keys,
+                       cscore, t0, I, top_blk, path);
+  return hipGetLastError();
+}
+
+hipError_t launch_flat_scores(const KDims& d, bool bf16, const void* q_idx, const float* w, const void* keys,
+                              const int* t0, float* scores, hipStream_t st) {
+  if (idx_mfma_ok(d, bf16)) {
+    // Few query rows: short key chunks spread the scan over the whole chip;
+    // many rows: long chunks keep the queries in registers across more keys.
+    const int kc = d.L <= 8 ? 64 : 2048;
+    hipLaunchKernelGGL(k_flat_scores_mfma, dim3(cdiv(d.Np_cap, kc), cdiv(d.L, 8), d.B), dim3(256), 0, st, d, kc,
+                       (const uint16_t*)q_idx, w, (const uint16_t*)keys, t0, scores);
+  } else if (bf16) {
+    hipLaunchKernelGGL(k_flat_scores_valu<uint16_t>, dim3(cdiv(d.Np_cap, 256), d.L, d.B), dim3(256), 0, st, d,
+                       (const uint16_t*)q_idx, w, (const uint16_t*)keys, t0, scores);
+  } else {
+    hipLaunchKernelGGL(k_flat_scores_valu<float>, dim3(cdiv(d.Np_cap, 256), d.L, d.B), dim3(256), 0, st, d,
+                       (const float*)q_idx, w, (const float*)keys, t0, scores);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_rows(const KDims& d, const float* scores, const int* t0, int* I, int* path, hipStream_t st) {
+  constexpr int kLdsCap = 32768;  // 128 KiB of keys
+  const int cap = d.Np_cap <= kLdsCap ? d.Np_cap : 0;
+  const size_t lds = (size_t)cap * sizeof(uint32_t);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_topk_rows, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       kLdsCap * (int)sizeof(uint32_t));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(k_topk_rows, dim3(d.L, d.B), dim3(kTopkRowsThreads), lds, st, d, cap, scores, t0, I, path);
+  return hipGetLastError();
+}
+
+}  // namespace hisa

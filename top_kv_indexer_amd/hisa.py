@@ -1,0 +1,218 @@
+"""Python binding of libhisa.so (ctypes).  Argument marshalling only: shapes are
+read off the torch tensors, outputs and the workspace are allocated with torch
+on the tensors' device, and every computation runs in the HIP kernels on the
+current torch stream.  The names follow the C ABI in include/hisa.h.
+"""
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhisa.so")
+
+F32, BF16 = 0, 1
+MODE_AUTO, MODE_FORCE_FLAT = 0, 1
+PATH_INVALID, PATH_DENSE, PATH_FLAT, PATH_HISA = -1, 0, 1, 2
+OP_BLOCK_SCORES, OP_SELECT_DECODE, OP_SELECT_PREFILL, OP_FLAT_TOPK, OP_ATTENTION = range(5)
+
+EXPORTS = ("hisa_block_scores", "hisa_select_decode", "hisa_select_prefill", "flat_topk_select",
+           "sparse_local_pooled_attention", "hisa_workspace_bytes", "hisa_last_error", "hisa_abi_version")
+
+
+class HisaError(RuntimeError):
+    pass
+
+
+class hisa_dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "B", "L", "ratio", "window", "topk", "index_block", "index_keep", "H_i", "D_i", "H", "Dk", "Dv",
+        "Np_cap", "Wl_cap", "kI", "mode", "idx_dtype", "attn_dtype")]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library; raises when it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise HisaError(f"{LIB_PATH} is missing: build it with top_kv_indexer_amd.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+        dp = ctypes.POINTER(hisa_dims)
+        sel = [dp, vp, vp, vp, vp]
+        L.hisa_block_scores.argtypes = sel + [vp, vp, vp, sz, vp]
+        L.hisa_select_decode.argtypes = sel + [vp, vp, vp, vp, sz, vp]
+        L.hisa_select_prefill.argtypes = sel + [vp, vp, vp, vp, sz, vp]
+        L.flat_topk_select.argtypes = sel + [vp, vp, sz, vp]
+        L.sparse_local_pooled_attention.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        for f in ("hisa_block_scores", "hisa_select_decode", "hisa_select_prefill", "flat_topk_select",
+                  "sparse_local_pooled_attention"):
+            getattr(L, f).restype = i32
+        L.hisa_workspace_bytes.argtypes = [i32, dp]
+        L.hisa_workspace_bytes.restype = sz
+        L.hisa_last_error.restype = ctypes.c_char_p
+        L.hisa_abi_version.restype = i32
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().hisa_last_error().decode()
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise HisaError(f"libhisa error {rc}: {last_error()}")
+
+
+def _code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise HisaError(f"unsupported dtype {t.dtype}")
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, ndim: int, dtype=None) -> torch.Tensor:
+    if t.dim() != ndim:
+        raise HisaError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise HisaError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise HisaError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _stream(dev: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def workspace_bytes(op: int, d: hisa_dims) -> int:
+    n = lib().hisa_workspace_bytes(op, ctypes.byref(d))
+    if n == ctypes.c_size_t(-1).value:
+        raise HisaError(last_error())
+    return int(n)
+
+
+def _workspace(op: int, d: hisa_dims, dev: torch.device, ws: Optional[torch.Tensor]):
+    n = workspace_bytes(op, d)
+    if ws is not None:
+        if ws.numel() * ws.element_size() < n:
+            raise HisaError(f"workspace of {ws.numel() * ws.element_size()} bytes < {n} needed")
+        return ws, ws.numel() * ws.element_size()
+    if n == 0:
+        return None, 0
+    return torch.empty(n, dtype=torch.uint8, device=dev), n
+
+
+def selection_dims(q_idx, keys, *, ratio, topk, index_block, index_keep, mode=MODE_AUTO) -> hisa_dims:
+    B, L, H_i, D_i = q_idx.shape
+    return hisa_dims(B=B, L=L, ratio=ratio, window=0, topk=topk, index_block=index_block, index_keep=index_keep,
+                     H_i=H_i, D_i=D_i, H=1, Dk=1, Dv=1, Np_cap=keys.shape[1], Wl_cap=0, kI=0, mode=mode,
+                     idx_dtype=_code(keys), attn_dtype=F32)
+
+
+def _sel_args(q_idx, w, keys, t0):
+    _need(q_idx, "q_idx", 4)
+    _need(w, "w", 3, torch.float32)
+    _need(keys, "keys", 3, q_idx.dtype)
+    _need(t0, "t0", 1, torch.int32)
+    B, L, H_i, D_i = q_idx.shape
+    if tuple(w.shape) != (B, L, H_i) or keys.shape[0] != B or keys.shape[2] != D_i or t0.shape[0] != B:
+        raise HisaError("inconsistent selection shapes")
+    return B, L
+
+
+def hisa_block_scores(q_idx, w, keys, t0, *, ratio, index_block, want_rep=False, ws=None):
+    """Coarse stage: returns cscore (B, L, nb_cap) and rep (B, nb_cap, D_i) or None."""
+    B, L = _sel_args(q_idx, w, keys, t0)
+    d = selection_dims(q_idx, keys, ratio=ratio, topk=1, index_block=index_block, index_keep=1)
+    dev = keys.device
+    nb_cap = keys.shape[1] // max(index_block, 1)
+    cs = torch.empty((B, L, nb_cap), dtype=torch.float32, device=dev)
+    rep = torch.empty((B, nb_cap, q_idx.shape[3]), dtype=torch.float32, device=dev) if want_rep else None
+    wsb, n = _workspace(OP_BLOCK_SCORES, d, dev, ws)
+    _check(lib().hisa_block_scores(ctypes.byref(d), _p(q_idx), _p(w), _p(keys), _p(t0), _p(cs), _p(rep), _p(wsb), n,
+                                   _stream(dev)))
+    return cs, rep
+
+
+def _select(fn, op, q_idx, w, keys, t0, ratio, topk, index_block, index_keep, mode, I, top_blk, path, ws):
+    B, L = _sel_args(q_idx, w, keys, t0)
+    d = selection_dims(q_idx, keys, ratio=ratio, topk=topk, index_block=index_block, index_keep=index_keep,
+                       mode=mode)
+    dev = keys.device
+    if I is None:
+        I = torch.empty((B, L, topk), dtype=torch.int32, device=dev)
+    if top_blk is None:
+        top_blk = torch.empty((B, L, index_keep), dtype=torch.int32, device=dev)
+    if path is None:
+        path = torch.empty((B,), dtype=torch.int32, device=dev)
+    wsb, n = _workspace(op, d, dev, ws)
+    _check(fn(ctypes.byref(d), _p(q_idx), _p(w), _p(keys), _p(t0), _p(I), _p(top_blk), _p(path), _p(wsb), n,
+              _stream(dev)))
+    return I, top_blk, path
+
+
+def hisa_select_decode(q_idx, w, keys, t0, *, ratio, topk, index_block=64, index_keep=16, mode=MODE_AUTO,
+                       I=None, top_blk=None, path=None, ws=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Single-token selection; returns I (B,1,topk), top_blk (B,1,index_keep), path (B)."""
+    return _select(lib().hisa_select_decode, OP_SELECT_DECODE, q_idx, w, keys, t0, ratio, topk, index_block,
+                   index_keep, mode, I, top_blk, path, ws)
+
+
+def hisa_select_prefill(q_idx, w, keys, t0, *, ratio, topk, index_block=64, index_keep=16, mode=MODE_AUTO,
+                        I=None, top_blk=None, path=None, ws=None):
+    """Multi-row selection; returns I (B,L,topk), top_blk (B,L,index_keep), path (B)."""
+    return _select(lib().hisa_select_prefill, OP_SELECT_PREFILL, q_idx, w, keys, t0, ratio, topk, index_block,
+                   index_keep, mode, I, top_blk, path, ws)
+
+
+def flat_topk_select(q_idx, w, keys, t0, *, ratio, topk, I=None, ws=None) -> torch.Tensor:
+    """Flat top-k indexer; returns I (B, L, topk)."""
+    B, L = _sel_args(q_idx, w, keys, t0)
+    d = selection_dims(q_idx, keys, ratio=ratio, topk=topk, index_block=0, index_keep=1)
+    dev = keys.device
+    if I is None:
+        I = torch.empty((B, L, topk), dtype=torch.int32, device=dev)
+    wsb, n = _workspace(OP_FLAT_TOPK, d, dev, ws)
+    _check(lib().flat_topk_select(ctypes.byref(d), _p(q_idx), _p(w), _p(keys), _p(t0), _p(I), _p(wsb), n,
+                                  _stream(dev)))
+    return I
+
+
+def attention_dims(q, local_kv, pooled_kv, I, *, ratio, window, Dv=None) -> hisa_dims:
+    B, L, H, Dk = q.shape
+    return hisa_dims(B=B, L=L, ratio=ratio, window=window, topk=1, index_block=0, index_keep=1, H_i=1, D_i=1,
+                     H=H, Dk=Dk, Dv=Dk if Dv is None else Dv, Np_cap=pooled_kv.shape[1],
+                     Wl_cap=0 if local_kv is None else local_kv.shape[1], kI=I.shape[2], mode=MODE_AUTO,
+                     idx_dtype=F32, attn_dtype=_code(q))
+
+
+def sparse_local_pooled_attention(q, local_kv, pooled_kv, I, sinks, t0, *, ratio, window, Dv=None, out=None,
+                                  ws=None) -> torch.Tensor:
+    """Sparse local + pooled combine; returns out (B, L, H, Dv)."""
+    _need(q, "q", 4)
+    _need(pooled_kv, "pooled_kv", 3, q.dtype)
+    if local_kv is not None:
+        _need(local_kv, "local_kv", 3, q.dtype)
+    _need(I, "I", 3, torch.int32)
+    _need(t0, "t0", 1, torch.int32)
+    if sinks is not None:
+        _need(sinks, "sinks", 1, torch.float32)
+    d = attention_dims(q, local_kv, pooled_kv, I, ratio=ratio, window=window, Dv=Dv)
+    dev = q.device
+    if out is None:
+        out = torch.empty((d.B, d.L, d.H, d.Dv), dtype=q.dtype, device=dev)
+    wsb, n = _workspace(OP_ATTENTION, d, dev, ws)
+    _check(lib().sparse_local_pooled_attention(ctypes.byref(d), _p(q), _p(local_kv), _p(pooled_kv), _p(I), _p(sinks),
+                                               _p(t0), _p(out), _p(wsb), n, _stream(dev)))
+    return out

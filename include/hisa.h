@@ -177,6 +177,22 @@ const char* hisa_last_error(void);
 /* HISA_ABI_VERSION of the loaded library. */
 int hisa_abi_version(void);
 
+/* Kernel timing, a tracing aid (off by default).  While enabled, each kernel
+ * the library launches is bracketed by two hipEvents recorded on the call's
+ * stream.  hisa_profile_collect() waits for the recorded events, adds their
+ * elapsed times to per-kernel totals, copies up to max_entries totals to out
+ * and returns how many kernels have totals (or a negative HISA_ERR_*).
+ * hisa_profile_enable(0) stops recording and clears the totals.  Not
+ * thread-safe; do not enable it while a HIP graph is being captured. */
+typedef struct {
+  char name[48];      /* kernel family, e.g. "decode_scan" */
+  int64_t launches;   /* launches timed since the totals were cleared */
+  double total_ms;    /* sum of their event-to-event durations */
+} hisa_kernel_time;
+
+int hisa_profile_enable(int on);
+int hisa_profile_collect(hisa_kernel_time* out, int max_entries);
+
 #ifdef __cplusplus
 }
 #endif

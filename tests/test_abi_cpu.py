@@ -48,8 +48,8 @@ def test_workspace_sizes(lib):
     # decode: f32 scores of every pooled row + one coarse score per block
     assert hisa.workspace_bytes(hisa.OP_SELECT_DECODE, d) == 16384 * 4 + 256 * 4
     assert hisa.workspace_bytes(hisa.OP_FLAT_TOPK, dims(L=4, Np_cap=1000)) == ((4 * 1000 * 4 + 255) // 256) * 256
-    # single-row attention splits the 640 rows into 20 parts of 32
-    assert hisa.workspace_bytes(hisa.OP_ATTENTION, d) == 20 * 64 * 514 * 4
+    # single-row attention splits the 640 rows into 10 parts of 64
+    assert hisa.workspace_bytes(hisa.OP_ATTENTION, d) == 10 * 64 * 514 * 4
     # many rows: no split, no workspace
     assert hisa.workspace_bytes(hisa.OP_ATTENTION, dims(L=2048, Wl_cap=2175)) == 0
     n = hisa.workspace_bytes(hisa.OP_SELECT_PREFILL, dims(L=2048))

@@ -26,6 +26,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kTile = 32;
+constexpr int kChunk = 512;  // row addresses staged in LDS at a time
 
 struct RowPlan {
   bool ok;
@@ -64,9 +65,10 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(KDims d, int splits, cons
   constexpr int NT = NW * 64;
   constexpr int NS = DK / 32;   // MFMA k-steps of S
   constexpr int NO = DV / 16;   // MFMA column tiles of O^T
+  constexpr int CPR = DK / 8;                       // 16-byte chunks per KV row
+  constexpr int CPT = (kTile * CPR + NT - 1) / NT;  // chunks per thread per tile
   __shared__ __align__(16) uint16_t kv[kTile * KPD];
-  __shared__ long long s_off[kTile];
-  __shared__ int s_src[kTile];
+  __shared__ const uint16_t* s_ptr[kChunk];
 
   const int split = blockIdx.x, row = blockIdx.y;
   const int b = row / d.L, j = row % d.L;
@@ -88,37 +90,47 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(KDims d, int splits, cons
   for (int n = 0; n < NO; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int* Irow = I + (size_t)row * d.kI;
-  for (int tb = begin; tb < end; tb += kTile) {
+  for (int cb = begin; cb < end; cb += kChunk) {
+    const int ce = min(end, cb + kChunk);
+    // Row addresses of this chunk of the row list (local window, then I).
     __syncthreads();
-    if (tid < kTile) {
-      const int e = tb + tid;
-      int src = 0;
-      long long off = 0;
-      if (e < end) {
-        if (e < rp.n_loc) {
-          src = 1;
-          off = ((long long)b * d.Wl_cap + (rp.s_lo - rp.ls + e)) * DK;
-        } else {
-          const int id = Irow[e - rp.n_loc];
-          if (id >= 0 && id < rp.V) {
-            src = 2;
-            off = ((long long)b * d.Np_cap + id) * DK;
-          }
-        }
+    for (int e = cb + tid; e < ce; e += NT) {
+      const uint16_t* p = nullptr;
+      if (e < rp.n_loc) {
+        p = local_kv + ((long long)b * d.Wl_cap + (rp.s_lo - rp.ls + e)) * DK;
+      } else {
+        const int id = Irow[e - rp.n_loc];
+        if (id >= 0 && id < rp.V) p = pooled_kv + ((long long)b * d.Np_cap + id) * DK;
       }
-      s_src[tid] = src;
-      s_off[tid] = off;
+      s_ptr[e - cb] = p;
     }
     __syncthreads();
-    for (int ch = tid; ch < kTile * (DK / 8); ch += NT) {
-      const int r = ch / (DK / 8), seg = (ch % (DK / 8)) * 8;
-      const int src = s_src[r];
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (src == 1) v = *(const uint4*)(local_kv + s_off[r] + seg);
-      else if (src == 2) v = *(const uint4*)(pooled_kv + s_off[r] + seg);
-      *(uint4*)(kv + r * KPD + seg) = v;
-    }
-    __syncthreads();
+    // Tiles of 32 rows; the next tile's rows are fetched into registers while
+    // the current one is computed from LDS.
+    uint4 reg[CPT];
+    auto fetch = [&](int tb) {
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int ch = tid + i * NT;
+        const int r = ch / CPR, seg = (ch % CPR) * 8;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (ch < kTile * CPR && tb + r < ce) {
+          const uint16_t* p = s_ptr[tb - cb + r];
+          if (p) v = *(const uint4*)(p + seg);
+        }
+        reg[i] = v;
+      }
+    };
+    fetch(cb);
+    for (int tb = cb; tb < ce; tb += kTile) {
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int ch = tid + i * NT;
+        if (ch < kTile * CPR) *(uint4*)(kv + (ch / CPR) * KPD + (ch % CPR) * 8) = reg[i];
+      }
+      __syncthreads();
+      if (tb + kTile < ce) fetch(tb + kTile);
 
     // S^T[row][head] for the tile's 32 rows and the wave's 16 heads.
     f32x4 st[2];
@@ -139,43 +151,55 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(KDims d, int splits, cons
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = mt * 16 + 4 * g + i;
-        const float v = s_src[r] ? st[mt][i] * d.attn_scale_log2 : -INFINITY;
+        const bool live = tb + r < ce && s_ptr[tb - cb + r] != nullptr;
+        const float v = live ? st[mt][i] * d.attn_scale_log2 : -INFINITY;
         x[mt * 4 + i] = v;
         tmax = fmaxf(tmax, v);
       }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m, tmax);
+    // Lazy rescaling: the reference max m moves (and O, l are rescaled) only
+    // when a head's scores exceed it by more than 2^8, so exp2(x - m) stays
+    // <= 256 and the 128-register rescale of O is rare.
+    if (m == -INFINITY) {
+      m = tmax;
+    } else if (__ballot(tmax > m + 8.f)) {
+      const float m_new = fmaxf(m, tmax);
+      const float alpha = exp2f(m - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int n = 0; n < NO; ++n) {
+        acc[n][0] *= alpha;
+        acc[n][1] *= alpha;
+        acc[n][2] *= alpha;
+        acc[n][3] *= alpha;
+      }
+      m = m_new;
+    }
     float p[8];
     float psum = 0.f;
-    float alpha = 1.f;
-    if (m_new == -INFINITY) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = 0.f;
-    } else {
-      alpha = exp2f(m - m_new);
+    if (m != -INFINITY) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        p[i] = exp2f(x[i] - m_new);
+        p[i] = exp2f(x[i] - m);
         psum += p[i];
       }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p[i] = 0.f;
     }
     psum += __shfl_xor(psum, 16, 64);
     psum += __shfl_xor(psum, 32, 64);
-    l = l * alpha + psum;
-    m = m_new;
+    l += psum;
     const bf16x8 pf = pack8(p);
 #pragma unroll
     for (int n = 0; n < NO; ++n) {
-      acc[n][0] *= alpha;
-      acc[n][1] *= alpha;
-      acc[n][2] *= alpha;
-      acc[n][3] *= alpha;
       const uint16_t* base = kv + (4 * g + (c >> 2)) * KPD + n * 16 + 4 * (c & 3);
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base));
       const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 16 * KPD));
       const i16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), pf, acc[n], 0, 0, 0);
+    }
     }
   }
 
@@ -207,29 +231,41 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(KDims d, int splits, cons
   }
 }
 
-// Merge of split partials (m and l in the log2 domain), sink included.
+// Merge of split partials (m and l in the log2 domain), sink included.  One
+// workgroup per (query row, head, 128 output columns); the first wave turns
+// the splits' (m, l) into normalised weights, then every thread sums its
+// column over the splits.
+constexpr int kMaxSplits = 64;
+
 template <typename T>
 __global__ __launch_bounds__(128) void k_attn_merge(KDims d, int splits, const float* __restrict__ part,
                                                     const float* __restrict__ sinks, T* __restrict__ out) {
+  __shared__ float s_w[kMaxSplits];
   const int row = blockIdx.x, h = blockIdx.y;
+  const int e = blockIdx.z * 128 + threadIdx.x;
   const size_t stride = (size_t)d.B * d.L * d.H * (d.Dv + 2);
   const float* p0 = part + ((size_t)row * d.H + h) * (d.Dv + 2);
-  const float sink2 = sinks ? sinks[h] * kLog2e : -INFINITY;
-  float mf = sink2;
-  for (int s = 0; s < splits; ++s) mf = fmaxf(mf, p0[s * stride + d.Dv]);
-  T* orow = out + ((size_t)row * d.H + h) * d.Dv;
-  if (mf == -INFINITY) {
-    for (int e = threadIdx.x; e < d.Dv; e += 128) stf(orow + e, 0.f);
-    return;
+  if (threadIdx.x < 64) {
+    const int s = threadIdx.x;
+    const float m = s < splits ? p0[s * stride + d.Dv] : -INFINITY;
+    const float l = s < splits ? p0[s * stride + d.Dv + 1] : 0.f;
+    const float sink2 = sinks ? sinks[h] * kLog2e : -INFINITY;
+    float mf = m;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mf = fmaxf(mf, __shfl_xor(mf, o, 64));
+    mf = fmaxf(mf, sink2);
+    const float wgt = (mf == -INFINITY || m == -INFINITY) ? 0.f : exp2f(m - mf);
+    float lf = wave_sum(l * wgt);
+    if (sinks && mf != -INFINITY) lf += exp2f(sink2 - mf);
+    const float inv = lf > 0.f ? 1.f / lf : 0.f;
+    s_w[s] = wgt * inv;
   }
-  float lf = sinks ? exp2f(sink2 - mf) : 0.f;
-  for (int s = 0; s < splits; ++s) lf += p0[s * stride + d.Dv + 1] * exp2f(p0[s * stride + d.Dv] - mf);
-  const float inv = lf > 0.f ? 1.f / lf : 0.f;
-  for (int e = threadIdx.x; e < d.Dv; e += 128) {
-    float o = 0.f;
-    for (int s = 0; s < splits; ++s) o += p0[s * stride + e] * exp2f(p0[s * stride + d.Dv] - mf);
-    stf(orow + e, o * inv);
-  }
+  __syncthreads();
+  if (e >= d.Dv) return;
+  float o = 0.f;
+#pragma unroll 8
+  for (int s = 0; s < splits; ++s) o += p0[s * stride + e] * s_w[s];
+  stf(out + ((size_t)row * d.H + h) * d.Dv + e, o);
 }
 
 // Any shape / dtype: one workgroup per (query row, head), two-pass softmax.
@@ -317,10 +353,6 @@ hipError_t launch_mfma(const KDims& d, const void* q, const void* local_kv, cons
   const dim3 grid(splits, d.B * d.L, d.H / 64);
   hipLaunchKernelGGL((k_attn_mfma<DK, DV, 4>), grid, dim3(256), 0, st, d, splits, (const uint16_t*)q,
                      (const uint16_t*)local_kv, (const uint16_t*)pooled_kv, I, sinks, t0, (uint16_t*)out, partial);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || splits == 1) return e;
-  hipLaunchKernelGGL(k_attn_merge<uint16_t>, dim3(d.B * d.L, d.H), dim3(128), 0, st, d, splits, partial, sinks,
-                     (uint16_t*)out);
   return hipGetLastError();
 }
 
@@ -338,15 +370,27 @@ int attn_splits(const KDims& d, bool bf16) {
   if (!attn_mfma_ok(d, bf16)) return 1;
   const long long work = (long long)d.B * d.L * (d.H / 64);
   const long long n_max = (long long)min(d.window, d.Wl_cap) + d.kI;
-  const long long max_splits = std::max(1LL, (n_max + kTile - 1) / kTile);
+  // at least two 32-row tiles per split, so that fetching overlaps compute
+  const long long max_splits = std::max(1LL, (n_max + 2 * kTile - 1) / (2 * kTile));
   long long want = (256 + work - 1) / work;
-  want = std::min(want, std::min(max_splits, 64LL));
+  want = std::min(want, std::min(max_splits, (long long)kMaxSplits));
   return (int)std::max(1LL, want);
 }
 
 size_t attn_partial_bytes(const KDims& d, int splits) {
   if (splits <= 1) return 0;
   return (size_t)splits * d.B * d.L * d.H * (d.Dv + 2) * sizeof(float);
+}
+
+hipError_t launch_attention_merge(const KDims& d, bool bf16, const float* partial, const float* sinks, void* out,
+                                  int splits, hipStream_t st) {
+  if (bf16)
+    hipLaunchKernelGGL(k_attn_merge<uint16_t>, dim3(d.B * d.L, d.H, (d.Dv + 127) / 128), dim3(128), 0, st, d, splits,
+                       partial, sinks, (uint16_t*)out);
+  else
+    hipLaunchKernelGGL(k_attn_merge<float>, dim3(d.B * d.L, d.H, (d.Dv + 127) / 128), dim3(128), 0, st, d, splits,
+                       partial, sinks, (float*)out);
+  return hipGetLastError();
 }
 
 hipError_t launch_attention(const KDims& d, bool bf16, const void* q, const void* local_kv, const void* pooled_kv,

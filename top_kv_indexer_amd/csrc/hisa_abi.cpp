@@ -7,7 +7,10 @@
 #include <initializer_list>
 #include <cstdarg>
 #include <cstdio>
+#include <cstring>
+#include <map>
 #include <string>
+#include <vector>
 
 #include "hisa.h"
 #include "hisa_internal.h"
@@ -160,6 +163,43 @@ int check_ptrs(std::initializer_list<const void*> ptrs, const char* names) {
   return HISA_OK;
 }
 
+// ---- kernel timing (opt-in tracing aid) ----
+struct ProfRecord {
+  const char* name;
+  hipEvent_t start, stop;
+};
+struct ProfTotal {
+  long long launches = 0;
+  double ms = 0.0;
+};
+bool g_prof_on = false;
+std::vector<ProfRecord> g_prof_pending;
+std::vector<hipEvent_t> g_prof_pool;
+std::map<std::string, ProfTotal> g_prof_totals;
+
+hipEvent_t prof_event() {
+  if (!g_prof_pool.empty()) {
+    hipEvent_t e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Runs one kernel launch, bracketed by events while timing is on.
+template <class F>
+hipError_t timed(const char* name, hipStream_t st, F launch) {
+  if (!g_prof_on) return launch();
+  ProfRecord r{name, prof_event(), prof_event()};
+  if (r.start) hipEventRecord(r.start, st);
+  const hipError_t e = launch();
+  if (r.stop) hipEventRecord(r.stop, st);
+  if (r.start && r.stop) g_prof_pending.push_back(r);
+  return e;
+}
+
 int prepare(int op, const hisa_dims* d, KDims* k, Layout* l, void* ws, size_t ws_bytes) {
   int rc = make_kdims(op, d, k);
   if (rc) return rc;
@@ -193,9 +233,9 @@ int hisa_block_scores(const hisa_dims* d, const void* q_idx, const float* w, con
   hipStream_t st = (hipStream_t)stream;
   float* rep = rep_out ? rep_out : at<float>(ws, l.rep);
   uint16_t* rep3 = hisa::idx_mfma_ok(k, bf) ? at<uint16_t>(ws, l.rep3) : nullptr;
-  hipError_t e = hisa::launch_block_mean(k, bf, true, keys, t0, rep, rep3, st);
+  hipError_t e = timed("block_mean", st, [&] { return hisa::launch_block_mean(k, bf, true, keys, t0, rep, rep3, st); });
   if (e != hipSuccess) return launch_fail(e, "block mean");
-  e = hisa::launch_coarse(k, bf, true, q_idx, w, rep, rep3, t0, cscore_out, st);
+  e = timed("coarse", st, [&] { return hisa::launch_coarse(k, bf, true, q_idx, w, rep, rep3, t0, cscore_out, st); });
   if (e != hipSuccess) return launch_fail(e, "coarse scores");
   return HISA_OK;
 }
@@ -213,9 +253,9 @@ int hisa_select_decode(const hisa_dims* d, const void* q_idx, const float* w, co
   hipStream_t st = (hipStream_t)stream;
   float* fscore = at<float>(ws, l.fscore);
   float* cscore = at<float>(ws, l.cscore);
-  hipError_t e = hisa::launch_decode_scan(k, bf, q_idx, w, keys, t0, fscore, cscore, st);
+  hipError_t e = timed("decode_scan", st, [&] { return hisa::launch_decode_scan(k, bf, q_idx, w, keys, t0, fscore, cscore, st); });
   if (e != hipSuccess) return launch_fail(e, "decode scan");
-  e = hisa::launch_decode_select(k, fscore, cscore, t0, I_out, top_blk_out, path_out, st);
+  e = timed("decode_select", st, [&] { return hisa::launch_decode_select(k, fscore, cscore, t0, I_out, top_blk_out, path_out, st); });
   if (e != hipSuccess) return launch_fail(e, "decode select");
   return HISA_OK;
 }
@@ -237,17 +277,17 @@ int hisa_select_prefill(const hisa_dims* d, const void* q_idx, const float* w, c
     float* rep = at<float>(ws, l.rep);
     uint16_t* rep3 = hisa::idx_mfma_ok(k, bf) ? at<uint16_t>(ws, l.rep3) : nullptr;
     cscore = at<float>(ws, l.cscore);
-    e = hisa::launch_block_mean(k, bf, false, keys, t0, rep, rep3, st);
+    e = timed("block_mean", st, [&] { return hisa::launch_block_mean(k, bf, false, keys, t0, rep, rep3, st); });
     if (e != hipSuccess) return launch_fail(e, "block mean");
-    e = hisa::launch_coarse(k, bf, false, q_idx, w, rep, rep3, t0, cscore, st);
+    e = timed("coarse", st, [&] { return hisa::launch_coarse(k, bf, false, q_idx, w, rep, rep3, t0, cscore, st); });
     if (e != hipSuccess) return launch_fail(e, "coarse scores");
   }
   float* scores = at<float>(ws, l.scores);
-  e = hisa::launch_flat_scores(k, bf, q_idx, w, keys, t0, scores, st);
+  e = timed("flat_scores", st, [&] { return hisa::launch_flat_scores(k, bf, q_idx, w, keys, t0, scores, st); });
   if (e != hipSuccess) return launch_fail(e, "flat scores");
-  e = hisa::launch_topk_rows(k, scores, t0, I_out, nullptr, st);
+  e = timed("topk_rows", st, [&] { return hisa::launch_topk_rows(k, scores, t0, I_out, nullptr, st); });
   if (e != hipSuccess) return launch_fail(e, "flat top-k");
-  e = hisa::launch_fine(k, bf, q_idx, w, keys, cscore, t0, I_out, top_blk_out, path_out, st);
+  e = timed("fine", st, [&] { return hisa::launch_fine(k, bf, q_idx, w, keys, cscore, t0, I_out, top_blk_out, path_out, st); });
   if (e != hipSuccess) return launch_fail(e, "fine selection");
   return HISA_OK;
 }
@@ -264,9 +304,9 @@ int flat_topk_select(const hisa_dims* d, const void* q_idx, const float* w, cons
   hipStream_t st = (hipStream_t)stream;
   k.force_path = hisa::PATH_FLAT;
   float* scores = at<float>(ws, l.scores);
-  hipError_t e = hisa::launch_flat_scores(k, bf, q_idx, w, keys, t0, scores, st);
+  hipError_t e = timed("flat_scores", st, [&] { return hisa::launch_flat_scores(k, bf, q_idx, w, keys, t0, scores, st); });
   if (e != hipSuccess) return launch_fail(e, "flat scores");
-  e = hisa::launch_topk_rows(k, scores, t0, I_out, nullptr, st);
+  e = timed("topk_rows", st, [&] { return hisa::launch_topk_rows(k, scores, t0, I_out, nullptr, st); });
   if (e != hipSuccess) return launch_fail(e, "flat top-k");
   return HISA_OK;
 }
@@ -283,11 +323,55 @@ int sparse_local_pooled_attention(const hisa_dims* d, const void* q, const void*
   if (d->window > 0 && !local_kv) return fail(HISA_ERR_ARG, "local_kv is NULL with window > 0");
   if (d->kI > 0 && !I) return fail(HISA_ERR_ARG, "I is NULL with kI > 0");
   const bool bf = d->attn_dtype == HISA_BF16;
-  hipError_t e = hisa::launch_attention(k, bf, q, local_kv, pooled_kv, I, sinks, t0, out,
-                                        l.splits > 1 ? at<float>(ws, l.partial) : nullptr, l.splits,
-                                        (hipStream_t)stream);
+  hipStream_t st = (hipStream_t)stream;
+  float* partial = l.splits > 1 ? at<float>(ws, l.partial) : nullptr;
+  hipError_t e = timed("attention", st, [&] {
+    return hisa::launch_attention(k, bf, q, local_kv, pooled_kv, I, sinks, t0, out, partial, l.splits, st);
+  });
+  if (e == hipSuccess && l.splits > 1)
+    e = timed("attention_merge", st, [&] { return hisa::launch_attention_merge(k, bf, partial, sinks, out, l.splits, st); });
   if (e != hipSuccess) return launch_fail(e, "attention");
   return HISA_OK;
+}
+
+int hisa_profile_enable(int on) {
+  if (!on) {
+    for (auto& r : g_prof_pending) {
+      hipEventSynchronize(r.stop);
+      g_prof_pool.push_back(r.start);
+      g_prof_pool.push_back(r.stop);
+    }
+    g_prof_pending.clear();
+    g_prof_totals.clear();
+  }
+  g_prof_on = on != 0;
+  return HISA_OK;
+}
+
+int hisa_profile_collect(hisa_kernel_time* out, int max_entries) {
+  for (auto& r : g_prof_pending) {
+    hipError_t e = hipEventSynchronize(r.stop);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.stop);
+    if (e != hipSuccess) return launch_fail(e, "profile events");
+    ProfTotal& t = g_prof_totals[r.name];
+    t.launches += 1;
+    t.ms += ms;
+    g_prof_pool.push_back(r.start);
+    g_prof_pool.push_back(r.stop);
+  }
+  g_prof_pending.clear();
+  int i = 0;
+  for (const auto& kv : g_prof_totals) {
+    if (out && i < max_entries) {
+      std::memset(out[i].name, 0, sizeof(out[i].name));
+      std::strncpy(out[i].name, kv.first.c_str(), sizeof(out[i].name) - 1);
+      out[i].launches = kv.second.launches;
+      out[i].total_ms = kv.second.ms;
+    }
+    ++i;
+  }
+  return i;
 }
 
 }  // extern "C"

@@ -49,6 +49,8 @@ hipError_t launch_attention(const KDims& d, bool bf16, const void* q, const void
                             const void* pooled_kv, const int* I, const float* sinks,
                             const int* t0, void* out, float* partial, int splits,
                             hipStream_t st);
+hipError_t launch_attention_merge(const KDims& d, bool bf16, const float* partial,
+                                  const float* sinks, void* out, int splits, hipStream_t st);
 
 // Shapes with hand-tuned MFMA selection kernels.
 inline bool idx_mfma_ok(const KDims& d, bool bf16) { return bf16 && d.H_i == 64 && d.D_i == 128; }

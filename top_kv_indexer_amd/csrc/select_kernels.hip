@@ -17,6 +17,8 @@
 //   flat scores + topk rows      the flat scan for any L.
 // The MFMA kernels serve bf16 keys with 64 heads x 128 dims (the V4-Flash and
 // V3.2 indexer shapes); other shapes and f32 inputs take plain VALU kernels.
+#include <algorithm>
+
 #include "hisa_device.h"
 
 namespace hisa {
@@ -30,17 +32,21 @@ __device__ __forceinline__ bf16x8 ldg8(const uint16_t* p) { return *(const bf16x
 
 // ------------------------------------------------------------------ decode scan
 
-// One 64-row tile of one sequence (bf16, H_i = 64, D_i = 128, index_block | 64).
-__global__ __launch_bounds__(256) void k_decode_scan_mfma(KDims d, const uint16_t* __restrict__ q_idx,
+// Consecutive 64-row tiles of one sequence (bf16, H_i = 64, D_i = 128,
+// index_block | 64).  The query goes to LDS once; the next tile's keys are
+// fetched into registers while the current tile is scored.
+__global__ __launch_bounds__(256) void k_decode_scan_mfma(KDims d, int tiles_per_wg,
+                                                          const uint16_t* __restrict__ q_idx,
                                                           const float* __restrict__ w,
                                                           const uint16_t* __restrict__ keys,
                                                           const int* __restrict__ t0,
                                                           float* __restrict__ fscore,
                                                           float* __restrict__ cscore) {
   const int b = blockIdx.y;
-  const int row0 = blockIdx.x * 64;
   const SeqInfo si = seq_info(d, t0[b]);
-  if (!si.ok || si.path == PATH_DENSE || row0 >= si.Np) return;
+  const int tile_begin = blockIdx.x * tiles_per_wg;
+  if (!si.ok || si.path == PATH_DENSE || tile_begin * 64 >= si.Np) return;
+  const int tile_end = min(tile_begin + tiles_per_wg, (si.Np + 63) / 64);
   __shared__ __align__(16) uint16_t sk[64 * KP];
   __shared__ __align__(16) uint16_t sq[64 * KP];
   __shared__ float s_weff[64];
@@ -48,72 +54,101 @@ __global__ __launch_bounds__(256) void k_decode_scan_mfma(KDims d, const uint16_
   __shared__ float s_red[4];
   const int tid = threadIdx.x;
   const uint16_t* qb = q_idx + (size_t)b * d.L * 64 * 128;
-  const uint16_t* kb = keys + ((size_t)b * d.Np_cap + row0) * 128;
-  const int nrows = min(64, si.Np - row0);
+  const uint16_t* kb = keys + (size_t)b * d.Np_cap * 128;
+  uint4 kreg[4];
+  auto fetch = [&](int tile) {
+    const int row0 = tile * 64;
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int ch = tid + it * 256;
-    const int r = ch >> 4, seg = (ch & 15) * 8;
-    const uint4 vq = *(const uint4*)(qb + r * 128 + seg);
-    uint4 vk = make_uint4(0, 0, 0, 0);
-    if (r < nrows) vk = *(const uint4*)(kb + (size_t)r * 128 + seg);
-    *(uint4*)(sq + r * KP + seg) = vq;
-    *(uint4*)(sk + r * KP + seg) = vk;
-  }
-  if (tid < 64) s_weff[tid] = w[(size_t)b * d.L * 64 + tid] * d.w_scale;
-  __syncthreads();
-
-  // Fine scores of the tile's rows: wave wv takes rows 16wv..16wv+15.
-  // A = q (rows = heads), B = keys^T (columns = rows); D[h][row].
-  const int lane = lane_id(), wv = wave_id(), g = lane >> 4, c = lane & 15;
-  f32x4 acc[4];
-#pragma unroll
-  for (int ht = 0; ht < 4; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const bf16x8 kf = lds8(sk + (wv * 16 + c) * KP + s * 32 + g * 8);
-#pragma unroll
-    for (int ht = 0; ht < 4; ++ht) {
-      const bf16x8 qf = lds8(sq + (ht * 16 + c) * KP + s * 32 + g * 8);
-      acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf, kf, acc[ht], 0, 0, 0);
+    for (int it = 0; it < 4; ++it) {
+      const int ch = tid + it * 256;
+      const int r = ch >> 4, seg = (ch & 15) * 8;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (row0 + r < si.Np) v = *(const uint4*)(kb + (size_t)(row0 + r) * 128 + seg);
+      kreg[it] = v;
     }
+  };
+  {
+    uint4 qreg[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int ch = tid + it * 256;
+      qreg[it] = *(const uint4*)(qb + (ch >> 4) * 128 + (ch & 15) * 8);
+    }
+    fetch(tile_begin);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int ch = tid + it * 256;
+      *(uint4*)(sq + (ch >> 4) * KP + (ch & 15) * 8) = qreg[it];
+    }
+    if (tid < 64) s_weff[tid] = w[(size_t)b * d.L * 64 + tid] * d.w_scale;
   }
-  float v = 0.f;
-#pragma unroll
-  for (int ht = 0; ht < 4; ++ht)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v += fmaxf(acc[ht][i], 0.f) * s_weff[ht * 16 + 4 * g + i];
-  v += __shfl_xor(v, 16, 64);
-  v += __shfl_xor(v, 32, 64);
-  if (g == 0 && wv * 16 + c < nrows) fscore[(size_t)b * d.Np_cap + row0 + wv * 16 + c] = v;
-
-  if (si.path != PATH_HISA) return;
-  // Block means and coarse scores of the blocks inside this tile.
+  const int lane = lane_id(), wv = wave_id(), g = lane >> 4, c = lane & 15;
   const int bsz = d.index_block;
   const int h = tid >> 2, part = tid & 3;
   float qr[32];
+  float wh = 0.f;
+  for (int tile = tile_begin; tile < tile_end; ++tile) {
+    const int row0 = tile * 64;
+    const int nrows = min(64, si.Np - row0);
+    __syncthreads();
 #pragma unroll
-  for (int e = 0; e < 32; ++e) qr[e] = bf2f(sq[h * KP + part * 32 + e]);
-  const float wh = s_weff[h];
-  for (int blk = 0; blk < 64 / bsz; ++blk) {
-    const int beta = row0 / bsz + blk;
-    if (beta >= si.nb) break;
-    if (tid < 128) {
-      float s = 0.f;
-      for (int r = 0; r < bsz; ++r) s += bf2f(sk[(blk * bsz + r) * KP + tid]);
-      s_rep[tid] = s / (float)bsz;
+    for (int it = 0; it < 4; ++it) {
+      const int ch = tid + it * 256;
+      *(uint4*)(sk + (ch >> 4) * KP + (ch & 15) * 8) = kreg[it];
     }
     __syncthreads();
-    float dot = 0.f;
+    if (tile + 1 < tile_end) fetch(tile + 1);
+    if (tile == tile_begin && si.path == PATH_HISA) {
 #pragma unroll
-    for (int e = 0; e < 32; ++e) dot += qr[e] * s_rep[part * 32 + e];
-    dot += __shfl_xor(dot, 1, 64);
-    dot += __shfl_xor(dot, 2, 64);
-    float contrib = part == 0 ? fmaxf(dot, 0.f) * wh : 0.f;
-    contrib = wave_sum(contrib);
-    if (lane == 0) s_red[wv] = contrib;
-    __syncthreads();
-    if (tid == 0) cscore[(size_t)b * d.nb_cap + beta] = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+      for (int e = 0; e < 32; ++e) qr[e] = bf2f(sq[h * KP + part * 32 + e]);
+      wh = s_weff[h];
+    }
+
+    // Fine scores of the tile's rows: wave wv takes rows 16wv..16wv+15.
+    // A = q (rows = heads), B = keys^T (columns = rows); D[h][row].
+    f32x4 acc[4];
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const bf16x8 kf = lds8(sk + (wv * 16 + c) * KP + s * 32 + g * 8);
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) {
+        const bf16x8 qf = lds8(sq + (ht * 16 + c) * KP + s * 32 + g * 8);
+        acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf, kf, acc[ht], 0, 0, 0);
+      }
+    }
+    float v = 0.f;
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v += fmaxf(acc[ht][i], 0.f) * s_weff[ht * 16 + 4 * g + i];
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    if (g == 0 && wv * 16 + c < nrows) fscore[(size_t)b * d.Np_cap + row0 + wv * 16 + c] = v;
+
+    if (si.path != PATH_HISA) continue;
+    // Block means and coarse scores of the blocks inside this tile.
+    for (int blk = 0; blk < 64 / bsz; ++blk) {
+      const int beta = row0 / bsz + blk;
+      if (beta >= si.nb) break;
+      if (tid < 128) {
+        float s = 0.f;
+        for (int r = 0; r < bsz; ++r) s += bf2f(sk[(blk * bsz + r) * KP + tid]);
+        s_rep[tid] = s / (float)bsz;
+      }
+      __syncthreads();
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) dot += qr[e] * s_rep[part * 32 + e];
+      dot += __shfl_xor(dot, 1, 64);
+      dot += __shfl_xor(dot, 2, 64);
+      float contrib = part == 0 ? fmaxf(dot, 0.f) * wh : 0.f;
+      contrib = wave_sum(contrib);
+      if (lane == 0) s_red[wv] = contrib;
+      __syncthreads();
+      if (tid == 0) cscore[(size_t)b * d.nb_cap + beta] = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+    }
   }
 }
 
@@ -173,42 +208,77 @@ __global__ __launch_bounds__(256) void k_decode_scan_valu(KDims d, const T* __re
 // ------------------------------------------------------------------ decode select
 
 constexpr int kMaxKeep = 1024;
+constexpr int kSelectThreads = 256;
+constexpr int kSelectLdsCap = 8192;    // keys staged in LDS per pass (32 KiB)
 
-__global__ __launch_bounds__(256) void k_decode_select(KDims d, const float* __restrict__ fscore,
-                                                       const float* __restrict__ cscore,
-                                                       const int* __restrict__ t0, int* __restrict__ I,
-                                                       int* __restrict__ top_blk, int* __restrict__ path) {
+// Stages n keys into LDS (when they fit) and returns whether it did.
+template <class SrcF>
+__device__ __forceinline__ bool stage_keys(uint32_t* s_keys, int n, int cap, SrcF src) {
+  if (n > cap) return false;
+  for (int i = threadIdx.x; i < n; i += 4 * kSelectThreads) {  // 4 loads in flight per thread
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int ii = i + u * kSelectThreads;
+      v[u] = ii < n ? src(ii) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int ii = i + u * kSelectThreads;
+      if (ii < n) s_keys[ii] = score_key(v[u]);
+    }
+  }
+  __syncthreads();
+  return true;
+}
+
+// One sequence per workgroup (one wave): gate, then the flat top-k or the
+// coarse top-Kb + fine top-k, reading the scan's scores through LDS.
+__global__ __launch_bounds__(kSelectThreads) void k_decode_select(KDims d, int lds_cap,
+                                                                  const float* __restrict__ fscore,
+                                                                  const float* __restrict__ cscore,
+                                                                  const int* __restrict__ t0, int* __restrict__ I,
+                                                                  int* __restrict__ top_blk, int* __restrict__ path) {
+  constexpr int NT = kSelectThreads;
   const int b = blockIdx.x, tid = threadIdx.x;
   const SeqInfo si = seq_info(d, t0[b]);
+  extern __shared__ uint32_t s_keys[];
   __shared__ TopkSmem sm;
   __shared__ int s_blk[kMaxKeep];
   int* Ib = I + (size_t)b * d.topk;
   const bool dense = si.path == PATH_DENSE;
   const int first_pad = (si.ok && !dense) ? si.k : 0;
-  for (int i = tid; i < d.topk; i += 256) {
+  for (int i = tid; i < d.topk; i += NT) {
     if (dense && i < si.Np) Ib[i] = i;
     else if (i >= first_pad) Ib[i] = -1;
   }
   if (top_blk)
-    for (int i = tid; i < d.index_keep; i += 256) top_blk[(size_t)b * d.index_keep + i] = -1;
+    for (int i = tid; i < d.index_keep; i += NT) top_blk[(size_t)b * d.index_keep + i] = -1;
   if (path && tid == 0) path[b] = si.path;
   if (!si.ok || dense) return;
   const float* fs = fscore + (size_t)b * d.Np_cap;
   if (si.path == PATH_FLAT) {
-    block_topk<256>(si.Np, si.k, [&](int i) { return score_key(fs[i]); },
-                    [&](int slot, int i) { Ib[slot] = i; }, sm);
+    auto emit = [&](int slot, int i) { Ib[slot] = i; };
+    if (stage_keys(s_keys, si.Np, lds_cap, [&](int i) { return fs[i]; }))
+      block_topk<NT>(si.Np, si.k, [&](int i) { return s_keys[i]; }, emit, sm);
+    else
+      block_topk<NT>(si.Np, si.k, [&](int i) { return score_key(fs[i]); }, emit, sm);
     return;
   }
   const float* cs = cscore + (size_t)b * d.nb_cap;
-  block_topk<256>(si.nb, si.Kb, [&](int i) { return score_key(cs[i]); },
-                  [&](int slot, int i) { s_blk[slot] = i; }, sm);
+  auto emit_blk = [&](int slot, int i) { s_blk[slot] = i; };
+  if (stage_keys(s_keys, si.nb, lds_cap, [&](int i) { return cs[i]; }))
+    block_topk<NT>(si.nb, si.Kb, [&](int i) { return s_keys[i]; }, emit_blk, sm);
+  else
+    block_topk<NT>(si.nb, si.Kb, [&](int i) { return score_key(cs[i]); }, emit_blk, sm);
   __syncthreads();
   if (top_blk)
-    for (int i = tid; i < si.Kb; i += 256) top_blk[(size_t)b * d.index_keep + i] = s_blk[i];
+    for (int i = tid; i < si.Kb; i += NT) top_blk[(size_t)b * d.index_keep + i] = s_blk[i];
   const int bsz = d.index_block;
   const int C = si.Kb * bsz;
-  block_topk<256>(C, si.k, [&](int c) { return score_key(fs[s_blk[c / bsz] * bsz + c % bsz]); },
-                  [&](int slot, int c) { Ib[slot] = s_blk[c / bsz] * bsz + c % bsz; }, sm);
+  auto pos = [&](int c) { return s_blk[c / bsz] * bsz + c % bsz; };
+  stage_keys(s_keys, C, lds_cap, [&](int c) { return fs[pos(c)]; });  // C <= keep * b <= the LDS cap
+  block_topk<NT>(C, si.k, [&](int c) { return s_keys[c]; }, [&](int slot, int c) { Ib[slot] = pos(c); }, sm);
 }
 
 // ------------------------------------------------------------------ batched path
@@ -229,6 +299,7 @@ __global__ __launch_bounds__(128) void k_block_mean(KDims d, int all_paths, cons
     float s = 0.f;
     if (live) {
       const T* kp = keys + ((size_t)b * d.Np_cap + (size_t)beta * bsz) * d.D_i + e;
+#pragma unroll 16
       for (int r = 0; r < bsz; ++r) s += ldf(kp + (size_t)r * d.D_i);
       s = s / (float)bsz;
     }
@@ -360,7 +431,7 @@ __device__ __forceinline__ bool fine_prologue(const KDims& d, const SeqInfo& si,
 
 // One query row per workgroup: coarse top-Kb, fine scores of the C = Kb*b
 // candidates on MFMA (keys gathered straight from HBM/L2), fine top-k.
-__global__ __launch_bounds__(256) void k_fine_mfma(KDims d, const uint16_t* __restrict__ q_idx,
+__global__ __launch_bounds__(256) void k_fine_mfma(KDims d, int lds_floats, const uint16_t* __restrict__ q_idx,
                                                    const float* __restrict__ w, const uint16_t* __restrict__ keys,
                                                    const float* __restrict__ cscore, const int* __restrict__ t0,
                                                    int* __restrict__ I, int* __restrict__ top_blk,
@@ -370,13 +441,19 @@ __global__ __launch_bounds__(256) void k_fine_mfma(KDims d, const uint16_t* __re
   int* Irow = I + ((size_t)b * d.L + j) * d.topk;
   int* blkrow = top_blk ? top_blk + ((size_t)b * d.L + j) * d.index_keep : nullptr;
   if (!fine_prologue(d, si, b, j, Irow, blkrow, path)) return;
-  extern __shared__ float s_fs[];
+  extern __shared__ float s_fs[];  // max(nb_cap, C) floats: coarse scores, then fine scores
   __shared__ TopkSmem sm;
   __shared__ int s_blk[kMaxKeep];
   const int valid = visible(t0[b] + j, d.ratio, si.Np);
   const float* cs = cscore + ((size_t)b * d.L + j) * d.nb_cap;
-  block_topk<256>(si.nb, si.Kb, [&](int i) { return score_key(cs[i]); },
-                  [&](int slot, int i) { s_blk[slot] = i; }, sm);
+  auto emit_blk = [&](int slot, int i) { s_blk[slot] = i; };
+  if (si.nb <= lds_floats) {
+    for (int i = threadIdx.x; i < si.nb; i += 256) s_fs[i] = cs[i];
+    __syncthreads();
+    block_topk<256>(si.nb, si.Kb, [&](int i) { return score_key(s_fs[i]); }, emit_blk, sm);
+  } else {
+    block_topk<256>(si.nb, si.Kb, [&](int i) { return score_key(cs[i]); }, emit_blk, sm);
+  }
   __syncthreads();
   if (blkrow)
     for (int i = threadIdx.x; i < si.Kb; i += 256) blkrow[i] = s_blk[i];
@@ -398,14 +475,27 @@ __global__ __launch_bounds__(256) void k_fine_mfma(KDims d, const uint16_t* __re
   const int bsz = d.index_block;
   const int C = si.Kb * bsz;
   const uint16_t* kb = keys + (size_t)b * d.Np_cap * 128;
+  // Candidate tiles of 16 rows, the next tile's keys in flight while the
+  // current one is scored.
+  auto cand = [&](int tile) {
+    const int cc = min(tile * 16 + c, C - 1);
+    return s_blk[cc / bsz] * bsz + cc % bsz;
+  };
+  bf16x8 kn[4];
+  auto fetch = [&](int tile) {
+    const uint16_t* kp = kb + (size_t)cand(tile) * 128 + g * 32;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) kn[s] = ldg8(kp + s * 8);
+  };
+  __syncthreads();  // s_fs is reused for the fine scores below
+  if (wv * 16 < C) fetch(wv);
   for (int tile = wv; tile * 16 < C; tile += 4) {
-    const int cidx = tile * 16 + c;
-    const int cc = min(cidx, C - 1);
-    const int pos = s_blk[cc / bsz] * bsz + cc % bsz;
-    const uint16_t* kp = kb + (size_t)pos * 128 + g * 32;
     bf16x8 kf[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) kf[s] = ldg8(kp + s * 8);
+    for (int s = 0; s < 4; ++s) kf[s] = kn[s];
+    if ((tile + 4) * 16 < C) fetch(tile + 4);
+    const int cidx = tile * 16 + c;
+    const int pos = cand(tile);
     f32x4 acc[4];
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) {
@@ -628,9 +718,13 @@ static inline unsigned cdiv(long long a, long long b) { return (unsigned)((a + b
 hipError_t launch_decode_scan(const KDims& d, bool bf16, const void* q_idx, const float* w, const void* keys,
                               const int* t0, float* fscore, float* cscore, hipStream_t st) {
   const dim3 grid(cdiv(d.Np_cap, 64), d.B);
-  if (idx_mfma_ok(d, bf16))
-    hipLaunchKernelGGL(k_decode_scan_mfma, grid, dim3(256), 0, st, d, (const uint16_t*)q_idx, w,
-                       (const uint16_t*)keys, t0, fscore, cscore);
+  if (idx_mfma_ok(d, bf16)) {
+    // Enough tiles per workgroup to keep ~2048 workgroups in the grid.
+    const long long tiles = (long long)d.B * cdiv(d.Np_cap, 64);
+    const int per = (int)std::min(16LL, std::max(1LL, tiles / 2048));
+    hipLaunchKernelGGL(k_decode_scan_mfma, dim3(cdiv(cdiv(d.Np_cap, 64), per), d.B), dim3(256), 0, st, d, per,
+                       (const uint16_t*)q_idx, w, (const uint16_t*)keys, t0, fscore, cscore);
+  }
   else if (bf16)
     hipLaunchKernelGGL(k_decode_scan_valu<uint16_t>, grid, dim3(256), 0, st, d, (const uint16_t*)q_idx, w,
                        (const uint16_t*)keys, t0, fscore, cscore);
@@ -642,7 +736,9 @@ hipError_t launch_decode_scan(const KDims& d, bool bf16, const void* q_idx, cons
 
 hipError_t launch_decode_select(const KDims& d, const float* fscore, const float* cscore, const int* t0, int* I,
                                 int* top_blk, int* path, hipStream_t st) {
-  hipLaunchKernelGGL(k_decode_select, dim3(d.B), dim3(256), 0, st, d, fscore, cscore, t0, I, top_blk, path);
+  const int cap = std::min(kSelectLdsCap, std::max({d.nb_cap, d.index_keep * d.index_block, d.Np_cap}));
+  hipLaunchKernelGGL(k_decode_select, dim3(d.B), dim3(kSelectThreads), (size_t)cap * sizeof(uint32_t), st, d, cap,
+                     fscore, cscore, t0, I, top_blk, path);
   return hipGetLastError();
 }
 
@@ -676,10 +772,12 @@ hipError_t launch_coarse(const KDims& d, bool bf16, bool all_paths, const void* 
 
 hipError_t launch_fine(const KDims& d, bool bf16, const void* q_idx, const float* w, const void* keys,
                        const float* cscore, const int* t0, int* I, int* top_blk, int* path, hipStream_t st) {
-  const size_t lds = (size_t)d.index_keep * d.index_block * sizeof(float);
+  // coarse scores are staged in LDS when they fit next to the fine scores
+  const int lds_floats = std::max(d.index_keep * d.index_block, std::min(d.nb_cap, 12288));
+  const size_t lds = (size_t)lds_floats * sizeof(float);
   const dim3 grid(d.L, d.B);
   if (idx_mfma_ok(d, bf16))
-    hipLaunchKernelGGL(k_fine_mfma, grid, dim3(256), lds, st, d, (const uint16_t*)q_idx, w, (const uint16_t*)keys,
+    hipLaunchKernelGGL(k_fine_mfma, grid, dim3(256), lds, st, d, lds_floats, (const uint16_t*)q_idx, w, (const uint16_t*)keys,
                        cscore, t0, I, top_blk, path);
   else if (bf16)
     hipLaunchKernelGGL(k_fine_valu<uint16_t>, grid, dim3(256), lds, st, d, (const uint16_t*)q_idx, w,

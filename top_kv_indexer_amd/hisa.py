@@ -18,11 +18,16 @@ PATH_INVALID, PATH_DENSE, PATH_FLAT, PATH_HISA = -1, 0, 1, 2
 OP_BLOCK_SCORES, OP_SELECT_DECODE, OP_SELECT_PREFILL, OP_FLAT_TOPK, OP_ATTENTION = range(5)
 
 EXPORTS = ("hisa_block_scores", "hisa_select_decode", "hisa_select_prefill", "flat_topk_select",
-           "sparse_local_pooled_attention", "hisa_workspace_bytes", "hisa_last_error", "hisa_abi_version")
+           "sparse_local_pooled_attention", "hisa_workspace_bytes", "hisa_last_error", "hisa_abi_version",
+           "hisa_profile_enable", "hisa_profile_collect")
 
 
 class HisaError(RuntimeError):
     pass
+
+
+class hisa_kernel_time(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double)]
 
 
 class hisa_dims(ctypes.Structure):
@@ -56,6 +61,10 @@ def lib() -> ctypes.CDLL:
         L.hisa_workspace_bytes.restype = sz
         L.hisa_last_error.restype = ctypes.c_char_p
         L.hisa_abi_version.restype = i32
+        L.hisa_profile_enable.argtypes = [i32]
+        L.hisa_profile_enable.restype = i32
+        L.hisa_profile_collect.argtypes = [ctypes.POINTER(hisa_kernel_time), i32]
+        L.hisa_profile_collect.restype = i32
         _lib = L
     return _lib
 
@@ -216,3 +225,17 @@ def sparse_local_pooled_attention(q, local_kv, pooled_kv, I, sinks, t0, *, ratio
     _check(lib().sparse_local_pooled_attention(ctypes.byref(d), _p(q), _p(local_kv), _p(pooled_kv), _p(I), _p(sinks),
                                                _p(t0), _p(out), _p(wsb), n, _stream(dev)))
     return out
+
+
+def hisa_profile_enable(on: bool) -> None:
+    """Turns the library's per-kernel event timing on or off (off clears the totals)."""
+    _check(lib().hisa_profile_enable(1 if on else 0))
+
+
+def hisa_profile_collect() -> dict:
+    """Waits for the timed launches and returns {kernel: (launches, total_ms)}."""
+    buf = (hisa_kernel_time * 64)()
+    n = lib().hisa_profile_collect(buf, 64)
+    if n < 0:
+        _check(n)
+    return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms)) for i in range(min(n, 64))}

@@ -26,7 +26,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kTile = 32;
-constexpr int kChunk = 512;  // row addresses staged in LDS at a time
+constexpr int kChunk = 512;  // rows of the row list staged in LDS at a time
 
 struct RowPlan {
   bool ok;
@@ -54,30 +54,49 @@ __device__ __forceinline__ bf16x8 pack8(const float (&p)[8]) {
   return __builtin_bit_cast(bf16x8, u);
 }
 
-template <int DK, int DV, int NW>
-__global__ __launch_bounds__(NW * 64) void k_attn_mfma(KDims d, int splits, const uint16_t* __restrict__ q,
-                                                       const uint16_t* __restrict__ local_kv,
-                                                       const uint16_t* __restrict__ pooled_kv,
-                                                       const int* __restrict__ I, const float* __restrict__ sinks,
-                                                       const int* __restrict__ t0, uint16_t* __restrict__ out,
-                                                       float* __restrict__ part) {
-  constexpr int KPD = DK + 16;  // LDS row pitch: 8 banks of skew per row for the transposing reads
+// One workgroup = NHG groups of 16 heads x 2 halves of the value width = 2*NHG
+// waves.  Wave (hg, dh) computes the scores of rows 16*dh..16*dh+15 of each
+// 32-row tile for its 16 heads; the pair exchanges them through LDS, both run
+// the same online softmax over the 32 rows, and each accumulates O for its
+// half of the value columns (16 heads x DV/2 = DV/8 accumulator registers).
+template <int DK, int DV, int NHG>
+__global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, const uint16_t* __restrict__ q,
+                                                         const uint16_t* __restrict__ local_kv,
+                                                         const uint16_t* __restrict__ pooled_kv,
+                                                         const int* __restrict__ I, const float* __restrict__ sinks,
+                                                         const int* __restrict__ t0, uint16_t* __restrict__ out,
+                                                         float* __restrict__ part) {
+  constexpr int NW = NHG * 2;
   constexpr int NT = NW * 64;
+  constexpr int KPD = DK + 16;  // LDS row pitch: 8 banks of skew per row for the transposing reads
   constexpr int NS = DK / 32;   // MFMA k-steps of S
-  constexpr int NO = DV / 16;   // MFMA column tiles of O^T
-  constexpr int CPR = DK / 8;                       // 16-byte chunks per KV row
-  constexpr int CPT = (kTile * CPR + NT - 1) / NT;  // chunks per thread per tile
+  constexpr int DVH = DV / 2;   // value columns per wave
+  constexpr int NO = DVH / 16;  // MFMA column tiles of O^T per wave
+  constexpr int CPR = DK / 8;   // 16-byte chunks per KV row
+  constexpr int TCH = kTile * CPR;
+  constexpr int CPT = (TCH + NT - 1) / NT;  // chunks per thread per tile
+  constexpr int SP = 17;        // padded pitch (floats) of the score exchange rows
   __shared__ __align__(16) uint16_t kv[kTile * KPD];
-  __shared__ const uint16_t* s_ptr[kChunk];
+  __shared__ float s_sc[NHG][kTile * SP];
+  // Row list of the current chunk: element offset of each row (>= 0 into
+  // pooled_kv, ~offset into local_kv) and whether the row is live.  Dead rows
+  // point at a readable row of the same sequence and are masked in the softmax.
+  __shared__ long long s_off[kChunk];
+  __shared__ unsigned char s_live[kChunk];
 
   const int split = blockIdx.x, row = blockIdx.y;
   const int b = row / d.L, j = row % d.L;
   const int tid = threadIdx.x, lane = lane_id(), wv = wave_id(), g = lane >> 4, c = lane & 15;
-  const int h0 = blockIdx.z * 16 * NW + wv * 16;
+  const int hg = wv >> 1, dh = wv & 1;
+  const int h0 = blockIdx.z * 16 * NHG + hg * 16;
   const int T0 = t0[b];
   const RowPlan rp = row_plan(d, T0, j);
   const int per = (((rp.n_list + splits - 1) / splits) + kTile - 1) / kTile * kTile;
   const int begin = split * per, end = min(rp.n_list, begin + per);
+  // a row every sequence with a non-empty list may read
+  const long long dummy = rp.n_loc > 0 ? ~(((long long)b * d.Wl_cap + (rp.s_lo - rp.ls)) * DK)
+                                       : (long long)b * d.Np_cap * DK;
+  const bool any_row = rp.n_loc > 0 || rp.V > 0;
 
   bf16x8 qf[NS];
   const uint16_t* qrow = q + ((size_t)row * d.H + h0 + c) * DK + g * 8;
@@ -90,116 +109,131 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(KDims d, int splits, cons
   for (int n = 0; n < NO; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int* Irow = I + (size_t)row * d.kI;
-  for (int cb = begin; cb < end; cb += kChunk) {
+  for (int cb = any_row ? begin : end; cb < end; cb += kChunk) {
     const int ce = min(end, cb + kChunk);
-    // Row addresses of this chunk of the row list (local window, then I).
     __syncthreads();
-    for (int e = cb + tid; e < ce; e += NT) {
-      const uint16_t* p = nullptr;
-      if (e < rp.n_loc) {
-        p = local_kv + ((long long)b * d.Wl_cap + (rp.s_lo - rp.ls + e)) * DK;
-      } else {
-        const int id = Irow[e - rp.n_loc];
-        if (id >= 0 && id < rp.V) p = pooled_kv + ((long long)b * d.Np_cap + id) * DK;
+    for (int e = cb + tid; e < cb + ((ce - cb + kTile - 1) / kTile) * kTile; e += NT) {
+      long long off = dummy;
+      bool live = false;
+      if (e < ce) {
+        if (e < rp.n_loc) {
+          off = ~(((long long)b * d.Wl_cap + (rp.s_lo - rp.ls + e)) * DK);
+          live = true;
+        } else {
+          const int id = Irow[e - rp.n_loc];
+          if (id >= 0 && id < rp.V) {
+            off = ((long long)b * d.Np_cap + id) * DK;
+            live = true;
+          }
+        }
       }
-      s_ptr[e - cb] = p;
+      s_off[e - cb] = off;
+      s_live[e - cb] = live;
     }
     __syncthreads();
     // Tiles of 32 rows; the next tile's rows are fetched into registers while
     // the current one is computed from LDS.
-    uint4 reg[CPT];
-    auto fetch = [&](int tb) {
-#pragma unroll
-      for (int i = 0; i < CPT; ++i) {
-        const int ch = tid + i * NT;
-        const int r = ch / CPR, seg = (ch % CPR) * 8;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (ch < kTile * CPR && tb + r < ce) {
-          const uint16_t* p = s_ptr[tb - cb + r];
-          if (p) v = *(const uint4*)(p + seg);
-        }
-        reg[i] = v;
-      }
+    // Each thread moves CPT 16-byte chunks per tile; chunk i of the thread is
+    // row (tid + i*NT) / CPR, column segment (tid + i*NT) % CPR.
+    uint4 reg0, reg1, reg2, reg3, reg4;
+    static_assert(CPT <= 5, "tile fetch holds at most 5 chunks per thread");
+    auto chunk_ptr = [&](int tb, int i) -> const uint16_t* {
+      const int ch = tid + i * NT;
+      const long long off = s_off[tb - cb + ch / CPR];
+      const uint16_t* p = off >= 0 ? pooled_kv + off : local_kv + ~off;
+      return p + (ch % CPR) * 8;
     };
-    fetch(cb);
+    auto has = [&](int i) { return i < CPT && (TCH % NT == 0 || tid + i * NT < TCH); };
+    if (has(0)) reg0 = *(const uint4*)chunk_ptr(cb, 0);
+    if (has(1)) reg1 = *(const uint4*)chunk_ptr(cb, 1);
+    if (has(2)) reg2 = *(const uint4*)chunk_ptr(cb, 2);
+    if (has(3)) reg3 = *(const uint4*)chunk_ptr(cb, 3);
+    if (has(4)) reg4 = *(const uint4*)chunk_ptr(cb, 4);
     for (int tb = cb; tb < ce; tb += kTile) {
       __syncthreads();
-#pragma unroll
-      for (int i = 0; i < CPT; ++i) {
+      auto put = [&](int i, const uint4& v) {
         const int ch = tid + i * NT;
-        if (ch < kTile * CPR) *(uint4*)(kv + (ch / CPR) * KPD + (ch % CPR) * 8) = reg[i];
-      }
+        *(uint4*)(kv + (ch / CPR) * KPD + (ch % CPR) * 8) = v;
+      };
+      if (has(0)) put(0, reg0);
+      if (has(1)) put(1, reg1);
+      if (has(2)) put(2, reg2);
+      if (has(3)) put(3, reg3);
+      if (has(4)) put(4, reg4);
       __syncthreads();
-      if (tb + kTile < ce) fetch(tb + kTile);
+      if (tb + kTile < ce) {
+        if (has(0)) reg0 = *(const uint4*)chunk_ptr(tb + kTile, 0);
+        if (has(1)) reg1 = *(const uint4*)chunk_ptr(tb + kTile, 1);
+        if (has(2)) reg2 = *(const uint4*)chunk_ptr(tb + kTile, 2);
+        if (has(3)) reg3 = *(const uint4*)chunk_ptr(tb + kTile, 3);
+        if (has(4)) reg4 = *(const uint4*)chunk_ptr(tb + kTile, 4);
+      }
 
-    // S^T[row][head] for the tile's 32 rows and the wave's 16 heads.
-    f32x4 st[2];
+      // S^T for rows 16*dh .. 16*dh+15 and the wave's 16 heads.
+      f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      st[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int s0 = 0; s0 < NS; s0 += 4) {
+        bf16x8 a4[4];
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const bf16x8 a = *(const bf16x8*)(kv + (mt * 16 + c) * KPD + s * 32 + g * 8);
-        st[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[s], st[mt], 0, 0, 0);
+        for (int u = 0; u < 4; ++u)
+          if (s0 + u < NS) a4[u] = *(const bf16x8*)(kv + (dh * 16 + c) * KPD + (s0 + u) * 32 + g * 8);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (s0 + u < NS) st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a4[u], qf[s0 + u], st, 0, 0, 0);
       }
-    }
-    // Lane (g, c) holds head c's scores of rows 4g+i (tile half 0) and 16+4g+i (half 1).
-    float x[8];
-    float tmax = -INFINITY;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+      for (int i = 0; i < 4; ++i) s_sc[hg][(dh * 16 + 4 * g + i) * SP + c] = st[i];
+      __syncthreads();
+      // Lane (g, c) takes head c's scores of rows 4g+i and 16+4g+i.
+      float x[8];
+      float tmax = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = mt * 16 + 4 * g + i;
-        const bool live = tb + r < ce && s_ptr[tb - cb + r] != nullptr;
-        const float v = live ? st[mt][i] * d.attn_scale_log2 : -INFINITY;
-        x[mt * 4 + i] = v;
-        tmax = fmaxf(tmax, v);
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = mt * 16 + 4 * g + i;
+          const float v = s_live[tb - cb + r] ? s_sc[hg][r * SP + c] * d.attn_scale_log2 : -INFINITY;
+          x[mt * 4 + i] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      tmax = max_rows(tmax);
+      // Lazy rescaling: the reference max m moves (and O, l are rescaled) only
+      // when a head's scores exceed it by more than 2^8, so exp2(x - m) stays
+      // <= 256 and the rescale of O is rare.
+      if (m == -INFINITY) {
+        m = tmax;
+      } else if (__ballot(tmax > m + 8.f)) {
+        const float m_new = fmaxf(m, tmax);
+        const float alpha = exp2f(m - m_new);
+        l *= alpha;
+#pragma unroll
+        for (int n = 0; n < NO; ++n) {
+          acc[n][0] *= alpha;
+          acc[n][1] *= alpha;
+          acc[n][2] *= alpha;
+          acc[n][3] *= alpha;
+        }
+        m = m_new;
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    // Lazy rescaling: the reference max m moves (and O, l are rescaled) only
-    // when a head's scores exceed it by more than 2^8, so exp2(x - m) stays
-    // <= 256 and the 128-register rescale of O is rare.
-    if (m == -INFINITY) {
-      m = tmax;
-    } else if (__ballot(tmax > m + 8.f)) {
-      const float m_new = fmaxf(m, tmax);
-      const float alpha = exp2f(m - m_new);
-      l *= alpha;
-#pragma unroll
-      for (int n = 0; n < NO; ++n) {
-        acc[n][0] *= alpha;
-        acc[n][1] *= alpha;
-        acc[n][2] *= alpha;
-        acc[n][3] *= alpha;
-      }
-      m = m_new;
-    }
-    float p[8];
-    float psum = 0.f;
-    if (m != -INFINITY) {
+      float p[8];
+      float psum = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        p[i] = exp2f(x[i] - m);
+        p[i] = m == -INFINITY ? 0.f : exp2f(x[i] - m);
         psum += p[i];
       }
-    } else {
+      psum = sum_rows(psum);
+      l += psum;
+      const bf16x8 pf = pack8(p);
+      // O^T[dv][h] += V^T[dv][rows] P^T[rows][h] over this wave's value half.
 #pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = 0.f;
-    }
-    psum += __shfl_xor(psum, 16, 64);
-    psum += __shfl_xor(psum, 32, 64);
-    l += psum;
-    const bf16x8 pf = pack8(p);
-#pragma unroll
-    for (int n = 0; n < NO; ++n) {
-      const uint16_t* base = kv + (4 * g + (c >> 2)) * KPD + n * 16 + 4 * (c & 3);
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 16 * KPD));
-      const i16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), pf, acc[n], 0, 0, 0);
-    }
+      for (int n = 0; n < NO; ++n) {
+        const uint16_t* base = kv + (4 * g + (c >> 2)) * KPD + dh * DVH + n * 16 + 4 * (c & 3);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 16 * KPD));
+        const i16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), pf, acc[n], 0, 0, 0);
+      }
     }
   }
 
@@ -212,7 +246,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(KDims d, int splits, cons
       const float lf = l * exp2f(m - mf) + (sinks ? exp2f(sink2 - mf) : 0.f);
       f = lf > 0.f ? exp2f(m - mf) / lf : 0.f;
     }
-    uint16_t* orow = out + ((size_t)row * d.H + h) * DV + 4 * g;
+    uint16_t* orow = out + ((size_t)row * d.H + h) * DV + dh * DVH + 4 * g;
 #pragma unroll
     for (int n = 0; n < NO; ++n) {
       uint2 v;
@@ -223,8 +257,8 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(KDims d, int splits, cons
   } else {
     float* pr = part + (((size_t)split * d.B * d.L + row) * d.H + h) * (DV + 2);
 #pragma unroll
-    for (int n = 0; n < NO; ++n) *(f32x4*)(pr + n * 16 + 4 * g) = acc[n];
-    if (g == 0) {
+    for (int n = 0; n < NO; ++n) *(f32x4*)(pr + dh * DVH + n * 16 + 4 * g) = acc[n];
+    if (g == 0 && dh == 0) {
       pr[DV] = m;
       pr[DV + 1] = l;
     }
@@ -250,9 +284,7 @@ __global__ __launch_bounds__(128) void k_attn_merge(KDims d, int splits, const f
     const float m = s < splits ? p0[s * stride + d.Dv] : -INFINITY;
     const float l = s < splits ? p0[s * stride + d.Dv + 1] : 0.f;
     const float sink2 = sinks ? sinks[h] * kLog2e : -INFINITY;
-    float mf = m;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mf = fmaxf(mf, __shfl_xor(mf, o, 64));
+    float mf = wave_max(m);
     mf = fmaxf(mf, sink2);
     const float wgt = (mf == -INFINITY || m == -INFINITY) ? 0.f : exp2f(m - mf);
     float lf = wave_sum(l * wgt);
@@ -315,8 +347,7 @@ __global__ __launch_bounds__(256) void k_attn_valu(KDims d, const T* __restrict_
     s_x[e] = x;
     mx = fmaxf(mx, x);
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  mx = wave_max(mx);
   if (lane_id() == 0) s_red[wave_id()] = mx;
   __syncthreads();
   mx = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
@@ -351,7 +382,7 @@ template <int DK, int DV>
 hipError_t launch_mfma(const KDims& d, const void* q, const void* local_kv, const void* pooled_kv, const int* I,
                        const float* sinks, const int* t0, void* out, float* partial, int splits, hipStream_t st) {
   const dim3 grid(splits, d.B * d.L, d.H / 64);
-  hipLaunchKernelGGL((k_attn_mfma<DK, DV, 4>), grid, dim3(256), 0, st, d, splits, (const uint16_t*)q,
+  hipLaunchKernelGGL((k_attn_mfma<DK, DV, 4>), grid, dim3(512), 0, st, d, splits, (const uint16_t*)q,
                      (const uint16_t*)local_kv, (const uint16_t*)pooled_kv, I, sinks, t0, (uint16_t*)out, partial);
   return hipGetLastError();
 }

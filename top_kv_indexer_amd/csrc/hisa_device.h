@@ -41,23 +41,89 @@ __device__ __forceinline__ uint32_t score_key(float f) {
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 __device__ __forceinline__ int wave_id() { return (int)(threadIdx.x >> 6); }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+// Cross-lane reductions in registers (no LDS traffic).  Lane l = 16*g + c:
+// the 16 lanes of a row share g.  DPP quad_perm / row mirrors combine lanes
+// within a row; the gfx950 permlane swaps exchange whole rows (xor 16, xor 32).
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  // rows outside ROW_MASK and invalid source lanes read 0
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+// Sum over aligned groups of `span` lanes within a row (span 1, 2, 4, 8, 16).
+__device__ __forceinline__ float sum_span(float v, int span) {
+  if (span >= 2) v += dpp_f<kDppXor1>(v);
+  if (span >= 4) v += dpp_f<kDppXor2>(v);
+  if (span >= 8) v += dpp_f<kDppHalfMirror>(v);
+  if (span >= 16) v += dpp_f<kDppMirror>(v);
   return v;
 }
+__device__ __forceinline__ float sum_row16(float v) {
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  return v + dpp_f<kDppMirror>(v);
+}
+__device__ __forceinline__ float max_row16(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  return fmaxf(v, dpp_f<kDppMirror>(v));
+}
+__device__ __forceinline__ float min_row16(float v) {
+  v = fminf(v, dpp_f<kDppXor1>(v));
+  v = fminf(v, dpp_f<kDppXor2>(v));
+  v = fminf(v, dpp_f<kDppHalfMirror>(v));
+  return fminf(v, dpp_f<kDppMirror>(v));
+}
+// Sum / max over the four rows (lanes c, c+16, c+32, c+48).
+__device__ __forceinline__ float sum_rows(float v) {
+  u32x2 p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(p.x) + __uint_as_float(p.y);
+  p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p.x) + __uint_as_float(p.y);
+}
+__device__ __forceinline__ float max_rows(float v) {
+  u32x2 p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(p.x), __uint_as_float(p.y));
+  p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p.x), __uint_as_float(p.y));
+}
+__device__ __forceinline__ float min_rows(float v) {
+  u32x2 p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fminf(__uint_as_float(p.x), __uint_as_float(p.y));
+  p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fminf(__uint_as_float(p.x), __uint_as_float(p.y));
+}
+__device__ __forceinline__ float wave_sum(float v) { return sum_rows(sum_row16(v)); }
+__device__ __forceinline__ float wave_max(float v) { return max_rows(max_row16(v)); }
+__device__ __forceinline__ float wave_min(float v) { return min_rows(min_row16(v)); }
 __device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += (int)dpp_u<kDppXor1>((uint32_t)v);
+  v += (int)dpp_u<kDppXor2>((uint32_t)v);
+  v += (int)dpp_u<kDppHalfMirror>((uint32_t)v);
+  v += (int)dpp_u<kDppMirror>((uint32_t)v);
+  u32x2 p = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+  v = (int)(p.x + p.y);
+  p = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+  return (int)(p.x + p.y);
 }
+// Inclusive prefix sum over the 64 lanes: row-local shifts 1, 2, 4, 8, then
+// row 15 -> rows 1 and 3, row 31 -> rows 2 and 3.
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t t = __shfl_up(v, o, 64);
-    if (lane >= o) v += t;
-  }
+  v += dpp_u<0x111>(v);
+  v += dpp_u<0x112>(v);
+  v += dpp_u<0x114>(v);
+  v += dpp_u<0x118>(v);
+  v += dpp_u<0x142, 0xA>(v);
+  v += dpp_u<0x143, 0xC>(v);
   return v;
 }
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
@@ -217,6 +283,160 @@ __device__ void block_topk(int n, int k, KeyF key, EmitF emit, TopkSmem& sm) {
     eq_run += __popcll(em);
     sel_run += __popcll(sm_);
   }
+}
+
+// Shared memory of block_topk_scores.
+struct TopkScoresSmem {
+  TopkSmem radix;             // fallback
+  float red[4][16];           // per-wave partials: min, max, masked count
+  int info[8];
+  float cand_s[256];
+  int cand_i[256];
+};
+
+constexpr int kTopkBins = 2048;
+
+// Top-k of n float scores (larger first, equal scores keep the lowest index;
+// kNeg marks masked entries, which rank below every real score), emitting
+// slots 0..k-1 in ascending index order like block_topk.  Scores are bucketed
+// linearly over [min, max] of the real scores into 2048 bins; everything above
+// the bin that holds the k-th score is selected, and the few entries inside
+// that bin are ranked exactly.  Falls back to the radix select when that bin
+// holds more than 256 entries (heavy ties) or the scores are degenerate.
+template <int NT, class ScoreF, class EmitF>
+__device__ void block_topk_scores(int n, int k, ScoreF score, EmitF emit, TopkScoresSmem& sm) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
+  if (k <= 0) return;
+  auto key_of = [&](int i) { return score_key(score(i)); };
+  if (k >= n) {
+    block_topk<NT>(n, k, key_of, emit, sm.radix);
+    return;
+  }
+  // 1. range of the real scores and the masked count
+  float lo = INFINITY, hi = -INFINITY;
+  int nmask = 0;
+  for (int i = tid; i < n; i += NT) {
+    const float v = score(i);
+    if (v <= -1e29f) ++nmask;
+    else {
+      lo = fminf(lo, v);
+      hi = fmaxf(hi, v);
+    }
+  }
+  lo = wave_min(lo);
+  hi = wave_max(hi);
+  nmask = wave_sum_i(nmask);
+  if (lane == 0) {
+    sm.red[0][wv] = lo;
+    sm.red[1][wv] = hi;
+    sm.red[2][wv] = (float)nmask;
+  }
+  for (int i = tid; i < kTopkBins; i += NT) sm.radix.hist[i] = 0;
+  __syncthreads();
+  lo = INFINITY;
+  hi = -INFINITY;
+  nmask = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    lo = fminf(lo, sm.red[0][w]);
+    hi = fmaxf(hi, sm.red[1][w]);
+    nmask += (int)sm.red[2][w];
+  }
+  const int nreal = n - nmask;
+  const float scale = (float)kTopkBins / (hi - lo) * 0.999999f;
+  if (nreal < k || !(hi > lo) || !(scale < 1e30f) || !(hi - lo < 1e30f)) {
+    // masked entries at the boundary, or a degenerate range
+    block_topk<NT>(n, k, key_of, emit, sm.radix);
+    return;
+  }
+  // 2. histogram of real scores over linear bins (monotone in the score)
+  auto bin_of = [&](float v) { return v <= -1e29f ? -1 : min(kTopkBins - 1, (int)((v - lo) * scale)); };
+  for (int i = tid; i < n; i += NT) {
+    const int bn = bin_of(score(i));
+    if (bn >= 0) atomicAdd(&sm.radix.hist[bn], 1u);
+  }
+  __syncthreads();
+  // 3. bin holding the k-th score, counted from the top
+  const int bpt = kTopkBins / NT;
+  uint32_t local = 0;
+  for (int i = 0; i < bpt; ++i) local += sm.radix.hist[kTopkBins - 1 - (tid * bpt + i)];
+  uint32_t tot;
+  const uint32_t above = block_excl_scan<NT>(local, sm.radix.wtot[0], &tot);
+  if (above < (uint32_t)k && above + local >= (uint32_t)k) {
+    uint32_t acc = above;
+    for (int i = 0; i < bpt; ++i) {
+      const int bn = kTopkBins - 1 - (tid * bpt + i);
+      const uint32_t cnt = sm.radix.hist[bn];
+      if (acc + cnt >= (uint32_t)k) {
+        sm.info[0] = bn;
+        sm.info[1] = (int)acc;
+        sm.info[2] = (int)cnt;
+        break;
+      }
+      acc += cnt;
+    }
+  }
+  if (tid == 0) sm.info[3] = 0;
+  __syncthreads();
+  const int T = sm.info[0];
+  const int r = k - sm.info[1];  // entries still needed from bin T
+  const int m = sm.info[2];      // entries in bin T
+  if (m > 256) {
+    block_topk<NT>(n, k, key_of, emit, sm.radix);
+    return;
+  }
+  // 4. gather bin T's entries and find the r-th best of them (score desc, index asc)
+  for (int i = tid; i < n; i += NT) {
+    const float v = score(i);
+    if (bin_of(v) == T) {
+      const int slot = atomicAdd(&sm.info[3], 1);
+      sm.cand_s[slot] = v;
+      sm.cand_i[slot] = i;
+    }
+  }
+  __syncthreads();
+  if (tid < m) {
+    const uint32_t kt = score_key(sm.cand_s[tid]);
+    const int it = sm.cand_i[tid];
+    int rank = 0;
+    for (int j = 0; j < m; ++j) {
+      const uint32_t kj = score_key(sm.cand_s[j]);
+      rank += (kj > kt) || (kj == kt && sm.cand_i[j] < it);
+    }
+    if (rank == r - 1) {
+      sm.info[4] = (int)kt;
+      sm.info[5] = it;
+    }
+  }
+  __syncthreads();
+  const uint32_t kthr = (uint32_t)sm.info[4];
+  const int ithr = sm.info[5];
+  auto selected = [&](int i) {
+    const float v = score(i);
+    const int bn = bin_of(v);
+    if (bn != T) return bn > T;
+    const uint32_t kv = score_key(v);
+    return kv > kthr || (kv == kthr && i <= ithr);
+  };
+  // 5. emission in index order (wave w scans a contiguous range)
+  const int chunk = (((n + NW - 1) / NW) + 63) & ~63;
+  const int lo_i = min(n, wv * chunk), hi_i = min(n, lo_i + chunk);
+  int cnt = 0;
+  for (int i = lo_i + lane; i < hi_i; i += 64) cnt += selected(i);
+  cnt = wave_sum_i(cnt);
+  if (lane == 0) sm.radix.wtot[0][wv] = (uint32_t)cnt;
+  __syncthreads();
+  int run = 0;
+  for (int w = 0; w < wv; ++w) run += (int)sm.radix.wtot[0][w];
+  for (int base = lo_i; base < hi_i; base += 64) {
+    const int i = base + lane;
+    const bool sel = i < hi_i && selected(i);
+    const uint64_t bm = __ballot(sel);
+    if (sel) emit(run + lanes_below(bm), i);
+    run += __popcll(bm);
+  }
+  __syncthreads();
 }
 
 }  // namespace hisa

@@ -32,123 +32,97 @@ __device__ __forceinline__ bf16x8 ldg8(const uint16_t* p) { return *(const bf16x
 
 // ------------------------------------------------------------------ decode scan
 
-// Consecutive 64-row tiles of one sequence (bf16, H_i = 64, D_i = 128,
-// index_block | 64).  The query goes to LDS once; the next tile's keys are
-// fetched into registers while the current tile is scored.
-__global__ __launch_bounds__(256) void k_decode_scan_mfma(KDims d, int tiles_per_wg,
-                                                          const uint16_t* __restrict__ q_idx,
-                                                          const float* __restrict__ w,
-                                                          const uint16_t* __restrict__ keys,
-                                                          const int* __restrict__ t0,
-                                                          float* __restrict__ fscore,
-                                                          float* __restrict__ cscore) {
+// One wave per 64-row slab of one sequence (bf16, H_i = 64, D_i = 128,
+// index_block | 64).  The wave's four 16-row tiles of keys go straight from
+// HBM into registers (all 16 loads in flight at once), and MFMA gives
+// D[h][row] = q_h . key_row.  Fine score of a row: sum_h relu(D) w_eff.
+// Coarse score of a block: the block mean is linear, so q_h . rep_beta is the
+// mean of D[h][row] over the block's rows; it is summed across the lanes that
+// hold those rows, then relu'd and weighted.  No LDS and no barriers.
+__global__ __launch_bounds__(64) void k_decode_scan_mfma(KDims d, const uint16_t* __restrict__ q_idx,
+                                                         const float* __restrict__ w,
+                                                         const uint16_t* __restrict__ keys,
+                                                         const int* __restrict__ t0,
+                                                         float* __restrict__ fscore,
+                                                         float* __restrict__ cscore) {
   const int b = blockIdx.y;
+  const int row0 = blockIdx.x * 64;
   const SeqInfo si = seq_info(d, t0[b]);
-  const int tile_begin = blockIdx.x * tiles_per_wg;
-  if (!si.ok || si.path == PATH_DENSE || tile_begin * 64 >= si.Np) return;
-  const int tile_end = min(tile_begin + tiles_per_wg, (si.Np + 63) / 64);
-  __shared__ __align__(16) uint16_t sk[64 * KP];
-  __shared__ __align__(16) uint16_t sq[64 * KP];
-  __shared__ float s_weff[64];
-  __shared__ float s_rep[128];
-  __shared__ float s_red[4];
-  const int tid = threadIdx.x;
-  const uint16_t* qb = q_idx + (size_t)b * d.L * 64 * 128;
-  const uint16_t* kb = keys + (size_t)b * d.Np_cap * 128;
-  uint4 kreg[4];
-  auto fetch = [&](int tile) {
-    const int row0 = tile * 64;
+  if (!si.ok || si.path == PATH_DENSE || row0 >= si.Np) return;
+  const int lane = threadIdx.x, g = lane >> 4, c = lane & 15;
+  // Keys: lane (g, c) of tile t holds row row0 + 16t + c, dims [32g, 32g + 32)
+  // (the k order of q below matches).  Rows past Np read row Np - 1 instead.
+  const uint16_t* kb = keys + (size_t)b * d.Np_cap * 128 + g * 32;
+  bf16x8 kf[4][4];
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int ch = tid + it * 256;
-      const int r = ch >> 4, seg = (ch & 15) * 8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (row0 + r < si.Np) v = *(const uint4*)(kb + (size_t)(row0 + r) * 128 + seg);
-      kreg[it] = v;
-    }
-  };
-  {
-    uint4 qreg[4];
+  for (int t = 0; t < 4; ++t) {
+    const int r = min(row0 + t * 16 + c, si.Np - 1);
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int ch = tid + it * 256;
-      qreg[it] = *(const uint4*)(qb + (ch >> 4) * 128 + (ch & 15) * 8);
-    }
-    fetch(tile_begin);
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int ch = tid + it * 256;
-      *(uint4*)(sq + (ch >> 4) * KP + (ch & 15) * 8) = qreg[it];
-    }
-    if (tid < 64) s_weff[tid] = w[(size_t)b * d.L * 64 + tid] * d.w_scale;
+    for (int s = 0; s < 4; ++s) kf[t][s] = ldg8(kb + (size_t)r * 128 + s * 8);
   }
-  const int lane = lane_id(), wv = wave_id(), g = lane >> 4, c = lane & 15;
+  const uint16_t* qrow = q_idx + (size_t)b * d.L * 64 * 128;
+  bf16x8 qf[4][4];
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qf[ht][s] = ldg8(qrow + (ht * 16 + c) * 128 + g * 32 + s * 8);
+  float wl[4][4];
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wl[ht][i] = w[(size_t)b * d.L * 64 + ht * 16 + 4 * g + i] * d.w_scale;
+  const bool hisa_path = si.path == PATH_HISA;
   const int bsz = d.index_block;
-  const int h = tid >> 2, part = tid & 3;
-  float qr[32];
-  float wh = 0.f;
-  for (int tile = tile_begin; tile < tile_end; ++tile) {
-    const int row0 = tile * 64;
-    const int nrows = min(64, si.Np - row0);
-    __syncthreads();
+  float bs[4][4];  // running block sums of D over rows, per (head tile, i)
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int ch = tid + it * 256;
-      *(uint4*)(sk + (ch >> 4) * KP + (ch & 15) * 8) = kreg[it];
-    }
-    __syncthreads();
-    if (tile + 1 < tile_end) fetch(tile + 1);
-    if (tile == tile_begin && si.path == PATH_HISA) {
+  for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
-      for (int e = 0; e < 32; ++e) qr[e] = bf2f(sq[h * KP + part * 32 + e]);
-      wh = s_weff[h];
-    }
-
-    // Fine scores of the tile's rows: wave wv takes rows 16wv..16wv+15.
-    // A = q (rows = heads), B = keys^T (columns = rows); D[h][row].
+    for (int i = 0; i < 4; ++i) bs[ht][i] = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
     f32x4 acc[4];
 #pragma unroll
-    for (int ht = 0; ht < 4; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ht = 0; ht < 4; ++ht) {
+      acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const bf16x8 kf = lds8(sk + (wv * 16 + c) * KP + s * 32 + g * 8);
-#pragma unroll
-      for (int ht = 0; ht < 4; ++ht) {
-        const bf16x8 qf = lds8(sq + (ht * 16 + c) * KP + s * 32 + g * 8);
-        acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf, kf, acc[ht], 0, 0, 0);
-      }
+      for (int s = 0; s < 4; ++s) acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ht][s], kf[t][s], acc[ht], 0, 0, 0);
     }
     float v = 0.f;
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v += fmaxf(acc[ht][i], 0.f) * s_weff[ht * 16 + 4 * g + i];
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    if (g == 0 && wv * 16 + c < nrows) fscore[(size_t)b * d.Np_cap + row0 + wv * 16 + c] = v;
-
-    if (si.path != PATH_HISA) continue;
-    // Block means and coarse scores of the blocks inside this tile.
-    for (int blk = 0; blk < 64 / bsz; ++blk) {
-      const int beta = row0 / bsz + blk;
-      if (beta >= si.nb) break;
-      if (tid < 128) {
-        float s = 0.f;
-        for (int r = 0; r < bsz; ++r) s += bf2f(sk[(blk * bsz + r) * KP + tid]);
-        s_rep[tid] = s / (float)bsz;
-      }
-      __syncthreads();
-      float dot = 0.f;
+      for (int i = 0; i < 4; ++i) v += fmaxf(acc[ht][i], 0.f) * wl[ht][i];
+    v = sum_rows(v);
+    const int r = row0 + t * 16 + c;
+    if (g == 0 && r < si.Np) fscore[(size_t)b * d.Np_cap + r] = v;
+    if (!hisa_path) continue;
+    // Block sums: rows of a block are consecutive lanes c (and tiles t).
 #pragma unroll
-      for (int e = 0; e < 32; ++e) dot += qr[e] * s_rep[part * 32 + e];
-      dot += __shfl_xor(dot, 1, 64);
-      dot += __shfl_xor(dot, 2, 64);
-      float contrib = part == 0 ? fmaxf(dot, 0.f) * wh : 0.f;
-      contrib = wave_sum(contrib);
-      if (lane == 0) s_red[wv] = contrib;
-      __syncthreads();
-      if (tid == 0) cscore[(size_t)b * d.nb_cap + beta] = s_red[0] + s_red[1] + s_red[2] + s_red[3];
-    }
+    for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bs[ht][i] += acc[ht][i];
+    const int span = bsz < 16 ? bsz : 16;  // rows of one block inside this tile
+    if (bsz > 16 && ((t + 1) * 16) % bsz != 0) continue;
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        bs[ht][i] = sum_span(bs[ht][i], span);
+      }
+    float cv = 0.f;
+    const float inv_b = 1.f / (float)bsz;
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        cv += fmaxf(bs[ht][i] * inv_b, 0.f) * wl[ht][i];
+        bs[ht][i] = 0.f;
+      }
+    cv = sum_rows(cv);
+    // lane c holds the sum of the block containing its row
+    const int beta = (row0 + t * 16 + c) / bsz;
+    const bool first_lane = bsz >= 16 ? c == 0 : (c % bsz) == 0;
+    if (g == 0 && first_lane && beta < si.nb) cscore[(size_t)b * d.nb_cap + beta] = cv;
   }
 }
 
@@ -176,8 +150,7 @@ __global__ __launch_bounds__(256) void k_decode_scan_valu(KDims d, const T* __re
   for (int h = 0; h < d.H_i; ++h) {
     float dot = 0.f;
     for (int e = part; e < d.D_i; e += 4) dot += ldf(qb + (size_t)h * d.D_i + e) * ldf(kp + e);
-    dot += __shfl_xor(dot, 1, 64);
-    dot += __shfl_xor(dot, 2, 64);
+    dot = sum_span(dot, 4);
     tot += fmaxf(dot, 0.f) * (wb[h] * d.w_scale);
   }
   if (live && part == 0) fscore[(size_t)b * d.Np_cap + p] = tot;
@@ -211,11 +184,11 @@ constexpr int kMaxKeep = 1024;
 constexpr int kSelectThreads = 256;
 constexpr int kSelectLdsCap = 8192;    // keys staged in LDS per pass (32 KiB)
 
-// Stages n keys into LDS (when they fit) and returns whether it did.
+// Stages n scores into LDS (when they fit) and returns whether it did.
 template <class SrcF>
-__device__ __forceinline__ bool stage_keys(uint32_t* s_keys, int n, int cap, SrcF src) {
+__device__ __forceinline__ bool stage_scores(float* s_sc, int n, int cap, SrcF src) {
   if (n > cap) return false;
-  for (int i = threadIdx.x; i < n; i += 4 * kSelectThreads) {  // 4 loads in flight per thread
+  for (int i = threadIdx.x; i < n; i += 4 * kSelectThreads) {
     float v[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -225,15 +198,15 @@ __device__ __forceinline__ bool stage_keys(uint32_t* s_keys, int n, int cap, Src
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int ii = i + u * kSelectThreads;
-      if (ii < n) s_keys[ii] = score_key(v[u]);
+      if (ii < n) s_sc[ii] = v[u];
     }
   }
   __syncthreads();
   return true;
 }
 
-// One sequence per workgroup (one wave): gate, then the flat top-k or the
-// coarse top-Kb + fine top-k, reading the scan's scores through LDS.
+// One sequence per workgroup: gate, then the flat top-k or the coarse top-Kb
+// + fine top-k, reading the scan's scores through LDS.
 __global__ __launch_bounds__(kSelectThreads) void k_decode_select(KDims d, int lds_cap,
                                                                   const float* __restrict__ fscore,
                                                                   const float* __restrict__ cscore,
@@ -242,8 +215,8 @@ __global__ __launch_bounds__(kSelectThreads) void k_decode_select(KDims d, int l
   constexpr int NT = kSelectThreads;
   const int b = blockIdx.x, tid = threadIdx.x;
   const SeqInfo si = seq_info(d, t0[b]);
-  extern __shared__ uint32_t s_keys[];
-  __shared__ TopkSmem sm;
+  extern __shared__ float s_sc[];
+  __shared__ TopkScoresSmem sm;
   __shared__ int s_blk[kMaxKeep];
   int* Ib = I + (size_t)b * d.topk;
   const bool dense = si.path == PATH_DENSE;
@@ -259,26 +232,26 @@ __global__ __launch_bounds__(kSelectThreads) void k_decode_select(KDims d, int l
   const float* fs = fscore + (size_t)b * d.Np_cap;
   if (si.path == PATH_FLAT) {
     auto emit = [&](int slot, int i) { Ib[slot] = i; };
-    if (stage_keys(s_keys, si.Np, lds_cap, [&](int i) { return fs[i]; }))
-      block_topk<NT>(si.Np, si.k, [&](int i) { return s_keys[i]; }, emit, sm);
+    if (stage_scores(s_sc, si.Np, lds_cap, [&](int i) { return fs[i]; }))
+      block_topk_scores<NT>(si.Np, si.k, [&](int i) { return s_sc[i]; }, emit, sm);
     else
-      block_topk<NT>(si.Np, si.k, [&](int i) { return score_key(fs[i]); }, emit, sm);
+      block_topk_scores<NT>(si.Np, si.k, [&](int i) { return fs[i]; }, emit, sm);
     return;
   }
   const float* cs = cscore + (size_t)b * d.nb_cap;
   auto emit_blk = [&](int slot, int i) { s_blk[slot] = i; };
-  if (stage_keys(s_keys, si.nb, lds_cap, [&](int i) { return cs[i]; }))
-    block_topk<NT>(si.nb, si.Kb, [&](int i) { return s_keys[i]; }, emit_blk, sm);
+  if (stage_scores(s_sc, si.nb, lds_cap, [&](int i) { return cs[i]; }))
+    block_topk_scores<NT>(si.nb, si.Kb, [&](int i) { return s_sc[i]; }, emit_blk, sm);
   else
-    block_topk<NT>(si.nb, si.Kb, [&](int i) { return score_key(cs[i]); }, emit_blk, sm);
+    block_topk_scores<NT>(si.nb, si.Kb, [&](int i) { return cs[i]; }, emit_blk, sm);
   __syncthreads();
   if (top_blk)
     for (int i = tid; i < si.Kb; i += NT) top_blk[(size_t)b * d.index_keep + i] = s_blk[i];
   const int bsz = d.index_block;
   const int C = si.Kb * bsz;
   auto pos = [&](int c) { return s_blk[c / bsz] * bsz + c % bsz; };
-  stage_keys(s_keys, C, lds_cap, [&](int c) { return fs[pos(c)]; });  // C <= keep * b <= the LDS cap
-  block_topk<NT>(C, si.k, [&](int c) { return s_keys[c]; }, [&](int slot, int c) { Ib[slot] = pos(c); }, sm);
+  stage_scores(s_sc, C, lds_cap, [&](int c) { return fs[pos(c)]; });  // C <= keep * b <= the LDS cap
+  block_topk_scores<NT>(C, si.k, [&](int c) { return s_sc[c]; }, [&](int slot, int c) { Ib[slot] = pos(c); }, sm);
 }
 
 // ------------------------------------------------------------------ batched path
@@ -372,8 +345,7 @@ __global__ __launch_bounds__(256) void k_coarse_mfma(KDims d, int all_paths, con
       for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
         for (int i = 0; i < 4; ++i) x += fmaxf(acc[ht][i], 0.f) * wl[ht][i];
-      x += __shfl_xor(x, 16, 64);
-      x += __shfl_xor(x, 32, 64);
+      x = sum_rows(x);
       if (beta < si.nb && beta * d.index_block < valid) v = x;
     }
     if (g == 0 && beta < d.nb_cap) out[beta] = v;
@@ -442,7 +414,7 @@ __global__ __launch_bounds__(256) void k_fine_mfma(KDims d, int lds_floats, cons
   int* blkrow = top_blk ? top_blk + ((size_t)b * d.L + j) * d.index_keep : nullptr;
   if (!fine_prologue(d, si, b, j, Irow, blkrow, path)) return;
   extern __shared__ float s_fs[];  // max(nb_cap, C) floats: coarse scores, then fine scores
-  __shared__ TopkSmem sm;
+  __shared__ TopkScoresSmem sm;
   __shared__ int s_blk[kMaxKeep];
   const int valid = visible(t0[b] + j, d.ratio, si.Np);
   const float* cs = cscore + ((size_t)b * d.L + j) * d.nb_cap;
@@ -450,9 +422,9 @@ __global__ __launch_bounds__(256) void k_fine_mfma(KDims d, int lds_floats, cons
   if (si.nb <= lds_floats) {
     for (int i = threadIdx.x; i < si.nb; i += 256) s_fs[i] = cs[i];
     __syncthreads();
-    block_topk<256>(si.nb, si.Kb, [&](int i) { return score_key(s_fs[i]); }, emit_blk, sm);
+    block_topk_scores<256>(si.nb, si.Kb, [&](int i) { return s_fs[i]; }, emit_blk, sm);
   } else {
-    block_topk<256>(si.nb, si.Kb, [&](int i) { return score_key(cs[i]); }, emit_blk, sm);
+    block_topk_scores<256>(si.nb, si.Kb, [&](int i) { return cs[i]; }, emit_blk, sm);
   }
   __syncthreads();
   if (blkrow)
@@ -508,13 +480,12 @@ __global__ __launch_bounds__(256) void k_fine_mfma(KDims d, int lds_floats, cons
     for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
       for (int i = 0; i < 4; ++i) x += fmaxf(acc[ht][i], 0.f) * wl[ht][i];
-    x += __shfl_xor(x, 16, 64);
-    x += __shfl_xor(x, 32, 64);
+    x = sum_rows(x);
     if (g == 0 && cidx < C) s_fs[cidx] = pos < valid ? x : kNeg;
   }
   __syncthreads();
-  block_topk<256>(C, si.k, [&](int cc) { return score_key(s_fs[cc]); },
-                  [&](int slot, int cc) { Irow[slot] = s_blk[cc / bsz] * bsz + cc % bsz; }, sm);
+  block_topk_scores<256>(C, si.k, [&](int cc) { return s_fs[cc]; },
+                         [&](int slot, int cc) { Irow[slot] = s_blk[cc / bsz] * bsz + cc % bsz; }, sm);
 }
 
 template <typename T>
@@ -528,12 +499,12 @@ __global__ __launch_bounds__(256) void k_fine_valu(KDims d, const T* __restrict_
   int* blkrow = top_blk ? top_blk + ((size_t)b * d.L + j) * d.index_keep : nullptr;
   if (!fine_prologue(d, si, b, j, Irow, blkrow, path)) return;
   extern __shared__ float s_fs[];
-  __shared__ TopkSmem sm;
+  __shared__ TopkScoresSmem sm;
   __shared__ int s_blk[kMaxKeep];
   const int valid = visible(t0[b] + j, d.ratio, si.Np);
   const float* cs = cscore + ((size_t)b * d.L + j) * d.nb_cap;
-  block_topk<256>(si.nb, si.Kb, [&](int i) { return score_key(cs[i]); },
-                  [&](int slot, int i) { s_blk[slot] = i; }, sm);
+  block_topk_scores<256>(si.nb, si.Kb, [&](int i) { return cs[i]; },
+                         [&](int slot, int i) { s_blk[slot] = i; }, sm);
   __syncthreads();
   if (blkrow)
     for (int i = threadIdx.x; i < si.Kb; i += 256) blkrow[i] = s_blk[i];
@@ -553,8 +524,8 @@ __global__ __launch_bounds__(256) void k_fine_valu(KDims d, const T* __restrict_
     s_fs[cc] = pos < valid ? tot : kNeg;
   }
   __syncthreads();
-  block_topk<256>(C, si.k, [&](int cc) { return score_key(s_fs[cc]); },
-                  [&](int slot, int cc) { Irow[slot] = s_blk[cc / bsz] * bsz + cc % bsz; }, sm);
+  block_topk_scores<256>(C, si.k, [&](int cc) { return s_fs[cc]; },
+                         [&](int slot, int cc) { Irow[slot] = s_blk[cc / bsz] * bsz + cc % bsz; }, sm);
 }
 
 // ------------------------------------------------------------------ flat scan
@@ -638,8 +609,7 @@ __global__ __launch_bounds__(256) void k_flat_scores_mfma(KDims d, int kc, const
           for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
             for (int i = 0; i < 4; ++i) v += fmaxf(acc[ht][i], 0.f) * wl[rr][ht][i];
-          v += __shfl_xor(v, 16, 64);
-          v += __shfl_xor(v, 32, 64);
+          v = sum_rows(v);
           if (p < Vr[rr]) x = v;
         }
         if (g == 0 && p < p_end) srow[p] = x;
@@ -695,17 +665,16 @@ __global__ __launch_bounds__(kTopkRowsThreads) void k_topk_rows(KDims d, int lds
       if (i >= si.k) Irow[i] = -1;
   }
   if (!act) return;
-  extern __shared__ uint32_t s_keys[];
-  __shared__ TopkSmem sm;
+  extern __shared__ float s_row[];
+  __shared__ TopkScoresSmem sm;
   const float* srow = scores + ((size_t)b * d.L + j) * d.Np_cap;
+  auto emit = [&](int slot, int i) { Irow[slot] = i; };
   if (si.Np <= lds_cap) {
-    for (int i = threadIdx.x; i < si.Np; i += kTopkRowsThreads) s_keys[i] = score_key(srow[i]);
+    for (int i = threadIdx.x; i < si.Np; i += kTopkRowsThreads) s_row[i] = srow[i];
     __syncthreads();
-    block_topk<kTopkRowsThreads>(si.Np, si.k, [&](int i) { return s_keys[i]; },
-                                 [&](int slot, int i) { Irow[slot] = i; }, sm);
+    block_topk_scores<kTopkRowsThreads>(si.Np, si.k, [&](int i) { return s_row[i]; }, emit, sm);
   } else {
-    block_topk<kTopkRowsThreads>(si.Np, si.k, [&](int i) { return score_key(srow[i]); },
-                                 [&](int slot, int i) { Irow[slot] = i; }, sm);
+    block_topk_scores<kTopkRowsThreads>(si.Np, si.k, [&](int i) { return srow[i]; }, emit, sm);
   }
 }
 
@@ -719,11 +688,8 @@ hipError_t launch_decode_scan(const KDims& d, bool bf16, const void* q_idx, cons
                               const int* t0, float* fscore, float* cscore, hipStream_t st) {
   const dim3 grid(cdiv(d.Np_cap, 64), d.B);
   if (idx_mfma_ok(d, bf16)) {
-    // Enough tiles per workgroup to keep ~2048 workgroups in the grid.
-    const long long tiles = (long long)d.B * cdiv(d.Np_cap, 64);
-    const int per = (int)std::min(16LL, std::max(1LL, tiles / 2048));
-    hipLaunchKernelGGL(k_decode_scan_mfma, dim3(cdiv(cdiv(d.Np_cap, 64), per), d.B), dim3(256), 0, st, d, per,
-                       (const uint16_t*)q_idx, w, (const uint16_t*)keys, t0, fscore, cscore);
+    hipLaunchKernelGGL(k_decode_scan_mfma, grid, dim3(64), 0, st, d, (const uint16_t*)q_idx, w,
+                       (const uint16_t*)keys, t0, fscore, cscore);
   }
   else if (bf16)
     hipLaunchKernelGGL(k_decode_scan_valu<uint16_t>, grid, dim3(256), 0, st, d, (const uint16_t*)q_idx, w,
@@ -737,7 +703,7 @@ hipError_t launch_decode_scan(const KDims& d, bool bf16, const void* q_idx, cons
 hipError_t launch_decode_select(const KDims& d, const float* fscore, const float* cscore, const int* t0, int* I,
                                 int* top_blk, int* path, hipStream_t st) {
   const int cap = std::min(kSelectLdsCap, std::max({d.nb_cap, d.index_keep * d.index_block, d.Np_cap}));
-  hipLaunchKernelGGL(k_decode_select, dim3(d.B), dim3(kSelectThreads), (size_t)cap * sizeof(uint32_t), st, d, cap,
+  hipLaunchKernelGGL(k_decode_select, dim3(d.B), dim3(kSelectThreads), (size_t)cap * sizeof(float), st, d, cap,
                      fscore, cscore, t0, I, top_blk, path);
   return hipGetLastError();
 }
@@ -809,11 +775,11 @@ hipError_t launch_flat_scores(const KDims& d, bool bf16, const void* q_idx, cons
 hipError_t launch_topk_rows(const KDims& d, const float* scores, const int* t0, int* I, int* path, hipStream_t st) {
   constexpr int kLdsCap = 32768;  // 128 KiB of keys
   const int cap = d.Np_cap <= kLdsCap ? d.Np_cap : 0;
-  const size_t lds = (size_t)cap * sizeof(uint32_t);
+  const size_t lds = (size_t)cap * sizeof(float);
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)k_topk_rows, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       kLdsCap * (int)sizeof(uint32_t));
+                                       kLdsCap * (int)sizeof(float));
     if (e != hipSuccess) return e;
     attr_set = true;
   }

@@ -72,11 +72,13 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
   constexpr int NS = DK / 32;   // MFMA k-steps of S
   constexpr int DVH = DV / 2;   // value columns per wave
   constexpr int NO = DVH / 16;  // MFMA column tiles of O^T per wave
-  constexpr int CPR = DK / 8;   // 16-byte chunks per KV row
-  constexpr int TCH = kTile * CPR;
-  constexpr int CPT = (TCH + NT - 1) / NT;  // chunks per thread per tile
   constexpr int SP = 17;        // padded pitch (floats) of the score exchange rows
-  __shared__ __align__(16) uint16_t kv[kTile * KPD];
+  static_assert(kChunk % NT == 0, "chunk rows must split evenly over the threads");
+  static_assert(kTile % NW == 0, "tile rows must split evenly over the waves");
+  static_assert(DK >= 512 && DK <= 1024 && DK % 8 == 0, "a KV row is one or two 64-lane 16-byte loads");
+  // Two LDS tiles: rows of the next tile stream in (global -> LDS, no
+  // registers) while the current one is computed.
+  __shared__ __align__(16) uint16_t kv[2][kTile * KPD];
   __shared__ float s_sc[NHG][kTile * SP];
   // Row list of the current chunk: element offset of each row (>= 0 into
   // pooled_kv, ~offset into local_kv) and whether the row is live.  Dead rows
@@ -89,11 +91,23 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
   const int tid = threadIdx.x, lane = lane_id(), wv = wave_id(), g = lane >> 4, c = lane & 15;
   const int hg = wv >> 1, dh = wv & 1;
   const int h0 = blockIdx.z * 16 * NHG + hg * 16;
+  // Row list: the kI pooled ids of I first, then `window` local slots (slot
+  // s holds position s_lo + s while s < n_loc).  The split geometry does not
+  // depend on t0, so the index loads below go out before t0 arrives.
+  const int n_geo = d.kI + d.window;
+  const int per = ((n_geo + splits - 1) / splits + kTile - 1) / kTile * kTile;
+  const int begin = min(n_geo, split * per), end = min(n_geo, begin + per);
+  const int* Irow = I + (size_t)row * d.kI;
+  constexpr int IPT = kChunk / NT;
+  int idpre[IPT];
+#pragma unroll
+  for (int u = 0; u < IPT; ++u) {
+    const int e = begin + tid + u * NT;
+    idpre[u] = (e < end && e < d.kI) ? Irow[e] : -1;
+  }
   const int T0 = t0[b];
   const RowPlan rp = row_plan(d, T0, j);
-  const int per = (((rp.n_list + splits - 1) / splits) + kTile - 1) / kTile * kTile;
-  const int begin = split * per, end = min(rp.n_list, begin + per);
-  // a row every sequence with a non-empty list may read
+  // a row every sequence with a live row may read (dead rows point at it)
   const long long dummy = rp.n_loc > 0 ? ~(((long long)b * d.Wl_cap + (rp.s_lo - rp.ls)) * DK)
                                        : (long long)b * d.Np_cap * DK;
   const bool any_row = rp.n_loc > 0 || rp.V > 0;
@@ -108,66 +122,56 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
 #pragma unroll
   for (int n = 0; n < NO; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int* Irow = I + (size_t)row * d.kI;
   for (int cb = any_row ? begin : end; cb < end; cb += kChunk) {
     const int ce = min(end, cb + kChunk);
+    const int cpad = cb + (ce - cb + kTile - 1) / kTile * kTile;
     __syncthreads();
-    for (int e = cb + tid; e < cb + ((ce - cb + kTile - 1) / kTile) * kTile; e += NT) {
-      long long off = dummy;
-      bool live = false;
-      if (e < ce) {
-        if (e < rp.n_loc) {
-          off = ~(((long long)b * d.Wl_cap + (rp.s_lo - rp.ls + e)) * DK);
-          live = true;
-        } else {
-          const int id = Irow[e - rp.n_loc];
-          if (id >= 0 && id < rp.V) {
-            off = ((long long)b * d.Np_cap + id) * DK;
+#pragma unroll
+    for (int u = 0; u < IPT; ++u) {
+      const int e = cb + tid + u * NT;
+      if (e < cpad) {
+        long long off = dummy;
+        bool live = false;
+        if (e < ce) {
+          if (e < d.kI) {
+            const int id = cb == begin ? idpre[u] : Irow[e];
+            if (id >= 0 && id < rp.V) {
+              off = ((long long)b * d.Np_cap + id) * DK;
+              live = true;
+            }
+          } else if (e - d.kI < rp.n_loc) {
+            off = ~(((long long)b * d.Wl_cap + (rp.s_lo - rp.ls + e - d.kI)) * DK);
             live = true;
           }
         }
+        s_off[e - cb] = off;
+        s_live[e - cb] = live;
       }
-      s_off[e - cb] = off;
-      s_live[e - cb] = live;
     }
     __syncthreads();
-    // Tiles of 32 rows; the next tile's rows are fetched into registers while
-    // the current one is computed from LDS.
-    // Each thread moves CPT 16-byte chunks per tile; chunk i of the thread is
-    // row (tid + i*NT) / CPR, column segment (tid + i*NT) % CPR.
-    uint4 reg0, reg1, reg2, reg3, reg4;
-    static_assert(CPT <= 5, "tile fetch holds at most 5 chunks per thread");
-    auto chunk_ptr = [&](int tb, int i) -> const uint16_t* {
-      const int ch = tid + i * NT;
-      const long long off = s_off[tb - cb + ch / CPR];
-      const uint16_t* p = off >= 0 ? pooled_kv + off : local_kv + ~off;
-      return p + (ch % CPR) * 8;
-    };
-    auto has = [&](int i) { return i < CPT && (TCH % NT == 0 || tid + i * NT < TCH); };
-    if (has(0)) reg0 = *(const uint4*)chunk_ptr(cb, 0);
-    if (has(1)) reg1 = *(const uint4*)chunk_ptr(cb, 1);
-    if (has(2)) reg2 = *(const uint4*)chunk_ptr(cb, 2);
-    if (has(3)) reg3 = *(const uint4*)chunk_ptr(cb, 3);
-    if (has(4)) reg4 = *(const uint4*)chunk_ptr(cb, 4);
-    for (int tb = cb; tb < ce; tb += kTile) {
-      __syncthreads();
-      auto put = [&](int i, const uint4& v) {
-        const int ch = tid + i * NT;
-        *(uint4*)(kv + (ch / CPR) * KPD + (ch % CPR) * 8) = v;
-      };
-      if (has(0)) put(0, reg0);
-      if (has(1)) put(1, reg1);
-      if (has(2)) put(2, reg2);
-      if (has(3)) put(3, reg3);
-      if (has(4)) put(4, reg4);
-      __syncthreads();
-      if (tb + kTile < ce) {
-        if (has(0)) reg0 = *(const uint4*)chunk_ptr(tb + kTile, 0);
-        if (has(1)) reg1 = *(const uint4*)chunk_ptr(tb + kTile, 1);
-        if (has(2)) reg2 = *(const uint4*)chunk_ptr(tb + kTile, 2);
-        if (has(3)) reg3 = *(const uint4*)chunk_ptr(tb + kTile, 3);
-        if (has(4)) reg4 = *(const uint4*)chunk_ptr(tb + kTile, 4);
+    // Tiles of 32 rows in two LDS buffers.  Wave w moves rows w, w+NW, ...:
+    // one 64-lane 16-byte global->LDS load per 512 columns of a row.
+    auto load_tile = [&](int tb, int buf) {
+#pragma unroll
+      for (int rr = 0; rr < kTile / NW; ++rr) {
+        const int r = wv + rr * NW;
+        const long long off = s_off[tb - cb + r];
+        const uint16_t* src = (off >= 0 ? pooled_kv + off : local_kv + ~off) + lane * 8;
+        uint16_t* dst = &kv[buf][r * KPD];
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                         (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+        if (DK > 512 && lane < DK / 8 - 64)
+          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + 512),
+                                           (__attribute__((address_space(3))) void*)(dst + 512), 16, 0, 0);
       }
+    };
+    load_tile(cb, 0);
+    for (int tb = cb, it = 0; tb < ce; tb += kTile, ++it) {
+      const int buf = it & 1;
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile `it` have landed
+      __syncthreads();                // ... and every wave's; buffer buf^1 is free
+      if (tb + kTile < ce) load_tile(tb + kTile, buf ^ 1);
+      const uint16_t* kvb = kv[buf];
 
       // S^T for rows 16*dh .. 16*dh+15 and the wave's 16 heads.
       f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -176,7 +180,7 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
         bf16x8 a4[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          if (s0 + u < NS) a4[u] = *(const bf16x8*)(kv + (dh * 16 + c) * KPD + (s0 + u) * 32 + g * 8);
+          if (s0 + u < NS) a4[u] = *(const bf16x8*)(kvb + (dh * 16 + c) * KPD + (s0 + u) * 32 + g * 8);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
           if (s0 + u < NS) st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a4[u], qf[s0 + u], st, 0, 0, 0);
@@ -228,7 +232,7 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
       // O^T[dv][h] += V^T[dv][rows] P^T[rows][h] over this wave's value half.
 #pragma unroll
       for (int n = 0; n < NO; ++n) {
-        const uint16_t* base = kv + (4 * g + (c >> 2)) * KPD + dh * DVH + n * 16 + 4 * (c & 3);
+        const uint16_t* base = kvb + (4 * g + (c >> 2)) * KPD + dh * DVH + n * 16 + 4 * (c & 3);
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 16 * KPD));
         const i16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -381,9 +385,15 @@ __global__ __launch_bounds__(256) void k_attn_valu(KDims d, const T* __restrict_
 template <int DK, int DV>
 hipError_t launch_mfma(const KDims& d, const void* q, const void* local_kv, const void* pooled_kv, const int* I,
                        const float* sinks, const int* t0, void* out, float* partial, int splits, hipStream_t st) {
-  const dim3 grid(splits, d.B * d.L, d.H / 64);
-  hipLaunchKernelGGL((k_attn_mfma<DK, DV, 4>), grid, dim3(512), 0, st, d, splits, (const uint16_t*)q,
-                     (const uint16_t*)local_kv, (const uint16_t*)pooled_kv, I, sinks, t0, (uint16_t*)out, partial);
+  if (attn_small_groups(d)) {
+    const dim3 grid(splits, d.B * d.L, d.H / 16);
+    hipLaunchKernelGGL((k_attn_mfma<DK, DV, 1>), grid, dim3(128), 0, st, d, splits, (const uint16_t*)q,
+                       (const uint16_t*)local_kv, (const uint16_t*)pooled_kv, I, sinks, t0, (uint16_t*)out, partial);
+  } else {
+    const dim3 grid(splits, d.B * d.L, d.H / 64);
+    hipLaunchKernelGGL((k_attn_mfma<DK, DV, 4>), grid, dim3(512), 0, st, d, splits, (const uint16_t*)q,
+                       (const uint16_t*)local_kv, (const uint16_t*)pooled_kv, I, sinks, t0, (uint16_t*)out, partial);
+  }
   return hipGetLastError();
 }
 
@@ -397,10 +407,14 @@ bool attn_generic_ok(const KDims& d) {
   return d.Dk <= kGenericMaxDk && (long long)d.window + d.kI <= kGenericMaxList;
 }
 
+// A handful of query rows: 16 heads per workgroup (more, smaller workgroups);
+// otherwise 64 heads per workgroup, so each gathered row feeds 4x more heads.
+bool attn_small_groups(const KDims& d) { return (long long)d.B * d.L * (d.H / 64) <= 8; }
+
 int attn_splits(const KDims& d, bool bf16) {
   if (!attn_mfma_ok(d, bf16)) return 1;
-  const long long work = (long long)d.B * d.L * (d.H / 64);
-  const long long n_max = (long long)min(d.window, d.Wl_cap) + d.kI;
+  const long long work = (long long)d.B * d.L * (d.H / (attn_small_groups(d) ? 16 : 64));
+  const long long n_max = (long long)d.window + d.kI;
   // at least two 32-row tiles per split, so that fetching overlaps compute
   const long long max_splits = std::max(1LL, (n_max + 2 * kTile - 1) / (2 * kTile));
   long long want = (256 + work - 1) / work;

@@ -44,6 +44,7 @@ hipError_t launch_topk_rows(const KDims& d, const float* scores, const int* t0, 
 int attn_splits(const KDims& d, bool bf16);
 bool attn_mfma_ok(const KDims& d, bool bf16);
 bool attn_generic_ok(const KDims& d);
+bool attn_small_groups(const KDims& d);
 size_t attn_partial_bytes(const KDims& d, int splits);
 hipError_t launch_attention(const KDims& d, bool bf16, const void* q, const void* local_kv,
                             const void* pooled_kv, const int* I, const float* sinks,

@@ -294,8 +294,6 @@ struct TopkScoresSmem {
   int cand_i[256];
 };
 
-constexpr int kTopkBins = 2048;
-
 // Top-k of n float scores (larger first, equal scores keep the lowest index;
 // kNeg marks masked entries, which rank below every real score), emitting
 // slots 0..k-1 in ascending index order like block_topk.  Scores are bucketed
@@ -303,8 +301,9 @@ constexpr int kTopkBins = 2048;
 // the bin that holds the k-th score is selected, and the few entries inside
 // that bin are ranked exactly.  Falls back to the radix select when that bin
 // holds more than 256 entries (heavy ties) or the scores are degenerate.
-template <int NT, class ScoreF, class EmitF>
+template <int NT, class ScoreF, class EmitF, int kTopkBins = 2048>
 __device__ void block_topk_scores(int n, int k, ScoreF score, EmitF emit, TopkScoresSmem& sm) {
+  static_assert(kTopkBins <= 2048 && kTopkBins % NT == 0, "bins must fit the histogram and split over threads");
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
   if (k <= 0) return;
@@ -396,9 +395,9 @@ __device__ void block_topk_scores(int n, int k, ScoreF score, EmitF emit, TopkSc
     }
   }
   __syncthreads();
-  if (tid < m) {
-    const uint32_t kt = score_key(sm.cand_s[tid]);
-    const int it = sm.cand_i[tid];
+  for (int t = tid; t < m; t += NT) {
+    const uint32_t kt = score_key(sm.cand_s[t]);
+    const int it = sm.cand_i[t];
     int rank = 0;
     for (int j = 0; j < m; ++j) {
       const uint32_t kj = score_key(sm.cand_s[j]);

@@ -182,6 +182,7 @@ __global__ __launch_bounds__(256) void k_decode_scan_valu(KDims d, const T* __re
 
 constexpr int kMaxKeep = 1024;
 constexpr int kSelectThreads = 256;
+constexpr int kSelectBins = 2048;
 constexpr int kSelectLdsCap = 8192;    // keys staged in LDS per pass (32 KiB)
 
 // Stages n scores into LDS (when they fit) and returns whether it did.
@@ -203,6 +204,11 @@ __device__ __forceinline__ bool stage_scores(float* s_sc, int n, int cap, SrcF s
   }
   __syncthreads();
   return true;
+}
+
+template <class ScoreF, class EmitF>
+__device__ __forceinline__ void select_topk(int n, int k, ScoreF score, EmitF emit, TopkScoresSmem& sm) {
+  block_topk_scores<kSelectThreads, ScoreF, EmitF, kSelectBins>(n, k, score, emit, sm);
 }
 
 // One sequence per workgroup: gate, then the flat top-k or the coarse top-Kb
@@ -233,17 +239,17 @@ __global__ __launch_bounds__(kSelectThreads) void k_decode_select(KDims d, int l
   if (si.path == PATH_FLAT) {
     auto emit = [&](int slot, int i) { Ib[slot] = i; };
     if (stage_scores(s_sc, si.Np, lds_cap, [&](int i) { return fs[i]; }))
-      block_topk_scores<NT>(si.Np, si.k, [&](int i) { return s_sc[i]; }, emit, sm);
+      select_topk(si.Np, si.k, [&](int i) { return s_sc[i]; }, emit, sm);
     else
-      block_topk_scores<NT>(si.Np, si.k, [&](int i) { return fs[i]; }, emit, sm);
+      select_topk(si.Np, si.k, [&](int i) { return fs[i]; }, emit, sm);
     return;
   }
   const float* cs = cscore + (size_t)b * d.nb_cap;
   auto emit_blk = [&](int slot, int i) { s_blk[slot] = i; };
   if (stage_scores(s_sc, si.nb, lds_cap, [&](int i) { return cs[i]; }))
-    block_topk_scores<NT>(si.nb, si.Kb, [&](int i) { return s_sc[i]; }, emit_blk, sm);
+    select_topk(si.nb, si.Kb, [&](int i) { return s_sc[i]; }, emit_blk, sm);
   else
-    block_topk_scores<NT>(si.nb, si.Kb, [&](int i) { return cs[i]; }, emit_blk, sm);
+    select_topk(si.nb, si.Kb, [&](int i) { return cs[i]; }, emit_blk, sm);
   __syncthreads();
   if (top_blk)
     for (int i = tid; i < si.Kb; i += NT) top_blk[(size_t)b * d.index_keep + i] = s_blk[i];
@@ -251,7 +257,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_decode_select(KDims d, int l
   const int C = si.Kb * bsz;
   auto pos = [&](int c) { return s_blk[c / bsz] * bsz + c % bsz; };
   stage_scores(s_sc, C, lds_cap, [&](int c) { return fs[pos(c)]; });  // C <= keep * b <= the LDS cap
-  block_topk_scores<NT>(C, si.k, [&](int c) { return s_sc[c]; }, [&](int slot, int c) { Ib[slot] = pos(c); }, sm);
+  select_topk(C, si.k, [&](int c) { return s_sc[c]; }, [&](int slot, int c) { Ib[slot] = pos(c); }, sm);
 }
 
 // ------------------------------------------------------------------ batched path

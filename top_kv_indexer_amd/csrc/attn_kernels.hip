@@ -26,7 +26,6 @@ typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kTile = 32;
-constexpr int kChunk = 512;  // rows of the row list staged in LDS at a time
 
 struct RowPlan {
   bool ok;
@@ -50,15 +49,34 @@ __device__ __forceinline__ RowPlan row_plan(const KDims& d, int T0, int j) {
 __device__ __forceinline__ bf16x8 pack8(const float (&p)[8]) {
   u32x4 u;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) u[k] = (uint32_t)f2bf(p[2 * k]) | ((uint32_t)f2bf(p[2 * k + 1]) << 16);
+  for (int k = 0; k < 4; ++k) u[k] = pack_bf16x2(p[2 * k], p[2 * k + 1]);
   return __builtin_bit_cast(bf16x8, u);
 }
 
-// One workgroup = NHG groups of 16 heads x 2 halves of the value width = 2*NHG
-// waves.  Wave (hg, dh) computes the scores of rows 16*dh..16*dh+15 of each
-// 32-row tile for its 16 heads; the pair exchanges them through LDS, both run
-// the same online softmax over the 32 rows, and each accumulates O for its
-// half of the value columns (16 heads x DV/2 = DV/8 accumulator registers).
+// One workgroup = HW = 16*NHG heads of one query row (one KV split), NW =
+// 2*NHG waves; KV tiles of 32 rows stream through a ring of NBUF LDS slots.
+// Step t of the tile loop:
+//  - scores of tile t+1: wave (hg, dh) computes S^T for rows 16*dh..+15 and
+//    heads 16*hg..+15 (16x16x32 MFMA, A = K rows from LDS, B = q in
+//    registers) into one of two score buffers;
+//  - softmax of tile t (scores stored in step t-1): wave w owns heads
+//    8w..8w+7 (m, l and the lazy rescale) and stores P in bf16 plus each
+//    head's rescale factor;
+//  - values of tile t: wave w accumulates O^T for every head of the group
+//    over its own 16-column tiles of the value width (A = V^T from the gfx950
+//    transposing LDS read, B = P^T), so each value column is read from LDS
+//    once;
+//  - the rows of tile t+NBUF-1 start streaming from global memory into LDS
+//    (issued through inline assembly, so LDS reads of the other slots never
+//    wait for them).
+// LDS rows are a whole number of 256-byte bank rounds with the first 64
+// 16-byte chunks XOR-swizzled by the row (slot position p holds chunk
+// p ^ sw(row)), so the K reads (16 rows x one chunk) and the transposing V
+// reads (8 rows x two chunks per half-wave) hit distinct banks.  Row
+// bookkeeping is resolved once per chunk of up to 1024 rows: the fetching
+// wave keeps the element offsets in registers (entry RPW*t + r of a wave
+// lives in lane (RPW*t + r) % 64, register (RPW*t + r) / 64), and a 32-bit
+// liveness mask per tile sits in LDS.
 template <int DK, int DV, int NHG>
 __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, const uint16_t* __restrict__ q,
                                                          const uint16_t* __restrict__ local_kv,
@@ -68,29 +86,41 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
                                                          float* __restrict__ part) {
   constexpr int NW = NHG * 2;
   constexpr int NT = NW * 64;
-  constexpr int KPD = DK + 16;  // LDS row pitch: 8 banks of skew per row for the transposing reads
-  constexpr int NS = DK / 32;   // MFMA k-steps of S
-  constexpr int DVH = DV / 2;   // value columns per wave
-  constexpr int NO = DVH / 16;  // MFMA column tiles of O^T per wave
-  constexpr int SP = 17;        // padded pitch (floats) of the score exchange rows
-  static_assert(kChunk % NT == 0, "chunk rows must split evenly over the threads");
-  static_assert(kTile % NW == 0, "tile rows must split evenly over the waves");
-  static_assert(DK >= 512 && DK <= 1024 && DK % 8 == 0, "a KV row is one or two 64-lane 16-byte loads");
-  // Two LDS tiles: rows of the next tile stream in (global -> LDS, no
-  // registers) while the current one is computed.
-  __shared__ __align__(16) uint16_t kv[2][kTile * KPD];
-  __shared__ float s_sc[NHG][kTile * SP];
-  // Row list of the current chunk: element offset of each row (>= 0 into
-  // pooled_kv, ~offset into local_kv) and whether the row is live.  Dead rows
-  // point at a readable row of the same sequence and are masked in the softmax.
-  __shared__ long long s_off[kChunk];
-  __shared__ unsigned char s_live[kChunk];
+  constexpr int HW = NHG * 16;          // heads of the workgroup
+  constexpr int KPD = (DK * 2 + 255) / 256 * 128;  // LDS row pitch (elements)
+  constexpr int NBUF = DK <= 512 ? 4 : 3;          // ring slots
+  constexpr int NS = DK / 32;           // MFMA k-steps of S
+  constexpr int NDT_ALL = DV / 16;      // 16-column tiles of the value width
+  constexpr int NDT = (NDT_ALL + NW - 1) / NW;  // ... per wave (tiles w, w+NW, ...)
+  constexpr int SSP = kTile + 4;        // score rows (floats) per head in LDS
+  constexpr int PSP = kTile;            // P entries (bf16) per head in LDS
+  constexpr int RPW = kTile / NW;       // rows of a tile each wave fetches
+  constexpr int CH = 1024;              // rows of the row list resolved at a time
+  constexpr int NTILE = CH / kTile;
+  constexpr int IPT = CH / NT;          // chunk rows per thread
+  constexpr int LPT = RPW * (DK > 512 ? 2 : 1);  // vector-memory loads per tile per wave
+  constexpr int KW = 8;                 // K fragments in flight
+  static_assert(NTILE * RPW == 64 * IPT, "a wave's row offsets of one chunk fill whole registers");
+  static_assert(HW == 8 * NW, "each wave owns the softmax of 8 heads");
+  static_assert(DV % 16 == 0 && DK >= 512 && DK <= 1024 && DK % 32 == 0, "shape");
+  __shared__ __align__(16) uint16_t kv[NBUF][kTile * KPD];
+  __shared__ __align__(16) float s_sc[2][HW * SSP];
+  __shared__ __align__(16) uint16_t s_p[HW * PSP];
+  __shared__ __align__(16) float s_alpha[HW];
+  __shared__ float s_ml[2][HW];
+  __shared__ uint32_t s_tmask[NTILE];
 
-  const int split = blockIdx.x, row = blockIdx.y;
+  const int split = blockIdx.x;
+  // consecutive query rows go to the same XCD (workgroups are dealt to the 8
+  // XCDs round-robin), so rows sharing their local window share its L2
+  const int row = [](int y, int n) {
+    const int x = y & 7, qn = n >> 3, rn = n & 7;
+    return x * qn + min(x, rn) + (y >> 3);
+  }(blockIdx.y, d.B * d.L);
   const int b = row / d.L, j = row % d.L;
   const int tid = threadIdx.x, lane = lane_id(), wv = wave_id(), g = lane >> 4, c = lane & 15;
   const int hg = wv >> 1, dh = wv & 1;
-  const int h0 = blockIdx.z * 16 * NHG + hg * 16;
+  const int hbase = blockIdx.z * HW;
   // Row list: the kI pooled ids of I first, then `window` local slots (slot
   // s holds position s_lo + s while s < n_loc).  The split geometry does not
   // depend on t0, so the index loads below go out before t0 arrives.
@@ -98,12 +128,17 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
   const int per = ((n_geo + splits - 1) / splits + kTile - 1) / kTile * kTile;
   const int begin = min(n_geo, split * per), end = min(n_geo, begin + per);
   const int* Irow = I + (size_t)row * d.kI;
-  constexpr int IPT = kChunk / NT;
-  int idpre[IPT];
+  auto ident_row = [&](int u) { return tid + u * NT; };
+  auto fetch_row = [&](int u) {  // entry 64u + lane = RPW*t + r -> tile t, wave-row r
+    const int e = 64 * u + lane;
+    return (e / RPW) * kTile + wv + NW * (e % RPW);
+  };
+  int id_a[IPT], id_f[IPT];
 #pragma unroll
   for (int u = 0; u < IPT; ++u) {
-    const int e = begin + tid + u * NT;
-    idpre[u] = (e < end && e < d.kI) ? Irow[e] : -1;
+    const int ea = begin + ident_row(u), ef = begin + fetch_row(u);
+    id_a[u] = (ea < end && ea < d.kI) ? Irow[ea] : -1;
+    id_f[u] = (ef < end && ef < d.kI) ? Irow[ef] : -1;
   }
   const int T0 = t0[b];
   const RowPlan rp = row_plan(d, T0, j);
@@ -111,160 +146,263 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
   const long long dummy = rp.n_loc > 0 ? ~(((long long)b * d.Wl_cap + (rp.s_lo - rp.ls)) * DK)
                                        : (long long)b * d.Np_cap * DK;
   const bool any_row = rp.n_loc > 0 || rp.V > 0;
+  auto sw = [](int r) { return ((r & 7) << 1) | ((r >> 3) & 1); };
+  // liveness and element offset (>= 0 into pooled_kv, ~offset into local_kv)
+  // of list entry e (given its pooled id when e < kI)
+  auto resolve = [&](int e, int id, long long& off) -> bool {
+    off = dummy;
+    if (e >= end) return false;
+    if (e < d.kI) {
+      if (id < 0 || id >= rp.V) return false;
+      off = ((long long)b * d.Np_cap + id) * DK;
+      return true;
+    }
+    if (e - d.kI >= rp.n_loc) return false;
+    off = ~(((long long)b * d.Wl_cap + (rp.s_lo - rp.ls + e - d.kI)) * DK);
+    return true;
+  };
 
+  // scores: this wave's 16 heads of q as the B operand
   bf16x8 qf[NS];
-  const uint16_t* qrow = q + ((size_t)row * d.H + h0 + c) * DK + g * 8;
+  {
+    const uint16_t* qrow = q + ((size_t)row * d.H + hbase + hg * 16 + c) * DK + g * 8;
 #pragma unroll
-  for (int s = 0; s < NS; ++s) qf[s] = *(const bf16x8*)(qrow + s * 32);
-
+    for (int s = 0; s < NS; ++s) qf[s] = *(const bf16x8*)(qrow + s * 32);
+  }
+  // softmax: lane (hq, rq) = (lane >> 3, lane & 7) holds rows 4rq..4rq+3 of head 8*wv + hq
+  const int hq = lane >> 3, rq = lane & 7;
+  const int hs = 8 * wv + hq;
   float m = -INFINITY, l = 0.f;
-  f32x4 acc[NO];
+  const float scale = d.attn_scale_log2;
+  // values: O^T tiles (16 value columns x 16 heads) of every head tile
+  f32x4 acc[NDT][NHG];
 #pragma unroll
-  for (int n = 0; n < NO; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int n = 0; n < NDT; ++n)
+#pragma unroll
+    for (int ht = 0; ht < NHG; ++ht) acc[n][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // transposing V reads: lane (g, c) takes rows 4g + c/4 (+16) and columns
+  // 4*(c%4) .. +3 of a 16-column value tile
+  const int vrow = 4 * g + (c >> 2);
+  const int vsw = sw(vrow);  // rows vrow and vrow + 16 share the swizzle
+  auto vaddr = [&](int dt, int hi) {
+    const int ch = 2 * dt + ((c & 3) >> 1);
+    return (vrow + 16 * hi) * KPD + (ch < 64 ? ch ^ vsw : ch) * 8 + 4 * (c & 1);
+  };
 
-  for (int cb = any_row ? begin : end; cb < end; cb += kChunk) {
-    const int ce = min(end, cb + kChunk);
-    const int cpad = cb + (ce - cb + kTile - 1) / kTile * kTile;
-    __syncthreads();
+  for (int cb = any_row ? begin : end; cb < end; cb += CH) {
+    const int ce = min(end, cb + CH);
+    const int ntile = (ce - cb + kTile - 1) / kTile;
+    long long offs[IPT];
 #pragma unroll
     for (int u = 0; u < IPT; ++u) {
-      const int e = cb + tid + u * NT;
-      if (e < cpad) {
-        long long off = dummy;
-        bool live = false;
-        if (e < ce) {
-          if (e < d.kI) {
-            const int id = cb == begin ? idpre[u] : Irow[e];
-            if (id >= 0 && id < rp.V) {
-              off = ((long long)b * d.Np_cap + id) * DK;
-              live = true;
-            }
-          } else if (e - d.kI < rp.n_loc) {
-            off = ~(((long long)b * d.Wl_cap + (rp.s_lo - rp.ls + e - d.kI)) * DK);
-            live = true;
-          }
-        }
-        s_off[e - cb] = off;
-        s_live[e - cb] = live;
+      const int ef = cb + fetch_row(u);
+      const int id = cb == begin ? id_f[u] : (ef < end && ef < d.kI ? Irow[ef] : -1);
+      resolve(ef, id, offs[u]);
+    }
+    __syncthreads();  // the previous chunk is done with every slot and mask
+#pragma unroll
+    for (int u = 0; u < IPT; ++u) {
+      const int ea = cb + ident_row(u);
+      const int id = cb == begin ? id_a[u] : (ea < end && ea < d.kI ? Irow[ea] : -1);
+      long long unused;
+      const uint64_t live = __ballot(resolve(ea, id, unused));
+      if (lane == 0) {
+        const int t = (wv * 64 + u * NT) / kTile;
+        s_tmask[t] = (uint32_t)live;
+        s_tmask[t + 1] = (uint32_t)(live >> 32);
       }
     }
-    __syncthreads();
-    // Tiles of 32 rows in two LDS buffers.  Wave w moves rows w, w+NW, ...:
-    // one 64-lane 16-byte global->LDS load per 512 columns of a row.
-    auto load_tile = [&](int tb, int buf) {
+    auto load_tile = [&](int t, uint16_t* kvdst) {
 #pragma unroll
-      for (int rr = 0; rr < kTile / NW; ++rr) {
-        const int r = wv + rr * NW;
-        const long long off = s_off[tb - cb + r];
-        const uint16_t* src = (off >= 0 ? pooled_kv + off : local_kv + ~off) + lane * 8;
-        uint16_t* dst = &kv[buf][r * KPD];
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                         (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
-        if (DK > 512 && lane < DK / 8 - 64)
-          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + 512),
-                                           (__attribute__((address_space(3))) void*)(dst + 512), 16, 0, 0);
+      for (int r = 0; r < RPW; ++r) {
+        const int e = RPW * t + r;  // wave entry
+        const int reg = e >> 6, src_lane = e & 63;
+        long long o = offs[0];
+#pragma unroll
+        for (int u = 1; u < IPT; ++u) o = reg == u ? offs[u] : o;
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)o, src_lane);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(o >> 32), src_lane);
+        const long long off = (long long)(((uint64_t)hi << 32) | lo);
+        const int trow = wv + NW * r;
+        const uint16_t* src = off >= 0 ? pooled_kv + off : local_kv + ~off;
+        const uint32_t dst = lds_addr(kvdst + trow * KPD);
+        g2lds16(src + (lane ^ sw(trow)) * 8, dst);
+        if (DK > 512 && lane < DK / 8 - 64) g2lds16(src + 512 + lane * 8, dst + 1024);
       }
     };
-    load_tile(cb, 0);
-    for (int tb = cb, it = 0; tb < ce; tb += kTile, ++it) {
-      const int buf = it & 1;
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile `it` have landed
-      __syncthreads();                // ... and every wave's; buffer buf^1 is free
-      if (tb + kTile < ce) load_tile(tb + kTile, buf ^ 1);
-      const uint16_t* kvb = kv[buf];
-
-      // S^T for rows 16*dh .. 16*dh+15 and the wave's 16 heads.
+    auto load_k = [&](const uint16_t* kvb, int s) {  // k-step s of rows 16*dh + c
+      const int ch = 4 * s + g;
+      return *(const bf16x8*)(kvb + (dh * 16 + c) * KPD + (ch < 64 ? ch ^ sw(c) : ch) * 8);
+    };
+    // S^T of rows 16*dh.. for heads 16*hg.. into score buffer sb; the first
+    // KW fragments arrive in ka, the rest are fetched KW steps ahead
+    auto scores = [&](const uint16_t* kvb, bf16x8 (&ka)[KW], int sb) {
       f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s0 = 0; s0 < NS; s0 += 4) {
-        bf16x8 a4[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (s0 + u < NS) a4[u] = *(const bf16x8*)(kvb + (dh * 16 + c) * KPD + (s0 + u) * 32 + g * 8);
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (s0 + u < NS) st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a4[u], qf[s0 + u], st, 0, 0, 0);
+      for (int s = 0; s < NS; ++s) {
+        const bf16x8 a = ka[s % KW];
+        if (s + KW < NS) ka[s % KW] = load_k(kvb, s + KW);
+        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[s], st, 0, 0, 0);
       }
+      *(f32x4*)&s_sc[sb][(hg * 16 + c) * SSP + dh * 16 + 4 * g] = st;
+    };
+    // wait until at most `keep` tiles' loads of this wave are still in flight
+    auto wait_loads = [&](int keep) {
+      if (keep >= 2) __builtin_amdgcn_s_waitcnt((2 * LPT & 15) | ((2 * LPT >> 4) << 14) | 0x0F70);
+      else if (keep == 1) __builtin_amdgcn_s_waitcnt((LPT & 15) | ((LPT >> 4) << 14) | 0x0F70);
+      else __builtin_amdgcn_s_waitcnt(0x0F70);
+    };
+    auto step = [&](int t) {
+      const uint16_t* kvP = kv[t % NBUF];
+      const uint16_t* kvS = kv[(t + 1) % NBUF];
+      uint16_t* kvL = kv[(t + NBUF - 1) % NBUF];
+      // tile t+1 must have landed; tiles t+2 .. t+NBUF-2 may still stream in
+      wait_loads(min(ntile - 1, t + NBUF - 2) - (t + 1));
+      lds_sync();  // every wave's tile t+1, scores of tile t, and slot kvL are ready
+      if (t + NBUF - 1 < ntile) load_tile(t + NBUF - 1, kvL);
+      const uint32_t tmask = __builtin_amdgcn_readfirstlane(s_tmask[t]);
+      const bool more = t + 1 < ntile;
+      const f32x4 sv = *(const f32x4*)&s_sc[t & 1][hs * SSP + 4 * rq];
+      bf16x8 ka[KW];
+      if (more) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s_sc[hg][(dh * 16 + 4 * g + i) * SP + c] = st[i];
-      __syncthreads();
-      // Lane (g, c) takes head c's scores of rows 4g+i and 16+4g+i.
-      float x[8];
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+        for (int s = 0; s < KW; ++s) ka[s] = load_k(kvS, s);
+      }
+      if (more) scores(kvS, ka, (t + 1) & 1);
+      // softmax of head hs over rows 4rq..4rq+3 of tile t (8 lanes per head)
+      {
+        const uint32_t lbits = tmask >> (4 * rq);
+        float x[4];
+        float tmax = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = mt * 16 + 4 * g + i;
-          const float v = s_live[tb - cb + r] ? s_sc[hg][r * SP + c] * d.attn_scale_log2 : -INFINITY;
-          x[mt * 4 + i] = v;
-          tmax = fmaxf(tmax, v);
+          x[i] = ((lbits >> i) & 1u) ? sv[i] * scale : -INFINITY;
+          tmax = fmaxf(tmax, x[i]);
         }
-      tmax = max_rows(tmax);
-      // Lazy rescaling: the reference max m moves (and O, l are rescaled) only
-      // when a head's scores exceed it by more than 2^8, so exp2(x - m) stays
-      // <= 256 and the rescale of O is rare.
-      if (m == -INFINITY) {
-        m = tmax;
-      } else if (__ballot(tmax > m + 8.f)) {
-        const float m_new = fmaxf(m, tmax);
-        const float alpha = exp2f(m - m_new);
-        l *= alpha;
-#pragma unroll
-        for (int n = 0; n < NO; ++n) {
-          acc[n][0] *= alpha;
-          acc[n][1] *= alpha;
-          acc[n][2] *= alpha;
-          acc[n][3] *= alpha;
+        tmax = max_span8(tmax);
+        // Lazy rescaling: the reference max m moves (and O, l are rescaled)
+        // only when a head's scores exceed it by more than 2^8, so exp2(x - m)
+        // stays <= 256 and the rescale of O is rare.
+        float alpha = 1.f;
+        if (m == -INFINITY) {
+          m = tmax;
+        } else if (tmax > m + 8.f) {
+          const float m_new = fmaxf(m, tmax);
+          alpha = __builtin_amdgcn_exp2f(m - m_new);
+          l *= alpha;
+          m = m_new;
         }
-        m = m_new;
-      }
-      float p[8];
-      float psum = 0.f;
+        const float m_sub = m == -INFINITY ? 0.f : m;  // exp2(-inf) = 0 while a head has no live score
+        float p[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        p[i] = m == -INFINITY ? 0.f : exp2f(x[i] - m);
-        psum += p[i];
+        for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - m_sub);
+        l += sum_span(p[0] + p[1] + p[2] + p[3], 8);
+        // P^T operand order: head row of 32 entries, entry 8*gg + e holds
+        // tile row 16*(e/4) + 4*gg + e%4.
+        uint2 pk;
+        pk.x = pack_bf16x2(p[0], p[1]);
+        pk.y = pack_bf16x2(p[2], p[3]);
+        *(uint2*)&s_p[hs * PSP + (rq & 3) * 8 + (rq >> 2) * 4] = pk;
+        if (rq == 0) s_alpha[hs] = alpha;
       }
-      psum = sum_rows(psum);
-      l += psum;
-      const bf16x8 pf = pack8(p);
-      // O^T[dv][h] += V^T[dv][rows] P^T[rows][h] over this wave's value half.
+      lds_sync();
+      // O^T[dv][h] += V^T[dv][rows] P^T[rows][h] over this wave's value tiles
+      float al[NHG];
+      bool any = false;
 #pragma unroll
-      for (int n = 0; n < NO; ++n) {
-        const uint16_t* base = kvb + (4 * g + (c >> 2)) * KPD + dh * DVH + n * 16 + 4 * (c & 3);
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 16 * KPD));
-        const i16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), pf, acc[n], 0, 0, 0);
+      for (int ht = 0; ht < NHG; ++ht) {
+        al[ht] = s_alpha[ht * 16 + c];
+        any |= al[ht] != 1.f;
       }
+      bf16x8 pb[NHG];
+#pragma unroll
+      for (int ht = 0; ht < NHG; ++ht) pb[ht] = *(const bf16x8*)&s_p[(ht * 16 + c) * PSP + g * 8];
+      i16x4 va[NDT][2];
+#pragma unroll
+      for (int n = 0; n < NDT; ++n) {
+        const int dt = wv + NW * n;
+        if (NDT * NW == NDT_ALL || dt < NDT_ALL) {
+          va[n][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(kvP + vaddr(dt, 0)));
+          va[n][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(kvP + vaddr(dt, 1)));
+        }
+      }
+      if (__ballot(any)) {
+#pragma unroll
+        for (int n = 0; n < NDT; ++n)
+#pragma unroll
+          for (int ht = 0; ht < NHG; ++ht) {
+            acc[n][ht][0] *= al[ht];
+            acc[n][ht][1] *= al[ht];
+            acc[n][ht][2] *= al[ht];
+            acc[n][ht][3] *= al[ht];
+          }
+      }
+#pragma unroll
+      for (int n = 0; n < NDT; ++n) {
+        const int dt = wv + NW * n;
+        if (NDT * NW == NDT_ALL || dt < NDT_ALL) {
+          const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(va[n][0], va[n][1], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+          for (int ht = 0; ht < NHG; ++ht)
+            acc[n][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[ht], acc[n][ht], 0, 0, 0);
+        }
+      }
+    };
+    // prologue: tiles 0 .. NBUF-2 in flight, scores of tile 0
+#pragma unroll
+    for (int t = 0; t < NBUF - 1; ++t)
+      if (t < ntile) load_tile(t, kv[t]);
+    wait_loads(min(ntile, NBUF - 1) - 1);
+    lds_sync();
+    {
+      bf16x8 ka[KW];
+#pragma unroll
+      for (int s = 0; s < KW; ++s) ka[s] = load_k(kv[0], s);
+      scores(kv[0], ka, 0);
     }
+    for (int t = 0; t < ntile; ++t) step(t);
   }
 
-  const int h = h0 + c;
-  if (splits == 1) {
-    const float sink2 = sinks ? sinks[h] * kLog2e : -INFINITY;
-    const float mf = fmaxf(m, sink2);
-    float f = 0.f;
-    if (mf != -INFINITY) {
-      const float lf = l * exp2f(m - mf) + (sinks ? exp2f(sink2 - mf) : 0.f);
-      f = lf > 0.f ? exp2f(m - mf) / lf : 0.f;
-    }
-    uint16_t* orow = out + ((size_t)row * d.H + h) * DV + dh * DVH + 4 * g;
+  // Per-head (m, l) from the softmax owners to every value wave.
+  if (rq == 0) {
+    s_ml[0][hs] = m;
+    s_ml[1][hs] = l;
+  }
+  __syncthreads();
 #pragma unroll
-    for (int n = 0; n < NO; ++n) {
-      uint2 v;
-      v.x = (uint32_t)f2bf(acc[n][0] * f) | ((uint32_t)f2bf(acc[n][1] * f) << 16);
-      v.y = (uint32_t)f2bf(acc[n][2] * f) | ((uint32_t)f2bf(acc[n][3] * f) << 16);
-      *(uint2*)(orow + n * 16) = v;
-    }
-  } else {
-    float* pr = part + (((size_t)split * d.B * d.L + row) * d.H + h) * (DV + 2);
+  for (int ht = 0; ht < NHG; ++ht) {
+    const int hl = ht * 16 + c, h = hbase + hl;
+    const float mh = s_ml[0][hl], lh = s_ml[1][hl];
+    if (splits == 1) {
+      const float sink2 = sinks ? sinks[h] * kLog2e : -INFINITY;
+      const float mf = fmaxf(mh, sink2);
+      float f = 0.f;
+      if (mf != -INFINITY) {
+        const float lf = lh * exp2f(mh - mf) + (sinks ? exp2f(sink2 - mf) : 0.f);
+        f = lf > 0.f ? exp2f(mh - mf) / lf : 0.f;
+      }
+      uint16_t* orow = out + ((size_t)row * d.H + h) * DV + 4 * g;
 #pragma unroll
-    for (int n = 0; n < NO; ++n) *(f32x4*)(pr + dh * DVH + n * 16 + 4 * g) = acc[n];
-    if (g == 0 && dh == 0) {
-      pr[DV] = m;
-      pr[DV + 1] = l;
+      for (int n = 0; n < NDT; ++n) {
+        const int dt = wv + NW * n;
+        if (NDT * NW == NDT_ALL || dt < NDT_ALL) {
+          uint2 v;
+          v.x = pack_bf16x2(acc[n][ht][0] * f, acc[n][ht][1] * f);
+          v.y = pack_bf16x2(acc[n][ht][2] * f, acc[n][ht][3] * f);
+          *(uint2*)(orow + dt * 16) = v;
+        }
+      }
+    } else {
+      float* pr = part + (((size_t)split * d.B * d.L + row) * d.H + h) * (DV + 2);
+#pragma unroll
+      for (int n = 0; n < NDT; ++n) {
+        const int dt = wv + NW * n;
+        if (NDT * NW == NDT_ALL || dt < NDT_ALL) *(f32x4*)(pr + dt * 16 + 4 * g) = acc[n][ht];
+      }
+      if (wv == 0 && g == 0) {
+        pr[DV] = mh;
+        pr[DV + 1] = lh;
+      }
     }
   }
 }

@@ -10,6 +10,7 @@ namespace hisa {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
 
 constexpr float kNeg = -1e30f;  // the selection paths' finite mask value
@@ -21,6 +22,41 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7FFFu + ((u >> 16) & 1u);  // round to nearest even (inputs here are finite)
   return (uint16_t)(u >> 16);
+}
+
+// Workgroup barrier that orders LDS traffic only: waits for this wave's LDS
+// operations (lgkmcnt 0) but leaves vector-memory loads in flight, including
+// global->LDS loads into a buffer no wave reads before a full barrier.
+// (__syncthreads() would wait for those loads as well.)
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63, expcnt 7, lgkmcnt 0
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Global -> LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4):
+// lane l's 16 bytes from gsrc land at LDS byte address lds_base + 16*l
+// (lds_base is wave-uniform).  It is issued through inline assembly so the
+// compiler does not hold later LDS accesses to other buffers behind it; the
+// caller waits on vmcnt and synchronises before any wave reads the
+// destination.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p);
+}
+__device__ __forceinline__ void g2lds16(const void* gsrc, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory", "m0");
+}
+
+// Two floats to a packed bf16 pair (low half = lo), round to nearest even, in
+// one gfx950 conversion instruction.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
 template <typename T> __device__ __forceinline__ float ldf(const T* p);
@@ -64,6 +100,11 @@ __device__ __forceinline__ float sum_span(float v, int span) {
   if (span >= 8) v += dpp_f<kDppHalfMirror>(v);
   if (span >= 16) v += dpp_f<kDppMirror>(v);
   return v;
+}
+__device__ __forceinline__ float max_span8(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  return fmaxf(v, dpp_f<kDppHalfMirror>(v));
 }
 __device__ __forceinline__ float sum_row16(float v) {
   v += dpp_f<kDppXor1>(v);

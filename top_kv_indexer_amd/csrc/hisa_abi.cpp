@@ -273,22 +273,33 @@ int hisa_select_prefill(const hisa_dims* d, const void* q_idx, const float* w, c
   hipStream_t st = (hipStream_t)stream;
   float* cscore = nullptr;
   hipError_t e;
+  // one query row per wave when the blocks and candidates fit its registers
+  const bool rows = k.nb_cap > 0 && hisa::select_rows_ok(k, bf);
   if (k.nb_cap > 0) {
     float* rep = at<float>(ws, l.rep);
     uint16_t* rep3 = hisa::idx_mfma_ok(k, bf) ? at<uint16_t>(ws, l.rep3) : nullptr;
     cscore = at<float>(ws, l.cscore);
     e = timed("block_mean", st, [&] { return hisa::launch_block_mean(k, bf, false, keys, t0, rep, rep3, st); });
     if (e != hipSuccess) return launch_fail(e, "block mean");
-    e = timed("coarse", st, [&] { return hisa::launch_coarse(k, bf, false, q_idx, w, rep, rep3, t0, cscore, st); });
-    if (e != hipSuccess) return launch_fail(e, "coarse scores");
+    if (rows) {
+      e = timed("select_rows", st, [&] {
+        return hisa::launch_select_rows(k, q_idx, w, keys, rep3, t0, I_out, top_blk_out, path_out, st);
+      });
+      if (e != hipSuccess) return launch_fail(e, "row selection");
+    } else {
+      e = timed("coarse", st, [&] { return hisa::launch_coarse(k, bf, false, q_idx, w, rep, rep3, t0, cscore, st); });
+      if (e != hipSuccess) return launch_fail(e, "coarse scores");
+    }
   }
   float* scores = at<float>(ws, l.scores);
   e = timed("flat_scores", st, [&] { return hisa::launch_flat_scores(k, bf, q_idx, w, keys, t0, scores, st); });
   if (e != hipSuccess) return launch_fail(e, "flat scores");
   e = timed("topk_rows", st, [&] { return hisa::launch_topk_rows(k, scores, t0, I_out, nullptr, st); });
   if (e != hipSuccess) return launch_fail(e, "flat top-k");
-  e = timed("fine", st, [&] { return hisa::launch_fine(k, bf, q_idx, w, keys, cscore, t0, I_out, top_blk_out, path_out, st); });
-  if (e != hipSuccess) return launch_fail(e, "fine selection");
+  if (!rows) {
+    e = timed("fine", st, [&] { return hisa::launch_fine(k, bf, q_idx, w, keys, cscore, t0, I_out, top_blk_out, path_out, st); });
+    if (e != hipSuccess) return launch_fail(e, "fine selection");
+  }
   return HISA_OK;
 }
 

@@ -32,6 +32,12 @@ hipError_t launch_block_mean(const KDims& d, bool bf16, bool all_paths, const vo
 hipError_t launch_coarse(const KDims& d, bool bf16, bool all_paths, const void* q_idx,
                          const float* w, const float* rep, const uint16_t* rep3, const int* t0,
                          float* cscore, hipStream_t st);
+// Batched HiSA selection with one query row per wave (bf16 64 x 128 indexer,
+// nb_cap and index_keep * index_block at most 1024).
+bool select_rows_ok(const KDims& d, bool bf16);
+hipError_t launch_select_rows(const KDims& d, const void* q_idx, const float* w, const void* keys,
+                              const uint16_t* rep3, const int* t0, int* I, int* top_blk, int* path,
+                              hipStream_t st);
 hipError_t launch_fine(const KDims& d, bool bf16, const void* q_idx, const float* w,
                        const void* keys, const float* cscore, const int* t0, int* I,
                        int* top_blk, int* path, hipStream_t st);

@@ -453,25 +453,21 @@ __global__ __launch_bounds__(256) void k_fine_mfma(KDims d, int lds_floats, cons
   const int bsz = d.index_block;
   const int C = si.Kb * bsz;
   const uint16_t* kb = keys + (size_t)b * d.Np_cap * 128;
-  // Candidate tiles of 16 rows, the next tile's keys in flight while the
-  // current one is scored.
+  // Candidate tiles of 16 rows; wave w scores tiles w, w+4, ... with the keys
+  // of the next three of its tiles in flight (a ring of four register sets).
   auto cand = [&](int tile) {
     const int cc = min(tile * 16 + c, C - 1);
     return s_blk[cc / bsz] * bsz + cc % bsz;
   };
-  bf16x8 kn[4];
-  auto fetch = [&](int tile) {
+  // (unconditional: past the end it re-reads the last candidate, which keeps
+  // the load count per iteration fixed for the compiler's wait placement)
+  auto fetch = [&](int tile, bf16x8 (&kd)[4]) {
     const uint16_t* kp = kb + (size_t)cand(tile) * 128 + g * 32;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) kn[s] = ldg8(kp + s * 8);
+    for (int s = 0; s < 4; ++s) kd[s] = ldg8(kp + s * 8);
   };
-  __syncthreads();  // s_fs is reused for the fine scores below
-  if (wv * 16 < C) fetch(wv);
-  for (int tile = wv; tile * 16 < C; tile += 4) {
-    bf16x8 kf[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) kf[s] = kn[s];
-    if ((tile + 4) * 16 < C) fetch(tile + 4);
+  auto score = [&](int tile, const bf16x8 (&kf)[4]) {
+    if (tile * 16 >= C) return;
     const int cidx = tile * 16 + c;
     const int pos = cand(tile);
     f32x4 acc[4];
@@ -488,6 +484,21 @@ __global__ __launch_bounds__(256) void k_fine_mfma(KDims d, int lds_floats, cons
       for (int i = 0; i < 4; ++i) x += fmaxf(acc[ht][i], 0.f) * wl[ht][i];
     x = sum_rows(x);
     if (g == 0 && cidx < C) s_fs[cidx] = pos < valid ? x : kNeg;
+  };
+  __syncthreads();  // s_fs is reused for the fine scores below
+  bf16x8 k0[4], k1[4], k2[4], k3[4];
+  fetch(wv, k0);
+  fetch(wv + 4, k1);
+  fetch(wv + 8, k2);
+  for (int tile = wv; tile * 16 < C; tile += 16) {
+    fetch(tile + 12, k3);
+    score(tile, k0);
+    fetch(tile + 16, k0);
+    score(tile + 4, k1);
+    fetch(tile + 20, k1);
+    score(tile + 8, k2);
+    fetch(tile + 24, k2);
+    score(tile + 12, k3);
   }
   __syncthreads();
   block_topk_scores<256>(C, si.k, [&](int cc) { return s_fs[cc]; },
@@ -532,6 +543,234 @@ __global__ __launch_bounds__(256) void k_fine_valu(KDims d, const T* __restrict_
   __syncthreads();
   block_topk_scores<256>(C, si.k, [&](int cc) { return s_fs[cc]; },
                          [&](int slot, int cc) { Irow[slot] = s_blk[cc / bsz] * bsz + cc % bsz; }, sm);
+}
+
+// ------------------------------------------------------------------ batched path, one row per wave
+
+// The whole batched HiSA selection of one query row in one wave (bf16, 64
+// indexer heads of dim 128, nb <= 1024 blocks, C = Kb*b <= 1024 candidates):
+// coarse block scores on MFMA (rep as three bf16 parts), coarse top-Kb,
+// fine scores of the C candidates on MFMA, fine top-k.  A workgroup holds
+// four query rows of one sequence; MFMA operands stream through LDS
+// (global->LDS loads two tiles ahead): the rep tiles once for all four
+// waves, the candidate keys per wave.  Both top-k steps run inside the wave
+// on register-resident keys (element r of lane l has order index 64r + l,
+// which is ascending in block id / pooled row): a bitwise search finds the
+// k-th largest key, and ballots emit the winners in ascending id order, ties
+// at the threshold going to the lowest ids.
+constexpr int kRowR = 16;     // keys per lane: up to 1024 blocks or candidates
+constexpr int kRowKeep = 64;  // retained blocks per row
+
+// k-th largest of the wave's keys (absent entries carry key 0, k <= number
+// of present entries); returns it with the count of strictly larger keys
+__device__ __forceinline__ uint32_t wave_kth_key(const uint32_t (&key)[kRowR], int nr, int k, int& n_gt) {
+  uint32_t t = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = t | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int r = 0; r < kRowR; ++r) cnt += (r < nr && key[r] >= cand) ? 1 : 0;
+    if (wave_sum_i(cnt) >= k) t = cand;
+  }
+  int gt = 0;
+#pragma unroll
+  for (int r = 0; r < kRowR; ++r) gt += (r < nr && key[r] > t) ? 1 : 0;
+  n_gt = wave_sum_i(gt);
+  return t;
+}
+
+// emits the k winners in ascending order index: emit(slot, r)
+template <class EmitF>
+__device__ __forceinline__ void wave_emit_topk(const uint32_t (&key)[kRowR], int nr, int k, EmitF emit) {
+  int n_gt;
+  const uint32_t t = wave_kth_key(key, nr, k, n_gt);
+  int ties = k - n_gt, base = 0;
+#pragma unroll
+  for (int r = 0; r < kRowR; ++r) {
+    if (r < nr) {
+      const bool eq = key[r] == t;
+      const uint64_t meq = __ballot(eq);
+      const bool take = key[r] > t || (eq && lanes_below(meq) < ties);
+      ties -= min(ties, (int)__popcll(meq));
+      const uint64_t mt = __ballot(take);
+      if (take) emit(base + lanes_below(mt), r);
+      base += (int)__popcll(mt);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_select_rows(KDims d, const uint16_t* __restrict__ q_idx,
+                                                     const float* __restrict__ w, const uint16_t* __restrict__ keys,
+                                                     const uint16_t* __restrict__ rep3, const int* __restrict__ t0,
+                                                     int* __restrict__ I, int* __restrict__ top_blk,
+                                                     int* __restrict__ path) {
+  // One LDS region serves the coarse stage (a ring of three 16-block tiles of
+  // rep, three bf16 parts each, shared by the four waves) and then the fine
+  // stage (a private ring of three 16-candidate key tiles per wave).  Rows
+  // are 256 bytes with their 16-byte chunks XOR-swizzled by the row (slot
+  // position p holds chunk p ^ row), so a 16-row MFMA operand read is
+  // bank-conflict free.
+  constexpr int kRepTile = 3 * 16 * 128;  // elements
+  constexpr int kKeyTile = 16 * 128;
+  constexpr int kRegion = 3 * kRepTile > 12 * kKeyTile ? 3 * kRepTile : 12 * kKeyTile;
+  __shared__ __align__(16) uint16_t s_ring[kRegion];
+  __shared__ float s_sc[4][kRowR * 64];  // per wave: coarse, then fine scores
+  __shared__ int s_blk[4][kRowKeep];
+  const int b = blockIdx.y, wv = wave_id(), j_raw = blockIdx.x * 4 + wv;
+  const bool live = j_raw < d.L;  // trailing waves of the last workgroup only help with the shared loads
+  const int j = live ? j_raw : d.L - 1;
+  const int lane = lane_id(), g = lane >> 4, c = lane & 15;
+  const SeqInfo si = seq_info(d, t0[b]);
+  int* Irow = I + ((size_t)b * d.L + j) * d.topk;
+  int* blkrow = top_blk ? top_blk + ((size_t)b * d.L + j) * d.index_keep : nullptr;
+  if (live) {
+    if (path && j == 0 && lane == 0) path[b] = si.path;
+    if (blkrow)
+      for (int i = lane; i < d.index_keep; i += 64) blkrow[i] = -1;
+    if (si.path != PATH_FLAT) {  // flat rows belong to the flat scan
+      const bool dense = si.path == PATH_DENSE;
+      const int first_pad = (si.ok && !dense) ? si.k : 0;
+      for (int i = lane; i < d.topk; i += 64) {
+        if (dense && i < si.Np) Irow[i] = i;
+        else if (i >= first_pad) Irow[i] = -1;
+      }
+    }
+  }
+  if (!si.ok || si.path != PATH_HISA) return;  // uniform over the workgroup (one sequence)
+  const int valid = visible(t0[b] + j, d.ratio, si.Np);
+  float* sc = s_sc[wv];
+
+  // q as the A operand (MFMA step s: dims 32s + 8g .. +7), per-head weights
+  const uint16_t* qrow = q_idx + ((size_t)b * d.L + j) * 64 * 128;
+  bf16x8 qf[4][4];
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qf[ht][s] = ldg8(qrow + (ht * 16 + c) * 128 + s * 32 + g * 8);
+  float wl[4][4];
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wl[ht][i] = w[((size_t)b * d.L + j) * 64 + ht * 16 + 4 * g + i] * d.w_scale;
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // q and w are in: only tile loads count on vmcnt below
+  auto head_sum = [&](const f32x4 (&acc)[4]) {
+    float x = 0.f;
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x += fmaxf(acc[ht][i], 0.f) * wl[ht][i];
+    return sum_rows(x);
+  };
+  // B operand of a 16-row tile in LDS: row c, MFMA step s
+  auto frag = [&](const uint16_t* rows, int s) {
+    return *(const bf16x8*)(rows + c * 128 + ((4 * s + g) ^ c) * 8);
+  };
+  auto wait_vm = [&](bool keep_one_tile, int per_tile) {
+    if (!keep_one_tile) __builtin_amdgcn_s_waitcnt(0x0F70);
+    else if (per_tile == 3) __builtin_amdgcn_s_waitcnt(0x0F73);
+    else __builtin_amdgcn_s_waitcnt(0x0F74);
+  };
+
+  // ---- coarse scores of blocks 16nt + c (eligible iff the block's first row is visible)
+  const int bsz = d.index_block, nb = si.nb;
+  const int lbsz = __builtin_ctz(bsz);
+  const size_t plane = (size_t)d.B * d.nb_cap * 128;
+  const int ntc = (nb + 15) / 16;
+  // tile nt: wave w moves parts/rows (i = w, w+4, w+8): part i/4, rows 4(i%4) .. +3
+  auto load_rep = [&](int nt) {
+    uint16_t* slot = s_ring + (nt % 3) * kRepTile;
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+      const int i = wv + 4 * u, part = i >> 2, r = 4 * (i & 3) + (lane >> 4);
+      const int beta = min(nt * 16 + r, d.nb_cap - 1);
+      const uint16_t* src = rep3 + part * plane + ((size_t)b * d.nb_cap + beta) * 128 + (((lane & 15) ^ r) * 8);
+      g2lds16(src, lds_addr(slot + part * 2048 + 4 * (i & 3) * 128));
+    }
+  };
+  load_rep(0);
+  if (ntc > 1) load_rep(1);
+  for (int nt = 0; nt < ntc; ++nt) {
+    wait_vm(nt + 1 < ntc, 3);
+    lds_sync();  // every wave's share of tile nt has landed; slot (nt+2)%3 is free
+    if (nt + 2 < ntc) load_rep(nt + 2);
+    const uint16_t* slot = s_ring + (nt % 3) * kRepTile;
+    f32x4 acc[4];
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int part = 0; part < 3; ++part)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8 bf = frag(slot + part * 2048, s);
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht)
+          acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ht][s], bf, acc[ht], 0, 0, 0);
+      }
+    const float x = head_sum(acc);
+    const int beta = nt * 16 + c;
+    if (g == 0 && beta < nb) sc[beta] = beta * bsz < valid ? x : kNeg;
+  }
+  __syncthreads();  // the rep ring is free for the key rings
+  const int nrc = (nb + 63) / 64;
+  uint32_t key[kRowR];
+#pragma unroll
+  for (int r = 0; r < kRowR; ++r) {
+    const int i = 64 * r + lane;
+    key[r] = (r < nrc && i < nb) ? score_key(sc[i]) : 0u;
+  }
+  int* blk = s_blk[wv];
+  wave_emit_topk(key, nrc, si.Kb, [&](int slot, int r) { blk[slot] = 64 * r + lane; });
+  if (blkrow && live)
+    for (int i = lane; i < si.Kb; i += 64) blkrow[i] = blk[i];
+
+  // ---- fine scores of the C candidates: candidate cc is row blk[cc / b]*b + cc % b
+  const int C = si.Kb * bsz;
+  const int ntf = (C + 15) / 16;
+  auto cand = [&](int cc) {
+    cc = min(cc, C - 1);
+    return (blk[cc >> lbsz] << lbsz) + (cc & (bsz - 1));
+  };
+  uint16_t* ring = s_ring + wv * 3 * kKeyTile;
+  const uint16_t* kb = keys + (size_t)b * d.Np_cap * 128;
+  // tile t: four loads of four candidate rows each (lane l: row 4i + l/16, chunk l%16)
+  auto load_keys = [&](int t) {
+    uint16_t* slot = ring + (t % 3) * kKeyTile;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * i + (lane >> 4);
+      const uint16_t* src = kb + (size_t)cand(t * 16 + r) * 128 + (((lane & 15) ^ r) * 8);
+      g2lds16(src, lds_addr(slot + 4 * i * 128));
+    }
+  };
+  load_keys(0);
+  if (ntf > 1) load_keys(1);
+  for (int t = 0; t < ntf; ++t) {
+    wait_vm(t + 1 < ntf, 4);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's reads of the slot reloaded below are done
+    if (t + 2 < ntf) load_keys(t + 2);
+    const uint16_t* slot = ring + (t % 3) * kKeyTile;
+    bf16x8 kf[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) kf[s] = frag(slot, s);
+    f32x4 acc[4];
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) {
+      acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ht][s], kf[s], acc[ht], 0, 0, 0);
+    }
+    const float x = head_sum(acc);
+    const int cidx = t * 16 + c;
+    if (g == 0 && cidx < C) sc[cidx] = cand(cidx) < valid ? x : kNeg;
+  }
+  if (!live) return;
+  const int nrf = (C + 63) / 64;
+#pragma unroll
+  for (int r = 0; r < kRowR; ++r) {
+    const int i = 64 * r + lane;
+    key[r] = (r < nrf && i < C) ? score_key(sc[i]) : 0u;
+  }
+  wave_emit_topk(key, nrf, si.k, [&](int slot, int r) { Irow[slot] = cand(64 * r + lane); });
 }
 
 // ------------------------------------------------------------------ flat scan
@@ -739,6 +978,18 @@ hipError_t launch_coarse(const KDims& d, bool bf16, bool all_paths, const void* 
   else
     hipLaunchKernelGGL(k_coarse_valu<float>, dim3(d.L, d.B), dim3(256), 0, st, d, (int)all_paths,
                        (const float*)q_idx, w, rep, t0, cscore);
+  return hipGetLastError();
+}
+
+bool select_rows_ok(const KDims& d, bool bf16) {
+  return idx_mfma_ok(d, bf16) && d.index_block > 0 && d.nb_cap <= 64 * kRowR &&
+         (long long)d.index_keep * d.index_block <= 64 * kRowR && d.index_keep <= kRowKeep;
+}
+
+hipError_t launch_select_rows(const KDims& d, const void* q_idx, const float* w, const void* keys, const uint16_t* rep3,
+                              const int* t0, int* I, int* top_blk, int* path, hipStream_t st) {
+  hipLaunchKernelGGL(k_select_rows, dim3(cdiv(d.L, 4), d.B), dim3(256), 0, st, d, (const uint16_t*)q_idx, w,
+                     (const uint16_t*)keys, rep3, t0, I, top_blk, path);
   return hipGetLastError();
 }
 

@@ -103,6 +103,8 @@ def algorithmic(w, x, unique_kv_rows=None):
         "flat_scores": {"bytes": keys + idx_q, "flops": sum(
             sum(min(n, (int(t) + j + 1) // w.ratio) for j in range(L)) for n, t in zip(Np, x["t0"])) * w.H_i * w.D_i * 2},
         "topk_rows": {"bytes": rows * kI * 4, "flops": 0},
+        "select_rows": {"bytes": idx_q + rows * kI * 4,
+                        "flops": L * sum(nb) * w.H_i * w.D_i * 2 + rows * C * w.H_i * w.D_i * 2},
     }
 
 

@@ -563,18 +563,19 @@ constexpr int kRowKeep = 64;  // retained blocks per row
 
 // k-th largest of the wave's keys (absent entries carry key 0, k <= number
 // of present entries); returns it with the count of strictly larger keys
-__device__ __forceinline__ uint32_t wave_kth_key(const uint32_t (&key)[kRowR], int nr, int k, int& n_gt) {
+__device__ __forceinline__ uint32_t wave_kth_key(const uint32_t (&key)[kRowR], int k, int& n_gt) {
+  // absent entries (key 0) never reach a candidate, which always has a bit set
   uint32_t t = 0;
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t cand = t | (1u << bit);
     int cnt = 0;
 #pragma unroll
-    for (int r = 0; r < kRowR; ++r) cnt += (r < nr && key[r] >= cand) ? 1 : 0;
+    for (int r = 0; r < kRowR; ++r) cnt += key[r] >= cand ? 1 : 0;
     if (wave_sum_i(cnt) >= k) t = cand;
   }
   int gt = 0;
 #pragma unroll
-  for (int r = 0; r < kRowR; ++r) gt += (r < nr && key[r] > t) ? 1 : 0;
+  for (int r = 0; r < kRowR; ++r) gt += key[r] > t ? 1 : 0;
   n_gt = wave_sum_i(gt);
   return t;
 }
@@ -583,7 +584,7 @@ __device__ __forceinline__ uint32_t wave_kth_key(const uint32_t (&key)[kRowR], i
 template <class EmitF>
 __device__ __forceinline__ void wave_emit_topk(const uint32_t (&key)[kRowR], int nr, int k, EmitF emit) {
   int n_gt;
-  const uint32_t t = wave_kth_key(key, nr, k, n_gt);
+  const uint32_t t = wave_kth_key(key, k, n_gt);
   int ties = k - n_gt, base = 0;
 #pragma unroll
   for (int r = 0; r < kRowR; ++r) {

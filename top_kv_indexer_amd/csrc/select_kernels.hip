@@ -32,97 +32,118 @@ __device__ __forceinline__ bf16x8 ldg8(const uint16_t* p) { return *(const bf16x
 
 // ------------------------------------------------------------------ decode scan
 
-// One wave per 64-row slab of one sequence (bf16, H_i = 64, D_i = 128,
-// index_block | 64).  The wave's four 16-row tiles of keys go straight from
-// HBM into registers (all 16 loads in flight at once), and MFMA gives
-// D[h][row] = q_h . key_row.  Fine score of a row: sum_h relu(D) w_eff.
-// Coarse score of a block: the block mean is linear, so q_h . rep_beta is the
-// mean of D[h][row] over the block's rows; it is summed across the lanes that
-// hold those rows, then relu'd and weighted.  No LDS and no barriers.
-__global__ __launch_bounds__(64) void k_decode_scan_mfma(KDims d, const uint16_t* __restrict__ q_idx,
-                                                         const float* __restrict__ w,
-                                                         const uint16_t* __restrict__ keys,
-                                                         const int* __restrict__ t0,
-                                                         float* __restrict__ fscore,
-                                                         float* __restrict__ cscore) {
+// One wave per `spw` consecutive 64-row slabs of one sequence (bf16,
+// H_i = 64, D_i = 128, index_block | 64).  A slab's four 16-row tiles of keys
+// go straight from HBM into registers (16 loads in flight) and the next
+// slab's keys stream in while the current one is scored.  With one slab per
+// wave (few slabs, latency-bound) the loads go out before t0 arrives, rows
+// clamped to the buffer rather than to Np; with several, only slabs below Np
+// are read.  MFMA gives D[h][row] = q_h . key_row.  Fine score of a row:
+// sum_h relu(D) w_eff.  Coarse score of a block: the block mean is linear, so
+// q_h . rep_beta is the mean of D[h][row] over the block's rows; it is summed
+// across the lanes that hold those rows, then relu'd and weighted.  No LDS,
+// no barriers.
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_decode_scan_mfma(
+    KDims d, int spw, const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
+    const uint16_t* __restrict__ keys, const int* __restrict__ t0, float* __restrict__ fscore,
+    float* __restrict__ cscore) {
   const int b = blockIdx.y;
-  const int row0 = blockIdx.x * 64;
-  const SeqInfo si = seq_info(d, t0[b]);
-  if (!si.ok || si.path == PATH_DENSE || row0 >= si.Np) return;
+  const int slab0 = blockIdx.x * spw;
   const int lane = threadIdx.x, g = lane >> 4, c = lane & 15;
-  // Keys: lane (g, c) of tile t holds row row0 + 16t + c, dims [32g, 32g + 32)
-  // (the k order of q below matches).  Rows past Np read row Np - 1 instead.
-  const uint16_t* kb = keys + (size_t)b * d.Np_cap * 128 + g * 32;
-  bf16x8 kf[4][4];
+  // Keys: lane (g, c) of tile t holds row 64*slab + 16t + c; MFMA step s takes
+  // dims 32s + 8g .. +7 (the k order of q below matches), so each load
+  // instruction reads one 64-byte run per row.
+  const uint16_t* kb = keys + (size_t)b * d.Np_cap * 128 + g * 8;
+  auto load = [&](int slab, int rmax, bf16x8 (&kf)[4][4]) {
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int r = min(row0 + t * 16 + c, si.Np - 1);
+    for (int t = 0; t < 4; ++t) {
+      const int r = min(slab * 64 + t * 16 + c, rmax);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) kf[t][s] = ldg8(kb + (size_t)r * 128 + s * 8);
-  }
+      for (int s = 0; s < 4; ++s) kf[t][s] = ldg8(kb + (size_t)r * 128 + s * 32);
+    }
+  };
+  bf16x8 ka[4][4], kn[4][4];
+  const bool early = spw == 1;
+  if (early && slab0 * 64 < d.Np_cap) load(slab0, d.Np_cap - 1, ka);
   const uint16_t* qrow = q_idx + (size_t)b * d.L * 64 * 128;
   bf16x8 qf[4][4];
 #pragma unroll
   for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) qf[ht][s] = ldg8(qrow + (ht * 16 + c) * 128 + g * 32 + s * 8);
+    for (int s = 0; s < 4; ++s) qf[ht][s] = ldg8(qrow + (ht * 16 + c) * 128 + s * 32 + g * 8);
   float wl[4][4];
 #pragma unroll
   for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
     for (int i = 0; i < 4; ++i) wl[ht][i] = w[(size_t)b * d.L * 64 + ht * 16 + 4 * g + i] * d.w_scale;
+  const SeqInfo si = seq_info(d, t0[b]);
+  if (!si.ok || si.path == PATH_DENSE) return;
+  const int nslab = (si.Np + 63) / 64;
+  if (slab0 >= nslab) return;
+  if (!early) load(slab0, si.Np - 1, ka);
   const bool hisa_path = si.path == PATH_HISA;
   const int bsz = d.index_block;
-  float bs[4][4];  // running block sums of D over rows, per (head tile, i)
+  // Scores of one slab (rows past Np are scored but never stored; a block
+  // past nb is never stored either, so their contents do not matter).
+  auto score = [&](int slab, const bf16x8 (&kf)[4][4]) {
+    const int row0 = slab * 64;
+    float bs[4][4];  // running block sums of D over rows, per (head tile, i)
 #pragma unroll
-  for (int ht = 0; ht < 4; ++ht)
+    for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) bs[ht][i] = 0.f;
+      for (int i = 0; i < 4; ++i) bs[ht][i] = 0.f;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    f32x4 acc[4];
+    for (int t = 0; t < 4; ++t) {
+      f32x4 acc[4];
 #pragma unroll
-    for (int ht = 0; ht < 4; ++ht) {
-      acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ht = 0; ht < 4; ++ht) {
+        acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 4; ++s) acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ht][s], kf[t][s], acc[ht], 0, 0, 0);
+        for (int s = 0; s < 4; ++s) acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ht][s], kf[t][s], acc[ht], 0, 0, 0);
+      }
+      float v = 0.f;
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v += fmaxf(acc[ht][i], 0.f) * wl[ht][i];
+      v = sum_rows(v);
+      const int r = row0 + t * 16 + c;
+      if (g == 0 && r < si.Np) fscore[(size_t)b * d.Np_cap + r] = v;
+      if (!hisa_path) continue;
+      // Block sums: rows of a block are consecutive lanes c (and tiles t).
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bs[ht][i] += acc[ht][i];
+      const int span = bsz < 16 ? bsz : 16;  // rows of one block inside this tile
+      if (bsz > 16 && ((t + 1) * 16) % bsz != 0) continue;
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bs[ht][i] = sum_span(bs[ht][i], span);
+      float cv = 0.f;
+      const float inv_b = 1.f / (float)bsz;
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          cv += fmaxf(bs[ht][i] * inv_b, 0.f) * wl[ht][i];
+          bs[ht][i] = 0.f;
+        }
+      cv = sum_rows(cv);
+      // lane c holds the sum of the block containing its row
+      const int beta = (row0 + t * 16 + c) / bsz;
+      const bool first_lane = bsz >= 16 ? c == 0 : (c % bsz) == 0;
+      if (g == 0 && first_lane && beta < si.nb) cscore[(size_t)b * d.nb_cap + beta] = cv;
     }
-    float v = 0.f;
-#pragma unroll
-    for (int ht = 0; ht < 4; ++ht)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v += fmaxf(acc[ht][i], 0.f) * wl[ht][i];
-    v = sum_rows(v);
-    const int r = row0 + t * 16 + c;
-    if (g == 0 && r < si.Np) fscore[(size_t)b * d.Np_cap + r] = v;
-    if (!hisa_path) continue;
-    // Block sums: rows of a block are consecutive lanes c (and tiles t).
-#pragma unroll
-    for (int ht = 0; ht < 4; ++ht)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) bs[ht][i] += acc[ht][i];
-    const int span = bsz < 16 ? bsz : 16;  // rows of one block inside this tile
-    if (bsz > 16 && ((t + 1) * 16) % bsz != 0) continue;
-#pragma unroll
-    for (int ht = 0; ht < 4; ++ht)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        bs[ht][i] = sum_span(bs[ht][i], span);
-      }
-    float cv = 0.f;
-    const float inv_b = 1.f / (float)bsz;
-#pragma unroll
-    for (int ht = 0; ht < 4; ++ht)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        cv += fmaxf(bs[ht][i] * inv_b, 0.f) * wl[ht][i];
-        bs[ht][i] = 0.f;
-      }
-    cv = sum_rows(cv);
-    // lane c holds the sum of the block containing its row
-    const int beta = (row0 + t * 16 + c) / bsz;
-    const bool first_lane = bsz >= 16 ? c == 0 : (c % bsz) == 0;
-    if (g == 0 && first_lane && beta < si.nb) cscore[(size_t)b * d.nb_cap + beta] = cv;
+  };
+  for (int u = 0; u < spw; u += 2) {
+    if (slab0 + u >= nslab) break;
+    if (u + 1 < spw && slab0 + u + 1 < nslab) load(slab0 + u + 1, si.Np - 1, kn);
+    score(slab0 + u, ka);
+    if (u + 1 >= spw || slab0 + u + 1 >= nslab) break;
+    if (u + 2 < spw && slab0 + u + 2 < nslab) load(slab0 + u + 2, si.Np - 1, ka);
+    score(slab0 + u + 1, kn);
   }
 }
 
@@ -934,8 +955,11 @@ hipError_t launch_decode_scan(const KDims& d, bool bf16, const void* q_idx, cons
                               const int* t0, float* fscore, float* cscore, hipStream_t st) {
   const dim3 grid(cdiv(d.Np_cap, 64), d.B);
   if (idx_mfma_ok(d, bf16)) {
-    hipLaunchKernelGGL(k_decode_scan_mfma, grid, dim3(64), 0, st, d, (const uint16_t*)q_idx, w,
-                       (const uint16_t*)keys, t0, fscore, cscore);
+    // several slabs per wave once there are enough to fill the chip
+    const long long slabs = (long long)cdiv(d.Np_cap, 64) * d.B;
+    const int spw = slabs >= 8192 ? 4 : slabs >= 4096 ? 2 : 1;
+    hipLaunchKernelGGL(k_decode_scan_mfma, dim3(cdiv(d.Np_cap, 64 * spw), d.B), dim3(64), 0, st, d, spw,
+                       (const uint16_t*)q_idx, w, (const uint16_t*)keys, t0, fscore, cscore);
   }
   else if (bf16)
     hipLaunchKernelGGL(k_decode_scan_valu<uint16_t>, grid, dim3(256), 0, st, d, (const uint16_t*)q_idx, w,

@@ -270,6 +270,31 @@ def test_prefill_early_rows_and_small_t0(hisa):
     check_attention(w, x, I, out, sample=40)
 
 
+ROWS = synth.Workload("rows_prefill_b4_l37", B=4, L=37, ratio=4, window=128, topk=64, index_block=8,
+                      index_keep=10, H_i=64, D_i=128, H=64, Dk=512, Dv=512, bf16=True,
+                      t0=[20000, 3000, 280, 200], planted=0, Np_cap=5016)
+
+
+def test_prefill_rows_small_blocks_mixed_paths(hisa):
+    # The one-row-per-wave batched selection with index_block 8 and keep 10:
+    # C = 80 candidates (a partial 16-row tile and a partial 64-entry key
+    # row), nb up to 626 blocks, L = 37 (the last workgroup holds one row),
+    # and one sequence on each of the HiSA / flat / dense paths.
+    w = ROWS
+    x, g = inputs(w, 11)
+    say("[run] small-block prefill")
+    I, blk, path = hisa.hisa_select_prefill(g["q_idx"], g["w"], g["keys"], g["t0"], **sel_kw(w))
+    torch.cuda.synchronize()
+    assert parity.to_np(path).tolist() == [hisa.PATH_HISA, hisa.PATH_HISA, hisa.PATH_FLAT, hisa.PATH_DENSE]
+    check_selection(w, x, I, blk, path)
+    Bk = parity.to_np(blk)
+    assert (Bk[2:] == -1).all() and (Bk[:2] >= 0).all()
+    assert (np.diff(Bk[:2], axis=-1) > 0).all()  # retained blocks ascending
+    In = parity.to_np(I)
+    assert (np.diff(In[:3], axis=-1) > 0).all()  # ids ascending, k = 64 of each visible prefix
+    np.testing.assert_array_equal(In[3], np.broadcast_to(np.r_[np.arange(59), -np.ones(5, int)], (37, 64)))
+
+
 def test_attention_masks_window0_no_sinks(hisa):
     w = synth.FLASH_DECODE.with_(name="flash_b3_window0", B=3, t0=[65536, 40000, 9000], window=0, sinks=False,
                                  planted=0, Np_cap=16384)

@@ -100,6 +100,8 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
   constexpr int IPT = CH / NT;          // chunk rows per thread
   constexpr int LPT = RPW * (DK > 512 ? 2 : 1);  // vector-memory loads per tile per wave
   constexpr int KW = 8;                 // K fragments in flight
+  constexpr int OP = DV + 8;            // pitch of the staged output rows (elements)
+  static_assert(HW * OP <= NBUF * kTile * KPD && HW <= 2 * kTile, "staging fits the ring");
   static_assert(NTILE * RPW == 64 * IPT, "a wave's row offsets of one chunk fill whole registers");
   static_assert(HW == 8 * NW, "each wave owns the softmax of 8 heads");
   static_assert(DV % 16 == 0 && DK >= 512 && DK <= 1024 && DK % 32 == 0, "shape");
@@ -121,6 +123,7 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
   const int tid = threadIdx.x, lane = lane_id(), wv = wave_id(), g = lane >> 4, c = lane & 15;
   const int hg = wv >> 1, dh = wv & 1;
   const int hbase = blockIdx.z * HW;
+  auto sw = [](int r) { return ((r & 7) << 1) | ((r >> 3) & 1); };
   // Row list: the kI pooled ids of I first, then `window` local slots (slot
   // s holds position s_lo + s while s < n_loc).  The split geometry does not
   // depend on t0, so the index loads below go out before t0 arrives.
@@ -146,7 +149,6 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
   const long long dummy = rp.n_loc > 0 ? ~(((long long)b * d.Wl_cap + (rp.s_lo - rp.ls)) * DK)
                                        : (long long)b * d.Np_cap * DK;
   const bool any_row = rp.n_loc > 0 || rp.V > 0;
-  auto sw = [](int r) { return ((r & 7) << 1) | ((r >> 3) & 1); };
   // liveness and element offset (>= 0 into pooled_kv, ~offset into local_kv)
   // of list entry e (given its pooled id when e < kI)
   auto resolve = [&](int e, int id, long long& off) -> bool {
@@ -162,9 +164,41 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
     return true;
   };
 
-  // scores: this wave's 16 heads of q as the B operand
+  // scores: this wave's 16 heads of q as the B operand.  With 64 heads the
+  // workgroup's head rows (contiguous in q) come in through the last two ring
+  // slots, one 1 KiB global->LDS load per row (swizzled like the KV rows);
+  // with 16 heads straight into registers.
   bf16x8 qf[NS];
-  {
+  auto issue_q = [&]() {
+    uint16_t* qs = kv[NBUF - 2];  // HW <= 64 rows span slots NBUF-2 and NBUF-1
+    const uint16_t* qg = q + ((size_t)row * d.H + hbase) * DK;
+#pragma unroll
+    for (int u = 0; u < HW / NW; ++u) {
+      const int h = wv + NW * u;
+      const uint32_t dst = lds_addr(qs + h * KPD);
+      g2lds16(qg + (size_t)h * DK + (lane ^ sw(h)) * 8, dst);
+      if (DK > 512 && lane < DK / 8 - 64) g2lds16(qg + (size_t)h * DK + 512 + lane * 8, dst + 1024);
+    }
+  };
+  // q fragments from LDS, once every wave's rows have landed (the caller has
+  // waited for its own q loads)
+  auto read_q = [&]() {
+    __syncthreads();
+    const uint16_t* qs = kv[NBUF - 2];
+    const int hr = hg * 16 + c;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int ch = 4 * s + g;
+      qf[s] = *(const bf16x8*)(qs + hr * KPD + (ch < 64 ? ch ^ sw(c) : ch) * 8);
+    }
+    __syncthreads();  // slots NBUF-2 and NBUF-1 are free again
+  };
+  if constexpr (NHG >= 4) {
+    // many heads per row: stage q through LDS before anything else
+    issue_q();
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0
+    read_q();
+  } else {
     const uint16_t* qrow = q + ((size_t)row * d.H + hbase + hg * 16 + c) * DK + g * 8;
 #pragma unroll
     for (int s = 0; s < NS; ++s) qf[s] = *(const bf16x8*)(qrow + s * 32);
@@ -381,7 +415,8 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
         const float lf = lh * exp2f(mh - mf) + (sinks ? exp2f(sink2 - mf) : 0.f);
         f = lf > 0.f ? exp2f(mh - mf) / lf : 0.f;
       }
-      uint16_t* orow = out + ((size_t)row * d.H + h) * DV + 4 * g;
+      // staged in the (now idle) ring: head row hl, padded pitch OP
+      uint16_t* orow = &kv[0][0] + hl * OP + 4 * g;
 #pragma unroll
       for (int n = 0; n < NDT; ++n) {
         const int dt = wv + NW * n;
@@ -403,6 +438,17 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
         pr[DV] = mh;
         pr[DV + 1] = lh;
       }
+    }
+  }
+  if (splits == 1) {
+    // The group's HW heads are contiguous in out: copy the staged rows out in
+    // 16-byte pieces, whole 128-byte lines per wave instruction.
+    __syncthreads();
+    uint16_t* og = out + ((size_t)row * d.H + hbase) * DV;
+    constexpr int CPR = DV / 8;  // 16-byte pieces per head row
+    for (int k = tid; k < HW * CPR; k += NT) {
+      const int hr = k / CPR, cc = k - hr * CPR;
+      *(u32x4*)(og + (size_t)k * 8) = *(const u32x4*)(&kv[0][0] + hr * OP + cc * 8);
     }
   }
 }

@@ -95,6 +95,7 @@ def algorithmic(w, x, unique_kv_rows=None):
     return {
         "decode_scan": {"bytes": keys + idx_q, "flops": sum(Np) * w.H_i * w.D_i * 2},
         "decode_select": {"bytes": rows * kI * 4, "flops": 0},
+        "decode_scan_select": {"bytes": keys + idx_q + rows * kI * 4, "flops": sum(Np) * w.H_i * w.D_i * 2},
         "attention": {"bytes": attn_bytes, "flops": attn_flops},
         "attention_merge": {"bytes": rows * w.H * w.Dv * bf, "flops": 0},
         "block_mean": {"bytes": keys, "flops": 0},
@@ -191,7 +192,7 @@ def main():
                                 ratio=w.ratio, window=w.window)
     out = torch.empty((w.B, w.L, w.H, w.Dv), dtype=dt, device=dev)
     op = {"decode": hisa.OP_SELECT_DECODE, "prefill": hisa.OP_SELECT_PREFILL, "flat": hisa.OP_FLAT_TOPK}[kind]
-    ws_sel = torch.empty(max(hisa.workspace_bytes(op, sel_d), 256), dtype=torch.uint8, device=dev)
+    ws_sel = torch.zeros(max(hisa.workspace_bytes(op, sel_d), 256), dtype=torch.uint8, device=dev)
     ws_att = torch.empty(max(hisa.workspace_bytes(hisa.OP_ATTENTION, att_d), 256), dtype=torch.uint8, device=dev)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())  # noqa: E731

@@ -45,8 +45,9 @@ def dims(**kw):
 
 def test_workspace_sizes(lib):
     d = dims()
-    # decode: f32 scores of every pooled row + one coarse score per block
-    assert hisa.workspace_bytes(hisa.OP_SELECT_DECODE, d) == 16384 * 4 + 256 * 4
+    # decode: the arrival counters (one 256-byte region), f32 scores of every
+    # pooled row + one coarse score per block
+    assert hisa.workspace_bytes(hisa.OP_SELECT_DECODE, d) == 256 + 16384 * 4 + 256 * 4
     assert hisa.workspace_bytes(hisa.OP_FLAT_TOPK, dims(L=4, Np_cap=1000)) == ((4 * 1000 * 4 + 255) // 256) * 256
     # single-row attention splits the 640 rows into 10 parts of 64
     assert hisa.workspace_bytes(hisa.OP_ATTENTION, d) == 10 * 64 * 514 * 4

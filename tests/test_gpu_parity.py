@@ -223,6 +223,33 @@ def test_mixed_paths_decode(hisa):
         assert parity.max_abs(o[b, 0], ref) <= 2e-2, b
 
 
+def test_decode_workspace_reuse(hisa):
+    # The fused decode scan + selection counts the waves that finished each
+    # sequence in the workspace and returns the counters to zero: three calls
+    # on one workspace, with pooled counts that change the number of waves per
+    # sequence between calls, each match the oracle, and the counters end zero.
+    w = MIXED
+    x, g = inputs(w, 5)
+    d = hisa.selection_dims(g["q_idx"], g["keys"], ratio=4, topk=512, index_block=64, index_keep=16)
+    ws = torch.zeros(hisa.workspace_bytes(hisa.OP_SELECT_DECODE, d), dtype=torch.uint8, device="cuda")
+    od = odims(w, x)
+    # each sequence's pooled count stays within its own (non-NaN) rows
+    for t0s in ([1200, 2800, 4096, 6000, 20000, 16400], [1200, 2100, 4096, 4500, 12000, 9000],
+                [1000, 2800, 3000, 6000, 20000, 16000]):
+        say(f"[run] decode on a reused workspace, t0 = {t0s}")
+        t0 = torch.tensor(t0s, dtype=torch.int32, device="cuda")
+        I, blk, path = hisa.hisa_select_decode(g["q_idx"], g["w"], g["keys"], t0, **sel_kw(w), ws=ws)
+        torch.cuda.synchronize()
+        xx = dict(x)
+        xx["t0"] = np.array(t0s, np.int32)
+        In, bn, p = parity.to_np(I), parity.to_np(blk), parity.to_np(path)
+        for b in range(w.B):
+            Io, blko, po = oracle.select_row(od, xx["q_idx"][b, 0], xx["w"][b, 0], xx["keys"][b], t0s[b], 0)
+            assert p[b] == po, (b, p[b], po)
+            parity.check_selection_row(od, xx, b, 0, In[b, 0], bn[b, 0], p[b], Io, blko, po)
+    assert (ws[: 4 * w.B].view(torch.int32) == 0).all()
+
+
 def test_invalid_sequence_outputs(hisa):
     x, g = inputs(MIXED, 5)
     w = MIXED

@@ -102,7 +102,7 @@ int make_kdims(int op, const hisa_dims* d, KDims* k) {
 
 struct Layout {
   size_t total = 0;
-  size_t rep = 0, rep3 = 0, cscore = 0, scores = 0, fscore = 0, partial = 0;
+  size_t rep = 0, rep3 = 0, cscore = 0, scores = 0, fscore = 0, partial = 0, cnt = 0;
   int splits = 1;
 };
 
@@ -123,6 +123,8 @@ Layout layout(int op, const hisa_dims* d, const KDims& k) {
       l.rep3 = hisa::idx_mfma_ok(k, bf) ? take(l, 3 * B * nb_cap * d->D_i * sizeof(uint16_t)) : 0;
       break;
     case HISA_OP_SELECT_DECODE:
+      // arrival counters first: the region callers zero once (see hisa.h)
+      l.cnt = take(l, B * sizeof(int));
       l.fscore = take(l, B * d->Np_cap * sizeof(float));
       l.cscore = take(l, B * std::max<size_t>(nb_cap, 1) * sizeof(float));
       break;
@@ -253,7 +255,17 @@ int hisa_select_decode(const hisa_dims* d, const void* q_idx, const float* w, co
   hipStream_t st = (hipStream_t)stream;
   float* fscore = at<float>(ws, l.fscore);
   float* cscore = at<float>(ws, l.cscore);
-  hipError_t e = timed("decode_scan", st, [&] { return hisa::launch_decode_scan(k, bf, q_idx, w, keys, t0, fscore, cscore, st); });
+  if (hisa::decode_fused_ok(k, bf)) {
+    int* cnt = at<int>(ws, l.cnt);
+    hipError_t e = timed("decode_scan_select", st, [&] {
+      return hisa::launch_decode_scan(k, bf, q_idx, w, keys, t0, fscore, cscore, cnt, I_out, top_blk_out, path_out, st);
+    });
+    if (e != hipSuccess) return launch_fail(e, "decode scan + select");
+    return HISA_OK;
+  }
+  hipError_t e = timed("decode_scan", st, [&] {
+    return hisa::launch_decode_scan(k, bf, q_idx, w, keys, t0, fscore, cscore, nullptr, nullptr, nullptr, nullptr, st);
+  });
   if (e != hipSuccess) return launch_fail(e, "decode scan");
   e = timed("decode_select", st, [&] { return hisa::launch_decode_select(k, fscore, cscore, t0, I_out, top_blk_out, path_out, st); });
   if (e != hipSuccess) return launch_fail(e, "decode select");

@@ -22,9 +22,13 @@ struct KDims {
 
 // Launchers (kernel files).  Each returns hipSuccess or the launch error.
 // Pointers are device pointers; bf16 data is passed as uint16_t.
+// Decode scan; with cnt != NULL (decode_fused_ok) it also runs the selection
+// and writes I / top_blk / path, and launch_decode_select is not needed.
+// cnt: B zeroed ints, left zeroed.
+bool decode_fused_ok(const KDims& d, bool bf16);
 hipError_t launch_decode_scan(const KDims& d, bool bf16, const void* q_idx, const float* w,
                               const void* keys, const int* t0, float* fscore, float* cscore,
-                              hipStream_t st);
+                              int* cnt, int* I, int* top_blk, int* path, hipStream_t st);
 hipError_t launch_decode_select(const KDims& d, const float* fscore, const float* cscore,
                                 const int* t0, int* I, int* top_blk, int* path, hipStream_t st);
 hipError_t launch_block_mean(const KDims& d, bool bf16, bool all_paths, const void* keys,

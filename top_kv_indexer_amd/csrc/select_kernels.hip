@@ -30,7 +30,177 @@ constexpr int KP = 136;  // LDS row pitch (bf16) of 128-dim rows: 272 B, 4 banks
 __device__ __forceinline__ bf16x8 lds8(const uint16_t* p) { return *(const bf16x8*)p; }
 __device__ __forceinline__ bf16x8 ldg8(const uint16_t* p) { return *(const bf16x8*)p; }
 
+// ------------------------------------------------------------------ in-wave top-k
+
+// Top-k inside one wave on register-resident keys (element r of lane l has
+// order index 64r + l, ascending in block id / pooled row): a bitwise search
+// finds the k-th largest key, and ballots emit the winners in ascending
+// order index, ties at the threshold going to the lowest indices.
+constexpr int kRowR = 16;     // keys per lane: up to 1024 blocks or candidates
+constexpr int kRowKeep = 64;  // retained blocks per row
+
+// Number of the wave's keys (registers r < NR) at or above the uniform c:
+// every compare goes to its own lane mask first, so the compares issue back
+// to back and the scalar popcounts follow.
+template <int NR>
+__device__ __forceinline__ int wave_count_ge(const uint32_t (&key)[kRowR], uint32_t c) {
+  uint64_t m[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) m[r] = __ballot(key[r] >= c);
+  // keep the compares together: a popcount placed between them would wait
+  // for the previous compare's mask to reach the scalar unit
+  __builtin_amdgcn_sched_barrier(0);
+  int cnt = 0;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) cnt += (int)__popcll(m[r]);
+  return cnt;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u<kDppXor1>(v));
+  v = max(v, dpp_u<kDppXor2>(v));
+  v = max(v, dpp_u<kDppHalfMirror>(v));
+  v = max(v, dpp_u<kDppMirror>(v));
+  u32x2 p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max(p.x, p.y);
+  p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max(p.x, p.y);
+}
+
+// Threshold of the top k of the wave's keys in registers r < NR (absent
+// entries carry key 0; 1 <= k <= number of present entries).  Returns t and
+// `ties`, such that the top k are the keys > t plus the first `ties` keys
+// == t in order index.  A bisection over [min, max] of the present keys
+// keeps count(>= lo) >= k and count(>= hi + 1) < k; it stops early at a
+// midpoint with exactly k keys at or above it (then every key >= t is
+// taken), otherwise it ends with lo == hi == the k-th largest key.  Distinct
+// scores separate after about log2(n) steps, ties cost at most 32.
+template <int NR>
+__device__ __forceinline__ uint32_t wave_topk_threshold(const uint32_t (&key)[kRowR], int k, int& ties) {
+  uint32_t hi = 0, nlo = 0;  // max key, and max of ~key over present keys (= ~min)
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    hi = max(hi, key[r]);
+    nlo = max(nlo, key[r] ? ~key[r] : 0u);
+  }
+  hi = __builtin_amdgcn_readfirstlane(wave_max_u32(hi));
+  uint32_t lo = ~__builtin_amdgcn_readfirstlane(wave_max_u32(nlo));
+  while (lo < hi) {
+    const uint32_t mid = lo + (hi - lo) / 2 + 1;  // in (lo, hi]
+    const int c = wave_count_ge<NR>(key, mid);
+    if (c >= k) {
+      lo = mid;
+      if (c == k) {
+        ties = k;  // every key == mid is inside the top k
+        return mid;
+      }
+    } else {
+      hi = mid - 1;
+    }
+  }
+  ties = lo == ~0u ? k : k - wave_count_ge<NR>(key, lo + 1);
+  return lo;
+}
+
+// emits the k winners in ascending order index: emit(slot, r)
+template <int NR, class EmitF>
+__device__ __forceinline__ void wave_emit_topk_n(const uint32_t (&key)[kRowR], int k, EmitF emit) {
+  int ties;
+  const uint32_t t = wave_topk_threshold<NR>(key, k, ties);
+  int base = 0;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const bool eq = key[r] == t;
+    const uint64_t meq = __ballot(eq);
+    const bool take = key[r] > t || (eq && lanes_below(meq) < ties);
+    ties -= min(ties, (int)__popcll(meq));
+    const uint64_t mt = __ballot(take);
+    if (take) emit(base + lanes_below(mt), r);
+    base += (int)__popcll(mt);
+  }
+}
+
+// the same for nr <= 16 registers in use (keys of registers >= nr are 0)
+template <class EmitF>
+__device__ __forceinline__ void wave_emit_topk(const uint32_t (&key)[kRowR], int nr, int k, EmitF emit) {
+  if (nr <= 4) wave_emit_topk_n<4>(key, k, emit);
+  else if (nr <= 8) wave_emit_topk_n<8>(key, k, emit);
+  else wave_emit_topk_n<kRowR>(key, k, emit);
+}
+
 // ------------------------------------------------------------------ decode scan
+
+// Selection outputs of a sequence that is not scored: I = 0..Np-1 (dense) or
+// -1 (invalid t0), no retained blocks.
+__device__ __forceinline__ void write_unscored(const KDims& d, const SeqInfo& si, int b, int* I, int* top_blk,
+                                               int* path) {
+  const int lane = lane_id();
+  const bool dense = si.ok && si.path == PATH_DENSE;
+  for (int i = lane; i < d.topk; i += 64) I[(size_t)b * d.topk + i] = (dense && i < si.Np) ? i : -1;
+  if (top_blk)
+    for (int i = lane; i < d.index_keep; i += 64) top_blk[(size_t)b * d.index_keep + i] = -1;
+  if (path && lane == 0) path[b] = si.path;
+}
+
+// Device-scope (all XCDs) store and load of a score: written through to, and
+// read from, the device's coherence point, so publishing them needs no L2
+// write-back.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Decode selection of sequence b by one wave, from the scan's fine scores fs
+// (Np entries) and block scores cs (nb entries): the flat top-k (Np <= 1024),
+// or the coarse top-Kb blocks (nb <= 1024, Kb <= 64) and the fine top-k of
+// their C = Kb*b <= 1024 rows (HiSA issue, HiSA decode path).  Ids come out
+// ascending, padded with -1.
+__device__ __forceinline__ void decode_select_wave(const KDims& d, const SeqInfo& si, int b, const float* fs,
+                                                   const float* cs, int* I, int* top_blk, int* path, int* s_blk) {
+  const int lane = lane_id();
+  int* Ib = I + (size_t)b * d.topk;
+  int* blkb = top_blk ? top_blk + (size_t)b * d.index_keep : nullptr;
+  for (int i = lane; i < d.topk; i += 64)
+    if (i >= si.k) Ib[i] = -1;
+  if (blkb)
+    for (int i = lane; i < d.index_keep; i += 64)
+      if (si.path != PATH_HISA || i >= si.Kb) blkb[i] = -1;
+  if (path && lane == 0) path[b] = si.path;
+  uint32_t key[kRowR];
+  if (si.path == PATH_FLAT) {
+    const int n = si.Np, nr = (n + 63) / 64;
+#pragma unroll
+    for (int r = 0; r < kRowR; ++r) {  // loads first (clamped, all in flight), then keys
+      const int i = 64 * r + lane;
+      const float v = ld_dev(fs + min(i, n - 1));
+      key[r] = (r < nr && i < n) ? score_key(v) : 0u;
+    }
+    wave_emit_topk(key, nr, si.k, [&](int slot, int r) { Ib[slot] = 64 * r + lane; });
+    return;
+  }
+  const int nb = si.nb, nrc = (nb + 63) / 64;
+#pragma unroll
+  for (int r = 0; r < kRowR; ++r) {
+    const int i = 64 * r + lane;
+    const float v = ld_dev(cs + min(i, nb - 1));
+    key[r] = (r < nrc && i < nb) ? score_key(v) : 0u;
+  }
+  wave_emit_topk(key, nrc, si.Kb, [&](int slot, int r) { s_blk[slot] = 64 * r + lane; });
+  if (blkb)
+    for (int i = lane; i < si.Kb; i += 64) blkb[i] = s_blk[i];
+  const int bsz = d.index_block, lbsz = __builtin_ctz(bsz);
+  const int C = si.Kb * bsz, nrf = (C + 63) / 64;
+  auto cand = [&](int cc) { return (s_blk[cc >> lbsz] << lbsz) + (cc & (bsz - 1)); };
+#pragma unroll
+  for (int r = 0; r < kRowR; ++r) {
+    const int cc = 64 * r + lane;
+    const float v = ld_dev(fs + cand(min(cc, C - 1)));
+    key[r] = (r < nrf && cc < C) ? score_key(v) : 0u;
+  }
+  wave_emit_topk(key, nrf, si.k, [&](int slot, int r) { Ib[slot] = cand(64 * r + lane); });
+}
 
 // One wave per `spw` consecutive 64-row slabs of one sequence (bf16,
 // H_i = 64, D_i = 128, index_block | 64).  A slab's four 16-row tiles of keys
@@ -41,12 +211,17 @@ __device__ __forceinline__ bf16x8 ldg8(const uint16_t* p) { return *(const bf16x
 // are read.  MFMA gives D[h][row] = q_h . key_row.  Fine score of a row:
 // sum_h relu(D) w_eff.  Coarse score of a block: the block mean is linear, so
 // q_h . rep_beta is the mean of D[h][row] over the block's rows; it is summed
-// across the lanes that hold those rows, then relu'd and weighted.  No LDS,
-// no barriers.
+// across the lanes that hold those rows, then relu'd and weighted.  No
+// barriers.
+// With cnt != NULL the selection is fused: each wave stores its scores at
+// device scope, waits for them to be acknowledged, counts itself in cnt[b],
+// and the last wave of the sequence runs decode_select_wave on everyone's
+// scores; it returns cnt[b] to 0 for the next call.  The first wave of a dense or
+// invalid sequence writes its outputs.
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_decode_scan_mfma(
     KDims d, int spw, const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
-    const uint16_t* __restrict__ keys, const int* __restrict__ t0, float* __restrict__ fscore,
-    float* __restrict__ cscore) {
+    const uint16_t* __restrict__ keys, const int* __restrict__ t0, float* fscore, float* cscore, int* cnt,
+    int* I, int* top_blk, int* path) {
   const int b = blockIdx.y;
   const int slab0 = blockIdx.x * spw;
   const int lane = threadIdx.x, g = lane >> 4, c = lane & 15;
@@ -77,7 +252,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
 #pragma unroll
     for (int i = 0; i < 4; ++i) wl[ht][i] = w[(size_t)b * d.L * 64 + ht * 16 + 4 * g + i] * d.w_scale;
   const SeqInfo si = seq_info(d, t0[b]);
-  if (!si.ok || si.path == PATH_DENSE) return;
+  if (!si.ok || si.path == PATH_DENSE) {
+    if (cnt && blockIdx.x == 0) write_unscored(d, si, b, I, top_blk, path);
+    return;
+  }
   const int nslab = (si.Np + 63) / 64;
   if (slab0 >= nslab) return;
   if (!early) load(slab0, si.Np - 1, ka);
@@ -108,7 +286,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
         for (int i = 0; i < 4; ++i) v += fmaxf(acc[ht][i], 0.f) * wl[ht][i];
       v = sum_rows(v);
       const int r = row0 + t * 16 + c;
-      if (g == 0 && r < si.Np) fscore[(size_t)b * d.Np_cap + r] = v;
+      if (g == 0 && r < si.Np) st_dev(fscore + (size_t)b * d.Np_cap + r, v);
       if (!hisa_path) continue;
       // Block sums: rows of a block are consecutive lanes c (and tiles t).
 #pragma unroll
@@ -134,7 +312,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
       // lane c holds the sum of the block containing its row
       const int beta = (row0 + t * 16 + c) / bsz;
       const bool first_lane = bsz >= 16 ? c == 0 : (c % bsz) == 0;
-      if (g == 0 && first_lane && beta < si.nb) cscore[(size_t)b * d.nb_cap + beta] = cv;
+      if (g == 0 && first_lane && beta < si.nb) st_dev(cscore + (size_t)b * d.nb_cap + beta, cv);
     }
   };
   for (int u = 0; u < spw; u += 2) {
@@ -145,6 +323,23 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     if (u + 2 < spw && slab0 + u + 2 < nslab) load(slab0 + u + 2, si.Np - 1, ka);
     score(slab0 + u + 1, kn);
   }
+  if (!cnt) return;
+  __shared__ int s_blk[kRowKeep];
+  const int nw = (nslab + spw - 1) / spw;  // waves scoring sequence b
+  // Publish: every score store above is device-scope; wait until all of them
+  // are acknowledged before this wave counts itself.
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0
+  asm volatile("" ::: "memory");
+  int prev = 0;
+  if (lane == 0) prev = __hip_atomic_fetch_add(cnt + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  prev = __builtin_amdgcn_readfirstlane(prev);
+  if (prev != nw - 1) return;
+  // the last wave: every wave's scores are at the coherence point, and the
+  // selection reads them with device-scope loads
+  if (lane == 0) __hip_atomic_store(cnt + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  decode_select_wave(d, si, b, fscore + (size_t)b * d.Np_cap, cscore + (size_t)b * d.nb_cap, I, top_blk, path,
+                     s_blk);
 }
 
 // Any shape / dtype: 4 threads per row, VALU dot products.
@@ -579,48 +774,6 @@ __global__ __launch_bounds__(256) void k_fine_valu(KDims d, const T* __restrict_
 // which is ascending in block id / pooled row): a bitwise search finds the
 // k-th largest key, and ballots emit the winners in ascending id order, ties
 // at the threshold going to the lowest ids.
-constexpr int kRowR = 16;     // keys per lane: up to 1024 blocks or candidates
-constexpr int kRowKeep = 64;  // retained blocks per row
-
-// k-th largest of the wave's keys (absent entries carry key 0, k <= number
-// of present entries); returns it with the count of strictly larger keys
-__device__ __forceinline__ uint32_t wave_kth_key(const uint32_t (&key)[kRowR], int k, int& n_gt) {
-  // absent entries (key 0) never reach a candidate, which always has a bit set
-  uint32_t t = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = t | (1u << bit);
-    int cnt = 0;
-#pragma unroll
-    for (int r = 0; r < kRowR; ++r) cnt += key[r] >= cand ? 1 : 0;
-    if (wave_sum_i(cnt) >= k) t = cand;
-  }
-  int gt = 0;
-#pragma unroll
-  for (int r = 0; r < kRowR; ++r) gt += key[r] > t ? 1 : 0;
-  n_gt = wave_sum_i(gt);
-  return t;
-}
-
-// emits the k winners in ascending order index: emit(slot, r)
-template <class EmitF>
-__device__ __forceinline__ void wave_emit_topk(const uint32_t (&key)[kRowR], int nr, int k, EmitF emit) {
-  int n_gt;
-  const uint32_t t = wave_kth_key(key, k, n_gt);
-  int ties = k - n_gt, base = 0;
-#pragma unroll
-  for (int r = 0; r < kRowR; ++r) {
-    if (r < nr) {
-      const bool eq = key[r] == t;
-      const uint64_t meq = __ballot(eq);
-      const bool take = key[r] > t || (eq && lanes_below(meq) < ties);
-      ties -= min(ties, (int)__popcll(meq));
-      const uint64_t mt = __ballot(take);
-      if (take) emit(base + lanes_below(mt), r);
-      base += (int)__popcll(mt);
-    }
-  }
-}
-
 __global__ __launch_bounds__(256) void k_select_rows(KDims d, const uint16_t* __restrict__ q_idx,
                                                      const float* __restrict__ w, const uint16_t* __restrict__ keys,
                                                      const uint16_t* __restrict__ rep3, const int* __restrict__ t0,
@@ -951,15 +1104,27 @@ __global__ __launch_bounds__(kTopkRowsThreads) void k_topk_rows(KDims d, int lds
 
 static inline unsigned cdiv(long long a, long long b) { return (unsigned)((a + b - 1) / b); }
 
+bool decode_fused_ok(const KDims& d, bool bf16) {
+  // every sequence's selection fits one wave: nb, C <= 1024 and Kb <= 64;
+  // a flat sequence has Np <= 1024 unless the gate can send a larger one
+  // there (forced flat, or b * keep < topk)
+  const long long bk = (long long)d.index_keep * d.index_block;
+  const bool big_flat = d.Np_cap > 64 * kRowR && (d.force_flat || bk < d.topk);
+  return idx_mfma_ok(d, bf16) && d.index_block > 0 && d.nb_cap <= 64 * kRowR && bk <= 64 * kRowR &&
+         d.index_keep <= kRowKeep && !big_flat;
+}
+
 hipError_t launch_decode_scan(const KDims& d, bool bf16, const void* q_idx, const float* w, const void* keys,
-                              const int* t0, float* fscore, float* cscore, hipStream_t st) {
+                              const int* t0, float* fscore, float* cscore, int* cnt, int* I, int* top_blk,
+                              int* path, hipStream_t st) {
   const dim3 grid(cdiv(d.Np_cap, 64), d.B);
   if (idx_mfma_ok(d, bf16)) {
     // several slabs per wave once there are enough to fill the chip
     const long long slabs = (long long)cdiv(d.Np_cap, 64) * d.B;
     const int spw = slabs >= 8192 ? 4 : slabs >= 4096 ? 2 : 1;
     hipLaunchKernelGGL(k_decode_scan_mfma, dim3(cdiv(d.Np_cap, 64 * spw), d.B), dim3(64), 0, st, d, spw,
-                       (const uint16_t*)q_idx, w, (const uint16_t*)keys, t0, fscore, cscore);
+                       (const uint16_t*)q_idx, w, (const uint16_t*)keys, t0, fscore, cscore, cnt, I, top_blk,
+                       path);
   }
   else if (bf16)
     hipLaunchKernelGGL(k_decode_scan_valu<uint16_t>, grid, dim3(256), 0, st, d, (const uint16_t*)q_idx, w,

@@ -119,7 +119,8 @@ def _workspace(op: int, d: hisa_dims, dev: torch.device, ws: Optional[torch.Tens
         return ws, ws.numel() * ws.element_size()
     if n == 0:
         return None, 0
-    return torch.empty(n, dtype=torch.uint8, device=dev), n
+    # zero-filled: the decode selection keeps arrival counters at its start
+    return torch.zeros(n, dtype=torch.uint8, device=dev), n
 
 
 def selection_dims(q_idx, keys, *, ratio, topk, index_block, index_keep, mode=MODE_AUTO) -> hisa_dims:

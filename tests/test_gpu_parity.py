@@ -250,6 +250,38 @@ def test_decode_workspace_reuse(hisa):
     assert (ws[: 4 * w.B].view(torch.int32) == 0).all()
 
 
+MIXED_STREAM = MIXED.with_(name="mixed_paths_b7_stream", B=7, t0=[1200, 2800, 4096, 6000, 160000, 16400, 90000],
+                           Np_cap=40000)
+
+
+def test_mixed_paths_decode_stream(hisa):
+    # Many 64-row slabs (7 x 625) take the persistent scan over the flattened
+    # live slabs: dense (Np 300), flat (700), HiSA with and without a tail
+    # block and with long pooled prefixes; one sequence then turns invalid
+    # (Np > Np_cap) on a reused workspace.
+    w = MIXED_STREAM
+    x, g = inputs(w, 21)
+    od = odims(w, x)
+    d = hisa.selection_dims(g["q_idx"], g["keys"], ratio=4, topk=512, index_block=64, index_keep=16)
+    ws = torch.zeros(hisa.workspace_bytes(hisa.OP_SELECT_DECODE, d), dtype=torch.uint8, device="cuda")
+    for t0s in (list(w.t0), [1200, 2800, 4096, 6000, 200000, 16400, 60000]):
+        say(f"[run] streaming decode scan, t0 = {t0s}")
+        t0 = torch.tensor(t0s, dtype=torch.int32, device="cuda")
+        I, blk, path = hisa.hisa_select_decode(g["q_idx"], g["w"], g["keys"], t0, **sel_kw(w), ws=ws)
+        torch.cuda.synchronize()
+        xx = dict(x)
+        xx["t0"] = np.array(t0s, np.int32)
+        In, bn, p = parity.to_np(I), parity.to_np(blk), parity.to_np(path)
+        for b in range(w.B):
+            if t0s[b] == 200000:  # Np = 50000 > Np_cap
+                assert p[b] == hisa.PATH_INVALID and (In[b] == -1).all() and (bn[b] == -1).all()
+                continue
+            Io, blko, po = oracle.select_row(od, xx["q_idx"][b, 0], xx["w"][b, 0], xx["keys"][b], t0s[b], 0)
+            assert p[b] == po, (b, p[b], po)
+            parity.check_selection_row(od, xx, b, 0, In[b, 0], bn[b, 0], p[b], Io, blko, po)
+    assert (ws[: 4 * w.B].view(torch.int32) == 0).all()
+
+
 def test_invalid_sequence_outputs(hisa):
     x, g = inputs(MIXED, 5)
     w = MIXED

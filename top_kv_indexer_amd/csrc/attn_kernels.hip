@@ -34,12 +34,12 @@ struct RowPlan {
 
 __device__ __forceinline__ RowPlan row_plan(const KDims& d, int T0, int j) {
   RowPlan r;
-  const long long np = ((long long)T0 + d.L) / d.ratio;
+  const uint32_t np = T0 >= 0 ? div_ratio(d, (uint32_t)T0 + (uint32_t)d.L) : 0u;
   r.ls = max(0, T0 - d.window + 1);
-  r.ok = T0 >= 0 && np <= d.Np_cap && (d.window == 0 || T0 + d.L - r.ls <= d.Wl_cap);
+  r.ok = T0 >= 0 && np <= (uint32_t)d.Np_cap && (d.window == 0 || (long long)T0 + d.L - r.ls <= d.Wl_cap);
   r.Np = r.ok ? (int)np : 0;
   const int t = T0 + j;
-  r.V = visible(t, d.ratio, r.Np);
+  r.V = visible(d, t, r.Np);
   r.s_lo = max(r.ls, t - d.window + 1);
   r.n_loc = (r.ok && d.window > 0) ? t - r.s_lo + 1 : 0;
   r.n_list = r.ok ? r.n_loc + d.kI : 0;

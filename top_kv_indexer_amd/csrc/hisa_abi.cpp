@@ -60,6 +60,7 @@ int make_kdims(int op, const hisa_dims* d, KDims* k) {
   kd.index_block = d->index_block; kd.index_keep = d->index_keep; kd.H_i = d->H_i; kd.D_i = d->D_i;
   kd.H = d->H; kd.Dk = d->Dk; kd.Dv = d->Dv; kd.Np_cap = d->Np_cap; kd.Wl_cap = d->Wl_cap; kd.kI = d->kI;
   kd.force_flat = d->mode == HISA_MODE_FORCE_FLAT;
+  kd.ratio_shift = (d->ratio > 0 && (d->ratio & (d->ratio - 1)) == 0) ? __builtin_ctz((unsigned)d->ratio) : -1;
   kd.force_path = -1;
   if (is_sel(op)) {
     if (d->idx_dtype != HISA_F32 && d->idx_dtype != HISA_BF16) return fail(HISA_ERR_DTYPE, "idx_dtype %d", d->idx_dtype);

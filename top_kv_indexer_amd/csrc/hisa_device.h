@@ -179,10 +179,17 @@ struct SeqInfo {
   bool ok;
 };
 
+// floor(x / ratio) for 0 <= x < 2^32: a shift for power-of-two ratios, else
+// one 32-bit unsigned division
+__device__ __forceinline__ uint32_t div_ratio(const KDims& d, uint32_t x) {
+  return d.ratio_shift >= 0 ? x >> d.ratio_shift : x / (uint32_t)d.ratio;
+}
+
 __device__ __forceinline__ SeqInfo seq_info(const KDims& d, int t0) {
   SeqInfo s;
-  const long long np = ((long long)t0 + d.L) / d.ratio;
-  s.ok = t0 >= 0 && np <= d.Np_cap;
+  // t0 + L < 2^32 for any t0 >= 0 (L <= 524280): unsigned 32-bit math is exact
+  const uint32_t np = t0 >= 0 ? div_ratio(d, (uint32_t)t0 + (uint32_t)d.L) : 0u;
+  s.ok = t0 >= 0 && np <= (uint32_t)d.Np_cap;
   s.Np = s.ok ? (int)np : 0;
   s.k = min(d.topk, s.Np);
   s.nb = d.index_block > 0 ? s.Np / d.index_block : 0;
@@ -196,8 +203,9 @@ __device__ __forceinline__ SeqInfo seq_info(const KDims& d, int t0) {
   return s;
 }
 
-__device__ __forceinline__ int visible(int t, int ratio, int Np) {
-  return min(Np, (int)(((long long)t + 1) / ratio));
+// V(t) = min(Np, floor((t + 1) / ratio)) for query position t (0 for t < 0)
+__device__ __forceinline__ int visible(const KDims& d, int t, int Np) {
+  return t < 0 ? 0 : min(Np, (int)div_ratio(d, (uint32_t)t + 1u));
 }
 
 // Shared memory of block_topk.

@@ -16,6 +16,7 @@ struct KDims {
   int force_flat;  // HISA_MODE_FORCE_FLAT
   int force_path;  // -1: run the gate; PATH_FLAT: flat for every valid sequence
   int nb_cap;      // Np_cap / index_block (0 when index_block == 0)
+  int ratio_shift; // log2(ratio) when ratio is a power of two, else -1
   float w_scale;   // (float)(1 / sqrt(H_i * D_i)), rounded once from double
   float attn_scale_log2;  // (float)(log2(e) / sqrt(Dk))
 };

@@ -39,74 +39,57 @@ __device__ __forceinline__ bf16x8 ldg8(const uint16_t* p) { return *(const bf16x
 constexpr int kRowR = 16;     // keys per lane: up to 1024 blocks or candidates
 constexpr int kRowKeep = 64;  // retained blocks per row
 
-// Number of the wave's keys (registers r < NR) at or above the uniform c:
-// every compare goes to its own lane mask first, so the compares issue back
-// to back and the scalar popcounts follow.
-template <int NR>
-__device__ __forceinline__ int wave_count_ge(const uint32_t (&key)[kRowR], uint32_t c) {
-  uint64_t m[NR];
-#pragma unroll
-  for (int r = 0; r < NR; ++r) m[r] = __ballot(key[r] >= c);
-  // keep the compares together: a popcount placed between them would wait
-  // for the previous compare's mask to reach the scalar unit
-  __builtin_amdgcn_sched_barrier(0);
-  int cnt = 0;
-#pragma unroll
-  for (int r = 0; r < NR; ++r) cnt += (int)__popcll(m[r]);
-  return cnt;
-}
-
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, dpp_u<kDppXor1>(v));
-  v = max(v, dpp_u<kDppXor2>(v));
-  v = max(v, dpp_u<kDppHalfMirror>(v));
-  v = max(v, dpp_u<kDppMirror>(v));
-  u32x2 p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  v = max(p.x, p.y);
-  p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  return max(p.x, p.y);
-}
-
 // Threshold of the top k of the wave's keys in registers r < NR (absent
-// entries carry key 0; 1 <= k <= number of present entries).  Returns t and
-// `ties`, such that the top k are the keys > t plus the first `ties` keys
-// == t in order index.  A bisection over [min, max] of the present keys
-// keeps count(>= lo) >= k and count(>= hi + 1) < k; it stops early at a
-// midpoint with exactly k keys at or above it (then every key >= t is
-// taken), otherwise it ends with lo == hi == the k-th largest key.  Distinct
-// scores separate after about log2(n) steps, ties cost at most 32.
+// entries carry key 0; 1 <= k <= number of present entries): returns the
+// k-th largest key t and `ties`, the number of keys == t inside the top k
+// (taken in order index).  Radix select, most significant byte first: per
+// pass the keys that still match the known prefix are counted into a
+// 256-bin histogram in LDS (hist: 256 words owned by this wave), and a wave
+// prefix sum over the bins, largest first, finds the byte of the k-th key.
 template <int NR>
-__device__ __forceinline__ uint32_t wave_topk_threshold(const uint32_t (&key)[kRowR], int k, int& ties) {
-  uint32_t hi = 0, nlo = 0;  // max key, and max of ~key over present keys (= ~min)
+__device__ __forceinline__ uint32_t wave_topk_threshold(const uint32_t (&key)[kRowR], int k, uint32_t* hist,
+                                                        int& ties) {
+  const int lane = lane_id();
+  uint32_t prefix = 0, mask = 0;
+  int remaining = k;  // keys still to take at or below the current prefix
+#pragma unroll 1
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    // one wave's LDS operations complete in program order: the clear lands
+    // before the adds, the adds before the read
+    *(uint4*)&hist[4 * lane] = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    hi = max(hi, key[r]);
-    nlo = max(nlo, key[r] ? ~key[r] : 0u);
-  }
-  hi = __builtin_amdgcn_readfirstlane(wave_max_u32(hi));
-  uint32_t lo = ~__builtin_amdgcn_readfirstlane(wave_max_u32(nlo));
-  while (lo < hi) {
-    const uint32_t mid = lo + (hi - lo) / 2 + 1;  // in (lo, hi]
-    const int c = wave_count_ge<NR>(key, mid);
-    if (c >= k) {
-      lo = mid;
-      if (c == k) {
-        ties = k;  // every key == mid is inside the top k
-        return mid;
-      }
-    } else {
-      hi = mid - 1;
+    for (int r = 0; r < NR; ++r) {
+      const uint32_t u = key[r];
+      if (u != 0u && (u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
     }
+    // lane l holds bins 255-4l (first) .. 252-4l
+    const uint4 h = *(const uint4*)&hist[252 - 4 * lane];
+    const uint32_t local = h.x + h.y + h.z + h.w;
+    const uint32_t incl = wave_incl_scan(local);
+    const uint32_t above = incl - local;  // keys in bins above this lane's
+    const bool hit = above < (uint32_t)remaining && incl >= (uint32_t)remaining;
+    const int src = __builtin_ctzll(__ballot(hit));
+    uint32_t acc = above, digit = 252 - 4 * lane;
+    if (acc + h.w >= (uint32_t)remaining) digit = 255 - 4 * lane;
+    else if ((acc += h.w) + h.z >= (uint32_t)remaining) digit = 254 - 4 * lane;
+    else if ((acc += h.z) + h.y >= (uint32_t)remaining) digit = 253 - 4 * lane;
+    else acc += h.y;
+    digit = (uint32_t)__builtin_amdgcn_readlane((int)digit, src);
+    acc = (uint32_t)__builtin_amdgcn_readlane((int)acc, src);
+    remaining -= (int)acc;
+    prefix |= digit << shift;
+    mask |= 0xFFu << shift;
   }
-  ties = lo == ~0u ? k : k - wave_count_ge<NR>(key, lo + 1);
-  return lo;
+  ties = remaining;
+  return prefix;
 }
 
 // emits the k winners in ascending order index: emit(slot, r)
 template <int NR, class EmitF>
-__device__ __forceinline__ void wave_emit_topk_n(const uint32_t (&key)[kRowR], int k, EmitF emit) {
+__device__ __forceinline__ void wave_emit_topk_n(const uint32_t (&key)[kRowR], int k, uint32_t* hist, EmitF emit) {
   int ties;
-  const uint32_t t = wave_topk_threshold<NR>(key, k, ties);
+  const uint32_t t = wave_topk_threshold<NR>(key, k, hist, ties);
   int base = 0;
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
@@ -122,10 +105,11 @@ __device__ __forceinline__ void wave_emit_topk_n(const uint32_t (&key)[kRowR], i
 
 // the same for nr <= 16 registers in use (keys of registers >= nr are 0)
 template <class EmitF>
-__device__ __forceinline__ void wave_emit_topk(const uint32_t (&key)[kRowR], int nr, int k, EmitF emit) {
-  if (nr <= 4) wave_emit_topk_n<4>(key, k, emit);
-  else if (nr <= 8) wave_emit_topk_n<8>(key, k, emit);
-  else wave_emit_topk_n<kRowR>(key, k, emit);
+__device__ __forceinline__ void wave_emit_topk(const uint32_t (&key)[kRowR], int nr, int k, uint32_t* hist,
+                                               EmitF emit) {
+  if (nr <= 4) wave_emit_topk_n<4>(key, k, hist, emit);
+  else if (nr <= 8) wave_emit_topk_n<8>(key, k, hist, emit);
+  else wave_emit_topk_n<kRowR>(key, k, hist, emit);
 }
 
 // ------------------------------------------------------------------ decode scan
@@ -158,7 +142,8 @@ __device__ __forceinline__ float ld_dev(const float* p) {
 // their C = Kb*b <= 1024 rows (HiSA issue, HiSA decode path).  Ids come out
 // ascending, padded with -1.
 __device__ __forceinline__ void decode_select_wave(const KDims& d, const SeqInfo& si, int b, const float* fs,
-                                                   const float* cs, int* I, int* top_blk, int* path, int* s_blk) {
+                                                   const float* cs, int* I, int* top_blk, int* path, int* s_blk,
+                                                   uint32_t* hist) {
   const int lane = lane_id();
   int* Ib = I + (size_t)b * d.topk;
   int* blkb = top_blk ? top_blk + (size_t)b * d.index_keep : nullptr;
@@ -171,175 +156,355 @@ __device__ __forceinline__ void decode_select_wave(const KDims& d, const SeqInfo
   uint32_t key[kRowR];
   if (si.path == PATH_FLAT) {
     const int n = si.Np, nr = (n + 63) / 64;
+    float v[kRowR];
 #pragma unroll
-    for (int r = 0; r < kRowR; ++r) {  // loads first (clamped, all in flight), then keys
-      const int i = 64 * r + lane;
-      const float v = ld_dev(fs + min(i, n - 1));
-      key[r] = (r < nr && i < n) ? score_key(v) : 0u;
-    }
-    wave_emit_topk(key, nr, si.k, [&](int slot, int r) { Ib[slot] = 64 * r + lane; });
+    for (int r = 0; r < kRowR; ++r) v[r] = ld_dev(fs + min(64 * r + lane, n - 1));
+    __builtin_amdgcn_sched_barrier(0);  // every load in flight before the first wait
+#pragma unroll
+    for (int r = 0; r < kRowR; ++r) key[r] = (r < nr && 64 * r + lane < n) ? score_key(v[r]) : 0u;
+    wave_emit_topk(key, nr, si.k, hist, [&](int slot, int r) { Ib[slot] = 64 * r + lane; });
     return;
   }
   const int nb = si.nb, nrc = (nb + 63) / 64;
+  float v[kRowR];
 #pragma unroll
-  for (int r = 0; r < kRowR; ++r) {
-    const int i = 64 * r + lane;
-    const float v = ld_dev(cs + min(i, nb - 1));
-    key[r] = (r < nrc && i < nb) ? score_key(v) : 0u;
-  }
-  wave_emit_topk(key, nrc, si.Kb, [&](int slot, int r) { s_blk[slot] = 64 * r + lane; });
+  for (int r = 0; r < kRowR; ++r) v[r] = ld_dev(cs + min(64 * r + lane, nb - 1));
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int r = 0; r < kRowR; ++r) key[r] = (r < nrc && 64 * r + lane < nb) ? score_key(v[r]) : 0u;
+  wave_emit_topk(key, nrc, si.Kb, hist, [&](int slot, int r) { s_blk[slot] = 64 * r + lane; });
   if (blkb)
     for (int i = lane; i < si.Kb; i += 64) blkb[i] = s_blk[i];
   const int bsz = d.index_block, lbsz = __builtin_ctz(bsz);
   const int C = si.Kb * bsz, nrf = (C + 63) / 64;
-  auto cand = [&](int cc) { return (s_blk[cc >> lbsz] << lbsz) + (cc & (bsz - 1)); };
+  // candidate cc is row s_blk[cc / b] * b + cc % b: every position first
+  // (LDS reads back to back), then every score load
+  int pos[kRowR];
 #pragma unroll
   for (int r = 0; r < kRowR; ++r) {
-    const int cc = 64 * r + lane;
-    const float v = ld_dev(fs + cand(min(cc, C - 1)));
-    key[r] = (r < nrf && cc < C) ? score_key(v) : 0u;
+    const int cc = min(64 * r + lane, C - 1);
+    pos[r] = (s_blk[cc >> lbsz] << lbsz) + (cc & (bsz - 1));
   }
-  wave_emit_topk(key, nrf, si.k, [&](int slot, int r) { Ib[slot] = cand(64 * r + lane); });
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int r = 0; r < kRowR; ++r) v[r] = ld_dev(fs + pos[r]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int r = 0; r < kRowR; ++r) key[r] = (r < nrf && 64 * r + lane < C) ? score_key(v[r]) : 0u;
+  wave_emit_topk(key, nrf, si.k, hist, [&](int slot, int r) { Ib[slot] = pos[r]; });
 }
 
-// One wave per `spw` consecutive 64-row slabs of one sequence (bf16,
-// H_i = 64, D_i = 128, index_block | 64).  A slab's four 16-row tiles of keys
-// go straight from HBM into registers (16 loads in flight) and the next
-// slab's keys stream in while the current one is scored.  With one slab per
-// wave (few slabs, latency-bound) the loads go out before t0 arrives, rows
-// clamped to the buffer rather than to Np; with several, only slabs below Np
-// are read.  MFMA gives D[h][row] = q_h . key_row.  Fine score of a row:
-// sum_h relu(D) w_eff.  Coarse score of a block: the block mean is linear, so
-// q_h . rep_beta is the mean of D[h][row] over the block's rows; it is summed
-// across the lanes that hold those rows, then relu'd and weighted.  No
-// barriers.
-// With cnt != NULL the selection is fused: each wave stores its scores at
-// device scope, waits for them to be acknowledged, counts itself in cnt[b],
-// and the last wave of the sequence runs decode_select_wave on everyone's
-// scores; it returns cnt[b] to 0 for the next call.  The first wave of a dense or
-// invalid sequence writes its outputs.
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_decode_scan_mfma(
-    KDims d, int spw, const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
-    const uint16_t* __restrict__ keys, const int* __restrict__ t0, float* fscore, float* cscore, int* cnt,
-    int* I, int* top_blk, int* path) {
-  const int b = blockIdx.y;
-  const int slab0 = blockIdx.x * spw;
-  const int lane = threadIdx.x, g = lane >> 4, c = lane & 15;
-  // Keys: lane (g, c) of tile t holds row 64*slab + 16t + c; MFMA step s takes
-  // dims 32s + 8g .. +7 (the k order of q below matches), so each load
-  // instruction reads one 64-byte run per row.
-  const uint16_t* kb = keys + (size_t)b * d.Np_cap * 128 + g * 8;
-  auto load = [&](int slab, int rmax, bf16x8 (&kf)[4][4]) {
+// relu as one instruction (v_med3): max(x, 0) for finite x
+__device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.f, 3.402823466e38f); }
+
+// ---- pieces shared by the two decode scan kernels (bf16, H_i = 64, D_i = 128,
+// index_block | 64, four waves per workgroup).  Wave w scores rows 16w ..
+// 16w+15 of a 64-row slab against all 64 heads: lane (g, c) holds row 16w + c
+// and MFMA step s takes dims 32s + 8g .. +7, so each load instruction reads
+// one 64-byte run per row.
+
+// q of one query row (64 heads x 256 B) into LDS: wave w moves heads 16w ..
+// 16w+15, four rows per instruction, 16-byte chunks XOR-swizzled by the row
+// (slot p holds chunk p ^ (h & 15)) so the operand reads are conflict free.
+__device__ __forceinline__ void issue_q_lds(const uint16_t* qrow, uint16_t* s_q) {
+  const int lane = lane_id(), wv = wave_id(), g = lane >> 4, c = lane & 15;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int r = min(slab * 64 + t * 16 + c, rmax);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) kf[t][s] = ldg8(kb + (size_t)r * 128 + s * 32);
-    }
-  };
-  bf16x8 ka[4][4], kn[4][4];
-  const bool early = spw == 1;
-  if (early && slab0 * 64 < d.Np_cap) load(slab0, d.Np_cap - 1, ka);
-  const uint16_t* qrow = q_idx + (size_t)b * d.L * 64 * 128;
-  bf16x8 qf[4][4];
+  for (int i = 0; i < 4; ++i) {
+    const int h = wv * 16 + 4 * i + g;
+    g2lds16(qrow + h * 128 + ((c ^ (h & 15)) * 8), lds_addr(s_q + (wv * 16 + 4 * i) * 128));
+  }
+}
+__device__ __forceinline__ void read_q_lds(const uint16_t* s_q, bf16x8 (&qf)[4][4]) {
+  const int lane = lane_id(), g = lane >> 4, c = lane & 15;
 #pragma unroll
   for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) qf[ht][s] = ldg8(qrow + (ht * 16 + c) * 128 + s * 32 + g * 8);
+    for (int s = 0; s < 4; ++s) qf[ht][s] = lds8(s_q + (ht * 16 + c) * 128 + (((4 * s + g) ^ c) * 8));
+}
+// this wave's 16 rows of a slab (rows clamped to rmax)
+__device__ __forceinline__ void load_slab_rows(const uint16_t* kb, int slab, int rmax, bf16x8 (&kf)[4]) {
+  const int lane = lane_id(), wv = wave_id(), g = lane >> 4, c = lane & 15;
+  const int r = min(slab * 64 + wv * 16 + c, rmax);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) kf[s] = ldg8(kb + (size_t)r * 128 + s * 32 + g * 8);
+}
+
+// Scores of one slab of sequence b: fine scores of its rows and, on the HiSA
+// path, coarse scores of its blocks (all four waves call it).  MFMA gives
+// D[h][row] = q_h . key_row; the fine score of a row is sum_h relu(D) w_eff.
+// The block mean is linear, so q_h . rep_beta is the mean of D[h][row] over
+// the block's rows: blocks of up to 16 rows are summed inside the wave,
+// larger ones from per-wave partial sums exchanged through s_part[par].
+// Rows past Np are scored but never stored, as are blocks past nb.
+__device__ __forceinline__ void score_slab(const KDims& d, const SeqInfo& si, int b, int slab, int par,
+                                           const bf16x8 (&qf)[4][4], const float (&wl)[4][4], float w_head,
+                                           const bf16x8 (&kf)[4], float* fscore, float* cscore,
+                                           float (*s_part)[4][64]) {
+  const int lane = lane_id(), wv = wave_id(), g = lane >> 4, c = lane & 15;
+  f32x4 acc[4];
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ht][s], kf[s], acc[ht], 0, 0, 0);
+  float v = 0.f;
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v += relu(acc[ht][i]) * wl[ht][i];
+  v = sum_rows(v);
+  const int r = slab * 64 + wv * 16 + c;
+  if (g == 0 && r < si.Np) st_dev(fscore + (size_t)b * d.Np_cap + r, v);
+  if (si.path != PATH_HISA) return;
+  const int bsz = d.index_block;
+  const float inv_b = 1.f / (float)bsz;
+  if (bsz <= 16) {
+    // blocks inside the wave's 16 rows: lanes c of one block share the sum
+    float cv = 0.f;
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cv += relu(sum_span(acc[ht][i], bsz) * inv_b) * wl[ht][i];
+    cv = sum_rows(cv);
+    const int beta = r / bsz;
+    if (g == 0 && (c & (bsz - 1)) == 0 && beta < si.nb) st_dev(cscore + (size_t)b * d.nb_cap + beta, cv);
+    return;
+  }
+  // blocks of 32 or 64 rows: per-head sums over this wave's rows to LDS,
+  // then wave j < 64 / bsz owns block j of the slab
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht) {
+    f32x4 p;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = sum_row16(acc[ht][i]);
+    if (c == 0) *(f32x4*)&s_part[par][wv][ht * 16 + 4 * g] = p;
+  }
+  lds_sync();
+  const int wpb = bsz >> 4;  // waves per block
+  if (wv < 64 / bsz) {
+    float sum = 0.f;
+    for (int u = 0; u < wpb; ++u) sum += s_part[par][wv * wpb + u][lane];
+    const float cv = wave_sum(relu(sum * inv_b) * w_head);
+    const int beta = (slab * 64) / bsz + wv;
+    if (lane == 0 && beta < si.nb) st_dev(cscore + (size_t)b * d.nb_cap + beta, cv);
+  }
+}
+
+// The end of a sequence's run of slabs in a workgroup: once every wave has
+// seen its device-scope score stores acknowledged, the workgroup adds `done`
+// slabs to cnt[b].  Returns (uniformly) whether this workgroup completed the
+// sequence (nslab slabs); it then returns cnt[b] to 0 and owes the
+// sequence's selection.  Every thread of the workgroup calls it.
+__device__ __forceinline__ bool publish_run(int b, int done, int nslab, int* cnt, int* s_flag) {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0
+  asm volatile("" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int prev = __hip_atomic_fetch_add(cnt + b, done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_flag = prev + done == nslab;
+    if (*s_flag) __hip_atomic_store(cnt + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  return *s_flag != 0;
+}
+
+// The selection of a completed sequence (wave 0 of the completing
+// workgroup): every score is at the coherence point, and decode_select_wave
+// reads them with device-scope loads.
+__device__ __forceinline__ void select_completed(const KDims& d, int b, const int* t0, const float* fscore,
+                                                 const float* cscore, int* I, int* top_blk, int* path, int* s_blk,
+                                                 uint32_t* s_hist) {
+  const SeqInfo si = seq_info(d, t0[b]);
+  decode_select_wave(d, si, b, fscore + (size_t)b * d.Np_cap, cscore + (size_t)b * d.nb_cap, I, top_blk, path,
+                     s_blk, s_hist);
+}
+
+// Latency-bound decode scan (few slabs): one workgroup per 64-row slab of one
+// sequence.  The slab's rows are requested before t0 arrives (rows clamped to
+// the buffer rather than to Np) and q comes into LDS in parallel.  With cnt
+// != NULL the selection is fused (publish_run with one slab per workgroup);
+// the first workgroup of a dense or invalid sequence writes its outputs.
+__global__ __launch_bounds__(256) void k_decode_scan_mfma(
+    KDims d, const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ keys,
+    const int* __restrict__ t0, float* fscore, float* cscore, int* cnt, int* I, int* top_blk, int* path) {
+  __shared__ __align__(16) uint16_t s_q[64 * 128];
+  __shared__ __align__(16) float s_part[2][4][64];
+  __shared__ int s_blk[kRowKeep];
+  __shared__ __align__(16) uint32_t s_hist[256];
+  __shared__ int s_flag;
+  const int b = blockIdx.y, slab = blockIdx.x;
+  const int lane = lane_id(), g = lane >> 4;
+  const uint16_t* kb = keys + (size_t)b * d.Np_cap * 128;
+  bf16x8 kf[4];
+  load_slab_rows(kb, slab, d.Np_cap - 1, kf);
+  issue_q_lds(q_idx + (size_t)b * d.L * 64 * 128, s_q);
+  // raw head weights now, scaled after the barrier (no wait on them here)
+  const float* wrow = w + (size_t)b * d.L * 64;
   float wl[4][4];
 #pragma unroll
   for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wl[ht][i] = w[(size_t)b * d.L * 64 + ht * 16 + 4 * g + i] * d.w_scale;
+    for (int i = 0; i < 4; ++i) wl[ht][i] = wrow[ht * 16 + 4 * g + i];
+  float w_head = wrow[lane];  // weight of head `lane` (block owners)
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0: this wave's q rows (and its keys) are in
+  __syncthreads();
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wl[ht][i] *= d.w_scale;
+  w_head *= d.w_scale;
+  bf16x8 qf[4][4];
+  read_q_lds(s_q, qf);
   const SeqInfo si = seq_info(d, t0[b]);
   if (!si.ok || si.path == PATH_DENSE) {
-    if (cnt && blockIdx.x == 0) write_unscored(d, si, b, I, top_blk, path);
+    if (cnt && slab == 0 && wave_id() == 0) write_unscored(d, si, b, I, top_blk, path);
     return;
   }
   const int nslab = (si.Np + 63) / 64;
-  if (slab0 >= nslab) return;
-  if (!early) load(slab0, si.Np - 1, ka);
-  const bool hisa_path = si.path == PATH_HISA;
-  const int bsz = d.index_block;
-  // Scores of one slab (rows past Np are scored but never stored; a block
-  // past nb is never stored either, so their contents do not matter).
-  auto score = [&](int slab, const bf16x8 (&kf)[4][4]) {
-    const int row0 = slab * 64;
-    float bs[4][4];  // running block sums of D over rows, per (head tile, i)
+  if (slab >= nslab) return;  // uniform over the workgroup
+  score_slab(d, si, b, slab, 0, qf, wl, w_head, kf, fscore, cscore, s_part);
+  if (cnt && publish_run(b, 1, nslab, cnt, &s_flag) && wave_id() == 0)
+    select_completed(d, b, t0, fscore, cscore, I, top_blk, path, s_blk, s_hist);
+}
+
+// Bandwidth-bound decode scan (many slabs, ragged batches): a persistent
+// grid over the flattened list of live slabs (every sequence's slabs below
+// its Np, in order).  Each workgroup takes an equal contiguous share, so
+// ragged pooled counts stay balanced and q is reloaded only where the share
+// crosses into the next sequence; the rows of the next two slabs stream in
+// while one is scored.  With cnt != NULL each run of a sequence's slabs is
+// published with one atomic (publish_run), and the workgroup that completes
+// a sequence selects for it.  Workgroup x writes the outputs of the dense or
+// invalid sequences b with b % gridDim.x == x.  B <= kStreamMaxB.
+constexpr int kStreamMaxB = 1024;
+
+__global__ __launch_bounds__(256) void k_decode_scan_stream(
+    KDims d, const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ keys,
+    const int* __restrict__ t0, float* fscore, float* cscore, int* cnt, int* I, int* top_blk, int* path) {
+  __shared__ __align__(16) uint16_t s_q[64 * 128];
+  __shared__ __align__(16) float s_part[2][4][64];
+  __shared__ int s_pre[kStreamMaxB + 1];  // first flattened slab of each sequence
+  __shared__ uint32_t s_wsum[4];
+  __shared__ int s_blk[kRowKeep];
+  __shared__ __align__(16) uint32_t s_hist[256];
+  __shared__ int s_flag;
+  __shared__ int s_done[kStreamMaxB];  // sequences this workgroup completed
+  const int tid = threadIdx.x, lane = lane_id(), wv = wave_id(), g = lane >> 4;
+  // slab counts and their prefix: thread t sums sequences 4t .. 4t+3
+  {
+    int n[4];
+    uint32_t loc = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int bb = 4 * tid + u;
+      n[u] = 0;
+      if (bb < d.B) {
+        const SeqInfo sb = seq_info(d, t0[bb]);
+        if (sb.ok && sb.path != PATH_DENSE) n[u] = (sb.Np + 63) / 64;
+      }
+      loc += (uint32_t)n[u];
+    }
+    uint32_t total;
+    uint32_t run = block_excl_scan<256>(loc, s_wsum, &total);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int bb = 4 * tid + u;
+      if (bb <= d.B) s_pre[bb] = (int)run;
+      run += (uint32_t)n[u];
+    }
+    __syncthreads();
+  }
+  // outputs of the sequences that are not scored
+  if (cnt && wv == 0)
+    for (int bb = blockIdx.x; bb < d.B; bb += gridDim.x) {
+      const SeqInfo sb = seq_info(d, t0[bb]);
+      if (!sb.ok || sb.path == PATH_DENSE) write_unscored(d, sb, bb, I, top_blk, path);
+    }
+  const int total = s_pre[d.B];
+  const int share = (total + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int g_begin = min(total, (int)blockIdx.x * share), g_end = min(total, g_begin + share);
+  if (g_begin >= g_end) return;
+  // sequence holding flattened slab x (x < total), given that it is `from`
+  // or later: the last sequence whose first slab is <= x (empty sequences
+  // share their first slab with the next one, so the last is non-empty)
+  auto seq_of = [&](int x, int from) {
+    if (s_pre[from + 1] > x) return from;
+    int lo = from + 1, hi = d.B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_pre[mid] <= x) lo = mid;
+      else hi = mid - 1;
+    }
+    return lo;
+  };
+  int b = seq_of(g_begin, 0);
+  SeqInfo si = seq_info(d, t0[b]);
+  // rows of flattened slab x (x < total), given that its sequence is `from` or later
+  auto load_flat = [&](int x, int from, bf16x8 (&kf)[4]) {
+    const int bx = seq_of(x, from);
+    const int np_x = bx == b ? si.Np : seq_info(d, t0[bx]).Np;
+    load_slab_rows(keys + (size_t)bx * d.Np_cap * 128, x - s_pre[bx], np_x - 1, kf);
+  };
+  // the next two slabs stream in while one is scored
+  bf16x8 k0[4], k1[4], k2[4];
+  load_flat(g_begin, b, k0);
+  if (g_begin + 1 < g_end) load_flat(g_begin + 1, b, k1);
+  bf16x8 qf[4][4];
+  float wl[4][4], w_head = 0.f;
+  int run_start = g_begin, n_done = 0;
+  auto enter = [&](int bb) {  // q and the head weights of sequence bb
+    __syncthreads();  // every wave is done reading the previous q
+    issue_q_lds(q_idx + (size_t)bb * d.L * 64 * 128, s_q);
+    const float* wrow = w + (size_t)bb * d.L * 64;
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) bs[ht][i] = 0.f;
+      for (int i = 0; i < 4; ++i) wl[ht][i] = wrow[ht * 16 + 4 * g + i];
+    w_head = wrow[lane];
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0 (the slab rows in flight land too)
+    __syncthreads();
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      f32x4 acc[4];
+    for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
-      for (int ht = 0; ht < 4; ++ht) {
-        acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ht][s], kf[t][s], acc[ht], 0, 0, 0);
-      }
-      float v = 0.f;
-#pragma unroll
-      for (int ht = 0; ht < 4; ++ht)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v += fmaxf(acc[ht][i], 0.f) * wl[ht][i];
-      v = sum_rows(v);
-      const int r = row0 + t * 16 + c;
-      if (g == 0 && r < si.Np) st_dev(fscore + (size_t)b * d.Np_cap + r, v);
-      if (!hisa_path) continue;
-      // Block sums: rows of a block are consecutive lanes c (and tiles t).
-#pragma unroll
-      for (int ht = 0; ht < 4; ++ht)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bs[ht][i] += acc[ht][i];
-      const int span = bsz < 16 ? bsz : 16;  // rows of one block inside this tile
-      if (bsz > 16 && ((t + 1) * 16) % bsz != 0) continue;
-#pragma unroll
-      for (int ht = 0; ht < 4; ++ht)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bs[ht][i] = sum_span(bs[ht][i], span);
-      float cv = 0.f;
-      const float inv_b = 1.f / (float)bsz;
-#pragma unroll
-      for (int ht = 0; ht < 4; ++ht)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          cv += fmaxf(bs[ht][i] * inv_b, 0.f) * wl[ht][i];
-          bs[ht][i] = 0.f;
-        }
-      cv = sum_rows(cv);
-      // lane c holds the sum of the block containing its row
-      const int beta = (row0 + t * 16 + c) / bsz;
-      const bool first_lane = bsz >= 16 ? c == 0 : (c % bsz) == 0;
-      if (g == 0 && first_lane && beta < si.nb) st_dev(cscore + (size_t)b * d.nb_cap + beta, cv);
-    }
+      for (int i = 0; i < 4; ++i) wl[ht][i] *= d.w_scale;
+    w_head *= d.w_scale;
+    read_q_lds(s_q, qf);
   };
-  for (int u = 0; u < spw; u += 2) {
-    if (slab0 + u >= nslab) break;
-    if (u + 1 < spw && slab0 + u + 1 < nslab) load(slab0 + u + 1, si.Np - 1, kn);
-    score(slab0 + u, ka);
-    if (u + 1 >= spw || slab0 + u + 1 >= nslab) break;
-    if (u + 2 < spw && slab0 + u + 2 < nslab) load(slab0 + u + 2, si.Np - 1, ka);
-    score(slab0 + u + 1, kn);
+  enter(b);
+  for (int x = g_begin; x < g_end; ++x) {
+    const int slab = x - s_pre[b];
+    if (x + 2 < g_end) load_flat(x + 2, b, k2);
+    const int bn = x + 1 < g_end ? seq_of(x + 1, b) : b;
+    score_slab(d, si, b, slab, x & 1, qf, wl, w_head, k0, fscore, cscore, s_part);
+    const bool seq_ends = x + 1 == g_end || bn != b;
+    if (seq_ends) {
+      const int nslab = s_pre[b + 1] - s_pre[b];
+      if (cnt && publish_run(b, x + 1 - run_start, nslab, cnt, &s_flag)) {
+        if (tid == 0) s_done[n_done] = b;
+        ++n_done;
+      }
+      if (x + 1 < g_end) {
+        b = bn;
+        si = seq_info(d, t0[b]);
+        run_start = x + 1;
+        enter(b);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      k0[s] = k1[s];
+      k1[s] = k2[s];
+    }
   }
-  if (!cnt) return;
-  __shared__ int s_blk[kRowKeep];
-  const int nw = (nslab + spw - 1) / spw;  // waves scoring sequence b
-  // Publish: every score store above is device-scope; wait until all of them
-  // are acknowledged before this wave counts itself.
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0
-  asm volatile("" ::: "memory");
-  int prev = 0;
-  if (lane == 0) prev = __hip_atomic_fetch_add(cnt + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  prev = __builtin_amdgcn_readfirstlane(prev);
-  if (prev != nw - 1) return;
-  // the last wave: every wave's scores are at the coherence point, and the
-  // selection reads them with device-scope loads
-  if (lane == 0) __hip_atomic_store(cnt + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  decode_select_wave(d, si, b, fscore + (size_t)b * d.Np_cap, cscore + (size_t)b * d.nb_cap, I, top_blk, path,
-                     s_blk);
+  // selections of the sequences this workgroup completed (after the scan,
+  // so its registers are free)
+  if (n_done == 0) return;
+  __syncthreads();
+  if (wv == 0)
+    for (int u = 0; u < n_done; ++u)
+      select_completed(d, s_done[u], t0, fscore, cscore, I, top_blk, path, s_blk, s_hist);
 }
 
 // Any shape / dtype: 4 threads per row, VALU dot products.
@@ -530,7 +695,7 @@ __global__ __launch_bounds__(256) void k_coarse_mfma(KDims d, int all_paths, con
     for (int i = lane; i < d.nb_cap; i += 64) out[i] = kNeg;
     return;
   }
-  const int valid = visible(t0[b] + j, d.ratio, si.Np);
+  const int valid = visible(d, t0[b] + j, si.Np);
   const uint16_t* qrow = q_idx + ((size_t)b * d.L + j) * 64 * 128;
   bf16x8 qf[4][4];
 #pragma unroll
@@ -582,7 +747,7 @@ __global__ __launch_bounds__(256) void k_coarse_valu(KDims d, int all_paths, con
   const SeqInfo si = seq_info(d, t0[b]);
   if (!all_paths && si.path != PATH_HISA) return;
   float* out = cscore + ((size_t)b * d.L + j) * d.nb_cap;
-  const int valid = si.ok ? visible(t0[b] + j, d.ratio, si.Np) : 0;
+  const int valid = si.ok ? visible(d, t0[b] + j, si.Np) : 0;
   const T* qrow = q_idx + ((size_t)b * d.L + j) * d.H_i * d.D_i;
   const float* wrow = w + ((size_t)b * d.L + j) * d.H_i;
   for (int beta = threadIdx.x; beta < d.nb_cap; beta += 256) {
@@ -638,7 +803,7 @@ __global__ __launch_bounds__(256) void k_fine_mfma(KDims d, int lds_floats, cons
   extern __shared__ float s_fs[];  // max(nb_cap, C) floats: coarse scores, then fine scores
   __shared__ TopkScoresSmem sm;
   __shared__ int s_blk[kMaxKeep];
-  const int valid = visible(t0[b] + j, d.ratio, si.Np);
+  const int valid = visible(d, t0[b] + j, si.Np);
   const float* cs = cscore + ((size_t)b * d.L + j) * d.nb_cap;
   auto emit_blk = [&](int slot, int i) { s_blk[slot] = i; };
   if (si.nb <= lds_floats) {
@@ -734,7 +899,7 @@ __global__ __launch_bounds__(256) void k_fine_valu(KDims d, const T* __restrict_
   extern __shared__ float s_fs[];
   __shared__ TopkScoresSmem sm;
   __shared__ int s_blk[kMaxKeep];
-  const int valid = visible(t0[b] + j, d.ratio, si.Np);
+  const int valid = visible(d, t0[b] + j, si.Np);
   const float* cs = cscore + ((size_t)b * d.L + j) * d.nb_cap;
   block_topk_scores<256>(si.nb, si.Kb, [&](int i) { return cs[i]; },
                          [&](int slot, int i) { s_blk[slot] = i; }, sm);
@@ -791,6 +956,7 @@ __global__ __launch_bounds__(256) void k_select_rows(KDims d, const uint16_t* __
   __shared__ __align__(16) uint16_t s_ring[kRegion];
   __shared__ float s_sc[4][kRowR * 64];  // per wave: coarse, then fine scores
   __shared__ int s_blk[4][kRowKeep];
+  __shared__ __align__(16) uint32_t s_hist[4][256];  // per wave: top-k histogram
   const int b = blockIdx.y, wv = wave_id(), j_raw = blockIdx.x * 4 + wv;
   const bool live = j_raw < d.L;  // trailing waves of the last workgroup only help with the shared loads
   const int j = live ? j_raw : d.L - 1;
@@ -812,7 +978,7 @@ __global__ __launch_bounds__(256) void k_select_rows(KDims d, const uint16_t* __
     }
   }
   if (!si.ok || si.path != PATH_HISA) return;  // uniform over the workgroup (one sequence)
-  const int valid = visible(t0[b] + j, d.ratio, si.Np);
+  const int valid = visible(d, t0[b] + j, si.Np);
   float* sc = s_sc[wv];
 
   // q as the A operand (MFMA step s: dims 32s + 8g .. +7), per-head weights
@@ -894,7 +1060,7 @@ __global__ __launch_bounds__(256) void k_select_rows(KDims d, const uint16_t* __
     key[r] = (r < nrc && i < nb) ? score_key(sc[i]) : 0u;
   }
   int* blk = s_blk[wv];
-  wave_emit_topk(key, nrc, si.Kb, [&](int slot, int r) { blk[slot] = 64 * r + lane; });
+  wave_emit_topk(key, nrc, si.Kb, s_hist[wv], [&](int slot, int r) { blk[slot] = 64 * r + lane; });
   if (blkrow && live)
     for (int i = lane; i < si.Kb; i += 64) blkrow[i] = blk[i];
 
@@ -945,7 +1111,7 @@ __global__ __launch_bounds__(256) void k_select_rows(KDims d, const uint16_t* __
     const int i = 64 * r + lane;
     key[r] = (r < nrf && i < C) ? score_key(sc[i]) : 0u;
   }
-  wave_emit_topk(key, nrf, si.k, [&](int slot, int r) { Irow[slot] = cand(64 * r + lane); });
+  wave_emit_topk(key, nrf, si.k, s_hist[wv], [&](int slot, int r) { Irow[slot] = cand(64 * r + lane); });
 }
 
 // ------------------------------------------------------------------ flat scan
@@ -970,7 +1136,7 @@ __global__ __launch_bounds__(256) void k_flat_scores_mfma(KDims d, int kc, const
   const int j0 = blockIdx.y * 8;
   const int lane = lane_id(), wv = wave_id(), g = lane >> 4, c = lane & 15, tid = threadIdx.x;
   const int jlast = min(d.L - 1, j0 + 7);
-  const int Vmax = visible(t0[b] + jlast, d.ratio, si.Np);
+  const int Vmax = visible(d, t0[b] + jlast, si.Np);
   int jr[2], Vr[2];
   bool live[2];
   bf16x8 qf[2][4][4];
@@ -980,7 +1146,7 @@ __global__ __launch_bounds__(256) void k_flat_scores_mfma(KDims d, int kc, const
     jr[rr] = j0 + wv * 2 + rr;
     live[rr] = jr[rr] < d.L;
     const int jj = live[rr] ? jr[rr] : 0;
-    Vr[rr] = live[rr] ? visible(t0[b] + jj, d.ratio, si.Np) : 0;
+    Vr[rr] = live[rr] ? visible(d, t0[b] + jj, si.Np) : 0;
     const uint16_t* qrow = q_idx + ((size_t)b * d.L + jj) * 64 * 128;
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) {
@@ -1047,7 +1213,7 @@ __global__ __launch_bounds__(256) void k_flat_scores_valu(KDims d, const T* __re
   if (!flat_active(d, si)) return;
   const int p = blockIdx.x * 256 + threadIdx.x;
   if (p >= si.Np) return;
-  const int valid = visible(t0[b] + j, d.ratio, si.Np);
+  const int valid = visible(d, t0[b] + j, si.Np);
   float v = kNeg;
   if (p < valid) {
     const T* qrow = q_idx + ((size_t)b * d.L + j) * d.H_i * d.D_i;
@@ -1119,14 +1285,17 @@ hipError_t launch_decode_scan(const KDims& d, bool bf16, const void* q_idx, cons
                               int* path, hipStream_t st) {
   const dim3 grid(cdiv(d.Np_cap, 64), d.B);
   if (idx_mfma_ok(d, bf16)) {
-    // several slabs per wave once there are enough to fill the chip
     const long long slabs = (long long)cdiv(d.Np_cap, 64) * d.B;
-    const int spw = slabs >= 8192 ? 4 : slabs >= 4096 ? 2 : 1;
-    hipLaunchKernelGGL(k_decode_scan_mfma, dim3(cdiv(d.Np_cap, 64 * spw), d.B), dim3(64), 0, st, d, spw,
-                       (const uint16_t*)q_idx, w, (const uint16_t*)keys, t0, fscore, cscore, cnt, I, top_blk,
-                       path);
-  }
-  else if (bf16)
+    if (slabs <= 1024 || d.B > kStreamMaxB) {
+      // latency-bound: one workgroup per slab, rows requested before t0 is known
+      hipLaunchKernelGGL(k_decode_scan_mfma, grid, dim3(256), 0, st, d, (const uint16_t*)q_idx, w,
+                         (const uint16_t*)keys, t0, fscore, cscore, cnt, I, top_blk, path);
+    } else {
+      // bandwidth-bound: two resident workgroups per CU share the live slabs
+      hipLaunchKernelGGL(k_decode_scan_stream, dim3(512), dim3(256), 0, st, d, (const uint16_t*)q_idx, w,
+                         (const uint16_t*)keys, t0, fscore, cscore, cnt, I, top_blk, path);
+    }
+  }  else if (bf16)
     hipLaunchKernelGGL(k_decode_scan_valu<uint16_t>, grid, dim3(256), 0, st, d, (const uint16_t*)q_idx, w,
                        (const uint16_t*)keys, t0, fscore, cscore);
   else

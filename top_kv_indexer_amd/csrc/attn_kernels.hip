@@ -73,10 +73,9 @@ __device__ __forceinline__ bf16x8 pack8(const float (&p)[8]) {
 // 16-byte chunks XOR-swizzled by the row (slot position p holds chunk
 // p ^ sw(row)), so the K reads (16 rows x one chunk) and the transposing V
 // reads (8 rows x two chunks per half-wave) hit distinct banks.  Row
-// bookkeeping is resolved once per chunk of up to 1024 rows: the fetching
-// wave keeps the element offsets in registers (entry RPW*t + r of a wave
-// lives in lane (RPW*t + r) % 64, register (RPW*t + r) / 64), and a 32-bit
-// liveness mask per tile sits in LDS.
+// bookkeeping is resolved once per chunk of up to 1024 rows into LDS: a
+// 32-bit row code per entry (pooled row, or local row) and a 32-bit liveness
+// mask per tile; wave w fetches rows RPW*w .. RPW*w + RPW-1 of each tile.
 template <int DK, int DV, int NHG>
 __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, const uint16_t* __restrict__ q,
                                                          const uint16_t* __restrict__ local_kv,
@@ -102,7 +101,7 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
   constexpr int KW = 8;                 // K fragments in flight
   constexpr int OP = DV + 8;            // pitch of the staged output rows (elements)
   static_assert(HW * OP <= NBUF * kTile * KPD && HW <= 2 * kTile, "staging fits the ring");
-  static_assert(NTILE * RPW == 64 * IPT, "a wave's row offsets of one chunk fill whole registers");
+  static_assert(RPW % 4 == 0 && CH % NT == 0, "row codes are read four at a time; a chunk splits over threads");
   static_assert(HW == 8 * NW, "each wave owns the softmax of 8 heads");
   static_assert(DV % 16 == 0 && DK >= 512 && DK <= 1024 && DK % 32 == 0, "shape");
   __shared__ __align__(16) uint16_t kv[NBUF][kTile * KPD];
@@ -111,6 +110,7 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
   __shared__ __align__(16) float s_alpha[HW];
   __shared__ float s_ml[2][HW];
   __shared__ uint32_t s_tmask[NTILE];
+  __shared__ __align__(16) int s_code[CH];  // row code of each entry of the current chunk
 
   const int split = blockIdx.x;
   // consecutive query rows go to the same XCD (workgroups are dealt to the 8
@@ -121,6 +121,7 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
   }(blockIdx.y, d.B * d.L);
   const int b = row / d.L, j = row % d.L;
   const int tid = threadIdx.x, lane = lane_id(), wv = wave_id(), g = lane >> 4, c = lane & 15;
+  const int wvs = __builtin_amdgcn_readfirstlane(wv);  // the wave index, known to be uniform
   const int hg = wv >> 1, dh = wv & 1;
   const int hbase = blockIdx.z * HW;
   auto sw = [](int r) { return ((r & 7) << 1) | ((r >> 3) & 1); };
@@ -132,35 +133,29 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
   const int begin = min(n_geo, split * per), end = min(n_geo, begin + per);
   const int* Irow = I + (size_t)row * d.kI;
   auto ident_row = [&](int u) { return tid + u * NT; };
-  auto fetch_row = [&](int u) {  // entry 64u + lane = RPW*t + r -> tile t, wave-row r
-    const int e = 64 * u + lane;
-    return (e / RPW) * kTile + wv + NW * (e % RPW);
-  };
-  int id_a[IPT], id_f[IPT];
+  int id_a[IPT];
 #pragma unroll
   for (int u = 0; u < IPT; ++u) {
-    const int ea = begin + ident_row(u), ef = begin + fetch_row(u);
+    const int ea = begin + ident_row(u);
     id_a[u] = (ea < end && ea < d.kI) ? Irow[ea] : -1;
-    id_f[u] = (ef < end && ef < d.kI) ? Irow[ef] : -1;
   }
   const int T0 = t0[b];
   const RowPlan rp = row_plan(d, T0, j);
   // a row every sequence with a live row may read (dead rows point at it)
-  const long long dummy = rp.n_loc > 0 ? ~(((long long)b * d.Wl_cap + (rp.s_lo - rp.ls)) * DK)
-                                       : (long long)b * d.Np_cap * DK;
+  const int dummy = rp.n_loc > 0 ? -1 - (rp.s_lo - rp.ls) : 0;
   const bool any_row = rp.n_loc > 0 || rp.V > 0;
-  // liveness and element offset (>= 0 into pooled_kv, ~offset into local_kv)
-  // of list entry e (given its pooled id when e < kI)
-  auto resolve = [&](int e, int id, long long& off) -> bool {
-    off = dummy;
+  // liveness and row code of list entry e (given its pooled id when e < kI):
+  // code >= 0 is pooled row `code`, code < 0 local row -1 - code
+  auto resolve = [&](int e, int id, int& code) -> bool {
+    code = dummy;
     if (e >= end) return false;
     if (e < d.kI) {
       if (id < 0 || id >= rp.V) return false;
-      off = ((long long)b * d.Np_cap + id) * DK;
+      code = id;
       return true;
     }
     if (e - d.kI >= rp.n_loc) return false;
-    off = ~(((long long)b * d.Wl_cap + (rp.s_lo - rp.ls + e - d.kI)) * DK);
+    code = -1 - (rp.s_lo - rp.ls + e - d.kI);
     return true;
   };
 
@@ -226,39 +221,37 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
   for (int cb = any_row ? begin : end; cb < end; cb += CH) {
     const int ce = min(end, cb + CH);
     const int ntile = (ce - cb + kTile - 1) / kTile;
-    long long offs[IPT];
-#pragma unroll
-    for (int u = 0; u < IPT; ++u) {
-      const int ef = cb + fetch_row(u);
-      const int id = cb == begin ? id_f[u] : (ef < end && ef < d.kI ? Irow[ef] : -1);
-      resolve(ef, id, offs[u]);
-    }
-    __syncthreads();  // the previous chunk is done with every slot and mask
+    __syncthreads();  // the previous chunk is done with every slot, code and mask
 #pragma unroll
     for (int u = 0; u < IPT; ++u) {
       const int ea = cb + ident_row(u);
       const int id = cb == begin ? id_a[u] : (ea < end && ea < d.kI ? Irow[ea] : -1);
-      long long unused;
-      const uint64_t live = __ballot(resolve(ea, id, unused));
+      int code;
+      const uint64_t live = __ballot(resolve(ea, id, code));
+      s_code[ident_row(u)] = code;
       if (lane == 0) {
         const int t = (wv * 64 + u * NT) / kTile;
         s_tmask[t] = (uint32_t)live;
         s_tmask[t + 1] = (uint32_t)(live >> 32);
       }
     }
+    __syncthreads();  // every row code of the chunk is in
+    // Tile t, wave w: tile rows RPW*w .. RPW*w + RPW-1.  Their codes come
+    // from LDS in one broadcast read per four rows and the addresses are
+    // formed in vector registers; the LDS destination is scalar, so no
+    // value crosses from the vector to the scalar unit.
+    const uint16_t* pooled_b = pooled_kv + (size_t)b * d.Np_cap * DK;
+    const uint16_t* local_b = local_kv + (size_t)b * d.Wl_cap * DK;
     auto load_tile = [&](int t, uint16_t* kvdst) {
+      int4 code4[RPW / 4];
+#pragma unroll
+      for (int q4 = 0; q4 < RPW / 4; ++q4) code4[q4] = *(const int4*)&s_code[t * kTile + RPW * wvs + 4 * q4];
 #pragma unroll
       for (int r = 0; r < RPW; ++r) {
-        const int e = RPW * t + r;  // wave entry
-        const int reg = e >> 6, src_lane = e & 63;
-        long long o = offs[0];
-#pragma unroll
-        for (int u = 1; u < IPT; ++u) o = reg == u ? offs[u] : o;
-        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)o, src_lane);
-        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(o >> 32), src_lane);
-        const long long off = (long long)(((uint64_t)hi << 32) | lo);
-        const int trow = wv + NW * r;
-        const uint16_t* src = off >= 0 ? pooled_kv + off : local_kv + ~off;
+        const int4 c4 = code4[r >> 2];
+        const int cd = (r & 3) == 0 ? c4.x : (r & 3) == 1 ? c4.y : (r & 3) == 2 ? c4.z : c4.w;
+        const uint16_t* src = cd >= 0 ? pooled_b + (size_t)cd * DK : local_b + (size_t)(-1 - cd) * DK;
+        const int trow = RPW * wvs + r;
         const uint32_t dst = lds_addr(kvdst + trow * KPD);
         g2lds16(src + (lane ^ sw(trow)) * 8, dst);
         if (DK > 512 && lane < DK / 8 - 64) g2lds16(src + 512 + lane * 8, dst + 1024);
@@ -336,7 +329,10 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
         uint2 pk;
         pk.x = pack_bf16x2(p[0], p[1]);
         pk.y = pack_bf16x2(p[2], p[3]);
-        *(uint2*)&s_p[hs * PSP + (rq & 3) * 8 + (rq >> 2) * 4] = pk;
+        // 16-byte chunk j of head row h sits at chunk j ^ ((h >> 2) & 3), so
+        // the operand reads below (rows c, c+4, c+8, c+12 at once) and these
+        // writes are bank-conflict free
+        *(uint2*)&s_p[hs * PSP + (((rq & 3) ^ ((hs >> 2) & 3)) * 8) + (rq >> 2) * 4] = pk;
         if (rq == 0) s_alpha[hs] = alpha;
       }
       lds_sync();
@@ -350,7 +346,7 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
       }
       bf16x8 pb[NHG];
 #pragma unroll
-      for (int ht = 0; ht < NHG; ++ht) pb[ht] = *(const bf16x8*)&s_p[(ht * 16 + c) * PSP + g * 8];
+      for (int ht = 0; ht < NHG; ++ht) pb[ht] = *(const bf16x8*)&s_p[(ht * 16 + c) * PSP + ((g ^ ((c >> 2) & 3)) * 8)];
       i16x4 va[NDT][2];
 #pragma unroll
       for (int n = 0; n < NDT; ++n) {

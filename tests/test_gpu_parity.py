@@ -169,6 +169,37 @@ def test_flat_dsa(hisa, w):
     say(f"  max-abs {check_attention(w, x, I, out, sample=3):.3g}")
 
 
+def test_flat_topk_long_rows_masked_and_ties(hisa):
+    # Rows longer than 8192 keys take the register-resident top-k.  Sequence
+    # 0 (t0 = 100, ratio 1, 700 pooled rows) sees only 101 + j keys on row j,
+    # fewer than k = 512 on rows j < 411, which are completed with the
+    # lowest-index masked ids; sequence 1 has 2500 copies of one key row, so
+    # thousands of exactly equal scores straddle the k-th score on many rows
+    # and the lowest ids must win.  (Tiny attention shapes: unused here.)
+    w = synth.DSA_DECODE.with_(name="dsa_long_rows_edges", B=2, L=600, t0=[100, 6000], Np_cap=9000, topk=512,
+                               H=4, Dk=64, Dv=64)
+    x, g = inputs(w, 31)
+    x = dict(x)
+    keys = x["keys"].copy()
+    keys[1, 3000:5500] = keys[1, 3000]
+    x["keys"] = keys
+    gk = torch.from_numpy(keys).to("cuda").to(torch.bfloat16).contiguous()
+    say("[run] flat top-k on long rows with masked fill and heavy ties")
+    I = hisa.flat_topk_select(g["q_idx"], g["w"], gk, g["t0"], ratio=1, topk=w.topk)
+    torch.cuda.synchronize()
+    d = dataclasses.replace(odims(w, x), index_block=0)
+    In = parity.to_np(I)
+    rows = rows_of(w, 14) + [(0, 0), (0, 200), (0, 410), (0, 411), (0, 599)]
+    for b, j in rows:
+        q, ww, kb, t0 = x["q_idx"][b, j], x["w"][b, j], x["keys"][b], int(x["t0"][b])
+        Io, _, _ = oracle.select_row(d, q, ww, kb, t0, j)
+        V = t0 + j + 1
+        if b == 0 and V < w.topk:  # every visible id, then the lowest masked ids
+            np.testing.assert_array_equal(In[b, j], np.arange(w.topk))
+        parity.compare_sets(In[b, j], Io, lambda ids: oracle.scores_of(d, q, ww, kb, t0, j, ids), what=f"({b},{j})")
+        assert (np.diff(In[b, j][In[b, j] >= 0]) > 0).all()
+
+
 def test_block_scores(hisa):
     for w in (synth.FLASH_DECODE, synth.TINY_DECODE, synth.PREFILL.with_(L=96)):
         seed = 77

@@ -328,7 +328,16 @@ int flat_topk_select(const hisa_dims* d, const void* q_idx, const float* w, cons
   hipStream_t st = (hipStream_t)stream;
   k.force_path = hisa::PATH_FLAT;
   float* scores = at<float>(ws, l.scores);
-  hipError_t e = timed("flat_scores", st, [&] { return hisa::launch_flat_scores(k, bf, q_idx, w, keys, t0, scores, st); });
+  hipError_t e;
+  if (d->L == 1 && hisa::idx_mfma_ok(k, bf)) {
+    // one query row per sequence: the decode key scan scores every row (its
+    // per-sequence score rows are the (B, 1, Np_cap) layout of `scores`)
+    e = timed("flat_scores", st, [&] {
+      return hisa::launch_decode_scan(k, bf, q_idx, w, keys, t0, scores, nullptr, nullptr, nullptr, nullptr, nullptr, st);
+    });
+  } else {
+    e = timed("flat_scores", st, [&] { return hisa::launch_flat_scores(k, bf, q_idx, w, keys, t0, scores, st); });
+  }
   if (e != hipSuccess) return launch_fail(e, "flat scores");
   e = timed("topk_rows", st, [&] { return hisa::launch_topk_rows(k, scores, t0, I_out, nullptr, st); });
   if (e != hipSuccess) return launch_fail(e, "flat top-k");

@@ -1264,6 +1264,236 @@ __global__ __launch_bounds__(kTopkRowsThreads) void k_topk_rows(KDims d, int lds
   }
 }
 
+// Flat top-k of one query row held in registers: 1024 threads x 32 scores
+// (n <= 32768).  Element r of lane l in wave w is index 2048w + 64r + l, so a
+// wave covers a contiguous index range.  The k-th element in (score desc,
+// index asc) order, (kthr, ithr), is found as follows: if fewer than k scores
+// are real, every real score and the lowest-index masked ones are taken;
+// otherwise the real scores are counted into 2048 linear bins over [min, max]
+// (narrowed to the k-th score's bin while that bin holds more than 1024
+// entries), and the few entries of the k-th score's bin are ranked exactly.
+// Selected: key > kthr, or key == kthr and index <= ithr; emitted in index
+// order (ties at the threshold keep the lowest indices).
+constexpr int kTkNT = 1024, kTkR = 32, kTkBins = 2048, kTkCand = 1024;
+
+struct TopkRegSmem {
+  uint32_t hist[kTkBins];
+  float cand_s[kTkCand];
+  int cand_i[kTkCand];
+  int wcnt[2][16];
+  float red[3][16];
+  int info[8];
+};
+
+// index of the r-th (1-based) element, in index order, with pred true;
+// every thread of the block calls it and gets the answer
+template <class PredF>
+__device__ __forceinline__ int block_rth_index(int r, PredF pred, TopkRegSmem& sm) {
+  const int lane = lane_id(), wv = wave_id();
+  int cnt = 0;
+#pragma unroll
+  for (int q = 0; q < kTkR; ++q) cnt += (int)__popcll(__ballot(pred(q)));
+  if (lane == 0) sm.wcnt[0][wv] = cnt;
+  __syncthreads();
+  int before = 0;
+  for (int u = 0; u < wv; ++u) before += sm.wcnt[0][u];
+  if (before < r && before + cnt >= r) {  // this wave holds it
+    int need = r - before;
+#pragma unroll
+    for (int q = 0; q < kTkR; ++q) {
+      const uint64_t mq = __ballot(pred(q));
+      const int c = (int)__popcll(mq);
+      if (need > 0 && need <= c) {
+        // the need-th set bit of mq
+        uint64_t x = mq;
+        for (int s = 1; s < need; ++s) x &= x - 1;
+        if (lane == 0) sm.info[6] = 2048 * wv + 64 * q + __builtin_ctzll(x);
+      }
+      need -= c;
+    }
+  }
+  __syncthreads();
+  const int res = sm.info[6];
+  __syncthreads();
+  return res;
+}
+
+__global__ __launch_bounds__(kTkNT) void k_topk_rows_reg(KDims d, const float* __restrict__ scores,
+                                                         const int* __restrict__ t0, int* __restrict__ I,
+                                                         int* __restrict__ path) {
+  __shared__ TopkRegSmem sm;
+  const int b = blockIdx.y, j = blockIdx.x;
+  const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
+  const SeqInfo si = seq_info(d, t0[b]);
+  int* Irow = I + ((size_t)b * d.L + j) * d.topk;
+  const bool act = flat_active(d, si);
+  if (d.force_path == PATH_FLAT) {
+    const int first_pad = act ? si.k : 0;
+    for (int i = tid; i < d.topk; i += kTkNT)
+      if (i >= first_pad) Irow[i] = -1;
+    if (path && j == 0 && tid == 0) path[b] = si.ok ? PATH_FLAT : PATH_INVALID;
+  } else if (act) {
+    for (int i = tid; i < d.topk; i += kTkNT)
+      if (i >= si.k) Irow[i] = -1;
+  }
+  if (!act) return;
+  const int n = si.Np, k = si.k;
+  const float* srow = scores + ((size_t)b * d.L + j) * d.Np_cap;
+  auto idx_of = [&](int q) { return 2048 * wv + 64 * q + lane; };
+  // absent entries (index >= n) take -inf: below every real or masked score
+  const float* pw = srow + 2048 * wv + lane;
+  const int nw = n - 2048 * wv - lane;  // element q is present iff 64q < nw
+  float v[kTkR];
+#pragma unroll
+  for (int q = 0; q < kTkR; ++q) v[q] = 64 * q < nw ? pw[64 * q] : -INFINITY;
+  // 1. range of the real scores, count of masked ones
+  float lo = INFINITY, hi = -INFINITY;
+  int nmask = 0;
+#pragma unroll
+  for (int q = 0; q < kTkR; ++q) {
+    const float x = v[q];
+    const bool real = x > -1e29f;
+    nmask += (!real && x != -INFINITY) ? 1 : 0;
+    lo = real ? fminf(lo, x) : lo;
+    hi = real ? fmaxf(hi, x) : hi;
+  }
+  lo = wave_min(lo);
+  hi = wave_max(hi);
+  nmask = wave_sum_i(nmask);
+  if (lane == 0) {
+    sm.red[0][wv] = lo;
+    sm.red[1][wv] = hi;
+    sm.red[2][wv] = (float)nmask;
+  }
+  for (int i = tid; i < kTkBins; i += kTkNT) sm.hist[i] = 0;
+  __syncthreads();
+  lo = INFINITY;
+  hi = -INFINITY;
+  nmask = 0;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    lo = fminf(lo, sm.red[0][u]);
+    hi = fmaxf(hi, sm.red[1][u]);
+    nmask += (int)sm.red[2][u];
+  }
+  const int nreal = n - nmask;
+  uint32_t kthr;
+  int ithr;
+  if (nreal < k) {
+    // every real score, then the lowest-index masked entries
+    kthr = score_key(kNeg);
+    ithr = block_rth_index(k - nreal, [&](int q) { return v[q] <= -1e29f && v[q] != -INFINITY; }, sm);
+  } else {
+    // 2. bins over [blo, bhi]; narrow to the k-th score's bin while it is crowded
+    float blo = lo, bhi = hi;
+    int need = k;  // entries still to take inside [blo, bhi]
+    bool done = false;
+    kthr = 0;
+    ithr = 0;
+    for (int round = 0; round < 4 && !done; ++round) {
+      if (!(bhi > blo)) {
+        // every remaining score equals blo: ties, lowest indices first
+        kthr = score_key(blo);
+        const float tv = blo;
+        ithr = block_rth_index(need, [&](int q) { return v[q] == tv; }, sm);
+        done = true;
+        break;
+      }
+      const float scale = (float)kTkBins / (bhi - blo) * 0.999999f;
+      auto bin_of = [&](float x) {
+        return (x < blo || x > bhi) ? -1 : min(kTkBins - 1, (int)((x - blo) * scale));
+      };
+      if (round > 0) {
+        for (int i = tid; i < kTkBins; i += kTkNT) sm.hist[i] = 0;
+        __syncthreads();
+      }
+#pragma unroll
+      for (int q = 0; q < kTkR; ++q) {
+        const int bn = bin_of(v[q]);
+        if (bn >= 0) atomicAdd(&sm.hist[bn], 1u);
+      }
+      __syncthreads();
+      // bin holding the need-th score from the top: thread t owns bins 2047-2t, 2046-2t
+      const uint32_t h0 = sm.hist[kTkBins - 1 - 2 * tid], h1 = sm.hist[kTkBins - 2 - 2 * tid];
+      uint32_t tot;
+      const uint32_t above = block_excl_scan<kTkNT>(h0 + h1, (uint32_t*)sm.wcnt[1], &tot);
+      if (tid == 0) sm.info[3] = 0;
+      if (above < (uint32_t)need && above + h0 + h1 >= (uint32_t)need) {
+        const bool first = above + h0 >= (uint32_t)need;
+        sm.info[0] = first ? kTkBins - 1 - 2 * tid : kTkBins - 2 - 2 * tid;
+        sm.info[1] = (int)(first ? above : above + h0);
+        sm.info[2] = (int)(first ? h0 : h1);
+      }
+      __syncthreads();
+      const int T = sm.info[0], mcnt = sm.info[2];
+      need -= sm.info[1];
+      if (mcnt > kTkCand) {
+        // crowded bin: its range becomes the next round's
+        const float nlo = blo + (float)T / scale, nhi = blo + (float)(T + 1) / scale;
+        // scores exactly at the float bin edges stay inside by the clamp of bin_of
+        blo = fmaxf(blo, nlo);
+        bhi = fminf(bhi, nhi);
+        __syncthreads();
+        continue;
+      }
+      // 3. gather bin T's entries and rank them (score desc, index asc)
+#pragma unroll
+      for (int q = 0; q < kTkR; ++q)
+        if (bin_of(v[q]) == T) {
+          const int slot = atomicAdd(&sm.info[3], 1);
+          sm.cand_s[slot] = v[q];
+          sm.cand_i[slot] = idx_of(q);
+        }
+      __syncthreads();
+      for (int t = tid; t < mcnt; t += kTkNT) {
+        const uint32_t kt = score_key(sm.cand_s[t]);
+        const int it = sm.cand_i[t];
+        int rank = 0;
+        for (int u = 0; u < mcnt; ++u) {
+          const uint32_t ku = score_key(sm.cand_s[u]);
+          rank += (ku > kt) || (ku == kt && sm.cand_i[u] < it);
+        }
+        if (rank == need - 1) {
+          sm.info[4] = (int)kt;
+          sm.info[5] = it;
+        }
+      }
+      __syncthreads();
+      kthr = (uint32_t)sm.info[4];
+      ithr = sm.info[5];
+      done = true;
+    }
+    if (!done) {
+      // still crowded after four narrowings: the k-th score is the largest
+      // value whose count from the top reaches `need`; take its ties by index
+      // (exact: the crowded bin's scores are then a handful of equal values)
+      kthr = score_key(blo);
+      const float tv = blo;
+      ithr = block_rth_index(need, [&](int q) { return v[q] == tv; }, sm);
+    }
+  }
+  // 4. emission in index order
+  auto selected = [&](int q) {
+    const uint32_t kv = score_key(v[q]);
+    return v[q] != -INFINITY && (kv > kthr || (kv == kthr && idx_of(q) <= ithr));
+  };
+  int cnt = 0;
+#pragma unroll
+  for (int q = 0; q < kTkR; ++q) cnt += (int)__popcll(__ballot(selected(q)));
+  __syncthreads();
+  if (lane == 0) sm.wcnt[0][wv] = cnt;
+  __syncthreads();
+  int base = 0;
+  for (int u = 0; u < wv; ++u) base += sm.wcnt[0][u];
+#pragma unroll
+  for (int q = 0; q < kTkR; ++q) {
+    const bool sel = selected(q);
+    const uint64_t mq = __ballot(sel);
+    if (sel) Irow[base + lanes_below(mq)] = idx_of(q);
+    base += (int)__popcll(mq);
+  }
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ launchers
@@ -1389,6 +1619,11 @@ hipError_t launch_flat_scores(const KDims& d, bool bf16, const void* q_idx, cons
 }
 
 hipError_t launch_topk_rows(const KDims& d, const float* scores, const int* t0, int* I, int* path, hipStream_t st) {
+  if (d.Np_cap > 8192 && d.Np_cap <= kTkNT * kTkR) {
+    // long rows: scores held in registers of a 1024-thread workgroup
+    hipLaunchKernelGGL(k_topk_rows_reg, dim3(d.L, d.B), dim3(kTkNT), 0, st, d, scores, t0, I, path);
+    return hipGetLastError();
+  }
   constexpr int kLdsCap = 32768;  // 128 KiB of keys
   const int cap = d.Np_cap <= kLdsCap ? d.Np_cap : 0;
   const size_t lds = (size_t)cap * sizeof(float);

@@ -932,28 +932,24 @@ __global__ __launch_bounds__(256) void k_fine_valu(KDims d, const T* __restrict_
 // indexer heads of dim 128, nb <= 1024 blocks, C = Kb*b <= 1024 candidates):
 // coarse block scores on MFMA (rep as three bf16 parts), coarse top-Kb,
 // fine scores of the C candidates on MFMA, fine top-k.  A workgroup holds
-// four query rows of one sequence; MFMA operands stream through LDS
-// (global->LDS loads two tiles ahead): the rep tiles once for all four
-// waves, the candidate keys per wave.  Both top-k steps run inside the wave
-// on register-resident keys (element r of lane l has order index 64r + l,
-// which is ascending in block id / pooled row): a bitwise search finds the
-// k-th largest key, and ballots emit the winners in ascending id order, ties
-// at the threshold going to the lowest ids.
+// four query rows of one sequence; the rep tiles stream through LDS once for
+// all four waves (global->LDS loads two tiles ahead), each wave's candidate
+// keys come straight into registers three tiles ahead.  Both top-k steps run
+// inside the wave on register-resident keys (element r of lane l has order
+// index 64r + l, which is ascending in block id / pooled row): a radix
+// select finds the k-th largest key, and ballots emit the winners in
+// ascending id order, ties at the threshold going to the lowest ids.
 __global__ __launch_bounds__(256) void k_select_rows(KDims d, const uint16_t* __restrict__ q_idx,
                                                      const float* __restrict__ w, const uint16_t* __restrict__ keys,
                                                      const uint16_t* __restrict__ rep3, const int* __restrict__ t0,
                                                      int* __restrict__ I, int* __restrict__ top_blk,
                                                      int* __restrict__ path) {
-  // One LDS region serves the coarse stage (a ring of three 16-block tiles of
-  // rep, three bf16 parts each, shared by the four waves) and then the fine
-  // stage (a private ring of three 16-candidate key tiles per wave).  Rows
-  // are 256 bytes with their 16-byte chunks XOR-swizzled by the row (slot
-  // position p holds chunk p ^ row), so a 16-row MFMA operand read is
-  // bank-conflict free.
+  // The coarse stage streams a ring of three 16-block tiles of rep (three
+  // bf16 parts each, shared by the four waves) through LDS.  Rows are 256
+  // bytes with their 16-byte chunks XOR-swizzled by the row (slot position p
+  // holds chunk p ^ row), so a 16-row MFMA operand read is bank-conflict free.
   constexpr int kRepTile = 3 * 16 * 128;  // elements
-  constexpr int kKeyTile = 16 * 128;
-  constexpr int kRegion = 3 * kRepTile > 12 * kKeyTile ? 3 * kRepTile : 12 * kKeyTile;
-  __shared__ __align__(16) uint16_t s_ring[kRegion];
+  __shared__ __align__(16) uint16_t s_ring[3 * kRepTile];
   __shared__ float s_sc[4][kRowR * 64];  // per wave: coarse, then fine scores
   __shared__ int s_blk[4][kRowKeep];
   __shared__ __align__(16) uint32_t s_hist[4][256];  // per wave: top-k histogram
@@ -1071,39 +1067,69 @@ __global__ __launch_bounds__(256) void k_select_rows(KDims d, const uint16_t* __
     cc = min(cc, C - 1);
     return (blk[cc >> lbsz] << lbsz) + (cc & (bsz - 1));
   };
-  uint16_t* ring = s_ring + wv * 3 * kKeyTile;
-  const uint16_t* kb = keys + (size_t)b * d.Np_cap * 128;
-  // tile t: four loads of four candidate rows each (lane l: row 4i + l/16, chunk l%16)
-  auto load_keys = [&](int t) {
-    uint16_t* slot = ring + (t % 3) * kKeyTile;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 4 * i + (lane >> 4);
-      const uint16_t* src = kb + (size_t)cand(t * 16 + r) * 128 + (((lane & 15) ^ r) * 8);
-      g2lds16(src, lds_addr(slot + 4 * i * 128));
-    }
+  // B operand of candidate tile t straight from memory into registers: lane
+  // (g, c) takes row cand(16t + c), dims 32s + 8g .. +7 (the k order of q),
+  // and keeps the row id for the causal mask.  Four register sets keep three
+  // tiles of loads in flight; past the end the last candidate is re-read, so
+  // every step issues the same loads.  The MFMAs of tile t go out before the
+  // epilogue (relu, head weights, head sum) of tile t-1, so the matrix and
+  // vector units overlap within the wave.
+  const uint16_t* kb = keys + (size_t)b * d.Np_cap * 128 + g * 8;
+  struct Tile {
+    bf16x8 k[4];
+    int pos;
   };
-  load_keys(0);
-  if (ntf > 1) load_keys(1);
-  for (int t = 0; t < ntf; ++t) {
-    wait_vm(t + 1 < ntf, 4);
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's reads of the slot reloaded below are done
-    if (t + 2 < ntf) load_keys(t + 2);
-    const uint16_t* slot = ring + (t % 3) * kKeyTile;
-    bf16x8 kf[4];
+  auto fetch = [&](int t, Tile& tl) {
+    tl.pos = cand(t * 16 + c);
+    const uint16_t* kp = kb + (size_t)tl.pos * 128;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) kf[s] = frag(slot, s);
-    f32x4 acc[4];
+    for (int s = 0; s < 4; ++s) tl.k[s] = ldg8(kp + s * 32);
+  };
+  auto mma = [&](const Tile& tl, f32x4 (&acc)[4]) {
 #pragma unroll
-    for (int ht = 0; ht < 4; ++ht) {
-      acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ht = 0; ht < 4; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 4; ++s) acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ht][s], kf[s], acc[ht], 0, 0, 0);
-    }
-    const float x = head_sum(acc);
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ht][s], tl.k[s], acc[ht], 0, 0, 0);
+  };
+  auto epi = [&](int t, int pos, const f32x4 (&acc)[4]) {
+    if (t < 0 || t >= ntf) return;
+    float x = 0.f;
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x += relu(acc[ht][i]) * wl[ht][i];
+    x = sum_rows(x);
     const int cidx = t * 16 + c;
-    if (g == 0 && cidx < C) sc[cidx] = cand(cidx) < valid ? x : kNeg;
+    if (g == 0 && cidx < C) sc[cidx] = pos < valid ? x : kNeg;
+  };
+  Tile k0, k1, k2, k3;
+  f32x4 accA[4], accB[4];
+  int posA = 0, posB = 0;
+  fetch(0, k0);
+  fetch(1, k1);
+  fetch(2, k2);
+  for (int t = 0; t < ntf; t += 4) {
+    fetch(t + 3, k3);
+    mma(k0, accA);
+    posA = k0.pos;
+    epi(t - 1, posB, accB);
+    fetch(t + 4, k0);
+    mma(k1, accB);
+    posB = k1.pos;
+    epi(t, posA, accA);
+    fetch(t + 5, k1);
+    mma(k2, accA);
+    posA = k2.pos;
+    epi(t + 1, posB, accB);
+    fetch(t + 6, k2);
+    mma(k3, accB);
+    posB = k3.pos;
+    epi(t + 2, posA, accA);
   }
+  // the last tile of the last step (t + 3)
+  epi(((ntf + 3) / 4) * 4 - 1, posB, accB);
   if (!live) return;
   const int nrf = (C + 63) / 64;
 #pragma unroll

@@ -121,7 +121,8 @@ int hisa_block_scores(const hisa_dims* d, const void* q_idx, const float* w, con
  * Workspace: its first B * 4 bytes are per-sequence arrival counters of the
  * fused scan + selection kernel.  They must be zero before the first call
  * that uses the workspace (zero-fill it once after allocating it); every
- * call leaves them zero.
+ * call leaves them zero.  Two calls that share a workspace must not run at
+ * the same time (on different streams); calls on one stream are ordered.
  *   I_out       (B, 1, topk) int32.
  *   top_blk_out (B, 1, index_keep) int32 or NULL: the retained blocks (HiSA
  *               path only, ascending; -1 elsewhere).

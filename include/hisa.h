@@ -118,10 +118,10 @@ int hisa_block_scores(const hisa_dims* d, const void* q_idx, const float* w, con
  * runs per sequence: dense -> I = 0..Np-1; flat -> the flat top-k; HiSA ->
  * coarse top-Kb blocks then the fine top-k within them (the tail rows
  * [nb*b, Np) are never selected).
- * Workspace: its first B * 4 bytes are per-sequence arrival counters of the
- * fused scan + selection kernel.  They must be zero before the first call
- * that uses the workspace (zero-fill it once after allocating it); every
- * call leaves them zero.  Two calls that share a workspace must not run at
+ * Workspace: its first B * (1 + ceil(ceil(Np_cap / 64) / 16)) * 64 bytes are
+ * arrival counters of the fused scan + selection kernel.  They must be zero
+ * before the first call that uses the workspace (zero-fill it once after
+ * allocating it); every call leaves them zero.  Two calls that share a workspace must not run at
  * the same time (on different streams); calls on one stream are ordered.
  *   I_out       (B, 1, topk) int32.
  *   top_blk_out (B, 1, index_keep) int32 or NULL: the retained blocks (HiSA

@@ -45,9 +45,13 @@ def dims(**kw):
 
 def test_workspace_sizes(lib):
     d = dims()
-    # decode: the arrival counters (one 256-byte region), f32 scores of every
-    # pooled row + one coarse score per block
-    assert hisa.workspace_bytes(hisa.OP_SELECT_DECODE, d) == 256 + 16384 * 4 + 256 * 4
+    # decode: the arrival counters (1 sequence + 16 slab-group counters, 64
+    # bytes each, rounded up to 256), f32 scores of every pooled row + one
+    # coarse score per block
+    assert hisa.workspace_bytes(hisa.OP_SELECT_DECODE, d) == 1280 + 16384 * 4 + 256 * 4
+    # 32 sequences of up to 512 slabs: 32 sequence counters + 32 x 32 group counters
+    assert hisa.workspace_bytes(hisa.OP_SELECT_DECODE, dims(B=32, Np_cap=32768)) == (
+        32 * 33 * 64 + 32 * 32768 * 4 + 32 * 512 * 4)
     assert hisa.workspace_bytes(hisa.OP_FLAT_TOPK, dims(L=4, Np_cap=1000)) == ((4 * 1000 * 4 + 255) // 256) * 256
     # single-row attention splits the 640 rows into 10 parts of 64
     assert hisa.workspace_bytes(hisa.OP_ATTENTION, d) == 10 * 64 * 514 * 4

@@ -278,7 +278,13 @@ def test_decode_workspace_reuse(hisa):
             Io, blko, po = oracle.select_row(od, xx["q_idx"][b, 0], xx["w"][b, 0], xx["keys"][b], t0s[b], 0)
             assert p[b] == po, (b, p[b], po)
             parity.check_selection_row(od, xx, b, 0, In[b, 0], bn[b, 0], p[b], Io, blko, po)
-    assert (ws[: 4 * w.B].view(torch.int32) == 0).all()
+    assert (ws[: counter_bytes(w)].view(torch.int32) == 0).all()
+
+
+def counter_bytes(w):
+    # arrival counters of the fused decode: B x (1 + ceil(slabs / 16)), 64 bytes each
+    slabs = -(-w.Np_cap // 64)
+    return w.B * (1 + -(-slabs // 16)) * 64
 
 
 MIXED_STREAM = MIXED.with_(name="mixed_paths_b7_stream", B=7, t0=[1200, 2800, 4096, 6000, 160000, 16400, 90000],
@@ -310,7 +316,53 @@ def test_mixed_paths_decode_stream(hisa):
             Io, blko, po = oracle.select_row(od, xx["q_idx"][b, 0], xx["w"][b, 0], xx["keys"][b], t0s[b], 0)
             assert p[b] == po, (b, p[b], po)
             parity.check_selection_row(od, xx, b, 0, In[b, 0], bn[b, 0], p[b], Io, blko, po)
-    assert (ws[: 4 * w.B].view(torch.int32) == 0).all()
+    assert (ws[: counter_bytes(w)].view(torch.int32) == 0).all()
+
+
+@pytest.mark.parametrize("case", [(MIXED, 5), (MIXED_STREAM, 21)], ids=["latency_scan", "streaming_scan"])
+def test_decode_exact_ties(hisa, case):
+    # Exact score ties straddle both top-k boundaries of the decode selection:
+    # the best-scoring row of each HiSA sequence is copied over rows 640 ..
+    # 2559 (blocks 10 .. 39), so up to 30 blocks share the top coarse score
+    # and up to 1920 rows the top fine score; the flat sequence gets 500 equal
+    # rows.  Both sides break ties by the lowest id, so the tied ids that are
+    # kept must be exactly the oracle's.
+    w, seed = case
+    x, g = inputs(w, seed)
+    od = odims(w, x)
+    keys = x["keys"].copy()
+    dup = {}
+    for b in range(w.B):
+        t0 = int(w.t0[b])
+        Np = oracle.num_pooled(t0, 1, w.ratio)
+        _, _, po = oracle.select_row(od, x["q_idx"][b, 0], x["w"][b, 0], x["keys"][b], t0, 0)
+        if po == oracle.PATH_FLAT:
+            lo, hi = 100, 600
+        elif po == oracle.PATH_HISA:
+            lo, hi = 640, min(2560, Np)
+        else:
+            continue
+        sc = oracle.scores_of(od, x["q_idx"][b, 0], x["w"][b, 0], x["keys"][b], t0, 0, np.arange(Np, dtype=np.int32))
+        keys[b, lo:hi] = x["keys"][b, int(np.argmax(sc))]
+        dup[b] = (lo, hi)
+    xx = dict(x)
+    xx["keys"] = keys
+    gk = torch.from_numpy(keys).to("cuda").to(torch.bfloat16).contiguous()
+    say(f"[run] decode with exact ties, {w.name}")
+    I, blk, path = hisa.hisa_select_decode(g["q_idx"], g["w"], gk, g["t0"], **sel_kw(w))
+    torch.cuda.synchronize()
+    In, bn, p = parity.to_np(I), parity.to_np(blk), parity.to_np(path)
+    for b, (lo, hi) in dup.items():
+        t0 = int(w.t0[b])
+        Io, blko, po = oracle.select_row(od, xx["q_idx"][b, 0], xx["w"][b, 0], keys[b], t0, 0)
+        assert p[b] == po, (b, p[b], po)
+        parity.check_selection_row(od, xx, b, 0, In[b, 0], bn[b, 0], p[b], Io, blko, po)
+        tied = lambda ids: set(i for i in ids.tolist() if lo <= i < hi)
+        assert tied(In[b, 0]) == tied(Io), b
+        assert len(tied(Io)) > 0
+        if po == oracle.PATH_HISA:
+            tb = lambda ids: set(i for i in ids.tolist() if lo // 64 <= i < -(-hi // 64))
+            assert tb(bn[b, 0]) == tb(blko), b
 
 
 def test_invalid_sequence_outputs(hisa):

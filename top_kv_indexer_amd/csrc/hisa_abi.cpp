@@ -125,7 +125,7 @@ Layout layout(int op, const hisa_dims* d, const KDims& k) {
       break;
     case HISA_OP_SELECT_DECODE:
       // arrival counters first: the region callers zero once (see hisa.h)
-      l.cnt = take(l, B * sizeof(int));
+      l.cnt = take(l, hisa::decode_counter_ints(k) * sizeof(int));
       l.fscore = take(l, B * d->Np_cap * sizeof(float));
       l.cscore = take(l, B * std::max<size_t>(nb_cap, 1) * sizeof(float));
       break;

@@ -25,7 +25,13 @@ struct KDims {
 // Pointers are device pointers; bf16 data is passed as uint16_t.
 // Decode scan; with cnt != NULL (decode_fused_ok) it also runs the selection
 // and writes I / top_blk / path, and launch_decode_select is not needed.
-// cnt: B zeroed ints, left zeroed.
+// cnt: decode_counter_ints(d) zeroed ints, left zeroed.
+constexpr int kCntStride = 16;  // ints between arrival counters: one 64-byte line each
+inline size_t decode_counter_ints(const KDims& d) {
+  // B sequence counters + B x ceil(ceil(Np_cap / 64) / 16) slab-group counters
+  const size_t slabs = ((size_t)d.Np_cap + 63) / 64;
+  return (size_t)d.B * (1 + (slabs + 15) / 16) * kCntStride;
+}
 bool decode_fused_ok(const KDims& d, bool bf16);
 hipError_t launch_decode_scan(const KDims& d, bool bf16, const void* q_idx, const float* w,
                               const void* keys, const int* t0, float* fscore, float* cscore,

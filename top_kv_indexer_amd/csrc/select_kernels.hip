@@ -136,62 +136,237 @@ __device__ __forceinline__ float ld_dev(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Decode selection of sequence b by one wave, from the scan's fine scores fs
-// (Np entries) and block scores cs (nb entries): the flat top-k (Np <= 1024),
-// or the coarse top-Kb blocks (nb <= 1024, Kb <= 64) and the fine top-k of
-// their C = Kb*b <= 1024 rows (HiSA issue, HiSA decode path).  Ids come out
-// ascending, padded with -1.
-__device__ __forceinline__ void decode_select_wave(const KDims& d, const SeqInfo& si, int b, const float* fs,
-                                                   const float* cs, int* I, int* top_blk, int* path, int* s_blk,
-                                                   uint32_t* hist) {
-  const int lane = lane_id();
+// ---- workgroup top-k (256 threads): thread t holds element 256 r + t in
+// key[r], r < NR (order index = element index, ascending in id); key 0 marks
+// an absent element.
+struct WgTopkSmem {
+  uint32_t hist[3][256];  // rotating histograms: one barrier per radix pass
+  uint32_t red[2][4];     // per-wave min and max of the present keys
+  uint32_t cnt[2][4][4];  // per register and wave: keys equal to the threshold, keys taken
+};
+
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+  v = max(v, dpp_u<kDppXor1>(v));
+  v = max(v, dpp_u<kDppXor2>(v));
+  v = max(v, dpp_u<kDppHalfMirror>(v));
+  v = max(v, dpp_u<kDppMirror>(v));
+  u32x2 p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max(p.x, p.y);
+  p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max(p.x, p.y);
+}
+__device__ __forceinline__ uint32_t wave_umin(uint32_t v) {
+  v = min(v, dpp_u<kDppXor1>(v));
+  v = min(v, dpp_u<kDppXor2>(v));
+  v = min(v, dpp_u<kDppHalfMirror>(v));
+  v = min(v, dpp_u<kDppMirror>(v));
+  u32x2 p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = min(p.x, p.y);
+  p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return min(p.x, p.y);
+}
+
+// Threshold of the top k present keys (1 <= k <= present count): returns t
+// and `ties` such that the top k are the keys > t and the first `ties` keys
+// == t in order index (kAllTies: every key == t).  Radix select that starts at the highest bit where the
+// present keys differ (above it they all agree, so no pass is spent on it)
+// and stops as soon as the bin holding the k-th key is taken whole.  Every
+// wave evaluates the same scan of the shared histogram, so the control flow
+// is uniform over the workgroup.
+constexpr int kAllTies = 0x7FFFFFFF;
+template <int NR>
+__device__ __forceinline__ uint32_t wg_topk_threshold(const uint32_t (&key)[4], int k, WgTopkSmem& sm, int& ties) {
+  const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+    if (key[r] != 0u) {
+      mn = min(mn, key[r]);
+      mx = max(mx, key[r]);
+    }
+  mn = wave_umin(mn);
+  mx = wave_umax(mx);
+  if (lane == 0) {
+    sm.red[0][wv] = mn;
+    sm.red[1][wv] = mx;
+  }
+  sm.hist[0][tid] = 0u;
+  sm.hist[1][tid] = 0u;
+  __syncthreads();
+  mn = min(min(sm.red[0][0], sm.red[0][1]), min(sm.red[0][2], sm.red[0][3]));
+  mx = max(max(sm.red[1][0], sm.red[1][1]), max(sm.red[1][2], sm.red[1][3]));
+  if (mn == mx) {  // every present key is equal
+    ties = k;
+    return mx;
+  }
+  int top = 31 - __builtin_clz(mn ^ mx);  // highest bit still unknown
+  uint32_t mask = top == 31 ? 0u : ~0u << (top + 1);
+  uint32_t prefix = mx & mask;
+  int remaining = k;  // keys still to take at or below the known prefix
+#pragma unroll 1
+  for (int pass = 0;; ++pass) {
+    const int shift = max(top - 7, 0);
+    uint32_t* h = sm.hist[pass % 3];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const uint32_t u = key[r];
+      if (u != 0u && (u & mask) == prefix) atomicAdd(&h[(u >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    // lane l holds bins 255-4l (first) .. 252-4l
+    const uint4 hv = *(const uint4*)&h[252 - 4 * lane];
+    // the buffer of pass + 2: every thread finished reading it (pass - 1)
+    sm.hist[(pass + 2) % 3][tid] = 0u;
+    const uint32_t local = hv.x + hv.y + hv.z + hv.w;
+    const uint32_t incl = wave_incl_scan(local);
+    const uint32_t above = incl - local;
+    const bool hit = above < (uint32_t)remaining && incl >= (uint32_t)remaining;
+    const int src = __builtin_ctzll(__ballot(hit));
+    uint32_t acc = above, digit = 252 - 4 * lane, inbin = hv.x;
+    if (acc + hv.w >= (uint32_t)remaining) { digit = 255 - 4 * lane; inbin = hv.w; }
+    else if ((acc += hv.w) + hv.z >= (uint32_t)remaining) { digit = 254 - 4 * lane; inbin = hv.z; }
+    else if ((acc += hv.z) + hv.y >= (uint32_t)remaining) { digit = 253 - 4 * lane; inbin = hv.y; }
+    else acc += hv.y;
+    digit = (uint32_t)__builtin_amdgcn_readlane((int)digit, src);
+    acc = (uint32_t)__builtin_amdgcn_readlane((int)acc, src);
+    inbin = (uint32_t)__builtin_amdgcn_readlane((int)inbin, src);
+    remaining -= (int)acc;
+    prefix = (prefix & ~(255u << shift)) | (digit << shift);
+    mask = ~0u << shift;
+    if ((uint32_t)remaining == inbin) {  // the whole bin is taken: keys >= prefix
+      ties = kAllTies;
+      return prefix;
+    }
+    if (shift == 0) {  // fully resolved: t is the k-th key, shared by inbin keys
+      ties = remaining;
+      return prefix;
+    }
+    top = shift - 1;
+  }
+}
+
+// emits the k winners in ascending order index: emit(slot, r)
+template <int NR, class EmitF>
+__device__ __forceinline__ void wg_emit_topk_n(const uint32_t (&key)[4], int k, WgTopkSmem& sm, EmitF emit) {
+  const int lane = lane_id(), wv = wave_id();
+  int ties;
+  const uint32_t t = wg_topk_threshold<NR>(key, k, sm, ties);
+  bool take[NR];
+  if (ties == kAllTies) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) take[r] = key[r] != 0u && key[r] >= t;
+  } else {
+    // ranks of the keys == t: counts per register and wave first
+    uint64_t meq[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      meq[r] = __ballot(key[r] != 0u && key[r] == t);
+      if (lane == 0) sm.cnt[0][r][wv] = (uint32_t)__popcll(meq[r]);
+    }
+    __syncthreads();
+    int eq_base = 0;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      int before = eq_base, tot = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = (int)sm.cnt[0][r][u];
+        before += u < wv ? c : 0;
+        tot += c;
+      }
+      const bool eq = key[r] != 0u && key[r] == t;
+      take[r] = key[r] > t || (eq && before + lanes_below(meq[r]) < ties);
+      eq_base += tot;
+    }
+  }
+  uint64_t mt[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    mt[r] = __ballot(take[r]);
+    if (lane == 0) sm.cnt[1][r][wv] = (uint32_t)__popcll(mt[r]);
+  }
+  __syncthreads();
+  int base = 0;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    int before = base, tot = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = (int)sm.cnt[1][r][u];
+      before += u < wv ? c : 0;
+      tot += c;
+    }
+    if (take[r]) emit(before + lanes_below(mt[r]), r);
+    base += tot;
+  }
+}
+
+// the same for n <= 1024 elements (keys of elements >= n are 0)
+template <class EmitF>
+__device__ __forceinline__ void wg_emit_topk(const uint32_t (&key)[4], int n, int k, WgTopkSmem& sm, EmitF emit) {
+  if (n <= 256) wg_emit_topk_n<1>(key, k, sm, emit);
+  else if (n <= 512) wg_emit_topk_n<2>(key, k, sm, emit);
+  else wg_emit_topk_n<4>(key, k, sm, emit);
+}
+
+// Decode selection of sequence b by a whole workgroup (256 threads), from the
+// scan's fine scores fs (Np entries) and block scores cs (nb entries): the
+// flat top-k (Np <= 1024), or the coarse top-Kb blocks (nb <= 1024, Kb <= 64)
+// and the fine top-k of their C = Kb*b <= 1024 rows (HiSA issue, HiSA decode
+// path).  Ids come out ascending, padded with -1.  Every thread calls it.
+struct DecodeSelSmem {
+  WgTopkSmem tk;
+  int blk[kRowKeep];
+};
+__device__ __forceinline__ void decode_select_wg(const KDims& d, const SeqInfo& si, int b, const float* fs,
+                                                 const float* cs, int* I, int* top_blk, int* path,
+                                                 DecodeSelSmem& sm) {
+  const int tid = threadIdx.x;
   int* Ib = I + (size_t)b * d.topk;
   int* blkb = top_blk ? top_blk + (size_t)b * d.index_keep : nullptr;
-  for (int i = lane; i < d.topk; i += 64)
-    if (i >= si.k) Ib[i] = -1;
+  for (int i = si.k + tid; i < d.topk; i += 256) Ib[i] = -1;
   if (blkb)
-    for (int i = lane; i < d.index_keep; i += 64)
+    for (int i = tid; i < d.index_keep; i += 256)
       if (si.path != PATH_HISA || i >= si.Kb) blkb[i] = -1;
-  if (path && lane == 0) path[b] = si.path;
-  uint32_t key[kRowR];
+  if (path && tid == 0) path[b] = si.path;
+  uint32_t key[4];
+  float v[4];
   if (si.path == PATH_FLAT) {
-    const int n = si.Np, nr = (n + 63) / 64;
-    float v[kRowR];
+    const int n = si.Np;
 #pragma unroll
-    for (int r = 0; r < kRowR; ++r) v[r] = ld_dev(fs + min(64 * r + lane, n - 1));
+    for (int r = 0; r < 4; ++r) v[r] = ld_dev(fs + min(256 * r + tid, n - 1));
     __builtin_amdgcn_sched_barrier(0);  // every load in flight before the first wait
 #pragma unroll
-    for (int r = 0; r < kRowR; ++r) key[r] = (r < nr && 64 * r + lane < n) ? score_key(v[r]) : 0u;
-    wave_emit_topk(key, nr, si.k, hist, [&](int slot, int r) { Ib[slot] = 64 * r + lane; });
+    for (int r = 0; r < 4; ++r) key[r] = 256 * r + tid < n ? score_key(v[r]) : 0u;
+    wg_emit_topk(key, n, si.k, sm.tk, [&](int slot, int r) { Ib[slot] = 256 * r + tid; });
     return;
   }
-  const int nb = si.nb, nrc = (nb + 63) / 64;
-  float v[kRowR];
+  const int nb = si.nb;
 #pragma unroll
-  for (int r = 0; r < kRowR; ++r) v[r] = ld_dev(cs + min(64 * r + lane, nb - 1));
+  for (int r = 0; r < 4; ++r) v[r] = ld_dev(cs + min(256 * r + tid, nb - 1));
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int r = 0; r < kRowR; ++r) key[r] = (r < nrc && 64 * r + lane < nb) ? score_key(v[r]) : 0u;
-  wave_emit_topk(key, nrc, si.Kb, hist, [&](int slot, int r) { s_blk[slot] = 64 * r + lane; });
-  if (blkb)
-    for (int i = lane; i < si.Kb; i += 64) blkb[i] = s_blk[i];
+  for (int r = 0; r < 4; ++r) key[r] = 256 * r + tid < nb ? score_key(v[r]) : 0u;
+  wg_emit_topk(key, nb, si.Kb, sm.tk, [&](int slot, int r) { sm.blk[slot] = 256 * r + tid; });
+  __syncthreads();
+  if (blkb && tid < si.Kb) blkb[tid] = sm.blk[tid];
   const int bsz = d.index_block, lbsz = __builtin_ctz(bsz);
-  const int C = si.Kb * bsz, nrf = (C + 63) / 64;
-  // candidate cc is row s_blk[cc / b] * b + cc % b: every position first
-  // (LDS reads back to back), then every score load
-  int pos[kRowR];
+  const int C = si.Kb * bsz;
+  // candidate cc is row blk[cc / b] * b + cc % b: every position first (LDS
+  // reads back to back), then every score load
+  int pos[4];
 #pragma unroll
-  for (int r = 0; r < kRowR; ++r) {
-    const int cc = min(64 * r + lane, C - 1);
-    pos[r] = (s_blk[cc >> lbsz] << lbsz) + (cc & (bsz - 1));
+  for (int r = 0; r < 4; ++r) {
+    const int cc = min(256 * r + tid, C - 1);
+    pos[r] = (sm.blk[cc >> lbsz] << lbsz) + (cc & (bsz - 1));
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int r = 0; r < kRowR; ++r) v[r] = ld_dev(fs + pos[r]);
+  for (int r = 0; r < 4; ++r) v[r] = ld_dev(fs + pos[r]);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int r = 0; r < kRowR; ++r) key[r] = (r < nrf && 64 * r + lane < C) ? score_key(v[r]) : 0u;
-  wave_emit_topk(key, nrf, si.k, hist, [&](int slot, int r) { Ib[slot] = pos[r]; });
+  for (int r = 0; r < 4; ++r) key[r] = 256 * r + tid < C ? score_key(v[r]) : 0u;
+  wg_emit_topk(key, C, si.k, sm.tk, [&](int slot, int r) { Ib[slot] = pos[r]; });
 }
 
 // relu as one instruction (v_med3): max(x, 0) for finite x
@@ -291,51 +466,52 @@ __device__ __forceinline__ void score_slab(const KDims& d, const SeqInfo& si, in
   }
 }
 
-// The end of a sequence's run of slabs in a workgroup: once every wave has
-// seen its device-scope score stores acknowledged, the workgroup adds `done`
-// slabs to cnt[b].  Returns (uniformly) whether this workgroup completed the
-// sequence (nslab slabs); it then returns cnt[b] to 0 and owes the
-// sequence's selection.  Every thread of the workgroup calls it.
-__device__ __forceinline__ bool publish_run(int b, int done, int nslab, int* cnt, int* s_flag) {
+// Adds n to a device-scope arrival counter that completes at `total`;
+// returns whether this call completed it (and then returns it to 0).
+__device__ __forceinline__ bool arrive(int* c, int n, int total) {
+  const int prev = __hip_atomic_fetch_add(c, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (prev + n != total) return false;
+  __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
+// Once every wave has seen its device-scope score stores acknowledged (so
+// they are visible to device-scope loads anywhere), thread 0 runs `count`
+// and the workgroup learns its uniform result.
+template <class CountF>
+__device__ __forceinline__ bool publish(CountF count, int* s_flag) {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0
   asm volatile("" ::: "memory");
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const int prev = __hip_atomic_fetch_add(cnt + b, done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *s_flag = prev + done == nslab;
-    if (*s_flag) __hip_atomic_store(cnt + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (threadIdx.x == 0) *s_flag = count();
   __syncthreads();
   return *s_flag != 0;
 }
 
-// The selection of a completed sequence (wave 0 of the completing
-// workgroup): every score is at the coherence point, and decode_select_wave
-// reads them with device-scope loads.
-__device__ __forceinline__ void select_completed(const KDims& d, int b, const int* t0, const float* fscore,
-                                                 const float* cscore, int* I, int* top_blk, int* path, int* s_blk,
-                                                 uint32_t* s_hist) {
-  const SeqInfo si = seq_info(d, t0[b]);
-  decode_select_wave(d, si, b, fscore + (size_t)b * d.Np_cap, cscore + (size_t)b * d.nb_cap, I, top_blk, path,
-                     s_blk, s_hist);
-}
+// Counters of the latency-bound scan: one per group of kArriveGroup slabs
+// and one per sequence that counts completed groups.  Atomics on one 64-byte
+// line are performed one after another (~11 ns each), so every counter has a
+// line of its own (kCntStride ints) and sees at most kArriveGroup (or
+// slabs / kArriveGroup) of them.
+constexpr int kArriveGroup = 16;
 
 // Latency-bound decode scan (few slabs): one workgroup per 64-row slab of one
 // sequence.  The slab's rows are requested before t0 arrives (rows clamped to
 // the buffer rather than to Np) and q comes into LDS in parallel.  With cnt
-// != NULL the selection is fused (publish_run with one slab per workgroup);
-// the first workgroup of a dense or invalid sequence writes its outputs.
+// != NULL the selection is fused: the workgroup that completes the last group
+// of slabs selects; the first workgroup of a dense or invalid sequence writes
+// its outputs.
 __global__ __launch_bounds__(256) void k_decode_scan_mfma(
     KDims d, const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ keys,
     const int* __restrict__ t0, float* fscore, float* cscore, int* cnt, int* I, int* top_blk, int* path) {
   __shared__ __align__(16) uint16_t s_q[64 * 128];
   __shared__ __align__(16) float s_part[2][4][64];
-  __shared__ int s_blk[kRowKeep];
-  __shared__ __align__(16) uint32_t s_hist[256];
+  __shared__ DecodeSelSmem s_sel;
   __shared__ int s_flag;
   const int b = blockIdx.y, slab = blockIdx.x;
   const int lane = lane_id(), g = lane >> 4;
+  const int t0b = t0[b];  // requested first, needed after the rows arrive
   const uint16_t* kb = keys + (size_t)b * d.Np_cap * 128;
   bf16x8 kf[4];
   load_slab_rows(kb, slab, d.Np_cap - 1, kf);
@@ -357,7 +533,7 @@ __global__ __launch_bounds__(256) void k_decode_scan_mfma(
   w_head *= d.w_scale;
   bf16x8 qf[4][4];
   read_q_lds(s_q, qf);
-  const SeqInfo si = seq_info(d, t0[b]);
+  const SeqInfo si = seq_info(d, t0b);
   if (!si.ok || si.path == PATH_DENSE) {
     if (cnt && slab == 0 && wave_id() == 0) write_unscored(d, si, b, I, top_blk, path);
     return;
@@ -365,8 +541,19 @@ __global__ __launch_bounds__(256) void k_decode_scan_mfma(
   const int nslab = (si.Np + 63) / 64;
   if (slab >= nslab) return;  // uniform over the workgroup
   score_slab(d, si, b, slab, 0, qf, wl, w_head, kf, fscore, cscore, s_part);
-  if (cnt && publish_run(b, 1, nslab, cnt, &s_flag) && wave_id() == 0)
-    select_completed(d, b, t0, fscore, cscore, I, top_blk, path, s_blk, s_hist);
+  if (!cnt) return;
+  // cnt: B sequence counters, then B x ngmax group counters, kCntStride apart
+  const int grp = slab / kArriveGroup, ngrp = (nslab + kArriveGroup - 1) / kArriveGroup;
+  const int ngmax = (gridDim.x + kArriveGroup - 1) / kArriveGroup;
+  const bool last = publish(
+      [&] {
+        const int members = min(kArriveGroup, nslab - grp * kArriveGroup);
+        int* c_grp = cnt + (size_t)(d.B + (size_t)b * ngmax + grp) * kCntStride;
+        return arrive(c_grp, 1, members) && arrive(cnt + (size_t)b * kCntStride, 1, ngrp);
+      },
+      &s_flag);
+  if (last)
+    decode_select_wg(d, si, b, fscore + (size_t)b * d.Np_cap, cscore + (size_t)b * d.nb_cap, I, top_blk, path, s_sel);
 }
 
 // Bandwidth-bound decode scan (many slabs, ragged batches): a persistent
@@ -375,7 +562,7 @@ __global__ __launch_bounds__(256) void k_decode_scan_mfma(
 // ragged pooled counts stay balanced and q is reloaded only where the share
 // crosses into the next sequence; the rows of the next two slabs stream in
 // while one is scored.  With cnt != NULL each run of a sequence's slabs is
-// published with one atomic (publish_run), and the workgroup that completes
+// published with one atomic (publish, arrive), and the workgroup that completes
 // a sequence selects for it.  Workgroup x writes the outputs of the dense or
 // invalid sequences b with b % gridDim.x == x.  B <= kStreamMaxB.
 constexpr int kStreamMaxB = 1024;
@@ -387,8 +574,7 @@ __global__ __launch_bounds__(256) void k_decode_scan_stream(
   __shared__ __align__(16) float s_part[2][4][64];
   __shared__ int s_pre[kStreamMaxB + 1];  // first flattened slab of each sequence
   __shared__ uint32_t s_wsum[4];
-  __shared__ int s_blk[kRowKeep];
-  __shared__ __align__(16) uint32_t s_hist[256];
+  __shared__ DecodeSelSmem s_sel;
   __shared__ int s_flag;
   __shared__ int s_done[kStreamMaxB];  // sequences this workgroup completed
   const int tid = threadIdx.x, lane = lane_id(), wv = wave_id(), g = lane >> 4;
@@ -481,7 +667,7 @@ __global__ __launch_bounds__(256) void k_decode_scan_stream(
     const bool seq_ends = x + 1 == g_end || bn != b;
     if (seq_ends) {
       const int nslab = s_pre[b + 1] - s_pre[b];
-      if (cnt && publish_run(b, x + 1 - run_start, nslab, cnt, &s_flag)) {
+      if (cnt && publish([&] { return arrive(cnt + (size_t)b * kCntStride, x + 1 - run_start, nslab); }, &s_flag)) {
         if (tid == 0) s_done[n_done] = b;
         ++n_done;
       }
@@ -502,9 +688,12 @@ __global__ __launch_bounds__(256) void k_decode_scan_stream(
   // so its registers are free)
   if (n_done == 0) return;
   __syncthreads();
-  if (wv == 0)
-    for (int u = 0; u < n_done; ++u)
-      select_completed(d, s_done[u], t0, fscore, cscore, I, top_blk, path, s_blk, s_hist);
+  for (int u = 0; u < n_done; ++u) {
+    const int bd = s_done[u];
+    decode_select_wg(d, seq_info(d, t0[bd]), bd, fscore + (size_t)bd * d.Np_cap, cscore + (size_t)bd * d.nb_cap, I,
+                     top_blk, path, s_sel);
+    __syncthreads();  // s_sel is reused by the next selection
+  }
 }
 
 // Any shape / dtype: 4 threads per row, VALU dot products.

@@ -112,6 +112,7 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
   __shared__ uint32_t s_tmask[NTILE];
   __shared__ __align__(16) int s_code[CH];  // row code of each entry of the current chunk
 
+  args_now(d, splits, q, local_kv, pooled_kv, I, sinks, t0, out, part);
   const int split = blockIdx.x;
   // consecutive query rows go to the same XCD (workgroups are dealt to the 8
   // XCDs round-robin), so rows sharing their local window share its L2
@@ -125,6 +126,36 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
   const int hg = wv >> 1, dh = wv & 1;
   const int hbase = blockIdx.z * HW;
   auto sw = [](int r) { return ((r & 7) << 1) | ((r >> 3) & 1); };
+  const uint32_t kv_lds = lds_addr(&kv[0][0]);
+  // scores: this wave's 16 heads of q as the B operand.  With 64 heads the
+  // workgroup's head rows (contiguous in q) come in through the last two ring
+  // slots, one 1 KiB global->LDS load per row (swizzled like the KV rows);
+  // with 16 heads straight into registers.
+  bf16x8 qf[NS];
+  auto issue_q = [&]() {
+    uint16_t* qs = kv[NBUF - 2];  // HW <= 64 rows span slots NBUF-2 and NBUF-1
+    const uint16_t* qg = q + ((size_t)row * d.H + hbase) * DK;
+#pragma unroll
+    for (int u = 0; u < HW / NW; ++u) {
+      const int h = wv + NW * u;
+      const uint32_t dst = kv_lds + (uint32_t)(((NBUF - 2) * kTile + h) * KPD * 2);
+      g2lds16(qg + (size_t)h * DK + (lane ^ sw(h)) * 8, dst);
+      if (DK > 512 && lane < DK / 8 - 64) g2lds16(qg + (size_t)h * DK + 512 + lane * 8, dst + 1024);
+    }
+  };
+  // q fragments from LDS, once every wave's rows have landed (the caller has
+  // waited for its own q loads)
+  auto read_q = [&]() {
+    __syncthreads();
+    const uint16_t* qs = kv[NBUF - 2];
+    const int hr = hg * 16 + c;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int ch = 4 * s + g;
+      qf[s] = *(const bf16x8*)(qs + hr * KPD + (ch < 64 ? ch ^ sw(c) : ch) * 8);
+    }
+    __syncthreads();  // slots NBUF-2 and NBUF-1 are free again
+  };
   // Row list: the kI pooled ids of I first, then `window` local slots (slot
   // s holds position s_lo + s while s < n_loc).  The split geometry does not
   // depend on t0, so the index loads below go out before t0 arrives.
@@ -139,7 +170,63 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
     const int ea = begin + ident_row(u);
     id_a[u] = (ea < end && ea < d.kI) ? Irow[ea] : -1;
   }
-  const int T0 = t0[b];
+  // a scalar load (b is uniform), so waiting for it does not wait for the
+  // vector loads around it
+  const int T0 = t0[__builtin_amdgcn_readfirstlane(b)];
+  // q is requested right after the ids and t0, so its latency overlaps
+  // theirs and the row bookkeeping waits only for them
+  if constexpr (NHG >= 4) {
+    issue_q();  // many heads per row: staged through LDS (read below)
+  } else {
+    const uint16_t* qrow = q + ((size_t)row * d.H + hbase + hg * 16 + c) * DK + g * 8;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qf[s] = *(const bf16x8*)(qrow + s * 32);
+  }
+  // values: O^T tiles (16 value columns x 16 heads) of every head tile
+  f32x4 acc[NDT][NHG];
+#pragma unroll
+  for (int n = 0; n < NDT; ++n)
+#pragma unroll
+    for (int ht = 0; ht < NHG; ++ht) acc[n][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // softmax: lane (hq, rq) = (lane >> 3, lane & 7) holds rows 4rq..4rq+3 of head 8*wv + hq
+  const int hq = lane >> 3, rq = lane & 7;
+  const int hs = 8 * wv + hq;
+  float m = -INFINITY, l = 0.f;
+  const float scale = d.attn_scale_log2;
+  // transposing V reads: lane (g, c) takes rows 4g + c/4 (+16) and columns
+  // 4*(c%4) .. +3 of a 16-column value tile
+  const int vrow = 4 * g + (c >> 2);
+  const int vsw = sw(vrow);  // rows vrow and vrow + 16 share the swizzle
+  auto vaddr = [&](int dt, int hi) {
+    const int ch = 2 * dt + ((c & 3) >> 1);
+    return (vrow + 16 * hi) * KPD + (ch < 64 ? ch ^ vsw : ch) * 8 + 4 * (c & 1);
+  };
+  // This lane's LDS element offsets inside a ring slot for the K reads of
+  // every MFMA k-step and the V reads of every value tile it owns, and of
+  // its 16-byte piece of each tile row the wave fetches.  They depend on the
+  // lane alone.  With 16 heads (few, latency-bound workgroups) they are
+  // pinned here, while the loads above are in flight, instead of being
+  // computed where the compiler hoists them (after the waits); with 64 heads
+  // the compiler keeps folding them into the LDS instructions' offsets.
+  int k_el[NS], v_el[NDT][2], src_el[RPW];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int ch = 4 * s + g;
+    k_el[s] = (dh * 16 + c) * KPD + (ch < 64 ? ch ^ sw(c) : ch) * 8;
+    if constexpr (NHG == 1) asm volatile("" : "+v"(k_el[s]));
+  }
+#pragma unroll
+  for (int n = 0; n < NDT; ++n)
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      v_el[n][hi] = vaddr(wv + NW * n, hi);
+      if constexpr (NHG == 1) asm volatile("" : "+v"(v_el[n][hi]));
+    }
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    src_el[r] = (lane ^ sw(RPW * wvs + r)) * 8;
+    if constexpr (NHG == 1) asm volatile("" : "+v"(src_el[r]));
+  }
   const RowPlan rp = row_plan(d, T0, j);
   // a row every sequence with a live row may read (dead rows point at it)
   const int dummy = rp.n_loc > 0 ? -1 - (rp.s_lo - rp.ls) : 0;
@@ -158,65 +245,10 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
     code = -1 - (rp.s_lo - rp.ls + e - d.kI);
     return true;
   };
-
-  // scores: this wave's 16 heads of q as the B operand.  With 64 heads the
-  // workgroup's head rows (contiguous in q) come in through the last two ring
-  // slots, one 1 KiB global->LDS load per row (swizzled like the KV rows);
-  // with 16 heads straight into registers.
-  bf16x8 qf[NS];
-  auto issue_q = [&]() {
-    uint16_t* qs = kv[NBUF - 2];  // HW <= 64 rows span slots NBUF-2 and NBUF-1
-    const uint16_t* qg = q + ((size_t)row * d.H + hbase) * DK;
-#pragma unroll
-    for (int u = 0; u < HW / NW; ++u) {
-      const int h = wv + NW * u;
-      const uint32_t dst = lds_addr(qs + h * KPD);
-      g2lds16(qg + (size_t)h * DK + (lane ^ sw(h)) * 8, dst);
-      if (DK > 512 && lane < DK / 8 - 64) g2lds16(qg + (size_t)h * DK + 512 + lane * 8, dst + 1024);
-    }
-  };
-  // q fragments from LDS, once every wave's rows have landed (the caller has
-  // waited for its own q loads)
-  auto read_q = [&]() {
-    __syncthreads();
-    const uint16_t* qs = kv[NBUF - 2];
-    const int hr = hg * 16 + c;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int ch = 4 * s + g;
-      qf[s] = *(const bf16x8*)(qs + hr * KPD + (ch < 64 ? ch ^ sw(c) : ch) * 8);
-    }
-    __syncthreads();  // slots NBUF-2 and NBUF-1 are free again
-  };
   if constexpr (NHG >= 4) {
-    // many heads per row: stage q through LDS before anything else
-    issue_q();
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0: q (and the ids) are in
     read_q();
-  } else {
-    const uint16_t* qrow = q + ((size_t)row * d.H + hbase + hg * 16 + c) * DK + g * 8;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) qf[s] = *(const bf16x8*)(qrow + s * 32);
   }
-  // softmax: lane (hq, rq) = (lane >> 3, lane & 7) holds rows 4rq..4rq+3 of head 8*wv + hq
-  const int hq = lane >> 3, rq = lane & 7;
-  const int hs = 8 * wv + hq;
-  float m = -INFINITY, l = 0.f;
-  const float scale = d.attn_scale_log2;
-  // values: O^T tiles (16 value columns x 16 heads) of every head tile
-  f32x4 acc[NDT][NHG];
-#pragma unroll
-  for (int n = 0; n < NDT; ++n)
-#pragma unroll
-    for (int ht = 0; ht < NHG; ++ht) acc[n][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // transposing V reads: lane (g, c) takes rows 4g + c/4 (+16) and columns
-  // 4*(c%4) .. +3 of a 16-column value tile
-  const int vrow = 4 * g + (c >> 2);
-  const int vsw = sw(vrow);  // rows vrow and vrow + 16 share the swizzle
-  auto vaddr = [&](int dt, int hi) {
-    const int ch = 2 * dt + ((c & 3) >> 1);
-    return (vrow + 16 * hi) * KPD + (ch < 64 ? ch ^ vsw : ch) * 8 + 4 * (c & 1);
-  };
 
   for (int cb = any_row ? begin : end; cb < end; cb += CH) {
     const int ce = min(end, cb + CH);
@@ -224,6 +256,7 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
     __syncthreads();  // the previous chunk is done with every slot, code and mask
 #pragma unroll
     for (int u = 0; u < IPT; ++u) {
+      if (cb + u * NT >= ce) break;  // whole tiles past the chunk's end: never read
       const int ea = cb + ident_row(u);
       const int id = cb == begin ? id_a[u] : (ea < end && ea < d.kI ? Irow[ea] : -1);
       int code;
@@ -242,24 +275,28 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
     // value crosses from the vector to the scalar unit.
     const uint16_t* pooled_b = pooled_kv + (size_t)b * d.Np_cap * DK;
     const uint16_t* local_b = local_kv + (size_t)b * d.Wl_cap * DK;
-    auto load_tile = [&](int t, uint16_t* kvdst) {
+    // The code reads use a lane-varying (always zero) offset, so the codes
+    // stay in vector registers instead of being moved to scalar ones row by
+    // row; LDS destinations are plain 32-bit offsets from the ring's base.
+    const int vz = vector_zero();
+    auto load_tile = [&](int t, int slot) {
       int4 code4[RPW / 4];
 #pragma unroll
-      for (int q4 = 0; q4 < RPW / 4; ++q4) code4[q4] = *(const int4*)&s_code[t * kTile + RPW * wvs + 4 * q4];
+      for (int q4 = 0; q4 < RPW / 4; ++q4) code4[q4] = *(const int4*)&s_code[t * kTile + RPW * wvs + 4 * q4 + vz];
 #pragma unroll
       for (int r = 0; r < RPW; ++r) {
         const int4 c4 = code4[r >> 2];
         const int cd = (r & 3) == 0 ? c4.x : (r & 3) == 1 ? c4.y : (r & 3) == 2 ? c4.z : c4.w;
-        const uint16_t* src = cd >= 0 ? pooled_b + (size_t)cd * DK : local_b + (size_t)(-1 - cd) * DK;
+        const bool pooled = cd >= 0;
+        const uint16_t* src = (pooled ? pooled_b : local_b) + (size_t)(uint32_t)(pooled ? cd : -1 - cd) * DK;
         const int trow = RPW * wvs + r;
-        const uint32_t dst = lds_addr(kvdst + trow * KPD);
-        g2lds16(src + (lane ^ sw(trow)) * 8, dst);
+        const uint32_t dst = kv_lds + (uint32_t)((slot * kTile + trow) * KPD * 2);
+        g2lds16(src + src_el[r], dst);
         if (DK > 512 && lane < DK / 8 - 64) g2lds16(src + 512 + lane * 8, dst + 1024);
       }
     };
     auto load_k = [&](const uint16_t* kvb, int s) {  // k-step s of rows 16*dh + c
-      const int ch = 4 * s + g;
-      return *(const bf16x8*)(kvb + (dh * 16 + c) * KPD + (ch < 64 ? ch ^ sw(c) : ch) * 8);
+      return *(const bf16x8*)(kvb + k_el[s]);
     };
     // S^T of rows 16*dh.. for heads 16*hg.. into score buffer sb; the first
     // KW fragments arrive in ka, the rest are fetched KW steps ahead
@@ -282,11 +319,10 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
     auto step = [&](int t) {
       const uint16_t* kvP = kv[t % NBUF];
       const uint16_t* kvS = kv[(t + 1) % NBUF];
-      uint16_t* kvL = kv[(t + NBUF - 1) % NBUF];
       // tile t+1 must have landed; tiles t+2 .. t+NBUF-2 may still stream in
       wait_loads(min(ntile - 1, t + NBUF - 2) - (t + 1));
-      lds_sync();  // every wave's tile t+1, scores of tile t, and slot kvL are ready
-      if (t + NBUF - 1 < ntile) load_tile(t + NBUF - 1, kvL);
+      lds_sync();  // every wave's tile t+1, scores of tile t, and the slot of tile t+NBUF-1 are ready
+      if (t + NBUF - 1 < ntile) load_tile(t + NBUF - 1, (t + NBUF - 1) % NBUF);
       const uint32_t tmask = __builtin_amdgcn_readfirstlane(s_tmask[t]);
       const bool more = t + 1 < ntile;
       const f32x4 sv = *(const f32x4*)&s_sc[t & 1][hs * SSP + 4 * rq];
@@ -352,8 +388,8 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
       for (int n = 0; n < NDT; ++n) {
         const int dt = wv + NW * n;
         if (NDT * NW == NDT_ALL || dt < NDT_ALL) {
-          va[n][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(kvP + vaddr(dt, 0)));
-          va[n][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(kvP + vaddr(dt, 1)));
+          va[n][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(kvP + v_el[n][0]));
+          va[n][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(kvP + v_el[n][1]));
         }
       }
       if (__ballot(any)) {
@@ -381,7 +417,7 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
     // prologue: tiles 0 .. NBUF-2 in flight, scores of tile 0
 #pragma unroll
     for (int t = 0; t < NBUF - 1; ++t)
-      if (t < ntile) load_tile(t, kv[t]);
+      if (t < ntile) load_tile(t, t);
     wait_loads(min(ntile, NBUF - 1) - 1);
     lds_sync();
     {
@@ -459,10 +495,17 @@ template <typename T>
 __global__ __launch_bounds__(128) void k_attn_merge(KDims d, int splits, const float* __restrict__ part,
                                                     const float* __restrict__ sinks, T* __restrict__ out) {
   __shared__ float s_w[kMaxSplits];
+  args_now(d, splits, part, sinks, out);
   const int row = blockIdx.x, h = blockIdx.y;
   const int e = blockIdx.z * 128 + threadIdx.x;
   const size_t stride = (size_t)d.B * d.L * d.H * (d.Dv + 2);
   const float* p0 = part + ((size_t)row * d.H + h) * (d.Dv + 2);
+  // the column's partials are requested together with (m, l)
+  constexpr int kPre = 16;
+  const int ec = min(e, d.Dv - 1);
+  float pre[kPre];
+#pragma unroll
+  for (int s = 0; s < kPre; ++s) pre[s] = s < splits ? p0[s * stride + ec] : 0.f;
   if (threadIdx.x < 64) {
     const int s = threadIdx.x;
     const float m = s < splits ? p0[s * stride + d.Dv] : -INFINITY;
@@ -479,8 +522,10 @@ __global__ __launch_bounds__(128) void k_attn_merge(KDims d, int splits, const f
   __syncthreads();
   if (e >= d.Dv) return;
   float o = 0.f;
-#pragma unroll 8
-  for (int s = 0; s < splits; ++s) o += p0[s * stride + e] * s_w[s];
+#pragma unroll
+  for (int s = 0; s < kPre; ++s)
+    if (s < splits) o += pre[s] * s_w[s];
+  for (int s = kPre; s < splits; ++s) o += p0[s * stride + e] * s_w[s];
   stf(out + ((size_t)row * d.H + h) * d.Dv + e, o);
 }
 

@@ -44,6 +44,13 @@ __device__ __forceinline__ void lds_sync() {
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p);
 }
+// 0 in every lane, opaque to the compiler: added to an LDS address that is
+// the same in every lane, it keeps the loaded value in vector registers.
+__device__ __forceinline__ int vector_zero() {
+  int z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return z;
+}
 __device__ __forceinline__ void g2lds16(const void* gsrc, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
@@ -183,6 +190,26 @@ struct SeqInfo {
 // one 32-bit unsigned division
 __device__ __forceinline__ uint32_t div_ratio(const KDims& d, uint32_t x) {
   return d.ratio_shift >= 0 ? x >> d.ratio_shift : x / (uint32_t)d.ratio;
+}
+
+// Every kernel argument into scalar registers at once, at the top of a
+// latency-bound kernel: a kernel-argument load that misses the scalar cache
+// takes ~0.6 us, and left alone the compiler issues each where it is first
+// used, behind its own wait, so several of them line up one after another.
+__device__ __forceinline__ void args_now(const KDims& d) {
+  asm volatile("" ::"s"(d.B), "s"(d.L), "s"(d.ratio), "s"(d.window), "s"(d.topk), "s"(d.index_block),
+               "s"(d.index_keep), "s"(d.H_i), "s"(d.D_i), "s"(d.H), "s"(d.Dk), "s"(d.Dv), "s"(d.Np_cap),
+               "s"(d.Wl_cap), "s"(d.kI), "s"(d.force_flat), "s"(d.force_path), "s"(d.nb_cap), "s"(d.ratio_shift),
+               "s"(d.w_scale), "s"(d.attn_scale_log2));
+}
+template <class T>
+__device__ __forceinline__ void arg_now(T v) {
+  asm volatile("" ::"s"(v));
+}
+template <class... T>
+__device__ __forceinline__ void args_now(const KDims& d, T... v) {
+  args_now(d);
+  (arg_now(v), ...);
 }
 
 __device__ __forceinline__ SeqInfo seq_info(const KDims& d, int t0) {

@@ -509,6 +509,7 @@ __global__ __launch_bounds__(256) void k_decode_scan_mfma(
   __shared__ __align__(16) float s_part[2][4][64];
   __shared__ DecodeSelSmem s_sel;
   __shared__ int s_flag;
+  args_now(d, q_idx, w, keys, t0, fscore, cscore, cnt, I, top_blk, path);
   const int b = blockIdx.y, slab = blockIdx.x;
   const int lane = lane_id(), g = lane >> 4;
   const int t0b = t0[b];  // requested first, needed after the rows arrive
@@ -577,6 +578,7 @@ __global__ __launch_bounds__(256) void k_decode_scan_stream(
   __shared__ DecodeSelSmem s_sel;
   __shared__ int s_flag;
   __shared__ int s_done[kStreamMaxB];  // sequences this workgroup completed
+  args_now(d, q_idx, w, keys, t0, fscore, cscore, cnt, I, top_blk, path);
   const int tid = threadIdx.x, lane = lane_id(), wv = wave_id(), g = lane >> 4;
   // slab counts and their prefix: thread t sums sequences 4t .. 4t+3
   {

@@ -193,7 +193,7 @@ def main():
     out = torch.empty((w.B, w.L, w.H, w.Dv), dtype=dt, device=dev)
     op = {"decode": hisa.OP_SELECT_DECODE, "prefill": hisa.OP_SELECT_PREFILL, "flat": hisa.OP_FLAT_TOPK}[kind]
     ws_sel = torch.zeros(max(hisa.workspace_bytes(op, sel_d), 256), dtype=torch.uint8, device=dev)
-    ws_att = torch.empty(max(hisa.workspace_bytes(hisa.OP_ATTENTION, att_d), 256), dtype=torch.uint8, device=dev)
+    ws_att = torch.zeros(max(hisa.workspace_bytes(hisa.OP_ATTENTION, att_d), 256), dtype=torch.uint8, device=dev)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())  # noqa: E731
     sel_ref, att_ref = ctypes.byref(sel_d), ctypes.byref(att_d)

@@ -365,6 +365,35 @@ def test_decode_exact_ties(hisa, case):
             assert tb(bn[b, 0]) == tb(blko), b
 
 
+def test_attention_split_merge_paths(hisa):
+    # Few query rows split their 640-row lists over several workgroups whose
+    # partial results a second kernel merges: three calls on one workspace
+    # give bit-identical outputs that match the oracle; 6 sequences (16-head
+    # workgroups, 10 splits) and 40 sequences (64-head workgroups, 7 splits)
+    # match it on sampled rows.
+    w = synth.FLASH_DECODE
+    x, g = inputs(w, synth.SEEDS[w.name])
+    I, _, _ = hisa.hisa_select_decode(g["q_idx"], g["w"], g["keys"], g["t0"], **sel_kw(w))
+    d = hisa.attention_dims(g["q"], g["local_kv"], g["pooled_kv"], I, ratio=w.ratio, window=w.window)
+    ws = torch.zeros(hisa.workspace_bytes(hisa.OP_ATTENTION, d), dtype=torch.uint8, device="cuda")
+    outs = []
+    for rep in range(3):
+        say(f"[run] split attention on one workspace, call {rep}")
+        outs.append(hisa.sparse_local_pooled_attention(g["q"], g["local_kv"], g["pooled_kv"], I, g["sinks"], g["t0"],
+                                                       ratio=w.ratio, window=w.window, ws=ws))
+        torch.cuda.synchronize()
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
+    check_attention(w, x, I, outs[0])
+    for wl, seed in ((MIXED, 5), (MIXED.with_(name="mixed_b40", B=40, t0=[1200 + 337 * b for b in range(40)],
+                                              Np_cap=5000), 8)):
+        x, g = inputs(wl, seed)
+        say(f"[run] attention split merge, {wl.name}")
+        I, _, _ = hisa.hisa_select_decode(g["q_idx"], g["w"], g["keys"], g["t0"], **sel_kw(wl))
+        out = run_attention(hisa, wl, g, I)
+        torch.cuda.synchronize()
+        check_attention(wl, x, I, out, sample=12)
+
+
 def test_invalid_sequence_outputs(hisa):
     x, g = inputs(MIXED, 5)
     w = MIXED

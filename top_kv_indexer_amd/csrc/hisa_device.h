@@ -179,6 +179,16 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
   return __popcll(mask & ((1ull << lane) - 1ull));
 }
 
+// Device-scope (all XCDs) store and load of a float: written through to, and
+// read from, the device's coherence point, so handing values to workgroups
+// on other XCDs needs no L2 write-back.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Per-sequence facts (HiSA issue: pooled count, gate).  ok == false marks a
 // sequence whose t0 breaks the buffer bounds.
 struct SeqInfo {

@@ -126,15 +126,6 @@ __device__ __forceinline__ void write_unscored(const KDims& d, const SeqInfo& si
   if (path && lane == 0) path[b] = si.path;
 }
 
-// Device-scope (all XCDs) store and load of a score: written through to, and
-// read from, the device's coherence point, so publishing them needs no L2
-// write-back.
-__device__ __forceinline__ void st_dev(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_dev(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // ---- workgroup top-k (256 threads): thread t holds element 256 r + t in
 // key[r], r < NR (order index = element index, ascending in id); key 0 marks

@@ -112,7 +112,8 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
   __shared__ uint32_t s_tmask[NTILE];
   __shared__ __align__(16) int s_code[CH];  // row code of each entry of the current chunk
 
-  args_now(d, splits, q, local_kv, pooled_kv, I, sinks, t0, out, part);
+  // few, latency-bound workgroups: every argument in scalar registers at once
+  if constexpr (NHG == 1) args_now(d, splits, q, local_kv, pooled_kv, I, sinks, t0, out, part);
   const int split = blockIdx.x;
   // consecutive query rows go to the same XCD (workgroups are dealt to the 8
   // XCDs round-robin), so rows sharing their local window share its L2
@@ -170,8 +171,7 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
     const int ea = begin + ident_row(u);
     id_a[u] = (ea < end && ea < d.kI) ? Irow[ea] : -1;
   }
-  // a scalar load (b is uniform), so waiting for it does not wait for the
-  // vector loads around it
+  // issued before q, so waiting for it does not wait for q
   const int T0 = t0[__builtin_amdgcn_readfirstlane(b)];
   // q is requested right after the ids and t0, so its latency overlaps
   // theirs and the row bookkeeping waits only for them
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
   // lane alone.  With 16 heads (few, latency-bound workgroups) they are
   // pinned here, while the loads above are in flight, instead of being
   // computed where the compiler hoists them (after the waits); with 64 heads
-  // the compiler keeps folding them into the LDS instructions' offsets.
+  // they are formed at each use, as the compiler prefers.
   int k_el[NS], v_el[NDT][2], src_el[RPW];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
@@ -270,15 +270,15 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
     }
     __syncthreads();  // every row code of the chunk is in
     // Tile t, wave w: tile rows RPW*w .. RPW*w + RPW-1.  Their codes come
-    // from LDS in one broadcast read per four rows and the addresses are
-    // formed in vector registers; the LDS destination is scalar, so no
-    // value crosses from the vector to the scalar unit.
+    // from LDS in one broadcast read per four rows.
     const uint16_t* pooled_b = pooled_kv + (size_t)b * d.Np_cap * DK;
     const uint16_t* local_b = local_kv + (size_t)b * d.Wl_cap * DK;
-    // The code reads use a lane-varying (always zero) offset, so the codes
-    // stay in vector registers instead of being moved to scalar ones row by
-    // row; LDS destinations are plain 32-bit offsets from the ring's base.
-    const int vz = vector_zero();
+    // With 16 heads (16 rows per wave per tile) the code reads use a
+    // lane-varying (always zero) offset, so the codes stay in vector
+    // registers instead of being moved to scalar ones row by row; with 64
+    // heads (4 rows) the scalar unit, idle there, forms the addresses.  LDS
+    // destinations are plain 32-bit offsets from the ring's base.
+    const int vz = NHG == 1 ? vector_zero() : 0;
     auto load_tile = [&](int t, int slot) {
       int4 code4[RPW / 4];
 #pragma unroll
@@ -291,12 +291,14 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
         const uint16_t* src = (pooled ? pooled_b : local_b) + (size_t)(uint32_t)(pooled ? cd : -1 - cd) * DK;
         const int trow = RPW * wvs + r;
         const uint32_t dst = kv_lds + (uint32_t)((slot * kTile + trow) * KPD * 2);
-        g2lds16(src + src_el[r], dst);
+        g2lds16(src + (NHG == 1 ? src_el[r] : (lane ^ sw(trow)) * 8), dst);
         if (DK > 512 && lane < DK / 8 - 64) g2lds16(src + 512 + lane * 8, dst + 1024);
       }
     };
     auto load_k = [&](const uint16_t* kvb, int s) {  // k-step s of rows 16*dh + c
-      return *(const bf16x8*)(kvb + k_el[s]);
+      if constexpr (NHG == 1) return *(const bf16x8*)(kvb + k_el[s]);
+      const int ch = 4 * s + g;
+      return *(const bf16x8*)(kvb + (dh * 16 + c) * KPD + (ch < 64 ? ch ^ sw(c) : ch) * 8);
     };
     // S^T of rows 16*dh.. for heads 16*hg.. into score buffer sb; the first
     // KW fragments arrive in ka, the rest are fetched KW steps ahead
@@ -388,8 +390,8 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
       for (int n = 0; n < NDT; ++n) {
         const int dt = wv + NW * n;
         if (NDT * NW == NDT_ALL || dt < NDT_ALL) {
-          va[n][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(kvP + v_el[n][0]));
-          va[n][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(kvP + v_el[n][1]));
+          va[n][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(kvP + (NHG == 1 ? v_el[n][0] : vaddr(dt, 0))));
+          va[n][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(kvP + (NHG == 1 ? v_el[n][1] : vaddr(dt, 1))));
         }
       }
       if (__ballot(any)) {

@@ -303,13 +303,21 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
     // S^T of rows 16*dh.. for heads 16*hg.. into score buffer sb; the first
     // KW fragments arrive in ka, the rest are fetched KW steps ahead
     auto scores = [&](const uint16_t* kvb, bf16x8 (&ka)[KW], int sb) {
-      f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
+      // 16 heads (one wave per SIMD, latency-bound): four independent MFMA
+      // chains; 64 heads: one (the other waves hide its latency)
+      constexpr int NACC = NHG == 1 ? 4 : 1;
+      f32x4 sa[NACC];
+#pragma unroll
+      for (int u = 0; u < NACC; ++u) sa[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const bf16x8 a = ka[s % KW];
         if (s + KW < NS) ka[s % KW] = load_k(kvb, s + KW);
-        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[s], st, 0, 0, 0);
+        sa[s % NACC] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[s], sa[s % NACC], 0, 0, 0);
       }
+      f32x4 st = sa[0];
+#pragma unroll
+      for (int u = 1; u < NACC; ++u) st += sa[u];
       *(f32x4*)&s_sc[sb][(hg * 16 + c) * SSP + dh * 16 + 4 * g] = st;
     };
     // wait until at most `keep` tiles' loads of this wave are still in flight

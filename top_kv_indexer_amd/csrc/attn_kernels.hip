@@ -495,6 +495,290 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
   }
 }
 
+// Many query rows (prefill; no split): one workgroup per (query row, 64
+// heads), four waves, and wave w owns heads 16w .. 16w+15 from end to end,
+// in the manner of flash attention with the heads in the place of query
+// rows.  Per 32-row tile: S = K q^T for its heads as two 16-row MFMA blocks
+// (lane (g, c) holds rows 4g+i and 16+4g+i of head c), the online softmax in
+// registers (row max and sum over the four lanes of a head by lane swaps),
+// and O^T += V^T P^T where P^T is the lane's own eight probabilities: the
+// value MFMA's k order (entry 8g+e <-> tile row 16*(e/4) + 4g + e%4) is the
+// score layout, so nothing moves between lanes or waves.  The only barrier
+// per tile makes the tile's rows (fetched by all four waves, global->LDS)
+// visible and frees the ring slot of the tile NBUF-1 ahead.
+template <int DK, int DV>
+__global__ __launch_bounds__(256, 2) void k_attn_fa(KDims d, const uint16_t* __restrict__ q,
+                                                 const uint16_t* __restrict__ local_kv,
+                                                 const uint16_t* __restrict__ pooled_kv, const int* __restrict__ I,
+                                                 const float* __restrict__ sinks, const int* __restrict__ t0,
+                                                 uint16_t* __restrict__ out) {
+  constexpr int NW = 4, NT = 256, HW = 64;
+  constexpr int KPD = (DK * 2 + 255) / 256 * 128;  // LDS row pitch (elements)
+  constexpr int NBUF = 2;                          // ring slots (two workgroups per CU)
+  constexpr int NS = DK / 32;                      // MFMA k-steps of S
+  constexpr int NDT = DV / 16;                     // 16-column value tiles (all of them, every wave)
+  constexpr int RPW = kTile / NW;                  // rows of a tile each wave fetches
+  constexpr int CH = 1024;                         // rows of the row list resolved at a time
+  constexpr int NTILE = CH / kTile;
+  constexpr int IPT = CH / NT;
+  constexpr int LPT = RPW * (DK > 512 ? 2 : 1);    // vector-memory loads per tile per wave
+  constexpr int KW = 4;                            // K fragments in flight (both row blocks)
+  constexpr int NACC = 2;                          // accumulation chains per row block
+  constexpr int PVG = 8;                           // value tiles whose reads are in flight together
+  constexpr int OP = DV + 8;                       // pitch of the staged output rows (elements)
+  static_assert(HW / 2 * OP <= NBUF * kTile * KPD, "half the heads' staging fits the ring");
+  static_assert(RPW % 4 == 0 && CH % NT == 0, "shape of the row fetch");
+  static_assert(DV % 16 == 0 && DV <= DK && DK >= 512 && DK <= 1024 && DK % 32 == 0, "shape");
+  __shared__ __align__(16) uint16_t kv[NBUF][kTile * KPD];
+  __shared__ uint32_t s_tmask[NTILE];
+  __shared__ __align__(16) int s_code[CH];
+
+  const int row = [](int y, int n) {  // consecutive query rows on one XCD (shared local window)
+    const int x = y & 7, qn = n >> 3, rn = n & 7;
+    return x * qn + min(x, rn) + (y >> 3);
+  }(blockIdx.y, d.B * d.L);
+  const int b = row / d.L, j = row % d.L;
+  const int tid = threadIdx.x, lane = lane_id(), wv = wave_id(), g = lane >> 4, c = lane & 15;
+  const int wvs = __builtin_amdgcn_readfirstlane(wv);
+  const int hbase = blockIdx.z * HW;
+  auto sw = [](int r) { return ((r & 7) << 1) | ((r >> 3) & 1); };
+  const uint32_t kv_lds = lds_addr(&kv[0][0]);
+  const int n_geo = d.kI + d.window;
+  const int* Irow = I + (size_t)row * d.kI;
+  int id_a[IPT];
+#pragma unroll
+  for (int u = 0; u < IPT; ++u) {
+    const int ea = tid + u * NT;
+    id_a[u] = (ea < n_geo && ea < d.kI) ? Irow[ea] : -1;
+  }
+  const int T0 = t0[__builtin_amdgcn_readfirstlane(b)];
+  // this wave's 16 heads of q (the B operand of S), straight into registers
+  bf16x8 qf[NS];
+  {
+    const uint16_t* qrow = q + ((size_t)row * d.H + hbase + 16 * wv + c) * DK + g * 8;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qf[s] = *(const bf16x8*)(qrow + s * 32);
+  }
+  const RowPlan rp = row_plan(d, T0, j);
+  const int dummy = rp.n_loc > 0 ? -1 - (rp.s_lo - rp.ls) : 0;
+  const bool any_row = rp.n_loc > 0 || rp.V > 0;
+  auto resolve = [&](int e, int id, int& code) -> bool {
+    code = dummy;
+    if (e >= n_geo) return false;
+    if (e < d.kI) {
+      if (id < 0 || id >= rp.V) return false;
+      code = id;
+      return true;
+    }
+    if (e - d.kI >= rp.n_loc) return false;
+    code = -1 - (rp.s_lo - rp.ls + e - d.kI);
+    return true;
+  };
+  // head c of this wave: running max m (log2 domain) and sum l, on all four
+  // lanes that hold it
+  float m = -INFINITY, l = 0.f;
+  const float scale = d.attn_scale_log2;
+  f32x4 acc[NDT];
+#pragma unroll
+  for (int n = 0; n < NDT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int vrow = 4 * g + (c >> 2);
+  const int vsw = sw(vrow);
+  // chunk 2dt + (c%4)/2 of row vrow (+16): as for K, the swizzle stays in
+  // the low four bits, so tiles dt and dt+8 differ by 256 bytes
+  auto vaddr = [&](int dt, int hi) {
+    const int ch = 2 * dt + ((c & 3) >> 1);
+    if (ch >= 64) return (vrow + 16 * hi) * KPD + ch * 8 + 4 * (c & 1);
+    return (vrow + 16 * hi) * KPD + (((2 * (dt & 7) + ((c & 3) >> 1)) ^ vsw) * 8) + (dt >> 3) * 128 + 4 * (c & 1);
+  };
+  const uint16_t* pooled_b = pooled_kv + (size_t)b * d.Np_cap * DK;
+  const uint16_t* local_b = local_kv + (size_t)b * d.Wl_cap * DK;
+
+  for (int cb = any_row ? 0 : n_geo; cb < n_geo; cb += CH) {
+    const int ce = min(n_geo, cb + CH);
+    const int ntile = (ce - cb + kTile - 1) / kTile;
+    __syncthreads();  // the previous chunk is done with every slot, code and mask
+#pragma unroll
+    for (int u = 0; u < IPT; ++u) {
+      if (cb + u * NT >= ce) break;
+      const int ea = cb + tid + u * NT;
+      const int id = cb == 0 ? id_a[u] : (ea < n_geo && ea < d.kI ? Irow[ea] : -1);
+      int code;
+      const uint64_t live = __ballot(resolve(ea, id, code));
+      s_code[tid + u * NT] = code;
+      if (lane == 0) {
+        const int t = (wv * 64 + u * NT) / kTile;
+        s_tmask[t] = (uint32_t)live;
+        s_tmask[t + 1] = (uint32_t)(live >> 32);
+      }
+    }
+    __syncthreads();  // every row code of the chunk is in
+    auto load_tile = [&](int t, int slot) {
+      int4 code4[RPW / 4];
+#pragma unroll
+      for (int q4 = 0; q4 < RPW / 4; ++q4) code4[q4] = *(const int4*)&s_code[t * kTile + RPW * wvs + 4 * q4];
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        const int4 c4 = code4[r >> 2];
+        const int cd = (r & 3) == 0 ? c4.x : (r & 3) == 1 ? c4.y : (r & 3) == 2 ? c4.z : c4.w;
+        const bool pooled = cd >= 0;
+        const uint16_t* src = (pooled ? pooled_b : local_b) + (size_t)(uint32_t)(pooled ? cd : -1 - cd) * DK;
+        const int trow = RPW * wvs + r;
+        const uint32_t dst = kv_lds + (uint32_t)((slot * kTile + trow) * KPD * 2);
+        g2lds16(src + (lane ^ sw(trow)) * 8, dst);
+        if (DK > 512 && lane < DK / 8 - 64) g2lds16(src + 512 + lane * 8, dst + 1024);
+      }
+    };
+    auto wait_loads = [&](int keep) {  // at most `keep` later tiles' loads still in flight
+      if (keep >= 2) __builtin_amdgcn_s_waitcnt((2 * LPT & 15) | ((2 * LPT >> 4) << 14) | 0x0F70);
+      else if (keep == 1) __builtin_amdgcn_s_waitcnt((LPT & 15) | ((LPT >> 4) << 14) | 0x0F70);
+      else __builtin_amdgcn_s_waitcnt(0x0F70);
+    };
+#pragma unroll
+    for (int t = 0; t < NBUF - 1; ++t)
+      if (t < ntile) load_tile(t, t);
+    for (int t = 0; t < ntile; ++t) {
+      const uint16_t* kvb = kv[t % NBUF];
+      wait_loads(min(ntile - 1, t + NBUF - 2) - t);
+      lds_sync();  // every wave's rows of tile t are in; every wave is done with tile t-1
+      if (t + NBUF - 1 < ntile) load_tile(t + NBUF - 1, (t + NBUF - 1) % NBUF);
+      const uint32_t tmask = __builtin_amdgcn_readfirstlane(s_tmask[t]);
+      // Lane offsets are formed here each tile from an opaque zero: hoisted
+      // out of the loop they would be spilled (the accumulators and q take
+      // 192 of the 256 registers) and reloaded behind full waits.
+      int zl = 0;
+      asm volatile("" : "+v"(zl));
+      const int cz = c + zl;
+      // scores: rows 16*rb + c of the tile (A) against this wave's heads (B)
+      f32x4 sc[2];
+      {
+        f32x4 sa[2][NACC];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int u = 0; u < NACC; ++u) sa[rb][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // chunk 4s+g of row 16rb+c: the swizzle touches only the low four
+        // bits of the chunk index, so chunk (4s+g) ^ sw = 16*(s/4) + ((4*(s%4)+g) ^ sw)
+        auto load_k = [&](int rb, int s) {
+          const int ch = 4 * s + g;
+          if (ch >= 64) return *(const bf16x8*)(kvb + (rb * 16 + cz) * KPD + ch * 8);
+          return *(const bf16x8*)(kvb + (rb * 16 + cz) * KPD + (((4 * (s & 3) + g) ^ sw(cz)) * 8) + (s >> 2) * 128);
+        };
+        bf16x8 ka[2][KW / 2];
+#pragma unroll
+        for (int s = 0; s < KW / 2; ++s) {
+          ka[0][s] = load_k(0, s);
+          ka[1][s] = load_k(1, s);
+        }
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const bf16x8 a0 = ka[0][s % (KW / 2)], a1 = ka[1][s % (KW / 2)];
+          if (s + KW / 2 < NS) {
+            ka[0][s % (KW / 2)] = load_k(0, s + KW / 2);
+            ka[1][s % (KW / 2)] = load_k(1, s + KW / 2);
+          }
+          sa[0][s % NACC] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[s], sa[0][s % NACC], 0, 0, 0);
+          sa[1][s % NACC] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[s], sa[1][s % NACC], 0, 0, 0);
+        }
+        sc[0] = sa[0][0];
+        sc[1] = sa[1][0];
+#pragma unroll
+        for (int u = 1; u < NACC; ++u) {
+          sc[0] += sa[0][u];
+          sc[1] += sa[1][u];
+        }
+      }
+      // online softmax of head c over the tile's 32 rows
+      float x[8];
+      float tmax = -INFINITY;
+      const uint32_t tb = tmask >> (4 * (g + zl));  // rows 4g+i and 16+4g+i at bits i and 16+i
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[4 * rb + i] = ((tb >> (16 * rb + i)) & 1u) ? sc[rb][i] * scale : -INFINITY;
+          tmax = fmaxf(tmax, x[4 * rb + i]);
+        }
+      tmax = max_rows(tmax);
+      // lazy rescale: the reference max moves only when exceeded by 2^8
+      float alpha = 1.f;
+      if (m == -INFINITY) {
+        m = tmax;
+      } else if (tmax > m + 8.f) {
+        const float m_new = fmaxf(m, tmax);
+        alpha = __builtin_amdgcn_exp2f(m - m_new);
+        l *= alpha;
+        m = m_new;
+      }
+      const float m_sub = m == -INFINITY ? 0.f : m;
+      float p[8];
+      float psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = __builtin_amdgcn_exp2f(x[e] - m_sub);
+        psum += p[e];
+      }
+      l += sum_rows(psum);
+      if (__ballot(alpha != 1.f)) {
+#pragma unroll
+        for (int n = 0; n < NDT; ++n)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[n][i] *= alpha;
+      }
+      // P^T operand: entry e of lane (g, c) is tile row 16*(e/4) + 4g + e%4
+      u32x4 pu;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) pu[k] = pack_bf16x2(p[2 * k], p[2 * k + 1]);
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, pu);
+      // O^T += V^T P^T over every 16-column value tile, PVG tiles' reads in
+      // flight at a time (registers)
+#pragma unroll
+      for (int n0 = 0; n0 < NDT; n0 += PVG) {
+#pragma unroll
+        for (int n = n0; n < n0 + PVG && n < NDT; ++n) {
+          const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(kvb + zl + vaddr(n, 0)));
+          const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(kvb + zl + vaddr(n, 1)));
+          const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb, acc[n], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+  // normalise (sink included) and stage the rows in the idle ring for
+  // whole-line stores
+  const int h = hbase + 16 * wv + c;
+  const float sink2 = sinks ? sinks[h] * kLog2e : -INFINITY;
+  const float mf = fmaxf(m, sink2);
+  float f = 0.f;
+  if (mf != -INFINITY) {
+    const float lf = l * exp2f(m - mf) + (sinks ? exp2f(sink2 - mf) : 0.f);
+    f = lf > 0.f ? exp2f(m - mf) / lf : 0.f;
+  }
+  // two halves of 32 heads: waves 2h and 2h+1 stage, then all copy out
+  uint16_t* og = out + ((size_t)row * d.H + hbase) * DV;
+  constexpr int CPR = DV / 8;  // 16-byte pieces per head row
+#pragma unroll 1
+  for (int half = 0; half < 2; ++half) {
+    __syncthreads();  // every wave is done with the ring (or the previous half)
+    if ((wv >> 1) == half) {
+      uint16_t* orow = &kv[0][0] + (16 * (wv & 1) + c) * OP + 4 * g;
+#pragma unroll
+      for (int n = 0; n < NDT; ++n) {
+        uint2 v;
+        v.x = pack_bf16x2(acc[n][0] * f, acc[n][1] * f);
+        v.y = pack_bf16x2(acc[n][2] * f, acc[n][3] * f);
+        *(uint2*)(orow + n * 16) = v;
+      }
+    }
+    __syncthreads();
+    uint16_t* oh = og + (size_t)half * 32 * DV;
+    for (int k = tid; k < 32 * CPR; k += NT) {
+      const int hr = k / CPR, cc = k - hr * CPR;
+      *(u32x4*)(oh + (size_t)k * 8) = *(const u32x4*)(&kv[0][0] + hr * OP + cc * 8);
+    }
+  }
+}
+
 // Merge of split partials (m and l in the log2 domain), sink included.  One
 // workgroup per (query row, head, 128 output columns); the first wave turns
 // the splits' (m, l) into normalised weights, then every thread sums its
@@ -624,7 +908,19 @@ hipError_t launch_mfma(const KDims& d, const void* q, const void* local_kv, cons
     const dim3 grid(splits, d.B * d.L, d.H / 16);
     hipLaunchKernelGGL((k_attn_mfma<DK, DV, 1>), grid, dim3(128), 0, st, d, splits, (const uint16_t*)q,
                        (const uint16_t*)local_kv, (const uint16_t*)pooled_kv, I, sinks, t0, (uint16_t*)out, partial);
-  } else {
+    return hipGetLastError();
+  }
+  if constexpr (DK == 512) {
+    // many rows, 512 wide: the flash-style kernel, two workgroups per CU
+    // (at 576 wide it holds one and the kernel below is faster)
+    if (splits == 1) {
+      const dim3 grid(1, d.B * d.L, d.H / 64);
+      hipLaunchKernelGGL((k_attn_fa<DK, DV>), grid, dim3(256), 0, st, d, (const uint16_t*)q,
+                         (const uint16_t*)local_kv, (const uint16_t*)pooled_kv, I, sinks, t0, (uint16_t*)out);
+      return hipGetLastError();
+    }
+  }
+  {
     const dim3 grid(splits, d.B * d.L, d.H / 64);
     hipLaunchKernelGGL((k_attn_mfma<DK, DV, 4>), grid, dim3(512), 0, st, d, splits, (const uint16_t*)q,
                        (const uint16_t*)local_kv, (const uint16_t*)pooled_kv, I, sinks, t0, (uint16_t*)out, partial);

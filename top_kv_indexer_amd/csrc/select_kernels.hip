@@ -1485,47 +1485,42 @@ __global__ __launch_bounds__(kTopkRowsThreads) void k_topk_rows(KDims d, int lds
 constexpr int kTkNT = 1024, kTkR = 32, kTkBins = 2048, kTkCand = 1024;
 
 struct TopkRegSmem {
+  float row[kTkNT * kTkR];  // the row, staged: thread t's 32 scores, 16-byte pieces XOR-swizzled
   uint32_t hist[kTkBins];
   float cand_s[kTkCand];
   int cand_i[kTkCand];
-  int wcnt[2][16];
+  uint32_t wsum[16];
   float red[3][16];
   int info[8];
 };
 
-// index of the r-th (1-based) element, in index order, with pred true;
-// every thread of the block calls it and gets the answer
-template <class PredF>
-__device__ __forceinline__ int block_rth_index(int r, PredF pred, TopkRegSmem& sm) {
-  const int lane = lane_id(), wv = wave_id();
-  int cnt = 0;
+// Sum over the block of one int per thread (every thread gets it).
+__device__ __forceinline__ int block_sum_i(int v, TopkRegSmem& sm) {
+  v = wave_sum_i(v);
+  if (lane_id() == 0) sm.wsum[wave_id()] = (uint32_t)v;
+  __syncthreads();
+  int all = 0;
 #pragma unroll
-  for (int q = 0; q < kTkR; ++q) cnt += (int)__popcll(__ballot(pred(q)));
-  if (lane == 0) sm.wcnt[0][wv] = cnt;
+  for (int u = 0; u < kTkNT / 64; ++u) all += (int)sm.wsum[u];
   __syncthreads();
-  int before = 0;
-  for (int u = 0; u < wv; ++u) before += sm.wcnt[0][u];
-  if (before < r && before + cnt >= r) {  // this wave holds it
-    int need = r - before;
-#pragma unroll
-    for (int q = 0; q < kTkR; ++q) {
-      const uint64_t mq = __ballot(pred(q));
-      const int c = (int)__popcll(mq);
-      if (need > 0 && need <= c) {
-        // the need-th set bit of mq
-        uint64_t x = mq;
-        for (int s = 1; s < need; ++s) x &= x - 1;
-        if (lane == 0) sm.info[6] = 2048 * wv + 64 * q + __builtin_ctzll(x);
-      }
-      need -= c;
-    }
-  }
-  __syncthreads();
-  const int res = sm.info[6];
-  __syncthreads();
-  return res;
+  return all;
 }
 
+// Rows of 8193..32768 scores, one workgroup per row, thread t holding the 32
+// consecutive scores 32t .. 32t+31 in registers.
+//  1. range [lo, hi] of the real scores (masked ones are -1e30) and their count;
+//  2. fewer than k real scores: all of them plus the lowest-index masked ones;
+//  3. otherwise the k-th score: a histogram of one sample per thread (indices
+//     32t) over 2048 linear bins of [lo, hi] brackets it with a margin of
+//     three standard deviations of the sample rank; one pass counts the
+//     scores above the bracket, and if the k-th lies inside it, the exact
+//     histogram rounds below only touch the scores in the bracket (else they
+//     start from the whole range).  Each round bins the remaining range into
+//     2048 bins and narrows to the k-th score's bin while it holds more than
+//     1024 entries; then that bin's entries are ranked exactly (score desc,
+//     index asc);
+//  4. emission in index order: per-thread counts, a block prefix sum, and
+//     each thread writes its own ids.
 __global__ __launch_bounds__(kTkNT) void k_topk_rows_reg(KDims d, const float* __restrict__ scores,
                                                          const int* __restrict__ t0, int* __restrict__ I,
                                                          int* __restrict__ path) {
@@ -1546,14 +1541,39 @@ __global__ __launch_bounds__(kTkNT) void k_topk_rows_reg(KDims d, const float* _
   }
   if (!act) return;
   const int n = si.Np, k = si.k;
+  const int i0 = kTkR * tid;  // index of v[0]
   const float* srow = scores + ((size_t)b * d.L + j) * d.Np_cap;
-  auto idx_of = [&](int q) { return 2048 * wv + 64 * q + lane; };
   // absent entries (index >= n) take -inf: below every real or masked score
-  const float* pw = srow + 2048 * wv + lane;
-  const int nw = n - 2048 * wv - lane;  // element q is present iff 64q < nw
   float v[kTkR];
+  if ((d.Np_cap & 3) == 0) {
+    // The row goes global -> LDS in coalesced 1 KiB pieces (wave w moves
+    // pieces w, w+16, ...; piece p = threads 8p .. 8p+7).  LDS position l of
+    // a piece holds the 16 bytes at chunk (l % 8) ^ (l / 8) of thread
+    // 8p + l / 8, so each thread's eight 16-byte reads below hit distinct
+    // banks.  Pieces past the row's end are not fetched (their scores are
+    // absent).
+    const uint32_t row_lds = lds_addr(sm.row);
+    const int lr = lane >> 3, lc = (lane & 7) ^ lr;
+    for (int pc = wv; pc < kTkNT / 8; pc += kTkNT / 64)
+      if (pc * 8 * kTkR < n) {
+        const int src = min(pc * 8 * kTkR + lr * kTkR + lc * 4, d.Np_cap - 4);
+        g2lds16(srow + src, row_lds + pc * 1024);
+      }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0
+    __syncthreads();
+    const float* mine = sm.row + (tid >> 3) * 8 * kTkR + (tid & 7) * kTkR;
 #pragma unroll
-  for (int q = 0; q < kTkR; ++q) v[q] = 64 * q < nw ? pw[64 * q] : -INFINITY;
+    for (int u = 0; u < kTkR / 4; ++u) {
+      const float4 x = *(const float4*)(mine + 4 * (u ^ (tid & 7)));
+      v[4 * u] = i0 + 4 * u < n ? x.x : -INFINITY;
+      v[4 * u + 1] = i0 + 4 * u + 1 < n ? x.y : -INFINITY;
+      v[4 * u + 2] = i0 + 4 * u + 2 < n ? x.z : -INFINITY;
+      v[4 * u + 3] = i0 + 4 * u + 3 < n ? x.w : -INFINITY;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < kTkR; ++q) v[q] = i0 + q < n ? srow[i0 + q] : -INFINITY;
+  }
   // 1. range of the real scores, count of masked ones
   float lo = INFINITY, hi = -INFINITY;
   int nmask = 0;
@@ -1585,29 +1605,103 @@ __global__ __launch_bounds__(kTkNT) void k_topk_rows_reg(KDims d, const float* _
     nmask += (int)sm.red[2][u];
   }
   const int nreal = n - nmask;
+  // the selection: scores with key > kthr, and those with key == kthr at
+  // index <= ithr
   uint32_t kthr;
   int ithr;
+  // index of the r-th (1-based) entry, in index order, with pred true
+  auto rth_index = [&](int r, auto pred) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int q = 0; q < kTkR; ++q) m |= pred(q) ? 1u << q : 0u;
+    uint32_t tot;
+    const uint32_t before = block_excl_scan<kTkNT>((uint32_t)__popc(m), sm.wsum, &tot);
+    if ((int)before < r && (int)before + __popc(m) >= r) {
+      uint32_t x = m;
+      for (int s = (int)before + 1; s < r; ++s) x &= x - 1;
+      sm.info[6] = i0 + __builtin_ctz(x);
+    }
+    __syncthreads();
+    const int res = sm.info[6];
+    __syncthreads();
+    return res;
+  };
   if (nreal < k) {
     // every real score, then the lowest-index masked entries
     kthr = score_key(kNeg);
-    ithr = block_rth_index(k - nreal, [&](int q) { return v[q] <= -1e29f && v[q] != -INFINITY; }, sm);
+    ithr = rth_index(k - nreal, [&](int q) { return v[q] <= -1e29f && v[q] != -INFINITY; });
   } else {
-    // 2. bins over [blo, bhi]; narrow to the k-th score's bin while it is crowded
     float blo = lo, bhi = hi;
     int need = k;  // entries still to take inside [blo, bhi]
     bool done = false;
     kthr = 0;
     ithr = 0;
+    auto bins_of = [&](float rlo, float rhi, float& scale) {
+      scale = (float)kTkBins / (rhi - rlo) * 0.999999f;
+    };
+    // the bin holding the r-th entry from the top of hist: (bin, entries above it, entries in it)
+    auto find_bin = [&](int r, int& T, int& above_T, int& in_T) {
+      const uint32_t h0 = sm.hist[kTkBins - 1 - 2 * tid], h1 = sm.hist[kTkBins - 2 - 2 * tid];
+      uint32_t tot;
+      const uint32_t above = block_excl_scan<kTkNT>(h0 + h1, sm.wsum, &tot);
+      if (above < (uint32_t)r && above + h0 + h1 >= (uint32_t)r) {
+        const bool first = above + h0 >= (uint32_t)r;
+        sm.info[0] = first ? kTkBins - 1 - 2 * tid : kTkBins - 2 - 2 * tid;
+        sm.info[1] = (int)(first ? above : above + h0);
+        sm.info[2] = (int)(first ? h0 : h1);
+      }
+      __syncthreads();
+      T = sm.info[0];
+      above_T = sm.info[1];
+      in_T = sm.info[2];
+      __syncthreads();
+    };
+    if (hi > lo) {
+      // 3a. bracket the k-th score with one sample per thread
+      float scale;
+      bins_of(lo, hi, scale);
+      const float x0 = v[0];
+      const bool sreal = x0 > -1e29f;
+      if (sreal) atomicAdd(&sm.hist[min(kTkBins - 1, (int)((x0 - lo) * scale))], 1u);
+      const int ns = block_sum_i(sreal ? 1 : 0, sm);  // also orders the adds before the scan
+      const float target = (float)k * (float)ns / (float)nreal;
+      const float margin = 3.f * sqrtf(fmaxf(target, 1.f)) + 4.f;
+      const int r_hi = max(1, (int)(target - margin)), r_lo = min(ns, (int)ceilf(target + margin));
+      if (ns > 0 && r_hi <= r_lo) {
+        int Tt, at, it, Tb, ab, ib;
+        find_bin(r_hi, Tt, at, it);
+        find_bin(r_lo, Tb, ab, ib);
+        const float clo = Tb == 0 ? lo : fmaxf(lo, lo + (float)Tb / scale);
+        const float chi = Tt == kTkBins - 1 ? hi : fminf(hi, lo + (float)(Tt + 1) / scale);
+        int n_above = 0, n_in = 0;
+#pragma unroll
+        for (int q = 0; q < kTkR; ++q) {
+          n_above += v[q] > chi ? 1 : 0;
+          n_in += (v[q] >= clo && v[q] <= chi) ? 1 : 0;
+        }
+        n_above = block_sum_i(n_above, sm);
+        n_in = block_sum_i(n_in, sm);
+        if (n_above < k && n_above + n_in >= k && chi > clo) {
+          blo = clo;
+          bhi = chi;
+          need = k - n_above;
+        }
+      }
+      for (int i = tid; i < kTkBins; i += kTkNT) sm.hist[i] = 0;
+      __syncthreads();
+    }
+    // 3b. exact histogram rounds inside [blo, bhi]
     for (int round = 0; round < 4 && !done; ++round) {
       if (!(bhi > blo)) {
         // every remaining score equals blo: ties, lowest indices first
         kthr = score_key(blo);
         const float tv = blo;
-        ithr = block_rth_index(need, [&](int q) { return v[q] == tv; }, sm);
+        ithr = rth_index(need, [&](int q) { return v[q] == tv; });
         done = true;
         break;
       }
-      const float scale = (float)kTkBins / (bhi - blo) * 0.999999f;
+      float scale;
+      bins_of(blo, bhi, scale);
       auto bin_of = [&](float x) {
         return (x < blo || x > bhi) ? -1 : min(kTkBins - 1, (int)((x - blo) * scale));
       };
@@ -1620,37 +1714,26 @@ __global__ __launch_bounds__(kTkNT) void k_topk_rows_reg(KDims d, const float* _
         const int bn = bin_of(v[q]);
         if (bn >= 0) atomicAdd(&sm.hist[bn], 1u);
       }
-      __syncthreads();
-      // bin holding the need-th score from the top: thread t owns bins 2047-2t, 2046-2t
-      const uint32_t h0 = sm.hist[kTkBins - 1 - 2 * tid], h1 = sm.hist[kTkBins - 2 - 2 * tid];
-      uint32_t tot;
-      const uint32_t above = block_excl_scan<kTkNT>(h0 + h1, (uint32_t*)sm.wcnt[1], &tot);
       if (tid == 0) sm.info[3] = 0;
-      if (above < (uint32_t)need && above + h0 + h1 >= (uint32_t)need) {
-        const bool first = above + h0 >= (uint32_t)need;
-        sm.info[0] = first ? kTkBins - 1 - 2 * tid : kTkBins - 2 - 2 * tid;
-        sm.info[1] = (int)(first ? above : above + h0);
-        sm.info[2] = (int)(first ? h0 : h1);
-      }
       __syncthreads();
-      const int T = sm.info[0], mcnt = sm.info[2];
-      need -= sm.info[1];
+      int T, above_T, mcnt;
+      find_bin(need, T, above_T, mcnt);
+      need -= above_T;
       if (mcnt > kTkCand) {
         // crowded bin: its range becomes the next round's
         const float nlo = blo + (float)T / scale, nhi = blo + (float)(T + 1) / scale;
         // scores exactly at the float bin edges stay inside by the clamp of bin_of
         blo = fmaxf(blo, nlo);
         bhi = fminf(bhi, nhi);
-        __syncthreads();
         continue;
       }
-      // 3. gather bin T's entries and rank them (score desc, index asc)
+      // 3c. gather bin T's entries and rank them (score desc, index asc)
 #pragma unroll
       for (int q = 0; q < kTkR; ++q)
         if (bin_of(v[q]) == T) {
           const int slot = atomicAdd(&sm.info[3], 1);
           sm.cand_s[slot] = v[q];
-          sm.cand_i[slot] = idx_of(q);
+          sm.cand_i[slot] = i0 + q;
         }
       __syncthreads();
       for (int t = tid; t < mcnt; t += kTkNT) {
@@ -1677,28 +1760,24 @@ __global__ __launch_bounds__(kTkNT) void k_topk_rows_reg(KDims d, const float* _
       // (exact: the crowded bin's scores are then a handful of equal values)
       kthr = score_key(blo);
       const float tv = blo;
-      ithr = block_rth_index(need, [&](int q) { return v[q] == tv; }, sm);
+      ithr = rth_index(need, [&](int q) { return v[q] == tv; });
     }
   }
-  // 4. emission in index order
-  auto selected = [&](int q) {
-    const uint32_t kv = score_key(v[q]);
-    return v[q] != -INFINITY && (kv > kthr || (kv == kthr && idx_of(q) <= ithr));
-  };
-  int cnt = 0;
-#pragma unroll
-  for (int q = 0; q < kTkR; ++q) cnt += (int)__popcll(__ballot(selected(q)));
-  __syncthreads();
-  if (lane == 0) sm.wcnt[0][wv] = cnt;
-  __syncthreads();
-  int base = 0;
-  for (int u = 0; u < wv; ++u) base += sm.wcnt[0][u];
+  // 4. emission in index order (float compares: the key order is the float
+  // order, with -0 == +0)
+  const float tv = score_of_key(kthr);
+  uint32_t m = 0;
 #pragma unroll
   for (int q = 0; q < kTkR; ++q) {
-    const bool sel = selected(q);
-    const uint64_t mq = __ballot(sel);
-    if (sel) Irow[base + lanes_below(mq)] = idx_of(q);
-    base += (int)__popcll(mq);
+    const bool sel = v[q] > tv || (v[q] == tv && i0 + q <= ithr);
+    m |= sel ? 1u << q : 0u;
+  }
+  uint32_t tot;
+  int slot = (int)block_excl_scan<kTkNT>((uint32_t)__popc(m), sm.wsum, &tot);
+  while (m) {
+    const int q = __builtin_ctz(m);
+    Irow[slot++] = i0 + q;
+    m &= m - 1;
   }
 }
 

@@ -1329,7 +1329,11 @@ __device__ __forceinline__ bool flat_active(const KDims& d, const SeqInfo& si) {
 }
 
 // Scores of 8 query rows (2 per wave) against a chunk of kc keys, streamed
-// through LDS in 64-row tiles.  Masked entries (p >= V) are written as -1e30.
+// through LDS in 64-row tiles, double-buffered: the next tile's rows go
+// global -> LDS (1 KiB = four rows per wave instruction) while the current one
+// is scored.  Rows are dense (256 B) with 16-byte chunk p of row r holding
+// chunk p ^ (r & 15), so the operand reads (16 rows x one chunk) are
+// conflict free.  Masked entries (p >= V) are written as -1e30.
 __global__ __launch_bounds__(256) void k_flat_scores_mfma(KDims d, int kc, const uint16_t* __restrict__ q_idx,
                                                           const float* __restrict__ w,
                                                           const uint16_t* __restrict__ keys,
@@ -1342,9 +1346,10 @@ __global__ __launch_bounds__(256) void k_flat_scores_mfma(KDims d, int kc, const
   if (p_begin >= si.Np) return;
   const int p_end = min(si.Np, p_begin + kc);
   const int j0 = blockIdx.y * 8;
-  const int lane = lane_id(), wv = wave_id(), g = lane >> 4, c = lane & 15, tid = threadIdx.x;
+  const int lane = lane_id(), wv = wave_id(), g = lane >> 4, c = lane & 15;
   const int jlast = min(d.L - 1, j0 + 7);
   const int Vmax = visible(d, t0[b] + jlast, si.Np);
+  const int p_stop = min(p_end, Vmax);  // tiles from here on are fully masked
   int jr[2], Vr[2];
   bool live[2];
   bf16x8 qf[2][4][4];
@@ -1364,22 +1369,29 @@ __global__ __launch_bounds__(256) void k_flat_scores_mfma(KDims d, int kc, const
       for (int i = 0; i < 4; ++i) wl[rr][ht][i] = w[((size_t)b * d.L + jj) * 64 + ht * 16 + 4 * g + i] * d.w_scale;
     }
   }
-  __shared__ __align__(16) uint16_t sk[64 * KP];
+  __shared__ __align__(16) uint16_t sk[2][64 * 128];
   const uint16_t* kb = keys + (size_t)b * d.Np_cap * 128;
-  for (int p0 = p_begin; p0 < p_end; p0 += 64) {
-    const bool compute = p0 < Vmax;
-    __syncthreads();
-    if (compute) {
+  const uint32_t sk_lds = lds_addr(&sk[0][0]);
+  // wave w moves rows 16w .. 16w+15 of a tile: instruction u covers rows
+  // 16w+4u .. +3, lane l row 16w+4u+l/16 at position l%16 (rows past the
+  // chunk end read a valid row whose scores are never stored)
+  auto load_tile = [&](int p0, int buf) {
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int ch = tid + it * 256;
-        const int r = ch >> 4, seg = (ch & 15) * 8;
-        uint4 vk = make_uint4(0, 0, 0, 0);
-        if (p0 + r < p_end) vk = *(const uint4*)(kb + (size_t)(p0 + r) * 128 + seg);
-        *(uint4*)(sk + r * KP + seg) = vk;
-      }
+    for (int u = 0; u < 4; ++u) {
+      const int r = 16 * wv + 4 * u + (lane >> 4);
+      const int ch = (lane & 15) ^ (r & 15);
+      const int pr = min(p0 + r, d.Np_cap - 1);
+      g2lds16(kb + (size_t)pr * 128 + ch * 8, sk_lds + (uint32_t)(buf * 64 * 256 + (16 * wv + 4 * u) * 256));
     }
-    __syncthreads();
+  };
+  if (p_begin < p_stop) load_tile(p_begin, 0);
+  int buf = 0;
+  for (int p0 = p_begin; p0 < p_end; p0 += 64, buf ^= 1) {
+    const bool compute = p0 < p_stop;
+    if (compute) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0: this wave's rows of the tile
+    __syncthreads();  // every wave's rows are in; the other buffer is free
+    if (p0 + 64 < p_stop) load_tile(p0 + 64, buf ^ 1);
+    const uint16_t* skb = sk[buf];
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
       if (!live[rr]) continue;
@@ -1387,13 +1399,14 @@ __global__ __launch_bounds__(256) void k_flat_scores_mfma(KDims d, int kc, const
       for (int sub = 0; sub < 4; ++sub) {
         const int p = p0 + sub * 16 + c;
         float x = kNeg;
-        if (p0 + sub * 16 < Vr[rr]) {
+        if (compute && p0 + sub * 16 < Vr[rr]) {
+          const int r = sub * 16 + c;
           f32x4 acc[4];
 #pragma unroll
           for (int ht = 0; ht < 4; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
-            const bf16x8 kf = lds8(sk + (sub * 16 + c) * KP + s * 32 + g * 8);
+            const bf16x8 kf = lds8(skb + r * 128 + (((4 * s + g) ^ c) * 8));
 #pragma unroll
             for (int ht = 0; ht < 4; ++ht)
               acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[rr][ht][s], kf, acc[ht], 0, 0, 0);
@@ -1402,7 +1415,7 @@ __global__ __launch_bounds__(256) void k_flat_scores_mfma(KDims d, int kc, const
 #pragma unroll
           for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v += fmaxf(acc[ht][i], 0.f) * wl[rr][ht][i];
+            for (int i = 0; i < 4; ++i) v += relu(acc[ht][i]) * wl[rr][ht][i];
           v = sum_rows(v);
           if (p < Vr[rr]) x = v;
         }

@@ -506,15 +506,17 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
 // score layout, so nothing moves between lanes or waves.  The only barrier
 // per tile makes the tile's rows (fetched by all four waves, global->LDS)
 // visible and frees the ring slot of the tile NBUF-1 ahead.
-template <int DK, int DV>
-__global__ __launch_bounds__(256, 2) void k_attn_fa(KDims d, const uint16_t* __restrict__ q,
-                                                 const uint16_t* __restrict__ local_kv,
-                                                 const uint16_t* __restrict__ pooled_kv, const int* __restrict__ I,
-                                                 const float* __restrict__ sinks, const int* __restrict__ t0,
-                                                 uint16_t* __restrict__ out) {
-  constexpr int NW = 4, NT = 256, HW = 64;
+template <int DK, int DV, int NW>
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_fa(KDims d, const uint16_t* __restrict__ q,
+                                                                      const uint16_t* __restrict__ local_kv,
+                                                                      const uint16_t* __restrict__ pooled_kv,
+                                                                      const int* __restrict__ I,
+                                                                      const float* __restrict__ sinks,
+                                                                      const int* __restrict__ t0,
+                                                                      uint16_t* __restrict__ out) {
+  constexpr int NT = NW * 64, HW = NW * 16;
   constexpr int KPD = (DK * 2 + 255) / 256 * 128;  // LDS row pitch (elements)
-  constexpr int NBUF = 2;                          // ring slots (two workgroups per CU)
+  constexpr int NBUF = 2;                          // ring slots (LDS for two workgroups per CU at 512 wide)
   constexpr int NS = DK / 32;                      // MFMA k-steps of S
   constexpr int NDT = DV / 16;                     // 16-column value tiles (all of them, every wave)
   constexpr int RPW = kTile / NW;                  // rows of a tile each wave fetches
@@ -526,7 +528,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fa(KDims d, const uint16_t* __r
   constexpr int NACC = 2;                          // accumulation chains per row block
   constexpr int PVG = 8;                           // value tiles whose reads are in flight together
   constexpr int OP = DV + 8;                       // pitch of the staged output rows (elements)
-  static_assert(HW / 2 * OP <= NBUF * kTile * KPD, "half the heads' staging fits the ring");
+  static_assert(32 * OP <= NBUF * kTile * KPD, "32 heads' staging fits the ring");
   static_assert(RPW % 4 == 0 && CH % NT == 0, "shape of the row fetch");
   static_assert(DV % 16 == 0 && DV <= DK && DK >= 512 && DK <= 1024 && DK % 32 == 0, "shape");
   __shared__ __align__(16) uint16_t kv[NBUF][kTile * KPD];
@@ -754,11 +756,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_fa(KDims d, const uint16_t* __r
     const float lf = l * exp2f(m - mf) + (sinks ? exp2f(sink2 - mf) : 0.f);
     f = lf > 0.f ? exp2f(m - mf) / lf : 0.f;
   }
-  // two halves of 32 heads: waves 2h and 2h+1 stage, then all copy out
+  // groups of 32 heads: waves 2h and 2h+1 stage, then all copy out
   uint16_t* og = out + ((size_t)row * d.H + hbase) * DV;
   constexpr int CPR = DV / 8;  // 16-byte pieces per head row
 #pragma unroll 1
-  for (int half = 0; half < 2; ++half) {
+  for (int half = 0; half < NW / 2; ++half) {
     __syncthreads();  // every wave is done with the ring (or the previous half)
     if ((wv >> 1) == half) {
       uint16_t* orow = &kv[0][0] + (16 * (wv & 1) + c) * OP + 4 * g;
@@ -911,15 +913,16 @@ hipError_t launch_mfma(const KDims& d, const void* q, const void* local_kv, cons
     return hipGetLastError();
   }
   if constexpr (DK == 512) {
-    // many rows, 512 wide: the flash-style kernel, two workgroups per CU
-    // (at 576 wide it holds one and the kernel below is faster)
+    // many rows, 512 wide: the flash-style kernel, 64 heads, two workgroups per CU
     if (splits == 1) {
       const dim3 grid(1, d.B * d.L, d.H / 64);
-      hipLaunchKernelGGL((k_attn_fa<DK, DV>), grid, dim3(256), 0, st, d, (const uint16_t*)q,
+      hipLaunchKernelGGL((k_attn_fa<DK, DV, 4>), grid, dim3(256), 0, st, d, (const uint16_t*)q,
                          (const uint16_t*)local_kv, (const uint16_t*)pooled_kv, I, sinks, t0, (uint16_t*)out);
       return hipGetLastError();
     }
   }
+  // (576 wide, the flash-style kernel holds one workgroup per CU, with 64
+  // heads or with 128, and the kernel below is faster)
   {
     const dim3 grid(splits, d.B * d.L, d.H / 64);
     hipLaunchKernelGGL((k_attn_mfma<DK, DV, 4>), grid, dim3(512), 0, st, d, splits, (const uint16_t*)q,

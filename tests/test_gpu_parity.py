@@ -369,7 +369,7 @@ def test_attention_split_merge_paths(hisa):
     # Few query rows split their 640-row lists over several workgroups whose
     # partial results a second kernel merges: three calls on one workspace
     # give bit-identical outputs that match the oracle; 6 sequences (16-head
-    # workgroups, 10 splits) and 40 sequences (64-head workgroups, 7 splits)
+    # workgroups, 10 splits) and 40 sequences (64-head workgroups, 4 splits)
     # match it on sampled rows.
     w = synth.FLASH_DECODE
     x, g = inputs(w, synth.SEEDS[w.name])

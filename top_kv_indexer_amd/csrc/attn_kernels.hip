@@ -951,7 +951,10 @@ int attn_splits(const KDims& d, bool bf16) {
   const long long n_max = (long long)d.window + d.kI;
   // at least two 32-row tiles per split, so that fetching overlaps compute
   const long long max_splits = std::max(1LL, (n_max + 2 * kTile - 1) / (2 * kTile));
-  long long want = (256 + work - 1) / work;
+  // about 256 two-wave workgroups (16 heads) or 128 eight-wave ones (64
+  // heads): more splits only add partials to merge
+  const long long target = attn_small_groups(d) ? 256 : 128;
+  long long want = (target + work - 1) / work;
   want = std::min(want, std::min(max_splits, (long long)kMaxSplits));
   return (int)std::max(1LL, want);
 }

@@ -109,6 +109,17 @@ def algorithmic(w, x, unique_kv_rows=None):
     }
 
 
+def rate(a, seconds):
+    """Roofline position of one launch with algorithmic cost `a` that took
+    `seconds`: bf16 MFMA-bound when its flops take longer at peak than its
+    bytes at HBM peak, else HBM-bound."""
+    if a["flops"] / BF16_PEAK_TFLOPS / 1e12 > a["bytes"] / HBM_PEAK_GBPS / 1e9:
+        ach = a["flops"] / seconds / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 2), "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4)}
+    ach = a["bytes"] / seconds / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4)}
+
+
 def cpu_baseline(w, x, seconds):
     """The oracle (as it stands) on the host: threads each run whole decode
     steps (selection + attention of one query row) until `seconds` elapse."""
@@ -274,6 +285,8 @@ def main():
     for name, (n, tot) in prof.items():
         avg_ms = tot / max(n, 1)
         kernels[name] = {"launches_per_step": n // args.steps, "avg_us": round(avg_ms * 1e3, 3)}
+        if name in alg and avg_ms > 0:
+            kernels[name].update(rate(alg[name], avg_ms / 1e3))
     dominant = max(prof.items(), key=lambda kv: kv[1][1])[0]
     dom_avg_s = prof[dominant][1] / prof[dominant][0] / 1e3
     timing = "HIP events around each launch"
@@ -300,17 +313,11 @@ def main():
         dom_avg_s = e2.elapsed_time(e3) / args.steps / 1e3
         timing = f"{args.steps} back-to-back launches of its library call between two HIP events"
     a = alg.get(dominant, {"bytes": 0, "flops": 0})
-    mfma_bound = a["flops"] / BF16_PEAK_TFLOPS / 1e12 > a["bytes"] / HBM_PEAK_GBPS / 1e9
-    if mfma_bound:
-        ach = a["flops"] / dom_avg_s / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": stored_traffic(w.name, dominant)}
-    else:
-        ach = a["bytes"] / dom_avg_s / 1e9
-        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": stored_traffic(w.name, dominant)}
+    roof = rate(a, dom_avg_s)
+    roof["peak"] = BF16_PEAK_TFLOPS if roof["bound"] == "mfma" else HBM_PEAK_GBPS
+    roof["traffic"] = stored_traffic(w.name, dominant)
     roof["kernel"] = dominant
-    roof["algorithmic_per_launch"] = a["flops"] if mfma_bound else a["bytes"]
+    roof["algorithmic_per_launch"] = a["flops"] if roof["bound"] == "mfma" else a["bytes"]
     roof["avg_us"] = round(dom_avg_s * 1e6, 3)
     roof["timing"] = timing
 

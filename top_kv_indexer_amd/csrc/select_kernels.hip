@@ -1385,43 +1385,67 @@ __global__ __launch_bounds__(256) void k_flat_scores_mfma(KDims d, int kc, const
     }
   };
   if (p_begin < p_stop) load_tile(p_begin, 0);
+  float* srow[2];
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) srow[rr] = scores + ((size_t)b * d.L + (live[rr] ? jr[rr] : 0)) * d.Np_cap;
   int buf = 0;
   for (int p0 = p_begin; p0 < p_end; p0 += 64, buf ^= 1) {
     const bool compute = p0 < p_stop;
     if (compute) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0: this wave's rows of the tile
     __syncthreads();  // every wave's rows are in; the other buffer is free
     if (p0 + 64 < p_stop) load_tile(p0 + 64, buf ^ 1);
-    const uint16_t* skb = sk[buf];
+    float x[2] = {kNeg, kNeg};
+    if (compute) {
+      // units u = 0..7: keys 16*(u/2) .. +15 of the tile against row u%2; the
+      // MFMAs of unit u+1 are issued before the epilogue of unit u, and the
+      // two rows share each key fragment read from LDS
+      const uint16_t* skb = sk[buf];
+      bf16x8 kf[4];
+      f32x4 acc[2][4];
+      float sv[2][4];
+      auto mma = [&](int u, f32x4(&a)[4]) {
+        if ((u & 1) == 0) {
+          const int r = (u >> 1) * 16 + c;
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      if (!live[rr]) continue;
-      float* srow = scores + ((size_t)b * d.L + jr[rr]) * d.Np_cap;
-      for (int sub = 0; sub < 4; ++sub) {
-        const int p = p0 + sub * 16 + c;
-        float x = kNeg;
-        if (compute && p0 + sub * 16 < Vr[rr]) {
-          const int r = sub * 16 + c;
-          f32x4 acc[4];
+          for (int s = 0; s < 4; ++s) kf[s] = lds8(skb + r * 128 + (((4 * s + g) ^ c) * 8));
+        }
 #pragma unroll
-          for (int ht = 0; ht < 4; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ht = 0; ht < 4; ++ht) a[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const bf16x8 kf = lds8(skb + r * 128 + (((4 * s + g) ^ c) * 8));
-#pragma unroll
-            for (int ht = 0; ht < 4; ++ht)
-              acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[rr][ht][s], kf, acc[ht], 0, 0, 0);
-          }
-          float v = 0.f;
+        for (int s = 0; s < 4; ++s)
 #pragma unroll
           for (int ht = 0; ht < 4; ++ht)
+            a[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[u & 1][ht][s], kf[s], a[ht], 0, 0, 0);
+      };
+      mma(0, acc[0]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v += relu(acc[ht][i]) * wl[rr][ht][i];
-          v = sum_rows(v);
-          if (p < Vr[rr]) x = v;
-        }
-        if (g == 0 && p < p_end) srow[p] = x;
+      for (int u = 0; u < 8; ++u) {
+        if (u + 1 < 8) mma(u + 1, acc[(u + 1) & 1]);
+        float v = 0.f;
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v += relu(acc[u & 1][ht][i]) * wl[u & 1][ht][i];
+        sv[u & 1][u >> 1] = v;
+      }
+      // sum over the four lane rows of all four key groups at once: lane
+      // 16*g + c ends with key 16*g + c of the tile
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        u32x2 a = __builtin_amdgcn_permlane32_swap(__float_as_uint(sv[rr][0]), __float_as_uint(sv[rr][2]), false,
+                                                   false);
+        const float s02 = __uint_as_float(a.x) + __uint_as_float(a.y);
+        a = __builtin_amdgcn_permlane32_swap(__float_as_uint(sv[rr][1]), __float_as_uint(sv[rr][3]), false, false);
+        const float s13 = __uint_as_float(a.x) + __uint_as_float(a.y);
+        a = __builtin_amdgcn_permlane16_swap(__float_as_uint(s02), __float_as_uint(s13), false, false);
+        const float v = __uint_as_float(a.x) + __uint_as_float(a.y);
+        if (p0 + lane < Vr[rr]) x[rr] = v;
       }
     }
+    const int p = p0 + lane;
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr)
+      if (live[rr] && p < p_end) srow[rr][p] = x[rr];
   }
 }
 

@@ -477,7 +477,7 @@ __device__ __forceinline__ bool publish(CountF count, int* s_flag) {
   __syncthreads();
   if (threadIdx.x == 0) *s_flag = count();
   __syncthreads();
-  return *s_flag != 0;
+  return __builtin_amdgcn_readfirstlane(*s_flag) != 0;
 }
 
 // Counters of the latency-bound scan: one per group of kArriveGroup slabs
@@ -565,6 +565,7 @@ __global__ __launch_bounds__(256) void k_decode_scan_stream(
   __shared__ __align__(16) uint16_t s_q[64 * 128];
   __shared__ __align__(16) float s_part[2][4][64];
   __shared__ int s_pre[kStreamMaxB + 1];  // first flattened slab of each sequence
+  __shared__ int s_t0[kStreamMaxB];       // t0 of each sequence
   __shared__ uint32_t s_wsum[4];
   __shared__ DecodeSelSmem s_sel;
   __shared__ int s_flag;
@@ -580,7 +581,9 @@ __global__ __launch_bounds__(256) void k_decode_scan_stream(
       const int bb = 4 * tid + u;
       n[u] = 0;
       if (bb < d.B) {
-        const SeqInfo sb = seq_info(d, t0[bb]);
+        const int t0bb = t0[bb];
+        s_t0[bb] = t0bb;
+        const SeqInfo sb = seq_info(d, t0bb);
         if (sb.ok && sb.path != PATH_DENSE) n[u] = (sb.Np + 63) / 64;
       }
       loc += (uint32_t)n[u];
@@ -598,10 +601,15 @@ __global__ __launch_bounds__(256) void k_decode_scan_stream(
   // outputs of the sequences that are not scored
   if (cnt && wv == 0)
     for (int bb = blockIdx.x; bb < d.B; bb += gridDim.x) {
-      const SeqInfo sb = seq_info(d, t0[bb]);
+      const SeqInfo sb = seq_info(d, s_t0[bb]);
       if (!sb.ok || sb.path == PATH_DENSE) write_unscored(d, sb, bb, I, top_blk, path);
     }
-  const int total = s_pre[d.B];
+  // the prefix and t0 tables are read into scalar registers: every branch
+  // and loop below is then uniform over the wave, which keeps the waits for
+  // in-flight slab rows exact
+  auto pre = [&](int i) { return __builtin_amdgcn_readfirstlane(s_pre[i]); };
+  auto t0_of = [&](int i) { return __builtin_amdgcn_readfirstlane(s_t0[i]); };
+  const int total = pre(d.B);
   const int share = (total + (int)gridDim.x - 1) / (int)gridDim.x;
   const int g_begin = min(total, (int)blockIdx.x * share), g_end = min(total, g_begin + share);
   if (g_begin >= g_end) return;
@@ -609,30 +617,18 @@ __global__ __launch_bounds__(256) void k_decode_scan_stream(
   // or later: the last sequence whose first slab is <= x (empty sequences
   // share their first slab with the next one, so the last is non-empty)
   auto seq_of = [&](int x, int from) {
-    if (s_pre[from + 1] > x) return from;
+    if (pre(from + 1) > x) return from;
     int lo = from + 1, hi = d.B - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (s_pre[mid] <= x) lo = mid;
+      if (pre(mid) <= x) lo = mid;
       else hi = mid - 1;
     }
     return lo;
   };
-  int b = seq_of(g_begin, 0);
-  SeqInfo si = seq_info(d, t0[b]);
-  // rows of flattened slab x (x < total), given that its sequence is `from` or later
-  auto load_flat = [&](int x, int from, bf16x8 (&kf)[4]) {
-    const int bx = seq_of(x, from);
-    const int np_x = bx == b ? si.Np : seq_info(d, t0[bx]).Np;
-    load_slab_rows(keys + (size_t)bx * d.Np_cap * 128, x - s_pre[bx], np_x - 1, kf);
-  };
-  // the next two slabs stream in while one is scored
-  bf16x8 k0[4], k1[4], k2[4];
-  load_flat(g_begin, b, k0);
-  if (g_begin + 1 < g_end) load_flat(g_begin + 1, b, k1);
   bf16x8 qf[4][4];
   float wl[4][4], w_head = 0.f;
-  int run_start = g_begin, n_done = 0;
+  int n_done = 0;
   auto enter = [&](int bb) {  // q and the head weights of sequence bb
     __syncthreads();  // every wave is done reading the previous q
     issue_q_lds(q_idx + (size_t)bb * d.L * 64 * 128, s_q);
@@ -651,31 +647,41 @@ __global__ __launch_bounds__(256) void k_decode_scan_stream(
     w_head *= d.w_scale;
     read_q_lds(s_q, qf);
   };
-  enter(b);
-  for (int x = g_begin; x < g_end; ++x) {
-    const int slab = x - s_pre[b];
-    if (x + 2 < g_end) load_flat(x + 2, b, k2);
-    const int bn = x + 1 < g_end ? seq_of(x + 1, b) : b;
-    score_slab(d, si, b, slab, x & 1, qf, wl, w_head, k0, fscore, cscore, s_part);
-    const bool seq_ends = x + 1 == g_end || bn != b;
-    if (seq_ends) {
-      const int nslab = s_pre[b + 1] - s_pre[b];
-      if (cnt && publish([&] { return arrive(cnt + (size_t)b * kCntStride, x + 1 - run_start, nslab); }, &s_flag)) {
-        if (tid == 0) s_done[n_done] = b;
-        ++n_done;
-      }
-      if (x + 1 < g_end) {
-        b = bn;
-        si = seq_info(d, t0[b]);
-        run_start = x + 1;
-        enter(b);
-      }
+  // runs: the slabs of one sequence inside the share
+  for (int x0 = g_begin, b = seq_of(g_begin, 0);;) {
+    const SeqInfo si = seq_info(d, t0_of(b));
+    const int first = pre(b), x1 = min(g_end, pre(b + 1)), n = __builtin_amdgcn_readfirstlane(x1 - x0);
+    const uint16_t* kb = keys + (size_t)b * d.Np_cap * 128;
+    // slab i of the run; past the run's end its last slab is read again (a
+    // cache hit), so every step issues the same loads and each wait for a
+    // slab's rows leaves the two younger slabs in flight
+    auto load = [&](int i, bf16x8(&kf)[4]) { load_slab_rows(kb, x0 + min(i, n - 1) - first, si.Np - 1, kf); };
+    auto score = [&](int i, const bf16x8(&kf)[4]) {
+      score_slab(d, si, b, x0 + i - first, (x0 + i) & 1, qf, wl, w_head, kf, fscore, cscore, s_part);
+    };
+    bf16x8 k0[4], k1[4], k2[4];
+    load(0, k0);
+    load(1, k1);
+    enter(b);
+    // the three buffers take turns by name (no register copies)
+    for (int i = 0;; i += 3) {
+      load(i + 2, k2);
+      score(i, k0);
+      if (i + 1 >= n) break;
+      load(i + 3, k0);
+      score(i + 1, k1);
+      if (i + 2 >= n) break;
+      load(i + 4, k1);
+      score(i + 2, k2);
+      if (i + 3 >= n) break;
     }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      k0[s] = k1[s];
-      k1[s] = k2[s];
+    if (cnt && publish([&] { return arrive(cnt + (size_t)b * kCntStride, n, pre(b + 1) - first); }, &s_flag)) {
+      if (tid == 0) s_done[n_done] = b;
+      ++n_done;
     }
+    if (x1 >= g_end) break;
+    x0 = x1;
+    b = seq_of(x0, b + 1);
   }
   // selections of the sequences this workgroup completed (after the scan,
   // so its registers are free)
@@ -683,7 +689,7 @@ __global__ __launch_bounds__(256) void k_decode_scan_stream(
   __syncthreads();
   for (int u = 0; u < n_done; ++u) {
     const int bd = s_done[u];
-    decode_select_wg(d, seq_info(d, t0[bd]), bd, fscore + (size_t)bd * d.Np_cap, cscore + (size_t)bd * d.nb_cap, I,
+    decode_select_wg(d, seq_info(d, s_t0[bd]), bd, fscore + (size_t)bd * d.Np_cap, cscore + (size_t)bd * d.nb_cap, I,
                      top_blk, path, s_sel);
     __syncthreads();  // s_sel is reused by the next selection
   }

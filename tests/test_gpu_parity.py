@@ -510,6 +510,27 @@ def test_generic_kernels_prefill_f32(hisa):
                                                                            x["keys"][b], int(x["t0"][b]), j, ids))
 
 
+@pytest.mark.parametrize("shape", ["wide_rows", "odd_width", "many_index_heads"])
+def test_generic_kernels_shapes_f32(hisa, shape):
+    # f32 VALU kernels off the tiny shape: rows wider than a workgroup
+    # (Dk = Dv = 300: one thread per value column, and a dot-product tail past
+    # the 16-wide steps), a value width that does not divide 256 (96), and
+    # more than 64 indexer heads (block scores from block means of the keys).
+    kw = {"wide_rows": dict(H=3, Dk=300, Dv=300),
+          "odd_width": dict(H=5, Dk=96, Dv=96),
+          "many_index_heads": dict(H_i=72, D_i=20, index_block=8)}[shape]
+    w = synth.TINY_DECODE.with_(name="generic_" + shape, B=2, L=1, t0=[4000, 2600], Np_cap=1000, planted=3, **kw)
+    x, g = inputs(w, 19)
+    say(f"[run] generic decode selection {shape}")
+    I, blk, path = hisa.hisa_select_decode(g["q_idx"], g["w"], g["keys"], g["t0"], **sel_kw(w))
+    torch.cuda.synchronize()
+    check_selection(w, x, I, blk, path)
+    say(f"[run] generic attention {shape}")
+    out = run_attention(hisa, w, g, I)
+    torch.cuda.synchronize()
+    check_attention(w, x, I, out)
+
+
 def test_dense_equivalence(hisa):
     # HiSA issue, Validation: with every pooled row selected (k == Np) the
     # sparse combine equals dense local + pooled attention.

@@ -864,10 +864,19 @@ __global__ __launch_bounds__(256) void k_attn_valu(KDims d, const T* __restrict_
     float x = -INFINITY;
     const int code = s_row[e];
     if (code != -1) {
+      // sixteen loads of the row in flight per step, four partial sums
       const T* kp = row_ptr(code);
-      float acc = 0.f;
-      for (int k = 0; k < d.Dk; ++k) acc += s_q[k] * ldf(kp + k);
-      x = acc;
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+      int k = 0;
+      for (; k + 16 <= d.Dk; k += 16) {
+        float v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = ldf(kp + k + u);
+#pragma unroll
+        for (int u = 0; u < 16; ++u) acc[u & 3] += s_q[k + u] * v[u];
+      }
+      for (; k < d.Dk; ++k) acc[0] += s_q[k] * ldf(kp + k);
+      x = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     }
     s_x[e] = x;
     mx = fmaxf(mx, x);
@@ -893,12 +902,38 @@ __global__ __launch_bounds__(256) void k_attn_valu(KDims d, const T* __restrict_
   __syncthreads();
   z = s_red[0] + s_red[1] + s_red[2] + s_red[3] + (sinks ? expf(sinks[h] - mx) : 0.f);
   const float inv = 1.f / z;
+  // P V: with Dv < 256, G = 256 / Dv thread groups each sum every G-th row
+  // (partials combined in LDS, in s_q, which the scores no longer need);
+  // eight rows' loads are in flight per step
+  const int G = d.Dv >= 256 ? 1 : 256 / d.Dv;
+  const int span = G == 1 ? 256 : d.Dv;
+  const int grp = tid / span;
+  if (grp < G)
+    for (int e = tid % span; e < d.Dv; e += span) {
+      float o = 0.f;
+      int r = grp;
+      for (; r + 7 * G < n; r += 8 * G) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int code = s_row[r + u * G];
+          v[u] = code != -1 ? ldf(row_ptr(code) + e) : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) o += s_x[r + u * G] * v[u];
+      }
+      for (; r < n; r += G) {
+        const int code = s_row[r];
+        if (code != -1) o += s_x[r] * ldf(row_ptr(code) + e);
+      }
+      if (G == 1) stf(orow + e, o * inv);
+      else s_q[grp * d.Dv + e] = o;
+    }
+  if (G == 1) return;
+  __syncthreads();
   for (int e = tid; e < d.Dv; e += 256) {
     float o = 0.f;
-    for (int r = 0; r < n; ++r) {
-      const int code = s_row[r];
-      if (code != -1) o += s_x[r] * ldf(row_ptr(code) + e);
-    }
+    for (int gg = 0; gg < G; ++gg) o += s_q[gg * d.Dv + e];
     stf(orow + e, o * inv);
   }
 }

@@ -707,6 +707,8 @@ __global__ __launch_bounds__(256) void k_decode_scan_valu(KDims d, const T* __re
   const int row0 = blockIdx.x * 64;
   const SeqInfo si = seq_info(d, t0[b]);
   if (!si.ok || si.path == PATH_DENSE || row0 >= si.Np) return;
+  // pre-relu dots of the slab's rows, per head, for the block scores (heads <= 64)
+  __shared__ float s_dot[64 * 64];
   __shared__ float s_rep[1024];
   __shared__ float s_red[4];
   const int tid = threadIdx.x, part = tid & 3, r = tid >> 2;
@@ -715,16 +717,36 @@ __global__ __launch_bounds__(256) void k_decode_scan_valu(KDims d, const T* __re
   const int p = row0 + r;
   const bool live = p < si.Np;
   const T* kp = keys + ((size_t)b * d.Np_cap + (live ? p : row0)) * d.D_i;
+  const bool keep_dots = si.path == PATH_HISA && d.H_i <= 64;
   float tot = 0.f;
   for (int h = 0; h < d.H_i; ++h) {
     float dot = 0.f;
+#pragma unroll 8
     for (int e = part; e < d.D_i; e += 4) dot += ldf(qb + (size_t)h * d.D_i + e) * ldf(kp + e);
     dot = sum_span(dot, 4);
+    if (keep_dots && part == 0) s_dot[h * 64 + r] = dot;
     tot += fmaxf(dot, 0.f) * (wb[h] * d.w_scale);
   }
   if (live && part == 0) fscore[(size_t)b * d.Np_cap + p] = tot;
   if (si.path != PATH_HISA) return;
   const int bsz = d.index_block;
+  if (keep_dots) {
+    // The block mean is linear: q_h . rep_beta is the mean of the block's row
+    // dots, so each block score comes from the dots already in LDS.
+    __syncthreads();
+    const int blk = tid, beta = row0 / bsz + blk;
+    if (blk < 64 / bsz && beta < si.nb) {
+      const float inv_b = 1.f / (float)bsz;
+      float cv = 0.f;
+      for (int h = 0; h < d.H_i; ++h) {
+        float sum = 0.f;
+        for (int rr = 0; rr < bsz; ++rr) sum += s_dot[h * 64 + blk * bsz + rr];
+        cv += fmaxf(sum * inv_b, 0.f) * (wb[h] * d.w_scale);
+      }
+      cscore[(size_t)b * d.nb_cap + beta] = cv;
+    }
+    return;
+  }
   for (int blk = 0; blk < 64 / bsz; ++blk) {
     const int beta = row0 / bsz + blk;
     if (beta >= si.nb) break;

@@ -663,17 +663,25 @@ __global__ __launch_bounds__(256) void k_decode_scan_stream(
     load(0, k0);
     load(1, k1);
     enter(b);
-    // the three buffers take turns by name (no register copies)
-    for (int i = 0;; i += 3) {
+    // the three buffers take turns by name (no register copies); the loop
+    // body has no exit of its own (the last one or two slabs follow it), so
+    // the waits inside it count the younger slabs exactly
+    int i = 0;
+    for (; i + 3 <= n; i += 3) {
       load(i + 2, k2);
       score(i, k0);
-      if (i + 1 >= n) break;
       load(i + 3, k0);
       score(i + 1, k1);
-      if (i + 2 >= n) break;
       load(i + 4, k1);
       score(i + 2, k2);
-      if (i + 3 >= n) break;
+    }
+    if (i < n) {
+      load(i + 2, k2);
+      score(i, k0);
+      if (i + 1 < n) {
+        load(i + 3, k0);
+        score(i + 1, k1);
+      }
     }
     if (cnt && publish([&] { return arrive(cnt + (size_t)b * kCntStride, n, pre(b + 1) - first); }, &s_flag)) {
       if (tid == 0) s_done[n_done] = b;

@@ -72,7 +72,7 @@ def stored_traffic(workload, kernel):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
-def algorithmic(w, x, unique_kv_rows=None):
+def algorithmic(w, x, unique_kv_rows=None, flat_seqs=None):
     """Compulsory bytes / flops per kernel family for one step of workload w.
     Bytes: every input read once and every output written once; flops: the
     method's own multiply-adds (x2).  unique_kv_rows: distinct KV rows the
@@ -91,6 +91,7 @@ def algorithmic(w, x, unique_kv_rows=None):
         + rows * kI * 4 + (w.H * 4 if w.sinks else 0)
     attn_flops = rows * (kI + n_local) * w.H * (w.Dk + w.Dv) * 2
     nb = [n // w.index_block for n in Np] if w.index_block else [0] * B
+    flat = list(range(B)) if flat_seqs is None else [b for b in range(B) if flat_seqs[b]]
     C = w.index_keep * w.index_block
     return {
         "decode_scan": {"bytes": keys + idx_q, "flops": sum(Np) * w.H_i * w.D_i * 2},
@@ -101,9 +102,11 @@ def algorithmic(w, x, unique_kv_rows=None):
         "block_mean": {"bytes": keys, "flops": 0},
         "coarse": {"bytes": idx_q, "flops": L * sum(nb) * w.H_i * w.D_i * 2},
         "fine": {"bytes": idx_q + rows * kI * 4, "flops": rows * C * w.H_i * w.D_i * 2},
-        "flat_scores": {"bytes": keys + idx_q, "flops": sum(
-            sum(min(n, (int(t) + j + 1) // w.ratio) for j in range(L)) for n, t in zip(Np, x["t0"])) * w.H_i * w.D_i * 2},
-        "topk_rows": {"bytes": rows * kI * 4, "flops": 0},
+        # the flat scan scores only the sequences on the flat path
+        "flat_scores": {"bytes": sum(Np[b] for b in flat) * w.D_i * bf + len(flat) * L * (w.H_i * w.D_i * bf + w.H_i * 4),
+                        "flops": sum(sum(min(Np[b], (int(x["t0"][b]) + j + 1) // w.ratio) for j in range(L))
+                                     for b in flat) * w.H_i * w.D_i * 2},
+        "topk_rows": {"bytes": len(flat) * L * kI * 4, "flops": 0},
         "select_rows": {"bytes": idx_q + rows * kI * 4,
                         "flops": L * sum(nb) * w.H_i * w.D_i * 2 + rows * C * w.H_i * w.D_i * 2},
     }
@@ -280,7 +283,8 @@ def main():
         ids = In[b].reshape(-1)
         uniq += len(np.unique(ids[(ids >= 0) & (ids < int(x["Np"][b]))]))
         uniq += int(x["Wl"][b]) if w.window else 0
-    alg = algorithmic(w, x, unique_kv_rows=uniq)
+    flat_seqs = [int(v) == hisa.PATH_FLAT for v in path.cpu().tolist()]
+    alg = algorithmic(w, x, unique_kv_rows=uniq, flat_seqs=flat_seqs)
     kernels = {}
     for name, (n, tot) in prof.items():
         avg_ms = tot / max(n, 1)

@@ -304,11 +304,17 @@ int hisa_select_prefill(const hisa_dims* d, const void* q_idx, const float* w, c
       if (e != hipSuccess) return launch_fail(e, "coarse scores");
     }
   }
-  float* scores = at<float>(ws, l.scores);
-  e = timed("flat_scores", st, [&] { return hisa::launch_flat_scores(k, bf, q_idx, w, keys, t0, scores, st); });
-  if (e != hipSuccess) return launch_fail(e, "flat scores");
-  e = timed("topk_rows", st, [&] { return hisa::launch_topk_rows(k, scores, t0, I_out, nullptr, st); });
-  if (e != hipSuccess) return launch_fail(e, "flat top-k");
+  // The row selection also takes the flat sequences when they are short: with
+  // index_block * index_keep >= topk a flat sequence has Np below that product
+  // (at most 1024 where the row selection runs).  Otherwise the flat scan runs.
+  const bool flat_in_rows = rows && !k.force_flat && (long long)k.index_block * k.index_keep >= k.topk;
+  if (!flat_in_rows) {
+    float* scores = at<float>(ws, l.scores);
+    e = timed("flat_scores", st, [&] { return hisa::launch_flat_scores(k, bf, q_idx, w, keys, t0, scores, st); });
+    if (e != hipSuccess) return launch_fail(e, "flat scores");
+    e = timed("topk_rows", st, [&] { return hisa::launch_topk_rows(k, scores, t0, I_out, nullptr, st); });
+    if (e != hipSuccess) return launch_fail(e, "flat top-k");
+  }
   if (!rows) {
     e = timed("fine", st, [&] { return hisa::launch_fine(k, bf, q_idx, w, keys, cscore, t0, I_out, top_blk_out, path_out, st); });
     if (e != hipSuccess) return launch_fail(e, "fine selection");

@@ -1178,11 +1178,16 @@ __global__ __launch_bounds__(256) void k_select_rows(KDims d, const uint16_t* __
   const SeqInfo si = seq_info(d, t0[b]);
   int* Irow = I + ((size_t)b * d.L + j) * d.topk;
   int* blkrow = top_blk ? top_blk + ((size_t)b * d.L + j) * d.index_keep : nullptr;
+  // With index_block * index_keep >= topk (and at most 1024 here) a flat
+  // sequence has Np < index_block * index_keep: its row takes every pooled
+  // row as a candidate of the fine stage, without the coarse stage.
+  // Otherwise flat rows belong to the flat scan.
+  const bool flat_here = si.path == PATH_FLAT && !d.force_flat && d.index_block * d.index_keep >= d.topk;
   if (live) {
     if (path && j == 0 && lane == 0) path[b] = si.path;
     if (blkrow)
       for (int i = lane; i < d.index_keep; i += 64) blkrow[i] = -1;
-    if (si.path != PATH_FLAT) {  // flat rows belong to the flat scan
+    if (si.path != PATH_FLAT || flat_here) {
       const bool dense = si.path == PATH_DENSE;
       const int first_pad = (si.ok && !dense) ? si.k : 0;
       for (int i = lane; i < d.topk; i += 64) {
@@ -1191,7 +1196,7 @@ __global__ __launch_bounds__(256) void k_select_rows(KDims d, const uint16_t* __
       }
     }
   }
-  if (!si.ok || si.path != PATH_HISA) return;  // uniform over the workgroup (one sequence)
+  if (!si.ok || (si.path != PATH_HISA && !flat_here)) return;  // uniform over the workgroup (one sequence)
   const int valid = visible(d, t0[b] + j, si.Np);
   float* sc = s_sc[wv];
 
@@ -1226,64 +1231,66 @@ __global__ __launch_bounds__(256) void k_select_rows(KDims d, const uint16_t* __
     else __builtin_amdgcn_s_waitcnt(0x0F74);
   };
 
-  // ---- coarse scores of blocks 16nt + c (eligible iff the block's first row is visible)
   const int bsz = d.index_block, nb = si.nb;
   const int lbsz = __builtin_ctz(bsz);
-  const size_t plane = (size_t)d.B * d.nb_cap * 128;
-  const int ntc = (nb + 15) / 16;
-  // tile nt: wave w moves parts/rows (i = w, w+4, w+8): part i/4, rows 4(i%4) .. +3
-  auto load_rep = [&](int nt) {
-    uint16_t* slot = s_ring + (nt % 3) * kRepTile;
-#pragma unroll
-    for (int u = 0; u < 3; ++u) {
-      const int i = wv + 4 * u, part = i >> 2, r = 4 * (i & 3) + (lane >> 4);
-      const int beta = min(nt * 16 + r, d.nb_cap - 1);
-      const uint16_t* src = rep3 + part * plane + ((size_t)b * d.nb_cap + beta) * 128 + (((lane & 15) ^ r) * 8);
-      g2lds16(src, lds_addr(slot + part * 2048 + 4 * (i & 3) * 128));
-    }
-  };
-  load_rep(0);
-  if (ntc > 1) load_rep(1);
-  for (int nt = 0; nt < ntc; ++nt) {
-    wait_vm(nt + 1 < ntc, 3);
-    lds_sync();  // every wave's share of tile nt has landed; slot (nt+2)%3 is free
-    if (nt + 2 < ntc) load_rep(nt + 2);
-    const uint16_t* slot = s_ring + (nt % 3) * kRepTile;
-    f32x4 acc[4];
-#pragma unroll
-    for (int ht = 0; ht < 4; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int part = 0; part < 3; ++part)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8 bf = frag(slot + part * 2048, s);
-#pragma unroll
-        for (int ht = 0; ht < 4; ++ht)
-          acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ht][s], bf, acc[ht], 0, 0, 0);
-      }
-    const float x = head_sum(acc);
-    const int beta = nt * 16 + c;
-    if (g == 0 && beta < nb) sc[beta] = beta * bsz < valid ? x : kNeg;
-  }
-  __syncthreads();  // the rep ring is free for the key rings
-  const int nrc = (nb + 63) / 64;
-  uint32_t key[kRowR];
-#pragma unroll
-  for (int r = 0; r < kRowR; ++r) {
-    const int i = 64 * r + lane;
-    key[r] = (r < nrc && i < nb) ? score_key(sc[i]) : 0u;
-  }
   int* blk = s_blk[wv];
-  wave_emit_topk(key, nrc, si.Kb, s_hist[wv], [&](int slot, int r) { blk[slot] = 64 * r + lane; });
-  if (blkrow && live)
-    for (int i = lane; i < si.Kb; i += 64) blkrow[i] = blk[i];
+  uint32_t key[kRowR];
+  if (!flat_here) {
+    // ---- coarse scores of blocks 16nt + c (eligible iff the block's first row is visible)
+    const size_t plane = (size_t)d.B * d.nb_cap * 128;
+    const int ntc = (nb + 15) / 16;
+    // tile nt: wave w moves parts/rows (i = w, w+4, w+8): part i/4, rows 4(i%4) .. +3
+    auto load_rep = [&](int nt) {
+      uint16_t* slot = s_ring + (nt % 3) * kRepTile;
+#pragma unroll
+      for (int u = 0; u < 3; ++u) {
+        const int i = wv + 4 * u, part = i >> 2, r = 4 * (i & 3) + (lane >> 4);
+        const int beta = min(nt * 16 + r, d.nb_cap - 1);
+        const uint16_t* src = rep3 + part * plane + ((size_t)b * d.nb_cap + beta) * 128 + (((lane & 15) ^ r) * 8);
+        g2lds16(src, lds_addr(slot + part * 2048 + 4 * (i & 3) * 128));
+      }
+    };
+    load_rep(0);
+    if (ntc > 1) load_rep(1);
+    for (int nt = 0; nt < ntc; ++nt) {
+      wait_vm(nt + 1 < ntc, 3);
+      lds_sync();  // every wave's share of tile nt has landed; slot (nt+2)%3 is free
+      if (nt + 2 < ntc) load_rep(nt + 2);
+      const uint16_t* slot = s_ring + (nt % 3) * kRepTile;
+      f32x4 acc[4];
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int part = 0; part < 3; ++part)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8 bf = frag(slot + part * 2048, s);
+#pragma unroll
+          for (int ht = 0; ht < 4; ++ht)
+            acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ht][s], bf, acc[ht], 0, 0, 0);
+        }
+      const float x = head_sum(acc);
+      const int beta = nt * 16 + c;
+      if (g == 0 && beta < nb) sc[beta] = beta * bsz < valid ? x : kNeg;
+    }
+    __syncthreads();  // the rep ring is free for the key rings
+    const int nrc = (nb + 63) / 64;
+#pragma unroll
+    for (int r = 0; r < kRowR; ++r) {
+      const int i = 64 * r + lane;
+      key[r] = (r < nrc && i < nb) ? score_key(sc[i]) : 0u;
+    }
+    wave_emit_topk(key, nrc, si.Kb, s_hist[wv], [&](int slot, int r) { blk[slot] = 64 * r + lane; });
+    if (blkrow && live)
+      for (int i = lane; i < si.Kb; i += 64) blkrow[i] = blk[i];
+  }
 
   // ---- fine scores of the C candidates: candidate cc is row blk[cc / b]*b + cc % b
-  const int C = si.Kb * bsz;
+  const int C = flat_here ? si.Np : si.Kb * bsz;
   const int ntf = (C + 15) / 16;
   auto cand = [&](int cc) {
     cc = min(cc, C - 1);
-    return (blk[cc >> lbsz] << lbsz) + (cc & (bsz - 1));
+    return flat_here ? cc : (blk[cc >> lbsz] << lbsz) + (cc & (bsz - 1));
   };
   // B operand of candidate tile t straight from memory into registers: lane
   // (g, c) takes row cand(16t + c), dims 32s + 8g .. +7 (the k order of q),

@@ -47,13 +47,16 @@ def parse():
 
 
 def kernel_sources_sha():
-    """Hash of the kernel sources, to tell whether stored counters still apply."""
+    """Hash of the kernel sources and the build script (its compiler flags),
+    to tell whether stored counters still apply."""
     import hashlib
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "top_kv_indexer_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+    pkg = os.path.join(ROOT, "top_kv_indexer_amd")
+    csrc = os.path.join(pkg, "csrc")
+    files = [os.path.join(csrc, f) for f in sorted(os.listdir(csrc))] + [os.path.join(pkg, "build.py")]
+    for path in files:
+        with open(path, "rb") as fh:
+            h.update(os.path.basename(path).encode() + fh.read())
     return h.hexdigest()[:16]
 
 
@@ -283,7 +286,8 @@ def main():
         ids = In[b].reshape(-1)
         uniq += len(np.unique(ids[(ids >= 0) & (ids < int(x["Np"][b]))]))
         uniq += int(x["Wl"][b]) if w.window else 0
-    flat_seqs = [int(v) == hisa.PATH_FLAT for v in path.cpu().tolist()]
+    # flat_topk_select has no path output: every sequence is on the flat path
+    flat_seqs = [True] * w.B if kind == "flat" else [int(v) == hisa.PATH_FLAT for v in path.cpu().tolist()]
     alg = algorithmic(w, x, unique_kv_rows=uniq, flat_seqs=flat_seqs)
     kernels = {}
     for name, (n, tot) in prof.items():

@@ -21,6 +21,13 @@ namespace hisa {
 
 namespace {
 
+// LDS slot (16-byte units) of chunk ch of a KV or q row whose swizzle is x
+// (0..15): the first 64 chunks (512 dims) XOR x in their low four bits; the
+// chunks past them XOR x inside the row's tail, which the row pitch rounds up
+// to whole 256-byte groups.  16 rows with distinct x then read one chunk from
+// 16 distinct 16-byte slots, conflict free, in the tail as in the body.
+__device__ __forceinline__ int tail_pos(int ch, int x) { return ch < 64 ? (ch ^ x) : 64 + ((ch - 64) ^ x); }
+
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -141,7 +148,7 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
       const int h = wv + NW * u;
       const uint32_t dst = kv_lds + (uint32_t)(((NBUF - 2) * kTile + h) * KPD * 2);
       g2lds16(qg + (size_t)h * DK + (lane ^ sw(h)) * 8, dst);
-      if (DK > 512 && lane < DK / 8 - 64) g2lds16(qg + (size_t)h * DK + 512 + lane * 8, dst + 1024);
+      if (DK > 512 && (lane ^ sw(h)) < DK / 8 - 64) g2lds16(qg + (size_t)h * DK + 512 + (lane ^ sw(h)) * 8, dst + 1024);
     }
   };
   // q fragments from LDS, once every wave's rows have landed (the caller has
@@ -153,7 +160,7 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int ch = 4 * s + g;
-      qf[s] = *(const bf16x8*)(qs + hr * KPD + (ch < 64 ? ch ^ sw(c) : ch) * 8);
+      qf[s] = *(const bf16x8*)(qs + hr * KPD + tail_pos(ch, sw(c)) * 8);
     }
     __syncthreads();  // slots NBUF-2 and NBUF-1 are free again
   };
@@ -199,7 +206,7 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
   const int vsw = sw(vrow);  // rows vrow and vrow + 16 share the swizzle
   auto vaddr = [&](int dt, int hi) {
     const int ch = 2 * dt + ((c & 3) >> 1);
-    return (vrow + 16 * hi) * KPD + (ch < 64 ? ch ^ vsw : ch) * 8 + 4 * (c & 1);
+    return (vrow + 16 * hi) * KPD + tail_pos(ch, vsw) * 8 + 4 * (c & 1);
   };
   // This lane's LDS element offsets inside a ring slot for the K reads of
   // every MFMA k-step and the V reads of every value tile it owns, and of
@@ -212,7 +219,7 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int ch = 4 * s + g;
-    k_el[s] = (dh * 16 + c) * KPD + (ch < 64 ? ch ^ sw(c) : ch) * 8;
+    k_el[s] = (dh * 16 + c) * KPD + tail_pos(ch, sw(c)) * 8;
     if constexpr (NHG == 1) asm volatile("" : "+v"(k_el[s]));
   }
 #pragma unroll
@@ -292,13 +299,13 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
         const int trow = RPW * wvs + r;
         const uint32_t dst = kv_lds + (uint32_t)((slot * kTile + trow) * KPD * 2);
         g2lds16(src + (NHG == 1 ? src_el[r] : (lane ^ sw(trow)) * 8), dst);
-        if (DK > 512 && lane < DK / 8 - 64) g2lds16(src + 512 + lane * 8, dst + 1024);
+        if (DK > 512 && (lane ^ sw(trow)) < DK / 8 - 64) g2lds16(src + 512 + (lane ^ sw(trow)) * 8, dst + 1024);
       }
     };
     auto load_k = [&](const uint16_t* kvb, int s) {  // k-step s of rows 16*dh + c
       if constexpr (NHG == 1) return *(const bf16x8*)(kvb + k_el[s]);
       const int ch = 4 * s + g;
-      return *(const bf16x8*)(kvb + (dh * 16 + c) * KPD + (ch < 64 ? ch ^ sw(c) : ch) * 8);
+      return *(const bf16x8*)(kvb + (dh * 16 + c) * KPD + tail_pos(ch, sw(c)) * 8);
     };
     // S^T of rows 16*dh.. for heads 16*hg.. into score buffer sb; the first
     // KW fragments arrive in ka, the rest are fetched KW steps ahead
@@ -589,7 +596,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_fa(KDims d, c
   // the low four bits, so tiles dt and dt+8 differ by 256 bytes
   auto vaddr = [&](int dt, int hi) {
     const int ch = 2 * dt + ((c & 3) >> 1);
-    if (ch >= 64) return (vrow + 16 * hi) * KPD + ch * 8 + 4 * (c & 1);
+    if (ch >= 64) return (vrow + 16 * hi) * KPD + tail_pos(ch, vsw) * 8 + 4 * (c & 1);
     return (vrow + 16 * hi) * KPD + (((2 * (dt & 7) + ((c & 3) >> 1)) ^ vsw) * 8) + (dt >> 3) * 128 + 4 * (c & 1);
   };
   const uint16_t* pooled_b = pooled_kv + (size_t)b * d.Np_cap * DK;
@@ -627,7 +634,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_fa(KDims d, c
         const int trow = RPW * wvs + r;
         const uint32_t dst = kv_lds + (uint32_t)((slot * kTile + trow) * KPD * 2);
         g2lds16(src + (lane ^ sw(trow)) * 8, dst);
-        if (DK > 512 && lane < DK / 8 - 64) g2lds16(src + 512 + lane * 8, dst + 1024);
+        if (DK > 512 && (lane ^ sw(trow)) < DK / 8 - 64) g2lds16(src + 512 + (lane ^ sw(trow)) * 8, dst + 1024);
       }
     };
     auto wait_loads = [&](int keep) {  // at most `keep` later tiles' loads still in flight
@@ -662,7 +669,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_fa(KDims d, c
         // bits of the chunk index, so chunk (4s+g) ^ sw = 16*(s/4) + ((4*(s%4)+g) ^ sw)
         auto load_k = [&](int rb, int s) {
           const int ch = 4 * s + g;
-          if (ch >= 64) return *(const bf16x8*)(kvb + (rb * 16 + cz) * KPD + ch * 8);
+          if (ch >= 64) return *(const bf16x8*)(kvb + (rb * 16 + cz) * KPD + tail_pos(ch, sw(cz)) * 8);
           return *(const bf16x8*)(kvb + (rb * 16 + cz) * KPD + (((4 * (s & 3) + g) ^ sw(cz)) * 8) + (s >> 2) * 128);
         };
         bf16x8 ka[2][KW / 2];

@@ -1367,6 +1367,8 @@ __global__ __launch_bounds__(256) void k_select_rows(KDims d, const uint16_t* __
 
 // ------------------------------------------------------------------ flat scan
 
+constexpr int kFlatTile = 128;  // key rows per LDS tile of the flat scoring
+
 __device__ __forceinline__ bool flat_active(const KDims& d, const SeqInfo& si) {
   return si.ok && (d.force_path == PATH_FLAT || si.path == PATH_FLAT);
 }
@@ -1377,7 +1379,7 @@ __device__ __forceinline__ bool flat_active(const KDims& d, const SeqInfo& si) {
 // is scored.  Rows are dense (256 B) with 16-byte chunk p of row r holding
 // chunk p ^ (r & 15), so the operand reads (16 rows x one chunk) are
 // conflict free.  Masked entries (p >= V) are written as -1e30.
-__global__ __launch_bounds__(256) void k_flat_scores_mfma(KDims d, int kc, const uint16_t* __restrict__ q_idx,
+__global__ __launch_bounds__(256, 2) void k_flat_scores_mfma(KDims d, int kc, const uint16_t* __restrict__ q_idx,
                                                           const float* __restrict__ w,
                                                           const uint16_t* __restrict__ keys,
                                                           const int* __restrict__ t0,
@@ -1412,19 +1414,20 @@ __global__ __launch_bounds__(256) void k_flat_scores_mfma(KDims d, int kc, const
       for (int i = 0; i < 4; ++i) wl[rr][ht][i] = w[((size_t)b * d.L + jj) * 64 + ht * 16 + 4 * g + i] * d.w_scale;
     }
   }
-  __shared__ __align__(16) uint16_t sk[2][64 * 128];
+  constexpr int TK = kFlatTile;  // key rows per tile
+  __shared__ __align__(16) uint16_t sk[2][TK * 128];
   const uint16_t* kb = keys + (size_t)b * d.Np_cap * 128;
   const uint32_t sk_lds = lds_addr(&sk[0][0]);
-  // wave w moves rows 16w .. 16w+15 of a tile: instruction u covers rows
-  // 16w+4u .. +3, lane l row 16w+4u+l/16 at position l%16 (rows past the
-  // chunk end read a valid row whose scores are never stored)
+  // wave w moves rows (TK/4)w .. of a tile: instruction u covers 4 rows, lane
+  // l row (TK/4)w+4u+l/16 at position l%16 (rows past the chunk end read a
+  // valid row whose scores are never stored)
   auto load_tile = [&](int p0, int buf) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int r = 16 * wv + 4 * u + (lane >> 4);
+    for (int u = 0; u < TK / 16; ++u) {
+      const int r = (TK / 4) * wv + 4 * u + (lane >> 4);
       const int ch = (lane & 15) ^ (r & 15);
       const int pr = min(p0 + r, d.Np_cap - 1);
-      g2lds16(kb + (size_t)pr * 128 + ch * 8, sk_lds + (uint32_t)(buf * 64 * 256 + (16 * wv + 4 * u) * 256));
+      g2lds16(kb + (size_t)pr * 128 + ch * 8, sk_lds + (uint32_t)(buf * TK * 256 + ((TK / 4) * wv + 4 * u) * 256));
     }
   };
   if (p_begin < p_stop) load_tile(p_begin, 0);
@@ -1432,16 +1435,21 @@ __global__ __launch_bounds__(256) void k_flat_scores_mfma(KDims d, int kc, const
 #pragma unroll
   for (int rr = 0; rr < 2; ++rr) srow[rr] = scores + ((size_t)b * d.L + (live[rr] ? jr[rr] : 0)) * d.Np_cap;
   int buf = 0;
-  for (int p0 = p_begin; p0 < p_end; p0 += 64, buf ^= 1) {
+  for (int p0 = p_begin; p0 < p_end; p0 += TK, buf ^= 1) {
     const bool compute = p0 < p_stop;
     if (compute) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0: this wave's rows of the tile
     __syncthreads();  // every wave's rows are in; the other buffer is free
-    if (p0 + 64 < p_stop) load_tile(p0 + 64, buf ^ 1);
-    float x[2] = {kNeg, kNeg};
+    if (p0 + TK < p_stop) load_tile(p0 + TK, buf ^ 1);
+    constexpr int NU = TK / 8;  // units: 16 keys x one row
+    float x[2][TK / 64];
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+      for (int q = 0; q < TK / 64; ++q) x[rr][q] = kNeg;
     if (compute) {
-      // units u = 0..7: keys 16*(u/2) .. +15 of the tile against row u%2; the
-      // MFMAs of unit u+1 are issued before the epilogue of unit u, and the
-      // two rows share each key fragment read from LDS
+      // units u: keys 16*(u/2) .. +15 of the tile against row u%2; the MFMAs
+      // of unit u+1 are issued before the epilogue of unit u, and the two rows
+      // share each key fragment read from LDS
       const uint16_t* skb = sk[buf];
       bf16x8 kf[4];
       f32x4 acc[2][4];
@@ -1462,33 +1470,40 @@ __global__ __launch_bounds__(256) void k_flat_scores_mfma(KDims d, int kc, const
       };
       mma(0, acc[0]);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (u + 1 < 8) mma(u + 1, acc[(u + 1) & 1]);
+      for (int u = 0; u < NU; ++u) {
+        if (u + 1 < NU) mma(u + 1, acc[(u + 1) & 1]);
         float v = 0.f;
 #pragma unroll
         for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
           for (int i = 0; i < 4; ++i) v += relu(acc[u & 1][ht][i]) * wl[u & 1][ht][i];
-        sv[u & 1][u >> 1] = v;
-      }
-      // sum over the four lane rows of all four key groups at once: lane
-      // 16*g + c ends with key 16*g + c of the tile
+        sv[u & 1][(u >> 1) & 3] = v;
+        if ((u & 7) == 7) {
+          // the four 16-key groups of keys 64q .. 64q+63 are in: sum over the
+          // four lane rows of all of them at once, lane 16*g + c ending with
+          // key 64q + 16*g + c of the tile
+          const int q = u >> 3;
 #pragma unroll
-      for (int rr = 0; rr < 2; ++rr) {
-        u32x2 a = __builtin_amdgcn_permlane32_swap(__float_as_uint(sv[rr][0]), __float_as_uint(sv[rr][2]), false,
-                                                   false);
-        const float s02 = __uint_as_float(a.x) + __uint_as_float(a.y);
-        a = __builtin_amdgcn_permlane32_swap(__float_as_uint(sv[rr][1]), __float_as_uint(sv[rr][3]), false, false);
-        const float s13 = __uint_as_float(a.x) + __uint_as_float(a.y);
-        a = __builtin_amdgcn_permlane16_swap(__float_as_uint(s02), __float_as_uint(s13), false, false);
-        const float v = __uint_as_float(a.x) + __uint_as_float(a.y);
-        if (p0 + lane < Vr[rr]) x[rr] = v;
+          for (int rr = 0; rr < 2; ++rr) {
+            u32x2 a = __builtin_amdgcn_permlane32_swap(__float_as_uint(sv[rr][0]), __float_as_uint(sv[rr][2]), false,
+                                                       false);
+            const float s02 = __uint_as_float(a.x) + __uint_as_float(a.y);
+            a = __builtin_amdgcn_permlane32_swap(__float_as_uint(sv[rr][1]), __float_as_uint(sv[rr][3]), false, false);
+            const float s13 = __uint_as_float(a.x) + __uint_as_float(a.y);
+            a = __builtin_amdgcn_permlane16_swap(__float_as_uint(s02), __float_as_uint(s13), false, false);
+            const float vq = __uint_as_float(a.x) + __uint_as_float(a.y);
+            if (p0 + 64 * q + lane < Vr[rr]) x[rr][q] = vq;
+          }
+        }
       }
     }
-    const int p = p0 + lane;
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr)
-      if (live[rr] && p < p_end) srow[rr][p] = x[rr];
+    for (int q = 0; q < TK / 64; ++q) {
+      const int p = p0 + 64 * q + lane;
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr)
+        if (live[rr] && p < p_end) srow[rr][p] = x[rr][q];
+    }
   }
 }
 
@@ -1972,7 +1987,7 @@ hipError_t launch_flat_scores(const KDims& d, bool bf16, const void* q_idx, cons
   if (idx_mfma_ok(d, bf16)) {
     // Few query rows: short key chunks spread the scan over the whole chip;
     // many rows: long chunks keep the queries in registers across more keys.
-    const int kc = d.L <= 8 ? 64 : 2048;
+    const int kc = d.L <= 8 ? kFlatTile : 2048;
     hipLaunchKernelGGL(k_flat_scores_mfma, dim3(cdiv(d.Np_cap, kc), cdiv(d.L, 8), d.B), dim3(256), 0, st, d, kc,
                        (const uint16_t*)q_idx, w, (const uint16_t*)keys, t0, scores);
   } else if (bf16) {

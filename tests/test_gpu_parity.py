@@ -319,6 +319,22 @@ def test_mixed_paths_decode_stream(hisa):
     assert (ws[: counter_bytes(w)].view(torch.int32) == 0).all()
 
 
+def test_decode_stream_many_short_sequences(hisa):
+    # 300 sequences of 1100..1400 pooled rows (about 6000 slabs: the streaming
+    # scan), so each workgroup's share of about 12 slabs crosses into another
+    # sequence: runs of every length from one slab, the steps after the loop
+    # of whole three-slab steps, and one published count per run.
+    rng = np.random.default_rng(5)
+    t0 = [int(v) for v in rng.integers(4400, 5600, size=300)]
+    w = MIXED.with_(name="stream_b300_short", B=300, t0=t0, Np_cap=1400, planted=2, H=4, Dk=64, Dv=64)
+    x, g = inputs(w, 23)
+    say("[run] streaming decode scan over 300 short sequences")
+    I, blk, path = hisa.hisa_select_decode(g["q_idx"], g["w"], g["keys"], g["t0"], **sel_kw(w))
+    torch.cuda.synchronize()
+    assert (parity.to_np(path) == hisa.PATH_HISA).all()
+    check_selection(w, x, I, blk, path, sample=48)
+
+
 @pytest.mark.parametrize("case", [(MIXED, 5), (MIXED_STREAM, 21)], ids=["latency_scan", "streaming_scan"])
 def test_decode_exact_ties(hisa, case):
     # Exact score ties straddle both top-k boundaries of the decode selection:

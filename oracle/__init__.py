@@ -25,7 +25,7 @@ NEG = np.float32(-1e30)
 class _Dims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
         "B", "L", "ratio", "window", "topk", "index_block", "index_keep",
-        "H_i", "D_i", "H", "Dk", "Dv", "Np_cap", "force_flat")]
+        "H_i", "D_i", "H", "Dk", "Dv", "Np_cap", "force_flat", "force_dense")]
 
 
 @dataclass
@@ -44,6 +44,7 @@ class Dims:
     Dv: int = 512
     Np_cap: int = 0
     force_flat: int = 0
+    force_dense: int = 0
 
     def c(self) -> _Dims:
         return _Dims(*(int(getattr(self, f)) for f, _ in _Dims._fields_))

@@ -39,11 +39,13 @@ int orc_visible(int t, int ratio, int Np) {
 
 /* [HiSA issue] "HiSA decode path" / "HiSA batched path" gate conditions and the
  * "Engagement thresholds" table; the sparse-combine section's branch 2 makes
- * Np <= index_topk the dense case.  The force-flat kill-switch ("Implementation
- * plan", item 1) replaces only the hierarchy. */
+ * Np <= index_topk the dense case.  Of the two kill-switches ("Implementation
+ * plan", item 1), force-flat replaces only the hierarchy and force-dense turns
+ * the indexer off altogether (every pooled row goes to the combine). */
 int orc_gate(const orc_dims* d, int Np) {
   int k = imin(d->topk, Np);
   long long bk = (long long)d->index_block * d->index_keep;
+  if (d->force_dense) return ORC_PATH_DENSE;
   if (Np <= d->topk) return ORC_PATH_DENSE;
   if (!d->force_flat && d->index_block > 0 && Np >= bk && bk >= k) return ORC_PATH_HISA;
   return ORC_PATH_FLAT;
@@ -55,10 +57,11 @@ static float finish_score(double acc) {
   return s;
 }
 
-/* [HiSA issue] "Flat selection": s[h] = relu(sum_d q[h,d] * key[d]);
- * score = sum_h s[h] * scale * w[h], with scale = D_i^-1/2 and w already
- * carrying H_i^-1/2 ("The indexer query and per-head weights"); the DSA issue
- * (item 1, Score) writes the same head weight as n_heads^-0.5 * head_dim^-0.5.
+/* [HiSA issue] "Flat selection": per indexer head, the dot product of the
+ * head's query with the key, clipped below at zero; the heads are then added
+ * up, each weighted by its learned weight times 1/sqrt(H_i * D_i) (the H_i
+ * factor from "The indexer query and per-head weights", the D_i factor from
+ * the scoring step; the DSA issue, item 1, Score, states the same product).
  * q_row is (H_i, D_i), w_row is the raw weights_proj output (H_i). */
 float orc_score(const orc_dims* d, const float* q_row, const float* w_row, const float* key) {
   const double c = 1.0 / sqrt((double)d->H_i * (double)d->D_i);
@@ -72,8 +75,8 @@ float orc_score(const orc_dims* d, const float* q_row, const float* w_row, const
   return finish_score(acc);
 }
 
-/* The same head combine against a block-mean representative (HiSA decode path,
- * coarse: cs = relu(q . rep), cscore = sum_h cs * scale * w). */
+/* The same head combine with a block's mean row in place of a key (HiSA
+ * decode path, coarse stage); the mean is given in double. */
 float orc_score_rep(const orc_dims* d, const float* q_row, const float* w_row, const double* rep) {
   const double c = 1.0 / sqrt((double)d->H_i * (double)d->D_i);
   double acc = 0.0;
@@ -86,8 +89,8 @@ float orc_score_rep(const orc_dims* d, const float* q_row, const float* w_row, c
   return finish_score(acc);
 }
 
-/* [HiSA issue] "HiSA decode path", coarse: rep[beta, d] = mean of pooled[p, d]
- * over the b rows p of block beta = [beta*b, (beta+1)*b - 1]. */
+/* [HiSA issue] "HiSA decode path", coarse stage: block beta is the b pooled
+ * rows starting at beta * b; its representative is their elementwise mean. */
 void orc_block_mean(const orc_dims* d, const float* keys_b, int beta, double* rep) {
   const int b = d->index_block;
   for (int e = 0; e < d->D_i; e++) {
@@ -150,8 +153,10 @@ void orc_select_row(const orc_dims* d, const float* q_row, const float* w_row,
   *path = p;
 
   if (p == ORC_PATH_DENSE) {
-    /* Sparse combine, branch 2: every pooled row would be selected. */
-    for (int i = 0; i < Np; i++) I_row[i] = i;
+    /* Sparse combine, branch 2: every pooled row would be selected.  (Under
+     * force-dense with Np > topk the row cannot hold them all; it keeps the
+     * first topk, and callers size the index row to the pooled capacity.) */
+    for (int i = 0; i < Np && i < d->topk; i++) I_row[i] = i;
     return;
   }
 
@@ -182,8 +187,10 @@ void orc_select_row(const orc_dims* d, const float* q_row, const float* w_row,
     for (int i = 0; i < Kb; i++) top_blk[i] = given_blocks[i];
     qsort(top_blk, (size_t)Kb, sizeof(int), by_int_asc);
   } else {
-    /* coarse: score block-mean representatives; a block is eligible iff its
-     * first row is visible (beta * b < valid_len), else -1e30. */
+    /* Coarse stage: each block is represented by the mean of its b key rows
+     * and scored like a key.  For a row of a batched step a block takes part
+     * only when its first pooled row is visible to that row; the others get
+     * the mask value. */
     float* cs = (float*)malloc(sizeof(float) * (size_t)nb);
     int* bid = (int*)malloc(sizeof(int) * (size_t)nb);
     double* rep = (double*)malloc(sizeof(double) * (size_t)d->D_i);
@@ -203,9 +210,11 @@ void orc_select_row(const orc_dims* d, const float* q_row, const float* w_row,
   }
   for (int i = 0; i < Kb; i++) blk_row[i] = top_blk[i];
 
-  /* fine: pos[c] = top_blk[c // b] * b + (c % b); rescore exactly; rows at or
-   * beyond valid_len get -1e30; top-k over the candidates, mapped back to
-   * absolute pooled ids. */
+  /* Fine stage: the candidates are every row of the retained blocks, block
+   * after block in ascending block order (candidate c lies in retained block
+   * c / b at offset c % b inside it).  Each candidate gets its full score,
+   * the ones this row cannot see get the mask value, and the k best
+   * candidates are reported by their absolute pooled row ids. */
   float* fs = (float*)malloc(sizeof(float) * (size_t)C);
   int* pos = (int*)malloc(sizeof(int) * (size_t)C);
   for (int c = 0; c < C; c++) {

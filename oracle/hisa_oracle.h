@@ -35,7 +35,8 @@ extern "C" {
 typedef struct {
   int B, L, ratio, window, topk, index_block, index_keep;
   int H_i, D_i, H, Dk, Dv, Np_cap;
-  int force_flat; /* 1: skip the hierarchy (the "force flat scan" kill-switch) */
+  int force_flat;  /* 1: skip the hierarchy (the "force flat scan" kill-switch) */
+  int force_dense; /* 1: no indexer at all (the dense-fallback kill-switch) */
 } orc_dims;
 
 enum { ORC_PATH_DENSE = 0, ORC_PATH_FLAT = 1, ORC_PATH_HISA = 2 };

@@ -72,6 +72,25 @@ def test_engagement_table():
     # The force-flat switch replaces only the hierarchy.
     assert oracle.gate(Dims(topk=512, force_flat=1), 4096) == PATH_FLAT
     assert oracle.gate(Dims(topk=512, force_flat=1), 300) == PATH_DENSE
+    # The dense-fallback switch turns the indexer off at every length.
+    for Np in (0, 300, 700, 4096, 16384):
+        assert oracle.gate(Dims(topk=512, force_dense=1), Np) == PATH_DENSE
+
+
+def test_force_dense_selects_every_pooled_row():
+    # HiSA issue, Implementation plan item 1 (dense fallback): with the indexer
+    # off, a row's index list is every pooled row, in order, padded with -1
+    # (the index row is sized to the pooled capacity).
+    rng = np.random.default_rng(23)
+    H, D, Np_cap = 2, 4, 40
+    d = Dims(B=2, L=3, ratio=1, topk=Np_cap, H_i=H, D_i=D, index_block=4, index_keep=2, window=0, Np_cap=Np_cap,
+             force_dense=1)
+    q, w, keys, t0 = _rand_problem(rng, 2, 3, Np_cap, H, D, [10, 37])
+    I, blk, path = oracle.select(d, q, w, keys, t0)
+    assert (path == PATH_DENSE).all() and (blk == -1).all()
+    for b, Np in enumerate((13, 40)):
+        for j in range(3):
+            np.testing.assert_array_equal(I[b, j], np.r_[np.arange(Np), -np.ones(Np_cap - Np, int)])
 
 
 # ---------------------------------------------------------------- scoring
@@ -338,6 +357,85 @@ def test_hisa_blocks_are_library_sort_of_cscore():
         np.testing.assert_array_equal(np.sort(blk[0, j]), np.sort(order[:keep]))
 
 
+def _np_score(q_row, w_row, key_or_mean):
+    """The indexer score written out with numpy in float64, rounded once to f32."""
+    H, D = q_row.shape
+    dots = q_row.astype(np.float64) @ np.asarray(key_or_mean, np.float64)
+    return np.float32(np.sum(np.maximum(dots, 0.0) * w_row.astype(np.float64)) / math.sqrt(H * D))
+
+
+def test_scores_of_visible_ids_and_masks():
+    # The tie-band judge: every id visible to row j gets that row's score of
+    # its own key; negative ids and ids at or past V(t0 + j) get the mask.
+    # t0 = 40, ratio 4, L = 6: Np = 11 but rows j < 3 see only 10 rows.
+    rng = np.random.default_rng(21)
+    H, D, r, L, t0 = 3, 8, 4, 6, 40
+    Np, Np_cap = (t0 + L) // r, (t0 + L) // r + 5
+    d = Dims(B=1, L=L, ratio=r, topk=4, H_i=H, D_i=D, index_block=0, window=0, Np_cap=Np_cap)
+    q, w, keys, _ = _rand_problem(rng, 1, L, Np_cap, H, D, [t0])
+    seen_partial = False
+    for j in range(L):
+        V = min(Np, (t0 + j + 1) // r)
+        seen_partial |= V < Np
+        ids = np.array([-3, -1, 0, 1, V - 1, V, V + 1, Np - 1, Np, Np_cap - 1], np.int32)
+        got = oracle.scores_of(d, q[0, j], w[0, j], keys[0], t0, j, ids)
+        for i, p in enumerate(ids.tolist()):
+            if 0 <= p < V:
+                np.testing.assert_allclose(got[i], _np_score(q[0, j], w[0, j], keys[0, p]), rtol=1e-6, atol=1e-7)
+            else:
+                assert got[i] == oracle.NEG, (j, p)
+    assert seen_partial
+
+
+def test_coarse_row_eligibility_and_past_nb_masks():
+    # HiSA batched path: block beta takes part for row j iff its first row is
+    # visible (beta * b < V), so a partly visible block is scored; blocks past
+    # nb = floor(Np / b) (allocated capacity, or the incomplete tail block) are
+    # masked as well, and their block means read as zero.
+    rng = np.random.default_rng(22)
+    H, D, b, L, t0 = 2, 8, 4, 12, 30
+    Np, Np_cap = t0 + L, 60          # ratio 1: V = t0 + j + 1 = 31 .. 42; nb = 10 < nb_cap = 15
+    nb = Np // b
+    d = Dims(B=1, L=L, ratio=1, topk=8, H_i=H, D_i=D, index_block=b, index_keep=3, window=0, Np_cap=Np_cap)
+    q, w, keys, t0a = _rand_problem(rng, 1, L, Np_cap, H, D, [t0])
+    cs, rep = oracle.block_scores(d, q, w, keys, t0a)
+    partly, tail = 0, 0
+    for j in range(L):
+        V = t0 + j + 1
+        row = oracle.coarse_row(d, q[0, j], w[0, j], keys[0], t0, j)
+        np.testing.assert_array_equal(row, cs[0, j])
+        for beta in range(Np_cap // b):
+            if beta < nb and beta * b < V:
+                mean = keys[0, beta * b:(beta + 1) * b].astype(np.float64).mean(axis=0)
+                np.testing.assert_allclose(cs[0, j, beta], _np_score(q[0, j], w[0, j], mean), rtol=1e-6, atol=1e-7)
+                partly += (beta + 1) * b > V
+            else:
+                assert cs[0, j, beta] == oracle.NEG, (j, beta)
+                tail += beta == nb and beta * b < V
+    assert partly > 0 and tail > 0
+    np.testing.assert_allclose(rep[0, :nb], keys[0, :nb * b].astype(np.float64).reshape(nb, b, D).mean(axis=1),
+                               rtol=1e-6, atol=1e-7)
+    assert (rep[0, nb:] == 0).all()
+
+
+def test_hisa_select_uses_the_coarse_masks():
+    # With index_keep above the number of eligible blocks, the retained blocks
+    # of a row are all its eligible blocks plus the lowest masked ones: the
+    # selector's own mask must equal the coarse stage's (a library sort of the
+    # coarse scores, ties to the lowest block).
+    rng = np.random.default_rng(24)
+    H, D, b, L, t0 = 2, 8, 4, 10, 22
+    Np = t0 + L                      # 32, nb = 8; row j sees 23 + j rows
+    d = Dims(B=1, L=L, ratio=1, topk=6, H_i=H, D_i=D, index_block=b, index_keep=7, window=0, Np_cap=Np)
+    q, w, keys, t0a = _rand_problem(rng, 1, L, Np, H, D, [t0])
+    _, blk, path = oracle.select(d, q, w, keys, t0a)
+    cs, _ = oracle.block_scores(d, q, w, keys, t0a)
+    assert (path == PATH_HISA).all()
+    for j in range(L):
+        order = np.lexsort((np.arange(cs.shape[-1]), -cs[0, j]))
+        np.testing.assert_array_equal(np.sort(blk[0, j]), np.sort(order[:7]))
+
+
 def test_selectors_dense_case_and_given_blocks():
     rng = np.random.default_rng(12)
     H, D = 2, 4
@@ -498,10 +596,20 @@ def test_pins_catch_planted_mistakes(tmp_path):
         "no sink": ("double Z = sinks ? exp((double)sinks[h] - m) : 0.0;", "double Z = 0.0;"),
         "window too wide": ("const int s_lo = imax(ls, t - d->window + 1);", "const int s_lo = imax(ls, t - d->window);"),
         "no pooled re-mask": ("if (id >= 0 && id < V) rows[n++]", "if (id >= 0) rows[n++]"),
+        "scores_of masks at Np": ("out[i] = (p >= 0 && p < valid) ?", "out[i] = (p >= 0 && p < Np) ?"),
+        "scores_of ignores the row": ("const int valid = orc_visible(t0 + j, d->ratio, Np);\n  for (int i = 0; i < n; i++) {",
+                                      "const int valid = orc_visible(t0, d->ratio, Np);\n  for (int i = 0; i < n; i++) {"),
+        "coarse row without eligibility": ("if (beta < nb && beta * b < valid) {", "if (beta < nb) {"),
+        "coarse row without nb mask": ("if (beta < nb && beta * b < valid) {", "if (beta * b < valid) {"),
+        "coarse eligibility on the last row": ("if (beta * b < valid) {\n        orc_block_mean",
+                                               "if (beta * b + b <= valid) {\n        orc_block_mean"),
+        "force-dense ignored": ("if (d->force_dense) return ORC_PATH_DENSE;", ""),
     }
     import importlib
     import sys
-    tests = [test_score_hand_example, test_score_two_head_hand_example, test_score_single_head_is_relu_of_library_dot,
+    tests = [test_scores_of_visible_ids_and_masks, test_coarse_row_eligibility_and_past_nb_masks,
+             test_hisa_select_uses_the_coarse_masks, test_engagement_table, test_force_dense_selects_every_pooled_row,
+             test_score_hand_example, test_score_two_head_hand_example, test_score_single_head_is_relu_of_library_dot,
              test_score_one_hot_weight_picks_one_head, test_score_invariants, test_block_mean_is_library_mean,
              test_coarse_score_is_mean_of_pre_relu_dots, test_topk_matches_library_sort,
              test_flat_hand_example_decode_and_batched, test_flat_equals_brute_force_sort_with_and_without_cutoff,

@@ -47,10 +47,15 @@ enum hisa_dtype { HISA_F32 = 0, HISA_BF16 = 1 };
 /* mode: HISA_MODE_AUTO runs the gate of the HiSA issue (dense when Np <= topk;
  * HiSA when index_block > 0, Np >= index_block*index_keep and
  * index_block*index_keep >= min(topk, Np); flat otherwise).
- * HISA_MODE_FORCE_FLAT is the "force the flat scan" switch of the HiSA issue's
- * implementation plan: it replaces the hierarchy by the flat scan (the dense
- * case Np <= topk is kept). */
-enum hisa_mode { HISA_MODE_AUTO = 0, HISA_MODE_FORCE_FLAT = 1 };
+ * The other two are the kill-switches of the HiSA issue's implementation plan
+ * (item 1).  HISA_MODE_FORCE_FLAT replaces the hierarchy by the flat scan (the
+ * dense case Np <= topk is kept).  HISA_MODE_FORCE_DENSE turns the indexer off
+ * (the dense fallback): hisa_select_decode / hisa_select_prefill score
+ * nothing and list every pooled row, I = 0..Np-1 padded with -1, so the
+ * attention call attends to all of them; topk is then the width of I and must
+ * be >= Np_cap (HISA_ERR_ARG otherwise), and no workspace is needed.
+ * hisa_block_scores and flat_topk_select ignore the mode's switches. */
+enum hisa_mode { HISA_MODE_AUTO = 0, HISA_MODE_FORCE_FLAT = 1, HISA_MODE_FORCE_DENSE = 2 };
 
 enum hisa_path { HISA_PATH_INVALID = -1, HISA_PATH_DENSE = 0, HISA_PATH_FLAT = 1, HISA_PATH_HISA = 2 };
 
@@ -121,7 +126,9 @@ int hisa_block_scores(const hisa_dims* d, const void* q_idx, const float* w, con
  * Workspace: its first B * (1 + ceil(ceil(Np_cap / 64) / 16)) * 64 bytes are
  * arrival counters of the fused scan + selection kernel.  They must be zero
  * before the first call that uses the workspace (zero-fill it once after
- * allocating it); every call leaves them zero.  Two calls that share a workspace must not run at
+ * allocating it); every call leaves them zero.  The region grows with B and
+ * Np_cap: before a call with a larger region than the previous calls on the
+ * workspace, zero it again.  Two calls that share a workspace must not run at
  * the same time (on different streams); calls on one stream are ordered.
  *   I_out       (B, 1, topk) int32.
  *   top_blk_out (B, 1, index_keep) int32 or NULL: the retained blocks (HiSA

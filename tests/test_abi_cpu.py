@@ -57,8 +57,35 @@ def test_workspace_sizes(lib):
     assert hisa.workspace_bytes(hisa.OP_ATTENTION, d) == 10 * 64 * 514 * 4
     # many rows: no split, no workspace
     assert hisa.workspace_bytes(hisa.OP_ATTENTION, dims(L=2048, Wl_cap=2175)) == 0
-    n = hisa.workspace_bytes(hisa.OP_SELECT_PREFILL, dims(L=2048))
-    assert n >= 2048 * 16384 * 4 + 2048 * 256 * 4
+    # batched selection, sized by the kernels that run: one query row per wave
+    # needs only the block means (f32 + three bf16 parts) ...
+    rep = 256 * 128 * 4 + 3 * 256 * 128 * 2
+    assert hisa.workspace_bytes(hisa.OP_SELECT_PREFILL, dims(L=2048)) == rep
+    # ... plus the flat scores of every row when the flat scan runs (forced flat)
+    assert hisa.workspace_bytes(hisa.OP_SELECT_PREFILL, dims(L=2048, mode=hisa.MODE_FORCE_FLAT)) == (
+        rep + 2048 * 16384 * 4)
+    # candidates past one wave's registers: coarse scores per row and the flat scan
+    assert hisa.workspace_bytes(hisa.OP_SELECT_PREFILL, dims(L=2048, index_keep=64)) == (
+        rep + 2048 * 256 * 4 + 2048 * 16384 * 4)
+    # no hierarchy: only the flat scan
+    assert hisa.workspace_bytes(hisa.OP_SELECT_PREFILL, dims(L=4, index_block=0, Np_cap=1000)) == (
+        (4 * 1000 * 4 + 255) // 256 * 256)
+    # the dense fallback fills I and needs nothing
+    for op in (hisa.OP_SELECT_DECODE, hisa.OP_SELECT_PREFILL):
+        assert hisa.workspace_bytes(op, dims(topk=16384, mode=hisa.MODE_FORCE_DENSE)) == 0
+
+
+def test_force_dense_needs_room_for_every_pooled_row(lib):
+    d = dims(topk=512, mode=hisa.MODE_FORCE_DENSE)
+    for op in (hisa.OP_SELECT_DECODE, hisa.OP_SELECT_PREFILL):
+        assert lib.hisa_workspace_bytes(op, ctypes.byref(d)) == ctypes.c_size_t(-1).value
+        assert "FORCE_DENSE" in hisa.last_error()
+    fake = ctypes.c_void_p(256)
+    rc = lib.hisa_select_decode(ctypes.byref(d), fake, fake, fake, fake, fake, None, None, None, 0, None)
+    assert rc == -1
+    # the switches do not apply to the coarse stage alone or to the flat indexer
+    assert hisa.workspace_bytes(hisa.OP_BLOCK_SCORES, d) > 0
+    assert hisa.workspace_bytes(hisa.OP_FLAT_TOPK, d) > 0
 
 
 @pytest.mark.parametrize("op,kw,code", [
@@ -68,6 +95,7 @@ def test_workspace_sizes(lib):
     (hisa.OP_SELECT_DECODE, dict(index_keep=2000), -1),
     (hisa.OP_SELECT_DECODE, dict(idx_dtype=7), -2),
     (hisa.OP_SELECT_DECODE, dict(topk=0), -1),
+    (hisa.OP_SELECT_DECODE, dict(mode=3), -1),
     (hisa.OP_SELECT_DECODE, dict(B=0), -1),
     (hisa.OP_SELECT_DECODE, dict(Np_cap=0), -1),
     (hisa.OP_SELECT_DECODE, dict(ratio=4, Np_cap=600000000), -4),

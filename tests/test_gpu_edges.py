@@ -1,0 +1,253 @@
+"""Edge cases of the HIP library against the CPU oracle, through the C ABI:
+no pooled rows at all (local-only attention), ratio-128 layers (dense pooled
+lists and HiSA on a long ratio-128 stream), a ratio that is not a power of
+two, value rows narrower than key rows (Dv < Dk), HiSA blocks of 8, 16 and 32
+rows on both decode scans, a 1024-sequence streaming decode scan, the dense
+fallback switch, and a decode step replayed from a captured HIP graph."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import parity
+from tests.test_gpu_parity import (EARLY, MIXED, MIXED_STREAM, check_attention, check_selection, counter_bytes,
+                                   inputs, odims, run_attention, sel_kw)
+from top_kv_indexer_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def hisa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from top_kv_indexer_amd import hisa as h
+    h.lib()
+    return h
+
+
+def selection_then_attention(hisa, w, x, g, prefill, sample=None, att_sample=None):
+    fn = hisa.hisa_select_prefill if prefill else hisa.hisa_select_decode
+    I, blk, path = fn(g["q_idx"], g["w"], g["keys"], g["t0"], **sel_kw(w))
+    torch.cuda.synchronize()
+    check_selection(w, x, I, blk, path, sample=sample)
+    out = hisa.sparse_local_pooled_attention(g["q"], g["local_kv"], g["pooled_kv"], I, g["sinks"], g["t0"],
+                                             ratio=w.ratio, window=w.window, Dv=w.Dv)
+    torch.cuda.synchronize()
+    say(f"  attention max-abs {check_attention(w, x, I, out, sample=att_sample):.3g}")
+    return parity.to_np(I), parity.to_np(path)
+
+
+# ---------------------------------------------------------------- no pooled rows
+
+NP0 = synth.Workload("np0_local_only", B=3, L=1, ratio=4, window=128, topk=512, index_block=64, index_keep=16,
+                     H_i=64, D_i=128, H=64, Dk=512, Dv=512, bf16=True, t0=[2, 0, 70], planted=0, Np_cap=64)
+
+
+def test_no_pooled_rows_decode(hisa):
+    # HiSA issue, Consuming the selection, branch 1 (Np == 0): the selector
+    # lists nothing and the combine attends to the local window alone
+    # (t0 = 2 and 0: Np = 0 with 3 and 1 local rows; t0 = 70: Np = 17, dense).
+    w = NP0
+    x, g = inputs(w, 41)
+    say("[run] decode with Np = 0")
+    I, path = selection_then_attention(hisa, w, x, g, prefill=False)
+    assert path.tolist() == [hisa.PATH_DENSE] * 3
+    assert (I[:2] == -1).all()
+    np.testing.assert_array_equal(I[2, 0, :17], np.arange(17))
+
+
+def test_no_pooled_rows_prefill(hisa):
+    # t0 = 0, L = 16, ratio 4: Np = 4, and rows 0..2 see no pooled row yet.
+    w = NP0.with_(name="np0_prefill", B=2, L=16, t0=[0, 5])
+    x, g = inputs(w, 42)
+    say("[run] prefill whose first rows see no pooled row")
+    I, path = selection_then_attention(hisa, w, x, g, prefill=True)
+    assert path.tolist() == [hisa.PATH_DENSE] * 2
+
+
+# ---------------------------------------------------------------- ratio 128 and ratio 3
+
+def test_ratio128_layers(hisa):
+    # DeepSeek-V4's ratio-128 layers (HiSA issue, Dependency): Np = 512 at
+    # t0 = 65536 (dense: I = iota), Np = 1093 at t0 = 140000 (HiSA), Np = 0 at
+    # t0 = 100; then a 256-row prefill chunk on the dense branch.
+    w = synth.FLASH_DECODE.with_(name="ratio128_decode_b3", B=3, ratio=128, t0=[65536, 140000, 100], planted=4,
+                                 Np_cap=1100)
+    x, g = inputs(w, 43)
+    say("[run] ratio-128 decode")
+    I, path = selection_then_attention(hisa, w, x, g, prefill=False)
+    assert path.tolist() == [hisa.PATH_DENSE, hisa.PATH_HISA, hisa.PATH_DENSE]
+    np.testing.assert_array_equal(I[0, 0], np.arange(512))
+    w = synth.PREFILL.with_(name="ratio128_prefill_l256", L=256, ratio=128, t0=[65000], Np_cap=512)
+    x, g = inputs(w, 44)
+    say("[run] ratio-128 prefill (dense pooled list, rows see 507..509)")
+    I, path = selection_then_attention(hisa, w, x, g, prefill=True, sample=24, att_sample=24)
+    assert path.tolist() == [hisa.PATH_DENSE]
+    np.testing.assert_array_equal(I[0], np.broadcast_to(np.r_[np.arange(509), -np.ones(3, int)], (256, 512)))
+
+
+def test_ratio3_division(hisa):
+    # A ratio that is not a power of two takes the division in the pooled
+    # count and the visibility: Np = 16384 (HiSA) and 1000 (flat) in decode,
+    # 10021 (HiSA) and 521 (flat) in a 64-row prefill.
+    w = synth.FLASH_DECODE.with_(name="ratio3_decode_b2", B=2, ratio=3, t0=[49152, 3000], planted=8, Np_cap=16384)
+    x, g = inputs(w, 45)
+    say("[run] ratio-3 decode")
+    _, path = selection_then_attention(hisa, w, x, g, prefill=False)
+    assert path.tolist() == [hisa.PATH_HISA, hisa.PATH_FLAT]
+    w = synth.PREFILL.with_(name="ratio3_prefill_b2_l64", B=2, L=64, ratio=3, t0=[30000, 1500], Np_cap=10100)
+    x, g = inputs(w, 46)
+    say("[run] ratio-3 prefill")
+    _, path = selection_then_attention(hisa, w, x, g, prefill=True, sample=32, att_sample=16)
+    assert path.tolist() == [hisa.PATH_HISA, hisa.PATH_FLAT]
+
+
+# ---------------------------------------------------------------- Dv < Dk
+
+@pytest.mark.parametrize("bf16", [True, False], ids=["bf16", "f32"])
+def test_value_narrower_than_key(hisa, bf16):
+    # MLA-style rows: 576-wide keys whose first 512 entries are the value.
+    w = MIXED.with_(name="dv512_dk576", B=2, L=3, H=16, Dk=576, Dv=512, t0=[20000, 9000], bf16=bf16, planted=2)
+    x, g = inputs(w, 47)
+    say(f"[run] attention Dk 576 / Dv 512 ({'bf16' if bf16 else 'f32'})")
+    selection_then_attention(hisa, w, x, g, prefill=True)
+
+
+# ---------------------------------------------------------------- small HiSA blocks
+
+@pytest.mark.parametrize("block,keep", [(8, 64), (16, 32), (32, 16)])
+@pytest.mark.parametrize("scan", ["latency", "streaming"])
+def test_decode_small_blocks(hisa, block, keep, scan):
+    # index_block below 64 on the bf16 MFMA decode scans: blocks of <= 16 rows
+    # are summed across the lanes of one wave, 32-row blocks across two waves.
+    # index_block * index_keep = 512 = topk keeps the HiSA path.  Latency scan:
+    # one sequence of 256 slabs; streaming: 5 sequences of up to 256 slabs.
+    # (Blocks of 16 and 32 rows keep the selection fused into both scans.)
+    if scan == "latency":
+        w = synth.FLASH_DECODE.with_(name=f"flash_b{block}", index_block=block, index_keep=keep, planted=24)
+        seed = 48
+    else:
+        w = MIXED_STREAM.with_(name=f"stream_b{block}", B=5, t0=[65000, 16400, 40000, 30000, 5000], Np_cap=16384,
+                               index_block=block, index_keep=keep, planted=24, H=4, Dk=64, Dv=64)
+        seed = 49
+    x, g = inputs(w, seed)
+    say(f"[run] {scan} decode scan with index_block {block}, keep {keep}")
+    I, blk, path = hisa.hisa_select_decode(g["q_idx"], g["w"], g["keys"], g["t0"], **sel_kw(w))
+    torch.cuda.synchronize()
+    assert (parity.to_np(path) == hisa.PATH_HISA).all()
+    check_selection(w, x, I, blk, path)
+
+
+# ---------------------------------------------------------------- 1024 sequences
+
+def test_decode_stream_b1024(hisa):
+    # The streaming scan's largest batch: 1024 sequences of 1025..1100 pooled
+    # rows (about 18000 slabs).  The end of the last sequence's slab list sits
+    # past every thread's four sequences of the prefix table.
+    rng = np.random.default_rng(50)
+    t0 = [int(v) for v in rng.integers(4100, 4400, size=1024)]
+    w = MIXED.with_(name="stream_b1024", B=1024, t0=t0, Np_cap=1100, planted=2, H=4, Dk=64, Dv=64)
+    x, g = inputs(w, 51)
+    d = hisa.selection_dims(g["q_idx"], g["keys"], ratio=4, topk=512, index_block=64, index_keep=16)
+    ws = torch.zeros(hisa.workspace_bytes(hisa.OP_SELECT_DECODE, d), dtype=torch.uint8, device="cuda")
+    say("[run] streaming decode scan, B = 1024")
+    I, blk, path = hisa.hisa_select_decode(g["q_idx"], g["w"], g["keys"], g["t0"], **sel_kw(w), ws=ws)
+    torch.cuda.synchronize()
+    assert (parity.to_np(path) == hisa.PATH_HISA).all()
+    rows = sorted({(0, 0), (1023, 0), (511, 0)} | {(int(b), 0) for b in rng.choice(1024, 45, replace=False)})
+    check_selection(w, x, I, blk, path, rows=rows)
+    assert (ws[: counter_bytes(w)].view(torch.int32) == 0).all()
+
+
+# ---------------------------------------------------------------- dense fallback switch
+
+def test_force_dense_switch(hisa):
+    # HiSA issue, Implementation plan item 1: with the indexer off, every row
+    # lists all pooled rows (the index width is the pooled capacity) and the
+    # combine is dense attention over the window and every visible pooled row.
+    w = synth.FLASH_DECODE.with_(name="flash_force_dense", B=2, t0=[65536, 20000], planted=0, Np_cap=16384,
+                                 topk=16384)
+    x, g = inputs(w, 52)
+    say("[run] decode, dense fallback")
+    I, blk, path = hisa.hisa_select_decode(g["q_idx"], g["w"], g["keys"], g["t0"], **sel_kw(w, mode=2))
+    out = run_attention(hisa, w, g, I)
+    torch.cuda.synchronize()
+    In = parity.to_np(I)
+    assert (parity.to_np(path) == hisa.PATH_DENSE).all() and (parity.to_np(blk) == -1).all()
+    for b, Np in enumerate(x["Np"].tolist()):
+        np.testing.assert_array_equal(In[b, 0], np.r_[np.arange(Np), -np.ones(16384 - Np, int)])
+    say(f"  attention max-abs {check_attention(w, x, I, out):.3g}")
+    w = EARLY.with_(name="early_force_dense", topk=1100)
+    x, g = inputs(w, 53)
+    say("[run] prefill, dense fallback")
+    I, blk, path = hisa.hisa_select_prefill(g["q_idx"], g["w"], g["keys"], g["t0"], **sel_kw(w, mode=2))
+    out = run_attention(hisa, w, g, I)
+    torch.cuda.synchronize()
+    d = odims(w, x)
+    d.force_dense = 1
+    Io, blko, po = oracle.select(d, x["q_idx"], x["w"], x["keys"], x["t0"])
+    np.testing.assert_array_equal(parity.to_np(I), Io)
+    assert (parity.to_np(path) == hisa.PATH_DENSE).all() and (parity.to_np(blk) == -1).all()
+    say(f"  attention max-abs {check_attention(w, x, I, out, sample=24):.3g}")
+
+
+# ---------------------------------------------------------------- HIP graph replay
+
+def test_decode_step_graph_replay(hisa):
+    # The two calls of a decode step captured once into a HIP graph (outputs
+    # and workspaces allocated beforehand, the selection's counters zeroed
+    # before capture) and replayed three times, with eager work and a
+    # synchronisation between replays: every replay equals the eager step.
+    w = synth.FLASH_DECODE
+    x, g = inputs(w, synth.SEEDS[w.name])
+    dev = torch.device("cuda")
+    sd = hisa.selection_dims(g["q_idx"], g["keys"], ratio=w.ratio, topk=w.topk, index_block=w.index_block,
+                             index_keep=w.index_keep)
+    ws_sel = torch.zeros(hisa.workspace_bytes(hisa.OP_SELECT_DECODE, sd), dtype=torch.uint8, device=dev)
+    I = torch.empty((1, 1, w.topk), dtype=torch.int32, device=dev)
+    blk = torch.empty((1, 1, w.index_keep), dtype=torch.int32, device=dev)
+    path = torch.empty((1,), dtype=torch.int32, device=dev)
+    ad = hisa.attention_dims(g["q"], g["local_kv"], g["pooled_kv"], I, ratio=w.ratio, window=w.window)
+    ws_att = torch.zeros(max(hisa.workspace_bytes(hisa.OP_ATTENTION, ad), 256), dtype=torch.uint8, device=dev)
+    out = torch.empty((1, 1, w.H, w.Dv), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        hisa.hisa_select_decode(g["q_idx"], g["w"], g["keys"], g["t0"], **sel_kw(w), I=I, top_blk=blk, path=path,
+                                ws=ws_sel)
+        hisa.sparse_local_pooled_attention(g["q"], g["local_kv"], g["pooled_kv"], I, g["sinks"], g["t0"],
+                                           ratio=w.ratio, window=w.window, out=out, ws=ws_att)
+
+    say("[run] eager decode step")
+    step()
+    torch.cuda.synchronize()
+    I_ref, out_ref = I.clone(), out.clone()
+    check_attention(w, x, I_ref, out_ref)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    say("[run] capture")
+    with torch.cuda.graph(graph, stream=s):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        I.fill_(-7)
+        out.fill_(0.5)
+        torch.cuda.synchronize()
+        say(f"[run] replay {rep}")
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(I, I_ref), rep
+        assert torch.equal(out, out_ref), rep
+        step()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(I, I_ref) and torch.equal(out, out_ref)
+    assert (ws_sel[: counter_bytes(w.with_(Np_cap=int(x["Np_cap"])))].view(torch.int32) == 0).all()

@@ -72,13 +72,55 @@ def rows_of(w, sample):
     return sorted(picks)
 
 
-def check_selection(w, x, I, blk, path, mode=0, sample=None):
+def oracle_rows(d, x, rows):
+    """The oracle's selection of each (b, j) in rows, on host threads (the C
+    oracle releases the GIL)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    def one(bj):
+        b, j = bj
+        return oracle.select_row(d, x["q_idx"][b, j], x["w"][b, j], x["keys"][b], int(x["t0"][b]), j)
+
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        return dict(zip(rows, ex.map(one, rows)))
+
+
+def check_selection(w, x, I, blk, path, mode=0, sample=None, rows=None):
     d = odims(w, x, force_flat=mode)
     I, blk, path = parity.to_np(I), parity.to_np(blk), parity.to_np(path)
-    for b, j in rows_of(w, sample):
-        Io, blko, po = oracle.select_row(d, x["q_idx"][b, j], x["w"][b, j], x["keys"][b], int(x["t0"][b]), j)
+    rows = rows if rows is not None else rows_of(w, sample)
+    ref = oracle_rows(d, x, rows)
+    for b, j in rows:
+        Io, blko, po = ref[(b, j)]
         assert path[b] == po, (b, path[b], po)
         parity.check_selection_row(d, x, b, j, I[b, j], blk[b, j] if blk is not None else None, po, Io, blko, po)
+
+
+def slot_rows(L, per_slot=8, seed=7, slots=8):
+    """Query rows of a single sequence covering every row slot of an 8-row (or
+    4-row) workgroup several times, plus the first and last workgroups whole."""
+    rng = np.random.default_rng(seed)
+    js = set(range(min(slots, L))) | set(range(max(0, L - slots), L))
+    for sl in range(slots):
+        cand = np.arange(sl, L, slots)
+        js |= set(rng.choice(cand, size=min(per_slot, len(cand)), replace=False).tolist())
+    return [(0, int(j)) for j in sorted(js)]
+
+
+def check_rows_invariants(I, t0, ratio, topk, Np):
+    """All rows of a one-sequence flat or HiSA selection whose rows all see at
+    least k pooled rows: ids ascending, unique, visible, exactly k of them."""
+    I = parity.to_np(I)[0]
+    L = I.shape[0]
+    V = np.minimum(Np, (t0 + np.arange(L) + 1) // ratio)
+    k = np.minimum(topk, V)
+    valid = I >= 0
+    assert (valid.sum(axis=1) == k).all()
+    assert (np.where(valid, I, -1) < V[:, None]).all()
+    # ascending and unique among the valid entries (which come first)
+    assert (valid[:, :-1] | ~valid[:, 1:]).all(), "-1 padding before a valid id"
+    d = np.diff(I, axis=1)
+    assert ((d > 0) | ~valid[:, 1:]).all()
 
 
 def check_attention(w, x, I, out, sample=None, tol=None):
@@ -140,15 +182,20 @@ def test_prefill_selection_and_attention(hisa):
     I, blk, path = hisa.hisa_select_prefill(g["q_idx"], g["w"], g["keys"], g["t0"], **sel_kw(w))
     torch.cuda.synchronize()
     assert (parity.to_np(path) == hisa.PATH_HISA).all()
-    check_selection(w, x, I, blk, path, sample=40)
-    # causality on every row: all selected ids are visible (>= k rows visible here)
-    In = parity.to_np(I)
+    # every row: ascending, unique, visible, k of them (every row sees >= k rows here)
+    check_rows_invariants(I, int(x["t0"][0]), w.ratio, w.topk, int(x["Np"][0]))
+    # retained blocks of every row: ascending, eligible (first row visible)
+    Bn = parity.to_np(blk)[0]
     V = (int(x["t0"][0]) + np.arange(w.L) + 1) // w.ratio
-    assert (In[0] < V[:, None]).all() and (In >= 0).all()
+    assert (np.diff(Bn, axis=1) > 0).all() and (Bn * w.index_block < V[:, None]).all()
+    # the oracle on rows covering each of the four row slots of a workgroup
+    rows = slot_rows(w.L, per_slot=16, slots=4)
+    assert len(rows) >= 64
+    check_selection(w, x, I, blk, path, rows=rows)
     say(f"[run] sparse_local_pooled_attention {w.name}")
     out = run_attention(hisa, w, g, I)
     torch.cuda.synchronize()
-    say(f"  max-abs {check_attention(w, x, I, out, sample=24):.3g}")
+    say(f"  max-abs {check_attention(w, x, I, out, sample=64):.3g}")
 
 
 @pytest.mark.parametrize("w", [synth.DSA_DECODE, synth.DSA_PREFILL], ids=lambda w: w.name)
@@ -157,16 +204,26 @@ def test_flat_dsa(hisa, w):
     say(f"[run] flat_topk_select {w.name}")
     I = hisa.flat_topk_select(g["q_idx"], g["w"], g["keys"], g["t0"], ratio=w.ratio, topk=w.topk)
     torch.cuda.synchronize()
-    d = odims(w, x)
+    d = dataclasses.replace(odims(w, x), index_block=0)
     In = parity.to_np(I)
-    for b, j in rows_of(w, 5):
+    if w.L > 1:
+        # every row: ascending, unique, visible, exactly k
+        check_rows_invariants(I, int(x["t0"][0]), w.ratio, w.topk, int(x["Np"][0]))
+        # the oracle on 64+ rows covering all 8 row slots of a flat-scoring workgroup
+        rows = slot_rows(w.L, per_slot=7, slots=8)
+        assert len(rows) >= 64
+    else:
+        rows = rows_of(w, None)
+    say(f"  oracle on {len(rows)} rows")
+    ref = oracle_rows(d, x, rows)
+    for b, j in rows:
         q, ww, kb, t0 = x["q_idx"][b, j], x["w"][b, j], x["keys"][b], int(x["t0"][b])
-        Io, _, _ = oracle.select_row(dataclasses.replace(d, index_block=0), q, ww, kb, t0, j)
-        parity.compare_sets(In[b, j], Io, lambda ids: oracle.scores_of(d, q, ww, kb, t0, j, ids), what=f"({b},{j})")
+        parity.compare_sets(In[b, j], ref[(b, j)][0], lambda ids: oracle.scores_of(d, q, ww, kb, t0, j, ids),
+                            what=f"({b},{j})")
     say(f"[run] sparse_local_pooled_attention {w.name}")
     out = run_attention(hisa, w, g, I)
     torch.cuda.synchronize()
-    say(f"  max-abs {check_attention(w, x, I, out, sample=3):.3g}")
+    say(f"  max-abs {check_attention(w, x, I, out, sample=16):.3g}")
 
 
 def test_flat_topk_long_rows_masked_and_ties(hisa):
@@ -200,22 +257,34 @@ def test_flat_topk_long_rows_masked_and_ties(hisa):
         assert (np.diff(In[b, j][In[b, j] >= 0]) > 0).all()
 
 
-def test_block_scores(hisa):
-    for w in (synth.FLASH_DECODE, synth.TINY_DECODE, synth.PREFILL.with_(L=96)):
-        seed = 77
-        x, g = inputs(w, seed)
-        say(f"[run] hisa_block_scores {w.name}")
-        cs, rep = hisa.hisa_block_scores(g["q_idx"], g["w"], g["keys"], g["t0"], ratio=w.ratio,
-                                         index_block=w.index_block, want_rep=True)
-        torch.cuda.synchronize()
-        d = odims(w, x)
-        cso, repo = oracle.block_scores(d, x["q_idx"], x["w"], x["keys"], x["t0"])
-        np.testing.assert_allclose(parity.to_np(rep), repo, rtol=1e-6, atol=1e-7)
-        csg = parity.to_np(cs)
-        masked = cso == np.float32(-1e30)
-        assert (csg[masked] == np.float32(-1e30)).all()
-        scale = np.abs(cso[~masked]).max()
-        np.testing.assert_allclose(csg[~masked], cso[~masked], rtol=1e-4, atol=1e-5 * scale)
+@pytest.mark.parametrize("case", ["flash_cap_past_np", "tiny_f32", "prefill_l96", "early_rows_ragged"])
+def test_block_scores(hisa, case):
+    # The coarse stage alone, including its masks: blocks past nb (capacity
+    # above the pooled count: flash_cap_past_np, and the shorter sequence of
+    # early_rows_ragged) and blocks whose first row a prefill row cannot see
+    # yet (early_rows_ragged: t0 = 300, ratio 1, so row j sees 301 + j rows,
+    # 5 of 17 blocks on row 0).
+    w = {"flash_cap_past_np": synth.FLASH_DECODE.with_(name="flash_cap20000", Np_cap=20000),
+         "tiny_f32": synth.TINY_DECODE,
+         "prefill_l96": synth.PREFILL.with_(L=96),
+         "early_rows_ragged": EARLY.with_(L=300)}[case]
+    seed = 77
+    x, g = inputs(w, seed)
+    say(f"[run] hisa_block_scores {w.name}")
+    cs, rep = hisa.hisa_block_scores(g["q_idx"], g["w"], g["keys"], g["t0"], ratio=w.ratio,
+                                     index_block=w.index_block, want_rep=True)
+    torch.cuda.synchronize()
+    d = odims(w, x)
+    cso, repo = oracle.block_scores(d, x["q_idx"], x["w"], x["keys"], x["t0"])
+    np.testing.assert_allclose(parity.to_np(rep), repo, rtol=1e-6, atol=1e-7)
+    csg = parity.to_np(cs)
+    masked = cso == np.float32(-1e30)
+    if case in ("flash_cap_past_np", "early_rows_ragged"):
+        assert masked.sum() > 0
+    np.testing.assert_array_equal(csg[masked], cso[masked])
+    assert (csg[~masked] > np.float32(-1e30)).all()
+    scale = np.abs(cso[~masked]).max()
+    np.testing.assert_allclose(csg[~masked], cso[~masked], rtol=1e-4, atol=1e-5 * scale)
 
 
 # ------------------------------------------------------------------ edge cases

@@ -60,11 +60,17 @@ int make_kdims(int op, const hisa_dims* d, KDims* k) {
   kd.index_block = d->index_block; kd.index_keep = d->index_keep; kd.H_i = d->H_i; kd.D_i = d->D_i;
   kd.H = d->H; kd.Dk = d->Dk; kd.Dv = d->Dv; kd.Np_cap = d->Np_cap; kd.Wl_cap = d->Wl_cap; kd.kI = d->kI;
   kd.force_flat = d->mode == HISA_MODE_FORCE_FLAT;
+  kd.force_dense = d->mode == HISA_MODE_FORCE_DENSE;
   kd.ratio_shift = (d->ratio > 0 && (d->ratio & (d->ratio - 1)) == 0) ? __builtin_ctz((unsigned)d->ratio) : -1;
   kd.force_path = -1;
   if (is_sel(op)) {
     if (d->idx_dtype != HISA_F32 && d->idx_dtype != HISA_BF16) return fail(HISA_ERR_DTYPE, "idx_dtype %d", d->idx_dtype);
-    if (d->mode != HISA_MODE_AUTO && d->mode != HISA_MODE_FORCE_FLAT) return fail(HISA_ERR_ARG, "mode = %d", d->mode);
+    if (d->mode != HISA_MODE_AUTO && d->mode != HISA_MODE_FORCE_FLAT && d->mode != HISA_MODE_FORCE_DENSE)
+      return fail(HISA_ERR_ARG, "mode = %d", d->mode);
+    if (d->mode == HISA_MODE_FORCE_DENSE && (op == HISA_OP_SELECT_DECODE || op == HISA_OP_SELECT_PREFILL) &&
+        d->topk < d->Np_cap)
+      return fail(HISA_ERR_ARG, "HISA_MODE_FORCE_DENSE lists every pooled row: topk = %d must be >= Np_cap = %d",
+                  d->topk, d->Np_cap);
     if (d->topk < 1) return fail(HISA_ERR_ARG, "topk = %d must be >= 1", d->topk);
     if (d->H_i < 1 || d->D_i < 1 || d->D_i > 1024) return fail(HISA_ERR_ARG, "H_i = %d, D_i = %d (need D_i in [1, 1024])", d->H_i, d->D_i);
     if (d->index_block < 0 || (d->index_block > 0 && 64 % d->index_block != 0))
@@ -113,6 +119,24 @@ size_t take(Layout& l, size_t bytes) {
   return off;
 }
 
+// Which kernels the batched selection runs (hisa_select_prefill); the
+// workspace holds only what they use.
+struct PrefillPlan {
+  bool rows;         // k_select_rows: one query row per wave (block means as bf16 parts)
+  bool coarse_fine;  // the coarse-score GEMM, then one workgroup per row for top-Kb + fine + top-k
+  bool flat_scan;    // flat scores of every row, then the row top-k (flat sequences)
+};
+PrefillPlan prefill_plan(const KDims& k, bool bf) {
+  PrefillPlan p;
+  p.rows = k.nb_cap > 0 && hisa::select_rows_ok(k, bf);
+  p.coarse_fine = k.nb_cap > 0 && !p.rows;
+  // The row selection also takes the flat sequences when they are short: with
+  // index_block * index_keep >= topk a flat sequence has Np below that product
+  // (at most 1024 where the row selection runs).  Otherwise the flat scan runs.
+  p.flat_scan = !(p.rows && !k.force_flat && (long long)k.index_block * k.index_keep >= k.topk);
+  return p;
+}
+
 Layout layout(int op, const hisa_dims* d, const KDims& k) {
   Layout l;
   const size_t B = (size_t)d->B, L = (size_t)d->L;
@@ -124,19 +148,23 @@ Layout layout(int op, const hisa_dims* d, const KDims& k) {
       l.rep3 = hisa::idx_mfma_ok(k, bf) ? take(l, 3 * B * nb_cap * d->D_i * sizeof(uint16_t)) : 0;
       break;
     case HISA_OP_SELECT_DECODE:
+      if (k.force_dense) break;  // the dense fallback only fills I
       // arrival counters first: the region callers zero once (see hisa.h)
       l.cnt = take(l, hisa::decode_counter_ints(k) * sizeof(int));
       l.fscore = take(l, B * d->Np_cap * sizeof(float));
       l.cscore = take(l, B * std::max<size_t>(nb_cap, 1) * sizeof(float));
       break;
-    case HISA_OP_SELECT_PREFILL:
+    case HISA_OP_SELECT_PREFILL: {
+      if (k.force_dense) break;
+      const PrefillPlan p = prefill_plan(k, bf);
       if (nb_cap > 0) {
         l.rep = take(l, B * nb_cap * d->D_i * sizeof(float));
         l.rep3 = hisa::idx_mfma_ok(k, bf) ? take(l, 3 * B * nb_cap * d->D_i * sizeof(uint16_t)) : 0;
-        l.cscore = take(l, B * L * nb_cap * sizeof(float));
       }
-      l.scores = take(l, B * L * d->Np_cap * sizeof(float));
+      if (p.coarse_fine) l.cscore = take(l, B * L * nb_cap * sizeof(float));
+      if (p.flat_scan) l.scores = take(l, B * L * d->Np_cap * sizeof(float));
       break;
+    }
     case HISA_OP_FLAT_TOPK:
       l.scores = take(l, B * L * d->Np_cap * sizeof(float));
       break;
@@ -254,6 +282,10 @@ int hisa_select_decode(const hisa_dims* d, const void* q_idx, const float* w, co
   if ((rc = check_ptrs({q_idx, w, keys, t0, I_out}, "q_idx, w, keys, t0, I_out"))) return rc;
   const bool bf = d->idx_dtype == HISA_BF16;
   hipStream_t st = (hipStream_t)stream;
+  if (k.force_dense) {
+    hipError_t e = timed("fill_dense", st, [&] { return hisa::launch_fill_dense(k, t0, I_out, top_blk_out, path_out, st); });
+    return e == hipSuccess ? HISA_OK : launch_fail(e, "dense fallback");
+  }
   float* fscore = at<float>(ws, l.fscore);
   float* cscore = at<float>(ws, l.cscore);
   if (hisa::decode_fused_ok(k, bf)) {
@@ -284,14 +316,19 @@ int hisa_select_prefill(const hisa_dims* d, const void* q_idx, const float* w, c
   if ((rc = check_ptrs({q_idx, w, keys, t0, I_out}, "q_idx, w, keys, t0, I_out"))) return rc;
   const bool bf = d->idx_dtype == HISA_BF16;
   hipStream_t st = (hipStream_t)stream;
+  if (k.force_dense) {
+    hipError_t e = timed("fill_dense", st, [&] { return hisa::launch_fill_dense(k, t0, I_out, top_blk_out, path_out, st); });
+    return e == hipSuccess ? HISA_OK : launch_fail(e, "dense fallback");
+  }
   float* cscore = nullptr;
   hipError_t e;
   // one query row per wave when the blocks and candidates fit its registers
-  const bool rows = k.nb_cap > 0 && hisa::select_rows_ok(k, bf);
+  const PrefillPlan plan = prefill_plan(k, bf);
+  const bool rows = plan.rows;
   if (k.nb_cap > 0) {
     float* rep = at<float>(ws, l.rep);
     uint16_t* rep3 = hisa::idx_mfma_ok(k, bf) ? at<uint16_t>(ws, l.rep3) : nullptr;
-    cscore = at<float>(ws, l.cscore);
+    cscore = plan.coarse_fine ? at<float>(ws, l.cscore) : nullptr;
     e = timed("block_mean", st, [&] { return hisa::launch_block_mean(k, bf, false, keys, t0, rep, rep3, st); });
     if (e != hipSuccess) return launch_fail(e, "block mean");
     if (rows) {
@@ -304,11 +341,7 @@ int hisa_select_prefill(const hisa_dims* d, const void* q_idx, const float* w, c
       if (e != hipSuccess) return launch_fail(e, "coarse scores");
     }
   }
-  // The row selection also takes the flat sequences when they are short: with
-  // index_block * index_keep >= topk a flat sequence has Np below that product
-  // (at most 1024 where the row selection runs).  Otherwise the flat scan runs.
-  const bool flat_in_rows = rows && !k.force_flat && (long long)k.index_block * k.index_keep >= k.topk;
-  if (!flat_in_rows) {
+  if (plan.flat_scan) {
     float* scores = at<float>(ws, l.scores);
     e = timed("flat_scores", st, [&] { return hisa::launch_flat_scores(k, bf, q_idx, w, keys, t0, scores, st); });
     if (e != hipSuccess) return launch_fail(e, "flat scores");

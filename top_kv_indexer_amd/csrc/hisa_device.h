@@ -239,7 +239,7 @@ __device__ __forceinline__ SeqInfo seq_info(const KDims& d, int t0) {
   const int bk = d.index_block * d.index_keep;
   if (!s.ok) s.path = PATH_INVALID;
   else if (d.force_path >= 0) s.path = d.force_path;
-  else if (s.Np <= d.topk) s.path = PATH_DENSE;
+  else if (d.force_dense || s.Np <= d.topk) s.path = PATH_DENSE;
   else if (!d.force_flat && d.index_block > 0 && s.Np >= bk && bk >= s.k) s.path = PATH_HISA;
   else s.path = PATH_FLAT;
   return s;

@@ -14,6 +14,7 @@ struct KDims {
   int B, L, ratio, window, topk, index_block, index_keep;
   int H_i, D_i, H, Dk, Dv, Np_cap, Wl_cap, kI;
   int force_flat;  // HISA_MODE_FORCE_FLAT
+  int force_dense; // HISA_MODE_FORCE_DENSE (the selection calls only fill I)
   int force_path;  // -1: run the gate; PATH_FLAT: flat for every valid sequence
   int nb_cap;      // Np_cap / index_block (0 when index_block == 0)
   int ratio_shift; // log2(ratio) when ratio is a power of two, else -1
@@ -56,6 +57,9 @@ hipError_t launch_flat_scores(const KDims& d, bool bf16, const void* q_idx, cons
                               const void* keys, const int* t0, float* scores, hipStream_t st);
 hipError_t launch_topk_rows(const KDims& d, const float* scores, const int* t0, int* I,
                             int* path, hipStream_t st);
+// The dense fallback (indexer off): I = 0..Np-1 padded with -1 on every row.
+hipError_t launch_fill_dense(const KDims& d, const int* t0, int* I, int* top_blk, int* path,
+                             hipStream_t st);
 
 // Attention.  splits > 1 writes partials to ws and merges them.
 int attn_splits(const KDims& d, bool bf16);

@@ -593,9 +593,11 @@ __global__ __launch_bounds__(256) void k_decode_scan_stream(
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int bb = 4 * tid + u;
-      if (bb <= d.B) s_pre[bb] = (int)run;
+      if (bb < d.B) s_pre[bb] = (int)run;
       run += (uint32_t)n[u];
     }
+    // the end of the last sequence (B may be 1024, past every thread's range)
+    if (tid == 0) s_pre[d.B] = (int)total;
     __syncthreads();
   }
   // outputs of the sequences that are not scored
@@ -1876,9 +1878,29 @@ __global__ __launch_bounds__(kTkNT) void k_topk_rows_reg(KDims d, const float* _
   }
 }
 
+// The dense fallback with the indexer switched off (HiSA issue, Implementation
+// plan item 1): every row of every valid sequence lists all Np pooled rows in
+// order (the host checks topk >= Np_cap), padded with -1; no block is kept.
+// One workgroup per (row, sequence).
+__global__ __launch_bounds__(256) void k_fill_dense(KDims d, const int* __restrict__ t0, int* I, int* top_blk,
+                                                    int* path) {
+  const int j = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const SeqInfo si = seq_info(d, t0[b]);
+  const size_t row = (size_t)b * d.L + j;
+  for (int i = tid; i < d.topk; i += 256) I[row * d.topk + i] = (si.ok && i < si.Np) ? i : -1;
+  if (top_blk)
+    for (int i = tid; i < d.index_keep; i += 256) top_blk[row * d.index_keep + i] = -1;
+  if (path && j == 0 && tid == 0) path[b] = si.ok ? PATH_DENSE : PATH_INVALID;
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ launchers
+
+hipError_t launch_fill_dense(const KDims& d, const int* t0, int* I, int* top_blk, int* path, hipStream_t st) {
+  hipLaunchKernelGGL(k_fill_dense, dim3(d.L, d.B), dim3(256), 0, st, d, t0, I, top_blk, path);
+  return hipGetLastError();
+}
 
 static inline unsigned cdiv(long long a, long long b) { return (unsigned)((a + b - 1) / b); }
 

@@ -13,7 +13,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libhisa.so")
 
 F32, BF16 = 0, 1
-MODE_AUTO, MODE_FORCE_FLAT = 0, 1
+MODE_AUTO, MODE_FORCE_FLAT, MODE_FORCE_DENSE = 0, 1, 2
 PATH_INVALID, PATH_DENSE, PATH_FLAT, PATH_HISA = -1, 0, 1, 2
 OP_BLOCK_SCORES, OP_SELECT_DECODE, OP_SELECT_PREFILL, OP_FLAT_TOPK, OP_ATTENTION = range(5)
 
@@ -90,14 +90,37 @@ def _p(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _need(t: torch.Tensor, name: str, ndim: int, dtype=None) -> torch.Tensor:
+def _need(t: torch.Tensor, name: str, ndim: int, dtype=None, shape=None) -> torch.Tensor:
+    """Checks one tensor argument; shape entries that are None are free."""
+    if not isinstance(t, torch.Tensor):
+        raise HisaError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
     if t.dim() != ndim:
         raise HisaError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
-    if not t.is_contiguous():
-        raise HisaError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise HisaError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None:
+        for ax, (have, want) in enumerate(zip(t.shape, shape)):
+            if want is not None and have != want:
+                raise HisaError(f"{name} has shape {tuple(t.shape)}; dim {ax} must be {want}")
+    if not t.is_contiguous():
+        raise HisaError(f"{name} must be contiguous")
     return t
+
+
+def _same_gpu(**tensors) -> torch.device:
+    """Every given tensor on one GPU (checked after the shapes, so shape errors
+    show on any device); returns that device."""
+    dev = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise HisaError(f"{name} must be on a GPU, got {t.device}")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise HisaError(f"{name} is on {t.device}, the other tensors on {dev}")
+    return dev
 
 
 def _stream(dev: torch.device) -> ctypes.c_void_p:
@@ -111,16 +134,30 @@ def workspace_bytes(op: int, d: hisa_dims) -> int:
     return int(n)
 
 
+# One workspace per (device, stream, op), grown on demand and reused by every
+# call of that op on that stream (calls on one stream are ordered, so they
+# never overlap).  The decode selection's arrival counters start zeroed and
+# every call leaves them zero; their region grows with B and Np_cap, so its
+# workspaces are kept per (B, Np_cap) as well.
+_ws_cache = {}
+
+
 def _workspace(op: int, d: hisa_dims, dev: torch.device, ws: Optional[torch.Tensor]):
     n = workspace_bytes(op, d)
     if ws is not None:
-        if ws.numel() * ws.element_size() < n:
-            raise HisaError(f"workspace of {ws.numel() * ws.element_size()} bytes < {n} needed")
-        return ws, ws.numel() * ws.element_size()
+        if ws.numel() < n:
+            raise HisaError(f"workspace of {ws.numel()} bytes < {n} needed")
+        return ws, ws.numel()
     if n == 0:
         return None, 0
-    # zero-filled: the decode selection keeps arrival counters at its start
-    return torch.zeros(n, dtype=torch.uint8, device=dev), n
+    key = (dev.index, torch.cuda.current_stream(dev).cuda_stream, op)
+    if op == OP_SELECT_DECODE:
+        key += (d.B, d.Np_cap)
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < n:
+        buf = torch.zeros(n, dtype=torch.uint8, device=dev)
+        _ws_cache[key] = buf
+    return buf, buf.numel()
 
 
 def selection_dims(q_idx, keys, *, ratio, topk, index_block, index_keep, mode=MODE_AUTO) -> hisa_dims:
@@ -130,22 +167,27 @@ def selection_dims(q_idx, keys, *, ratio, topk, index_block, index_keep, mode=MO
                      idx_dtype=_code(keys), attn_dtype=F32)
 
 
+def _ws_arg(ws):
+    if ws is not None:
+        _need(ws, "ws", 1, torch.uint8)
+    return ws
+
+
 def _sel_args(q_idx, w, keys, t0):
     _need(q_idx, "q_idx", 4)
-    _need(w, "w", 3, torch.float32)
-    _need(keys, "keys", 3, q_idx.dtype)
-    _need(t0, "t0", 1, torch.int32)
+    _code(q_idx)
     B, L, H_i, D_i = q_idx.shape
-    if tuple(w.shape) != (B, L, H_i) or keys.shape[0] != B or keys.shape[2] != D_i or t0.shape[0] != B:
-        raise HisaError("inconsistent selection shapes")
+    _need(w, "w", 3, torch.float32, (B, L, H_i))
+    _need(keys, "keys", 3, q_idx.dtype, (B, None, D_i))
+    _need(t0, "t0", 1, torch.int32, (B,))
     return B, L
 
 
 def hisa_block_scores(q_idx, w, keys, t0, *, ratio, index_block, want_rep=False, ws=None):
     """Coarse stage: returns cscore (B, L, nb_cap) and rep (B, nb_cap, D_i) or None."""
     B, L = _sel_args(q_idx, w, keys, t0)
+    dev = _same_gpu(q_idx=q_idx, w=w, keys=keys, t0=t0, ws=_ws_arg(ws))
     d = selection_dims(q_idx, keys, ratio=ratio, topk=1, index_block=index_block, index_keep=1)
-    dev = keys.device
     nb_cap = keys.shape[1] // max(index_block, 1)
     cs = torch.empty((B, L, nb_cap), dtype=torch.float32, device=dev)
     rep = torch.empty((B, nb_cap, q_idx.shape[3]), dtype=torch.float32, device=dev) if want_rep else None
@@ -157,9 +199,15 @@ def hisa_block_scores(q_idx, w, keys, t0, *, ratio, index_block, want_rep=False,
 
 def _select(fn, op, q_idx, w, keys, t0, ratio, topk, index_block, index_keep, mode, I, top_blk, path, ws):
     B, L = _sel_args(q_idx, w, keys, t0)
+    if I is not None:
+        _need(I, "I", 3, torch.int32, (B, L, topk))
+    if top_blk is not None:
+        _need(top_blk, "top_blk", 3, torch.int32, (B, L, index_keep))
+    if path is not None:
+        _need(path, "path", 1, torch.int32, (B,))
+    dev = _same_gpu(q_idx=q_idx, w=w, keys=keys, t0=t0, I=I, top_blk=top_blk, path=path, ws=_ws_arg(ws))
     d = selection_dims(q_idx, keys, ratio=ratio, topk=topk, index_block=index_block, index_keep=index_keep,
                        mode=mode)
-    dev = keys.device
     if I is None:
         I = torch.empty((B, L, topk), dtype=torch.int32, device=dev)
     if top_blk is None:
@@ -174,7 +222,8 @@ def _select(fn, op, q_idx, w, keys, t0, ratio, topk, index_block, index_keep, mo
 
 def hisa_select_decode(q_idx, w, keys, t0, *, ratio, topk, index_block=64, index_keep=16, mode=MODE_AUTO,
                        I=None, top_blk=None, path=None, ws=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    """Single-token selection; returns I (B,1,topk), top_blk (B,1,index_keep), path (B)."""
+    """Single-token selection; returns I (B,1,topk), top_blk (B,1,index_keep), path (B).
+    A caller-given ws must start with zeroed arrival counters (see include/hisa.h)."""
     return _select(lib().hisa_select_decode, OP_SELECT_DECODE, q_idx, w, keys, t0, ratio, topk, index_block,
                    index_keep, mode, I, top_blk, path, ws)
 
@@ -189,8 +238,10 @@ def hisa_select_prefill(q_idx, w, keys, t0, *, ratio, topk, index_block=64, inde
 def flat_topk_select(q_idx, w, keys, t0, *, ratio, topk, I=None, ws=None) -> torch.Tensor:
     """Flat top-k indexer; returns I (B, L, topk)."""
     B, L = _sel_args(q_idx, w, keys, t0)
+    if I is not None:
+        _need(I, "I", 3, torch.int32, (B, L, topk))
+    dev = _same_gpu(q_idx=q_idx, w=w, keys=keys, t0=t0, I=I, ws=_ws_arg(ws))
     d = selection_dims(q_idx, keys, ratio=ratio, topk=topk, index_block=0, index_keep=1)
-    dev = keys.device
     if I is None:
         I = torch.empty((B, L, topk), dtype=torch.int32, device=dev)
     wsb, n = _workspace(OP_FLAT_TOPK, d, dev, ws)
@@ -207,19 +258,30 @@ def attention_dims(q, local_kv, pooled_kv, I, *, ratio, window, Dv=None) -> hisa
                      idx_dtype=F32, attn_dtype=_code(q))
 
 
+def _attn_args(q, local_kv, pooled_kv, I, sinks, t0, window, Dv, out, ws):
+    _need(q, "q", 4)
+    _code(q)
+    B, L, H, Dk = q.shape
+    Dv = Dk if Dv is None else Dv
+    _need(pooled_kv, "pooled_kv", 3, q.dtype, (B, None, Dk))
+    if local_kv is not None:
+        _need(local_kv, "local_kv", 3, q.dtype, (B, None, Dk))
+    elif window > 0:
+        raise HisaError("local_kv is None but window > 0")
+    _need(I, "I", 3, torch.int32, (B, L, None))
+    _need(t0, "t0", 1, torch.int32, (B,))
+    if sinks is not None:
+        _need(sinks, "sinks", 1, torch.float32, (H,))
+    if out is not None:
+        _need(out, "out", 4, q.dtype, (B, L, H, Dv))
+    return _same_gpu(q=q, local_kv=local_kv, pooled_kv=pooled_kv, I=I, sinks=sinks, t0=t0, out=out, ws=_ws_arg(ws))
+
+
 def sparse_local_pooled_attention(q, local_kv, pooled_kv, I, sinks, t0, *, ratio, window, Dv=None, out=None,
                                   ws=None) -> torch.Tensor:
     """Sparse local + pooled combine; returns out (B, L, H, Dv)."""
-    _need(q, "q", 4)
-    _need(pooled_kv, "pooled_kv", 3, q.dtype)
-    if local_kv is not None:
-        _need(local_kv, "local_kv", 3, q.dtype)
-    _need(I, "I", 3, torch.int32)
-    _need(t0, "t0", 1, torch.int32)
-    if sinks is not None:
-        _need(sinks, "sinks", 1, torch.float32)
+    dev = _attn_args(q, local_kv, pooled_kv, I, sinks, t0, window, Dv, out, ws)
     d = attention_dims(q, local_kv, pooled_kv, I, ratio=ratio, window=window, Dv=Dv)
-    dev = q.device
     if out is None:
         out = torch.empty((d.B, d.L, d.H, d.Dv), dtype=q.dtype, device=dev)
     wsb, n = _workspace(OP_ATTENTION, d, dev, ws)

@@ -138,6 +138,26 @@ int hisa_select_decode(const hisa_dims* d, const void* q_idx, const float* w, co
                        const int32_t* t0, int32_t* I_out, int32_t* top_blk_out, int32_t* path_out,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* hisa_select_decode for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments, kernels and outputs as hisa_select_decode, but
+ * no caller workspace: the library keeps a HISA_DECODE_NOALLOC_MAX_BYTES
+ * workspace per GPU in a static device array (held from the first call on
+ * that GPU until the process ends) and zeroes its arrival counters at the
+ * start of every call, so no zero-fill contract applies.  It never calls
+ * hipMalloc or hipFree.
+ * Limits and errors: dims whose hisa_workspace_bytes(HISA_OP_SELECT_DECODE)
+ * exceeds HISA_DECODE_NOALLOC_MAX_BYTES give HISA_ERR_WORKSPACE (about
+ * B * Np_cap * 4 bytes: e.g. B = 32 at Np_cap = 32768 needs 4.3 MB); the
+ * stream must run on the current device (HISA_ERR_ARG otherwise).
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on
+ * one GPU (different streams, or threads without ordering) race and must not
+ * be issued; calls on one stream are ordered. */
+#define HISA_DECODE_NOALLOC_MAX_BYTES ((size_t)16 << 20)
+int hisa_select_decode_noalloc(const hisa_dims* d, const void* q_idx, const float* w, const void* keys,
+                               const int32_t* t0, int32_t* I_out, int32_t* top_blk_out, int32_t* path_out,
+                               void* stream);
+
 /* Multi-row selection (HiSA issue, HiSA batched path: prefill chunks and
  * multi-token verify; any L >= 1).  Per query row j: valid_len = V(t0+j);
  * blocks with b*beta >= valid_len score -1e30; candidates at or past

@@ -132,3 +132,17 @@ def test_small_workspace_and_null_pointers(lib):
     assert rc == -1 and "aligned" in hisa.last_error()
     rc = lib.flat_topk_select(None, fake, fake, fake, fake, fake, fake, 1 << 30, None)
     assert rc == -1
+
+
+def test_noalloc_decode_rejects_dims_past_its_workspace(lib):
+    # 16 MiB of library-held workspace: B = 32 at Np_cap = 32768 (4.3 MB) fits,
+    # B = 128 at Np_cap = 65536 (about 34 MB) does not and fails before any
+    # GPU call.
+    assert hisa.workspace_bytes(hisa.OP_SELECT_DECODE, dims(B=32, Np_cap=32768)) <= hisa.NOALLOC_MAX_BYTES
+    d = dims(B=128, Np_cap=65536)
+    assert hisa.workspace_bytes(hisa.OP_SELECT_DECODE, d) > hisa.NOALLOC_MAX_BYTES
+    fake = ctypes.c_void_p(256)
+    rc = lib.hisa_select_decode_noalloc(ctypes.byref(d), fake, fake, fake, fake, fake, None, None, None)
+    assert rc == -3 and "noalloc" in hisa.last_error()
+    rc = lib.hisa_select_decode_noalloc(ctypes.byref(dims(L=2)), fake, fake, fake, fake, fake, None, None, None)
+    assert rc == -1

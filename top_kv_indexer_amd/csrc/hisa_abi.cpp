@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -231,6 +232,45 @@ hipError_t timed(const char* name, hipStream_t st, F launch) {
   return e;
 }
 
+// ---- library-held workspace of hisa_select_decode_noalloc
+//
+// A file-scope device array, one copy per GPU, held until the process ends.
+// Host code never uses its name as an address: the device address of each
+// GPU's copy comes from hipGetSymbolAddress, taken once per device with that
+// device current, and only that address reaches kernels.
+constexpr size_t kScratchBytes = HISA_DECODE_NOALLOC_MAX_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (taken on its first use); checks that
+// `st` (NULL: the current device's null stream) runs on the current device.
+int scratch_of_current_device(hipStream_t st, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return launch_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(HISA_ERR_ARG, "device %d is past the %d supported", dev, kMaxDevices);
+  if (st) {
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(st, &sdev);
+    if (e != hipSuccess) return launch_fail(e, "hipStreamGetDevice");
+    if ((int)sdev != dev)
+      return fail(HISA_ERR_ARG, "the stream runs on device %d but device %d is current", (int)sdev, dev);
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return launch_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(HISA_ERR_LAUNCH, "hipGetSymbolAddress(scratch) gave NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return HISA_OK;
+}
+
 int prepare(int op, const hisa_dims* d, KDims* k, Layout* l, void* ws, size_t ws_bytes) {
   int rc = make_kdims(op, d, k);
   if (rc) return rc;
@@ -303,6 +343,32 @@ int hisa_select_decode(const hisa_dims* d, const void* q_idx, const float* w, co
   e = timed("decode_select", st, [&] { return hisa::launch_decode_select(k, fscore, cscore, t0, I_out, top_blk_out, path_out, st); });
   if (e != hipSuccess) return launch_fail(e, "decode select");
   return HISA_OK;
+}
+
+int hisa_select_decode_noalloc(const hisa_dims* d, const void* q_idx, const float* w, const void* keys,
+                               const int32_t* t0, int32_t* I_out, int32_t* top_blk_out, int32_t* path_out,
+                               void* stream) {
+  g_err.clear();
+  KDims k;
+  int rc = make_kdims(HISA_OP_SELECT_DECODE, d, &k);
+  if (rc) return rc;
+  const Layout l = layout(HISA_OP_SELECT_DECODE, d, k);
+  if (l.total > kScratchBytes)
+    return fail(HISA_ERR_WORKSPACE, "hisa_select_decode_noalloc holds %zu bytes of workspace; these dims need %zu",
+                kScratchBytes, l.total);
+  if ((rc = check_ptrs({q_idx, w, keys, t0, I_out}, "q_idx, w, keys, t0, I_out"))) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  void* ws = nullptr;
+  if ((rc = scratch_of_current_device(st, &ws))) return rc;
+  // The array keeps the previous call's contents (possibly scores laid out
+  // for other dims): the arrival counters start from zero on every call.
+  if (!k.force_dense) {
+    hipError_t e = timed("zero_counters", st, [&] {
+      return hisa::launch_zero_ints(at<int>(ws, l.cnt), hisa::decode_counter_ints(k), st);
+    });
+    if (e != hipSuccess) return launch_fail(e, "counter clear");
+  }
+  return hisa_select_decode(d, q_idx, w, keys, t0, I_out, top_blk_out, path_out, ws, kScratchBytes, stream);
 }
 
 int hisa_select_prefill(const hisa_dims* d, const void* q_idx, const float* w, const void* keys, const int32_t* t0,

@@ -57,6 +57,8 @@ hipError_t launch_flat_scores(const KDims& d, bool bf16, const void* q_idx, cons
                               const void* keys, const int* t0, float* scores, hipStream_t st);
 hipError_t launch_topk_rows(const KDims& d, const float* scores, const int* t0, int* I,
                             int* path, hipStream_t st);
+// Zeroes n ints on the stream (n < 2^31).
+hipError_t launch_zero_ints(int* p, size_t n, hipStream_t st);
 // The dense fallback (indexer off): I = 0..Np-1 padded with -1 on every row.
 hipError_t launch_fill_dense(const KDims& d, const int* t0, int* I, int* top_blk, int* path,
                              hipStream_t st);

@@ -1893,9 +1893,22 @@ __global__ __launch_bounds__(256) void k_fill_dense(KDims d, const int* __restri
   if (path && j == 0 && tid == 0) path[b] = si.ok ? PATH_DENSE : PATH_INVALID;
 }
 
+// Zeroes n ints (a fill kernel rather than a memset, so a captured graph holds
+// only kernel nodes).
+__global__ __launch_bounds__(256) void k_zero_ints(int* p, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0;
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ launchers
+
+hipError_t launch_zero_ints(int* p, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(k_zero_ints, dim3(blocks), dim3(256), 0, st, p, (int)n);
+  return hipGetLastError();
+}
 
 hipError_t launch_fill_dense(const KDims& d, const int* t0, int* I, int* top_blk, int* path, hipStream_t st) {
   hipLaunchKernelGGL(k_fill_dense, dim3(d.L, d.B), dim3(256), 0, st, d, t0, I, top_blk, path);

@@ -17,7 +17,8 @@ MODE_AUTO, MODE_FORCE_FLAT, MODE_FORCE_DENSE = 0, 1, 2
 PATH_INVALID, PATH_DENSE, PATH_FLAT, PATH_HISA = -1, 0, 1, 2
 OP_BLOCK_SCORES, OP_SELECT_DECODE, OP_SELECT_PREFILL, OP_FLAT_TOPK, OP_ATTENTION = range(5)
 
-EXPORTS = ("hisa_block_scores", "hisa_select_decode", "hisa_select_prefill", "flat_topk_select",
+EXPORTS = ("hisa_block_scores", "hisa_select_decode", "hisa_select_decode_noalloc", "hisa_select_prefill",
+           "flat_topk_select",
            "sparse_local_pooled_attention", "hisa_workspace_bytes", "hisa_last_error", "hisa_abi_version",
            "hisa_profile_enable", "hisa_profile_collect")
 
@@ -51,11 +52,12 @@ def lib() -> ctypes.CDLL:
         sel = [dp, vp, vp, vp, vp]
         L.hisa_block_scores.argtypes = sel + [vp, vp, vp, sz, vp]
         L.hisa_select_decode.argtypes = sel + [vp, vp, vp, vp, sz, vp]
+        L.hisa_select_decode_noalloc.argtypes = sel + [vp, vp, vp, vp]
         L.hisa_select_prefill.argtypes = sel + [vp, vp, vp, vp, sz, vp]
         L.flat_topk_select.argtypes = sel + [vp, vp, sz, vp]
         L.sparse_local_pooled_attention.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-        for f in ("hisa_block_scores", "hisa_select_decode", "hisa_select_prefill", "flat_topk_select",
-                  "sparse_local_pooled_attention"):
+        for f in ("hisa_block_scores", "hisa_select_decode", "hisa_select_decode_noalloc", "hisa_select_prefill",
+                  "flat_topk_select", "sparse_local_pooled_attention"):
             getattr(L, f).restype = i32
         L.hisa_workspace_bytes.argtypes = [i32, dp]
         L.hisa_workspace_bytes.restype = sz
@@ -226,6 +228,27 @@ def hisa_select_decode(q_idx, w, keys, t0, *, ratio, topk, index_block=64, index
     A caller-given ws must start with zeroed arrival counters (see include/hisa.h)."""
     return _select(lib().hisa_select_decode, OP_SELECT_DECODE, q_idx, w, keys, t0, ratio, topk, index_block,
                    index_keep, mode, I, top_blk, path, ws)
+
+
+NOALLOC_MAX_BYTES = 16 << 20  # HISA_DECODE_NOALLOC_MAX_BYTES
+
+
+def hisa_select_decode_noalloc(q_idx, w, keys, t0, I, top_blk, path, *, ratio, topk, index_block=64, index_keep=16,
+                               mode=MODE_AUTO) -> None:
+    """hisa_select_decode with the library's own per-GPU workspace: the caller
+    passes preallocated outputs I (B,1,topk), top_blk (B,1,index_keep) or None,
+    path (B) or None; nothing is allocated."""
+    B, L = _sel_args(q_idx, w, keys, t0)
+    _need(I, "I", 3, torch.int32, (B, L, topk))
+    if top_blk is not None:
+        _need(top_blk, "top_blk", 3, torch.int32, (B, L, index_keep))
+    if path is not None:
+        _need(path, "path", 1, torch.int32, (B,))
+    dev = _same_gpu(q_idx=q_idx, w=w, keys=keys, t0=t0, I=I, top_blk=top_blk, path=path)
+    d = selection_dims(q_idx, keys, ratio=ratio, topk=topk, index_block=index_block, index_keep=index_keep,
+                       mode=mode)
+    _check(lib().hisa_select_decode_noalloc(ctypes.byref(d), _p(q_idx), _p(w), _p(keys), _p(t0), _p(I), _p(top_blk),
+                                            _p(path), _stream(dev)))
 
 
 def hisa_select_prefill(q_idx, w, keys, t0, *, ratio, topk, index_block=64, index_keep=16, mode=MODE_AUTO,

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define HISA_ABI_VERSION 1
+#define HISA_ABI_VERSION 2
 
 enum hisa_dtype { HISA_F32 = 0, HISA_BF16 = 1 };
 
@@ -73,7 +73,9 @@ enum hisa_op {
   HISA_OP_SELECT_DECODE = 1,
   HISA_OP_SELECT_PREFILL = 2,
   HISA_OP_FLAT_TOPK = 3,
-  HISA_OP_ATTENTION = 4
+  HISA_OP_ATTENTION = 4,
+  HISA_OP_SELECT_DECODE_CACHED = 5,
+  HISA_OP_BLOCK_MEANS_UPDATE = 6
 };
 
 /* Problem sizes (HiSA issue, Configuration table). */
@@ -137,6 +139,41 @@ int hisa_block_scores(const hisa_dims* d, const void* q_idx, const float* w, con
 int hisa_select_decode(const hisa_dims* d, const void* q_idx, const float* w, const void* keys,
                        const int32_t* t0, int32_t* I_out, int32_t* top_blk_out, int32_t* path_out,
                        void* ws, size_t ws_bytes, void* stream);
+
+/* Decode selection on cached block means (HiSA issue, HiSA decode path: the
+ * coarse stage costs O(nb) scores and the fine stage O(Kb * b), so a step need
+ * not read every key; The pooled stream and positions: the pooled stream only
+ * grows in whole windows, so the mean of a complete block never changes).
+ * Same gate, outputs and tie rule as hisa_select_decode (L must be 1), but the
+ * block means come from rep, a caller-owned (B, nb_cap, D_i) f32 cache,
+ * nb_cap = Np_cap / index_block, row beta of sequence b holding the mean of
+ * its pooled key rows beta*b .. beta*b + b - 1 (rows summed in order in f32,
+ * then scaled by 1/b).  Before the call rep must hold every block completed
+ * before this step (all blocks below floor(floor(t0 / ratio) / index_block));
+ * the call computes the block this step's token completes, if any, from the
+ * keys and writes it into rep, so calling it step after step keeps the cache
+ * current.  hisa_block_means_update fills a cache (e.g. after a prefill
+ * chunk).  A step reads nb * D_i * 4 bytes of means and at most
+ * index_keep * index_block key rows instead of all Np_b key rows.
+ * Shapes: bf16 keys, H_i = 64, D_i = 128, index_block > 0, nb_cap <= 4096,
+ * index_keep <= 64, topk <= index_block * index_keep <= 1024, mode not
+ * HISA_MODE_FORCE_FLAT (HISA_ERR_ARG otherwise; use hisa_select_decode).
+ * HISA_MODE_FORCE_DENSE behaves as in hisa_select_decode and leaves rep alone.
+ * Workspace: its first part holds arrival counters under the same rule as
+ * hisa_select_decode's (zero before first use, left zero; zero again before
+ * a call with a larger B or Np_cap). */
+int hisa_select_decode_cached(const hisa_dims* d, const void* q_idx, const float* w, const void* keys,
+                              float* rep, const int32_t* t0, int32_t* I_out, int32_t* top_blk_out,
+                              int32_t* path_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Block means of the blocks that the step's L tokens complete, written into
+ * the cache rep (B, nb_cap, D_i) f32 of hisa_select_decode_cached: blocks beta
+ * with floor(floor(t0 / ratio) / b) <= beta < floor(Np_b / b), where
+ * Np_b = floor((t0 + L) / ratio).  With t0 = 0 and L the tokens so far, every
+ * complete block.  Other rows of rep are left alone.  idx_dtype bf16 or f32;
+ * needs index_block > 0; no workspace. */
+int hisa_block_means_update(const hisa_dims* d, const void* keys, const int32_t* t0, float* rep,
+                            void* stream);
 
 /* hisa_select_decode for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid

@@ -32,7 +32,7 @@ def test_exports_every_declared_function(lib):
     assert set(names) == set(hisa.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.hisa_abi_version() == 1
+    assert lib.hisa_abi_version() == 2
 
 
 def dims(**kw):
@@ -146,3 +146,24 @@ def test_noalloc_decode_rejects_dims_past_its_workspace(lib):
     assert rc == -3 and "noalloc" in hisa.last_error()
     rc = lib.hisa_select_decode_noalloc(ctypes.byref(dims(L=2)), fake, fake, fake, fake, fake, None, None, None)
     assert rc == -1
+
+
+def test_cached_decode_workspace_and_limits(lib):
+    # counters (1 sequence + 1 group counter for 16 workgroups, + 1 for the
+    # fine stage: 3 x 64 B, rounded to 256), block scores, kept blocks,
+    # 1024 candidate scores
+    d = dims()
+    assert hisa.workspace_bytes(hisa.OP_SELECT_DECODE_CACHED, d) == 256 + 256 * 4 + 256 + 1024 * 4
+    assert hisa.workspace_bytes(hisa.OP_BLOCK_MEANS_UPDATE, d) == 0
+    for kw in (dict(index_block=0), dict(Np_cap=64 * 4097), dict(index_keep=32), dict(mode=hisa.MODE_FORCE_FLAT),
+               dict(index_keep=4), dict(idx_dtype=hisa.F32), dict(H_i=32), dict(L=2)):
+        bad = dims(**kw)
+        assert lib.hisa_workspace_bytes(hisa.OP_SELECT_DECODE_CACHED, ctypes.byref(bad)) == ctypes.c_size_t(-1).value, kw
+    fake = ctypes.c_void_p(256)
+    rc = lib.hisa_select_decode_cached(ctypes.byref(dims(index_keep=32)), fake, fake, fake, fake, fake, fake, None, None,
+                                       fake, 1 << 30, None)
+    assert rc == -1 and "hisa_select_decode_cached needs" in hisa.last_error()
+    rc = lib.hisa_block_means_update(ctypes.byref(dims(index_block=0)), fake, fake, fake, None)
+    assert rc == -1
+    rc = lib.hisa_block_means_update(ctypes.byref(dims()), fake, fake, None, None)
+    assert rc == -1 and "NULL" in hisa.last_error()

@@ -1,0 +1,186 @@
+"""Decode selection on cached block means (hisa_select_decode_cached) and the
+cache update (hisa_block_means_update) against the CPU oracle, through the C
+ABI: the V4-Flash decode step and the ragged batch, mixed dense / flat / HiSA /
+invalid sequences, exact ties, steps that complete a block (the call writes
+the new mean into the cache and leaves the others alone), and the cache's
+contents against the oracle's block means."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import parity
+from tests.test_gpu_parity import MIXED, MIXED_STREAM, check_selection, inputs, odims, sel_kw
+from top_kv_indexer_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def hisa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from top_kv_indexer_amd import hisa as h
+    h.lib()
+    return h
+
+
+def full_cache(hisa, w, g):
+    """A cache holding every complete block of each sequence at its t0."""
+    _, rep = hisa.hisa_block_scores(g["q_idx"], g["w"], g["keys"], g["t0"], ratio=w.ratio,
+                                    index_block=w.index_block, want_rep=True)
+    return rep
+
+
+@pytest.mark.parametrize("case", ["flash", "batched", "mixed", "mixed_stream"])
+def test_cached_decode_matches_oracle(hisa, case):
+    w, seed = {"flash": (synth.FLASH_DECODE, synth.SEEDS[synth.FLASH_DECODE.name]),
+               "batched": (synth.BATCHED_DECODE, synth.SEEDS[synth.BATCHED_DECODE.name]),
+               "mixed": (MIXED, 5), "mixed_stream": (MIXED_STREAM, 21)}[case]
+    x, g = inputs(w, seed)
+    rep = full_cache(hisa, w, g)
+    rep0 = rep.clone()
+    say(f"[run] cached decode selection, {w.name}")
+    I, blk, path = hisa.hisa_select_decode_cached(g["q_idx"], g["w"], g["keys"], rep, g["t0"], **sel_kw(w))
+    torch.cuda.synchronize()
+    p = parity.to_np(path)
+    ref_paths = [oracle.gate(odims(w, x), int(n)) for n in x["Np"]]
+    assert p.tolist() == ref_paths
+    check_selection(w, x, I, blk, path)
+    # the blocks the cache already held are untouched; only the block this
+    # step's token completes (if any) was rewritten, with the same mean
+    nb = x["Np"] // w.index_block
+    first_new = (x["t0"] // w.ratio) // w.index_block
+    for b in range(w.B):
+        assert torch.equal(rep[b, :first_new[b]], rep0[b, :first_new[b]])
+        if nb[b] > first_new[b] and ref_paths[b] == oracle.PATH_HISA:
+            np.testing.assert_allclose(parity.to_np(rep[b, first_new[b]:nb[b]]),
+                                       parity.to_np(rep0[b, first_new[b]:nb[b]]), rtol=1e-6, atol=1e-7)
+    say("[run] stateless decode selection for comparison")
+    Is, _, ps = hisa.hisa_select_decode(g["q_idx"], g["w"], g["keys"], g["t0"], **sel_kw(w))
+    torch.cuda.synchronize()
+    assert torch.equal(ps, path)
+    same = (np.sort(parity.to_np(Is), -1) == np.sort(parity.to_np(I), -1)).mean()
+    say(f"  ids equal to the stateless path: {same:.5f}")
+
+
+def test_cached_decode_exact_ties(hisa):
+    # The best row of each HiSA sequence copied over blocks 10..39, so the
+    # coarse and the fine top-k both cut through exact ties; the lowest ids win
+    # on both sides.
+    w = MIXED
+    x, g = inputs(w, 5)
+    od = odims(w, x)
+    keys = x["keys"].copy()
+    for b in range(w.B):
+        t0 = int(w.t0[b])
+        Np = oracle.num_pooled(t0, 1, w.ratio)
+        if oracle.gate(od, Np) != oracle.PATH_HISA:
+            continue
+        sc = oracle.scores_of(od, x["q_idx"][b, 0], x["w"][b, 0], x["keys"][b], t0, 0, np.arange(Np, dtype=np.int32))
+        keys[b, 640:min(2560, Np)] = x["keys"][b, int(np.argmax(sc))]
+    xx = dict(x)
+    xx["keys"] = keys
+    gg = dict(g)
+    gg["keys"] = torch.from_numpy(keys).to("cuda").to(torch.bfloat16).contiguous()
+    rep = full_cache(hisa, w, gg)
+    say("[run] cached decode with exact ties")
+    I, blk, path = hisa.hisa_select_decode_cached(gg["q_idx"], gg["w"], gg["keys"], rep, gg["t0"], **sel_kw(w))
+    torch.cuda.synchronize()
+    In, bn = parity.to_np(I), parity.to_np(blk)
+    for b in range(w.B):
+        Io, blko, po = oracle.select_row(od, xx["q_idx"][b, 0], xx["w"][b, 0], keys[b], int(w.t0[b]), 0)
+        parity.check_selection_row(od, xx, b, 0, In[b, 0], bn[b, 0], int(parity.to_np(path)[b]), Io, blko, po)
+        if po == oracle.PATH_HISA:
+            assert set(In[b, 0].tolist()) == set(Io.tolist()), b
+            assert set(bn[b, 0].tolist()) == set(blko.tolist()), b
+
+
+def test_cached_decode_steps_complete_a_block(hisa):
+    # Decode steps at t0 = 65532 .. 65535 on the V4-Flash keys: the cache is
+    # built by hisa_block_means_update for the first 65532 tokens (255 complete
+    # blocks); the last step's token completes pooled row 16383 and with it
+    # block 255, whose mean the selection computes and stores.
+    w = synth.FLASH_DECODE
+    x, g = inputs(w, synth.SEEDS[w.name])
+    dev = torch.device("cuda")
+    rep = torch.full((1, 256, 128), float("nan"), dtype=torch.float32, device=dev)
+    say("[run] block means of the first 65532 tokens")
+    hisa.hisa_block_means_update(g["keys"], torch.zeros(1, dtype=torch.int32, device=dev), rep, ratio=4,
+                                 index_block=64, L=65532)
+    torch.cuda.synchronize()
+    _, rep_orc = oracle.block_scores(odims(w, x), x["q_idx"], x["w"], x["keys"], x["t0"])
+    np.testing.assert_allclose(parity.to_np(rep[0, :255]), rep_orc[0, :255], rtol=1e-6, atol=1e-7)
+    assert torch.isnan(rep[0, 255]).all()
+    d = hisa.selection_dims(g["q_idx"], g["keys"], **sel_kw(w))
+    ws = torch.zeros(hisa.workspace_bytes(hisa.OP_SELECT_DECODE_CACHED, d), dtype=torch.uint8, device=dev)
+    od = odims(w, x)
+    for t0 in (65532, 65533, 65534, 65535):
+        say(f"[run] cached decode at t0 = {t0}")
+        before = rep.clone()
+        tt = torch.tensor([t0], dtype=torch.int32, device=dev)
+        I, blk, path = hisa.hisa_select_decode_cached(g["q_idx"], g["w"], g["keys"], rep, tt, **sel_kw(w), ws=ws)
+        torch.cuda.synchronize()
+        xx = dict(x)
+        xx["t0"] = np.array([t0], np.int32)
+        Io, blko, po = oracle.select_row(od, x["q_idx"][0, 0], x["w"][0, 0], x["keys"][0], t0, 0)
+        parity.check_selection_row(od, xx, 0, 0, parity.to_np(I)[0, 0], parity.to_np(blk)[0, 0],
+                                   int(parity.to_np(path)[0]), Io, blko, po)
+        assert torch.equal(rep[0, :255], before[0, :255])
+        if t0 < 65535:  # Np = 16383: block 255 is not complete and stays untouched
+            assert parity.to_np(I)[0, 0].max() < 255 * 64
+            assert torch.isnan(rep[0, 255]).all()
+    np.testing.assert_allclose(parity.to_np(rep[0, 255]), rep_orc[0, 255], rtol=1e-6, atol=1e-7)
+    # the step's mean and the update call's mean are the same numbers
+    rep2 = torch.zeros_like(rep)
+    hisa.hisa_block_means_update(g["keys"], torch.zeros(1, dtype=torch.int32, device=dev), rep2, ratio=4,
+                                 index_block=64, L=65536)
+    torch.cuda.synchronize()
+    assert torch.equal(rep2, rep)
+    assert (ws[:256].view(torch.int32) == 0).all()
+
+
+@pytest.mark.parametrize("bf16", [True, False], ids=["bf16", "f32"])
+def test_block_means_update_ragged(hisa, bf16):
+    # A prefill chunk of 300 tokens (75 pooled rows) completes blocks
+    # [floor(floor(t0/r)/b), floor(floor((t0+300)/r)/b)) of each sequence;
+    # everything else keeps its value.
+    w = MIXED.with_(name="means_update", bf16=bf16, index_block=16, t0=[1200, 2800, 4096, 6000, 19900, 16400],
+                    L=1)
+    x, g = inputs(w, 55)
+    dev = torch.device("cuda")
+    nb_cap = int(x["Np_cap"]) // 16
+    rep = torch.full((w.B, nb_cap, w.D_i), -3.0, dtype=torch.float32, device=dev)
+    t0 = torch.tensor([t - 299 for t in w.t0], dtype=torch.int32, device=dev)
+    say(f"[run] block means update ({'bf16' if bf16 else 'f32'})")
+    hisa.hisa_block_means_update(g["keys"], t0, rep, ratio=4, index_block=16, L=300)
+    torch.cuda.synchronize()
+    R = parity.to_np(rep)
+    for b in range(w.B):
+        t0b = w.t0[b] - 299
+        lo = (t0b // 4) // 16
+        hi = ((t0b + 300) // 4) // 16
+        assert hi > lo, b
+        mean = x["keys"][b, :hi * 16].astype(np.float64).reshape(hi, 16, w.D_i).mean(axis=1)
+        np.testing.assert_allclose(R[b, lo:hi], mean[lo:hi], rtol=1e-6, atol=1e-7)
+        assert (R[b, :lo] == -3.0).all() and (R[b, hi:] == -3.0).all()
+
+
+def test_cached_decode_dense_switch_leaves_cache(hisa):
+    w = synth.FLASH_DECODE.with_(name="flash_cached_dense", topk=16384, planted=0)
+    x, g = inputs(w, 57)
+    rep = full_cache(hisa, w, g)
+    rep0 = rep.clone()
+    I, blk, path = hisa.hisa_select_decode_cached(g["q_idx"], g["w"], g["keys"], rep, g["t0"], **sel_kw(w, mode=2))
+    torch.cuda.synchronize()
+    assert torch.equal(rep, rep0)
+    np.testing.assert_array_equal(parity.to_np(I)[0, 0], np.arange(16384))
+    assert parity.to_np(path)[0] == hisa.PATH_DENSE

@@ -42,12 +42,12 @@ constexpr int kMaxCandidates = 8192;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-bool is_sel(int op) { return op == HISA_OP_BLOCK_SCORES || op == HISA_OP_SELECT_DECODE || op == HISA_OP_SELECT_PREFILL || op == HISA_OP_FLAT_TOPK; }
+bool is_sel(int op) { return op != HISA_OP_ATTENTION; }
 
 // Checks dims for `op` and fills the kernel-side description.
 int make_kdims(int op, const hisa_dims* d, KDims* k) {
   if (!d) return fail(HISA_ERR_ARG, "dims is NULL");
-  if (op < HISA_OP_BLOCK_SCORES || op > HISA_OP_ATTENTION) return fail(HISA_ERR_ARG, "unknown op %d", op);
+  if (op < HISA_OP_BLOCK_SCORES || op > HISA_OP_BLOCK_MEANS_UPDATE) return fail(HISA_ERR_ARG, "unknown op %d", op);
   if (d->B < 1 || d->B > 65535) return fail(HISA_ERR_ARG, "B = %d must be in [1, 65535]", d->B);
   if (d->L < 1 || d->L > 524280) return fail(HISA_ERR_ARG, "L = %d must be in [1, 524280]", d->L);
   if (d->ratio < 1) return fail(HISA_ERR_ARG, "ratio = %d must be >= 1", d->ratio);
@@ -68,7 +68,8 @@ int make_kdims(int op, const hisa_dims* d, KDims* k) {
     if (d->idx_dtype != HISA_F32 && d->idx_dtype != HISA_BF16) return fail(HISA_ERR_DTYPE, "idx_dtype %d", d->idx_dtype);
     if (d->mode != HISA_MODE_AUTO && d->mode != HISA_MODE_FORCE_FLAT && d->mode != HISA_MODE_FORCE_DENSE)
       return fail(HISA_ERR_ARG, "mode = %d", d->mode);
-    if (d->mode == HISA_MODE_FORCE_DENSE && (op == HISA_OP_SELECT_DECODE || op == HISA_OP_SELECT_PREFILL) &&
+    if (d->mode == HISA_MODE_FORCE_DENSE &&
+        (op == HISA_OP_SELECT_DECODE || op == HISA_OP_SELECT_PREFILL || op == HISA_OP_SELECT_DECODE_CACHED) &&
         d->topk < d->Np_cap)
       return fail(HISA_ERR_ARG, "HISA_MODE_FORCE_DENSE lists every pooled row: topk = %d must be >= Np_cap = %d",
                   d->topk, d->Np_cap);
@@ -80,7 +81,10 @@ int make_kdims(int op, const hisa_dims* d, KDims* k) {
     if ((long long)d->index_keep * d->index_block > kMaxCandidates)
       return fail(HISA_ERR_ARG, "index_keep * index_block = %lld exceeds %d", (long long)d->index_keep * d->index_block, kMaxCandidates);
     if (op == HISA_OP_BLOCK_SCORES && d->index_block == 0) return fail(HISA_ERR_ARG, "hisa_block_scores needs index_block > 0");
-    if (op == HISA_OP_SELECT_DECODE && d->L != 1) return fail(HISA_ERR_ARG, "hisa_select_decode needs L == 1 (got %d)", d->L);
+    if (op == HISA_OP_BLOCK_MEANS_UPDATE && d->index_block == 0)
+      return fail(HISA_ERR_ARG, "hisa_block_means_update needs index_block > 0");
+    if ((op == HISA_OP_SELECT_DECODE || op == HISA_OP_SELECT_DECODE_CACHED) && d->L != 1)
+      return fail(HISA_ERR_ARG, "decode selection needs L == 1 (got %d)", d->L);
     const long long rows = (long long)d->B * d->L;
     if (rows * d->H_i * d->D_i > kMaxElems || (long long)d->B * d->Np_cap * d->D_i > kMaxElems ||
         rows * d->Np_cap > kMaxElems || rows * d->topk > kMaxElems)
@@ -88,6 +92,10 @@ int make_kdims(int op, const hisa_dims* d, KDims* k) {
     if (d->idx_dtype == HISA_BF16 && d->D_i % 8 != 0) return fail(HISA_ERR_ARG, "bf16 keys need D_i %% 8 == 0");
     kd.nb_cap = d->index_block > 0 ? d->Np_cap / d->index_block : 0;
     kd.w_scale = (float)(1.0 / std::sqrt((double)d->H_i * (double)d->D_i));
+    if (op == HISA_OP_SELECT_DECODE_CACHED && !kd.force_dense && !hisa::cached_decode_ok(kd, d->idx_dtype == HISA_BF16))
+      return fail(HISA_ERR_ARG,
+                  "hisa_select_decode_cached needs bf16 keys, H_i = 64, D_i = 128, index_block > 0, nb_cap <= 4096, "
+                  "index_keep <= 64, topk <= index_block * index_keep <= 1024 and no forced flat scan");
   } else {
     if (d->attn_dtype != HISA_F32 && d->attn_dtype != HISA_BF16) return fail(HISA_ERR_DTYPE, "attn_dtype %d", d->attn_dtype);
     if (d->H < 1 || d->Dk < 1 || d->Dv < 1 || d->Dv > d->Dk) return fail(HISA_ERR_ARG, "H = %d, Dk = %d, Dv = %d (need 1 <= Dv <= Dk)", d->H, d->Dk, d->Dv);
@@ -110,7 +118,7 @@ int make_kdims(int op, const hisa_dims* d, KDims* k) {
 
 struct Layout {
   size_t total = 0;
-  size_t rep = 0, rep3 = 0, cscore = 0, scores = 0, fscore = 0, partial = 0, cnt = 0;
+  size_t rep = 0, rep3 = 0, cscore = 0, scores = 0, fscore = 0, partial = 0, cnt = 0, blk = 0;
   int splits = 1;
 };
 
@@ -154,6 +162,15 @@ Layout layout(int op, const hisa_dims* d, const KDims& k) {
       l.cnt = take(l, hisa::decode_counter_ints(k) * sizeof(int));
       l.fscore = take(l, B * d->Np_cap * sizeof(float));
       l.cscore = take(l, B * std::max<size_t>(nb_cap, 1) * sizeof(float));
+      break;
+    case HISA_OP_SELECT_DECODE_CACHED:
+      if (k.force_dense) break;
+      l.cnt = take(l, hisa::cached_counter_ints(k) * sizeof(int));
+      l.cscore = take(l, B * std::max<size_t>(nb_cap, 1) * sizeof(float));
+      l.blk = take(l, B * (size_t)d->index_keep * sizeof(int));
+      l.fscore = take(l, hisa::cached_fine_floats(k) * sizeof(float));
+      break;
+    case HISA_OP_BLOCK_MEANS_UPDATE:
       break;
     case HISA_OP_SELECT_PREFILL: {
       if (k.force_dense) break;
@@ -342,6 +359,42 @@ int hisa_select_decode(const hisa_dims* d, const void* q_idx, const float* w, co
   if (e != hipSuccess) return launch_fail(e, "decode scan");
   e = timed("decode_select", st, [&] { return hisa::launch_decode_select(k, fscore, cscore, t0, I_out, top_blk_out, path_out, st); });
   if (e != hipSuccess) return launch_fail(e, "decode select");
+  return HISA_OK;
+}
+
+int hisa_select_decode_cached(const hisa_dims* d, const void* q_idx, const float* w, const void* keys, float* rep,
+                              const int32_t* t0, int32_t* I_out, int32_t* top_blk_out, int32_t* path_out, void* ws,
+                              size_t ws_bytes, void* stream) {
+  g_err.clear();
+  KDims k;
+  Layout l;
+  int rc = prepare(HISA_OP_SELECT_DECODE_CACHED, d, &k, &l, ws, ws_bytes);
+  if (rc) return rc;
+  if ((rc = check_ptrs({q_idx, w, keys, rep, t0, I_out}, "q_idx, w, keys, rep, t0, I_out"))) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  if (k.force_dense) {
+    hipError_t e = timed("fill_dense", st, [&] { return hisa::launch_fill_dense(k, t0, I_out, top_blk_out, path_out, st); });
+    return e == hipSuccess ? HISA_OK : launch_fail(e, "dense fallback");
+  }
+  hipError_t e = timed("cached_decode", st, [&] {
+    return hisa::launch_cached_decode(k, q_idx, w, keys, rep, t0, at<float>(ws, l.cscore), at<int>(ws, l.blk),
+                                      at<float>(ws, l.fscore), at<int>(ws, l.cnt), I_out, top_blk_out, path_out, st);
+  });
+  if (e != hipSuccess) return launch_fail(e, "cached decode selection");
+  return HISA_OK;
+}
+
+int hisa_block_means_update(const hisa_dims* d, const void* keys, const int32_t* t0, float* rep, void* stream) {
+  g_err.clear();
+  KDims k;
+  int rc = make_kdims(HISA_OP_BLOCK_MEANS_UPDATE, d, &k);
+  if (rc) return rc;
+  if ((rc = check_ptrs({keys, t0, rep}, "keys, t0, rep"))) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = timed("block_means_update", st, [&] {
+    return hisa::launch_rep_update(k, d->idx_dtype == HISA_BF16, keys, t0, rep, st);
+  });
+  if (e != hipSuccess) return launch_fail(e, "block means update");
   return HISA_OK;
 }
 

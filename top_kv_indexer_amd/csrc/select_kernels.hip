@@ -133,7 +133,7 @@ __device__ __forceinline__ void write_unscored(const KDims& d, const SeqInfo& si
 struct WgTopkSmem {
   uint32_t hist[3][256];  // rotating histograms: one barrier per radix pass
   uint32_t red[2][4];     // per-wave min and max of the present keys
-  uint32_t cnt[2][4][4];  // per register and wave: keys equal to the threshold, keys taken
+  uint32_t cnt[2][16][4];  // per register and wave: keys equal to the threshold, keys taken
 };
 
 __device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
@@ -165,8 +165,8 @@ __device__ __forceinline__ uint32_t wave_umin(uint32_t v) {
 // wave evaluates the same scan of the shared histogram, so the control flow
 // is uniform over the workgroup.
 constexpr int kAllTies = 0x7FFFFFFF;
-template <int NR>
-__device__ __forceinline__ uint32_t wg_topk_threshold(const uint32_t (&key)[4], int k, WgTopkSmem& sm, int& ties) {
+template <int NR, int NK>
+__device__ __forceinline__ uint32_t wg_topk_threshold(const uint32_t (&key)[NK], int k, WgTopkSmem& sm, int& ties) {
   const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
 #pragma unroll
@@ -237,8 +237,8 @@ __device__ __forceinline__ uint32_t wg_topk_threshold(const uint32_t (&key)[4], 
 }
 
 // emits the k winners in ascending order index: emit(slot, r)
-template <int NR, class EmitF>
-__device__ __forceinline__ void wg_emit_topk_n(const uint32_t (&key)[4], int k, WgTopkSmem& sm, EmitF emit) {
+template <int NR, int NK, class EmitF>
+__device__ __forceinline__ void wg_emit_topk_n(const uint32_t (&key)[NK], int k, WgTopkSmem& sm, EmitF emit) {
   const int lane = lane_id(), wv = wave_id();
   int ties;
   const uint32_t t = wg_topk_threshold<NR>(key, k, sm, ties);
@@ -298,6 +298,13 @@ __device__ __forceinline__ void wg_emit_topk(const uint32_t (&key)[4], int n, in
   if (n <= 256) wg_emit_topk_n<1>(key, k, sm, emit);
   else if (n <= 512) wg_emit_topk_n<2>(key, k, sm, emit);
   else wg_emit_topk_n<4>(key, k, sm, emit);
+}
+// and for n <= 4096 elements, 16 keys per thread
+template <class EmitF>
+__device__ __forceinline__ void wg_emit_topk16(const uint32_t (&key)[16], int n, int k, WgTopkSmem& sm, EmitF emit) {
+  if (n <= 1024) wg_emit_topk_n<4>(key, k, sm, emit);
+  else if (n <= 2048) wg_emit_topk_n<8>(key, k, sm, emit);
+  else wg_emit_topk_n<16>(key, k, sm, emit);
 }
 
 // Decode selection of sequence b by a whole workgroup (256 threads), from the
@@ -1893,6 +1900,248 @@ __global__ __launch_bounds__(256) void k_fill_dense(KDims d, const int* __restri
   if (path && j == 0 && tid == 0) path[b] = si.ok ? PATH_DENSE : PATH_INVALID;
 }
 
+// ------------------------------------------------------------------ decode on cached block means
+
+// Decode selection that takes the block means from a caller-kept cache
+// instead of re-reading every key (HiSA issue, HiSA decode path: O(nb + Kb*b)
+// scores per step; The pooled stream and positions: the pooled stream grows
+// in whole windows, so a complete block never changes).  Two kernels:
+//   coarse (ceil(nb_cap / 16), B) x 256: wave w scores blocks 16x + 4w ..
+//          +3 with lane h holding head h; a block completed by this step's
+//          token is averaged from the keys (f32, rows in order) and written to
+//          the cache first, every other block is read from it.  The workgroup
+//          that completes a sequence keeps its top-Kb blocks.
+//   fine   (16, B) x 256: 64 candidates per workgroup (the retained blocks'
+//          rows, or the rows of a flat sequence) scored on MFMA like the scan;
+//          the workgroup that completes a sequence keeps the top-k.
+constexpr int kCachedBlocksPerWg = 16;
+constexpr int kCachedMaxNb = 4096;
+constexpr int kCachedMaxCand = 1024;
+
+__device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+// Mean of the b key rows of block beta, lane l holding dims 2l and 2l+1 (64
+// lanes, D_i = 128): rows summed in order in f32, then scaled by 1/b.
+__device__ __forceinline__ float2 block_mean_lane(const uint16_t* kb, int beta, int bsz) {
+  const uint32_t* src = (const uint32_t*)(kb + (size_t)beta * bsz * 128) + lane_id();
+  float sx = 0.f, sy = 0.f;
+#pragma unroll 8
+  for (int r = 0; r < bsz; ++r) {
+    const uint32_t v = src[r * 64];
+    sx += bf_lo(v);
+    sy += bf_hi(v);
+  }
+  const float inv = 1.f / (float)bsz;
+  return make_float2(sx * inv, sy * inv);
+}
+
+__global__ __launch_bounds__(256) void k_cached_coarse(KDims d, const uint16_t* __restrict__ q_idx,
+                                                       const float* __restrict__ w, const uint16_t* __restrict__ keys,
+                                                       float* rep, const int* __restrict__ t0, float* cscore, int* blk,
+                                                       int* cnt, int* I, int* top_blk, int* path) {
+  __shared__ __align__(16) float s_rep[4][4][128];
+  __shared__ WgTopkSmem s_tk;
+  __shared__ int s_flag;
+  args_now(d, q_idx, w, keys, rep, t0, cscore, blk, cnt, I, top_blk, path);
+  const int b = blockIdx.y, x = blockIdx.x;
+  const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
+  const int t0b = t0[b];
+  // this lane's head: q row (256 B) and weight, requested before t0 arrives
+  uint4 qv[16];
+  const uint4* qrow = (const uint4*)(q_idx + ((size_t)b * 64 + lane) * 128);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) qv[i] = qrow[i];
+  const float wh = w[(size_t)b * 64 + lane] * d.w_scale;
+  const SeqInfo si = seq_info(d, t0b);
+  if (!si.ok || si.path == PATH_DENSE) {
+    if (x == 0 && wv == 0) write_unscored(d, si, b, I, top_blk, path);
+    return;
+  }
+  if (si.path != PATH_HISA) {  // flat: the fine kernel selects
+    if (x == 0 && wv == 0) {
+      if (top_blk)
+        for (int i = lane; i < d.index_keep; i += 64) top_blk[(size_t)b * d.index_keep + i] = -1;
+      if (path && lane == 0) path[b] = si.path;
+    }
+    return;
+  }
+  const int nwg = (si.nb + kCachedBlocksPerWg - 1) / kCachedBlocksPerWg;
+  if (x >= nwg) return;
+  const int bsz = d.index_block;
+  // blocks completed by this step's token: the ones past the pooled rows
+  // that existed before it
+  const int first_new = (int)div_ratio(d, (uint32_t)t0b) / bsz;
+  const uint16_t* kb = keys + (size_t)b * d.Np_cap * 128;
+  float* repb = rep + (size_t)b * d.nb_cap * 128;
+  const int beta0 = x * kCachedBlocksPerWg + 4 * wv;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int beta = beta0 + j;
+    if (beta >= si.nb) break;  // uniform over the wave
+    float2 m;
+    if (beta >= first_new) {
+      m = block_mean_lane(kb, beta, bsz);
+      *(float2*)&repb[(size_t)beta * 128 + 2 * lane] = m;
+    } else {
+      m = *(const float2*)&repb[(size_t)beta * 128 + 2 * lane];
+    }
+    *(float2*)&s_rep[wv][j][2 * lane] = m;
+  }
+  __builtin_amdgcn_wave_barrier();
+  // one wave's LDS operations complete in order: the stores above land
+  // before the broadcast reads below
+#pragma unroll 1
+  for (int j = 0; j < 4; ++j) {
+    const int beta = beta0 + j;
+    if (beta >= si.nb) break;
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float4 r0 = *(const float4*)&s_rep[wv][j][8 * i];
+      const float4 r1 = *(const float4*)&s_rep[wv][j][8 * i + 4];
+      acc = fmaf(bf_lo(qv[i].x), r0.x, acc);
+      acc = fmaf(bf_hi(qv[i].x), r0.y, acc);
+      acc = fmaf(bf_lo(qv[i].y), r0.z, acc);
+      acc = fmaf(bf_hi(qv[i].y), r0.w, acc);
+      acc = fmaf(bf_lo(qv[i].z), r1.x, acc);
+      acc = fmaf(bf_hi(qv[i].z), r1.y, acc);
+      acc = fmaf(bf_lo(qv[i].w), r1.z, acc);
+      acc = fmaf(bf_hi(qv[i].w), r1.w, acc);
+    }
+    const float cs = wave_sum(relu(acc) * wh);
+    if (lane == 0) st_dev(cscore + (size_t)b * d.nb_cap + beta, cs);
+  }
+  // cnt: B sequence counters, then B x ngmax group counters
+  const int grp = x / kArriveGroup, ngrp = (nwg + kArriveGroup - 1) / kArriveGroup;
+  const int ngmax = (gridDim.x + kArriveGroup - 1) / kArriveGroup;
+  const bool last = publish(
+      [&] {
+        const int members = min(kArriveGroup, nwg - grp * kArriveGroup);
+        int* c_grp = cnt + (size_t)(d.B + (size_t)b * ngmax + grp) * kCntStride;
+        return arrive(c_grp, 1, members) && arrive(cnt + (size_t)b * kCntStride, 1, ngrp);
+      },
+      &s_flag);
+  if (!last) return;
+  // top-Kb of the sequence's nb block scores, ascending block ids
+  const float* csb = cscore + (size_t)b * d.nb_cap;
+  uint32_t key[16];
+  float v[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) v[r] = ld_dev(csb + min(256 * r + tid, si.nb - 1));
+#pragma unroll
+  for (int r = 0; r < 16; ++r) key[r] = 256 * r + tid < si.nb ? score_key(v[r]) : 0u;
+  int* blkb = blk + (size_t)b * d.index_keep;
+  int* tbo = top_blk ? top_blk + (size_t)b * d.index_keep : nullptr;
+  wg_emit_topk16(key, si.nb, si.Kb, s_tk, [&](int slot, int r) {
+    blkb[slot] = 256 * r + tid;
+    if (tbo) tbo[slot] = 256 * r + tid;
+  });
+  if (tbo)
+    for (int i = si.Kb + tid; i < d.index_keep; i += 256) tbo[i] = -1;
+  if (path && tid == 0) path[b] = si.path;
+}
+
+__global__ __launch_bounds__(256) void k_cached_fine(KDims d, const uint16_t* __restrict__ q_idx,
+                                                     const float* __restrict__ w, const uint16_t* __restrict__ keys,
+                                                     const int* __restrict__ t0, const int* __restrict__ blk,
+                                                     float* fs, int* cnt, int* I) {
+  __shared__ __align__(16) uint16_t s_q[64 * 128];
+  __shared__ WgTopkSmem s_tk;
+  __shared__ int s_blk[kRowKeep];
+  __shared__ int s_flag;
+  args_now(d, q_idx, w, keys, t0, blk, fs, cnt, I);
+  const int b = blockIdx.y, slab = blockIdx.x;
+  const int tid = threadIdx.x, lane = lane_id(), wv = wave_id(), g = lane >> 4, c = lane & 15;
+  const int t0b = t0[b];
+  issue_q_lds(q_idx + (size_t)b * 64 * 128, s_q);
+  const float* wrow = w + (size_t)b * 64;
+  float wl[4][4];
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wl[ht][i] = wrow[ht * 16 + 4 * g + i];
+  const SeqInfo si = seq_info(d, t0b);
+  if (!si.ok || si.path == PATH_DENSE) {  // outputs written by the coarse kernel
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // no global->LDS copy outlives the workgroup
+    return;
+  }
+  const bool hisa = si.path == PATH_HISA;
+  const int bsz = d.index_block, lbsz = __builtin_ctz(bsz);
+  const int n = hisa ? si.Kb * bsz : si.Np;  // candidates (<= 1024)
+  const int nslab = (n + 63) / 64;
+  if (slab >= nslab) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // no global->LDS copy outlives the workgroup
+    return;
+  }
+  if (tid < si.Kb && hisa) s_blk[tid] = blk[(size_t)b * d.index_keep + tid];
+  __syncthreads();
+  auto pos = [&](int cc) { return hisa ? (s_blk[cc >> lbsz] << lbsz) + (cc & (bsz - 1)) : cc; };
+  const int cand = min(slab * 64 + wv * 16 + c, n - 1);
+  const int r = pos(cand);
+  const uint16_t* kr = keys + ((size_t)b * d.Np_cap + r) * 128;
+  bf16x8 kf[4];
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) kf[s4] = ldg8(kr + s4 * 32 + g * 8);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0: q rows, weights and key rows are in
+  __syncthreads();
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wl[ht][i] *= d.w_scale;
+  bf16x8 qf[4][4];
+  read_q_lds(s_q, qf);
+  f32x4 acc[4];
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ht][s4], kf[s4], acc[ht], 0, 0, 0);
+  float v = 0.f;
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v += relu(acc[ht][i]) * wl[ht][i];
+  v = sum_rows(v);
+  const int cc = slab * 64 + wv * 16 + c;
+  float* fsb = fs + (size_t)b * kCachedMaxCand;
+  if (g == 0 && cc < n) st_dev(fsb + cc, v);
+  const bool last = publish([&] { return arrive(cnt + (size_t)b * kCntStride, 1, nslab); }, &s_flag);
+  if (!last) return;
+  int* Ib = I + (size_t)b * d.topk;
+  for (int i = si.k + tid; i < d.topk; i += 256) Ib[i] = -1;
+  uint32_t key[4];
+  float sv[4];
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) sv[rr] = ld_dev(fsb + min(256 * rr + tid, n - 1));
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) key[rr] = 256 * rr + tid < n ? score_key(sv[rr]) : 0u;
+  wg_emit_topk(key, n, si.k, s_tk, [&](int slot, int rr) { Ib[slot] = pos(256 * rr + tid); });
+}
+
+// Block means of the blocks completed by the step's L tokens: blocks
+// [floor(floor(t0 / r) / b), floor(Np / b)) (every complete block when t0 = 0),
+// rows summed in order in f32 and scaled by 1/b, as the cached decode does.
+template <typename T>
+__global__ __launch_bounds__(128) void k_rep_update(KDims d, const T* __restrict__ keys, const int* __restrict__ t0,
+                                                    float* rep) {
+  const int b = blockIdx.y, beta = blockIdx.x;
+  const int t0b = t0[b];
+  const SeqInfo si = seq_info(d, t0b);
+  if (!si.ok) return;
+  const int bsz = d.index_block;
+  const int first_new = (int)div_ratio(d, (uint32_t)t0b) / bsz;
+  if (beta < first_new || beta >= si.nb) return;
+  const T* kb = keys + ((size_t)b * d.Np_cap + (size_t)beta * bsz) * d.D_i;
+  const float inv = 1.f / (float)bsz;
+  for (int e = threadIdx.x; e < d.D_i; e += 128) {
+    float s = 0.f;
+    for (int r = 0; r < bsz; ++r) s += ldf(kb + (size_t)r * d.D_i + e);
+    rep[((size_t)b * d.nb_cap + beta) * d.D_i + e] = s * inv;
+  }
+}
+
 // Zeroes n ints (a fill kernel rather than a memset, so a captured graph holds
 // only kernel nodes).
 __global__ __launch_bounds__(256) void k_zero_ints(int* p, int n) {
@@ -1902,6 +2151,44 @@ __global__ __launch_bounds__(256) void k_zero_ints(int* p, int n) {
 }  // namespace
 
 // ------------------------------------------------------------------ launchers
+
+bool cached_decode_ok(const KDims& d, bool bf16) {
+  const long long bk = (long long)d.index_keep * d.index_block;
+  return idx_mfma_ok(d, bf16) && d.index_block > 0 && d.nb_cap <= kCachedMaxNb && bk <= kCachedMaxCand &&
+         d.index_keep <= kRowKeep && !d.force_flat && bk >= d.topk;
+}
+
+size_t cached_counter_ints(const KDims& d) {
+  const size_t wgs = ((size_t)d.nb_cap + kCachedBlocksPerWg - 1) / kCachedBlocksPerWg;
+  const size_t ngmax = (std::max<size_t>(wgs, 1) + kArriveGroup - 1) / kArriveGroup;
+  return (size_t)d.B * (1 + ngmax) * kCntStride + (size_t)d.B * kCntStride;
+}
+
+size_t cached_fine_floats(const KDims& d) { return (size_t)d.B * kCachedMaxCand; }
+
+hipError_t launch_cached_decode(const KDims& d, const void* q_idx, const float* w, const void* keys, float* rep,
+                                const int* t0, float* cscore, int* blk, float* fs, int* cnt, int* I, int* top_blk,
+                                int* path, hipStream_t st) {
+  const unsigned wgs = std::max(1u, (unsigned)((d.nb_cap + kCachedBlocksPerWg - 1) / kCachedBlocksPerWg));
+  const size_t ngmax = (wgs + kArriveGroup - 1) / kArriveGroup;
+  int* cnt_fine = cnt + (size_t)d.B * (1 + ngmax) * kCntStride;
+  hipLaunchKernelGGL(k_cached_coarse, dim3(wgs, d.B), dim3(256), 0, st, d, (const uint16_t*)q_idx, w,
+                     (const uint16_t*)keys, rep, t0, cscore, blk, cnt, I, top_blk, path);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_cached_fine, dim3(kCachedMaxCand / 64, d.B), dim3(256), 0, st, d, (const uint16_t*)q_idx, w,
+                     (const uint16_t*)keys, t0, blk, fs, cnt_fine, I);
+  return hipGetLastError();
+}
+
+hipError_t launch_rep_update(const KDims& d, bool bf16, const void* keys, const int* t0, float* rep, hipStream_t st) {
+  if (d.nb_cap == 0) return hipSuccess;
+  if (bf16)
+    hipLaunchKernelGGL(k_rep_update<uint16_t>, dim3(d.nb_cap, d.B), dim3(128), 0, st, d, (const uint16_t*)keys, t0, rep);
+  else
+    hipLaunchKernelGGL(k_rep_update<float>, dim3(d.nb_cap, d.B), dim3(128), 0, st, d, (const float*)keys, t0, rep);
+  return hipGetLastError();
+}
 
 hipError_t launch_zero_ints(int* p, size_t n, hipStream_t st) {
   if (n == 0) return hipSuccess;

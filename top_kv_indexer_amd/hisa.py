@@ -15,10 +15,11 @@ LIB_PATH = os.path.join(_PKG, "libhisa.so")
 F32, BF16 = 0, 1
 MODE_AUTO, MODE_FORCE_FLAT, MODE_FORCE_DENSE = 0, 1, 2
 PATH_INVALID, PATH_DENSE, PATH_FLAT, PATH_HISA = -1, 0, 1, 2
-OP_BLOCK_SCORES, OP_SELECT_DECODE, OP_SELECT_PREFILL, OP_FLAT_TOPK, OP_ATTENTION = range(5)
+(OP_BLOCK_SCORES, OP_SELECT_DECODE, OP_SELECT_PREFILL, OP_FLAT_TOPK, OP_ATTENTION, OP_SELECT_DECODE_CACHED,
+ OP_BLOCK_MEANS_UPDATE) = range(7)
 
-EXPORTS = ("hisa_block_scores", "hisa_select_decode", "hisa_select_decode_noalloc", "hisa_select_prefill",
-           "flat_topk_select",
+EXPORTS = ("hisa_block_scores", "hisa_select_decode", "hisa_select_decode_noalloc", "hisa_select_decode_cached",
+           "hisa_block_means_update", "hisa_select_prefill", "flat_topk_select",
            "sparse_local_pooled_attention", "hisa_workspace_bytes", "hisa_last_error", "hisa_abi_version",
            "hisa_profile_enable", "hisa_profile_collect")
 
@@ -53,11 +54,14 @@ def lib() -> ctypes.CDLL:
         L.hisa_block_scores.argtypes = sel + [vp, vp, vp, sz, vp]
         L.hisa_select_decode.argtypes = sel + [vp, vp, vp, vp, sz, vp]
         L.hisa_select_decode_noalloc.argtypes = sel + [vp, vp, vp, vp]
+        L.hisa_select_decode_cached.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.hisa_block_means_update.argtypes = [dp, vp, vp, vp, vp]
         L.hisa_select_prefill.argtypes = sel + [vp, vp, vp, vp, sz, vp]
         L.flat_topk_select.argtypes = sel + [vp, vp, sz, vp]
         L.sparse_local_pooled_attention.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-        for f in ("hisa_block_scores", "hisa_select_decode", "hisa_select_decode_noalloc", "hisa_select_prefill",
-                  "flat_topk_select", "sparse_local_pooled_attention"):
+        for f in ("hisa_block_scores", "hisa_select_decode", "hisa_select_decode_noalloc", "hisa_select_decode_cached",
+                  "hisa_block_means_update", "hisa_select_prefill", "flat_topk_select",
+                  "sparse_local_pooled_attention"):
             getattr(L, f).restype = i32
         L.hisa_workspace_bytes.argtypes = [i32, dp]
         L.hisa_workspace_bytes.restype = sz
@@ -153,7 +157,7 @@ def _workspace(op: int, d: hisa_dims, dev: torch.device, ws: Optional[torch.Tens
     if n == 0:
         return None, 0
     key = (dev.index, torch.cuda.current_stream(dev).cuda_stream, op)
-    if op == OP_SELECT_DECODE:
+    if op in (OP_SELECT_DECODE, OP_SELECT_DECODE_CACHED):
         key += (d.B, d.Np_cap)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < n:
@@ -228,6 +232,52 @@ def hisa_select_decode(q_idx, w, keys, t0, *, ratio, topk, index_block=64, index
     A caller-given ws must start with zeroed arrival counters (see include/hisa.h)."""
     return _select(lib().hisa_select_decode, OP_SELECT_DECODE, q_idx, w, keys, t0, ratio, topk, index_block,
                    index_keep, mode, I, top_blk, path, ws)
+
+
+def _rep_arg(rep, keys, index_block):
+    B, Np_cap, D_i = keys.shape
+    return _need(rep, "rep", 3, torch.float32, (B, Np_cap // max(index_block, 1), D_i))
+
+
+def hisa_select_decode_cached(q_idx, w, keys, rep, t0, *, ratio, topk, index_block=64, index_keep=16,
+                              mode=MODE_AUTO, I=None, top_blk=None, path=None, ws=None):
+    """Decode selection on the block-mean cache rep (B, Np_cap // index_block, D_i) f32, which it keeps
+    current (see include/hisa.h); returns I (B,1,topk), top_blk (B,1,index_keep), path (B)."""
+    B, L = _sel_args(q_idx, w, keys, t0)
+    _rep_arg(rep, keys, index_block)
+    if I is not None:
+        _need(I, "I", 3, torch.int32, (B, L, topk))
+    if top_blk is not None:
+        _need(top_blk, "top_blk", 3, torch.int32, (B, L, index_keep))
+    if path is not None:
+        _need(path, "path", 1, torch.int32, (B,))
+    dev = _same_gpu(q_idx=q_idx, w=w, keys=keys, rep=rep, t0=t0, I=I, top_blk=top_blk, path=path, ws=_ws_arg(ws))
+    d = selection_dims(q_idx, keys, ratio=ratio, topk=topk, index_block=index_block, index_keep=index_keep,
+                       mode=mode)
+    if I is None:
+        I = torch.empty((B, L, topk), dtype=torch.int32, device=dev)
+    if top_blk is None:
+        top_blk = torch.empty((B, L, index_keep), dtype=torch.int32, device=dev)
+    if path is None:
+        path = torch.empty((B,), dtype=torch.int32, device=dev)
+    wsb, n = _workspace(OP_SELECT_DECODE_CACHED, d, dev, ws)
+    _check(lib().hisa_select_decode_cached(ctypes.byref(d), _p(q_idx), _p(w), _p(keys), _p(rep), _p(t0), _p(I),
+                                           _p(top_blk), _p(path), _p(wsb), n, _stream(dev)))
+    return I, top_blk, path
+
+
+def hisa_block_means_update(keys, t0, rep, *, ratio, index_block, L) -> None:
+    """Writes into rep the means of the blocks that the step's L tokens (from position t0) complete."""
+    _need(keys, "keys", 3)
+    _code(keys)
+    B, Np_cap, D_i = keys.shape
+    _need(t0, "t0", 1, torch.int32, (B,))
+    _rep_arg(rep, keys, index_block)
+    dev = _same_gpu(keys=keys, t0=t0, rep=rep)
+    d = hisa_dims(B=B, L=L, ratio=ratio, window=0, topk=1, index_block=index_block, index_keep=1, H_i=1, D_i=D_i,
+                  H=1, Dk=1, Dv=1, Np_cap=Np_cap, Wl_cap=0, kI=0, mode=MODE_AUTO, idx_dtype=_code(keys),
+                  attn_dtype=F32)
+    _check(lib().hisa_block_means_update(ctypes.byref(d), _p(keys), _p(t0), _p(rep), _stream(dev)))
 
 
 NOALLOC_MAX_BYTES = 16 << 20  # HISA_DECODE_NOALLOC_MAX_BYTES

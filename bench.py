@@ -6,14 +6,22 @@ input: selection (gate, block means, coarse top-Kb, fine top-k, or the flat
 scan) followed by the sparse local + pooled attention that consumes it.  The
 default workload is one V4-Flash-shaped decode step at Np = 16384 pooled keys
 (B = 1, 64 x 128 bf16 indexer, top-512 of blocks of 64, 64 heads x 512, window
-128, sinks).  Inputs are resident in HBM before timing starts; R copies of the
-inputs are cycled so that each step reads data the 256 MiB Infinity Cache does
-not hold.
+128, sinks).  Inputs are resident in HBM before timing starts.
 
-Prints ONE JSON line: rows/s (B*L / step time), us per layer, step GB/s, the
-roofline of the dominant kernel (its algorithmic bytes or flops per launch over
-its average duration from HIP events on its stream), and the CPU oracle timed
-on the host's cores on a bounded sample of the same workload.
+Timing (HIP events on the stream the library launches on):
+  cold  before every step a kernel reads a 1 GiB buffer (outside the step's
+        events), which evicts the step's data from the 256 MiB Infinity Cache
+        and the L2s; K steps, each between its own pair of events; the median
+        is the headline, p10 / p90 beside it;
+  hot   K steps back to back between two events (data partly cache resident);
+  graph one step captured into a HIP graph and replayed, cold and hot.
+Selection alone is timed cold the same way.
+
+Prints ONE JSON line: rows/s (B*L / cold median step time), us per layer,
+step GB/s, the roofline of the dominant kernel (its algorithmic bytes or
+flops per launch over its cold median duration, from HIP events around its
+library call when that call launches it alone), and the CPU oracle timed on
+the host's cores on a bounded sample of the same workload.
 """
 import argparse
 import ctypes
@@ -29,7 +37,7 @@ sys.path.insert(0, ROOT)
 METRIC = "selected-query rows/sec + µs/layer decode at Np=16K; achieved HBM GB/s"
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
-MALL_DEFEAT_BYTES = 640 << 20
+FLUSH_BYTES = 1 << 30
 
 
 def parse():
@@ -38,7 +46,14 @@ def parse():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="v4flash_decode_np16384")
-    ap.add_argument("--graph", action="store_true", help="replay the timed steps from a captured HIP graph")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay figures")
+    ap.add_argument("--selector", choices=("cached", "stateless"), default="cached",
+                    help="decode selection: on the cached block means (the step keeps the cache current) or "
+                         "re-reading every key")
+    ap.add_argument("--crossover", action="store_true",
+                    help="flat vs HiSA decode selection and sparse vs dense prefill attention against Np")
+    ap.add_argument("--sweep-np", action="store_true",
+                    help="decode step time against the pooled count (both selectors), one JSON line per Np")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -110,6 +125,10 @@ def algorithmic(w, x, unique_kv_rows=None, flat_seqs=None):
                         "flops": sum(sum(min(Np[b], (int(x["t0"][b]) + j + 1) // w.ratio) for j in range(L))
                                      for b in flat) * w.H_i * w.D_i * 2},
         "topk_rows": {"bytes": len(flat) * L * kI * 4, "flops": 0},
+        # the cached decode reads each sequence's block means and its C candidate rows
+        "cached_decode": {"bytes": sum(nbb * w.D_i * 4 + min(C, n) * w.D_i * bf for nbb, n in zip(nb, Np))
+                          + idx_q + rows * kI * 4,
+                          "flops": sum(nb) * w.H_i * w.D_i * 2 + sum(min(C, n) for n in Np) * w.H_i * w.D_i * 2},
         "select_rows": {"bytes": idx_q + rows * kI * 4,
                         "flops": L * sum(nb) * w.H_i * w.D_i * 2 + rows * C * w.H_i * w.D_i * 2},
     }
@@ -126,12 +145,26 @@ def rate(a, seconds):
     return {"bound": "hbm", "achieved": round(ach, 1), "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4)}
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, x, seconds):
-    """The oracle (as it stands) on the host: threads each run whole decode
-    steps (selection + attention of one query row) until `seconds` elapse."""
-    import numpy as np
+    """The oracle (as it stands) on the host: threads each run whole query
+    rows (selection + attention of one row) until `seconds` elapse.  Threads:
+    OMP_NUM_THREADS when set (the host's CPU share), else every core in this
+    process's affinity set."""
     import oracle
-    ncores = max(1, min(16, len(os.sched_getaffinity(0))))
+    affinity = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    ncores = max(1, int(env)) if env.isdigit() else affinity
     d = oracle.Dims(B=w.B, L=w.L, ratio=w.ratio, window=w.window, topk=w.topk, index_block=w.index_block,
                     index_keep=w.index_keep, H_i=w.H_i, D_i=w.D_i, H=w.H, Dk=w.Dk, Dv=w.Dv, Np_cap=int(x["Np_cap"]))
     oracle.lib()
@@ -159,7 +192,229 @@ def cpu_baseline(w, x, seconds):
     n = sum(done)
     return {"value": n / el, "unit": "rows/s", "cores": ncores, "kind": "oracle",
             "sample": f"{n} query rows of {w.name} (selection + attention per row, whole rows on "
-                      f"{ncores} host threads for {el:.1f} s)"}
+                      f"{ncores} host threads for {el:.1f} s)",
+            "cpu_model": cpu_model(), "affinity_cores": affinity,
+            "threads_from": "OMP_NUM_THREADS" if env.isdigit() else "sched_getaffinity"}
+
+
+def percentiles(ms):
+    import numpy as np
+    a = np.asarray(ms, np.float64)
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)), "p90": float(np.percentile(a, 90)),
+            "mean": float(a.mean()), "n": int(a.size)}
+
+
+_flush_state = {}
+
+
+def flush():
+    """The cache flush: a read of 1 GiB (evicts the step's lines from the
+    Infinity Cache and the L2s; dirty ones are written back during the
+    flush, not during the step)."""
+    import torch
+    if not _flush_state:
+        _flush_state["buf"] = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda:0")
+        _flush_state["out"] = torch.empty((), dtype=torch.float32, device="cuda:0")
+    torch.sum(_flush_state["buf"], dim=0, out=_flush_state["out"])
+
+
+def harness(w, x, selector):
+    """Device copies of workload w's inputs x, outputs and workspaces, and the
+    step's two C calls with their arguments marshalled once."""
+    from types import SimpleNamespace
+
+    import torch
+    from top_kv_indexer_amd import hisa
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if w.bf16 else torch.float32
+    L = hisa.lib()
+
+    def put(a, dtype=dt):
+        return torch.from_numpy(a).to(dev).to(dtype).contiguous()
+
+    base = {k: put(x[k]) for k in ("q_idx", "keys", "q", "local_kv", "pooled_kv")}
+    base["w"] = put(x["w"], torch.float32)
+    t0 = put(x["t0"], torch.int32)
+    sinks = put(x["sinks"], torch.float32) if x["sinks"] is not None else None
+    kind = "decode" if (w.L == 1 and w.index_block) else ("prefill" if w.index_block else "flat")
+    sel_d = hisa.selection_dims(base["q_idx"], base["keys"], ratio=w.ratio, topk=w.topk,
+                                index_block=w.index_block, index_keep=w.index_keep)
+    I = torch.empty((w.B, w.L, w.topk), dtype=torch.int32, device=dev)
+    blk = torch.empty((w.B, w.L, w.index_keep), dtype=torch.int32, device=dev)
+    path = torch.empty((w.B,), dtype=torch.int32, device=dev)
+    att_d = hisa.attention_dims(base["q"], base["local_kv"] if w.window else None, base["pooled_kv"], I,
+                                ratio=w.ratio, window=w.window)
+    out = torch.empty((w.B, w.L, w.H, w.Dv), dtype=dt, device=dev)
+    cached = kind == "decode" and selector == "cached"
+    op = {"decode": hisa.OP_SELECT_DECODE_CACHED if cached else hisa.OP_SELECT_DECODE,
+          "prefill": hisa.OP_SELECT_PREFILL, "flat": hisa.OP_FLAT_TOPK}[kind]
+    rep = None
+    if cached:
+        # the cache as a decode loop keeps it: every block complete before this step
+        _, rep = hisa.hisa_block_scores(base["q_idx"], base["w"], base["keys"], t0, ratio=w.ratio,
+                                        index_block=w.index_block, want_rep=True)
+    ws_sel = torch.zeros(max(hisa.workspace_bytes(op, sel_d), 256), dtype=torch.uint8, device=dev)
+    ws_att = torch.zeros(max(hisa.workspace_bytes(hisa.OP_ATTENTION, att_d), 256), dtype=torch.uint8, device=dev)
+    main_stream = torch.cuda.current_stream(dev)
+    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    sel_ref, att_ref = ctypes.byref(sel_d), ctypes.byref(att_d)
+    n_sel, n_att = ws_sel.numel(), ws_att.numel()
+    c = base
+
+    def bound_calls(stream_handle):
+        """The step's two C calls with their arguments marshalled once."""
+        st = ctypes.c_void_p(stream_handle)
+        if kind == "flat":
+            a_sel = (sel_ref, P(c["q_idx"]), P(c["w"]), P(c["keys"]), P(t0), P(I), P(ws_sel), n_sel, st)
+            f_sel = L.flat_topk_select
+        elif cached:
+            a_sel = (sel_ref, P(c["q_idx"]), P(c["w"]), P(c["keys"]), P(rep), P(t0), P(I), P(blk), P(path),
+                     P(ws_sel), n_sel, st)
+            f_sel = L.hisa_select_decode_cached
+        else:
+            a_sel = (sel_ref, P(c["q_idx"]), P(c["w"]), P(c["keys"]), P(t0), P(I), P(blk), P(path), P(ws_sel),
+                     n_sel, st)
+            f_sel = L.hisa_select_decode if kind == "decode" else L.hisa_select_prefill
+        a_att = (att_ref, P(c["q"]), P(c["local_kv"]) if w.window else None, P(c["pooled_kv"]), P(I), P(sinks),
+                 P(t0), P(out), P(ws_att), n_att, st)
+        return f_sel, a_sel, L.sparse_local_pooled_attention, a_att
+
+    f1, a1, f2, a2 = bound_calls(main_stream.cuda_stream)
+
+    def call(f, a):
+        if f(*a):
+            raise hisa.HisaError(hisa.last_error())
+
+    def step(i=0):
+        call(f1, a1)
+        call(f2, a2)
+
+    def sel_only(i=0):
+        call(f1, a1)
+
+    def att_only(i=0):
+        call(f2, a2)
+
+    def cold(fn, k):
+        """k runs of fn, each after a flush and between its own two events;
+        returns the per-run milliseconds."""
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(k)]
+        for i in range(k):
+            flush()
+            ev[i][0].record()
+            fn(i)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in ev]
+
+    def hot(fn, k):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(k):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / k
+
+    return SimpleNamespace(**{k: v for k, v in locals().items() if k not in ("h", "SimpleNamespace")})
+
+
+def cold_ms(fn, k):
+    """k runs of fn(i), each after a flush and between its own two HIP events
+    (on the current stream); the median milliseconds."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(k)]
+    for i in range(k):
+        flush()
+        ev[i][0].record()
+        fn(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    return percentiles([a.elapsed_time(b) for a, b in ev])["median"]
+
+
+def crossover(args):
+    """The pages' engagement thresholds re-measured here (cold medians, one
+    JSON line per point): (1) decode selection, flat scan vs HiSA (re-reading
+    the keys, and on cached block means) at B = 1 for Np around the 1024
+    threshold; (2) a 512-row prefill chunk, selection + sparse attention vs
+    dense attention over every visible pooled row, against Np."""
+    import torch
+    from top_kv_indexer_amd import hisa, synth
+    dev = torch.device("cuda:0")
+    bf = torch.bfloat16
+
+    def put(a, dt=bf):
+        return torch.from_numpy(a).to(dev).to(dt).contiguous()
+
+    for Np in (600, 800, 1000, 1024, 1536, 2048, 4096, 8192, 16384, 32768):
+        w = synth.FLASH_DECODE.with_(name=f"crossover_decode_np{Np}", t0=[4 * Np], Np_cap=Np,
+                                     planted=min(32, Np // 64))
+        x = synth.make_inputs(w, 77, need_attention=False)
+        q, wt, keys, t0 = put(x["q_idx"]), put(x["w"], torch.float32), put(x["keys"]), put(x["t0"], torch.int32)
+        I = torch.empty((1, 1, 512), dtype=torch.int32, device=dev)
+        blk = torch.empty((1, 1, 16), dtype=torch.int32, device=dev)
+        path = torch.empty((1,), dtype=torch.int32, device=dev)
+        kw = dict(ratio=4, topk=512, index_block=64, index_keep=16, I=I, top_blk=blk, path=path)
+        line = {"kind": "decode_selection", "Np": Np}
+        hisa.hisa_select_decode(q, wt, keys, t0, **kw)
+        torch.cuda.synchronize()
+        line["gate"] = {0: "dense", 1: "flat", 2: "hisa"}[int(path[0])]
+        line["flat_us"] = round(1e3 * cold_ms(lambda i: hisa.hisa_select_decode(q, wt, keys, t0, mode=1, **kw),
+                                              args.steps), 3)
+        if line["gate"] == "hisa":
+            line["hisa_us"] = round(1e3 * cold_ms(lambda i: hisa.hisa_select_decode(q, wt, keys, t0, **kw),
+                                                  args.steps), 3)
+            _, rep = hisa.hisa_block_scores(q, wt, keys, t0, ratio=4, index_block=64, want_rep=True)
+            line["hisa_cached_us"] = round(1e3 * cold_ms(
+                lambda i: hisa.hisa_select_decode_cached(q, wt, keys, rep, t0, **kw), args.steps), 3)
+        print(json.dumps(line), flush=True)
+    L = 512
+    for Np in (512, 1024, 2048, 4096, 8192, 16384):
+        w = synth.PREFILL.with_(name=f"crossover_prefill_np{Np}", L=L, t0=[4 * Np - L])
+        x = synth.make_inputs(w, 78)
+        g = {k: put(x[k]) for k in ("q_idx", "keys", "q", "local_kv", "pooled_kv")}
+        wt, t0, sinks = put(x["w"], torch.float32), put(x["t0"], torch.int32), put(x["sinks"], torch.float32)
+        I = torch.empty((1, L, 512), dtype=torch.int32, device=dev)
+        out = torch.empty((1, L, 64, 512), dtype=bf, device=dev)
+        line = {"kind": "prefill_chunk_l512", "Np": Np}
+
+        def sparse(i):
+            hisa.hisa_select_prefill(g["q_idx"], wt, g["keys"], t0, ratio=4, topk=512, index_block=64, index_keep=16,
+                                     I=I)
+            hisa.sparse_local_pooled_attention(g["q"], g["local_kv"], g["pooled_kv"], I, sinks, t0, ratio=4,
+                                               window=128, out=out)
+
+        def dense(i):
+            hisa.sparse_local_pooled_attention(g["q"], g["local_kv"], g["pooled_kv"], None, sinks, t0, ratio=4,
+                                               window=128, out=out)
+
+        line["sparse_us"] = round(1e3 * cold_ms(sparse, max(3, args.steps // 4)), 3)
+        line["dense_us"] = round(1e3 * cold_ms(dense, max(3, args.steps // 4)), 3)
+        print(json.dumps(line), flush=True)
+        del g
+
+
+def sweep_np(args):
+    """Cold decode times against the pooled count, for both selectors: one
+    JSON line per Np (B = 1, the V4-Flash shapes otherwise)."""
+    import torch  # noqa: F401
+    from top_kv_indexer_amd import synth
+    for Np in (4096, 8192, 16384, 32768, 65536, 131072, 262144):
+        w = synth.FLASH_DECODE.with_(name=f"v4flash_decode_np{Np}", t0=[4 * Np], Np_cap=Np)
+        x = synth.make_inputs(w, synth.SEEDS[synth.FLASH_DECODE.name])
+        line = {"Np": Np}
+        for sel in ("stateless", "cached"):
+            H = harness(w, x, sel)
+            for i in range(args.warmup):
+                flush()
+                H.step(i)
+            line[sel] = {"selection_cold_us": round(percentiles(H.cold(H.sel_only, args.steps))["median"] * 1e3, 3),
+                         "step_cold_us": round(percentiles(H.cold(H.step, args.steps))["median"] * 1e3, 3),
+                         "step_hot_us": round(H.hot(H.step, args.steps) * 1e3, 3)}
+            del H
+        print(json.dumps(line), flush=True)
 
 
 def main():
@@ -184,97 +439,53 @@ def main():
 
     w = synth.WORKLOADS[args.workload]
     x = synth.make_inputs(w, synth.SEEDS[w.name])
-    dev = torch.device("cuda:0")
-    dt = torch.bfloat16 if w.bf16 else torch.float32
-    L = hisa.lib()
-
-    def put(a, dtype=dt):
-        return torch.from_numpy(a).to(dev).to(dtype).contiguous()
-
-    base = {k: put(x[k]) for k in ("q_idx", "keys", "q", "local_kv", "pooled_kv")}
-    base["w"] = put(x["w"], torch.float32)
-    t0 = put(x["t0"], torch.int32)
-    sinks = put(x["sinks"], torch.float32) if x["sinks"] is not None else None
-    per_copy = sum(v.numel() * v.element_size() for v in base.values())
-    R = max(2, -(-MALL_DEFEAT_BYTES // per_copy))
-    copies = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(R - 1)]
-
-    kind = "decode" if (w.L == 1 and w.index_block) else ("prefill" if w.index_block else "flat")
-    sel_d = hisa.selection_dims(base["q_idx"], base["keys"], ratio=w.ratio, topk=w.topk,
-                                index_block=w.index_block, index_keep=w.index_keep)
-    I = torch.empty((w.B, w.L, w.topk), dtype=torch.int32, device=dev)
-    blk = torch.empty((w.B, w.L, w.index_keep), dtype=torch.int32, device=dev)
-    path = torch.empty((w.B,), dtype=torch.int32, device=dev)
-    att_d = hisa.attention_dims(base["q"], base["local_kv"] if w.window else None, base["pooled_kv"], I,
-                                ratio=w.ratio, window=w.window)
-    out = torch.empty((w.B, w.L, w.H, w.Dv), dtype=dt, device=dev)
-    op = {"decode": hisa.OP_SELECT_DECODE, "prefill": hisa.OP_SELECT_PREFILL, "flat": hisa.OP_FLAT_TOPK}[kind]
-    ws_sel = torch.zeros(max(hisa.workspace_bytes(op, sel_d), 256), dtype=torch.uint8, device=dev)
-    ws_att = torch.zeros(max(hisa.workspace_bytes(hisa.OP_ATTENTION, att_d), 256), dtype=torch.uint8, device=dev)
-    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())  # noqa: E731
-    sel_ref, att_ref = ctypes.byref(sel_d), ctypes.byref(att_d)
-    n_sel, n_att = ws_sel.numel(), ws_att.numel()
-
-    # Pre-bound C calls (argument marshalling done once per copy).
-    calls = []
-    for c in copies:
-        if kind == "flat":
-            a_sel = (sel_ref, P(c["q_idx"]), P(c["w"]), P(c["keys"]), P(t0), P(I), P(ws_sel), n_sel, stream)
-            f_sel = L.flat_topk_select
-        else:
-            a_sel = (sel_ref, P(c["q_idx"]), P(c["w"]), P(c["keys"]), P(t0), P(I), P(blk), P(path), P(ws_sel),
-                     n_sel, stream)
-            f_sel = L.hisa_select_decode if kind == "decode" else L.hisa_select_prefill
-        a_att = (att_ref, P(c["q"]), P(c["local_kv"]) if w.window else None, P(c["pooled_kv"]), P(I), P(sinks),
-                 P(t0), P(out), P(ws_att), n_att, stream)
-        calls.append((f_sel, a_sel, L.sparse_local_pooled_attention, a_att))
-
-    def step(i):
-        f1, a1, f2, a2 = calls[i % R]
-        rc = f1(*a1)
-        rc |= f2(*a2)
-        if rc:
-            raise hisa.HisaError(hisa.last_error())
+    if args.sweep_np:
+        return sweep_np(args)
+    if args.crossover:
+        return crossover(args)
+    H = harness(w, x, args.selector)
+    dev, I, blk, path, kind, cached = H.dev, H.I, H.blk, H.path, H.kind, H.cached
+    step, sel_only, att_only, cold, hot, call, bound_calls = (H.step, H.sel_only, H.att_only, H.cold, H.hot, H.call,
+                                                             H.bound_calls)
+    main_stream = H.main_stream
 
     for i in range(args.warmup):
+        flush()
         step(i)
     torch.cuda.synchronize()
 
-    graph = None
-    if args.graph:
-        s = torch.cuda.Stream(device=dev)
-        s.wait_stream(torch.cuda.current_stream(dev))
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=s):
-            # the library launches on the stream it is given: point it at the capture stream
-            cap = ctypes.c_void_p(s.cuda_stream)
-            for i in range(args.steps):
-                f1, a1, f2, a2 = calls[i % R]
-                f1(*a1[:-1], cap)
-                f2(*a2[:-1], cap)
-        torch.cuda.synchronize()
-        graph.replay()
-        torch.cuda.synchronize()
-
-    # Timed region: K steps back to back.
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # Timed region: K cold steps (a flush before each, outside its events).
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    e0.record()
-    if graph is not None:
-        graph.replay()
-    else:
-        for i in range(args.steps):
-            step(i)
-    e1.record()
-    torch.cuda.synchronize()
+    step_ms = cold(step, args.steps)
     wall = time.perf_counter() - wall0
-    ms = e0.elapsed_time(e1) / args.steps
+    cold_step = percentiles(step_ms)
+    ms = cold_step["median"]
+    hot_ms = hot(step, args.steps)
+    sel_cold = percentiles(cold(sel_only, args.steps))
 
-    # Same steps again with the library's per-kernel HIP events (kernel roofline).
+    graph_fig = None
+    if not args.no_graph:
+        s = torch.cuda.Stream(device=dev)
+        s.wait_stream(main_stream)
+        graph = torch.cuda.CUDAGraph()
+        g1, b1, g2, b2 = bound_calls(s.cuda_stream)
+        with torch.cuda.graph(graph, stream=s):
+            call(g1, b1)
+            call(g2, b2)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        g_cold = percentiles(cold(lambda i: graph.replay(), args.steps))
+        g_hot = hot(lambda i: graph.replay(), args.steps)
+        graph_fig = {"cold_median_us": round(g_cold["median"] * 1e3, 3), "cold_p10_us": round(g_cold["p10"] * 1e3, 3),
+                     "cold_p90_us": round(g_cold["p90"] * 1e3, 3), "hot_us": round(g_hot * 1e3, 3)}
+
+    # Kernel ranking: the same cold steps with the library's per-kernel HIP
+    # events (each launch between its own two events).
     hisa.hisa_profile_enable(True)
     for i in range(args.steps):
+        flush()
         step(i)
     torch.cuda.synchronize()
     prof = hisa.hisa_profile_collect()
@@ -295,31 +506,22 @@ def main():
         kernels[name] = {"launches_per_step": n // args.steps, "avg_us": round(avg_ms * 1e3, 3)}
         if name in alg and avg_ms > 0:
             kernels[name].update(rate(alg[name], avg_ms / 1e3))
+    prof = {k: v for k, v in prof.items() if v[0] > 0}
     dominant = max(prof.items(), key=lambda kv: kv[1][1])[0]
     dom_avg_s = prof[dominant][1] / prof[dominant][0] / 1e3
-    timing = "HIP events around each launch"
-    # A per-launch event pair adds a few microseconds, which matters for
-    # microsecond kernels: when the library call holding the dominant kernel
-    # launches that kernel alone, time K back-to-back calls between two
-    # events on the library stream instead.
+    timing = "cold; mean of per-launch HIP event pairs (library kernel timing)"
+    # When the library call holding the dominant kernel launches that kernel
+    # alone, time that call: cold, its own event pair per launch, median.
     sel_kernels = {"decode": ("decode_scan_select",), "prefill": (), "flat": ()}[kind]
     alone = None
     if dominant in sel_kernels and set(prof) & {"decode_scan", "decode_select"} == set():
-        alone = 0
+        alone = sel_only
     elif dominant == "attention" and "attention_merge" not in prof:
-        alone = 2
+        alone = att_only
     if alone is not None:
-        torch.cuda.synchronize()
-        e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e2.record()
-        for i in range(args.steps):
-            f, a_ = calls[i % R][alone], calls[i % R][alone + 1]
-            if f(*a_):
-                raise hisa.HisaError(hisa.last_error())
-        e3.record()
-        torch.cuda.synchronize()
-        dom_avg_s = e2.elapsed_time(e3) / args.steps / 1e3
-        timing = f"{args.steps} back-to-back launches of its library call between two HIP events"
+        dom = percentiles(cold(alone, args.steps))
+        dom_avg_s = dom["median"] / 1e3
+        timing = f"cold; median of {args.steps} launches of its library call, each between two HIP events"
     a = alg.get(dominant, {"bytes": 0, "flops": 0})
     roof = rate(a, dom_avg_s)
     roof["peak"] = BF16_PEAK_TFLOPS if roof["bound"] == "mfma" else HBM_PEAK_GBPS
@@ -332,6 +534,7 @@ def main():
     step_bytes = sum(alg[k]["bytes"] for k in prof if k in alg and k not in ("attention_merge", "decode_select",
                                                                                 "topk_rows"))
     rows = w.B * w.L
+    us = lambda v: round(v * 1e3, 3)  # noqa: E731
     res = {
         "metric": METRIC,
         "value": round(rows / (ms / 1e3), 1),
@@ -348,9 +551,18 @@ def main():
         "config": {"workload": w.name, "B": w.B, "L": w.L, "Np": [int(n) for n in x["Np"]][:4],
                    "H_i": w.H_i, "D_i": w.D_i, "topk": w.topk, "index_block": w.index_block,
                    "index_keep": w.index_keep, "H": w.H, "head_dim": w.Dk, "window": w.window,
-                   "us_per_layer": round(ms * 1e3, 3), "step_algorithmic_bytes": step_bytes,
-                   "step_GBps": round(step_bytes / (ms / 1e3) / 1e9, 1), "input_copies_cycled": R,
-                   "hip_graph": bool(args.graph), "wall_s": round(wall, 4)},
+                   "selector": ("cached block means" if cached else "every key re-read") if kind == "decode"
+                   else kind,
+                   "us_per_layer": us(ms), "step_algorithmic_bytes": step_bytes,
+                   "step_GBps": round(step_bytes / (ms / 1e3) / 1e9, 1),
+                   "timing": "cold: 1 GiB read flush before each step, outside its HIP events; median",
+                   "cold_step_us": {"median": us(ms), "p10": us(cold_step["p10"]), "p90": us(cold_step["p90"])},
+                   "hot_step_us": us(hot_ms),
+                   "selection_only": {"rows_per_s": round(rows / (sel_cold["median"] / 1e3), 1),
+                                      "cold_median_us": us(sel_cold["median"]), "cold_p10_us": us(sel_cold["p10"]),
+                                      "cold_p90_us": us(sel_cold["p90"])},
+                   "hip_graph_step": graph_fig, "wall_s": round(wall, 4),
+                   "kernels_timing": "cold steps; per launch, the mean of its own HIP event pair (event cost included)"},
         "kernels": kernels,
         "roofline": roof,
     }

@@ -226,14 +226,36 @@ int flat_topk_select(const hisa_dims* d, const void* q_idx, const float* w, cons
  *             ls + r, ls = max(0, t0[b] - window + 1); rows run through
  *             position t0[b] + L - 1.
  *   pooled_kv (B, Np_cap, Dk) attn_dtype: the attention compressor's pooled rows.
- *   I         (B, L, kI) int32: pooled ids from a selection call (or any ids;
- *             dense attention over all pooled rows is I = 0..Np-1).
+ *   I         (B, L, kI) int32: pooled ids from a selection call (or any ids),
+ *             or NULL for dense attention over every visible pooled row (the
+ *             sparse combine's dense branch, Np <= index_topk, and layers
+ *             without an indexer such as the ratio-128 ones; HiSA issue,
+ *             Dependency and Consuming the selection): kI must then equal
+ *             Np_cap, and entry e of the list is pooled row e.
  *   sinks     (H) f32 or NULL.
  *   out       (B, L, H, Dv) attn_dtype. */
 int sparse_local_pooled_attention(const hisa_dims* d, const void* q, const void* local_kv,
                                   const void* pooled_kv, const int32_t* I, const float* sinks,
                                   const int32_t* t0, void* out, void* ws, size_t ws_bytes,
                                   void* stream);
+
+/* sparse_local_pooled_attention with the local window kept as a ring, the way
+ * a sliding-window KV cache of fixed capacity is written (hf2q source,
+ * forward_compressed_attention_rows: the window cache holds sliding_window
+ * rows and each token is written at the cache's write slot).  local_ring
+ * (B, Wl_cap, Dk): position s of sequence b sits in slot
+ * (ring_slot[b] + s - t0[b]) mod Wl_cap, where ring_slot (B) int32 (device)
+ * holds the slot of position t0[b]; ring_slot NULL means slot t0[b] mod
+ * Wl_cap.  Every position the step's rows see, t0 - window + 1 .. t0 + L - 1,
+ * must be present, so Wl_cap >= window + L - 1 (HISA_ERR_ARG otherwise): a
+ * decode step's ring is the window itself.  A sequence whose ring_slot is
+ * outside [0, Wl_cap) is not computed (output 0).  Everything else, including
+ * the workspace (hisa_workspace_bytes(HISA_OP_ATTENTION, d)), is as in
+ * sparse_local_pooled_attention. */
+int sparse_local_pooled_attention_ring(const hisa_dims* d, const void* q, const void* local_ring,
+                                       const void* pooled_kv, const int32_t* I, const float* sinks,
+                                       const int32_t* t0, const int32_t* ring_slot, void* out, void* ws,
+                                       size_t ws_bytes, void* stream);
 
 /* Workspace bytes the call `op` (enum hisa_op) needs for dims d (>= 256-byte
  * aligned offsets inside); 0 when it needs none.  Returns (size_t)-1 for

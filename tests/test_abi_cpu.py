@@ -167,3 +167,11 @@ def test_cached_decode_workspace_and_limits(lib):
     assert rc == -1
     rc = lib.hisa_block_means_update(ctypes.byref(dims()), fake, fake, None, None)
     assert rc == -1 and "NULL" in hisa.last_error()
+
+
+def test_ring_attention_needs_room_for_the_window(lib):
+    fake = ctypes.c_void_p(256)
+    d = dims(L=4, Wl_cap=130)  # window 128 + L - 1 = 131 positions
+    rc = lib.sparse_local_pooled_attention_ring(ctypes.byref(d), fake, fake, fake, fake, None, fake, None, fake, fake,
+                                                1 << 30, None)
+    assert rc == -1 and "ring" in hisa.last_error()

@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 from tests import parity
-from tests.test_gpu_parity import (EARLY, MIXED, MIXED_STREAM, check_attention, check_selection, counter_bytes,
+from tests.test_gpu_parity import (EARLY, MIXED, MIXED_STREAM, ROWS, check_attention, check_selection, counter_bytes,
                                    inputs, odims, run_attention, sel_kw)
 from top_kv_indexer_amd import synth
 
@@ -251,3 +251,86 @@ def test_decode_step_graph_replay(hisa):
         torch.cuda.synchronize()
         assert torch.equal(I, I_ref) and torch.equal(out, out_ref)
     assert (ws_sel[: counter_bytes(w.with_(Np_cap=int(x["Np_cap"])))].view(torch.int32) == 0).all()
+
+
+# ---------------------------------------------------------------- dense attention (no index list)
+
+@pytest.mark.parametrize("case", ["ratio128_decode", "ratio128_prefill", "ratio4_decode_b2"])
+def test_dense_attention_without_index_list(hisa, case):
+    # I = NULL: every visible pooled row (the sparse combine's dense branch and
+    # the ratio-128 layers, which have no indexer).  Against the oracle with
+    # the list 0..Np_cap-1 (it masks ids at or past V(t)), and equal to the
+    # attention over the dense fallback's index list.
+    w = {"ratio128_decode": synth.FLASH_DECODE.with_(name="r128_dense_b3", B=3, ratio=128,
+                                                     t0=[65536, 140000, 100], planted=0, Np_cap=1100),
+         "ratio128_prefill": synth.PREFILL.with_(name="r128_dense_prefill", L=256, ratio=128, t0=[65000],
+                                                 Np_cap=512),
+         "ratio4_decode_b2": synth.FLASH_DECODE.with_(name="flash_dense_b2", B=2, t0=[16000, 9000], planted=0,
+                                                      Np_cap=4000)}[case]
+    x, g = inputs(w, 58)
+    say(f"[run] dense attention, no index list, {w.name}")
+    out = hisa.sparse_local_pooled_attention(g["q"], g["local_kv"], g["pooled_kv"], None, g["sinks"], g["t0"],
+                                             ratio=w.ratio, window=w.window)
+    torch.cuda.synchronize()
+    Np_cap = int(x["Np_cap"])
+    full = torch.from_numpy(np.broadcast_to(np.arange(Np_cap, dtype=np.int32), (w.B, w.L, Np_cap)).copy())
+    say(f"  max-abs {check_attention(w, x, full, out, sample=24):.3g}")
+    Id, _, _ = hisa.hisa_select_prefill(g["q_idx"], g["w"], g["keys"], g["t0"],
+                                        **sel_kw(w.with_(topk=Np_cap), mode=2))
+    out2 = run_attention(hisa, w, g, Id)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+
+
+# ---------------------------------------------------------------- local window as a ring
+
+def ring_from_linear(x, w, R, slot0):
+    """The ring layout of the linear local rows: position s in slot (slot0[b] + s - t0[b]) mod R; every other
+    slot NaN (never read)."""
+    lin = x["local_kv"]
+    ring = np.full((w.B, R, lin.shape[2]), np.nan, np.float32)
+    for b in range(w.B):
+        t0 = int(x["t0"][b])
+        ls = max(0, t0 - w.window + 1)
+        for s in range(ls, t0 + w.L):
+            ring[b, (slot0[b] + s - t0) % R] = lin[b, s - ls]
+    return ring
+
+
+@pytest.mark.parametrize("case", ["decode_ring_is_window", "verify_l4", "prefill_l37_b4", "f32_generic"])
+def test_ring_window_equals_linear(hisa, case):
+    w = {"decode_ring_is_window": synth.FLASH_DECODE.with_(name="ring_flash", B=2, t0=[65536, 100], planted=4,
+                                                           Np_cap=16384),
+         "verify_l4": synth.FLASH_DECODE.with_(name="ring_verify_l4", B=3, L=4, t0=[65000, 5000, 60], planted=4,
+                                               Np_cap=16384),
+         "prefill_l37_b4": ROWS,
+         "f32_generic": synth.TINY_DECODE.with_(name="ring_tiny_f32", B=2, L=5, t0=[4000, 70], Np_cap=1100,
+                                                planted=2)}[case]
+    x, g = inputs(w, 61)
+    R = w.window + w.L - 1 + (0 if case == "decode_ring_is_window" else 19)
+    rng = np.random.default_rng(62)
+    slot0 = rng.integers(0, R, size=w.B).astype(np.int32)
+    dt = torch.bfloat16 if w.bf16 else torch.float32
+    ring = torch.from_numpy(ring_from_linear(x, w, R, slot0)).to("cuda").to(dt).contiguous()
+    say(f"[run] selection + ring attention, {w.name}, {R} slots")
+    fn = hisa.hisa_select_prefill if w.L > 1 else hisa.hisa_select_decode
+    I, _, _ = fn(g["q_idx"], g["w"], g["keys"], g["t0"], **sel_kw(w))
+    out_lin = run_attention(hisa, w, g, I)
+    s0 = torch.from_numpy(slot0).to("cuda")
+    out_ring = hisa.sparse_local_pooled_attention_ring(g["q"], ring, g["pooled_kv"], I, g["sinks"], g["t0"], s0,
+                                                       ratio=w.ratio, window=w.window)
+    torch.cuda.synchronize()
+    assert torch.equal(out_ring, out_lin)
+    say(f"  max-abs {check_attention(w, x, I, out_ring, sample=24):.3g}")
+    # the default slot of position t0 is t0 mod Wl_cap
+    ring2 = torch.from_numpy(ring_from_linear(x, w, R, (x["t0"] % R).astype(np.int32))).to("cuda").to(dt)
+    out2 = hisa.sparse_local_pooled_attention_ring(g["q"], ring2.contiguous(), g["pooled_kv"], I, g["sinks"],
+                                                   g["t0"], None, ratio=w.ratio, window=w.window)
+    # a slot outside the ring: that sequence is not computed
+    bad = s0.clone()
+    bad[0] = R
+    out3 = hisa.sparse_local_pooled_attention_ring(g["q"], ring, g["pooled_kv"], I, g["sinks"], g["t0"], bad,
+                                                   ratio=w.ratio, window=w.window)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, out_lin)
+    assert (out3[0] == 0).all() and torch.equal(out3[1:], out_lin[1:])

@@ -37,20 +37,46 @@ constexpr int kTile = 32;
 struct RowPlan {
   bool ok;
   int Np, V, ls, s_lo, n_loc, n_list;
+  int lbase;  // local_kv row of position s_lo (the first local entry)
 };
 
-__device__ __forceinline__ RowPlan row_plan(const KDims& d, int T0, int j) {
+// Ring slot of position t0[b] (ring layout only; read with t0).
+__device__ __forceinline__ int ring_slot0(const KDims& d, int b, int T0) {
+  if (!d.local_ring) return 0;
+  if (d.ring_slot) return d.ring_slot[b];
+  return T0 >= 0 ? T0 % d.Wl_cap : 0;
+}
+
+// Local rows: linear layout, row r holds position ls + r; ring layout
+// (Wl_cap >= window + L - 1, checked by the host), position s sits in slot
+// (S0 + s - T0) mod Wl_cap.  Either way local entry k is row lbase + k,
+// wrapped once past Wl_cap (which only the ring reaches).
+__device__ __forceinline__ RowPlan row_plan(const KDims& d, int T0, int S0, int j) {
   RowPlan r;
   const uint32_t np = T0 >= 0 ? div_ratio(d, (uint32_t)T0 + (uint32_t)d.L) : 0u;
   r.ls = max(0, T0 - d.window + 1);
-  r.ok = T0 >= 0 && np <= (uint32_t)d.Np_cap && (d.window == 0 || (long long)T0 + d.L - r.ls <= d.Wl_cap);
+  const bool local_ok = d.window == 0 || (d.local_ring ? (S0 >= 0 && S0 < d.Wl_cap)
+                                                       : (long long)T0 + d.L - r.ls <= d.Wl_cap);
+  r.ok = T0 >= 0 && np <= (uint32_t)d.Np_cap && local_ok;
   r.Np = r.ok ? (int)np : 0;
   const int t = T0 + j;
   r.V = visible(d, t, r.Np);
   r.s_lo = max(r.ls, t - d.window + 1);
   r.n_loc = (r.ok && d.window > 0) ? t - r.s_lo + 1 : 0;
   r.n_list = r.ok ? r.n_loc + d.kI : 0;
+  if (d.local_ring) {
+    int base = S0 + (r.s_lo - T0);  // in (-Wl_cap, 2 Wl_cap)
+    base = base < 0 ? base + d.Wl_cap : (base >= d.Wl_cap ? base - d.Wl_cap : base);
+    r.lbase = r.ok ? base : 0;
+  } else {
+    r.lbase = r.s_lo - r.ls;
+  }
   return r;
+}
+
+__device__ __forceinline__ int local_row(const KDims& d, const RowPlan& rp, int k) {
+  const int r = rp.lbase + k;
+  return r >= d.Wl_cap ? r - d.Wl_cap : r;
 }
 
 __device__ __forceinline__ bf16x8 pack8(const float (&p)[8]) {
@@ -182,16 +208,19 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
   const int n_geo = d.kI + d.window;
   const int per = ((n_geo + splits - 1) / splits + kTile - 1) / kTile * kTile;
   const int begin = min(n_geo, split * per), end = min(n_geo, begin + per);
-  const int* Irow = I + (size_t)row * d.kI;
+  // no index list (I == NULL): entry e names pooled row e (dense attention)
+  const int* Irow = I ? I + (size_t)row * d.kI : nullptr;
+  auto id_at = [&](int e) { return Irow ? Irow[e] : e; };
   auto ident_row = [&](int u) { return tid + u * NT; };
   int id_a[IPT];
 #pragma unroll
   for (int u = 0; u < IPT; ++u) {
     const int ea = begin + ident_row(u);
-    id_a[u] = (ea < end && ea < d.kI) ? Irow[ea] : -1;
+    id_a[u] = (ea < end && ea < d.kI) ? id_at(ea) : -1;
   }
   // issued before q, so waiting for it does not wait for q
   const int T0 = t0[__builtin_amdgcn_readfirstlane(b)];
+  const int S0 = ring_slot0(d, __builtin_amdgcn_readfirstlane(b), T0);
   // q is requested right after the ids and t0, so its latency overlaps
   // theirs and the row bookkeeping waits only for them
   if constexpr (NHG >= 4) {
@@ -246,9 +275,9 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
     src_el[r] = (lane ^ sw(RPW * wvs + r)) * 8;
     if constexpr (NHG == 1) asm volatile("" : "+v"(src_el[r]));
   }
-  const RowPlan rp = row_plan(d, T0, j);
+  const RowPlan rp = row_plan(d, T0, S0, j);
   // a row every sequence with a live row may read (dead rows point at it)
-  const int dummy = rp.n_loc > 0 ? -1 - (rp.s_lo - rp.ls) : 0;
+  const int dummy = rp.n_loc > 0 ? -1 - rp.lbase : 0;
   const bool any_row = rp.n_loc > 0 || rp.V > 0;
   // liveness and row code of list entry e (given its pooled id when e < kI):
   // code >= 0 is pooled row `code`, code < 0 local row -1 - code
@@ -261,7 +290,7 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
       return true;
     }
     if (e - d.kI >= rp.n_loc) return false;
-    code = -1 - (rp.s_lo - rp.ls + e - d.kI);
+    code = -1 - local_row(d, rp, e - d.kI);
     return true;
   };
   if constexpr (NHG >= 4) {
@@ -277,7 +306,7 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
     for (int u = 0; u < IPT; ++u) {
       if (cb + u * NT >= ce) break;  // whole tiles past the chunk's end: never read
       const int ea = cb + ident_row(u);
-      const int id = cb == begin ? id_a[u] : (ea < end && ea < d.kI ? Irow[ea] : -1);
+      const int id = cb == begin ? id_a[u] : (ea < end && ea < d.kI ? id_at(ea) : -1);
       int code;
       const uint64_t live = __ballot(resolve(ea, id, code));
       s_code[ident_row(u)] = code;
@@ -577,14 +606,17 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_fa(KDims d, c
     return (((r & 7) << 1) | ((r >> 3) & 1)) ^ hash;
   };
   const int n_geo = d.kI + d.window;
-  const int* Irow = I + (size_t)row * d.kI;
+  // no index list (I == NULL): entry e names pooled row e (dense attention)
+  const int* Irow = I ? I + (size_t)row * d.kI : nullptr;
+  auto id_at = [&](int e) { return Irow ? Irow[e] : e; };
   int id_a[IPT];
 #pragma unroll
   for (int u = 0; u < IPT; ++u) {
     const int ea = tid + u * NT;
-    id_a[u] = (ea < n_geo && ea < d.kI) ? Irow[ea] : -1;
+    id_a[u] = (ea < n_geo && ea < d.kI) ? id_at(ea) : -1;
   }
   const int T0 = t0[__builtin_amdgcn_readfirstlane(b)];
+  const int S0 = ring_slot0(d, __builtin_amdgcn_readfirstlane(b), T0);
   // this wave's 16 heads of q (the B operand of S), straight into registers
   bf16x8 qf[NS];
   {
@@ -592,8 +624,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_fa(KDims d, c
 #pragma unroll
     for (int s = 0; s < NS; ++s) qf[s] = *(const bf16x8*)(qrow + s * 32);
   }
-  const RowPlan rp = row_plan(d, T0, j);
-  const int dummy = rp.n_loc > 0 ? -1 - (rp.s_lo - rp.ls) : 0;
+  const RowPlan rp = row_plan(d, T0, S0, j);
+  const int dummy = rp.n_loc > 0 ? -1 - rp.lbase : 0;
   const bool any_row = rp.n_loc > 0 || rp.V > 0;
   auto resolve = [&](int e, int id, int& code) -> bool {
     code = dummy;
@@ -604,7 +636,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_fa(KDims d, c
       return true;
     }
     if (e - d.kI >= rp.n_loc) return false;
-    code = -1 - (rp.s_lo - rp.ls + e - d.kI);
+    code = -1 - local_row(d, rp, e - d.kI);
     return true;
   };
   // head c of this wave: running max m (log2 domain) and sum l, on all four
@@ -634,7 +666,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_fa(KDims d, c
     for (int u = 0; u < IPT; ++u) {
       if (cb + u * NT >= ce) break;
       const int ea = cb + tid + u * NT;
-      const int id = cb == 0 ? id_a[u] : (ea < n_geo && ea < d.kI ? Irow[ea] : -1);
+      const int id = cb == 0 ? id_a[u] : (ea < n_geo && ea < d.kI ? id_at(ea) : -1);
       int code;
       const uint64_t live = __ballot(resolve(ea, id, code));
       s_code[tid + u * NT] = code;
@@ -871,16 +903,17 @@ __global__ __launch_bounds__(256) void k_attn_valu(KDims d, const T* __restrict_
   __shared__ float s_red[4];
   const int row = blockIdx.x, h = blockIdx.y;
   const int b = row / d.L, j = row % d.L, tid = threadIdx.x;
-  const RowPlan rp = row_plan(d, t0[b], j);
+  const int T0 = t0[b];
+  const RowPlan rp = row_plan(d, T0, ring_slot0(d, b, T0), j);
   const int n = rp.n_list;
   const float scale = 1.0f / sqrtf((float)d.Dk);
   for (int e = tid; e < d.Dk; e += 256) s_q[e] = ldf(q + ((size_t)row * d.H + h) * d.Dk + e) * scale;
   // s_row: >= 0 pooled id, <= -2 local row -(r + 2), -1 masked
   for (int e = tid; e < n; e += 256) {
     int code = -1;
-    if (e < rp.n_loc) code = -((rp.s_lo - rp.ls + e) + 2);
+    if (e < rp.n_loc) code = -(local_row(d, rp, e) + 2);
     else {
-      const int id = I[(size_t)row * d.kI + e - rp.n_loc];
+      const int id = I ? I[(size_t)row * d.kI + e - rp.n_loc] : e - rp.n_loc;
       if (id >= 0 && id < rp.V) code = id;
     }
     s_row[e] = code;

@@ -295,6 +295,10 @@ int prepare(int op, const hisa_dims* d, KDims* k, Layout* l, void* ws, size_t ws
   return check_ws(*l, ws, ws_bytes);
 }
 
+int attention_call(const hisa_dims* d, const void* q, const void* local_kv, const void* pooled_kv, const int32_t* I,
+                   const float* sinks, const int32_t* t0, const int32_t* ring_slot, bool ring, void* out, void* ws,
+                   size_t ws_bytes, void* stream);
+
 }  // namespace
 
 extern "C" {
@@ -506,13 +510,26 @@ int sparse_local_pooled_attention(const hisa_dims* d, const void* q, const void*
                                   const int32_t* I, const float* sinks, const int32_t* t0, void* out, void* ws,
                                   size_t ws_bytes, void* stream) {
   g_err.clear();
+  return attention_call(d, q, local_kv, pooled_kv, I, sinks, t0, nullptr, false, out, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int attention_call(const hisa_dims* d, const void* q, const void* local_kv, const void* pooled_kv, const int32_t* I,
+                   const float* sinks, const int32_t* t0, const int32_t* ring_slot, bool ring, void* out, void* ws,
+                   size_t ws_bytes, void* stream) {
   KDims k;
   Layout l;
   int rc = prepare(HISA_OP_ATTENTION, d, &k, &l, ws, ws_bytes);
   if (rc) return rc;
+  k.local_ring = ring ? 1 : 0;
+  k.ring_slot = ring ? ring_slot : nullptr;
   if ((rc = check_ptrs({q, pooled_kv, t0, out}, "q, pooled_kv, t0, out"))) return rc;
   if (d->window > 0 && !local_kv) return fail(HISA_ERR_ARG, "local_kv is NULL with window > 0");
-  if (d->kI > 0 && !I) return fail(HISA_ERR_ARG, "I is NULL with kI > 0");
+  if (!I && d->kI != d->Np_cap)
+    return fail(HISA_ERR_ARG, "I is NULL (every pooled row) but kI = %d is not Np_cap = %d", d->kI, d->Np_cap);
   const bool bf = d->attn_dtype == HISA_BF16;
   hipStream_t st = (hipStream_t)stream;
   float* partial = l.splits > 1 ? at<float>(ws, l.partial) : nullptr;
@@ -523,6 +540,21 @@ int sparse_local_pooled_attention(const hisa_dims* d, const void* q, const void*
     e = timed("attention_merge", st, [&] { return hisa::launch_attention_merge(k, bf, partial, sinks, out, l.splits, st); });
   if (e != hipSuccess) return launch_fail(e, "attention");
   return HISA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sparse_local_pooled_attention_ring(const hisa_dims* d, const void* q, const void* local_ring,
+                                       const void* pooled_kv, const int32_t* I, const float* sinks,
+                                       const int32_t* t0, const int32_t* ring_slot, void* out, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  g_err.clear();
+  if (d && d->window > 0 && (long long)d->Wl_cap < (long long)d->window + d->L - 1)
+    return fail(HISA_ERR_ARG, "a ring of Wl_cap = %d slots cannot hold window + L - 1 = %lld positions", d->Wl_cap,
+                (long long)d->window + d->L - 1);
+  return attention_call(d, q, local_ring, pooled_kv, I, sinks, t0, ring_slot, true, out, ws, ws_bytes, stream);
 }
 
 int hisa_profile_enable(int on) {

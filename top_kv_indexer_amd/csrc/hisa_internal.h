@@ -20,6 +20,8 @@ struct KDims {
   int ratio_shift; // log2(ratio) when ratio is a power of two, else -1
   float w_scale;   // (float)(1 / sqrt(H_i * D_i)), rounded once from double
   float attn_scale_log2;  // (float)(log2(e) / sqrt(Dk))
+  int local_ring;         // local_kv is a ring of Wl_cap slots (attention)
+  const int* ring_slot;   // ring: slot of position t0[b] per sequence, or NULL for t0[b] mod Wl_cap
 };
 
 // Launchers (kernel files).  Each returns hipSuccess or the launch error.

@@ -1953,6 +1953,13 @@ __global__ __launch_bounds__(256) void k_cached_coarse(KDims d, const uint16_t* 
 #pragma unroll
   for (int i = 0; i < 16; ++i) qv[i] = qrow[i];
   const float wh = w[(size_t)b * 64 + lane] * d.w_scale;
+  // the cached means of this wave's blocks, also requested before t0 arrives
+  // (a block completed by this step is recomputed below instead)
+  const int beta0 = x * kCachedBlocksPerWg + 4 * wv;
+  float* repb = rep + (size_t)b * d.nb_cap * 128;
+  float2 mc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) mc[j] = *(const float2*)&repb[(size_t)min(beta0 + j, d.nb_cap - 1) * 128 + 2 * lane];
   const SeqInfo si = seq_info(d, t0b);
   if (!si.ok || si.path == PATH_DENSE) {
     if (x == 0 && wv == 0) write_unscored(d, si, b, I, top_blk, path);
@@ -1973,18 +1980,14 @@ __global__ __launch_bounds__(256) void k_cached_coarse(KDims d, const uint16_t* 
   // that existed before it
   const int first_new = (int)div_ratio(d, (uint32_t)t0b) / bsz;
   const uint16_t* kb = keys + (size_t)b * d.Np_cap * 128;
-  float* repb = rep + (size_t)b * d.nb_cap * 128;
-  const int beta0 = x * kCachedBlocksPerWg + 4 * wv;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int beta = beta0 + j;
     if (beta >= si.nb) break;  // uniform over the wave
-    float2 m;
+    float2 m = mc[j];
     if (beta >= first_new) {
       m = block_mean_lane(kb, beta, bsz);
       *(float2*)&repb[(size_t)beta * 128 + 2 * lane] = m;
-    } else {
-      m = *(const float2*)&repb[(size_t)beta * 128 + 2 * lane];
     }
     *(float2*)&s_rep[wv][j][2 * lane] = m;
   }
@@ -2017,6 +2020,7 @@ __global__ __launch_bounds__(256) void k_cached_coarse(KDims d, const uint16_t* 
   const int ngmax = (gridDim.x + kArriveGroup - 1) / kArriveGroup;
   const bool last = publish(
       [&] {
+        if (ngrp == 1) return arrive(cnt + (size_t)b * kCntStride, 1, nwg);  // one atomic on the path
         const int members = min(kArriveGroup, nwg - grp * kArriveGroup);
         int* c_grp = cnt + (size_t)(d.B + (size_t)b * ngmax + grp) * kCntStride;
         return arrive(c_grp, 1, members) && arrive(cnt + (size_t)b * kCntStride, 1, ngrp);
@@ -2054,6 +2058,8 @@ __global__ __launch_bounds__(256) void k_cached_fine(KDims d, const uint16_t* __
   const int b = blockIdx.y, slab = blockIdx.x;
   const int tid = threadIdx.x, lane = lane_id(), wv = wave_id(), g = lane >> 4, c = lane & 15;
   const int t0b = t0[b];
+  // the retained blocks (meaningful on the HiSA path only; always in bounds)
+  const int blk_tid = tid < d.index_keep ? blk[(size_t)b * d.index_keep + tid] : 0;
   issue_q_lds(q_idx + (size_t)b * 64 * 128, s_q);
   const float* wrow = w + (size_t)b * 64;
   float wl[4][4];
@@ -2074,7 +2080,7 @@ __global__ __launch_bounds__(256) void k_cached_fine(KDims d, const uint16_t* __
     __builtin_amdgcn_s_waitcnt(0x0F70);  // no global->LDS copy outlives the workgroup
     return;
   }
-  if (tid < si.Kb && hisa) s_blk[tid] = blk[(size_t)b * d.index_keep + tid];
+  if (tid < si.Kb && hisa) s_blk[tid] = blk_tid;
   __syncthreads();
   auto pos = [&](int cc) { return hisa ? (s_blk[cc >> lbsz] << lbsz) + (cc & (bsz - 1)) : cc; };
   const int cand = min(slab * 64 + wv * 16 + c, n - 1);

@@ -20,7 +20,8 @@ PATH_INVALID, PATH_DENSE, PATH_FLAT, PATH_HISA = -1, 0, 1, 2
 
 EXPORTS = ("hisa_block_scores", "hisa_select_decode", "hisa_select_decode_noalloc", "hisa_select_decode_cached",
            "hisa_block_means_update", "hisa_select_prefill", "flat_topk_select",
-           "sparse_local_pooled_attention", "hisa_workspace_bytes", "hisa_last_error", "hisa_abi_version",
+           "sparse_local_pooled_attention", "sparse_local_pooled_attention_ring", "hisa_workspace_bytes",
+           "hisa_last_error", "hisa_abi_version",
            "hisa_profile_enable", "hisa_profile_collect")
 
 
@@ -59,9 +60,10 @@ def lib() -> ctypes.CDLL:
         L.hisa_select_prefill.argtypes = sel + [vp, vp, vp, vp, sz, vp]
         L.flat_topk_select.argtypes = sel + [vp, vp, sz, vp]
         L.sparse_local_pooled_attention.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.sparse_local_pooled_attention_ring.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         for f in ("hisa_block_scores", "hisa_select_decode", "hisa_select_decode_noalloc", "hisa_select_decode_cached",
                   "hisa_block_means_update", "hisa_select_prefill", "flat_topk_select",
-                  "sparse_local_pooled_attention"):
+                  "sparse_local_pooled_attention", "sparse_local_pooled_attention_ring"):
             getattr(L, f).restype = i32
         L.hisa_workspace_bytes.argtypes = [i32, dp]
         L.hisa_workspace_bytes.restype = sz
@@ -324,10 +326,12 @@ def flat_topk_select(q_idx, w, keys, t0, *, ratio, topk, I=None, ws=None) -> tor
 
 
 def attention_dims(q, local_kv, pooled_kv, I, *, ratio, window, Dv=None) -> hisa_dims:
+    """I None: dense over every visible pooled row (kI = Np_cap)."""
     B, L, H, Dk = q.shape
     return hisa_dims(B=B, L=L, ratio=ratio, window=window, topk=1, index_block=0, index_keep=1, H_i=1, D_i=1,
                      H=H, Dk=Dk, Dv=Dk if Dv is None else Dv, Np_cap=pooled_kv.shape[1],
-                     Wl_cap=0 if local_kv is None else local_kv.shape[1], kI=I.shape[2], mode=MODE_AUTO,
+                     Wl_cap=0 if local_kv is None else local_kv.shape[1],
+                     kI=pooled_kv.shape[1] if I is None else I.shape[2], mode=MODE_AUTO,
                      idx_dtype=F32, attn_dtype=_code(q))
 
 
@@ -341,7 +345,8 @@ def _attn_args(q, local_kv, pooled_kv, I, sinks, t0, window, Dv, out, ws):
         _need(local_kv, "local_kv", 3, q.dtype, (B, None, Dk))
     elif window > 0:
         raise HisaError("local_kv is None but window > 0")
-    _need(I, "I", 3, torch.int32, (B, L, None))
+    if I is not None:
+        _need(I, "I", 3, torch.int32, (B, L, None))
     _need(t0, "t0", 1, torch.int32, (B,))
     if sinks is not None:
         _need(sinks, "sinks", 1, torch.float32, (H,))
@@ -352,7 +357,7 @@ def _attn_args(q, local_kv, pooled_kv, I, sinks, t0, window, Dv, out, ws):
 
 def sparse_local_pooled_attention(q, local_kv, pooled_kv, I, sinks, t0, *, ratio, window, Dv=None, out=None,
                                   ws=None) -> torch.Tensor:
-    """Sparse local + pooled combine; returns out (B, L, H, Dv)."""
+    """Sparse local + pooled combine; returns out (B, L, H, Dv).  I None: every visible pooled row."""
     dev = _attn_args(q, local_kv, pooled_kv, I, sinks, t0, window, Dv, out, ws)
     d = attention_dims(q, local_kv, pooled_kv, I, ratio=ratio, window=window, Dv=Dv)
     if out is None:
@@ -360,6 +365,24 @@ def sparse_local_pooled_attention(q, local_kv, pooled_kv, I, sinks, t0, *, ratio
     wsb, n = _workspace(OP_ATTENTION, d, dev, ws)
     _check(lib().sparse_local_pooled_attention(ctypes.byref(d), _p(q), _p(local_kv), _p(pooled_kv), _p(I), _p(sinks),
                                                _p(t0), _p(out), _p(wsb), n, _stream(dev)))
+    return out
+
+
+def sparse_local_pooled_attention_ring(q, local_ring, pooled_kv, I, sinks, t0, ring_slot=None, *, ratio, window,
+                                       Dv=None, out=None, ws=None) -> torch.Tensor:
+    """The combine with the local window as a ring of local_ring.shape[1] slots: position s of sequence b in
+    slot (ring_slot[b] + s - t0[b]) mod Wl_cap (ring_slot None: t0[b] mod Wl_cap); returns out (B, L, H, Dv)."""
+    dev = _attn_args(q, local_ring, pooled_kv, I, sinks, t0, window, Dv, out, ws)
+    if ring_slot is not None:
+        _need(ring_slot, "ring_slot", 1, torch.int32, (q.shape[0],))
+        _same_gpu(q=q, ring_slot=ring_slot)
+    d = attention_dims(q, local_ring, pooled_kv, I, ratio=ratio, window=window, Dv=Dv)
+    if out is None:
+        out = torch.empty((d.B, d.L, d.H, d.Dv), dtype=q.dtype, device=dev)
+    wsb, n = _workspace(OP_ATTENTION, d, dev, ws)
+    _check(lib().sparse_local_pooled_attention_ring(ctypes.byref(d), _p(q), _p(local_ring), _p(pooled_kv), _p(I),
+                                                    _p(sinks), _p(t0), _p(ring_slot), _p(out), _p(wsb), n,
+                                                    _stream(dev)))
     return out
 
 

@@ -144,15 +144,17 @@ int hisa_select_decode(const hisa_dims* d, const void* q_idx, const float* w, co
  * coarse stage costs O(nb) scores and the fine stage O(Kb * b), so a step need
  * not read every key; The pooled stream and positions: the pooled stream only
  * grows in whole windows, so the mean of a complete block never changes).
- * Same gate, outputs and tie rule as hisa_select_decode (L must be 1), but the
+ * Same gate, outputs and tie rule as hisa_select_decode, and L >= 1: a decode
+ * step (L = 1) or a short multi-token verify chunk, whose rows each select on
+ * their own with the masks of the HiSA batched path (B * L <= 65535).  The
  * block means come from rep, a caller-owned (B, nb_cap, D_i) f32 cache,
  * nb_cap = Np_cap / index_block, row beta of sequence b holding the mean of
  * its pooled key rows beta*b .. beta*b + b - 1 (rows summed in order in f32,
  * then scaled by 1/b).  Before the call rep must hold every block completed
  * before this step (all blocks below floor(floor(t0 / ratio) / index_block));
- * the call computes the block this step's token completes, if any, from the
- * keys and writes it into rep, so calling it step after step keeps the cache
- * current.  hisa_block_means_update fills a cache (e.g. after a prefill
+ * the call computes the blocks this step's tokens complete, if any, from the
+ * keys and writes them into rep, so calling it step after step keeps the
+ * cache current.  hisa_block_means_update fills a cache (e.g. after a prefill
  * chunk).  A step reads nb * D_i * 4 bytes of means and at most
  * index_keep * index_block key rows instead of all Np_b key rows.
  * Shapes: bf16 keys, H_i = 64, D_i = 128, index_block > 0, nb_cap <= 4096,
@@ -196,7 +198,9 @@ int hisa_select_decode_noalloc(const hisa_dims* d, const void* q_idx, const floa
                                void* stream);
 
 /* Multi-row selection (HiSA issue, HiSA batched path: prefill chunks and
- * multi-token verify; any L >= 1).  Per query row j: valid_len = V(t0+j);
+ * multi-token verify; any L >= 1).  Chunks of at most 8 rows per sequence
+ * (verify) take the cached-means kernels of hisa_select_decode_cached on
+ * block means computed into the workspace.  Per query row j: valid_len = V(t0+j);
  * blocks with b*beta >= valid_len score -1e30; candidates at or past
  * valid_len score -1e30.  Rows with fewer than k visible rows then carry
  * masked ids, which the attention call re-masks.

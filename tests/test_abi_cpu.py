@@ -67,6 +67,10 @@ def test_workspace_sizes(lib):
     # candidates past one wave's registers: coarse scores per row and the flat scan
     assert hisa.workspace_bytes(hisa.OP_SELECT_PREFILL, dims(L=2048, index_keep=64)) == (
         rep + 2048 * 256 * 4 + 2048 * 16384 * 4)
+    # a verify chunk (L <= 8): every block mean (f32), then per row the
+    # cached-means selection (counters, block scores, kept blocks, candidates)
+    assert hisa.workspace_bytes(hisa.OP_SELECT_PREFILL, dims(L=4)) == (
+        256 * 128 * 4 + 768 + 4 * 256 * 4 + 256 + 4 * 1024 * 4)
     # no hierarchy: only the flat scan
     assert hisa.workspace_bytes(hisa.OP_SELECT_PREFILL, dims(L=4, index_block=0, Np_cap=1000)) == (
         (4 * 1000 * 4 + 255) // 256 * 256)
@@ -156,7 +160,7 @@ def test_cached_decode_workspace_and_limits(lib):
     assert hisa.workspace_bytes(hisa.OP_SELECT_DECODE_CACHED, d) == 256 + 256 * 4 + 256 + 1024 * 4
     assert hisa.workspace_bytes(hisa.OP_BLOCK_MEANS_UPDATE, d) == 0
     for kw in (dict(index_block=0), dict(Np_cap=64 * 4097), dict(index_keep=32), dict(mode=hisa.MODE_FORCE_FLAT),
-               dict(index_keep=4), dict(idx_dtype=hisa.F32), dict(H_i=32), dict(L=2)):
+               dict(index_keep=4), dict(idx_dtype=hisa.F32), dict(H_i=32), dict(B=40000, L=2)):
         bad = dims(**kw)
         assert lib.hisa_workspace_bytes(hisa.OP_SELECT_DECODE_CACHED, ctypes.byref(bad)) == ctypes.c_size_t(-1).value, kw
     fake = ctypes.c_void_p(256)

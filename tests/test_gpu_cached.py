@@ -184,3 +184,51 @@ def test_cached_decode_dense_switch_leaves_cache(hisa):
     assert torch.equal(rep, rep0)
     np.testing.assert_array_equal(parity.to_np(I)[0, 0], np.arange(16384))
     assert parity.to_np(path)[0] == hisa.PATH_DENSE
+
+
+VERIFY = synth.Workload("verify_b4_l8", B=4, L=8, ratio=1, window=128, topk=512, index_block=64, index_keep=16,
+                        H_i=64, D_i=128, H=64, Dk=512, Dv=512, bf16=True,
+                        # ratio 1: Np = 1083 + L (HiSA; at L = 8 there are 17 blocks and the rows see 1084 ..
+                        # 1091, so block 16 is eligible but partly hidden on the first rows), 694 + L (flat),
+                        # 294 + L (dense), 16384 + L (HiSA)
+                        t0=[1083, 694, 294, 16384], planted=4, Np_cap=16400)
+
+
+@pytest.mark.parametrize("L", [1, 2, 4, 8])
+def test_short_prefill_chunks(hisa, L):
+    # hisa_select_prefill with at most 8 rows per sequence: block means of every
+    # complete block into the workspace, then the cached-means selection per row
+    w = VERIFY.with_(L=L)
+    x, g = inputs(w, 63)
+    say(f"[run] short prefill chunk, L = {L}")
+    I, blk, path = hisa.hisa_select_prefill(g["q_idx"], g["w"], g["keys"], g["t0"], **sel_kw(w))
+    torch.cuda.synchronize()
+    assert parity.to_np(path).tolist() == [hisa.PATH_HISA, hisa.PATH_FLAT, hisa.PATH_DENSE, hisa.PATH_HISA]
+    check_selection(w, x, I, blk, path)
+    # the same call on a workspace holding another call's data (the counters are zeroed by the call itself)
+    d = hisa.selection_dims(g["q_idx"], g["keys"], **sel_kw(w))
+    ws = torch.full((hisa.workspace_bytes(hisa.OP_SELECT_PREFILL, d),), 0x5A, dtype=torch.uint8, device="cuda")
+    I2, blk2, path2 = hisa.hisa_select_prefill(g["q_idx"], g["w"], g["keys"], g["t0"], **sel_kw(w), ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(I2, I) and torch.equal(blk2, blk) and torch.equal(path2, path)
+
+
+def test_cached_verify_chunk_updates_the_cache(hisa):
+    # A 4-row verify chunk on a caller cache: rows select on their own, and the
+    # blocks the chunk's tokens complete (here block 255 of the ratio-4
+    # sequence) are written into the cache.
+    w = synth.FLASH_DECODE.with_(name="flash_verify_l4", L=4, t0=[65532], planted=32)
+    x, g = inputs(w, synth.SEEDS[synth.FLASH_DECODE.name])
+    dev = torch.device("cuda")
+    rep = torch.full((1, 256, 128), float("nan"), dtype=torch.float32, device=dev)
+    hisa.hisa_block_means_update(g["keys"], torch.zeros(1, dtype=torch.int32, device=dev), rep, ratio=4,
+                                 index_block=64, L=65532)
+    say("[run] cached verify chunk, L = 4")
+    I, blk, path = hisa.hisa_select_decode_cached(g["q_idx"], g["w"], g["keys"], rep, g["t0"], **sel_kw(w))
+    torch.cuda.synchronize()
+    check_selection(w, x, I, blk, path)
+    _, rep_orc = oracle.block_scores(odims(w, x), x["q_idx"], x["w"], x["keys"], x["t0"])
+    np.testing.assert_allclose(parity.to_np(rep[0]), rep_orc[0], rtol=1e-6, atol=1e-7)
+    # rows 0..2 see 16383 pooled rows: block 255 is eligible there (its first
+    # row is visible) but its last row, pooled row 16383, is masked
+    assert (parity.to_np(I)[0, :3] < 16383).all()

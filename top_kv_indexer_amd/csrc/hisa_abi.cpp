@@ -83,8 +83,11 @@ int make_kdims(int op, const hisa_dims* d, KDims* k) {
     if (op == HISA_OP_BLOCK_SCORES && d->index_block == 0) return fail(HISA_ERR_ARG, "hisa_block_scores needs index_block > 0");
     if (op == HISA_OP_BLOCK_MEANS_UPDATE && d->index_block == 0)
       return fail(HISA_ERR_ARG, "hisa_block_means_update needs index_block > 0");
-    if ((op == HISA_OP_SELECT_DECODE || op == HISA_OP_SELECT_DECODE_CACHED) && d->L != 1)
-      return fail(HISA_ERR_ARG, "decode selection needs L == 1 (got %d)", d->L);
+    if (op == HISA_OP_SELECT_DECODE && d->L != 1)
+      return fail(HISA_ERR_ARG, "hisa_select_decode needs L == 1 (got %d)", d->L);
+    if (op == HISA_OP_SELECT_DECODE_CACHED && (long long)d->B * d->L > 65535)
+      return fail(HISA_ERR_ARG, "hisa_select_decode_cached takes at most 65535 query rows (B * L = %lld)",
+                  (long long)d->B * d->L);
     const long long rows = (long long)d->B * d->L;
     if (rows * d->H_i * d->D_i > kMaxElems || (long long)d->B * d->Np_cap * d->D_i > kMaxElems ||
         rows * d->Np_cap > kMaxElems || rows * d->topk > kMaxElems)
@@ -130,13 +133,21 @@ size_t take(Layout& l, size_t bytes) {
 
 // Which kernels the batched selection runs (hisa_select_prefill); the
 // workspace holds only what they use.
+constexpr int kSmallChunk = 8;  // query rows per sequence up to which a chunk takes the cached-means kernels
+
 struct PrefillPlan {
+  bool small;        // short chunk: every block mean, then the cached-means selection per row
   bool rows;         // k_select_rows: one query row per wave (block means as bf16 parts)
   bool coarse_fine;  // the coarse-score GEMM, then one workgroup per row for top-Kb + fine + top-k
   bool flat_scan;    // flat scores of every row, then the row top-k (flat sequences)
 };
 PrefillPlan prefill_plan(const KDims& k, bool bf) {
   PrefillPlan p;
+  p.small = k.L <= kSmallChunk && (long long)k.B * k.L <= 65535 && hisa::cached_decode_ok(k, bf);
+  if (p.small) {
+    p.rows = p.coarse_fine = p.flat_scan = false;
+    return p;
+  }
   p.rows = k.nb_cap > 0 && hisa::select_rows_ok(k, bf);
   p.coarse_fine = k.nb_cap > 0 && !p.rows;
   // The row selection also takes the flat sequences when they are short: with
@@ -175,6 +186,14 @@ Layout layout(int op, const hisa_dims* d, const KDims& k) {
     case HISA_OP_SELECT_PREFILL: {
       if (k.force_dense) break;
       const PrefillPlan p = prefill_plan(k, bf);
+      if (p.small) {
+        l.rep = take(l, B * nb_cap * d->D_i * sizeof(float));
+        l.cnt = take(l, hisa::cached_counter_ints(k) * sizeof(int));
+        l.cscore = take(l, B * L * nb_cap * sizeof(float));
+        l.blk = take(l, B * L * (size_t)d->index_keep * sizeof(int));
+        l.fscore = take(l, hisa::cached_fine_floats(k) * sizeof(float));
+        break;
+      }
       if (nb_cap > 0) {
         l.rep = take(l, B * nb_cap * d->D_i * sizeof(float));
         l.rep3 = hisa::idx_mfma_ok(k, bf) ? take(l, 3 * B * nb_cap * d->D_i * sizeof(uint16_t)) : 0;
@@ -396,7 +415,7 @@ int hisa_block_means_update(const hisa_dims* d, const void* keys, const int32_t*
   if ((rc = check_ptrs({keys, t0, rep}, "keys, t0, rep"))) return rc;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = timed("block_means_update", st, [&] {
-    return hisa::launch_rep_update(k, d->idx_dtype == HISA_BF16, keys, t0, rep, st);
+    return hisa::launch_rep_update(k, d->idx_dtype == HISA_BF16, false, keys, t0, rep, nullptr, 0, st);
   });
   if (e != hipSuccess) return launch_fail(e, "block means update");
   return HISA_OK;
@@ -447,6 +466,23 @@ int hisa_select_prefill(const hisa_dims* d, const void* q_idx, const float* w, c
   hipError_t e;
   // one query row per wave when the blocks and candidates fit its registers
   const PrefillPlan plan = prefill_plan(k, bf);
+  if (plan.small) {
+    // a short chunk (multi-token verify): every complete block's mean into
+    // the workspace (its first workgroup also zeroes the arrival counters),
+    // then the cached-means selection of each query row
+    float* rep = at<float>(ws, l.rep);
+    int* cnt = at<int>(ws, l.cnt);
+    hipError_t e = timed("block_mean", st, [&] {
+      return hisa::launch_rep_update(k, bf, true, keys, t0, rep, cnt, hisa::cached_counter_ints(k), st);
+    });
+    if (e != hipSuccess) return launch_fail(e, "block means");
+    e = timed("cached_decode", st, [&] {
+      return hisa::launch_cached_decode(k, q_idx, w, keys, rep, t0, at<float>(ws, l.cscore), at<int>(ws, l.blk),
+                                        at<float>(ws, l.fscore), cnt, I_out, top_blk_out, path_out, st);
+    });
+    if (e != hipSuccess) return launch_fail(e, "short-chunk selection");
+    return HISA_OK;
+  }
   const bool rows = plan.rows;
   if (k.nb_cap > 0) {
     float* rep = at<float>(ws, l.rep);

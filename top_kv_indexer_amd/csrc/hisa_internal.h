@@ -59,7 +59,8 @@ hipError_t launch_flat_scores(const KDims& d, bool bf16, const void* q_idx, cons
                               const void* keys, const int* t0, float* scores, hipStream_t st);
 hipError_t launch_topk_rows(const KDims& d, const float* scores, const int* t0, int* I,
                             int* path, hipStream_t st);
-// Decode selection on a caller-kept cache of f32 block means (B, nb_cap, D_i):
+// Selection on a caller-kept cache of f32 block means (B, nb_cap, D_i), one
+// query row (b, j) per grid row (decode, or a short verify chunk):
 // bf16 64 x 128 indexer, nb_cap <= 4096, index_keep <= 64 and
 // topk <= index_block * index_keep <= 1024, not forced flat.  The coarse
 // kernel also writes the means of the blocks completed by the step's token.
@@ -71,9 +72,10 @@ size_t cached_fine_floats(const KDims& d);
 hipError_t launch_cached_decode(const KDims& d, const void* q_idx, const float* w, const void* keys, float* rep,
                                 const int* t0, float* cscore, int* blk, float* fs, int* cnt, int* I,
                                 int* top_blk, int* path, hipStream_t st);
-// Means of the blocks completed by the step's tokens into rep (B, nb_cap, D_i).
-hipError_t launch_rep_update(const KDims& d, bool bf16, const void* keys, const int* t0, float* rep,
-                             hipStream_t st);
+// Means of the blocks completed by the step's tokens (all: every complete
+// block) into rep (B, nb_cap, D_i).
+hipError_t launch_rep_update(const KDims& d, bool bf16, bool all, const void* keys, const int* t0, float* rep,
+                             int* zero_p, size_t zero_n, hipStream_t st);
 // Zeroes n ints on the stream (n < 2^31).
 hipError_t launch_zero_ints(int* p, size_t n, hipStream_t st);
 // The dense fallback (indexer off): I = 0..Np-1 padded with -1 on every row.

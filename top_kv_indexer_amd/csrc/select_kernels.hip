@@ -127,6 +127,17 @@ __device__ __forceinline__ void write_unscored(const KDims& d, const SeqInfo& si
 }
 
 
+// The same for query row `row` = b * L + j of a multi-row call (path by j == 0).
+__device__ __forceinline__ void write_unscored_row(const KDims& d, const SeqInfo& si, int row, int j, int b, int* I,
+                                                   int* top_blk, int* path) {
+  const int lane = lane_id();
+  const bool dense = si.ok && si.path == PATH_DENSE;
+  for (int i = lane; i < d.topk; i += 64) I[(size_t)row * d.topk + i] = (dense && i < si.Np) ? i : -1;
+  if (top_blk)
+    for (int i = lane; i < d.index_keep; i += 64) top_blk[(size_t)row * d.index_keep + i] = -1;
+  if (path && lane == 0 && j == 0) path[b] = si.path;
+}
+
 // ---- workgroup top-k (256 threads): thread t holds element 256 r + t in
 // key[r], r < NR (order index = element index, ascending in id); key 0 marks
 // an absent element.
@@ -1944,35 +1955,40 @@ __global__ __launch_bounds__(256) void k_cached_coarse(KDims d, const uint16_t* 
   __shared__ WgTopkSmem s_tk;
   __shared__ int s_flag;
   args_now(d, q_idx, w, keys, rep, t0, cscore, blk, cnt, I, top_blk, path);
-  const int b = blockIdx.y, x = blockIdx.x;
+  // one query row (b, j) per grid row; several rows of a sequence (a verify
+  // chunk) each select on their own, with the batched masks
+  const int row = blockIdx.y, x = blockIdx.x;
+  const int b = row / d.L, j = row - b * d.L;
   const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
   const int t0b = t0[b];
   // this lane's head: q row (256 B) and weight, requested before t0 arrives
   uint4 qv[16];
-  const uint4* qrow = (const uint4*)(q_idx + ((size_t)b * 64 + lane) * 128);
+  const uint4* qrow = (const uint4*)(q_idx + ((size_t)row * 64 + lane) * 128);
 #pragma unroll
   for (int i = 0; i < 16; ++i) qv[i] = qrow[i];
-  const float wh = w[(size_t)b * 64 + lane] * d.w_scale;
+  const float wh = w[(size_t)row * 64 + lane] * d.w_scale;
   // the cached means of this wave's blocks, also requested before t0 arrives
   // (a block completed by this step is recomputed below instead)
   const int beta0 = x * kCachedBlocksPerWg + 4 * wv;
   float* repb = rep + (size_t)b * d.nb_cap * 128;
   float2 mc[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) mc[j] = *(const float2*)&repb[(size_t)min(beta0 + j, d.nb_cap - 1) * 128 + 2 * lane];
+  for (int jj = 0; jj < 4; ++jj) mc[jj] = *(const float2*)&repb[(size_t)min(beta0 + jj, d.nb_cap - 1) * 128 + 2 * lane];
   const SeqInfo si = seq_info(d, t0b);
   if (!si.ok || si.path == PATH_DENSE) {
-    if (x == 0 && wv == 0) write_unscored(d, si, b, I, top_blk, path);
+    if (x == 0 && wv == 0) write_unscored_row(d, si, row, j, b, I, top_blk, path);
     return;
   }
   if (si.path != PATH_HISA) {  // flat: the fine kernel selects
     if (x == 0 && wv == 0) {
       if (top_blk)
-        for (int i = lane; i < d.index_keep; i += 64) top_blk[(size_t)b * d.index_keep + i] = -1;
-      if (path && lane == 0) path[b] = si.path;
+        for (int i = lane; i < d.index_keep; i += 64) top_blk[(size_t)row * d.index_keep + i] = -1;
+      if (path && lane == 0 && j == 0) path[b] = si.path;
     }
     return;
   }
+  // blocks whose first row this query row cannot see score the mask value
+  const int V = visible(d, t0b + j, si.Np);
   const int nwg = (si.nb + kCachedBlocksPerWg - 1) / kCachedBlocksPerWg;
   if (x >= nwg) return;
   const int bsz = d.index_block;
@@ -1981,28 +1997,28 @@ __global__ __launch_bounds__(256) void k_cached_coarse(KDims d, const uint16_t* 
   const int first_new = (int)div_ratio(d, (uint32_t)t0b) / bsz;
   const uint16_t* kb = keys + (size_t)b * d.Np_cap * 128;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int beta = beta0 + j;
+  for (int jj = 0; jj < 4; ++jj) {
+    const int beta = beta0 + jj;
     if (beta >= si.nb) break;  // uniform over the wave
-    float2 m = mc[j];
+    float2 m = mc[jj];
     if (beta >= first_new) {
       m = block_mean_lane(kb, beta, bsz);
-      *(float2*)&repb[(size_t)beta * 128 + 2 * lane] = m;
+      if (row == b * d.L) *(float2*)&repb[(size_t)beta * 128 + 2 * lane] = m;  // the sequence's first row stores it
     }
-    *(float2*)&s_rep[wv][j][2 * lane] = m;
+    *(float2*)&s_rep[wv][jj][2 * lane] = m;
   }
   __builtin_amdgcn_wave_barrier();
   // one wave's LDS operations complete in order: the stores above land
   // before the broadcast reads below
 #pragma unroll 1
-  for (int j = 0; j < 4; ++j) {
-    const int beta = beta0 + j;
+  for (int jj = 0; jj < 4; ++jj) {
+    const int beta = beta0 + jj;
     if (beta >= si.nb) break;
     float acc = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float4 r0 = *(const float4*)&s_rep[wv][j][8 * i];
-      const float4 r1 = *(const float4*)&s_rep[wv][j][8 * i + 4];
+      const float4 r0 = *(const float4*)&s_rep[wv][jj][8 * i];
+      const float4 r1 = *(const float4*)&s_rep[wv][jj][8 * i + 4];
       acc = fmaf(bf_lo(qv[i].x), r0.x, acc);
       acc = fmaf(bf_hi(qv[i].x), r0.y, acc);
       acc = fmaf(bf_lo(qv[i].y), r0.z, acc);
@@ -2013,37 +2029,38 @@ __global__ __launch_bounds__(256) void k_cached_coarse(KDims d, const uint16_t* 
       acc = fmaf(bf_hi(qv[i].w), r1.w, acc);
     }
     const float cs = wave_sum(relu(acc) * wh);
-    if (lane == 0) st_dev(cscore + (size_t)b * d.nb_cap + beta, cs);
+    if (lane == 0) st_dev(cscore + (size_t)row * d.nb_cap + beta, beta * bsz < V ? cs : kNeg);
   }
-  // cnt: B sequence counters, then B x ngmax group counters
+  // cnt: B*L row counters, then B*L x ngmax group counters
+  const int nrows = d.B * d.L;
   const int grp = x / kArriveGroup, ngrp = (nwg + kArriveGroup - 1) / kArriveGroup;
   const int ngmax = (gridDim.x + kArriveGroup - 1) / kArriveGroup;
   const bool last = publish(
       [&] {
-        if (ngrp == 1) return arrive(cnt + (size_t)b * kCntStride, 1, nwg);  // one atomic on the path
+        if (ngrp == 1) return arrive(cnt + (size_t)row * kCntStride, 1, nwg);  // one atomic on the path
         const int members = min(kArriveGroup, nwg - grp * kArriveGroup);
-        int* c_grp = cnt + (size_t)(d.B + (size_t)b * ngmax + grp) * kCntStride;
-        return arrive(c_grp, 1, members) && arrive(cnt + (size_t)b * kCntStride, 1, ngrp);
+        int* c_grp = cnt + (size_t)(nrows + (size_t)row * ngmax + grp) * kCntStride;
+        return arrive(c_grp, 1, members) && arrive(cnt + (size_t)row * kCntStride, 1, ngrp);
       },
       &s_flag);
   if (!last) return;
-  // top-Kb of the sequence's nb block scores, ascending block ids
-  const float* csb = cscore + (size_t)b * d.nb_cap;
+  // top-Kb of the row's nb block scores, ascending block ids
+  const float* csb = cscore + (size_t)row * d.nb_cap;
   uint32_t key[16];
   float v[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) v[r] = ld_dev(csb + min(256 * r + tid, si.nb - 1));
 #pragma unroll
   for (int r = 0; r < 16; ++r) key[r] = 256 * r + tid < si.nb ? score_key(v[r]) : 0u;
-  int* blkb = blk + (size_t)b * d.index_keep;
-  int* tbo = top_blk ? top_blk + (size_t)b * d.index_keep : nullptr;
+  int* blkb = blk + (size_t)row * d.index_keep;
+  int* tbo = top_blk ? top_blk + (size_t)row * d.index_keep : nullptr;
   wg_emit_topk16(key, si.nb, si.Kb, s_tk, [&](int slot, int r) {
     blkb[slot] = 256 * r + tid;
     if (tbo) tbo[slot] = 256 * r + tid;
   });
   if (tbo)
     for (int i = si.Kb + tid; i < d.index_keep; i += 256) tbo[i] = -1;
-  if (path && tid == 0) path[b] = si.path;
+  if (path && tid == 0 && j == 0) path[b] = si.path;
 }
 
 __global__ __launch_bounds__(256) void k_cached_fine(KDims d, const uint16_t* __restrict__ q_idx,
@@ -2055,13 +2072,14 @@ __global__ __launch_bounds__(256) void k_cached_fine(KDims d, const uint16_t* __
   __shared__ int s_blk[kRowKeep];
   __shared__ int s_flag;
   args_now(d, q_idx, w, keys, t0, blk, fs, cnt, I);
-  const int b = blockIdx.y, slab = blockIdx.x;
+  const int row = blockIdx.y, slab = blockIdx.x;
+  const int b = row / d.L, j = row - b * d.L;
   const int tid = threadIdx.x, lane = lane_id(), wv = wave_id(), g = lane >> 4, c = lane & 15;
   const int t0b = t0[b];
   // the retained blocks (meaningful on the HiSA path only; always in bounds)
-  const int blk_tid = tid < d.index_keep ? blk[(size_t)b * d.index_keep + tid] : 0;
-  issue_q_lds(q_idx + (size_t)b * 64 * 128, s_q);
-  const float* wrow = w + (size_t)b * 64;
+  const int blk_tid = tid < d.index_keep ? blk[(size_t)row * d.index_keep + tid] : 0;
+  issue_q_lds(q_idx + (size_t)row * 64 * 128, s_q);
+  const float* wrow = w + (size_t)row * 64;
   float wl[4][4];
 #pragma unroll
   for (int ht = 0; ht < 4; ++ht)
@@ -2110,12 +2128,14 @@ __global__ __launch_bounds__(256) void k_cached_fine(KDims d, const uint16_t* __
 #pragma unroll
     for (int i = 0; i < 4; ++i) v += relu(acc[ht][i]) * wl[ht][i];
   v = sum_rows(v);
+  // candidates this query row cannot see score the mask value
+  if (r >= visible(d, t0b + j, si.Np)) v = kNeg;
   const int cc = slab * 64 + wv * 16 + c;
-  float* fsb = fs + (size_t)b * kCachedMaxCand;
+  float* fsb = fs + (size_t)row * kCachedMaxCand;
   if (g == 0 && cc < n) st_dev(fsb + cc, v);
-  const bool last = publish([&] { return arrive(cnt + (size_t)b * kCntStride, 1, nslab); }, &s_flag);
+  const bool last = publish([&] { return arrive(cnt + (size_t)row * kCntStride, 1, nslab); }, &s_flag);
   if (!last) return;
-  int* Ib = I + (size_t)b * d.topk;
+  int* Ib = I + (size_t)row * d.topk;
   for (int i = si.k + tid; i < d.topk; i += 256) Ib[i] = -1;
   uint32_t key[4];
   float sv[4];
@@ -2130,14 +2150,17 @@ __global__ __launch_bounds__(256) void k_cached_fine(KDims d, const uint16_t* __
 // [floor(floor(t0 / r) / b), floor(Np / b)) (every complete block when t0 = 0),
 // rows summed in order in f32 and scaled by 1/b, as the cached decode does.
 template <typename T>
-__global__ __launch_bounds__(128) void k_rep_update(KDims d, const T* __restrict__ keys, const int* __restrict__ t0,
-                                                    float* rep) {
+__global__ __launch_bounds__(128) void k_rep_update(KDims d, int all, const T* __restrict__ keys,
+                                                    const int* __restrict__ t0, float* rep, int* zero_p, int zero_n) {
   const int b = blockIdx.y, beta = blockIdx.x;
+  // the first workgroup also zeroes the arrival counters of the kernels that follow
+  if (zero_p && b == 0 && beta == 0)
+    for (int i = threadIdx.x; i < zero_n; i += 128) zero_p[i] = 0;
   const int t0b = t0[b];
   const SeqInfo si = seq_info(d, t0b);
   if (!si.ok) return;
   const int bsz = d.index_block;
-  const int first_new = (int)div_ratio(d, (uint32_t)t0b) / bsz;
+  const int first_new = all ? 0 : (int)div_ratio(d, (uint32_t)t0b) / bsz;
   if (beta < first_new || beta >= si.nb) return;
   const T* kb = keys + ((size_t)b * d.Np_cap + (size_t)beta * bsz) * d.D_i;
   const float inv = 1.f / (float)bsz;
@@ -2165,34 +2188,39 @@ bool cached_decode_ok(const KDims& d, bool bf16) {
 }
 
 size_t cached_counter_ints(const KDims& d) {
+  const size_t rows = (size_t)d.B * d.L;
   const size_t wgs = ((size_t)d.nb_cap + kCachedBlocksPerWg - 1) / kCachedBlocksPerWg;
   const size_t ngmax = (std::max<size_t>(wgs, 1) + kArriveGroup - 1) / kArriveGroup;
-  return (size_t)d.B * (1 + ngmax) * kCntStride + (size_t)d.B * kCntStride;
+  return rows * (1 + ngmax) * kCntStride + rows * kCntStride;
 }
 
-size_t cached_fine_floats(const KDims& d) { return (size_t)d.B * kCachedMaxCand; }
+size_t cached_fine_floats(const KDims& d) { return (size_t)d.B * d.L * kCachedMaxCand; }
 
 hipError_t launch_cached_decode(const KDims& d, const void* q_idx, const float* w, const void* keys, float* rep,
                                 const int* t0, float* cscore, int* blk, float* fs, int* cnt, int* I, int* top_blk,
                                 int* path, hipStream_t st) {
   const unsigned wgs = std::max(1u, (unsigned)((d.nb_cap + kCachedBlocksPerWg - 1) / kCachedBlocksPerWg));
   const size_t ngmax = (wgs + kArriveGroup - 1) / kArriveGroup;
-  int* cnt_fine = cnt + (size_t)d.B * (1 + ngmax) * kCntStride;
-  hipLaunchKernelGGL(k_cached_coarse, dim3(wgs, d.B), dim3(256), 0, st, d, (const uint16_t*)q_idx, w,
+  const unsigned rows = (unsigned)(d.B * d.L);
+  int* cnt_fine = cnt + (size_t)rows * (1 + ngmax) * kCntStride;
+  hipLaunchKernelGGL(k_cached_coarse, dim3(wgs, rows), dim3(256), 0, st, d, (const uint16_t*)q_idx, w,
                      (const uint16_t*)keys, rep, t0, cscore, blk, cnt, I, top_blk, path);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_cached_fine, dim3(kCachedMaxCand / 64, d.B), dim3(256), 0, st, d, (const uint16_t*)q_idx, w,
+  hipLaunchKernelGGL(k_cached_fine, dim3(kCachedMaxCand / 64, rows), dim3(256), 0, st, d, (const uint16_t*)q_idx, w,
                      (const uint16_t*)keys, t0, blk, fs, cnt_fine, I);
   return hipGetLastError();
 }
 
-hipError_t launch_rep_update(const KDims& d, bool bf16, const void* keys, const int* t0, float* rep, hipStream_t st) {
+hipError_t launch_rep_update(const KDims& d, bool bf16, bool all, const void* keys, const int* t0, float* rep,
+                             int* zero_p, size_t zero_n, hipStream_t st) {
   if (d.nb_cap == 0) return hipSuccess;
   if (bf16)
-    hipLaunchKernelGGL(k_rep_update<uint16_t>, dim3(d.nb_cap, d.B), dim3(128), 0, st, d, (const uint16_t*)keys, t0, rep);
+    hipLaunchKernelGGL(k_rep_update<uint16_t>, dim3(d.nb_cap, d.B), dim3(128), 0, st, d, (int)all,
+                       (const uint16_t*)keys, t0, rep, zero_p, (int)zero_n);
   else
-    hipLaunchKernelGGL(k_rep_update<float>, dim3(d.nb_cap, d.B), dim3(128), 0, st, d, (const float*)keys, t0, rep);
+    hipLaunchKernelGGL(k_rep_update<float>, dim3(d.nb_cap, d.B), dim3(128), 0, st, d, (int)all, (const float*)keys,
+                       t0, rep, zero_p, (int)zero_n);
   return hipGetLastError();
 }
 

@@ -2149,6 +2149,35 @@ __global__ __launch_bounds__(256) void k_cached_fine(KDims d, const uint16_t* __
 // Block means of the blocks completed by the step's L tokens: blocks
 // [floor(floor(t0 / r) / b), floor(Np / b)) (every complete block when t0 = 0),
 // rows summed in order in f32 and scaled by 1/b, as the cached decode does.
+// bf16 keys with 128 dims: wave w of workgroup x takes block 4x + w, lane l
+// dims 2l and 2l+1; all b rows are requested before the in-order sum, which
+// is the same sum as the cached decode's (so the two give the same bits).
+__global__ __launch_bounds__(256) void k_rep_update_bf16(KDims d, int all, const uint16_t* __restrict__ keys,
+                                                         const int* __restrict__ t0, float* rep, int* zero_p,
+                                                         int zero_n) {
+  const int b = blockIdx.y, beta = blockIdx.x * 4 + wave_id(), lane = lane_id();
+  if (zero_p && b == 0 && blockIdx.x == 0)
+    for (int i = threadIdx.x; i < zero_n; i += 256) zero_p[i] = 0;
+  const int t0b = t0[b];
+  const SeqInfo si = seq_info(d, t0b);
+  const int bsz = d.index_block;
+  const int first_new = all ? 0 : (int)div_ratio(d, (uint32_t)t0b) / bsz;
+  if (!si.ok || beta < first_new || beta >= si.nb) return;  // uniform over the wave
+  const uint32_t* src = (const uint32_t*)(keys + ((size_t)b * d.Np_cap + (size_t)beta * bsz) * 128) + lane;
+  uint32_t v[64];
+#pragma unroll
+  for (int r = 0; r < 64; ++r) v[r] = r < bsz ? src[r * 64] : 0u;
+  float sx = 0.f, sy = 0.f;
+#pragma unroll
+  for (int r = 0; r < 64; ++r)
+    if (r < bsz) {
+      sx += bf_lo(v[r]);
+      sy += bf_hi(v[r]);
+    }
+  const float inv = 1.f / (float)bsz;
+  *(float2*)&rep[((size_t)b * d.nb_cap + beta) * 128 + 2 * lane] = make_float2(sx * inv, sy * inv);
+}
+
 template <typename T>
 __global__ __launch_bounds__(128) void k_rep_update(KDims d, int all, const T* __restrict__ keys,
                                                     const int* __restrict__ t0, float* rep, int* zero_p, int zero_n) {
@@ -2215,7 +2244,10 @@ hipError_t launch_cached_decode(const KDims& d, const void* q_idx, const float* 
 hipError_t launch_rep_update(const KDims& d, bool bf16, bool all, const void* keys, const int* t0, float* rep,
                              int* zero_p, size_t zero_n, hipStream_t st) {
   if (d.nb_cap == 0) return hipSuccess;
-  if (bf16)
+  if (bf16 && d.D_i == 128)
+    hipLaunchKernelGGL(k_rep_update_bf16, dim3((d.nb_cap + 3) / 4, d.B), dim3(256), 0, st, d, (int)all,
+                       (const uint16_t*)keys, t0, rep, zero_p, (int)zero_n);
+  else if (bf16)
     hipLaunchKernelGGL(k_rep_update<uint16_t>, dim3(d.nb_cap, d.B), dim3(128), 0, st, d, (int)all,
                        (const uint16_t*)keys, t0, rep, zero_p, (int)zero_n);
   else

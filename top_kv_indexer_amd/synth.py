@@ -70,11 +70,17 @@ DSA_DECODE = Workload("dsa_flat_decode_kv32768", B=1, L=1, ratio=1, window=0, to
                       bf16=True, t0=[32767], layernorm_keys=True, sinks=False)
 DSA_PREFILL = DSA_DECODE.with_(name="dsa_flat_prefill_l4096_kv32768", L=4096, t0=[28672])
 
+# Multi-token verify chunks on the V4-Flash decode shapes: 4 rows (the short-
+# chunk selection) and 9 rows (just past it: the prefill row selection).
+VERIFY_L4 = FLASH_DECODE.with_(name="v4flash_verify_l4_np16384", L=4, t0=[65532])
+VERIFY_L9 = FLASH_DECODE.with_(name="v4flash_verify_l9_np16384", L=9, t0=[65527])
+
 WORKLOADS = {w.name: w for w in (TINY_DECODE, FLASH_DECODE, BATCHED_DECODE, PREFILL,
-                                 DSA_DECODE, DSA_PREFILL)}
+                                 DSA_DECODE, DSA_PREFILL, VERIFY_L4, VERIFY_L9)}
 # Seeds: one stream per workload family.
 SEEDS = {TINY_DECODE.name: 1001, FLASH_DECODE.name: 1002, BATCHED_DECODE.name: 1003,
-         PREFILL.name: 1004, DSA_DECODE.name: 1005, DSA_PREFILL.name: 1005}
+         PREFILL.name: 1004, DSA_DECODE.name: 1005, DSA_PREFILL.name: 1005,
+         VERIFY_L4.name: 1002, VERIFY_L9.name: 1002}
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:

@@ -47,9 +47,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="v4flash_decode_np16384")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay figures")
-    ap.add_argument("--selector", choices=("cached", "stateless"), default="cached",
-                    help="decode selection: on the cached block means (the step keeps the cache current) or "
-                         "re-reading every key")
+    ap.add_argument("--selector", choices=("cached", "stateless"), default="stateless",
+                    help="decode selection: re-reading every key (the faster at B = 1 below Np ~ 100K) or on "
+                         "cached block means (the step keeps the cache current; flat in Np, faster for batches)")
     ap.add_argument("--crossover", action="store_true",
                     help="flat vs HiSA decode selection and sparse vs dense prefill attention against Np")
     ap.add_argument("--sweep-np", action="store_true",

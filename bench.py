@@ -47,9 +47,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="v4flash_decode_np16384")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay figures")
-    ap.add_argument("--selector", choices=("cached", "stateless"), default="stateless",
+    ap.add_argument("--selector", choices=("auto", "cached", "stateless"), default="auto",
                     help="decode selection: re-reading every key (the faster at B = 1 below Np ~ 100K) or on "
-                         "cached block means (the step keeps the cache current; flat in Np, faster for batches)")
+                         "cached block means (the step keeps the cache current; flat in Np, faster for batches); "
+                         "auto takes the cached means for batches of 8+ rows or Np >= 131072, as measured")
     ap.add_argument("--crossover", action="store_true",
                     help="flat vs HiSA decode selection and sparse vs dense prefill attention against Np")
     ap.add_argument("--sweep-np", action="store_true",
@@ -443,7 +444,10 @@ def main():
         return sweep_np(args)
     if args.crossover:
         return crossover(args)
-    H = harness(w, x, args.selector)
+    selector = args.selector
+    if selector == "auto":
+        selector = "cached" if (w.B * w.L >= 8 or int(max(x["Np"])) >= 131072) else "stateless"
+    H = harness(w, x, selector)
     dev, I, blk, path, kind, cached = H.dev, H.I, H.blk, H.path, H.kind, H.cached
     step, sel_only, att_only, cold, hot, call, bound_calls = (H.step, H.sel_only, H.att_only, H.cold, H.hot, H.call,
                                                              H.bound_calls)

@@ -334,3 +334,41 @@ def test_ring_window_equals_linear(hisa, case):
     torch.cuda.synchronize()
     assert torch.equal(out2, out_lin)
     assert (out3[0] == 0).all() and torch.equal(out3[1:], out_lin[1:])
+
+
+# ---------------------------------------------------------------- flat top-k of long rows
+
+@pytest.mark.parametrize("case", ["ragged_b4", "heavy_ties"])
+def test_flat_topk_long_rows_decode(hisa, case):
+    # Decode rows of up to 32768 scores: a ragged batch (rows of 32768,
+    # 20001, 9001 and 5000 scores) and 3000 equal top scores straddling the
+    # k-th (the best key row copied over rows 1000..3999 of sequence 0: the
+    # 2048 kept must be the lowest ids).
+    w = {"ragged_b4": synth.DSA_DECODE.with_(name="dsa_decode_b4", B=4, t0=[32767, 20000, 9000, 4999], H=4, Dk=64,
+                                             Dv=64),
+         "heavy_ties": synth.DSA_DECODE.with_(name="dsa_decode_ties", B=2, t0=[32767, 15000], H=4, Dk=64,
+                                              Dv=64)}[case]
+    x, g = inputs(w, 65)
+    x = dict(x)
+    keys = x["keys"]
+    if case == "heavy_ties":
+        keys = keys.copy()
+        d0 = odims(w, x)
+        sc = oracle.scores_of(d0, x["q_idx"][0, 0], x["w"][0, 0], x["keys"][0], int(x["t0"][0]), 0,
+                              np.arange(32768, dtype=np.int32))
+        keys[0, 1000:4000] = x["keys"][0, int(np.argmax(sc))]
+        x["keys"] = keys
+    gk = torch.from_numpy(keys).to("cuda").to(torch.bfloat16).contiguous()
+    say(f"[run] flat top-k of long decode rows, {case}")
+    I = hisa.flat_topk_select(g["q_idx"], g["w"], gk, g["t0"], ratio=1, topk=w.topk)
+    torch.cuda.synchronize()
+    d = odims(w, x)
+    In = parity.to_np(I)
+    for b in range(w.B):
+        q, ww, kb, t0 = x["q_idx"][b, 0], x["w"][b, 0], x["keys"][b], int(x["t0"][b])
+        Io, _, _ = oracle.select_row(d, q, ww, kb, t0, 0)
+        parity.compare_sets(In[b, 0], Io, lambda ids: oracle.scores_of(d, q, ww, kb, t0, 0, ids), what=f"({b},0)")
+        v = In[b, 0][In[b, 0] >= 0]
+        assert (np.diff(v) > 0).all()
+        if case == "heavy_ties" and b == 0:
+            np.testing.assert_array_equal(v, np.arange(1000, 3048))

@@ -51,6 +51,9 @@ def parse():
                     help="decode selection: re-reading every key (the faster at B = 1 below Np ~ 100K) or on "
                          "cached block means (the step keeps the cache current; flat in Np, faster for batches); "
                          "auto takes the cached means for batches of 8+ rows or Np >= 131072, as measured")
+    ap.add_argument("--step-call", choices=("decode_step", "two_calls"), default="decode_step",
+                    help="decode with the stateless selector: hisa_decode_step (selection and attention in one call, "
+                         "one kernel for few sequences) or hisa_select_decode then sparse_local_pooled_attention")
     ap.add_argument("--crossover", action="store_true",
                     help="flat vs HiSA decode selection and sparse vs dense prefill attention against Np")
     ap.add_argument("--sweep-np", action="store_true",
@@ -116,6 +119,9 @@ def algorithmic(w, x, unique_kv_rows=None, flat_seqs=None):
         "decode_scan": {"bytes": keys + idx_q, "flops": sum(Np) * w.H_i * w.D_i * 2},
         "decode_select": {"bytes": rows * kI * 4, "flops": 0},
         "decode_scan_select": {"bytes": keys + idx_q + rows * kI * 4, "flops": sum(Np) * w.H_i * w.D_i * 2},
+        # selection and attention in one kernel: the step's whole compulsory traffic
+        "decode_step": {"bytes": keys + idx_q + rows * kI * 4 + attn_bytes,
+                        "flops": sum(Np) * w.H_i * w.D_i * 2 + attn_flops},
         "attention": {"bytes": attn_bytes, "flops": attn_flops},
         "attention_merge": {"bytes": rows * w.H * w.Dv * bf, "flops": 0},
         "block_mean": {"bytes": keys, "flops": 0},
@@ -219,9 +225,10 @@ def flush():
     torch.sum(_flush_state["buf"], dim=0, out=_flush_state["out"])
 
 
-def harness(w, x, selector):
+def harness(w, x, selector, step_call="two_calls"):
     """Device copies of workload w's inputs x, outputs and workspaces, and the
-    step's two C calls with their arguments marshalled once."""
+    step's C calls with their arguments marshalled once (stateless decode
+    with step_call "decode_step": the one call that selects and attends)."""
     from types import SimpleNamespace
 
     import torch
@@ -255,10 +262,17 @@ def harness(w, x, selector):
         _, rep = hisa.hisa_block_scores(base["q_idx"], base["w"], base["keys"], t0, ratio=w.ratio,
                                         index_block=w.index_block, want_rep=True)
     ws_sel = torch.zeros(max(hisa.workspace_bytes(op, sel_d), 256), dtype=torch.uint8, device=dev)
+    one_call = kind == "decode" and not cached and step_call == "decode_step"
+    step_d = hisa.decode_step_dims(base["q_idx"], base["keys"], base["q"], base["local_kv"] if w.window else None,
+                                   base["pooled_kv"], ratio=w.ratio, window=w.window, topk=w.topk,
+                                   index_block=w.index_block, index_keep=w.index_keep) if one_call else None
+    ws_step = torch.zeros(max(hisa.workspace_bytes(hisa.OP_DECODE_STEP, step_d), 256), dtype=torch.uint8,
+                          device=dev) if one_call else None
     ws_att = torch.zeros(max(hisa.workspace_bytes(hisa.OP_ATTENTION, att_d), 256), dtype=torch.uint8, device=dev)
     main_stream = torch.cuda.current_stream(dev)
     P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())  # noqa: E731
     sel_ref, att_ref = ctypes.byref(sel_d), ctypes.byref(att_d)
+    step_ref = ctypes.byref(step_d) if one_call else None
     n_sel, n_att = ws_sel.numel(), ws_att.numel()
     c = base
 
@@ -278,15 +292,21 @@ def harness(w, x, selector):
             f_sel = L.hisa_select_decode if kind == "decode" else L.hisa_select_prefill
         a_att = (att_ref, P(c["q"]), P(c["local_kv"]) if w.window else None, P(c["pooled_kv"]), P(I), P(sinks),
                  P(t0), P(out), P(ws_att), n_att, st)
-        return f_sel, a_sel, L.sparse_local_pooled_attention, a_att
+        a_step = (step_ref, P(c["q_idx"]), P(c["w"]), P(c["keys"]), P(c["q"]), P(c["local_kv"]) if w.window else None,
+                  P(c["pooled_kv"]), P(sinks), P(t0), P(I), P(blk), P(path), P(out), P(ws_step),
+                  ws_step.numel(), st) if one_call else None
+        return f_sel, a_sel, L.sparse_local_pooled_attention, a_att, L.hisa_decode_step, a_step
 
-    f1, a1, f2, a2 = bound_calls(main_stream.cuda_stream)
+    f1, a1, f2, a2, f3, a3 = bound_calls(main_stream.cuda_stream)
 
     def call(f, a):
         if f(*a):
             raise hisa.HisaError(hisa.last_error())
 
     def step(i=0):
+        if one_call:
+            call(f3, a3)
+            return
         call(f1, a1)
         call(f2, a2)
 
@@ -407,7 +427,7 @@ def sweep_np(args):
         x = synth.make_inputs(w, synth.SEEDS[synth.FLASH_DECODE.name])
         line = {"Np": Np}
         for sel in ("stateless", "cached"):
-            H = harness(w, x, sel)
+            H = harness(w, x, sel, args.step_call)
             for i in range(args.warmup):
                 flush()
                 H.step(i)
@@ -447,8 +467,8 @@ def main():
     selector = args.selector
     if selector == "auto":
         selector = "cached" if (w.B * w.L >= 8 or int(max(x["Np"])) >= 131072) else "stateless"
-    H = harness(w, x, selector)
-    dev, I, blk, path, kind, cached = H.dev, H.I, H.blk, H.path, H.kind, H.cached
+    H = harness(w, x, selector, args.step_call)
+    dev, I, blk, path, kind, cached, one_call = H.dev, H.I, H.blk, H.path, H.kind, H.cached, H.one_call
     step, sel_only, att_only, cold, hot, call, bound_calls = (H.step, H.sel_only, H.att_only, H.cold, H.hot, H.call,
                                                              H.bound_calls)
     main_stream = H.main_stream
@@ -473,10 +493,13 @@ def main():
         s = torch.cuda.Stream(device=dev)
         s.wait_stream(main_stream)
         graph = torch.cuda.CUDAGraph()
-        g1, b1, g2, b2 = bound_calls(s.cuda_stream)
+        g1, b1, g2, b2, g3, b3 = bound_calls(s.cuda_stream)
         with torch.cuda.graph(graph, stream=s):
-            call(g1, b1)
-            call(g2, b2)
+            if one_call:
+                call(g3, b3)
+            else:
+                call(g1, b1)
+                call(g2, b2)
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
@@ -557,6 +580,7 @@ def main():
                    "index_keep": w.index_keep, "H": w.H, "head_dim": w.Dk, "window": w.window,
                    "selector": ("cached block means" if cached else "every key re-read") if kind == "decode"
                    else kind,
+                   "step_call": "hisa_decode_step" if one_call else "selection call + attention call",
                    "us_per_layer": us(ms), "step_algorithmic_bytes": step_bytes,
                    "step_GBps": round(step_bytes / (ms / 1e3) / 1e9, 1),
                    "timing": "cold: 1 GiB read flush before each step, outside its HIP events; median",

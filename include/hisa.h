@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define HISA_ABI_VERSION 2
+#define HISA_ABI_VERSION 3
 
 enum hisa_dtype { HISA_F32 = 0, HISA_BF16 = 1 };
 
@@ -75,7 +75,8 @@ enum hisa_op {
   HISA_OP_FLAT_TOPK = 3,
   HISA_OP_ATTENTION = 4,
   HISA_OP_SELECT_DECODE_CACHED = 5,
-  HISA_OP_BLOCK_MEANS_UPDATE = 6
+  HISA_OP_BLOCK_MEANS_UPDATE = 6,
+  HISA_OP_DECODE_STEP = 7
 };
 
 /* Problem sizes (HiSA issue, Configuration table). */
@@ -260,6 +261,40 @@ int sparse_local_pooled_attention_ring(const hisa_dims* d, const void* q, const 
                                        const void* pooled_kv, const int32_t* I, const float* sinks,
                                        const int32_t* t0, const int32_t* ring_slot, void* out, void* ws,
                                        size_t ws_bytes, void* stream);
+
+/* A whole decode step: hisa_select_decode, then sparse_local_pooled_attention
+ * on the index row it produced (HiSA issue, HiSA decode path, then Consuming
+ * the selection: sparse combine).  L must be 1; kI is taken to be topk and
+ * the local window is linear (as in sparse_local_pooled_attention).  Outputs:
+ * I_out, top_blk_out (or NULL) and path_out (or NULL) exactly as
+ * hisa_select_decode writes them, and out (B, 1, H, Dv) as the attention call
+ * computes it on I_out, up to f32 rounding (the softmax is split and merged
+ * differently).
+ * For few sequences of the shapes the one-kernel step serves (bf16 keys with
+ * H_i = 64, D_i = 128, index_block 16, 32 or 64, index_keep * index_block and
+ * topk <= 1024; bf16 attention with Dk = Dv = 512, H a multiple of 16; at most
+ * 1024 key slabs of 64 rows over the batch, and B * H/16 * (ceil(max(
+ * index_keep * index_block, topk) / 64) + ceil(window / 64)) attention
+ * workgroups, at most 24 per head group and at most the device's compute
+ * units) the step is one kernel: the attention of the kept blocks gathers and
+ * scores their rows as soon as the coarse stage has chosen them, while the
+ * fine top-k is still running, and the local window is attended from the
+ * start.  Otherwise (and under HISA_MODE_FORCE_DENSE) it runs the two calls'
+ * kernels one after the other.  The selected set is hisa_select_decode's in
+ * both cases.
+ * Workspace (hisa_workspace_bytes(HISA_OP_DECODE_STEP, d)): its first part
+ * holds synchronisation words and the arrival counters of hisa_select_decode;
+ * like those counters it must be zero before the first call that uses the
+ * workspace, every call leaves it zero, and it must be zeroed again before a
+ * call whose B, H, Np_cap, topk, index_block or index_keep is larger than
+ * those of earlier calls on it.  Its first int32 becomes 1 if one of the
+ * one-kernel step's bounded waits ever gave up (never expected: that call's
+ * outputs are then undefined and the region must be zeroed again).  Calls
+ * that share a workspace must not overlap. */
+int hisa_decode_step(const hisa_dims* d, const void* q_idx, const float* w, const void* keys, const void* q,
+                     const void* local_kv, const void* pooled_kv, const float* sinks, const int32_t* t0,
+                     int32_t* I_out, int32_t* top_blk_out, int32_t* path_out, void* out, void* ws,
+                     size_t ws_bytes, void* stream);
 
 /* Workspace bytes the call `op` (enum hisa_op) needs for dims d (>= 256-byte
  * aligned offsets inside); 0 when it needs none.  Returns (size_t)-1 for

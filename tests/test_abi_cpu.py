@@ -32,7 +32,7 @@ def test_exports_every_declared_function(lib):
     assert set(names) == set(hisa.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.hisa_abi_version() == 2
+    assert lib.hisa_abi_version() == 3
 
 
 def dims(**kw):
@@ -55,6 +55,12 @@ def test_workspace_sizes(lib):
     assert hisa.workspace_bytes(hisa.OP_FLAT_TOPK, dims(L=4, Np_cap=1000)) == ((4 * 1000 * 4 + 255) // 256) * 256
     # single-row attention splits the 640 rows into 10 parts of 64
     assert hisa.workspace_bytes(hisa.OP_ATTENTION, d) == 10 * 64 * 514 * 4
+    # decode step: sync words (error word, then per sequence one line each of
+    # "seen" and threshold, 16 split descriptors of 8 bytes: 320 bytes,
+    # rounded to 512),
+    # the decode selection's workspace, and the partials of 16 pooled + 2 local
+    # splits of 64 heads (more than the attention call's 10)
+    assert hisa.workspace_bytes(hisa.OP_DECODE_STEP, d) == 512 + (1280 + 16384 * 4 + 256 * 4) + 18 * 64 * 514 * 4
     # many rows: no split, no workspace
     assert hisa.workspace_bytes(hisa.OP_ATTENTION, dims(L=2048, Wl_cap=2175)) == 0
     # batched selection, sized by the kernels that run: one query row per wave

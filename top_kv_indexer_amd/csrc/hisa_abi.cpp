@@ -43,11 +43,12 @@ constexpr int kMaxCandidates = 8192;
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 bool is_sel(int op) { return op != HISA_OP_ATTENTION; }
+bool is_att(int op) { return op == HISA_OP_ATTENTION || op == HISA_OP_DECODE_STEP; }
 
 // Checks dims for `op` and fills the kernel-side description.
 int make_kdims(int op, const hisa_dims* d, KDims* k) {
   if (!d) return fail(HISA_ERR_ARG, "dims is NULL");
-  if (op < HISA_OP_BLOCK_SCORES || op > HISA_OP_BLOCK_MEANS_UPDATE) return fail(HISA_ERR_ARG, "unknown op %d", op);
+  if (op < HISA_OP_BLOCK_SCORES || op > HISA_OP_DECODE_STEP) return fail(HISA_ERR_ARG, "unknown op %d", op);
   if (d->B < 1 || d->B > 65535) return fail(HISA_ERR_ARG, "B = %d must be in [1, 65535]", d->B);
   if (d->L < 1 || d->L > 524280) return fail(HISA_ERR_ARG, "L = %d must be in [1, 524280]", d->L);
   if (d->ratio < 1) return fail(HISA_ERR_ARG, "ratio = %d must be >= 1", d->ratio);
@@ -64,12 +65,14 @@ int make_kdims(int op, const hisa_dims* d, KDims* k) {
   kd.force_dense = d->mode == HISA_MODE_FORCE_DENSE;
   kd.ratio_shift = (d->ratio > 0 && (d->ratio & (d->ratio - 1)) == 0) ? __builtin_ctz((unsigned)d->ratio) : -1;
   kd.force_path = -1;
+  if (op == HISA_OP_DECODE_STEP) kd.kI = d->topk;  // the step attends to its own index row
   if (is_sel(op)) {
     if (d->idx_dtype != HISA_F32 && d->idx_dtype != HISA_BF16) return fail(HISA_ERR_DTYPE, "idx_dtype %d", d->idx_dtype);
     if (d->mode != HISA_MODE_AUTO && d->mode != HISA_MODE_FORCE_FLAT && d->mode != HISA_MODE_FORCE_DENSE)
       return fail(HISA_ERR_ARG, "mode = %d", d->mode);
     if (d->mode == HISA_MODE_FORCE_DENSE &&
-        (op == HISA_OP_SELECT_DECODE || op == HISA_OP_SELECT_PREFILL || op == HISA_OP_SELECT_DECODE_CACHED) &&
+        (op == HISA_OP_SELECT_DECODE || op == HISA_OP_SELECT_PREFILL || op == HISA_OP_SELECT_DECODE_CACHED ||
+         op == HISA_OP_DECODE_STEP) &&
         d->topk < d->Np_cap)
       return fail(HISA_ERR_ARG, "HISA_MODE_FORCE_DENSE lists every pooled row: topk = %d must be >= Np_cap = %d",
                   d->topk, d->Np_cap);
@@ -83,8 +86,9 @@ int make_kdims(int op, const hisa_dims* d, KDims* k) {
     if (op == HISA_OP_BLOCK_SCORES && d->index_block == 0) return fail(HISA_ERR_ARG, "hisa_block_scores needs index_block > 0");
     if (op == HISA_OP_BLOCK_MEANS_UPDATE && d->index_block == 0)
       return fail(HISA_ERR_ARG, "hisa_block_means_update needs index_block > 0");
-    if (op == HISA_OP_SELECT_DECODE && d->L != 1)
-      return fail(HISA_ERR_ARG, "hisa_select_decode needs L == 1 (got %d)", d->L);
+    if ((op == HISA_OP_SELECT_DECODE || op == HISA_OP_DECODE_STEP) && d->L != 1)
+      return fail(HISA_ERR_ARG, "%s needs L == 1 (got %d)",
+                  op == HISA_OP_SELECT_DECODE ? "hisa_select_decode" : "hisa_decode_step", d->L);
     if (op == HISA_OP_SELECT_DECODE_CACHED && (long long)d->B * d->L > 65535)
       return fail(HISA_ERR_ARG, "hisa_select_decode_cached takes at most 65535 query rows (B * L = %lld)",
                   (long long)d->B * d->L);
@@ -99,21 +103,22 @@ int make_kdims(int op, const hisa_dims* d, KDims* k) {
       return fail(HISA_ERR_ARG,
                   "hisa_select_decode_cached needs bf16 keys, H_i = 64, D_i = 128, index_block > 0, nb_cap <= 4096, "
                   "index_keep <= 64, topk <= index_block * index_keep <= 1024 and no forced flat scan");
-  } else {
+  }
+  if (is_att(op)) {
     if (d->attn_dtype != HISA_F32 && d->attn_dtype != HISA_BF16) return fail(HISA_ERR_DTYPE, "attn_dtype %d", d->attn_dtype);
     if (d->H < 1 || d->Dk < 1 || d->Dv < 1 || d->Dv > d->Dk) return fail(HISA_ERR_ARG, "H = %d, Dk = %d, Dv = %d (need 1 <= Dv <= Dk)", d->H, d->Dk, d->Dv);
-    if (d->kI < 0) return fail(HISA_ERR_ARG, "kI = %d must be >= 0", d->kI);
+    if (kd.kI < 0) return fail(HISA_ERR_ARG, "kI = %d must be >= 0", kd.kI);
     if (d->window > 0 && d->Wl_cap < 1) return fail(HISA_ERR_ARG, "Wl_cap = %d must be >= 1 when window > 0", d->Wl_cap);
     const long long rows = (long long)d->B * d->L;
     if (rows * d->H * d->Dk > kMaxElems || (long long)d->B * d->Np_cap * d->Dk > kMaxElems ||
-        (long long)d->B * d->Wl_cap * d->Dk > kMaxElems || rows * d->kI > kMaxElems)
+        (long long)d->B * d->Wl_cap * d->Dk > kMaxElems || rows * kd.kI > kMaxElems)
       return fail(HISA_ERR_OVERFLOW, "attention tensors too large");
     if (rows > 2147483647LL) return fail(HISA_ERR_OVERFLOW, "B * L overflows the grid");
     kd.attn_scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d->Dk));
     const bool bf = d->attn_dtype == HISA_BF16;
     if (!hisa::attn_mfma_ok(kd, bf) && !hisa::attn_generic_ok(kd))
       return fail(HISA_ERR_ARG, "shape not supported: Dk = %d, window + kI = %lld (generic path needs Dk <= 1024 and window + kI <= 4096)",
-                  d->Dk, (long long)d->window + d->kI);
+                  d->Dk, (long long)d->window + kd.kI);
   }
   *k = kd;
   return HISA_OK;
@@ -122,6 +127,7 @@ int make_kdims(int op, const hisa_dims* d, KDims* k) {
 struct Layout {
   size_t total = 0;
   size_t rep = 0, rep3 = 0, cscore = 0, scores = 0, fscore = 0, partial = 0, cnt = 0, blk = 0;
+  size_t sync = 0, sel = 0;  // decode step: its sync words, and the selection's part
   int splits = 1;
 };
 
@@ -209,6 +215,23 @@ Layout layout(int op, const hisa_dims* d, const KDims& k) {
       l.splits = hisa::attn_splits(k, d->attn_dtype == HISA_BF16);
       l.partial = take(l, hisa::attn_partial_bytes(k, l.splits));
       break;
+    case HISA_OP_DECODE_STEP: {
+      // The sync words of the one-kernel step, then hisa_select_decode's
+      // workspace (counters first), then room for either kind of partials:
+      // the same offsets whichever way a call runs, so the words that must
+      // rest at zero never share bytes with scratch data.
+      l.sync = take(l, hisa::decode_step_sync_bytes(k));
+      l.sel = l.total;
+      if (!k.force_dense) {
+        l.cnt = take(l, hisa::decode_counter_ints(k) * sizeof(int));
+        l.fscore = take(l, B * d->Np_cap * sizeof(float));
+        l.cscore = take(l, B * std::max<size_t>(nb_cap, 1) * sizeof(float));
+      }
+      l.partial = l.total;
+      l.splits = hisa::attn_splits(k, d->attn_dtype == HISA_BF16);
+      take(l, std::max(hisa::decode_step_partial_bytes(k), hisa::attn_partial_bytes(k, l.splits)));
+      break;
+    }
   }
   return l;
 }
@@ -304,6 +327,30 @@ int scratch_of_current_device(hipStream_t st, void** out) {
     g_scratch_ptr[dev] = p;
   }
   *out = g_scratch_ptr[dev];
+  return HISA_OK;
+}
+
+// Compute units of the device `st` runs on (NULL: the current device).
+int device_cus(hipStream_t st, int* cus) {
+  static std::mutex mu;
+  static int cache[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e;
+  if (st) {
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(st, &sdev);
+    dev = (int)sdev;
+  } else {
+    e = hipGetDevice(&dev);
+  }
+  if (e != hipSuccess) return launch_fail(e, "device of the stream");
+  if (dev < 0 || dev >= kMaxDevices) return fail(HISA_ERR_ARG, "device %d is past the %d supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!cache[dev]) {
+    e = hipDeviceGetAttribute(&cache[dev], hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return launch_fail(e, "hipDeviceGetAttribute");
+  }
+  *cus = cache[dev];
   return HISA_OK;
 }
 
@@ -591,6 +638,44 @@ int sparse_local_pooled_attention_ring(const hisa_dims* d, const void* q, const 
     return fail(HISA_ERR_ARG, "a ring of Wl_cap = %d slots cannot hold window + L - 1 = %lld positions", d->Wl_cap,
                 (long long)d->window + d->L - 1);
   return attention_call(d, q, local_ring, pooled_kv, I, sinks, t0, ring_slot, true, out, ws, ws_bytes, stream);
+}
+
+int hisa_decode_step(const hisa_dims* d, const void* q_idx, const float* w, const void* keys, const void* q,
+                     const void* local_kv, const void* pooled_kv, const float* sinks, const int32_t* t0,
+                     int32_t* I_out, int32_t* top_blk_out, int32_t* path_out, void* out, void* ws, size_t ws_bytes,
+                     void* stream) {
+  g_err.clear();
+  KDims k;
+  Layout l;
+  int rc = prepare(HISA_OP_DECODE_STEP, d, &k, &l, ws, ws_bytes);
+  if (rc) return rc;
+  if ((rc = check_ptrs({q_idx, w, keys, q, pooled_kv, t0, I_out, out}, "q_idx, w, keys, q, pooled_kv, t0, I_out, out")))
+    return rc;
+  if (d->window > 0 && !local_kv) return fail(HISA_ERR_ARG, "local_kv is NULL with window > 0");
+  hipStream_t st = (hipStream_t)stream;
+  int cus = 0;
+  if ((rc = device_cus(st, &cus))) return rc;
+  if (!k.force_dense && hisa::decode_step_ok(k, d->idx_dtype == HISA_BF16, d->attn_dtype == HISA_BF16, cus)) {
+    float* part = at<float>(ws, l.partial);
+    hipError_t e = timed("decode_step", st, [&] {
+      return hisa::launch_decode_step(k, q_idx, w, keys, t0, q, local_kv, pooled_kv, sinks, at<void>(ws, l.sync),
+                                      at<int>(ws, l.cnt), at<float>(ws, l.fscore), at<float>(ws, l.cscore), part,
+                                      I_out, top_blk_out, path_out, st);
+    });
+    if (e == hipSuccess)
+      e = timed("attention_merge", st, [&] {
+        return hisa::launch_attention_merge(k, true, part, sinks, out, hisa::decode_step_splits(k), st);
+      });
+    return e == hipSuccess ? HISA_OK : launch_fail(e, "decode step");
+  }
+  // the selection call, then the attention call on its index row
+  rc = hisa_select_decode(d, q_idx, w, keys, t0, I_out, top_blk_out, path_out, at<void>(ws, l.sel),
+                          l.partial - l.sel, stream);
+  if (rc) return rc;
+  hisa_dims da = *d;
+  da.kI = d->topk;
+  return attention_call(&da, q, local_kv, pooled_kv, I_out, sinks, t0, nullptr, false, out, at<void>(ws, l.partial),
+                        l.total - l.partial, stream);
 }
 
 int hisa_profile_enable(int on) {

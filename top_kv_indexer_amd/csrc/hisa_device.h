@@ -12,6 +12,8 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;  // LDS operand of the transposing reads
 
 constexpr float kNeg = -1e30f;  // the selection paths' finite mask value
 constexpr float kLog2e = 1.4426950408889634f;
@@ -248,6 +250,75 @@ __device__ __forceinline__ SeqInfo seq_info(const KDims& d, int t0) {
 // V(t) = min(Np, floor((t + 1) / ratio)) for query position t (0 for t < 0)
 __device__ __forceinline__ int visible(const KDims& d, int t, int Np) {
   return t < 0 ? 0 : min(Np, (int)div_ratio(d, (uint32_t)t + 1u));
+}
+
+// Device-scope int and 64-bit stores / loads (the same coherence point as
+// st_dev / ld_dev): flags and lists handed to workgroups on other XCDs.
+__device__ __forceinline__ void st_dev_i(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ld_dev_i(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev_u64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_dev_u64(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---- attention row lists (the sparse combine's local and pooled rows)
+
+// LDS slot (16-byte units) of chunk ch of a KV or q row whose swizzle is x
+// (0..15): the first 64 chunks (512 dims) XOR x in their low four bits; the
+// chunks past them XOR x inside the row's tail, which the row pitch rounds up
+// to whole 256-byte groups.  16 rows with distinct x then read one chunk from
+// 16 distinct 16-byte slots, conflict free, in the tail as in the body.
+__device__ __forceinline__ int tail_pos(int ch, int x) { return ch < 64 ? (ch ^ x) : 64 + ((ch - 64) ^ x); }
+
+struct RowPlan {
+  bool ok;
+  int Np, V, ls, s_lo, n_loc, n_list;
+  int lbase;  // local_kv row of position s_lo (the first local entry)
+};
+
+// Ring slot of position t0[b] (ring layout only; read with t0).
+__device__ __forceinline__ int ring_slot0(const KDims& d, int b, int T0) {
+  if (!d.local_ring) return 0;
+  if (d.ring_slot) return d.ring_slot[b];
+  return T0 >= 0 ? T0 % d.Wl_cap : 0;
+}
+
+// Local rows: linear layout, row r holds position ls + r; ring layout
+// (Wl_cap >= window + L - 1, checked by the host), position s sits in slot
+// (S0 + s - T0) mod Wl_cap.  Either way local entry k is row lbase + k,
+// wrapped once past Wl_cap (which only the ring reaches).
+__device__ __forceinline__ RowPlan row_plan(const KDims& d, int T0, int S0, int j) {
+  RowPlan r;
+  const uint32_t np = T0 >= 0 ? div_ratio(d, (uint32_t)T0 + (uint32_t)d.L) : 0u;
+  r.ls = max(0, T0 - d.window + 1);
+  const bool local_ok = d.window == 0 || (d.local_ring ? (S0 >= 0 && S0 < d.Wl_cap)
+                                                       : (long long)T0 + d.L - r.ls <= d.Wl_cap);
+  r.ok = T0 >= 0 && np <= (uint32_t)d.Np_cap && local_ok;
+  r.Np = r.ok ? (int)np : 0;
+  const int t = T0 + j;
+  r.V = visible(d, t, r.Np);
+  r.s_lo = max(r.ls, t - d.window + 1);
+  r.n_loc = (r.ok && d.window > 0) ? t - r.s_lo + 1 : 0;
+  r.n_list = r.ok ? r.n_loc + d.kI : 0;
+  if (d.local_ring) {
+    int base = S0 + (r.s_lo - T0);  // in (-Wl_cap, 2 Wl_cap)
+    base = base < 0 ? base + d.Wl_cap : (base >= d.Wl_cap ? base - d.Wl_cap : base);
+    r.lbase = r.ok ? base : 0;
+  } else {
+    r.lbase = r.s_lo - r.ls;
+  }
+  return r;
+}
+
+__device__ __forceinline__ int local_row(const KDims& d, const RowPlan& rp, int k) {
+  const int r = rp.lbase + k;
+  return r >= d.Wl_cap ? r - d.Wl_cap : r;
 }
 
 // Shared memory of block_topk.

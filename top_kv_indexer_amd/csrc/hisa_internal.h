@@ -39,6 +39,22 @@ bool decode_fused_ok(const KDims& d, bool bf16);
 hipError_t launch_decode_scan(const KDims& d, bool bf16, const void* q_idx, const float* w,
                               const void* keys, const int* t0, float* fscore, float* cscore,
                               int* cnt, int* I, int* top_blk, int* path, hipStream_t st);
+// The decode step (selection + sparse combine) of few sequences in one
+// launch up to the split partials, which launch_attention_merge (splits =
+// decode_step_splits) then combines: decode_step_ok (max_attn_wgs: attention
+// workgroups the device holds at once with room to spare, e.g. its CU
+// count).  Workspace: the sync region (decode_step_sync_bytes, zero at first
+// use and left zero; its first int becomes 1 if a hand-off ever timed out),
+// the scan counters (decode_counter_ints, the same rule), fscore, cscore and
+// the partials (decode_step_partial_bytes).
+bool decode_step_ok(const KDims& d, bool idx_bf16, bool attn_bf16, int max_attn_wgs);
+int decode_step_splits(const KDims& d);
+size_t decode_step_sync_bytes(const KDims& d);
+size_t decode_step_partial_bytes(const KDims& d);
+hipError_t launch_decode_step(const KDims& d, const void* q_idx, const float* w, const void* keys, const int* t0,
+                              const void* q, const void* local_kv, const void* pooled_kv, const float* sinks,
+                              void* sync, int* cnt, float* fscore, float* cscore, float* part, int* I, int* top_blk,
+                              int* path, hipStream_t st);
 hipError_t launch_decode_select(const KDims& d, const float* fscore, const float* cscore,
                                 const int* t0, int* I, int* top_blk, int* path, hipStream_t st);
 hipError_t launch_block_mean(const KDims& d, bool bf16, bool all_paths, const void* keys,

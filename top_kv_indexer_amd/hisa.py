@@ -16,11 +16,12 @@ F32, BF16 = 0, 1
 MODE_AUTO, MODE_FORCE_FLAT, MODE_FORCE_DENSE = 0, 1, 2
 PATH_INVALID, PATH_DENSE, PATH_FLAT, PATH_HISA = -1, 0, 1, 2
 (OP_BLOCK_SCORES, OP_SELECT_DECODE, OP_SELECT_PREFILL, OP_FLAT_TOPK, OP_ATTENTION, OP_SELECT_DECODE_CACHED,
- OP_BLOCK_MEANS_UPDATE) = range(7)
+ OP_BLOCK_MEANS_UPDATE, OP_DECODE_STEP) = range(8)
 
 EXPORTS = ("hisa_block_scores", "hisa_select_decode", "hisa_select_decode_noalloc", "hisa_select_decode_cached",
            "hisa_block_means_update", "hisa_select_prefill", "flat_topk_select",
-           "sparse_local_pooled_attention", "sparse_local_pooled_attention_ring", "hisa_workspace_bytes",
+           "sparse_local_pooled_attention", "sparse_local_pooled_attention_ring", "hisa_decode_step",
+           "hisa_workspace_bytes",
            "hisa_last_error", "hisa_abi_version",
            "hisa_profile_enable", "hisa_profile_collect")
 
@@ -61,9 +62,10 @@ def lib() -> ctypes.CDLL:
         L.flat_topk_select.argtypes = sel + [vp, vp, sz, vp]
         L.sparse_local_pooled_attention.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.sparse_local_pooled_attention_ring.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.hisa_decode_step.argtypes = [dp] + [vp] * 13 + [sz, vp]
         for f in ("hisa_block_scores", "hisa_select_decode", "hisa_select_decode_noalloc", "hisa_select_decode_cached",
                   "hisa_block_means_update", "hisa_select_prefill", "flat_topk_select",
-                  "sparse_local_pooled_attention", "sparse_local_pooled_attention_ring"):
+                  "sparse_local_pooled_attention", "sparse_local_pooled_attention_ring", "hisa_decode_step"):
             getattr(L, f).restype = i32
         L.hisa_workspace_bytes.argtypes = [i32, dp]
         L.hisa_workspace_bytes.restype = sz
@@ -145,8 +147,9 @@ def workspace_bytes(op: int, d: hisa_dims) -> int:
 # One workspace per (device, stream, op), grown on demand and reused by every
 # call of that op on that stream (calls on one stream are ordered, so they
 # never overlap).  The decode selection's arrival counters start zeroed and
-# every call leaves them zero; their region grows with B and Np_cap, so its
-# workspaces are kept per (B, Np_cap) as well.
+# every call leaves them zero; their region grows with B and Np_cap (and the
+# decode step's also with H, topk, index_block and index_keep), so those
+# workspaces are kept per such dims as well.
 _ws_cache = {}
 
 
@@ -161,6 +164,8 @@ def _workspace(op: int, d: hisa_dims, dev: torch.device, ws: Optional[torch.Tens
     key = (dev.index, torch.cuda.current_stream(dev).cuda_stream, op)
     if op in (OP_SELECT_DECODE, OP_SELECT_DECODE_CACHED):
         key += (d.B, d.Np_cap)
+    elif op == OP_DECODE_STEP:
+        key += (d.B, d.Np_cap, d.H, d.topk, d.index_block, d.index_keep)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < n:
         buf = torch.zeros(n, dtype=torch.uint8, device=dev)
@@ -384,6 +389,51 @@ def sparse_local_pooled_attention_ring(q, local_ring, pooled_kv, I, sinks, t0, r
                                                     _p(sinks), _p(t0), _p(ring_slot), _p(out), _p(wsb), n,
                                                     _stream(dev)))
     return out
+
+
+def decode_step_dims(q_idx, keys, q, local_kv, pooled_kv, *, ratio, window, topk, index_block, index_keep,
+                     mode=MODE_AUTO) -> hisa_dims:
+    B, L, H_i, D_i = q_idx.shape
+    H, Dk = q.shape[2], q.shape[3]
+    return hisa_dims(B=B, L=L, ratio=ratio, window=window, topk=topk, index_block=index_block,
+                     index_keep=index_keep, H_i=H_i, D_i=D_i, H=H, Dk=Dk, Dv=Dk, Np_cap=keys.shape[1],
+                     Wl_cap=0 if local_kv is None else local_kv.shape[1], kI=topk, mode=mode,
+                     idx_dtype=_code(keys), attn_dtype=_code(q))
+
+
+def hisa_decode_step(q_idx, w, keys, q, local_kv, pooled_kv, sinks, t0, *, ratio, window, topk, index_block=64,
+                     index_keep=16, mode=MODE_AUTO, I=None, top_blk=None, path=None, out=None, ws=None):
+    """The whole decode step (selection, then the combine on its index row); returns
+    I (B,1,topk), top_blk (B,1,index_keep), path (B), out (B,1,H,Dk).  pooled_kv and
+    keys share Np_cap.  A caller-given ws must start with its counter region zeroed
+    (see include/hisa.h)."""
+    B, L = _sel_args(q_idx, w, keys, t0)
+    if L != 1:
+        raise HisaError(f"hisa_decode_step takes one query row per sequence (q_idx has L = {L})")
+    dev = _attn_args(q, local_kv, pooled_kv, None, sinks, t0, window, None, out, ws)
+    _need(q, "q", 4, None, (B, 1, None, None))
+    _need(pooled_kv, "pooled_kv", 3, None, (B, keys.shape[1], None))
+    if I is not None:
+        _need(I, "I", 3, torch.int32, (B, 1, topk))
+    if top_blk is not None:
+        _need(top_blk, "top_blk", 3, torch.int32, (B, 1, index_keep))
+    if path is not None:
+        _need(path, "path", 1, torch.int32, (B,))
+    _same_gpu(q_idx=q_idx, w=w, keys=keys, q=q, I=I, top_blk=top_blk, path=path)
+    d = decode_step_dims(q_idx, keys, q, local_kv, pooled_kv, ratio=ratio, window=window, topk=topk,
+                         index_block=index_block, index_keep=index_keep, mode=mode)
+    if I is None:
+        I = torch.empty((B, 1, topk), dtype=torch.int32, device=dev)
+    if top_blk is None:
+        top_blk = torch.empty((B, 1, index_keep), dtype=torch.int32, device=dev)
+    if path is None:
+        path = torch.empty((B,), dtype=torch.int32, device=dev)
+    if out is None:
+        out = torch.empty((B, 1, d.H, d.Dv), dtype=q.dtype, device=dev)
+    wsb, n = _workspace(OP_DECODE_STEP, d, dev, ws)
+    _check(lib().hisa_decode_step(ctypes.byref(d), _p(q_idx), _p(w), _p(keys), _p(q), _p(local_kv), _p(pooled_kv),
+                                  _p(sinks), _p(t0), _p(I), _p(top_blk), _p(path), _p(out), _p(wsb), n, _stream(dev)))
+    return I, top_blk, path, out
 
 
 def hisa_profile_enable(on: bool) -> None:

@@ -174,7 +174,8 @@ __device__ __forceinline__ uint32_t wave_umin(uint32_t v) {
 // present keys differ (above it they all agree, so no pass is spent on it)
 // and stops as soon as the bin holding the k-th key is taken whole.  Every
 // wave evaluates the same scan of the shared histogram, so the control flow
-// is uniform over the workgroup.
+// is uniform over the workgroup.  Its barriers (and the emitter's) order
+// LDS only: loads and stores the caller has in flight stay in flight.
 constexpr int kAllTies = 0x7FFFFFFF;
 template <int NR, int NK>
 __device__ __forceinline__ uint32_t wg_topk_threshold(const uint32_t (&key)[NK], int k, WgTopkSmem& sm, int& ties) {
@@ -194,7 +195,7 @@ __device__ __forceinline__ uint32_t wg_topk_threshold(const uint32_t (&key)[NK],
   }
   sm.hist[0][tid] = 0u;
   sm.hist[1][tid] = 0u;
-  __syncthreads();
+  lds_sync();
   mn = min(min(sm.red[0][0], sm.red[0][1]), min(sm.red[0][2], sm.red[0][3]));
   mx = max(max(sm.red[1][0], sm.red[1][1]), max(sm.red[1][2], sm.red[1][3]));
   if (mn == mx) {  // every present key is equal
@@ -214,7 +215,7 @@ __device__ __forceinline__ uint32_t wg_topk_threshold(const uint32_t (&key)[NK],
       const uint32_t u = key[r];
       if (u != 0u && (u & mask) == prefix) atomicAdd(&h[(u >> shift) & 255u], 1u);
     }
-    __syncthreads();
+    lds_sync();
     // lane l holds bins 255-4l (first) .. 252-4l
     const uint4 hv = *(const uint4*)&h[252 - 4 * lane];
     // the buffer of pass + 2: every thread finished reading it (pass - 1)
@@ -274,7 +275,7 @@ __device__ __forceinline__ void wg_emit_topk_n(const uint32_t (&key)[NK], int k,
       meq[r] = __ballot(key[r] != 0u && key[r] == t);
       if (lane == 0) sm.cnt[0][r][wv] = (uint32_t)__popcll(meq[r]);
     }
-    __syncthreads();
+    lds_sync();
     int eq_base = 0;
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
@@ -298,7 +299,7 @@ __device__ __forceinline__ void wg_emit_topk_n(const uint32_t (&key)[NK], int k,
     mt[r] = __ballot(take[r]);
     if (lane == 0) sm.cnt[1][r][wv] = (uint32_t)__popcll(mt[r]);
   }
-  __syncthreads();
+  lds_sync();
   int base = 0;
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
@@ -369,7 +370,7 @@ __device__ __forceinline__ void decode_select_wg(const KDims& d, const SeqInfo& 
 #pragma unroll
   for (int r = 0; r < 4; ++r) key[r] = 256 * r + tid < nb ? score_key(v[r]) : 0u;
   wg_emit_topk(key, nb, si.Kb, sm.tk, [&](int slot, int r) { sm.blk[slot] = 256 * r + tid; });
-  __syncthreads();
+  lds_sync();
   if (blkb && tid < si.Kb) blkb[tid] = sm.blk[tid];
   const int bsz = d.index_block, lbsz = __builtin_ctz(bsz);
   const int C = si.Kb * bsz;
@@ -717,7 +718,7 @@ __device__ __forceinline__ void step_select_wg(const KDims& d, const SeqInfo& si
 #pragma unroll
   for (int r = 0; r < 4; ++r) key[r] = 256 * r + tid < nb ? score_key(v[r]) : 0u;
   wg_emit_topk(key, nb, si.Kb, sm.tk, [&](int slot, int r) { sm.blk[slot] = 256 * r + tid; });
-  __syncthreads();
+  lds_sync();
   if (blkb && tid < si.Kb) blkb[tid] = sm.blk[tid];
   const int bsz = d.index_block, lbsz = __builtin_ctz(bsz);
   {

@@ -2328,10 +2328,12 @@ __global__ __launch_bounds__(256) void k_fill_dense(KDims d, const int* __restri
 // instead of re-reading every key (HiSA issue, HiSA decode path: O(nb + Kb*b)
 // scores per step; The pooled stream and positions: the pooled stream grows
 // in whole windows, so a complete block never changes).  Two kernels:
-//   coarse (ceil(nb_cap / 16), B) x 256: wave w scores blocks 16x + 4w ..
-//          +3 with lane h holding head h; a block completed by this step's
-//          token is averaged from the keys (f32, rows in order) and written to
-//          the cache first, every other block is read from it.  The workgroup
+//   coarse (ceil(nb_cap / 16), B) x 256: the workgroup's 16 blocks are
+//          staged in LDS (a block completed by this step's token averaged
+//          from the keys, f32, rows in order, and written to the cache first;
+//          every other block read from it), then wave w scores them against
+//          heads 16w .. 16w+15 on MFMA, each f32 mean split into three bf16
+//          parts (a bf16 query times a part is exact in f32).  The workgroup
 //          that completes a sequence keeps its top-Kb blocks.
 //   fine   (16, B) x 256: 64 candidates per workgroup (the retained blocks'
 //          rows, or the rows of a flat sequence) scored on MFMA like the scan;
@@ -2362,7 +2364,10 @@ __global__ __launch_bounds__(256) void k_cached_coarse(KDims d, const uint16_t* 
                                                        const float* __restrict__ w, const uint16_t* __restrict__ keys,
                                                        float* rep, const int* __restrict__ t0, float* cscore, int* blk,
                                                        int* cnt, int* I, int* top_blk, int* path) {
-  __shared__ __align__(16) float s_rep[4][4][128];
+  // the workgroup's 16 block means; the row pitch of 132 floats puts the 16
+  // blocks' same chunk in distinct banks for the operand reads
+  __shared__ __align__(16) float s_rep[kCachedBlocksPerWg][132];
+  __shared__ float s_part[4][16];
   __shared__ WgTopkSmem s_tk;
   __shared__ int s_flag;
   args_now(d, q_idx, w, keys, rep, t0, cscore, blk, cnt, I, top_blk, path);
@@ -2370,17 +2375,24 @@ __global__ __launch_bounds__(256) void k_cached_coarse(KDims d, const uint16_t* 
   // chunk) each select on their own, with the batched masks
   const int row = blockIdx.y, x = blockIdx.x;
   const int b = row / d.L, j = row - b * d.L;
-  const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
+  const int tid = threadIdx.x, lane = lane_id(), wv = wave_id(), g = lane >> 4, c = lane & 15;
   const int t0b = t0[b];
-  // this lane's head: q row (256 B) and weight, requested before t0 arrives
-  uint4 qv[16];
-  const uint4* qrow = (const uint4*)(q_idx + ((size_t)row * 64 + lane) * 128);
+  // this wave's 16 heads as the MFMA A operand (lane (g, c): head 16w + c,
+  // dims 32s + 8g .. +7) and the weights of the lane's output heads
+  // 16w + 4g + i, requested before t0 arrives
+  bf16x8 qa[4];
+  {
+    const uint16_t* qrow = q_idx + ((size_t)row * 64 + 16 * wv + c) * 128 + 8 * g;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) qv[i] = qrow[i];
-  const float wh = w[(size_t)row * 64 + lane] * d.w_scale;
-  // the cached means of this wave's blocks, also requested before t0 arrives
-  // (a block completed by this step is recomputed below instead)
-  const int beta0 = x * kCachedBlocksPerWg + 4 * wv;
+    for (int s = 0; s < 4; ++s) qa[s] = *(const bf16x8*)(qrow + 32 * s);
+  }
+  float wl[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) wl[i] = w[(size_t)row * 64 + 16 * wv + 4 * g + i] * d.w_scale;
+  // the cached means of blocks 4w .. 4w+3 of the workgroup, also requested
+  // before t0 arrives (a block completed by this step is recomputed instead)
+  const int bx0 = x * kCachedBlocksPerWg;
+  const int beta0 = bx0 + 4 * wv;
   float* repb = rep + (size_t)b * d.nb_cap * 128;
   float2 mc[4];
 #pragma unroll
@@ -2410,37 +2422,54 @@ __global__ __launch_bounds__(256) void k_cached_coarse(KDims d, const uint16_t* 
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
     const int beta = beta0 + jj;
-    if (beta >= si.nb) break;  // uniform over the wave
-    float2 m = mc[jj];
-    if (beta >= first_new) {
-      m = block_mean_lane(kb, beta, bsz);
-      if (row == b * d.L) *(float2*)&repb[(size_t)beta * 128 + 2 * lane] = m;  // the sequence's first row stores it
+    float2 m = make_float2(0.f, 0.f);  // (blocks past nb are never stored)
+    if (beta < si.nb) {
+      m = mc[jj];
+      if (beta >= first_new) {
+        m = block_mean_lane(kb, beta, bsz);
+        if (row == b * d.L) *(float2*)&repb[(size_t)beta * 128 + 2 * lane] = m;  // the sequence's first row stores it
+      }
     }
-    *(float2*)&s_rep[wv][jj][2 * lane] = m;
+    *(float2*)&s_rep[4 * wv + jj][2 * lane] = m;
   }
-  __builtin_amdgcn_wave_barrier();
-  // one wave's LDS operations complete in order: the stores above land
-  // before the broadcast reads below
-#pragma unroll 1
-  for (int jj = 0; jj < 4; ++jj) {
-    const int beta = beta0 + jj;
-    if (beta >= si.nb) break;
-    float acc = 0.f;
+  __syncthreads();
+  // D[head][block] = q_head . rep_block: A = q, B = the block means (lane
+  // (g, c): block c, dims 32s + 8g .. +7) as hi + mid + lo bf16 parts
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float4 r0 = *(const float4*)&s_rep[wv][jj][8 * i];
-      const float4 r1 = *(const float4*)&s_rep[wv][jj][8 * i + 4];
-      acc = fmaf(bf_lo(qv[i].x), r0.x, acc);
-      acc = fmaf(bf_hi(qv[i].x), r0.y, acc);
-      acc = fmaf(bf_lo(qv[i].y), r0.z, acc);
-      acc = fmaf(bf_hi(qv[i].y), r0.w, acc);
-      acc = fmaf(bf_lo(qv[i].z), r1.x, acc);
-      acc = fmaf(bf_hi(qv[i].z), r1.y, acc);
-      acc = fmaf(bf_lo(qv[i].w), r1.z, acc);
-      acc = fmaf(bf_hi(qv[i].w), r1.w, acc);
+  for (int s = 0; s < 4; ++s) {
+    const float4 r0 = *(const float4*)&s_rep[c][32 * s + 8 * g];
+    const float4 r1 = *(const float4*)&s_rep[c][32 * s + 8 * g + 4];
+    const float xv[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+    u32x4 hi, mid, lo;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float x0 = xv[2 * k], x1 = xv[2 * k + 1];
+      const uint32_t hp = pack_bf16x2(x0, x1);
+      const float e0 = x0 - __uint_as_float(hp << 16), e1 = x1 - __uint_as_float(hp & 0xFFFF0000u);
+      const uint32_t mp = pack_bf16x2(e0, e1);
+      hi[k] = hp;
+      mid[k] = mp;
+      lo[k] = pack_bf16x2(e0 - __uint_as_float(mp << 16), e1 - __uint_as_float(mp & 0xFFFF0000u));
     }
-    const float cs = wave_sum(relu(acc) * wh);
-    if (lane == 0) st_dev(cscore + (size_t)row * d.nb_cap + beta, beta * bsz < V ? cs : kNeg);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], __builtin_bit_cast(bf16x8, hi), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], __builtin_bit_cast(bf16x8, mid), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], __builtin_bit_cast(bf16x8, lo), acc, 0, 0, 0);
+  }
+  // relu . w over the lane's heads 16w + 4g + i, then over the wave's 16
+  // heads (lanes c, c+16, c+32, c+48), then over the four waves
+  float hv = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) hv += relu(acc[i]) * wl[i];
+  hv = sum_rows(hv);
+  if (g == 0) s_part[wv][c] = hv;
+  __syncthreads();
+  if (wv == 0 && lane < 16) {
+    const int beta = bx0 + lane;
+    if (beta < si.nb) {
+      const float cs = (s_part[0][lane] + s_part[1][lane]) + (s_part[2][lane] + s_part[3][lane]);
+      st_dev(cscore + (size_t)row * d.nb_cap + beta, beta * bsz < V ? cs : kNeg);
+    }
   }
   // cnt: B*L row counters, then B*L x ngmax group counters
   const int nrows = d.B * d.L;

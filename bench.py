@@ -8,7 +8,10 @@ default workload is one V4-Flash-shaped decode step at Np = 16384 pooled keys
 (B = 1, 64 x 128 bf16 indexer, top-512 of blocks of 64, 64 heads x 512, window
 128, sinks).  Inputs are resident in HBM before timing starts.
 
-Timing (HIP events on the stream the library launches on):
+Timing (HIP events on the stream the library launches on, created with
+hipEventDisableSystemFence: a default event's record adds a system-scope
+cache writeback and invalidation, ~3 us, to the interval it closes; these
+events time the launches between them, as the profiler's kernel trace does):
   cold  before every step a kernel reads a 1 GiB buffer (outside the step's
         events), which evicts the step's data from the 256 MiB Infinity Cache
         and the L2s; K steps, each between its own pair of events; the median
@@ -204,6 +207,52 @@ def cpu_baseline(w, x, seconds):
             "threads_from": "OMP_NUM_THREADS" if env.isdigit() else "sched_getaffinity"}
 
 
+class HipEvent:
+    """A timing event of the HIP runtime that torch and the library share,
+    recorded on torch's current stream (the stream the library launches on)
+    without the system-scope fence of a default event."""
+    _hip = None
+    _DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence
+
+    @classmethod
+    def _rt(cls):
+        if cls._hip is None:
+            import torch  # noqa: F401  (loads the runtime; the soname below then names that copy)
+            h = ctypes.CDLL("libamdhip64.so.7")
+            vp = ctypes.c_void_p
+            h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(vp), ctypes.c_uint]
+            h.hipEventRecord.argtypes = [vp, vp]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+            h.hipEventDestroy.argtypes = [vp]
+            cls._hip = h
+        return cls._hip
+
+    def __init__(self):
+        self.e = ctypes.c_void_p()
+        r = self._rt().hipEventCreateWithFlags(ctypes.byref(self.e), self._DISABLE_SYSTEM_FENCE)
+        if r:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({r})")
+
+    def record(self):
+        import torch
+        r = self._rt().hipEventRecord(self.e, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if r:
+            raise RuntimeError(f"hipEventRecord failed ({r})")
+
+    def elapsed_time(self, end):
+        """Milliseconds from this event to end (both complete)."""
+        ms = ctypes.c_float()
+        r = self._rt().hipEventElapsedTime(ctypes.byref(ms), self.e, end.e)
+        if r:
+            raise RuntimeError(f"hipEventElapsedTime failed ({r})")
+        return ms.value
+
+    def __del__(self):
+        if self.e and HipEvent._hip is not None:
+            HipEvent._hip.hipEventDestroy(self.e)
+            self.e = ctypes.c_void_p()
+
+
 def percentiles(ms):
     import numpy as np
     a = np.asarray(ms, np.float64)
@@ -319,7 +368,7 @@ def harness(w, x, selector, step_call="two_calls"):
     def cold(fn, k):
         """k runs of fn, each after a flush and between its own two events;
         returns the per-run milliseconds."""
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(k)]
+        ev = [(HipEvent(), HipEvent()) for _ in range(k)]
         for i in range(k):
             flush()
             ev[i][0].record()
@@ -329,7 +378,7 @@ def harness(w, x, selector, step_call="two_calls"):
         return [a.elapsed_time(b) for a, b in ev]
 
     def hot(fn, k):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = HipEvent(), HipEvent()
         torch.cuda.synchronize()
         e0.record()
         for i in range(k):
@@ -345,7 +394,7 @@ def cold_ms(fn, k):
     """k runs of fn(i), each after a flush and between its own two HIP events
     (on the current stream); the median milliseconds."""
     import torch
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(k)]
+    ev = [(HipEvent(), HipEvent()) for _ in range(k)]
     for i in range(k):
         flush()
         ev[i][0].record()

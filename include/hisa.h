@@ -309,7 +309,9 @@ int hisa_abi_version(void);
 
 /* Kernel timing, a tracing aid (off by default).  While enabled, each kernel
  * the library launches is bracketed by two hipEvents recorded on the call's
- * stream.  hisa_profile_collect() waits for the recorded events, adds their
+ * stream (timing-only events, created with hipEventDisableSystemFence, so the
+ * interval holds the launch and not a system-scope cache writeback).
+ * hisa_profile_collect() waits for the recorded events, adds their
  * elapsed times to per-kernel totals, copies up to max_entries totals to out
  * and returns how many kernels have totals (or a negative HISA_ERR_*).
  * hisa_profile_enable(0) stops recording and clears the totals.  Not

@@ -274,8 +274,10 @@ hipEvent_t prof_event() {
     g_prof_pool.pop_back();
     return e;
   }
+  // timing only: without the system-scope fence of a default event, whose
+  // cache writeback and invalidation would be timed as part of the launch
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 

@@ -199,9 +199,9 @@ int hisa_select_decode_noalloc(const hisa_dims* d, const void* q_idx, const floa
                                void* stream);
 
 /* Multi-row selection (HiSA issue, HiSA batched path: prefill chunks and
- * multi-token verify; any L >= 1).  Chunks of at most 8 rows per sequence
- * (verify) take the cached-means kernels of hisa_select_decode_cached on
- * block means computed into the workspace.  Per query row j: valid_len = V(t0+j);
+ * multi-token verify; any L >= 1).  Chunks of at most 192 query rows in all
+ * (B * L; verify and short chunks) take the cached-means kernels of
+ * hisa_select_decode_cached on block means computed into the workspace.  Per query row j: valid_len = V(t0+j);
  * blocks with b*beta >= valid_len score -1e30; candidates at or past
  * valid_len score -1e30.  Rows with fewer than k visible rows then carry
  * masked ids, which the attention call re-masks.

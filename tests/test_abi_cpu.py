@@ -73,10 +73,14 @@ def test_workspace_sizes(lib):
     # candidates past one wave's registers: coarse scores per row and the flat scan
     assert hisa.workspace_bytes(hisa.OP_SELECT_PREFILL, dims(L=2048, index_keep=64)) == (
         rep + 2048 * 256 * 4 + 2048 * 16384 * 4)
-    # a verify chunk (L <= 8): every block mean (f32), then per row the
-    # cached-means selection (counters, block scores, kept blocks, candidates)
+    # a short chunk (B * L <= 192 rows): every block mean (f32), then per row
+    # the cached-means selection (counters, block scores, kept blocks, candidates)
     assert hisa.workspace_bytes(hisa.OP_SELECT_PREFILL, dims(L=4)) == (
         256 * 128 * 4 + 768 + 4 * 256 * 4 + 256 + 4 * 1024 * 4)
+    assert hisa.workspace_bytes(hisa.OP_SELECT_PREFILL, dims(L=192)) == (
+        256 * 128 * 4 + 192 * 3 * 64 + 192 * 256 * 4 + 192 * 16 * 4 + 192 * 1024 * 4)
+    # one row more: one query row per wave
+    assert hisa.workspace_bytes(hisa.OP_SELECT_PREFILL, dims(L=193)) == rep
     # no hierarchy: only the flat scan
     assert hisa.workspace_bytes(hisa.OP_SELECT_PREFILL, dims(L=4, index_block=0, Np_cap=1000)) == (
         (4 * 1000 * 4 + 255) // 256 * 256)

@@ -194,15 +194,22 @@ VERIFY = synth.Workload("verify_b4_l8", B=4, L=8, ratio=1, window=128, topk=512,
                         t0=[1083, 694, 294, 16384], planted=4, Np_cap=16400)
 
 
-@pytest.mark.parametrize("L", [1, 2, 4, 8])
+@pytest.mark.parametrize("L", [1, 2, 4, 8, 48])
 def test_short_prefill_chunks(hisa, L):
-    # hisa_select_prefill with at most 8 rows per sequence: block means of every
-    # complete block into the workspace, then the cached-means selection per row
-    w = VERIFY.with_(L=L)
+    # hisa_select_prefill with few query rows in all (4 sequences x L <= 192):
+    # block means of every complete block into the workspace, then the
+    # cached-means selection per row
+    w = VERIFY.with_(L=L, Np_cap=max(16400, 16384 + L))
     x, g = inputs(w, 63)
     say(f"[run] short prefill chunk, L = {L}")
-    I, blk, path = hisa.hisa_select_prefill(g["q_idx"], g["w"], g["keys"], g["t0"], **sel_kw(w))
-    torch.cuda.synchronize()
+    hisa.hisa_profile_enable(True)
+    try:
+        I, blk, path = hisa.hisa_select_prefill(g["q_idx"], g["w"], g["keys"], g["t0"], **sel_kw(w))
+        torch.cuda.synchronize()
+        names = set(hisa.hisa_profile_collect())
+    finally:
+        hisa.hisa_profile_enable(False)
+    assert "cached_decode" in names and "select_rows" not in names, names
     assert parity.to_np(path).tolist() == [hisa.PATH_HISA, hisa.PATH_FLAT, hisa.PATH_DENSE, hisa.PATH_HISA]
     check_selection(w, x, I, blk, path)
     # the same call on a workspace holding another call's data (the counters are zeroed by the call itself)

@@ -526,21 +526,28 @@ def test_prefill_early_rows_and_small_t0(hisa):
     check_attention(w, x, I, out, sample=40)
 
 
-ROWS = synth.Workload("rows_prefill_b4_l37", B=4, L=37, ratio=4, window=128, topk=64, index_block=8,
+ROWS = synth.Workload("rows_prefill_b4_l53", B=4, L=53, ratio=4, window=128, topk=64, index_block=8,
                       index_keep=10, H_i=64, D_i=128, H=64, Dk=512, Dv=512, bf16=True,
-                      t0=[20000, 3000, 280, 200], planted=0, Np_cap=5016)
+                      t0=[20000, 3000, 264, 200], planted=0, Np_cap=5016)
 
 
 def test_prefill_rows_small_blocks_mixed_paths(hisa):
-    # The one-row-per-wave batched selection with index_block 8 and keep 10:
-    # C = 80 candidates (a partial 16-row tile and a partial 64-entry key
-    # row), nb up to 626 blocks, L = 37 (the last workgroup holds one row),
-    # and one sequence on each of the HiSA / flat / dense paths.
+    # The one-row-per-wave batched selection (B * L = 212 rows, past the
+    # cached-means kernels' share) with index_block 8 and keep 10: C = 80
+    # candidates (a partial 16-row tile and a partial 64-entry key row), nb up
+    # to 626 blocks, L = 53 (the last workgroup holds one row), and one
+    # sequence on each of the HiSA / flat (Np = 79) / dense (Np = 63) paths.
     w = ROWS
     x, g = inputs(w, 11)
     say("[run] small-block prefill")
-    I, blk, path = hisa.hisa_select_prefill(g["q_idx"], g["w"], g["keys"], g["t0"], **sel_kw(w))
-    torch.cuda.synchronize()
+    hisa.hisa_profile_enable(True)
+    try:
+        I, blk, path = hisa.hisa_select_prefill(g["q_idx"], g["w"], g["keys"], g["t0"], **sel_kw(w))
+        torch.cuda.synchronize()
+        names = set(hisa.hisa_profile_collect())
+    finally:
+        hisa.hisa_profile_enable(False)
+    assert "select_rows" in names, names
     assert parity.to_np(path).tolist() == [hisa.PATH_HISA, hisa.PATH_HISA, hisa.PATH_FLAT, hisa.PATH_DENSE]
     check_selection(w, x, I, blk, path)
     Bk = parity.to_np(blk)
@@ -548,7 +555,7 @@ def test_prefill_rows_small_blocks_mixed_paths(hisa):
     assert (np.diff(Bk[:2], axis=-1) > 0).all()  # retained blocks ascending
     In = parity.to_np(I)
     assert (np.diff(In[:3], axis=-1) > 0).all()  # ids ascending, k = 64 of each visible prefix
-    np.testing.assert_array_equal(In[3], np.broadcast_to(np.r_[np.arange(59), -np.ones(5, int)], (37, 64)))
+    np.testing.assert_array_equal(In[3], np.broadcast_to(np.r_[np.arange(63), -np.ones(1, int)], (53, 64)))
 
 
 def test_attention_masks_window0_no_sinks(hisa):

@@ -139,7 +139,11 @@ size_t take(Layout& l, size_t bytes) {
 
 // Which kernels the batched selection runs (hisa_select_prefill); the
 // workspace holds only what they use.
-constexpr int kSmallChunk = 8;  // query rows per sequence up to which a chunk takes the cached-means kernels
+// Query rows (B * L) up to which a chunk takes the cached-means kernels (one
+// query row per pair of grid rows, ~21 us for 1 to 32 rows, ~0.16 us more per
+// row beyond) rather than the one-row-per-wave selection (~60 us up to a
+// thousand rows: each wave's chain is the same length whatever the chunk).
+constexpr int kSmallRows = 192;
 
 struct PrefillPlan {
   bool small;        // short chunk: every block mean, then the cached-means selection per row
@@ -149,7 +153,7 @@ struct PrefillPlan {
 };
 PrefillPlan prefill_plan(const KDims& k, bool bf) {
   PrefillPlan p;
-  p.small = k.L <= kSmallChunk && (long long)k.B * k.L <= 65535 && hisa::cached_decode_ok(k, bf);
+  p.small = (long long)k.B * k.L <= kSmallRows && hisa::cached_decode_ok(k, bf);
   if (p.small) {
     p.rows = p.coarse_fine = p.flat_scan = false;
     return p;

@@ -2020,18 +2020,6 @@ struct TopkRegSmem {
   int info[8];
 };
 
-// Sum over the block of one int per thread (every thread gets it).
-__device__ __forceinline__ int block_sum_i(int v, TopkRegSmem& sm) {
-  v = wave_sum_i(v);
-  if (lane_id() == 0) sm.wsum[wave_id()] = (uint32_t)v;
-  __syncthreads();
-  int all = 0;
-#pragma unroll
-  for (int u = 0; u < kTkNT / 64; ++u) all += (int)sm.wsum[u];
-  __syncthreads();
-  return all;
-}
-
 // Rows of 8193..32768 scores, one workgroup per row, thread t holding the 32
 // consecutive scores 32t .. 32t+31 in registers.
 //  1. range [lo, hi] of the real scores (masked ones are -1e30) and their count;
@@ -2183,38 +2171,51 @@ __global__ __launch_bounds__(kTkNT) void k_topk_rows_reg(KDims d, const float* _
       __syncthreads();
     };
     if (hi > lo) {
-      // 3a. bracket the k-th score with one sample per thread
+      // 3a. bracket the k-th score with one sample per thread: one scan of the
+      // sample histogram gives the sample count (its total) and the bins of
+      // both ends of the bracket; the histogram is cleared as it is read.
       float scale;
       bins_of(lo, hi, scale);
       const float x0 = v[0];
-      const bool sreal = x0 > -1e29f;
-      if (sreal) atomicAdd(&sm.hist[min(kTkBins - 1, (int)((x0 - lo) * scale))], 1u);
-      const int ns = block_sum_i(sreal ? 1 : 0, sm);  // also orders the adds before the scan
+      if (x0 > -1e29f) atomicAdd(&sm.hist[min(kTkBins - 1, (int)((x0 - lo) * scale))], 1u);
+      __syncthreads();
+      const int b0 = kTkBins - 1 - 2 * tid, b1 = kTkBins - 2 - 2 * tid;
+      const uint32_t h0 = sm.hist[b0], h1 = sm.hist[b1];
+      sm.hist[b0] = 0;
+      sm.hist[b1] = 0;
+      uint32_t ns_u;
+      const uint32_t above = block_excl_scan<kTkNT>(h0 + h1, sm.wsum, &ns_u);
+      const int ns = (int)ns_u;
       const float target = (float)k * (float)ns / (float)nreal;
       const float margin = 3.f * sqrtf(fmaxf(target, 1.f)) + 4.f;
       const int r_hi = max(1, (int)(target - margin)), r_lo = min(ns, (int)ceilf(target + margin));
-      if (ns > 0 && r_hi <= r_lo) {
-        int Tt, at, it, Tb, ab, ib;
-        find_bin(r_hi, Tt, at, it);
-        find_bin(r_lo, Tb, ab, ib);
+      if (ns > 0 && r_hi <= r_lo) {  // uniform
+        // the bin holding the r-th sample from the top, for r = r_hi and r_lo
+        auto locate = [&](int r, int slot) {
+          if (above < (uint32_t)r && above + h0 + h1 >= (uint32_t)r) sm.info[slot] = above + h0 >= (uint32_t)r ? b0 : b1;
+        };
+        locate(r_hi, 0);
+        locate(r_lo, 1);
+        __syncthreads();
+        const int Tt = sm.info[0], Tb = sm.info[1];
         const float clo = Tb == 0 ? lo : fmaxf(lo, lo + (float)Tb / scale);
         const float chi = Tt == kTkBins - 1 ? hi : fminf(hi, lo + (float)(Tt + 1) / scale);
-        int n_above = 0, n_in = 0;
+        // both counts in one sum: each is at most 32768, below 2^16
+        uint32_t cnt = 0;
 #pragma unroll
         for (int q = 0; q < kTkR; ++q) {
-          n_above += v[q] > chi ? 1 : 0;
-          n_in += (v[q] >= clo && v[q] <= chi) ? 1 : 0;
+          cnt += v[q] > chi ? 1u : 0u;
+          cnt += (v[q] >= clo && v[q] <= chi) ? 0x10000u : 0u;
         }
-        n_above = block_sum_i(n_above, sm);
-        n_in = block_sum_i(n_in, sm);
+        uint32_t both;
+        block_excl_scan<kTkNT>(cnt, sm.wsum, &both);  // (its barriers also order the reads of info)
+        const int n_above = (int)(both & 0xFFFFu), n_in = (int)(both >> 16);
         if (n_above < k && n_above + n_in >= k && chi > clo) {
           blo = clo;
           bhi = chi;
           need = k - n_above;
         }
       }
-      for (int i = tid; i < kTkBins; i += kTkNT) sm.hist[i] = 0;
-      __syncthreads();
     }
     // 3b. exact histogram rounds inside [blo, bhi]
     for (int round = 0; round < 4 && !done; ++round) {

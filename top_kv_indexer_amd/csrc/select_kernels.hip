@@ -2153,14 +2153,20 @@ __global__ __launch_bounds__(kTkNT) void k_topk_rows_reg(KDims d, const float* _
     auto bins_of = [&](float rlo, float rhi, float& scale) {
       scale = (float)kTkBins / (rhi - rlo) * 0.999999f;
     };
-    // the bin holding the r-th entry from the top of hist: (bin, entries above it, entries in it)
+    // the bin holding the r-th entry from the top of hist: (bin, entries above
+    // it, entries in it); hist is left cleared (each thread clears the bins it
+    // read; the scan's barriers order that before any later add).  info[0..2]
+    // are written again only past further barriers.
     auto find_bin = [&](int r, int& T, int& above_T, int& in_T) {
-      const uint32_t h0 = sm.hist[kTkBins - 1 - 2 * tid], h1 = sm.hist[kTkBins - 2 - 2 * tid];
+      const int b0 = kTkBins - 1 - 2 * tid, b1 = kTkBins - 2 - 2 * tid;
+      const uint32_t h0 = sm.hist[b0], h1 = sm.hist[b1];
+      sm.hist[b0] = 0;
+      sm.hist[b1] = 0;
       uint32_t tot;
       const uint32_t above = block_excl_scan<kTkNT>(h0 + h1, sm.wsum, &tot);
       if (above < (uint32_t)r && above + h0 + h1 >= (uint32_t)r) {
         const bool first = above + h0 >= (uint32_t)r;
-        sm.info[0] = first ? kTkBins - 1 - 2 * tid : kTkBins - 2 - 2 * tid;
+        sm.info[0] = first ? b0 : b1;
         sm.info[1] = (int)(first ? above : above + h0);
         sm.info[2] = (int)(first ? h0 : h1);
       }
@@ -2168,7 +2174,6 @@ __global__ __launch_bounds__(kTkNT) void k_topk_rows_reg(KDims d, const float* _
       T = sm.info[0];
       above_T = sm.info[1];
       in_T = sm.info[2];
-      __syncthreads();
     };
     if (hi > lo) {
       // 3a. bracket the k-th score with one sample per thread: one scan of the
@@ -2232,10 +2237,7 @@ __global__ __launch_bounds__(kTkNT) void k_topk_rows_reg(KDims d, const float* _
       auto bin_of = [&](float x) {
         return (x < blo || x > bhi) ? -1 : min(kTkBins - 1, (int)((x - blo) * scale));
       };
-      if (round > 0) {
-        for (int i = tid; i < kTkBins; i += kTkNT) sm.hist[i] = 0;
-        __syncthreads();
-      }
+      // (hist is clear: set so before the rounds, and by find_bin after each)
 #pragma unroll
       for (int q = 0; q < kTkR; ++q) {
         const int bn = bin_of(v[q]);

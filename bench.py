@@ -134,7 +134,9 @@ def algorithmic(w, x, unique_kv_rows=None, flat_seqs=None):
         "flat_scores": {"bytes": sum(Np[b] for b in flat) * w.D_i * bf + len(flat) * L * (w.H_i * w.D_i * bf + w.H_i * 4),
                         "flops": sum(sum(min(Np[b], (int(x["t0"][b]) + j + 1) // w.ratio) for j in range(L))
                                      for b in flat) * w.H_i * w.D_i * 2},
-        "topk_rows": {"bytes": len(flat) * L * kI * 4, "flops": 0},
+        # the row top-k reads each flat row's scores (an intermediate of the
+        # step, but this kernel's input) and writes its ids
+        "topk_rows": {"bytes": sum(Np[b] for b in flat) * L * 4 + len(flat) * L * kI * 4, "flops": 0},
         # the cached decode reads each sequence's block means and its C candidate rows
         "cached_decode": {"bytes": sum(nbb * w.D_i * 4 + min(C, n) * w.D_i * bf for nbb, n in zip(nb, Np))
                           + idx_q + rows * kI * 4,

@@ -790,6 +790,182 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_fa(KDims d, c
   }
 }
 
+// Few query rows (decode, short verify chunks; K = V rows 512 or 576 wide):
+// one workgroup per (64-entry split of the row list, query row, 16 heads),
+// four waves, the whole split in one pass.  Wave 0 resolves the split's 64
+// entries (pooled ids from I, then the local window) into row codes; wave w
+// brings rows 16w .. 16w+15 global->LDS and scores them against the 16 heads
+// (S = K q^T, 16x16x32 MFMA, lane (g, c) holding rows 16w + 4g + i of head c);
+// the softmax takes the exact maximum over the split's rows (one exchange of
+// per-wave maxima and sums through LDS); P^T goes to LDS in the value MFMA's k
+// order; O^T += V^T P^T reads V^T with the transposing LDS read, wave w owning
+// value tiles w, w+4, ...  The partial (m, l in the log2 domain, unnormalised
+// O) goes to the merge.  Rows and their 16-byte chunks are laid out as in the
+// other attention kernels (the chunk swizzle by row; 576-wide rows keep their
+// last eight chunks in a swizzled tail of a 1280-byte pitch).
+constexpr int kSplitRows = 64;
+
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void k_attn_split64(KDims d, int splits, const uint16_t* __restrict__ q,
+                                                      const uint16_t* __restrict__ local_kv,
+                                                      const uint16_t* __restrict__ pooled_kv,
+                                                      const int* __restrict__ I, const int* __restrict__ t0,
+                                                      float* __restrict__ part) {
+  static_assert(DK == DV && (DK == 512 || DK == 576), "shape");
+  constexpr int KPD = (DK * 2 + 255) / 256 * 128;  // LDS row pitch (elements)
+  constexpr int NS = DK / 32;                      // MFMA k-steps of S
+  constexpr int NDTW = DV / 16 / 4;                // value tiles per wave
+  constexpr int PP = kSplitRows + 8;               // P^T pitch (elements) per head
+  __shared__ __align__(1024) uint16_t kv[kSplitRows * KPD];
+  __shared__ __align__(16) uint16_t s_p[16 * PP];
+  __shared__ float s_red[2][4][16];
+  __shared__ int s_code[kSplitRows];
+  __shared__ uint32_t s_live[2];
+  args_now(d, splits, q, local_kv, pooled_kv, I, t0, part);
+  const int split = blockIdx.x, row = blockIdx.y, hbase = blockIdx.z * 16;
+  const int b = row / d.L, j = row - b * d.L;
+  const int lane = lane_id(), wv = wave_id(), g = lane >> 4, c = lane & 15;
+  // this row's 16 heads of q (the B operand of S), requested first
+  bf16x8 qf[NS];
+  {
+    const uint16_t* qrow = q + ((size_t)row * d.H + hbase + c) * DK + g * 8;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qf[s] = *(const bf16x8*)(qrow + s * 32);
+  }
+  const int T0 = t0[b];
+  const RowPlan rp = row_plan(d, T0, ring_slot0(d, b, T0), j);
+  // a row every live split may read (entries that take no part point at it)
+  const int dummy = rp.n_loc > 0 ? -1 - rp.lbase : 0;
+  if (wv == 0) {
+    const int e = split * kSplitRows + lane;
+    int code = dummy;
+    bool present = false;
+    if (rp.ok) {
+      if (e < d.kI) {
+        const int id = I ? I[(size_t)row * d.kI + e] : e;
+        if (id >= 0 && id < rp.V) {
+          present = true;
+          code = id;
+        }
+      } else if (e - d.kI < d.window && e - d.kI < rp.n_loc) {
+        present = true;
+        code = -1 - local_row(d, rp, e - d.kI);
+      }
+    }
+    s_code[lane] = code;
+    const uint64_t m = __ballot(present);
+    if (lane == 0) {
+      s_live[0] = (uint32_t)m;
+      s_live[1] = (uint32_t)(m >> 32);
+    }
+  }
+  lds_sync();  // the codes (q stays in flight)
+  const uint64_t live = ((uint64_t)s_live[1] << 32) | s_live[0];
+  const bool any = live != 0;
+  const uint32_t kv_lds = lds_addr(kv);
+  const int kvb10 = (int)((kv_lds >> 10) & 15);
+  auto sw = [kvb10](int r) {
+    const int t = kvb10 + (r & 15);
+    const int hash = KPD * 2 == 1024 ? ((t >> 2) ^ (t >> 3)) & 1 : 0;
+    return (((r & 7) << 1) | ((r >> 3) & 1)) ^ hash;
+  };
+  f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (any) {
+    // wave w brings rows 16w .. 16w+15 straight into LDS
+    const uint16_t* pooled_b = pooled_kv + (size_t)b * d.Np_cap * DK;
+    const uint16_t* local_b = local_kv + (size_t)b * d.Wl_cap * DK;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int r = 16 * wv + u;
+      const int cd = s_code[r];
+      const uint16_t* src = cd >= 0 ? pooled_b + (size_t)cd * DK : local_b + (size_t)(-1 - cd) * DK;
+      const int x = lane ^ sw(r);
+      const uint32_t dst = kv_lds + (uint32_t)(r * KPD * 2);
+      g2lds16(src + x * 8, dst);
+      if (DK > 512 && x < DK / 8 - 64) g2lds16(src + 512 + x * 8, dst + 1024);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0: this wave's rows are in LDS
+    // (each wave scores only the rows it brought)
+    const int rr = 16 * wv + c, rsw = sw(rr);
+    auto load_k = [&](int s) {
+      const int ch = 4 * s + g;
+      if (ch >= 64) return *(const bf16x8*)(kv + rr * KPD + tail_pos(ch, rsw) * 8);
+      return *(const bf16x8*)(kv + rr * KPD + (((4 * (s & 3) + g) ^ rsw) * 8) + (s >> 2) * 128);
+    };
+    bf16x8 ka[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) ka[s] = load_k(s);
+    f32x4 sa[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) sa[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) sa[s & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s], qf[s], sa[s & 3], 0, 0, 0);
+    sc = (sa[0] + sa[1]) + (sa[2] + sa[3]);
+  }
+  // softmax of head c over the split's rows, the exact maximum
+  const float scale = d.attn_scale_log2;
+  float x[4], mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * wv + 4 * g + i;
+    x[i] = ((live >> r) & 1) ? sc[i] * scale : -INFINITY;
+    mx = fmaxf(mx, x[i]);
+  }
+  mx = max_rows(mx);
+  if (g == 0) s_red[0][wv][c] = mx;
+  __syncthreads();
+  const float m = fmaxf(fmaxf(s_red[0][0][c], s_red[0][1][c]), fmaxf(s_red[0][2][c], s_red[0][3][c]));
+  const float m_sub = m == -INFINITY ? 0.f : m;
+  float p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - m_sub);
+  const float ps = sum_rows((p[0] + p[1]) + (p[2] + p[3]));
+  if (g == 0) s_red[1][wv][c] = ps;
+  // P^T operand of k-step kk: entry 8g + e of head c is row 32kk + 16(e/4) +
+  // 4g + e%4, i.e. waves 2kk and 2kk+1 give four entries each
+  uint2 pk;
+  pk.x = pack_bf16x2(p[0], p[1]);
+  pk.y = pack_bf16x2(p[2], p[3]);
+  *(uint2*)&s_p[c * PP + (wv >> 1) * 32 + 8 * g + 4 * (wv & 1)] = pk;
+  __syncthreads();  // every wave's P, sums, and rows (each wave waited for its own)
+  const float l = (s_red[1][0][c] + s_red[1][1][c]) + (s_red[1][2][c] + s_red[1][3][c]);
+  f32x4 acc[NDTW];
+#pragma unroll
+  for (int n = 0; n < NDTW; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (any) {
+    // transposing V reads: lane (g, c) takes rows 4g + c/4 (+16) and columns
+    // 4(c%4) .. +3 of a 16-column value tile
+    const int vrow = 4 * g + (c >> 2), vsw = sw(vrow);
+    auto vaddr = [&](int dt) {
+      const int ch = 2 * dt + ((c & 3) >> 1);
+      if (ch >= 64) return vrow * KPD + tail_pos(ch, vsw) * 8 + 4 * (c & 1);
+      return vrow * KPD + (((2 * (dt & 7) + ((c & 3) >> 1)) ^ vsw) * 8) + (dt >> 3) * 128 + 4 * (c & 1);
+    };
+    const bf16x8 pb0 = *(const bf16x8*)&s_p[c * PP + 8 * g];
+    const bf16x8 pb1 = *(const bf16x8*)&s_p[c * PP + 32 + 8 * g];
+#pragma unroll
+    for (int n = 0; n < NDTW; ++n) {
+      const int off = vaddr(wv + 4 * n);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const uint16_t* base = kv + kk * 32 * KPD + off;
+        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)base);
+        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 16 * KPD));
+        const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, kk ? pb1 : pb0, acc[n], 0, 0, 0);
+      }
+    }
+  }
+  // the split's partial: O^T tile (16dt + 4g + i, head c) per lane, then (m, l)
+  float* pr = part + (((size_t)split * d.B * d.L + row) * d.H + hbase + c) * (DV + 2);
+#pragma unroll
+  for (int n = 0; n < NDTW; ++n) *(f32x4*)(pr + 16 * (wv + 4 * n) + 4 * g) = acc[n];
+  if (wv == 0 && g == 0) {
+    pr[DV] = m;
+    pr[DV + 1] = l;
+  }
+}
+
 // Merge of split partials (m and l in the log2 domain), sink included.  One
 // workgroup per (query row, head, 128 output columns); the first wave turns
 // the splits' (m, l) into normalised weights, then every thread sums its
@@ -951,6 +1127,12 @@ __global__ __launch_bounds__(256) void k_attn_valu(KDims d, const T* __restrict_
 template <int DK, int DV>
 hipError_t launch_mfma(const KDims& d, const void* q, const void* local_kv, const void* pooled_kv, const int* I,
                        const float* sinks, const int* t0, void* out, float* partial, int splits, hipStream_t st) {
+  if (attn_split64_ok(d)) {
+    const dim3 grid(splits, d.B * d.L, d.H / 16);
+    hipLaunchKernelGGL((k_attn_split64<DK, DV>), grid, dim3(256), 0, st, d, splits, (const uint16_t*)q,
+                       (const uint16_t*)local_kv, (const uint16_t*)pooled_kv, I, t0, partial);
+    return hipGetLastError();
+  }
   if (attn_small_groups(d)) {
     const dim3 grid(splits, d.B * d.L, d.H / 16);
     hipLaunchKernelGGL((k_attn_mfma<DK, DV, 1>), grid, dim3(128), 0, st, d, splits, (const uint16_t*)q,
@@ -990,8 +1172,17 @@ bool attn_generic_ok(const KDims& d) {
 // otherwise 64 heads per workgroup, so each gathered row feeds 4x more heads.
 bool attn_small_groups(const KDims& d) { return (long long)d.B * d.L * (d.H / 64) <= 8; }
 
+// A handful of query rows with a row list of 2 .. kMaxSplits 64-entry splits:
+// one workgroup per split (k_attn_split64, MFMA shapes only; its partials
+// always go through the merge).
+bool attn_split64_ok(const KDims& d) {
+  const long long n_geo = (long long)d.kI + d.window;
+  return attn_small_groups(d) && n_geo > kSplitRows && n_geo <= (long long)kSplitRows * kMaxSplits;
+}
+
 int attn_splits(const KDims& d, bool bf16) {
   if (!attn_mfma_ok(d, bf16)) return 1;
+  if (attn_split64_ok(d)) return std::max(1, (d.kI + d.window + kSplitRows - 1) / kSplitRows);
   const long long work = (long long)d.B * d.L * (d.H / (attn_small_groups(d) ? 16 : 64));
   const long long n_max = (long long)d.window + d.kI;
   // at least two 32-row tiles per split, so that fetching overlaps compute

@@ -103,6 +103,7 @@ int attn_splits(const KDims& d, bool bf16);
 bool attn_mfma_ok(const KDims& d, bool bf16);
 bool attn_generic_ok(const KDims& d);
 bool attn_small_groups(const KDims& d);
+bool attn_split64_ok(const KDims& d);  // (with attn_mfma_ok) few rows: one workgroup per 64-entry split
 size_t attn_partial_bytes(const KDims& d, int splits);
 hipError_t launch_attention(const KDims& d, bool bf16, const void* q, const void* local_kv,
                             const void* pooled_kv, const int* I, const float* sinks,

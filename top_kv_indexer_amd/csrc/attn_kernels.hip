@@ -1172,12 +1172,16 @@ bool attn_generic_ok(const KDims& d) {
 // otherwise 64 heads per workgroup, so each gathered row feeds 4x more heads.
 bool attn_small_groups(const KDims& d) { return (long long)d.B * d.L * (d.H / 64) <= 8; }
 
-// A handful of query rows with a row list of 2 .. kMaxSplits 64-entry splits:
-// one workgroup per split (k_attn_split64, MFMA shapes only; its partials
-// always go through the merge).
+// Up to twelve query rows' worth of 64-head groups with a row list of 2 ..
+// kMaxSplits 64-entry splits: one workgroup per split (k_attn_split64, MFMA
+// shapes only; its partials always go through the merge).  Measured against
+// the split kernels at 64 heads x 640 entries: faster at 9 and 12 rows
+// (17.7 / 19.3 against 18.9 / 20.1 us), slower from 16 rows on (26.3 against
+// 23.0; 32 rows of a batch: 31.0 against 19.0), where its one workgroup per
+// 64 entries and 16 heads turns into more partials than the merge pays back.
 bool attn_split64_ok(const KDims& d) {
   const long long n_geo = (long long)d.kI + d.window;
-  return attn_small_groups(d) && n_geo > kSplitRows && n_geo <= (long long)kSplitRows * kMaxSplits;
+  return (long long)d.B * d.L * (d.H / 64) <= 12 && n_geo > kSplitRows && n_geo <= (long long)kSplitRows * kMaxSplits;
 }
 
 int attn_splits(const KDims& d, bool bf16) {

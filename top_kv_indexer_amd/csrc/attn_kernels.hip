@@ -14,6 +14,7 @@
 // gfx950 transposing LDS read and P^T straight from the S^T registers.  Split
 // partials (m, l, O) are merged by a second kernel.
 #include <algorithm>
+#include <type_traits>
 
 #include "hisa_device.h"
 
@@ -825,24 +826,26 @@ __global__ __launch_bounds__(256) void k_attn_split64(KDims d, int splits, const
   const int split = blockIdx.x, row = blockIdx.y, hbase = blockIdx.z * 16;
   const int b = row / d.L, j = row - b * d.L;
   const int lane = lane_id(), wv = wave_id(), g = lane >> 4, c = lane & 15;
-  // this row's 16 heads of q (the B operand of S), requested first
+  // this row's 16 heads of q (the B operand of S) and wave 0's entries of
+  // the index row, requested before t0 (nothing of theirs depends on it)
   bf16x8 qf[NS];
   {
     const uint16_t* qrow = q + ((size_t)row * d.H + hbase + c) * DK + g * 8;
 #pragma unroll
     for (int s = 0; s < NS; ++s) qf[s] = *(const bf16x8*)(qrow + s * 32);
   }
+  const int e = split * kSplitRows + lane;
+  int id = -1;
+  if (wv == 0 && e < d.kI) id = I ? I[(size_t)row * d.kI + e] : e;
   const int T0 = t0[b];
   const RowPlan rp = row_plan(d, T0, ring_slot0(d, b, T0), j);
   // a row every live split may read (entries that take no part point at it)
   const int dummy = rp.n_loc > 0 ? -1 - rp.lbase : 0;
   if (wv == 0) {
-    const int e = split * kSplitRows + lane;
     int code = dummy;
     bool present = false;
     if (rp.ok) {
       if (e < d.kI) {
-        const int id = I ? I[(size_t)row * d.kI + e] : e;
         if (id >= 0 && id < rp.V) {
           present = true;
           code = id;
@@ -969,10 +972,12 @@ __global__ __launch_bounds__(256) void k_attn_split64(KDims d, int splits, const
 // Merge of split partials (m and l in the log2 domain), sink included.  One
 // workgroup per (query row, head, 128 output columns); the first wave turns
 // the splits' (m, l) into normalised weights, then every thread sums its
-// column over the splits.
+// column over the splits.  The first PRE splits' values are requested with
+// (m, l), the rest after the weights (PRE is picked from the split count: a
+// deeper prefetch than needed costs predicated loads in every thread).
 constexpr int kMaxSplits = 64;
 
-template <typename T>
+template <typename T, int PRE>
 __global__ __launch_bounds__(128) void k_attn_merge(KDims d, int splits, const float* __restrict__ part,
                                                     const float* __restrict__ sinks, T* __restrict__ out) {
   __shared__ float s_w[kMaxSplits];
@@ -982,7 +987,7 @@ __global__ __launch_bounds__(128) void k_attn_merge(KDims d, int splits, const f
   const size_t stride = (size_t)d.B * d.L * d.H * (d.Dv + 2);
   const float* p0 = part + ((size_t)row * d.H + h) * (d.Dv + 2);
   // the column's partials are requested together with (m, l)
-  constexpr int kPre = 24;
+  constexpr int kPre = PRE;
   const int ec = min(e, d.Dv - 1);
   float pre[kPre];
 #pragma unroll
@@ -1206,12 +1211,18 @@ size_t attn_partial_bytes(const KDims& d, int splits) {
 
 hipError_t launch_attention_merge(const KDims& d, bool bf16, const float* partial, const float* sinks, void* out,
                                   int splits, hipStream_t st) {
-  if (bf16)
-    hipLaunchKernelGGL(k_attn_merge<uint16_t>, dim3(d.B * d.L, d.H, (d.Dv + 127) / 128), dim3(128), 0, st, d, splits,
-                       partial, sinks, (uint16_t*)out);
-  else
-    hipLaunchKernelGGL(k_attn_merge<float>, dim3(d.B * d.L, d.H, (d.Dv + 127) / 128), dim3(128), 0, st, d, splits,
-                       partial, sinks, (float*)out);
+  const dim3 grid(d.B * d.L, d.H, (d.Dv + 127) / 128);
+  auto go = [&](auto pre) {
+    constexpr int P = decltype(pre)::value;
+    if (bf16)
+      hipLaunchKernelGGL((k_attn_merge<uint16_t, P>), grid, dim3(128), 0, st, d, splits, partial, sinks,
+                         (uint16_t*)out);
+    else
+      hipLaunchKernelGGL((k_attn_merge<float, P>), grid, dim3(128), 0, st, d, splits, partial, sinks, (float*)out);
+  };
+  if (splits <= 8) go(std::integral_constant<int, 8>{});
+  else if (splits <= 24) go(std::integral_constant<int, 24>{});
+  else go(std::integral_constant<int, 32>{});
   return hipGetLastError();
 }
 

@@ -970,9 +970,10 @@ __global__ __launch_bounds__(256) void k_attn_split64(KDims d, int splits, const
 }
 
 // Merge of split partials (m and l in the log2 domain), sink included.  One
-// workgroup per (query row, head, 128 output columns); the first wave turns
-// the splits' (m, l) into normalised weights, then every thread sums its
-// column over the splits.  The first PRE splits' values are requested with
+// workgroup per (query row, head, 256 output columns, Dv even); the first
+// wave turns the splits' (m, l) into normalised weights, then every thread
+// sums its two columns over the splits (8-byte loads: partial rows are
+// Dv + 2 floats apart).  The first PRE splits' values are requested with
 // (m, l), the rest after the weights (PRE is picked from the split count: a
 // deeper prefetch than needed costs predicated loads in every thread).
 constexpr int kMaxSplits = 64;
@@ -983,15 +984,15 @@ __global__ __launch_bounds__(128) void k_attn_merge(KDims d, int splits, const f
   __shared__ float s_w[kMaxSplits];
   args_now(d, splits, part, sinks, out);
   const int row = blockIdx.x, h = blockIdx.y;
-  const int e = blockIdx.z * 128 + threadIdx.x;
+  const int e = blockIdx.z * 256 + 2 * threadIdx.x;
   const size_t stride = (size_t)d.B * d.L * d.H * (d.Dv + 2);
   const float* p0 = part + ((size_t)row * d.H + h) * (d.Dv + 2);
-  // the column's partials are requested together with (m, l)
+  // the columns' partials are requested together with (m, l)
   constexpr int kPre = PRE;
-  const int ec = min(e, d.Dv - 1);
-  float pre[kPre];
+  const int ec = min(e, d.Dv - 2);
+  float2 pre[kPre];
 #pragma unroll
-  for (int s = 0; s < kPre; ++s) pre[s] = s < splits ? p0[s * stride + ec] : 0.f;
+  for (int s = 0; s < kPre; ++s) pre[s] = s < splits ? *(const float2*)(p0 + s * stride + ec) : float2{0.f, 0.f};
   if (threadIdx.x < 64) {
     const int s = threadIdx.x;
     const float m = s < splits ? p0[s * stride + d.Dv] : -INFINITY;
@@ -1007,12 +1008,21 @@ __global__ __launch_bounds__(128) void k_attn_merge(KDims d, int splits, const f
   }
   __syncthreads();
   if (e >= d.Dv) return;
-  float o = 0.f;
+  float ox = 0.f, oy = 0.f;
 #pragma unroll
   for (int s = 0; s < kPre; ++s)
-    if (s < splits) o += pre[s] * s_w[s];
-  for (int s = kPre; s < splits; ++s) o += p0[s * stride + e] * s_w[s];
-  stf(out + ((size_t)row * d.H + h) * d.Dv + e, o);
+    if (s < splits) {
+      ox += pre[s].x * s_w[s];
+      oy += pre[s].y * s_w[s];
+    }
+  for (int s = kPre; s < splits; ++s) {
+    const float2 v = *(const float2*)(p0 + s * stride + e);
+    ox += v.x * s_w[s];
+    oy += v.y * s_w[s];
+  }
+  T* op = out + ((size_t)row * d.H + h) * d.Dv + e;
+  stf(op, ox);
+  stf(op + 1, oy);
 }
 
 // Any shape / dtype: one workgroup per (query row, head), two-pass softmax.
@@ -1211,7 +1221,8 @@ size_t attn_partial_bytes(const KDims& d, int splits) {
 
 hipError_t launch_attention_merge(const KDims& d, bool bf16, const float* partial, const float* sinks, void* out,
                                   int splits, hipStream_t st) {
-  const dim3 grid(d.B * d.L, d.H, (d.Dv + 127) / 128);
+  if (d.Dv & 1) return hipErrorInvalidValue;  // (split attention only for 512- or 576-wide values)
+  const dim3 grid(d.B * d.L, d.H, (d.Dv + 255) / 256);
   auto go = [&](auto pre) {
     constexpr int P = decltype(pre)::value;
     if (bf16)

@@ -54,13 +54,13 @@ def test_workspace_sizes(lib):
         32 * 33 * 64 + 32 * 32768 * 4 + 32 * 512 * 4)
     assert hisa.workspace_bytes(hisa.OP_FLAT_TOPK, dims(L=4, Np_cap=1000)) == ((4 * 1000 * 4 + 255) // 256) * 256
     # single-row attention splits the 640 rows into 10 parts of 64
-    assert hisa.workspace_bytes(hisa.OP_ATTENTION, d) == 10 * 64 * 514 * 4
+    assert hisa.workspace_bytes(hisa.OP_ATTENTION, d) == 10 * 64 * (2 * 512 + 8)
     # decode step: sync words (error word, then per sequence one line each of
     # "seen" and threshold, 16 split descriptors of 8 bytes: 320 bytes,
     # rounded to 512),
     # the decode selection's workspace, and the partials of 16 pooled + 2 local
     # splits of 64 heads (more than the attention call's 10)
-    assert hisa.workspace_bytes(hisa.OP_DECODE_STEP, d) == 512 + (1280 + 16384 * 4 + 256 * 4) + 18 * 64 * 514 * 4
+    assert hisa.workspace_bytes(hisa.OP_DECODE_STEP, d) == 512 + (1280 + 16384 * 4 + 256 * 4) + 18 * 64 * (2 * 512 + 8)
     # many rows: no split, no workspace
     assert hisa.workspace_bytes(hisa.OP_ATTENTION, dims(L=2048, Wl_cap=2175)) == 0
     # batched selection, sized by the kernels that run: one query row per wave

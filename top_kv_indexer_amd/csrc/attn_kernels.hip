@@ -465,16 +465,14 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
         }
       }
     } else {
-      float* pr = part + (((size_t)split * d.B * d.L + row) * d.H + h) * (DV + 2);
+      const size_t prow = ((size_t)split * d.B * d.L + row) * d.H + h;
+      const float inv = lh > 0.f ? 1.f / lh : 0.f;
 #pragma unroll
       for (int n = 0; n < NDT; ++n) {
         const int dt = wv + NW * n;
-        if (NDT * NW == NDT_ALL || dt < NDT_ALL) *(f32x4*)(pr + dt * 16 + 4 * g) = acc[n][ht];
+        if (NDT * NW == NDT_ALL || dt < NDT_ALL) store_part4(part, prow, DV, dt * 16 + 4 * g, acc[n][ht], inv);
       }
-      if (wv == 0 && g == 0) {
-        pr[DV] = mh;
-        pr[DV + 1] = lh;
-      }
+      if (wv == 0 && g == 0) store_part_ml(part, prow, DV, mh, lh);
     }
   }
   if (splits == 1) {
@@ -800,8 +798,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_fa(KDims d, c
 // the softmax takes the exact maximum over the split's rows (one exchange of
 // per-wave maxima and sums through LDS); P^T goes to LDS in the value MFMA's k
 // order; O^T += V^T P^T reads V^T with the transposing LDS read, wave w owning
-// value tiles w, w+4, ...  The partial (m, l in the log2 domain, unnormalised
-// O) goes to the merge.  Rows and their 16-byte chunks are laid out as in the
+// value tiles w, w+4, ...  The partial (O / l in bf16, m and l in the log2
+// domain) goes to the merge.  Rows and their 16-byte chunks are laid out as in the
 // other attention kernels (the chunk swizzle by row; 576-wide rows keep their
 // last eight chunks in a swizzled tail of a 1280-byte pitch).
 constexpr int kSplitRows = 64;
@@ -959,23 +957,22 @@ __global__ __launch_bounds__(256) void k_attn_split64(KDims d, int splits, const
       }
     }
   }
-  // the split's partial: O^T tile (16dt + 4g + i, head c) per lane, then (m, l)
-  float* pr = part + (((size_t)split * d.B * d.L + row) * d.H + hbase + c) * (DV + 2);
+  // the split's partial: O^T tile (16dt + 4g + i, head c) per lane over l, then (m, l)
+  const size_t prow = ((size_t)split * d.B * d.L + row) * d.H + hbase + c;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-  for (int n = 0; n < NDTW; ++n) *(f32x4*)(pr + 16 * (wv + 4 * n) + 4 * g) = acc[n];
-  if (wv == 0 && g == 0) {
-    pr[DV] = m;
-    pr[DV + 1] = l;
-  }
+  for (int n = 0; n < NDTW; ++n) store_part4(part, prow, DV, 16 * (wv + 4 * n) + 4 * g, acc[n], inv);
+  if (wv == 0 && g == 0) store_part_ml(part, prow, DV, m, l);
 }
 
-// Merge of split partials (m and l in the log2 domain), sink included.  One
-// workgroup per (query row, head, 256 output columns, Dv even); the first
-// wave turns the splits' (m, l) into normalised weights, then every thread
-// sums its two columns over the splits (8-byte loads: partial rows are
-// Dv + 2 floats apart).  The first PRE splits' values are requested with
-// (m, l), the rest after the weights (PRE is picked from the split count: a
-// deeper prefetch than needed costs predicated loads in every thread).
+// Merge of split partials (part_row_bytes: O / l in bf16, then m and l in the
+// log2 domain), sink included.  One workgroup per (query row, head, 256
+// output columns, Dv even); the first wave turns the splits' (m, l) into
+// weights exp2(m - M) l / (sum of them and the sink's), then every thread sums
+// its two columns over the splits (one 4-byte load per split).  The first PRE
+// splits' values are requested with (m, l), the rest after the weights (PRE
+// is picked from the split count: a deeper prefetch than needed costs
+// predicated loads in every thread).
 constexpr int kMaxSplits = 64;
 
 template <typename T, int PRE>
@@ -985,23 +982,25 @@ __global__ __launch_bounds__(128) void k_attn_merge(KDims d, int splits, const f
   args_now(d, splits, part, sinks, out);
   const int row = blockIdx.x, h = blockIdx.y;
   const int e = blockIdx.z * 256 + 2 * threadIdx.x;
-  const size_t stride = (size_t)d.B * d.L * d.H * (d.Dv + 2);
-  const float* p0 = part + ((size_t)row * d.H + h) * (d.Dv + 2);
+  const size_t rb = part_row_bytes(d.Dv);
+  const size_t stride = (size_t)d.B * d.L * d.H * rb;  // bytes between splits
+  const char* p0 = (const char*)part + ((size_t)row * d.H + h) * rb;
   // the columns' partials are requested together with (m, l)
   constexpr int kPre = PRE;
   const int ec = min(e, d.Dv - 2);
-  float2 pre[kPre];
+  uint32_t pre[kPre];
 #pragma unroll
-  for (int s = 0; s < kPre; ++s) pre[s] = s < splits ? *(const float2*)(p0 + s * stride + ec) : float2{0.f, 0.f};
+  for (int s = 0; s < kPre; ++s) pre[s] = s < splits ? *(const uint32_t*)(p0 + s * stride + 2 * ec) : 0u;
   if (threadIdx.x < 64) {
     const int s = threadIdx.x;
-    const float m = s < splits ? p0[s * stride + d.Dv] : -INFINITY;
-    const float l = s < splits ? p0[s * stride + d.Dv + 1] : 0.f;
+    const float* ml = (const float*)(p0 + s * stride + 2 * (size_t)d.Dv);
+    const float m = s < splits ? ml[0] : -INFINITY;
+    const float l = s < splits ? ml[1] : 0.f;
     const float sink2 = sinks ? sinks[h] * kLog2e : -INFINITY;
     float mf = wave_max(m);
     mf = fmaxf(mf, sink2);
-    const float wgt = (mf == -INFINITY || m == -INFINITY) ? 0.f : exp2f(m - mf);
-    float lf = wave_sum(l * wgt);
+    const float wgt = (mf == -INFINITY || m == -INFINITY) ? 0.f : exp2f(m - mf) * l;
+    float lf = wave_sum(wgt);
     if (sinks && mf != -INFINITY) lf += exp2f(sink2 - mf);
     const float inv = lf > 0.f ? 1.f / lf : 0.f;
     s_w[s] = wgt * inv;
@@ -1012,13 +1011,13 @@ __global__ __launch_bounds__(128) void k_attn_merge(KDims d, int splits, const f
 #pragma unroll
   for (int s = 0; s < kPre; ++s)
     if (s < splits) {
-      ox += pre[s].x * s_w[s];
-      oy += pre[s].y * s_w[s];
+      ox += bf_lo(pre[s]) * s_w[s];
+      oy += bf_hi(pre[s]) * s_w[s];
     }
   for (int s = kPre; s < splits; ++s) {
-    const float2 v = *(const float2*)(p0 + s * stride + e);
-    ox += v.x * s_w[s];
-    oy += v.y * s_w[s];
+    const uint32_t v = *(const uint32_t*)(p0 + s * stride + 2 * e);
+    ox += bf_lo(v) * s_w[s];
+    oy += bf_hi(v) * s_w[s];
   }
   T* op = out + ((size_t)row * d.H + h) * d.Dv + e;
   stf(op, ox);
@@ -1216,7 +1215,7 @@ int attn_splits(const KDims& d, bool bf16) {
 
 size_t attn_partial_bytes(const KDims& d, int splits) {
   if (splits <= 1) return 0;
-  return (size_t)splits * d.B * d.L * d.H * (d.Dv + 2) * sizeof(float);
+  return (size_t)splits * d.B * d.L * d.H * part_row_bytes(d.Dv);
 }
 
 hipError_t launch_attention_merge(const KDims& d, bool bf16, const float* partial, const float* sinks, void* out,

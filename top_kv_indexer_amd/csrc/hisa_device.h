@@ -62,6 +62,23 @@ __device__ __forceinline__ void g2lds16(const void* gsrc, uint32_t lds_base) {
 
 // Two floats to a packed bf16 pair (low half = lo), round to nearest even, in
 // one gfx950 conversion instruction.
+// The low / high bf16 of a packed pair, as floats.
+__device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+// One split partial row (see part_row_bytes): the four normalised output
+// values of columns col .. col+3 (o times inv = 1 / l), and (m, l).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi);
+__device__ __forceinline__ void store_part4(void* part, size_t prow, int Dv, int col, f32x4 o, float inv) {
+  uint2 v;
+  v.x = pack_bf16x2(o[0] * inv, o[1] * inv);
+  v.y = pack_bf16x2(o[2] * inv, o[3] * inv);
+  *(uint2*)((char*)part + prow * part_row_bytes(Dv) + 2 * (size_t)col) = v;
+}
+__device__ __forceinline__ void store_part_ml(void* part, size_t prow, int Dv, float m, float l) {
+  float* ml = (float*)((char*)part + prow * part_row_bytes(Dv) + 2 * (size_t)Dv);
+  ml[0] = m;
+  ml[1] = l;
+}
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
   typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;

@@ -98,7 +98,11 @@ hipError_t launch_zero_ints(int* p, size_t n, hipStream_t st);
 hipError_t launch_fill_dense(const KDims& d, const int* t0, int* I, int* top_blk, int* path,
                              hipStream_t st);
 
-// Attention.  splits > 1 writes partials to ws and merges them.
+// Attention.  splits > 1 writes partials to ws and merges them.  The partial
+// of one (split, query row, head): the split's output normalised by its own
+// sum (O / l) as Dv bf16 values, then m and l (f32, the log2 domain); rows
+// part_row_bytes(Dv) apart (8-byte aligned for Dv % 4 == 0).
+inline constexpr size_t part_row_bytes(int Dv) { return 2 * (size_t)Dv + 8; }
 int attn_splits(const KDims& d, bool bf16);
 bool attn_mfma_ok(const KDims& d, bool bf16);
 bool attn_generic_ok(const KDims& d);

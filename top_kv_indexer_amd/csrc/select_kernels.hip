@@ -620,8 +620,8 @@ __global__ __launch_bounds__(256) void k_decode_scan_mfma(
 //               cc is selected iff its key is > t, or == t with cc <= last.
 // A pooled split gathers and scores its rows as soon as its descriptor is
 // out, in parallel with the fine selection, and needs the threshold only
-// for its softmax.  Each split writes the split attention's partial (m, l,
-// unnormalised O) with plain stores; the split attention's merge kernel runs
+// for its softmax.  Each split writes the split attention's partial (O / l,
+// m, l) with plain stores; the split attention's merge kernel runs
 // next (hand-offs inside the kernel cost a device-scope round trip each, a
 // kernel boundary less than the barrier and loads a merge here would need).
 // Only attention workgroups wait; every wait is bounded (err is set when one
@@ -755,8 +755,8 @@ __device__ __forceinline__ void step_select_wg(const KDims& d, const SeqInfo& si
 // Wave w scores rows 16w .. 16w+15 (S = K q^T, 16x16x32 MFMA, lane (g, c)
 // holding rows 16w + 4g + i of head c); the softmax takes the exact maximum
 // over the split's rows; O^T += V^T P^T takes V^T from the transposing LDS
-// read, wave w owning value tiles w, w+4, ...; the partial (m, l in the log2
-// domain, unnormalised O) goes to part like the split attention's.
+// read, wave w owning value tiles w, w+4, ...; the partial (O / l in bf16, m
+// and l in the log2 domain) goes to part like the split attention's.
 __device__ __forceinline__ void step_attn_wg(const KDims& d, int nps, int nspl, int aw, StepAttnSmem& sm,
                                              const uint16_t* __restrict__ q, const uint16_t* __restrict__ local_kv,
                                              const uint16_t* __restrict__ pooled_kv, const float* __restrict__ sinks,
@@ -931,14 +931,12 @@ __device__ __forceinline__ void step_attn_wg(const KDims& d, int nps, int nspl, 
       }
     }
   }
-  // the split's partial: O^T tile (16dt + 4g + i, head c) per lane, then (m, l)
-  float* pr = part + (((size_t)split * d.B + b) * d.H + hbase + c) * (DK + 2);
+  // the split's partial: O^T tile (16dt + 4g + i, head c) per lane over l, then (m, l)
+  const size_t prow = ((size_t)split * d.B + b) * d.H + hbase + c;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-  for (int n = 0; n < 8; ++n) *(f32x4*)(pr + 16 * (wv + 4 * n) + 4 * g) = acc[n];
-  if (wv == 0 && g == 0) {
-    pr[DK] = m;
-    pr[DK + 1] = l;
-  }
+  for (int n = 0; n < 8; ++n) store_part4(part, prow, DK, 16 * (wv + 4 * n) + 4 * g, acc[n], inv);
+  if (wv == 0 && g == 0) store_part_ml(part, prow, DK, m, l);
   if (pooled && tid == 0) {
     // done with the sequence's descriptor and threshold: the last pooled
     // split of the sequence clears them
@@ -2345,9 +2343,6 @@ constexpr int kCachedBlocksPerWg = 16;
 constexpr int kCachedMaxNb = 4096;
 constexpr int kCachedMaxCand = 1024;
 
-__device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
-
 // Mean of the b key rows of block beta, lane l holding dims 2l and 2l+1 (64
 // lanes, D_i = 128): rows summed in order in f32, then scaled by 1/b.
 __device__ __forceinline__ float2 block_mean_lane(const uint16_t* kb, int beta, int bsz) {
@@ -2782,7 +2777,7 @@ StepSyncLayout step_sync_layout(const KDims& d) {
 size_t decode_step_sync_bytes(const KDims& d) { return step_sync_layout(d).total; }
 
 size_t decode_step_partial_bytes(const KDims& d) {
-  return (size_t)decode_step_splits(d) * d.B * d.H * (d.Dv + 2) * sizeof(float);
+  return (size_t)decode_step_splits(d) * d.B * d.H * part_row_bytes(d.Dv);
 }
 
 hipError_t launch_decode_step(const KDims& d, const void* q_idx, const float* w, const void* keys, const int* t0,

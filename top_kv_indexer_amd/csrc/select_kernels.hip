@@ -765,7 +765,15 @@ __device__ __forceinline__ void step_attn_wg(const KDims& d, int nps, int nspl, 
   constexpr int DK = 512;
   const int tid = threadIdx.x, lane = lane_id(), wv = wave_id(), g = lane >> 4, c = lane & 15;
   const int ngrp = d.H >> 4;
-  const int split = aw % nspl, hg = (aw / nspl) % ngrp, b = aw / (nspl * ngrp);
+  // workgroup aw takes head group hg of (sequence, split) pair p, with
+  // aw = 8 ngrp (p / 8) + 8 hg + p % 8: the head groups of one split are 8
+  // workgroups apart, so they are dealt to one XCD (round-robin over 8) and
+  // three of the four gathers of its rows find them in that XCD's L2; pairs
+  // past the last are padding
+  const int sg = aw / (8 * ngrp), rem = aw - sg * (8 * ngrp);
+  const int hg = rem >> 3, pair = 8 * sg + (rem & 7);
+  if (pair >= d.B * nspl) return;
+  const int split = pair % nspl, b = pair / nspl;
   const int hbase = hg * 16;
   const bool pooled = split < nps;
   // this group's q (the B operand of the scores), requested first
@@ -2747,14 +2755,19 @@ int decode_step_pooled_splits(const KDims& d) {
 }
 int decode_step_splits(const KDims& d) { return decode_step_pooled_splits(d) + cdiv(d.window, kStepRows); }
 
+// Attention workgroups of the decode step: 8 (sequence, split) pairs x H/16
+// head groups per group of 8 H/16 workgroups, the last group padded.
+static long long decode_step_attn_wgs(const KDims& d) {
+  return 8LL * (d.H / 16) * cdiv((long long)d.B * decode_step_splits(d), 8);
+}
+
 bool decode_step_ok(const KDims& d, bool idx_bf16, bool attn_bf16, int max_attn_wgs) {
   if (!decode_fused_ok(d, idx_bf16) || d.L != 1 || d.local_ring) return false;
   // kept blocks of 16, 32 or 64 rows (a split's block ids fit one word); a
   // 512-wide bf16 KV in groups of 16 heads
   if (d.index_block < 16 || d.topk > 1024 || !attn_bf16 || d.Dk != 512 || d.Dv != 512 || d.H % 16 != 0) return false;
   const long long slabs = (long long)d.B * cdiv(d.Np_cap, 64);
-  const long long attn = (long long)d.B * (d.H / 16) * decode_step_splits(d);
-  return slabs <= 1024 && decode_step_splits(d) <= kStepMaxSplits && attn <= max_attn_wgs;
+  return slabs <= 1024 && decode_step_splits(d) <= kStepMaxSplits && decode_step_attn_wgs(d) <= max_attn_wgs;
 }
 
 // Sync words of the decode step, 64-byte lines: err, then per sequence seen
@@ -2793,7 +2806,7 @@ hipError_t launch_decode_step(const KDims& d, const void* q_idx, const float* w,
   sy.desc = (uint64_t*)(base + l.desc);
   const int nslab = cdiv(d.Np_cap, 64);
   const int nspl = decode_step_splits(d), nps = decode_step_pooled_splits(d);
-  const int grid = d.B * nslab + d.B * (d.H / 16) * nspl;
+  const int grid = d.B * nslab + (int)decode_step_attn_wgs(d);
   hipLaunchKernelGGL(k_decode_step, dim3(grid), dim3(256), 0, st, d, nslab, nps, nspl, (const uint16_t*)q_idx, w,
                      (const uint16_t*)keys, t0, (const uint16_t*)q, (const uint16_t*)local_kv,
                      (const uint16_t*)pooled_kv, sinks, fscore, cscore, cnt, I, top_blk, path, part, sy);

@@ -26,12 +26,6 @@ typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
 
 constexpr int kTile = 32;
 
-__device__ __forceinline__ bf16x8 pack8(const float (&p)[8]) {
-  u32x4 u;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) u[k] = pack_bf16x2(p[2 * k], p[2 * k + 1]);
-  return __builtin_bit_cast(bf16x8, u);
-}
 
 // One workgroup = HW = 16*NHG heads of one query row (one KV split), NW =
 // 2*NHG waves; KV tiles of 32 rows stream through a ring of NBUF LDS slots.
@@ -126,7 +120,7 @@ __global__ __launch_bounds__(NHG * 128) void k_attn_mfma(KDims d, int splits, co
   // with 16 heads straight into registers.
   bf16x8 qf[NS];
   auto issue_q = [&]() {
-    uint16_t* qs = kv[NBUF - 2];  // HW <= 64 rows span slots NBUF-2 and NBUF-1
+    // HW <= 64 rows span ring slots NBUF-2 and NBUF-1
     const uint16_t* qg = q + ((size_t)row * d.H + hbase) * DK;
 #pragma unroll
     for (int u = 0; u < HW / NW; ++u) {
@@ -634,8 +628,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_fa(KDims d, c
         const uint16_t* src = (pooled ? pooled_b : local_b) + (size_t)(uint32_t)(pooled ? cd : -1 - cd) * DK;
         const int trow = RPW * wvs + r;
         const uint32_t dst = kv_lds + (uint32_t)((slot * kTile + trow) * KPD * 2);
-        g2lds16(src + (lane ^ sw(trow)) * 8, dst);
-        if (DK > 512 && (lane ^ sw(trow)) < DK / 8 - 64) g2lds16(src + 512 + (lane ^ sw(trow)) * 8, dst + 1024);
+        g2lds16_builtin(src + (lane ^ sw(trow)) * 8, dst);
+        if (DK > 512 && (lane ^ sw(trow)) < DK / 8 - 64) g2lds16_builtin(src + 512 + (lane ^ sw(trow)) * 8, dst + 1024);
       }
     };
     auto wait_loads = [&](int keep) {  // at most `keep` later tiles' loads still in flight
@@ -821,7 +815,15 @@ __global__ __launch_bounds__(256) void k_attn_split64(KDims d, int splits, const
   __shared__ int s_code[kSplitRows];
   __shared__ uint32_t s_live[2];
   args_now(d, splits, q, local_kv, pooled_kv, I, t0, part);
-  const int split = blockIdx.x, row = blockIdx.y, hbase = blockIdx.z * 16;
+  // workgroup wg takes head group hg of (query row, split) pair p, with
+  // wg = 8 ngrp (p / 8) + 8 hg + p % 8: the head groups of one split are 8
+  // workgroups apart, so they are dealt to one XCD (round-robin over 8) and
+  // share its L2 for the split's rows; pairs past the last are padding
+  const int ngrp = d.H >> 4, wg = blockIdx.x;
+  const int sg = wg / (8 * ngrp), rem = wg - sg * (8 * ngrp);
+  const int pair = 8 * sg + (rem & 7);
+  if (pair >= splits * d.B * d.L) return;
+  const int split = pair % splits, row = pair / splits, hbase = (rem >> 3) * 16;
   const int b = row / d.L, j = row - b * d.L;
   const int lane = lane_id(), wv = wave_id(), g = lane >> 4, c = lane & 15;
   // this row's 16 heads of q (the B operand of S) and wave 0's entries of
@@ -1142,7 +1144,7 @@ template <int DK, int DV>
 hipError_t launch_mfma(const KDims& d, const void* q, const void* local_kv, const void* pooled_kv, const int* I,
                        const float* sinks, const int* t0, void* out, float* partial, int splits, hipStream_t st) {
   if (attn_split64_ok(d)) {
-    const dim3 grid(splits, d.B * d.L, d.H / 16);
+    const dim3 grid(8 * (d.H / 16) * ((splits * d.B * d.L + 7) / 8));
     hipLaunchKernelGGL((k_attn_split64<DK, DV>), grid, dim3(256), 0, st, d, splits, (const uint16_t*)q,
                        (const uint16_t*)local_kv, (const uint16_t*)pooled_kv, I, t0, partial);
     return hipGetLastError();

@@ -290,10 +290,15 @@ template <class F>
 hipError_t timed(const char* name, hipStream_t st, F launch) {
   if (!g_prof_on) return launch();
   ProfRecord r{name, prof_event(), prof_event()};
-  if (r.start) hipEventRecord(r.start, st);
+  bool ok = r.start && r.stop && hipEventRecord(r.start, st) == hipSuccess;
   const hipError_t e = launch();
-  if (r.stop) hipEventRecord(r.stop, st);
-  if (r.start && r.stop) g_prof_pending.push_back(r);
+  ok = ok && hipEventRecord(r.stop, st) == hipSuccess;
+  if (ok) {
+    g_prof_pending.push_back(r);
+  } else {  // this launch goes untimed; the events go back to the pool
+    if (r.start) g_prof_pool.push_back(r.start);
+    if (r.stop) g_prof_pool.push_back(r.stop);
+  }
   return e;
 }
 
@@ -687,7 +692,7 @@ int hisa_decode_step(const hisa_dims* d, const void* q_idx, const float* w, cons
 int hisa_profile_enable(int on) {
   if (!on) {
     for (auto& r : g_prof_pending) {
-      hipEventSynchronize(r.stop);
+      (void)hipEventSynchronize(r.stop);  // drained only; the timings are discarded
       g_prof_pool.push_back(r.start);
       g_prof_pool.push_back(r.stop);
     }

@@ -53,11 +53,25 @@ __device__ __forceinline__ int vector_zero() {
   asm volatile("v_mov_b32 %0, 0" : "=v"(z));
   return z;
 }
+// 16 bytes per lane from global memory straight into LDS (gfx950
+// global_load_lds_dwordx4): lane i's bytes land at lds_base + 16 i, lds_base
+// the same in every lane (it goes to the instruction through m0, which the
+// compiler sets as the asm's input).  Counted on vmcnt like any vector load;
+// the callers wait for it explicitly.  (As asm, the load is invisible to the
+// compiler's own LDS-DMA wait insertion, which cannot tell ring slots of one
+// LDS array apart and would otherwise drain every prefetch before LDS reads.)
 __device__ __forceinline__ void g2lds16(const void* gsrc, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
-               : "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-               : "memory", "m0");
+               : "v"(gsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
+}
+// The same load as a compiler builtin, which the compiler schedules and waits
+// for itself (it adds a full vmcnt wait before any LDS read it cannot tell
+// apart from the load's destination): for kernels whose LDS reads it can.
+__device__ __forceinline__ void g2lds16_builtin(const void* gsrc, uint32_t lds_base) {
+  __builtin_amdgcn_global_load_lds(
+      gsrc, (__attribute__((address_space(3))) void*)(uintptr_t)__builtin_amdgcn_readfirstlane(lds_base), 16, 0, 0);
 }
 
 // Two floats to a packed bf16 pair (low half = lo), round to nearest even, in

@@ -25,7 +25,6 @@ namespace hisa {
 
 namespace {
 
-constexpr int KP = 136;  // LDS row pitch (bf16) of 128-dim rows: 272 B, 4 banks of skew per row
 
 __device__ __forceinline__ bf16x8 lds8(const uint16_t* p) { return *(const bf16x8*)p; }
 __device__ __forceinline__ bf16x8 ldg8(const uint16_t* p) { return *(const bf16x8*)p; }

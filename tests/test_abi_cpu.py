@@ -76,9 +76,9 @@ def test_workspace_sizes(lib):
     # a short chunk (B * L <= 192 rows): every block mean (f32), then per row
     # the cached-means selection (counters, block scores, kept blocks, candidates)
     assert hisa.workspace_bytes(hisa.OP_SELECT_PREFILL, dims(L=4)) == (
-        256 * 128 * 4 + 768 + 4 * 256 * 4 + 256 + 4 * 1024 * 4)
+        256 * 128 * 4 + r256(cached_counter_bytes(4)) + 4 * 256 * 4 + 256 + 4 * 1024 * 4)
     assert hisa.workspace_bytes(hisa.OP_SELECT_PREFILL, dims(L=192)) == (
-        256 * 128 * 4 + 192 * 3 * 64 + 192 * 256 * 4 + 192 * 16 * 4 + 192 * 1024 * 4)
+        256 * 128 * 4 + r256(cached_counter_bytes(192)) + 192 * 256 * 4 + 192 * 16 * 4 + 192 * 1024 * 4)
     # one row more: one query row per wave
     assert hisa.workspace_bytes(hisa.OP_SELECT_PREFILL, dims(L=193)) == rep
     # no hierarchy: only the flat scan
@@ -162,12 +162,24 @@ def test_noalloc_decode_rejects_dims_past_its_workspace(lib):
     assert rc == -1
 
 
+def r256(n):
+    return (n + 255) // 256 * 256
+
+
+def cached_counter_bytes(rows, groups=1):
+    # per row one coarse counter and the group counters, one fine counter (each
+    # on its own 64-byte line), then the error line and 16 descriptor words per
+    # row (the one-launch form's hand-off of the kept blocks)
+    return rows * (1 + groups) * 64 + rows * 64 + 64 + rows * 16 * 8
+
+
 def test_cached_decode_workspace_and_limits(lib):
     # counters (1 sequence + 1 group counter for 16 workgroups, + 1 for the
-    # fine stage: 3 x 64 B, rounded to 256), block scores, kept blocks,
-    # 1024 candidate scores
+    # fine stage, the error line and the descriptors, rounded to 256), block
+    # scores, kept blocks, 1024 candidate scores
     d = dims()
-    assert hisa.workspace_bytes(hisa.OP_SELECT_DECODE_CACHED, d) == 256 + 256 * 4 + 256 + 1024 * 4
+    assert hisa.workspace_bytes(hisa.OP_SELECT_DECODE_CACHED, d) == (
+        r256(cached_counter_bytes(1)) + 256 * 4 + 256 + 1024 * 4)
     assert hisa.workspace_bytes(hisa.OP_BLOCK_MEANS_UPDATE, d) == 0
     for kw in (dict(index_block=0), dict(Np_cap=64 * 4097), dict(index_keep=32), dict(mode=hisa.MODE_FORCE_FLAT),
                dict(index_keep=4), dict(idx_dtype=hisa.F32), dict(H_i=32), dict(B=40000, L=2)):

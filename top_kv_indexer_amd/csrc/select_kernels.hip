@@ -2349,6 +2349,7 @@ __global__ __launch_bounds__(256) void k_fill_dense(KDims d, const int* __restri
 constexpr int kCachedBlocksPerWg = 16;
 constexpr int kCachedMaxNb = 4096;
 constexpr int kCachedMaxCand = 1024;
+constexpr int kCachedSlabs = kCachedMaxCand / 64;  // fine workgroups (64 candidates each) per query row
 
 // Mean of the b key rows of block beta, lane l holding dims 2l and 2l+1 (64
 // lanes, D_i = 128): rows summed in order in f32, then scaled by 1/b.
@@ -2365,20 +2366,24 @@ __device__ __forceinline__ float2 block_mean_lane(const uint16_t* kb, int beta, 
   return make_float2(sx * inv, sy * inv);
 }
 
-__global__ __launch_bounds__(256) void k_cached_coarse(KDims d, const uint16_t* __restrict__ q_idx,
-                                                       const float* __restrict__ w, const uint16_t* __restrict__ keys,
-                                                       float* rep, const int* __restrict__ t0, float* cscore, int* blk,
-                                                       int* cnt, int* I, int* top_blk, int* path) {
+// Stage 1, workgroup x of query row `row` (FUSED: the one-launch form, whose
+// completing workgroup hands the kept blocks to the fine workgroups through
+// desc instead of blk).
+template <bool FUSED>
+__device__ __forceinline__ void cached_coarse_wg(const KDims& d, const uint16_t* __restrict__ q_idx,
+                                                 const float* __restrict__ w, const uint16_t* __restrict__ keys,
+                                                 float* rep, const int* __restrict__ t0, float* cscore, int* blk,
+                                                 int* cnt, int* I, int* top_blk, int* path, int x, int row, int ngmax,
+                                                 uint64_t* desc) {
   // the workgroup's 16 block means; the row pitch of 132 floats puts the 16
   // blocks' same chunk in distinct banks for the operand reads
   __shared__ __align__(16) float s_rep[kCachedBlocksPerWg][132];
   __shared__ float s_part[4][16];
   __shared__ WgTopkSmem s_tk;
+  __shared__ int s_kept[kRowKeep];
   __shared__ int s_flag;
-  args_now(d, q_idx, w, keys, rep, t0, cscore, blk, cnt, I, top_blk, path);
-  // one query row (b, j) per grid row; several rows of a sequence (a verify
+  // one query row (b, j) per row; several rows of a sequence (a verify
   // chunk) each select on their own, with the batched masks
-  const int row = blockIdx.y, x = blockIdx.x;
   const int b = row / d.L, j = row - b * d.L;
   const int tid = threadIdx.x, lane = lane_id(), wv = wave_id(), g = lane >> 4, c = lane & 15;
   const int t0b = t0[b];
@@ -2479,7 +2484,6 @@ __global__ __launch_bounds__(256) void k_cached_coarse(KDims d, const uint16_t* 
   // cnt: B*L row counters, then B*L x ngmax group counters
   const int nrows = d.B * d.L;
   const int grp = x / kArriveGroup, ngrp = (nwg + kArriveGroup - 1) / kArriveGroup;
-  const int ngmax = (gridDim.x + kArriveGroup - 1) / kArriveGroup;
   const bool last = publish(
       [&] {
         if (ngrp == 1) return arrive(cnt + (size_t)row * kCntStride, 1, nwg);  // one atomic on the path
@@ -2497,32 +2501,48 @@ __global__ __launch_bounds__(256) void k_cached_coarse(KDims d, const uint16_t* 
   for (int r = 0; r < 16; ++r) v[r] = ld_dev(csb + min(256 * r + tid, si.nb - 1));
 #pragma unroll
   for (int r = 0; r < 16; ++r) key[r] = 256 * r + tid < si.nb ? score_key(v[r]) : 0u;
-  int* blkb = blk + (size_t)row * d.index_keep;
   int* tbo = top_blk ? top_blk + (size_t)row * d.index_keep : nullptr;
   wg_emit_topk16(key, si.nb, si.Kb, s_tk, [&](int slot, int r) {
-    blkb[slot] = 256 * r + tid;
+    if (FUSED) s_kept[slot] = 256 * r + tid;
+    else blk[(size_t)row * d.index_keep + slot] = 256 * r + tid;
     if (tbo) tbo[slot] = 256 * r + tid;
   });
   if (tbo)
     for (int i = si.Kb + tid; i < d.index_keep; i += 256) tbo[i] = -1;
   if (path && tid == 0 && j == 0) path[b] = si.path;
+  if constexpr (FUSED) {
+    // one word per 64 candidates: the ids (plus one) of its 64 / b kept
+    // blocks, 13 bits each, above the mode bits
+    lds_sync();
+    const int lbsz = __builtin_ctz(bsz), per = 64 >> lbsz;
+    const int nslab = (si.Kb * bsz + 63) / 64;
+    if (tid < nslab) {
+      uint64_t dv = kDescHisa;
+      for (int jj = 0; jj < per; ++jj)
+        if (tid * per + jj < si.Kb) dv |= (uint64_t)(s_kept[tid * per + jj] + 1) << (2 + 13 * jj);
+      st_dev_u64(desc + (size_t)row * kCachedSlabs + tid, dv);
+    }
+  }
 }
 
-__global__ __launch_bounds__(256) void k_cached_fine(KDims d, const uint16_t* __restrict__ q_idx,
-                                                     const float* __restrict__ w, const uint16_t* __restrict__ keys,
-                                                     const int* __restrict__ t0, const int* __restrict__ blk,
-                                                     float* fs, int* cnt, int* I) {
+// Stage 2, 64 candidates (slab) of query row `row` (FUSED: the kept blocks
+// come from the completing coarse workgroup of the same launch through desc,
+// polled with a bounded wait; the row's completing workgroup clears them).
+template <bool FUSED>
+__device__ __forceinline__ void cached_fine_wg(const KDims& d, const uint16_t* __restrict__ q_idx,
+                                               const float* __restrict__ w, const uint16_t* __restrict__ keys,
+                                               const int* __restrict__ t0, const int* __restrict__ blk, float* fs,
+                                               int* cnt, int* I, int slab, int row, uint64_t* desc, int* err) {
   __shared__ __align__(16) uint16_t s_q[64 * 128];
   __shared__ WgTopkSmem s_tk;
   __shared__ int s_blk[kRowKeep];
+  __shared__ uint64_t s_word;
   __shared__ int s_flag;
-  args_now(d, q_idx, w, keys, t0, blk, fs, cnt, I);
-  const int row = blockIdx.y, slab = blockIdx.x;
   const int b = row / d.L, j = row - b * d.L;
   const int tid = threadIdx.x, lane = lane_id(), wv = wave_id(), g = lane >> 4, c = lane & 15;
   const int t0b = t0[b];
   // the retained blocks (meaningful on the HiSA path only; always in bounds)
-  const int blk_tid = tid < d.index_keep ? blk[(size_t)row * d.index_keep + tid] : 0;
+  const int blk_tid = (!FUSED && tid < d.index_keep) ? blk[(size_t)row * d.index_keep + tid] : 0;
   issue_q_lds(q_idx + (size_t)row * 64 * 128, s_q);
   const float* wrow = w + (size_t)row * 64;
   float wl[4][4];
@@ -2543,7 +2563,23 @@ __global__ __launch_bounds__(256) void k_cached_fine(KDims d, const uint16_t* __
     __builtin_amdgcn_s_waitcnt(0x0F70);  // no global->LDS copy outlives the workgroup
     return;
   }
-  if (tid < si.Kb && hisa) s_blk[tid] = blk_tid;
+  // a descriptor's block field: the id plus one (0 after a timed-out wait;
+  // clamped so that every row read stays inside keys)
+  auto desc_blk = [&](uint64_t dv, int jj) {
+    const int fld = (int)((dv >> (2 + 13 * jj)) & 0x1FFFu);
+    return min(max(fld - 1, 0), d.nb_cap - 1);
+  };
+  const int per = 64 >> lbsz;
+  if constexpr (FUSED) {
+    if (hisa) {
+      if (tid == 0) s_word = poll_nonzero(desc + (size_t)row * kCachedSlabs + slab, err);
+      __syncthreads();
+      const uint64_t dv = s_word;
+      if (tid < per) s_blk[slab * per + tid] = desc_blk(dv, tid);
+    }
+  } else {
+    if (tid < si.Kb && hisa) s_blk[tid] = blk_tid;
+  }
   __syncthreads();
   auto pos = [&](int cc) { return hisa ? (s_blk[cc >> lbsz] << lbsz) + (cc & (bsz - 1)) : cc; };
   const int cand = min(slab * 64 + wv * 16 + c, n - 1);
@@ -2580,6 +2616,20 @@ __global__ __launch_bounds__(256) void k_cached_fine(KDims d, const uint16_t* __
   if (g == 0 && cc < n) st_dev(fsb + cc, v);
   const bool last = publish([&] { return arrive(cnt + (size_t)row * kCntStride, 1, nslab); }, &s_flag);
   if (!last) return;
+  if constexpr (FUSED) {
+    if (hisa) {
+      // every kept block, from the row's descriptors (each fine workgroup read
+      // its own before it arrived, so they are cleared here)
+      if (tid < nslab) {
+        uint64_t* dp = desc + (size_t)row * kCachedSlabs + tid;
+        const uint64_t dv = ld_dev_u64(dp);
+        for (int jj = 0; jj < per; ++jj)
+          if (tid * per + jj < si.Kb) s_blk[tid * per + jj] = desc_blk(dv, jj);
+        st_dev_u64(dp, 0);
+      }
+      __syncthreads();
+    }
+  }
   int* Ib = I + (size_t)row * d.topk;
   for (int i = si.k + tid; i < d.topk; i += 256) Ib[i] = -1;
   uint32_t key[4];
@@ -2589,6 +2639,47 @@ __global__ __launch_bounds__(256) void k_cached_fine(KDims d, const uint16_t* __
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) key[rr] = 256 * rr + tid < n ? score_key(sv[rr]) : 0u;
   wg_emit_topk(key, n, si.k, s_tk, [&](int slot, int rr) { Ib[slot] = pos(256 * rr + tid); });
+}
+
+// The two stages as separate launches (blk carries the kept blocks).
+__global__ __launch_bounds__(256) void k_cached_coarse(KDims d, const uint16_t* __restrict__ q_idx,
+                                                       const float* __restrict__ w, const uint16_t* __restrict__ keys,
+                                                       float* rep, const int* __restrict__ t0, float* cscore, int* blk,
+                                                       int* cnt, int* I, int* top_blk, int* path) {
+  args_now(d, q_idx, w, keys, rep, t0, cscore, blk, cnt, I, top_blk, path);
+  cached_coarse_wg<false>(d, q_idx, w, keys, rep, t0, cscore, blk, cnt, I, top_blk, path, blockIdx.x, blockIdx.y,
+                          (gridDim.x + kArriveGroup - 1) / kArriveGroup, nullptr);
+}
+
+__global__ __launch_bounds__(256) void k_cached_fine(KDims d, const uint16_t* __restrict__ q_idx,
+                                                     const float* __restrict__ w, const uint16_t* __restrict__ keys,
+                                                     const int* __restrict__ t0, const int* __restrict__ blk,
+                                                     float* fs, int* cnt, int* I) {
+  args_now(d, q_idx, w, keys, t0, blk, fs, cnt, I);
+  cached_fine_wg<false>(d, q_idx, w, keys, t0, blk, fs, cnt, I, blockIdx.x, blockIdx.y, nullptr, nullptr);
+}
+
+// Both stages in one launch (index_block >= 16, so one 64-bit word holds the
+// kept blocks of 64 candidates): rows x nwg_c coarse workgroups, then rows x
+// kCachedSlabs fine workgroups, which start at once (q, weights) and wait for
+// their descriptor.  The coarse workgroups come first in dispatch order and
+// wait for nothing, so the waiting ones cannot hold them off; every wait is
+// bounded (err becomes 1 if one ever timed out).
+__global__ __launch_bounds__(256) void k_cached_step(KDims d, int nwg_c, const uint16_t* __restrict__ q_idx,
+                                                     const float* __restrict__ w, const uint16_t* __restrict__ keys,
+                                                     float* rep, const int* __restrict__ t0, float* cscore, float* fs,
+                                                     int* cnt_c, int* cnt_f, int* I, int* top_blk, int* path,
+                                                     uint64_t* desc, int* err) {
+  args_now(d, nwg_c, q_idx, w, keys, rep, t0, cscore, fs, cnt_c, cnt_f, I, top_blk, path, desc, err);
+  const int nc = d.B * d.L * nwg_c, bid = blockIdx.x;
+  if (bid < nc) {
+    const int row = bid / nwg_c;
+    cached_coarse_wg<true>(d, q_idx, w, keys, rep, t0, cscore, nullptr, cnt_c, I, top_blk, path, bid - row * nwg_c,
+                           row, (nwg_c + kArriveGroup - 1) / kArriveGroup, desc);
+    return;
+  }
+  const int f = bid - nc, row = f / kCachedSlabs;
+  cached_fine_wg<true>(d, q_idx, w, keys, t0, nullptr, fs, cnt_f, I, f - row * kCachedSlabs, row, desc, err);
 }
 
 // Block means of the blocks completed by the step's L tokens: blocks
@@ -2661,11 +2752,14 @@ bool cached_decode_ok(const KDims& d, bool bf16) {
          d.index_keep <= kRowKeep && !d.force_flat && bk >= d.topk;
 }
 
+// Counters of the cached decode: per row a coarse counter and ngmax group
+// counters, then per row a fine counter, then the error line and the one-launch
+// form's descriptors (rows x kCachedSlabs 64-bit words); all zero at rest.
 size_t cached_counter_ints(const KDims& d) {
   const size_t rows = (size_t)d.B * d.L;
   const size_t wgs = ((size_t)d.nb_cap + kCachedBlocksPerWg - 1) / kCachedBlocksPerWg;
   const size_t ngmax = (std::max<size_t>(wgs, 1) + kArriveGroup - 1) / kArriveGroup;
-  return rows * (1 + ngmax) * kCntStride + rows * kCntStride;
+  return rows * (1 + ngmax) * kCntStride + rows * kCntStride + kCntStride + rows * kCachedSlabs * 2;
 }
 
 size_t cached_fine_floats(const KDims& d) { return (size_t)d.B * d.L * kCachedMaxCand; }
@@ -2677,6 +2771,15 @@ hipError_t launch_cached_decode(const KDims& d, const void* q_idx, const float* 
   const size_t ngmax = (wgs + kArriveGroup - 1) / kArriveGroup;
   const unsigned rows = (unsigned)(d.B * d.L);
   int* cnt_fine = cnt + (size_t)rows * (1 + ngmax) * kCntStride;
+  if (d.index_block >= 16) {
+    // one launch: a descriptor word holds the kept blocks of 64 candidates
+    int* err = cnt_fine + (size_t)rows * kCntStride;
+    uint64_t* desc = (uint64_t*)(err + kCntStride);
+    hipLaunchKernelGGL(k_cached_step, dim3(rows * (wgs + kCachedSlabs)), dim3(256), 0, st, d, (int)wgs,
+                       (const uint16_t*)q_idx, w, (const uint16_t*)keys, rep, t0, cscore, fs, cnt, cnt_fine, I,
+                       top_blk, path, desc, err);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_cached_coarse, dim3(wgs, rows), dim3(256), 0, st, d, (const uint16_t*)q_idx, w,
                      (const uint16_t*)keys, rep, t0, cscore, blk, cnt, I, top_blk, path);
   hipError_t e = hipGetLastError();

@@ -162,9 +162,12 @@ int hisa_select_decode(const hisa_dims* d, const void* q_idx, const float* w, co
  * index_keep <= 64, topk <= index_block * index_keep <= 1024, mode not
  * HISA_MODE_FORCE_FLAT (HISA_ERR_ARG otherwise; use hisa_select_decode).
  * HISA_MODE_FORCE_DENSE behaves as in hisa_select_decode and leaves rep alone.
- * Workspace: its first part holds arrival counters under the same rule as
- * hisa_select_decode's (zero before first use, left zero; zero again before
- * a call with a larger B or Np_cap). */
+ * Workspace: its first part holds arrival counters and, with index_block >= 16
+ * (both stages in one launch), the words that hand each row's kept blocks to
+ * its fine stage, under the same rule as hisa_select_decode's counters (zero
+ * before first use, left zero; zero again before a call with a larger B, L or
+ * Np_cap); an int after the counters becomes 1 if such a hand-off ever timed
+ * out (its bounded wait, about a second). */
 int hisa_select_decode_cached(const hisa_dims* d, const void* q_idx, const float* w, const void* keys,
                               float* rep, const int32_t* t0, int32_t* I_out, int32_t* top_blk_out,
                               int32_t* path_out, void* ws, size_t ws_bytes, void* stream);

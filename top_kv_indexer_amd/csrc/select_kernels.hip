@@ -2685,15 +2685,17 @@ __global__ __launch_bounds__(256) void k_cached_step(KDims d, int nwg_c, const u
 // Block means of the blocks completed by the step's L tokens: blocks
 // [floor(floor(t0 / r) / b), floor(Np / b)) (every complete block when t0 = 0),
 // rows summed in order in f32 and scaled by 1/b, as the cached decode does.
-// bf16 keys with 128 dims: wave w of workgroup x takes block 4x + w, lane l
-// dims 2l and 2l+1; all b rows are requested before the in-order sum, which
-// is the same sum as the cached decode's (so the two give the same bits).
-__global__ __launch_bounds__(256) void k_rep_update_bf16(KDims d, int all, const uint16_t* __restrict__ keys,
-                                                         const int* __restrict__ t0, float* rep, int* zero_p,
-                                                         int zero_n) {
-  const int b = blockIdx.y, beta = blockIdx.x * 4 + wave_id(), lane = lane_id();
-  if (zero_p && b == 0 && blockIdx.x == 0)
-    for (int i = threadIdx.x; i < zero_n; i += 256) zero_p[i] = 0;
+// bf16 keys with 128 dims: one wave (workgroup) per block, spread over every
+// CU, lane l dims 2l and 2l+1; all b rows are requested before the in-order
+// sum, which is the same sum as the cached decode's (so the two give the same
+// bits).
+__global__ __launch_bounds__(64) void k_rep_update_bf16(KDims d, int all, const uint16_t* __restrict__ keys,
+                                                        const int* __restrict__ t0, float* rep, int* zero_p,
+                                                        int zero_n) {
+  const int b = blockIdx.y, beta = blockIdx.x, lane = lane_id();
+  // sequence 0's workgroups also zero the arrival counters of the kernels that follow
+  if (zero_p && b == 0)
+    for (int i = blockIdx.x * 64 + lane; i < zero_n; i += gridDim.x * 64) zero_p[i] = 0;
   const int t0b = t0[b];
   const SeqInfo si = seq_info(d, t0b);
   const int bsz = d.index_block;
@@ -2793,7 +2795,7 @@ hipError_t launch_rep_update(const KDims& d, bool bf16, bool all, const void* ke
                              int* zero_p, size_t zero_n, hipStream_t st) {
   if (d.nb_cap == 0) return hipSuccess;
   if (bf16 && d.D_i == 128)
-    hipLaunchKernelGGL(k_rep_update_bf16, dim3((d.nb_cap + 3) / 4, d.B), dim3(256), 0, st, d, (int)all,
+    hipLaunchKernelGGL(k_rep_update_bf16, dim3(d.nb_cap, d.B), dim3(64), 0, st, d, (int)all,
                        (const uint16_t*)keys, t0, rep, zero_p, (int)zero_n);
   else if (bf16)
     hipLaunchKernelGGL(k_rep_update<uint16_t>, dim3(d.nb_cap, d.B), dim3(128), 0, st, d, (int)all,

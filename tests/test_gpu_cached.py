@@ -72,6 +72,41 @@ def test_cached_decode_matches_oracle(hisa, case):
     say(f"  ids equal to the stateless path: {same:.5f}")
 
 
+def cached_counter_bytes(w):
+    """The cached selection's counter region: per query row a coarse counter
+    and its group counters (16 coarse workgroups of 16 blocks to a group) and a
+    fine counter, one 64-byte line each, then the error line and 16 descriptor
+    words per row."""
+    rows = w.B * w.L
+    wgs = -(-(w.Np_cap // w.index_block) // 16)
+    groups = -(-wgs // 16)
+    return rows * (1 + groups) * 64 + rows * 64 + 64 + rows * 16 * 8
+
+
+@pytest.mark.parametrize("block,keep", [(8, 64), (16, 64), (32, 32)])
+def test_cached_decode_small_blocks(hisa, block, keep):
+    # Blocks of 8 rows take the two-launch form (eight block ids per 64
+    # candidates do not fit one descriptor word); blocks of 16 and 32 the
+    # one-launch form, four and two kept blocks per descriptor word.  Two
+    # calls on one workspace: its counters, error word and descriptors are
+    # back to zero after each.
+    w = synth.FLASH_DECODE.with_(name=f"flash_cached_b{block}", B=2, t0=[65536, 30001], Np_cap=16384,
+                                 index_block=block, index_keep=keep, planted=24)
+    x, g = inputs(w, 77)
+    rep = full_cache(hisa, w, g)
+    d = hisa.selection_dims(g["q_idx"], g["keys"], **sel_kw(w))
+    ws = torch.zeros(hisa.workspace_bytes(hisa.OP_SELECT_DECODE_CACHED, d), dtype=torch.uint8, device="cuda")
+    nbytes = cached_counter_bytes(w)
+    for call in range(2):
+        say(f"[run] cached decode, blocks of {block}, call {call}")
+        I, blk, path = hisa.hisa_select_decode_cached(g["q_idx"], g["w"], g["keys"], rep, g["t0"], **sel_kw(w),
+                                                      ws=ws)
+        torch.cuda.synchronize()
+        assert parity.to_np(path).tolist() == [hisa.PATH_HISA, hisa.PATH_HISA]
+        check_selection(w, x, I, blk, path)
+        assert (ws[:nbytes].view(torch.int32) == 0).all()
+
+
 def test_cached_decode_exact_ties(hisa):
     # The best row of each HiSA sequence copied over blocks 10..39, so the
     # coarse and the fine top-k both cut through exact ties; the lowest ids win

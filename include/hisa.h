@@ -276,10 +276,11 @@ int sparse_local_pooled_attention_ring(const hisa_dims* d, const void* q, const 
  * For few sequences of the shapes the one-kernel step serves (bf16 keys with
  * H_i = 64, D_i = 128, index_block 16, 32 or 64, index_keep * index_block and
  * topk <= 1024; bf16 attention with Dk = Dv = 512, H a multiple of 16; at most
- * 1024 key slabs of 64 rows over the batch, and B * H/16 * (ceil(max(
- * index_keep * index_block, topk) / 64) + ceil(window / 64)) attention
- * workgroups, at most 24 per head group and at most the device's compute
- * units) the step is one kernel: the attention of the kept blocks gathers and
+ * 1024 key slabs of 64 rows over the batch; S = ceil(max(index_keep *
+ * index_block, topk) / 64) + ceil(window / 64) attention splits per sequence,
+ * at most 24, and H/16 * 8 * ceil(B * S / 8) attention workgroups (the head
+ * groups of a split on one XCD), at most the device's compute units) the step
+ * is one kernel: the attention of the kept blocks gathers and
  * scores their rows as soon as the coarse stage has chosen them, while the
  * fine top-k is still running, and the local window is attended from the
  * start.  Otherwise (and under HISA_MODE_FORCE_DENSE) it runs the two calls'

@@ -107,6 +107,54 @@ def test_cached_decode_small_blocks(hisa, block, keep):
         assert (ws[:nbytes].view(torch.int32) == 0).all()
 
 
+def test_cached_decode_graph_replay(hisa):
+    # The one-launch cached selection of the B = 32 ragged batch captured once
+    # into a HIP graph (outputs, cache and workspace allocated beforehand) and
+    # replayed three times with eager calls and synchronisations between
+    # replays: every replay equals the eager call, the blocks it completes are
+    # rewritten with the same means, and the workspace words end at zero.
+    w = synth.BATCHED_DECODE
+    x, g = inputs(w, synth.SEEDS[w.name])
+    dev = torch.device("cuda")
+    rep = full_cache(hisa, w, g)
+    d = hisa.selection_dims(g["q_idx"], g["keys"], **sel_kw(w))
+    ws = torch.zeros(hisa.workspace_bytes(hisa.OP_SELECT_DECODE_CACHED, d), dtype=torch.uint8, device=dev)
+    I = torch.empty((w.B, 1, w.topk), dtype=torch.int32, device=dev)
+    blk = torch.empty((w.B, 1, w.index_keep), dtype=torch.int32, device=dev)
+    path = torch.empty((w.B,), dtype=torch.int32, device=dev)
+
+    def call():
+        hisa.hisa_select_decode_cached(g["q_idx"], g["w"], g["keys"], rep, g["t0"], **sel_kw(w), I=I, top_blk=blk,
+                                       path=path, ws=ws)
+
+    say("[run] eager cached selection")
+    call()
+    torch.cuda.synchronize()
+    check_selection(w, x, I, blk, path)
+    I_ref, blk_ref, path_ref, rep_ref = I.clone(), blk.clone(), path.clone(), rep.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    say("[run] capture")
+    with torch.cuda.graph(graph, stream=s):
+        call()
+    torch.cuda.synchronize()
+    for r in range(3):
+        I.fill_(-7)
+        blk.fill_(-7)
+        path.fill_(-7)
+        torch.cuda.synchronize()
+        say(f"[run] replay {r}")
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(I, I_ref) and torch.equal(blk, blk_ref) and torch.equal(path, path_ref), r
+        assert torch.equal(rep, rep_ref), r
+        call()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(I, I_ref)
+    assert (ws[:cached_counter_bytes(w.with_(Np_cap=int(x["Np_cap"])))].view(torch.int32) == 0).all()
+
+
 def test_cached_decode_exact_ties(hisa):
     # The best row of each HiSA sequence copied over blocks 10..39, so the
     # coarse and the fine top-k both cut through exact ties; the lowest ids win

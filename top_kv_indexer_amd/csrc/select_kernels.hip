@@ -431,8 +431,9 @@ __device__ __forceinline__ void load_slab_rows(const uint16_t* kb, int slab, int
 // The block mean is linear, so q_h . rep_beta is the mean of D[h][row] over
 // the block's rows: blocks of up to 16 rows are summed inside the wave,
 // larger ones from per-wave partial sums exchanged through s_part[par].
-// Rows past Np are scored but never stored, as are blocks past nb.
-__device__ __forceinline__ void score_slab(const KDims& d, const SeqInfo& si, int b, int slab, int par,
+// Rows past Np are scored but never stored, as are blocks past nb.  Returns
+// the fine score of row slab*64 + 16*wave + (lane & 15) (lanes < 16 hold it).
+__device__ __forceinline__ float score_slab(const KDims& d, const SeqInfo& si, int b, int slab, int par,
                                            const bf16x8 (&qf)[4][4], const float (&wl)[4][4], float w_head,
                                            const bf16x8 (&kf)[4], float* fscore, float* cscore,
                                            float (*s_part)[4][64]) {
@@ -452,7 +453,7 @@ __device__ __forceinline__ void score_slab(const KDims& d, const SeqInfo& si, in
   v = sum_rows(v);
   const int r = slab * 64 + wv * 16 + c;
   if (g == 0 && r < si.Np) st_dev(fscore + (size_t)b * d.Np_cap + r, v);
-  if (si.path != PATH_HISA) return;
+  if (si.path != PATH_HISA) return v;
   const int bsz = d.index_block;
   const float inv_b = 1.f / (float)bsz;
   if (bsz <= 16) {
@@ -465,7 +466,7 @@ __device__ __forceinline__ void score_slab(const KDims& d, const SeqInfo& si, in
     cv = sum_rows(cv);
     const int beta = r / bsz;
     if (g == 0 && (c & (bsz - 1)) == 0 && beta < si.nb) st_dev(cscore + (size_t)b * d.nb_cap + beta, cv);
-    return;
+    return v;
   }
   // blocks of 32 or 64 rows: per-head sums over this wave's rows to LDS,
   // then wave j < 64 / bsz owns block j of the slab
@@ -485,6 +486,7 @@ __device__ __forceinline__ void score_slab(const KDims& d, const SeqInfo& si, in
     const int beta = (slab * 64) / bsz + wv;
     if (lane == 0 && beta < si.nb) st_dev(cscore + (size_t)b * d.nb_cap + beta, cv);
   }
+  return v;
 }
 
 // Adds n to a device-scope arrival counter that completes at `total`;
@@ -522,6 +524,7 @@ struct ScanSlabSmem {
   __align__(16) uint16_t s_q[64 * 128];
   __align__(16) float s_part[2][4][64];
   DecodeSelSmem sel;
+  uint32_t bins[kHintBins];  // the slab's scores per coarse key bin
   int flag;
 };
 
@@ -530,15 +533,19 @@ struct ScanSlabSmem {
 // parallel.  With cnt != NULL the selection is fused: select(si) runs in the
 // workgroup that completes the last group of the sequence's slabs, and
 // unscored(si) in wave 0 of slab 0 of a dense or invalid sequence.  ngmax:
-// slab-group counters per sequence.
+// slab-group counters per sequence.  With hint != NULL the slab's stored
+// scores are also counted per coarse key bin (the top 8 bits of score_key)
+// into the sequence's bin counts, copy slab % kHintCopies: one device-scope
+// add per bin the slab holds.
 template <class UnscoredF, class SelectF>
 __device__ __forceinline__ void decode_scan_slab(const KDims& d, int b, int slab, int ngmax,
                                                  const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
                                                  const uint16_t* __restrict__ keys, const int* __restrict__ t0,
-                                                 float* fscore, float* cscore, int* cnt, ScanSlabSmem& sm,
-                                                 UnscoredF unscored, SelectF select) {
+                                                 float* fscore, float* cscore, int* cnt, int* hint,
+                                                 ScanSlabSmem& sm, UnscoredF unscored, SelectF select) {
   const int lane = lane_id(), g = lane >> 4;
   const int t0b = t0[b];  // requested first, needed after the rows arrive
+  if (hint) sm.bins[threadIdx.x] = 0;  // ordered before the adds by the barrier below
   const uint16_t* kb = keys + (size_t)b * d.Np_cap * 128;
   bf16x8 kf[4];
   load_slab_rows(kb, slab, d.Np_cap - 1, kf);
@@ -567,7 +574,16 @@ __device__ __forceinline__ void decode_scan_slab(const KDims& d, int b, int slab
   }
   const int nslab = (si.Np + 63) / 64;
   if (slab >= nslab) return;  // uniform over the workgroup
-  score_slab(d, si, b, slab, 0, qf, wl, w_head, kf, fscore, cscore, sm.s_part);
+  const float v = score_slab(d, si, b, slab, 0, qf, wl, w_head, kf, fscore, cscore, sm.s_part);
+  if (hint) {
+    const int r = slab * 64 + wave_id() * 16 + (lane & 15);
+    if (g == 0 && r < si.Np) atomicAdd(&sm.bins[score_key(v) >> 24], 1u);
+    __syncthreads();
+    const uint32_t h = sm.bins[threadIdx.x];
+    if (h)
+      __hip_atomic_fetch_add(hint + hint_slot(b, slab % kHintCopies, threadIdx.x), (int)h, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+  }
   if (!cnt) return;
   // cnt: B sequence counters, then B x ngmax group counters, kCntStride apart
   const int grp = slab / kArriveGroup, ngrp = (nslab + kArriveGroup - 1) / kArriveGroup;
@@ -585,12 +601,14 @@ __device__ __forceinline__ void decode_scan_slab(const KDims& d, int b, int slab
 // sequence (decode_scan_slab); the completing workgroup of a sequence selects.
 __global__ __launch_bounds__(256) void k_decode_scan_mfma(
     KDims d, const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ keys,
-    const int* __restrict__ t0, float* fscore, float* cscore, int* cnt, int* I, int* top_blk, int* path) {
+    const int* __restrict__ t0, float* fscore, float* cscore, int* cnt, int* hint, int* I, int* top_blk,
+    int* path) {
   __shared__ ScanSlabSmem sm;
-  args_now(d, q_idx, w, keys, t0, fscore, cscore, cnt, I, top_blk, path);
+  args_now(d, q_idx, w, keys, t0, fscore, cscore, cnt, hint, I, top_blk, path);
   const int b = blockIdx.y;
   decode_scan_slab(
-      d, b, blockIdx.x, (gridDim.x + kArriveGroup - 1) / kArriveGroup, q_idx, w, keys, t0, fscore, cscore, cnt, sm,
+      d, b, blockIdx.x, (gridDim.x + kArriveGroup - 1) / kArriveGroup, q_idx, w, keys, t0, fscore, cscore, cnt, hint,
+      sm,
       [&](const SeqInfo& si) { write_unscored(d, si, b, I, top_blk, path); },
       [&](const SeqInfo& si) {
         decode_select_wg(d, si, b, fscore + (size_t)b * d.Np_cap, cscore + (size_t)b * d.nb_cap, I, top_blk, path,
@@ -972,7 +990,7 @@ __global__ __launch_bounds__(256) void k_decode_step(KDims d, int nslab, int nps
     const int b = x / nslab;
     decode_scan_slab(
         d, b, x - b * nslab, (nslab + kArriveGroup - 1) / kArriveGroup, q_idx, w, keys, t0, fscore, cscore, cnt,
-        sm.scan, [&](const SeqInfo& si) { step_unscored(d, si, b, nps, I, top_blk, path, sy); },
+        nullptr, sm.scan, [&](const SeqInfo& si) { step_unscored(d, si, b, nps, I, top_blk, path, sy); },
         [&](const SeqInfo& si) {
           step_select_wg(d, si, b, nps, fscore + (size_t)b * d.Np_cap, cscore + (size_t)b * d.nb_cap, I, top_blk,
                          path, sm.scan.sel, sy);
@@ -2017,16 +2035,34 @@ constexpr int kTkNT = 1024, kTkR = 32, kTkBins = 2048, kTkCand = 1024;
 
 struct TopkRegSmem {
   float row[kTkNT * kTkR];  // the row, staged: thread t's 32 scores, 16-byte pieces XOR-swizzled
-  uint32_t hist[kTkBins];
-  float cand_s[kTkCand];
-  int cand_i[kTkCand];
+  union {
+    struct {
+      uint32_t hist[kTkBins];
+      float cand_s[kTkCand];
+      int cand_i[kTkCand];
+    };
+    uint32_t h12[4096];  // hinted path: histogram of 12 key bits
+  };
   uint32_t wsum[16];
   float red[3][16];
   int info[8];
+  uint32_t hint[kHintBins];  // hinted path: the scan's coarse bin counts, summed over copies
+  uint32_t few[64];          // hinted path: the keys under the k-th key's top 20 bits
 };
+// Scores of the k-th key's coarse bin ranked in LDS, in the row's place
+// (hinted path).
+constexpr int kHintCand = kTkNT * kTkR;
 
 // Rows of 8193..32768 scores, one workgroup per row, thread t holding the 32
 // consecutive scores 32t .. 32t+31 in registers.
+//  0. with the decode scan's coarse bin counts (hint): their sum must be the
+//     row's score count, and they name the bin S (top 8 key bits) holding
+//     the k-th key; one pass of two float compares per score counts the
+//     entries above S and in S (the row's own counts decide), S's scores go
+//     to LDS, a 12-bit histogram of them narrows to 20 key bits, and the few
+//     entries under those are ranked by one wave (a second 12-bit round if
+//     more than 64); ties of the k-th key are taken lowest index first.  Any
+//     check that fails leaves the row to steps 1-3;
 //  1. range [lo, hi] of the real scores (masked ones are -1e30) and their count;
 //  2. fewer than k real scores: all of them plus the lowest-index masked ones;
 //  3. otherwise the k-th score: a histogram of one sample per thread (indices
@@ -2042,11 +2078,47 @@ struct TopkRegSmem {
 //     each thread writes its own ids.
 __global__ __launch_bounds__(kTkNT) void k_topk_rows_reg(KDims d, const float* __restrict__ scores,
                                                          const int* __restrict__ t0, int* __restrict__ I,
-                                                         int* __restrict__ path) {
+                                                         int* __restrict__ path, int* __restrict__ hint) {
   __shared__ TopkRegSmem sm;
   const int b = blockIdx.y, j = blockIdx.x;
   const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
-  const SeqInfo si = seq_info(d, t0[b]);
+  const int t0b = t0[b];  // requested first, needed once the row's loads are out
+  const float* srow = scores + ((size_t)b * d.L + j) * d.Np_cap;
+  const bool staged = (d.Np_cap & 3) == 0;
+  if (staged) {
+    // The row goes global -> LDS in coalesced 1 KiB pieces (wave w moves
+    // pieces w, w+16, ...; piece p = threads 8p .. 8p+7), the whole buffer
+    // row before its length is known.  LDS position l of a piece holds the 16
+    // bytes at chunk (l % 8) ^ (l / 8) of thread 8p + l / 8, so each thread's
+    // eight 16-byte reads below hit distinct banks.
+    const uint32_t row_lds = lds_addr(sm.row);
+    const int lr = lane >> 3, lc = (lane & 7) ^ lr;
+    for (int pc = wv; pc < kTkNT / 8; pc += kTkNT / 64)
+      if (pc * 8 * kTkR < d.Np_cap) {
+        const int src = min(pc * 8 * kTkR + lr * kTkR + lc * 4, d.Np_cap - 4);
+        g2lds16(srow + src, row_lds + pc * 1024);
+      }
+  }
+  // The scan's coarse bin counts (one query row per sequence): four lanes per
+  // bin read two copies each, requested behind the row's loads; summed into
+  // sm.hint once the row is in, and cleared for the next scan at the end.
+  // Plain loads and stores: the kernel boundaries order them with the scans'
+  // device-scope adds.
+  int* hp0 = hint ? hint + hint_slot(b, tid & 3, tid >> 2) : nullptr;
+  int* hp1 = hint ? hint + hint_slot(b, (tid & 3) + 4, tid >> 2) : nullptr;
+  int hv0 = 0, hv1 = 0;
+  if (hint) {
+    hv0 = *hp0;
+    hv1 = *hp1;
+    for (int i = tid; i < 4096; i += kTkNT) sm.h12[i] = 0;  // ordered before any add by later barriers
+  }
+  auto clear_hint = [&] {
+    if (hint) {
+      *hp0 = 0;
+      *hp1 = 0;
+    }
+  };
+  const SeqInfo si = seq_info(d, t0b);
   int* Irow = I + ((size_t)b * d.L + j) * d.topk;
   const bool act = flat_active(d, si);
   if (d.force_path == PATH_FLAT) {
@@ -2058,27 +2130,26 @@ __global__ __launch_bounds__(kTkNT) void k_topk_rows_reg(KDims d, const float* _
     for (int i = tid; i < d.topk; i += kTkNT)
       if (i >= si.k) Irow[i] = -1;
   }
-  if (!act) return;
+  if (!act) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0: the row's LDS writes have landed
+    clear_hint();
+    return;
+  }
   const int n = si.Np, k = si.k;
   const int i0 = kTkR * tid;  // index of v[0]
-  const float* srow = scores + ((size_t)b * d.L + j) * d.Np_cap;
   // absent entries (index >= n) take -inf: below every real or masked score
   float v[kTkR];
-  if ((d.Np_cap & 3) == 0) {
-    // The row goes global -> LDS in coalesced 1 KiB pieces (wave w moves
-    // pieces w, w+16, ...; piece p = threads 8p .. 8p+7).  LDS position l of
-    // a piece holds the 16 bytes at chunk (l % 8) ^ (l / 8) of thread
-    // 8p + l / 8, so each thread's eight 16-byte reads below hit distinct
-    // banks.  Pieces past the row's end are not fetched (their scores are
-    // absent).
-    const uint32_t row_lds = lds_addr(sm.row);
-    const int lr = lane >> 3, lc = (lane & 7) ^ lr;
-    for (int pc = wv; pc < kTkNT / 8; pc += kTkNT / 64)
-      if (pc * 8 * kTkR < n) {
-        const int src = min(pc * 8 * kTkR + lr * kTkR + lc * 4, d.Np_cap - 4);
-        g2lds16(srow + src, row_lds + pc * 1024);
-      }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0
+  // the counts summed over copies into sm.hint (published by the barrier
+  // after the row's loads, or the one below)
+  auto sum_hint = [&] {
+    uint32_t h = (uint32_t)(hv0 + hv1);
+    h += __shfl_xor(h, 1);
+    h += __shfl_xor(h, 2);
+    if ((tid & 3) == 0) sm.hint[tid >> 2] = h;
+  };
+  if (staged) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0 (the counts too)
+    if (hint) sum_hint();
     __syncthreads();
     const float* mine = sm.row + (tid >> 3) * 8 * kTkR + (tid & 7) * kTkR;
 #pragma unroll
@@ -2092,42 +2163,15 @@ __global__ __launch_bounds__(kTkNT) void k_topk_rows_reg(KDims d, const float* _
   } else {
 #pragma unroll
     for (int q = 0; q < kTkR; ++q) v[q] = i0 + q < n ? srow[i0 + q] : -INFINITY;
+    if (hint) {
+      sum_hint();
+      __syncthreads();
+    }
   }
-  // 1. range of the real scores, count of masked ones
-  float lo = INFINITY, hi = -INFINITY;
-  int nmask = 0;
-#pragma unroll
-  for (int q = 0; q < kTkR; ++q) {
-    const float x = v[q];
-    const bool real = x > -1e29f;
-    nmask += (!real && x != -INFINITY) ? 1 : 0;
-    lo = real ? fminf(lo, x) : lo;
-    hi = real ? fmaxf(hi, x) : hi;
-  }
-  lo = wave_min(lo);
-  hi = wave_max(hi);
-  nmask = wave_sum_i(nmask);
-  if (lane == 0) {
-    sm.red[0][wv] = lo;
-    sm.red[1][wv] = hi;
-    sm.red[2][wv] = (float)nmask;
-  }
-  for (int i = tid; i < kTkBins; i += kTkNT) sm.hist[i] = 0;
-  __syncthreads();
-  lo = INFINITY;
-  hi = -INFINITY;
-  nmask = 0;
-#pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    lo = fminf(lo, sm.red[0][u]);
-    hi = fmaxf(hi, sm.red[1][u]);
-    nmask += (int)sm.red[2][u];
-  }
-  const int nreal = n - nmask;
   // the selection: scores with key > kthr, and those with key == kthr at
   // index <= ithr
-  uint32_t kthr;
-  int ithr;
+  uint32_t kthr = 0;
+  int ithr = 0;
   // index of the r-th (1-based) entry, in index order, with pred true
   auto rth_index = [&](int r, auto pred) {
     uint32_t m = 0;
@@ -2145,166 +2189,342 @@ __global__ __launch_bounds__(kTkNT) void k_topk_rows_reg(KDims d, const float* _
     __syncthreads();
     return res;
   };
-  if (nreal < k) {
-    // every real score, then the lowest-index masked entries
-    kthr = score_key(kNeg);
-    ithr = rth_index(k - nreal, [&](int q) { return v[q] <= -1e29f && v[q] != -INFINITY; });
-  } else {
-    float blo = lo, bhi = hi;
-    int need = k;  // entries still to take inside [blo, bhi]
-    bool done = false;
-    kthr = 0;
-    ithr = 0;
-    auto bins_of = [&](float rlo, float rhi, float& scale) {
-      scale = (float)kTkBins / (rhi - rlo) * 0.999999f;
-    };
-    // the bin holding the r-th entry from the top of hist: (bin, entries above
-    // it, entries in it); hist is left cleared (each thread clears the bins it
-    // read; the scan's barriers order that before any later add).  info[0..2]
-    // are written again only past further barriers.
-    auto find_bin = [&](int r, int& T, int& above_T, int& in_T) {
-      const int b0 = kTkBins - 1 - 2 * tid, b1 = kTkBins - 2 - 2 * tid;
-      const uint32_t h0 = sm.hist[b0], h1 = sm.hist[b1];
-      sm.hist[b0] = 0;
-      sm.hist[b1] = 0;
-      uint32_t tot;
-      const uint32_t above = block_excl_scan<kTkNT>(h0 + h1, sm.wsum, &tot);
-      if (above < (uint32_t)r && above + h0 + h1 >= (uint32_t)r) {
-        const bool first = above + h0 >= (uint32_t)r;
-        sm.info[0] = first ? b0 : b1;
-        sm.info[1] = (int)(first ? above : above + h0);
-        sm.info[2] = (int)(first ? h0 : h1);
-      }
-      __syncthreads();
-      T = sm.info[0];
-      above_T = sm.info[1];
-      in_T = sm.info[2];
-    };
-    if (hi > lo) {
-      // 3a. bracket the k-th score with one sample per thread: one scan of the
-      // sample histogram gives the sample count (its total) and the bins of
-      // both ends of the bracket; the histogram is cleared as it is read.
-      float scale;
-      bins_of(lo, hi, scale);
-      const float x0 = v[0];
-      if (x0 > -1e29f) atomicAdd(&sm.hist[min(kTkBins - 1, (int)((x0 - lo) * scale))], 1u);
-      __syncthreads();
-      const int b0 = kTkBins - 1 - 2 * tid, b1 = kTkBins - 2 - 2 * tid;
-      const uint32_t h0 = sm.hist[b0], h1 = sm.hist[b1];
-      sm.hist[b0] = 0;
-      sm.hist[b1] = 0;
-      uint32_t ns_u;
-      const uint32_t above = block_excl_scan<kTkNT>(h0 + h1, sm.wsum, &ns_u);
-      const int ns = (int)ns_u;
-      const float target = (float)k * (float)ns / (float)nreal;
-      const float margin = 3.f * sqrtf(fmaxf(target, 1.f)) + 4.f;
-      const int r_hi = max(1, (int)(target - margin)), r_lo = min(ns, (int)ceilf(target + margin));
-      if (ns > 0 && r_hi <= r_lo) {  // uniform
-        // the bin holding the r-th sample from the top, for r = r_hi and r_lo
-        auto locate = [&](int r, int slot) {
-          if (above < (uint32_t)r && above + h0 + h1 >= (uint32_t)r) sm.info[slot] = above + h0 >= (uint32_t)r ? b0 : b1;
-        };
-        locate(r_hi, 0);
-        locate(r_lo, 1);
-        __syncthreads();
-        const int Tt = sm.info[0], Tb = sm.info[1];
-        const float clo = Tb == 0 ? lo : fmaxf(lo, lo + (float)Tb / scale);
-        const float chi = Tt == kTkBins - 1 ? hi : fminf(hi, lo + (float)(Tt + 1) / scale);
-        // both counts in one sum: each is at most 32768, below 2^16
-        uint32_t cnt = 0;
+  bool have = false;      // kthr / ithr known
+  bool all_ties = false;  // every entry with key kthr is selected
+  if (hint) {
+    // 0. the scan's bin counts name the coarse bin S (top 8 key bits) of the
+    // k-th key; the row's own counts check it (the hint only steers).
+    // Every wave finds S alone: lane l holds bins 255-4l .. 252-4l
+    uint32_t hb[4], s4 = 0;
 #pragma unroll
-        for (int q = 0; q < kTkR; ++q) {
-          cnt += v[q] > chi ? 1u : 0u;
-          cnt += (v[q] >= clo && v[q] <= chi) ? 0x10000u : 0u;
+    for (int u = 0; u < 4; ++u) {
+      hb[u] = sm.hint[kHintBins - 1 - 4 * lane - u];
+      s4 += hb[u];
+    }
+    const uint32_t inc = wave_incl_scan(s4);
+    const uint32_t htot = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+    int S = -1;
+    if (htot == (uint32_t)n && k >= 1) {  // then exactly one lane holds the k-th
+      int Sl = -1;
+      uint32_t acc = inc - s4;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (acc < (uint32_t)k && acc + hb[u] >= (uint32_t)k) Sl = kHintBins - 1 - 4 * lane - u;
+        acc += hb[u];
+      }
+      const uint64_t hit = __ballot(Sl >= 0);
+      if (hit) S = __builtin_amdgcn_readlane(Sl, (int)__builtin_ctzll(hit));
+    }
+    // bin 0 holds -inf and NaN keys only: left to the exact path
+    if (S >= 1) {
+      // key >= (S << 24) <=> score >= flo and key >= ((S + 1) << 24) <=>
+      // score >= fhi (the key order is the float order; no key lies past
+      // bin 255)
+      const float flo = score_of_key((uint32_t)S << 24);
+      const float fhi = S == kHintBins - 1 ? __builtin_nanf("") : score_of_key((uint32_t)(S + 1) << 24);
+      // entries at or above S (low half) and above S (high half): each <= 32768
+      uint32_t c = 0;
+#pragma unroll
+      for (int q = 0; q < kTkR; ++q) {
+        c += v[q] >= fhi ? 0x10000u : 0u;
+        c += v[q] >= flo ? 1u : 0u;
+      }
+      uint32_t ctot;
+      const uint32_t cex = block_excl_scan<kTkNT>(c, sm.wsum, &ctot);
+      const int n_above = (int)(ctot >> 16), n_in = (int)(ctot & 0xFFFFu) - n_above;
+      if (n_above < k && n_above + n_in >= k) {  // uniform: S holds the k-th key
+        // S's scores into LDS (the row's copy there is no longer read: every
+        // thread loaded its scores before the scan's barriers), then the
+        // 4096-bin histogram of their key bits 23..12
+        float* cf = sm.row;
+        int pos = (int)(cex & 0xFFFFu) - (int)(cex >> 16);
+#pragma unroll
+        for (int q = 0; q < kTkR; ++q)
+          if (v[q] >= flo && !(v[q] >= fhi)) cf[pos++] = v[q];
+        if (tid == 0) sm.info[3] = 0;
+        __syncthreads();
+        for (int i = tid; i < n_in; i += kTkNT) atomicAdd(&sm.h12[(score_key(cf[i]) >> 12) & 4095u], 1u);
+        __syncthreads();
+        int r = k - n_above;  // rank of the k-th key among S's entries, from 1
+        // the bin of h12 holding the r-th entry from the top: thread t reads
+        // (and clears) bins 4095-4t .. 4092-4t; (bin, entries above it,
+        // entries in it) come back through info[slot .. slot+2]
+        auto find12 = [&](int slot, int& T, int& above, int& m) {
+          const int top = 4095 - 4 * tid;
+          uint32_t hx[4], sx = 0;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            hx[u] = sm.h12[top - u];
+            sm.h12[top - u] = 0;
+            sx += hx[u];
+          }
+          uint32_t tx;
+          const uint32_t ax = block_excl_scan<kTkNT>(sx, sm.wsum, &tx);
+          if (ax < (uint32_t)r && ax + sx >= (uint32_t)r) {
+            uint32_t acc = ax;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              if (acc < (uint32_t)r && acc + hx[u] >= (uint32_t)r) {
+                sm.info[slot] = top - u;
+                sm.info[slot + 1] = (int)acc;
+                sm.info[slot + 2] = (int)hx[u];
+              }
+              acc += hx[u];
+            }
+          }
+          __syncthreads();
+          T = sm.info[slot];
+          above = sm.info[slot + 1];
+          m = sm.info[slot + 2];
+        };
+        int T, above, m;
+        find12(0, T, above, m);
+        r -= above;
+        const uint32_t pre = ((uint32_t)S << 12) | (uint32_t)T;  // top 20 bits of the k-th key
+        uint32_t kt;
+        int mt;  // entries with key kt; the r lowest-index ones are taken
+        if (m <= 64) {
+          // the few entries under pre, ranked by one wave
+          for (int i = tid; i < n_in; i += kTkNT) {
+            const uint32_t kk = score_key(cf[i]);
+            if ((kk >> 12) == pre) sm.few[atomicAdd(&sm.info[3], 1)] = kk;
+          }
+          __syncthreads();
+          if (wv == 0) {
+            const uint32_t x0 = lane < m ? sm.few[lane] : 0u;
+            int gt = 0, ge = 0;
+            for (int u = 0; u < m; ++u) {
+              const uint32_t x = sm.few[u];
+              gt += x > x0 ? 1 : 0;
+              ge += x >= x0 ? 1 : 0;
+            }
+            if (lane < m && gt < r && ge >= r) {  // every such lane holds the same key
+              sm.info[4] = (int)x0;
+              sm.info[5] = r - gt;
+              sm.info[6] = ge - gt;
+            }
+          }
+          __syncthreads();
+          kt = (uint32_t)sm.info[4];
+          r = sm.info[5];
+          mt = sm.info[6];
+        } else {
+          // many entries share the top 20 bits: one more 12-bit round
+          for (int i = tid; i < n_in; i += kTkNT) {
+            const uint32_t kk = score_key(cf[i]);
+            if ((kk >> 12) == pre) atomicAdd(&sm.h12[kk & 4095u], 1u);
+          }
+          __syncthreads();
+          int U;
+          find12(4, U, above, mt);
+          kt = (pre << 12) | (uint32_t)U;
+          r -= above;
         }
-        uint32_t both;
-        block_excl_scan<kTkNT>(cnt, sm.wsum, &both);  // (its barriers also order the reads of info)
-        const int n_above = (int)(both & 0xFFFFu), n_in = (int)(both >> 16);
-        if (n_above < k && n_above + n_in >= k && chi > clo) {
-          blo = clo;
-          bhi = chi;
-          need = k - n_above;
-        }
+        kthr = kt;
+        all_ties = r == mt;
+        ithr = all_ties ? n : rth_index(r, [&](int q) { return i0 + q < n && score_key(v[q]) == kt; });
+        have = true;
       }
     }
-    // 3b. exact histogram rounds inside [blo, bhi]
-    for (int round = 0; round < 4 && !done; ++round) {
-      if (!(bhi > blo)) {
-        // every remaining score equals blo: ties, lowest indices first
+  }
+  if (!have) {
+    // 1. range of the real scores, count of masked ones
+    float lo = INFINITY, hi = -INFINITY;
+    int nmask = 0;
+  #pragma unroll
+    for (int q = 0; q < kTkR; ++q) {
+      const float x = v[q];
+      const bool real = x > -1e29f;
+      nmask += (!real && x != -INFINITY) ? 1 : 0;
+      lo = real ? fminf(lo, x) : lo;
+      hi = real ? fmaxf(hi, x) : hi;
+    }
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    nmask = wave_sum_i(nmask);
+    if (lane == 0) {
+      sm.red[0][wv] = lo;
+      sm.red[1][wv] = hi;
+      sm.red[2][wv] = (float)nmask;
+    }
+    for (int i = tid; i < kTkBins; i += kTkNT) sm.hist[i] = 0;
+    __syncthreads();
+    lo = INFINITY;
+    hi = -INFINITY;
+    nmask = 0;
+  #pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      lo = fminf(lo, sm.red[0][u]);
+      hi = fmaxf(hi, sm.red[1][u]);
+      nmask += (int)sm.red[2][u];
+    }
+    const int nreal = n - nmask;
+    if (nreal < k) {
+      // every real score, then the lowest-index masked entries
+      kthr = score_key(kNeg);
+      ithr = rth_index(k - nreal, [&](int q) { return v[q] <= -1e29f && v[q] != -INFINITY; });
+    } else {
+      float blo = lo, bhi = hi;
+      int need = k;  // entries still to take inside [blo, bhi]
+      bool done = false;
+      kthr = 0;
+      ithr = 0;
+      auto bins_of = [&](float rlo, float rhi, float& scale) {
+        scale = (float)kTkBins / (rhi - rlo) * 0.999999f;
+      };
+      // the bin holding the r-th entry from the top of hist: (bin, entries above
+      // it, entries in it); hist is left cleared (each thread clears the bins it
+      // read; the scan's barriers order that before any later add).  info[0..2]
+      // are written again only past further barriers.
+      auto find_bin = [&](int r, int& T, int& above_T, int& in_T) {
+        const int b0 = kTkBins - 1 - 2 * tid, b1 = kTkBins - 2 - 2 * tid;
+        const uint32_t h0 = sm.hist[b0], h1 = sm.hist[b1];
+        sm.hist[b0] = 0;
+        sm.hist[b1] = 0;
+        uint32_t tot;
+        const uint32_t above = block_excl_scan<kTkNT>(h0 + h1, sm.wsum, &tot);
+        if (above < (uint32_t)r && above + h0 + h1 >= (uint32_t)r) {
+          const bool first = above + h0 >= (uint32_t)r;
+          sm.info[0] = first ? b0 : b1;
+          sm.info[1] = (int)(first ? above : above + h0);
+          sm.info[2] = (int)(first ? h0 : h1);
+        }
+        __syncthreads();
+        T = sm.info[0];
+        above_T = sm.info[1];
+        in_T = sm.info[2];
+      };
+      if (hi > lo) {
+        // 3a. bracket the k-th score with one sample per thread: one scan of the
+        // sample histogram gives the sample count (its total) and the bins of
+        // both ends of the bracket; the histogram is cleared as it is read.
+        float scale;
+        bins_of(lo, hi, scale);
+        const float x0 = v[0];
+        if (x0 > -1e29f) atomicAdd(&sm.hist[min(kTkBins - 1, (int)((x0 - lo) * scale))], 1u);
+        __syncthreads();
+        const int b0 = kTkBins - 1 - 2 * tid, b1 = kTkBins - 2 - 2 * tid;
+        const uint32_t h0 = sm.hist[b0], h1 = sm.hist[b1];
+        sm.hist[b0] = 0;
+        sm.hist[b1] = 0;
+        uint32_t ns_u;
+        const uint32_t above = block_excl_scan<kTkNT>(h0 + h1, sm.wsum, &ns_u);
+        const int ns = (int)ns_u;
+        const float target = (float)k * (float)ns / (float)nreal;
+        const float margin = 3.f * sqrtf(fmaxf(target, 1.f)) + 4.f;
+        const int r_hi = max(1, (int)(target - margin)), r_lo = min(ns, (int)ceilf(target + margin));
+        if (ns > 0 && r_hi <= r_lo) {  // uniform
+          // the bin holding the r-th sample from the top, for r = r_hi and r_lo
+          auto locate = [&](int r, int slot) {
+            if (above < (uint32_t)r && above + h0 + h1 >= (uint32_t)r) sm.info[slot] = above + h0 >= (uint32_t)r ? b0 : b1;
+          };
+          locate(r_hi, 0);
+          locate(r_lo, 1);
+          __syncthreads();
+          const int Tt = sm.info[0], Tb = sm.info[1];
+          const float clo = Tb == 0 ? lo : fmaxf(lo, lo + (float)Tb / scale);
+          const float chi = Tt == kTkBins - 1 ? hi : fminf(hi, lo + (float)(Tt + 1) / scale);
+          // both counts in one sum: each is at most 32768, below 2^16
+          uint32_t cnt = 0;
+  #pragma unroll
+          for (int q = 0; q < kTkR; ++q) {
+            cnt += v[q] > chi ? 1u : 0u;
+            cnt += (v[q] >= clo && v[q] <= chi) ? 0x10000u : 0u;
+          }
+          uint32_t both;
+          block_excl_scan<kTkNT>(cnt, sm.wsum, &both);  // (its barriers also order the reads of info)
+          const int n_above = (int)(both & 0xFFFFu), n_in = (int)(both >> 16);
+          if (n_above < k && n_above + n_in >= k && chi > clo) {
+            blo = clo;
+            bhi = chi;
+            need = k - n_above;
+          }
+        }
+      }
+      // 3b. exact histogram rounds inside [blo, bhi]
+      for (int round = 0; round < 4 && !done; ++round) {
+        if (!(bhi > blo)) {
+          // every remaining score equals blo: ties, lowest indices first
+          kthr = score_key(blo);
+          const float tv = blo;
+          ithr = rth_index(need, [&](int q) { return v[q] == tv; });
+          done = true;
+          break;
+        }
+        float scale;
+        bins_of(blo, bhi, scale);
+        auto bin_of = [&](float x) {
+          return (x < blo || x > bhi) ? -1 : min(kTkBins - 1, (int)((x - blo) * scale));
+        };
+        // (hist is clear: set so before the rounds, and by find_bin after each)
+  #pragma unroll
+        for (int q = 0; q < kTkR; ++q) {
+          const int bn = bin_of(v[q]);
+          if (bn >= 0) atomicAdd(&sm.hist[bn], 1u);
+        }
+        if (tid == 0) sm.info[3] = 0;
+        __syncthreads();
+        int T, above_T, mcnt;
+        find_bin(need, T, above_T, mcnt);
+        need -= above_T;
+        if (mcnt > kTkCand) {
+          // crowded bin: its range becomes the next round's
+          const float nlo = blo + (float)T / scale, nhi = blo + (float)(T + 1) / scale;
+          // scores exactly at the float bin edges stay inside by the clamp of bin_of
+          blo = fmaxf(blo, nlo);
+          bhi = fminf(bhi, nhi);
+          continue;
+        }
+        // 3c. gather bin T's entries and rank them (score desc, index asc)
+  #pragma unroll
+        for (int q = 0; q < kTkR; ++q)
+          if (bin_of(v[q]) == T) {
+            const int slot = atomicAdd(&sm.info[3], 1);
+            sm.cand_s[slot] = v[q];
+            sm.cand_i[slot] = i0 + q;
+          }
+        __syncthreads();
+        for (int t = tid; t < mcnt; t += kTkNT) {
+          const uint32_t kt = score_key(sm.cand_s[t]);
+          const int it = sm.cand_i[t];
+          int rank = 0;
+          for (int u = 0; u < mcnt; ++u) {
+            const uint32_t ku = score_key(sm.cand_s[u]);
+            rank += (ku > kt) || (ku == kt && sm.cand_i[u] < it);
+          }
+          if (rank == need - 1) {
+            sm.info[4] = (int)kt;
+            sm.info[5] = it;
+          }
+        }
+        __syncthreads();
+        kthr = (uint32_t)sm.info[4];
+        ithr = sm.info[5];
+        done = true;
+      }
+      if (!done) {
+        // still crowded after four narrowings: the k-th score is the largest
+        // value whose count from the top reaches `need`; take its ties by index
+        // (exact: the crowded bin's scores are then a handful of equal values)
         kthr = score_key(blo);
         const float tv = blo;
         ithr = rth_index(need, [&](int q) { return v[q] == tv; });
-        done = true;
-        break;
       }
-      float scale;
-      bins_of(blo, bhi, scale);
-      auto bin_of = [&](float x) {
-        return (x < blo || x > bhi) ? -1 : min(kTkBins - 1, (int)((x - blo) * scale));
-      };
-      // (hist is clear: set so before the rounds, and by find_bin after each)
-#pragma unroll
-      for (int q = 0; q < kTkR; ++q) {
-        const int bn = bin_of(v[q]);
-        if (bn >= 0) atomicAdd(&sm.hist[bn], 1u);
-      }
-      if (tid == 0) sm.info[3] = 0;
-      __syncthreads();
-      int T, above_T, mcnt;
-      find_bin(need, T, above_T, mcnt);
-      need -= above_T;
-      if (mcnt > kTkCand) {
-        // crowded bin: its range becomes the next round's
-        const float nlo = blo + (float)T / scale, nhi = blo + (float)(T + 1) / scale;
-        // scores exactly at the float bin edges stay inside by the clamp of bin_of
-        blo = fmaxf(blo, nlo);
-        bhi = fminf(bhi, nhi);
-        continue;
-      }
-      // 3c. gather bin T's entries and rank them (score desc, index asc)
-#pragma unroll
-      for (int q = 0; q < kTkR; ++q)
-        if (bin_of(v[q]) == T) {
-          const int slot = atomicAdd(&sm.info[3], 1);
-          sm.cand_s[slot] = v[q];
-          sm.cand_i[slot] = i0 + q;
-        }
-      __syncthreads();
-      for (int t = tid; t < mcnt; t += kTkNT) {
-        const uint32_t kt = score_key(sm.cand_s[t]);
-        const int it = sm.cand_i[t];
-        int rank = 0;
-        for (int u = 0; u < mcnt; ++u) {
-          const uint32_t ku = score_key(sm.cand_s[u]);
-          rank += (ku > kt) || (ku == kt && sm.cand_i[u] < it);
-        }
-        if (rank == need - 1) {
-          sm.info[4] = (int)kt;
-          sm.info[5] = it;
-        }
-      }
-      __syncthreads();
-      kthr = (uint32_t)sm.info[4];
-      ithr = sm.info[5];
-      done = true;
-    }
-    if (!done) {
-      // still crowded after four narrowings: the k-th score is the largest
-      // value whose count from the top reaches `need`; take its ties by index
-      // (exact: the crowded bin's scores are then a handful of equal values)
-      kthr = score_key(blo);
-      const float tv = blo;
-      ithr = rth_index(need, [&](int q) { return v[q] == tv; });
     }
   }
   // 4. emission in index order (float compares: the key order is the float
   // order, with -0 == +0)
   const float tv = score_of_key(kthr);
   uint32_t m = 0;
+  if (all_ties) {
 #pragma unroll
-  for (int q = 0; q < kTkR; ++q) {
-    const bool sel = v[q] > tv || (v[q] == tv && i0 + q <= ithr);
-    m |= sel ? 1u << q : 0u;
+    for (int q = 0; q < kTkR; ++q) m |= v[q] >= tv ? 1u << q : 0u;
+  } else {
+#pragma unroll
+    for (int q = 0; q < kTkR; ++q) {
+      const bool sel = v[q] > tv || (v[q] == tv && i0 + q <= ithr);
+      m |= sel ? 1u << q : 0u;
+    }
   }
   uint32_t tot;
   int slot = (int)block_excl_scan<kTkNT>((uint32_t)__popc(m), sm.wsum, &tot);
@@ -2313,6 +2533,7 @@ __global__ __launch_bounds__(kTkNT) void k_topk_rows_reg(KDims d, const float* _
     Irow[slot++] = i0 + q;
     m &= m - 1;
   }
+  clear_hint();
 }
 
 // The dense fallback with the indexer switched off (HiSA issue, Implementation
@@ -2830,16 +3051,26 @@ bool decode_fused_ok(const KDims& d, bool bf16) {
          d.index_keep <= kRowKeep && !big_flat;
 }
 
+// The one-slab-per-workgroup scan runs (rather than the streaming one).
+static bool decode_scan_per_slab(const KDims& d) {
+  const long long slabs = (long long)cdiv(d.Np_cap, 64) * d.B;
+  return slabs <= 1024 || d.B > kStreamMaxB;
+}
+
+bool flat_hint_ok(const KDims& d, bool bf16) {
+  return d.L == 1 && idx_mfma_ok(d, bf16) && decode_scan_per_slab(d) && d.Np_cap > 8192 && d.Np_cap <= kTkNT * kTkR;
+}
+
 hipError_t launch_decode_scan(const KDims& d, bool bf16, const void* q_idx, const float* w, const void* keys,
                               const int* t0, float* fscore, float* cscore, int* cnt, int* I, int* top_blk,
-                              int* path, hipStream_t st) {
+                              int* path, hipStream_t st, int* hint) {
   const dim3 grid(cdiv(d.Np_cap, 64), d.B);
+  if (hint && !flat_hint_ok(d, bf16)) return hipErrorInvalidValue;
   if (idx_mfma_ok(d, bf16)) {
-    const long long slabs = (long long)cdiv(d.Np_cap, 64) * d.B;
-    if (slabs <= 1024 || d.B > kStreamMaxB) {
+    if (decode_scan_per_slab(d)) {
       // latency-bound: one workgroup per slab, rows requested before t0 is known
       hipLaunchKernelGGL(k_decode_scan_mfma, grid, dim3(256), 0, st, d, (const uint16_t*)q_idx, w,
-                         (const uint16_t*)keys, t0, fscore, cscore, cnt, I, top_blk, path);
+                         (const uint16_t*)keys, t0, fscore, cscore, cnt, hint, I, top_blk, path);
     } else {
       // bandwidth-bound: two resident workgroups per CU share the live slabs
       hipLaunchKernelGGL(k_decode_scan_stream, dim3(512), dim3(256), 0, st, d, (const uint16_t*)q_idx, w,
@@ -3001,10 +3232,12 @@ hipError_t launch_flat_scores(const KDims& d, bool bf16, const void* q_idx, cons
   return hipGetLastError();
 }
 
-hipError_t launch_topk_rows(const KDims& d, const float* scores, const int* t0, int* I, int* path, hipStream_t st) {
+hipError_t launch_topk_rows(const KDims& d, const float* scores, const int* t0, int* I, int* path, hipStream_t st,
+                            int* hint) {
+  if (hint && (d.L != 1 || d.Np_cap <= 8192 || d.Np_cap > kTkNT * kTkR)) return hipErrorInvalidValue;
   if (d.Np_cap > 8192 && d.Np_cap <= kTkNT * kTkR) {
     // long rows: scores held in registers of a 1024-thread workgroup
-    hipLaunchKernelGGL(k_topk_rows_reg, dim3(d.L, d.B), dim3(kTkNT), 0, st, d, scores, t0, I, path);
+    hipLaunchKernelGGL(k_topk_rows_reg, dim3(d.L, d.B), dim3(kTkNT), 0, st, d, scores, t0, I, path, hint);
     return hipGetLastError();
   }
   constexpr int kLdsCap = 32768;  // 128 KiB of keys

@@ -524,7 +524,6 @@ struct ScanSlabSmem {
   __align__(16) uint16_t s_q[64 * 128];
   __align__(16) float s_part[2][4][64];
   DecodeSelSmem sel;
-  uint32_t bins[kHintBins];  // the slab's scores per coarse key bin
   int flag;
 };
 
@@ -533,19 +532,19 @@ struct ScanSlabSmem {
 // parallel.  With cnt != NULL the selection is fused: select(si) runs in the
 // workgroup that completes the last group of the sequence's slabs, and
 // unscored(si) in wave 0 of slab 0 of a dense or invalid sequence.  ngmax:
-// slab-group counters per sequence.  With hint != NULL the slab's stored
-// scores are also counted per coarse key bin (the top 8 bits of score_key)
-// into the sequence's bin counts, copy slab % kHintCopies: one device-scope
-// add per bin the slab holds.
-template <class UnscoredF, class SelectF>
+// slab-group counters per sequence.  With HINT the slab's stored scores are
+// also counted per coarse key bin (the top 8 bits of score_key; bins: LDS of
+// kHintBins words) into the sequence's bin counts `hint`, copy slab %
+// kHintCopies: one device-scope add per bin the slab holds.
+template <bool HINT, class UnscoredF, class SelectF>
 __device__ __forceinline__ void decode_scan_slab(const KDims& d, int b, int slab, int ngmax,
                                                  const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
                                                  const uint16_t* __restrict__ keys, const int* __restrict__ t0,
-                                                 float* fscore, float* cscore, int* cnt, int* hint,
+                                                 float* fscore, float* cscore, int* cnt, int* hint, uint32_t* bins,
                                                  ScanSlabSmem& sm, UnscoredF unscored, SelectF select) {
   const int lane = lane_id(), g = lane >> 4;
   const int t0b = t0[b];  // requested first, needed after the rows arrive
-  if (hint) sm.bins[threadIdx.x] = 0;  // ordered before the adds by the barrier below
+  if constexpr (HINT) bins[threadIdx.x] = 0;  // ordered before the adds by the barrier below
   const uint16_t* kb = keys + (size_t)b * d.Np_cap * 128;
   bf16x8 kf[4];
   load_slab_rows(kb, slab, d.Np_cap - 1, kf);
@@ -575,11 +574,11 @@ __device__ __forceinline__ void decode_scan_slab(const KDims& d, int b, int slab
   const int nslab = (si.Np + 63) / 64;
   if (slab >= nslab) return;  // uniform over the workgroup
   const float v = score_slab(d, si, b, slab, 0, qf, wl, w_head, kf, fscore, cscore, sm.s_part);
-  if (hint) {
+  if constexpr (HINT) {
     const int r = slab * 64 + wave_id() * 16 + (lane & 15);
-    if (g == 0 && r < si.Np) atomicAdd(&sm.bins[score_key(v) >> 24], 1u);
+    if (g == 0 && r < si.Np) atomicAdd(&bins[score_key(v) >> 24], 1u);
     __syncthreads();
-    const uint32_t h = sm.bins[threadIdx.x];
+    const uint32_t h = bins[threadIdx.x];
     if (h)
       __hip_atomic_fetch_add(hint + hint_slot(b, slab % kHintCopies, threadIdx.x), (int)h, __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
@@ -599,16 +598,21 @@ __device__ __forceinline__ void decode_scan_slab(const KDims& d, int b, int slab
 
 // Latency-bound decode scan (few slabs): one workgroup per 64-row slab of one
 // sequence (decode_scan_slab); the completing workgroup of a sequence selects.
+// HINT: the flat decode's scan, which also counts its scores per coarse key
+// bin into `hint` (cnt is then NULL).
+template <bool HINT>
 __global__ __launch_bounds__(256) void k_decode_scan_mfma(
     KDims d, const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ keys,
     const int* __restrict__ t0, float* fscore, float* cscore, int* cnt, int* hint, int* I, int* top_blk,
     int* path) {
   __shared__ ScanSlabSmem sm;
-  args_now(d, q_idx, w, keys, t0, fscore, cscore, cnt, hint, I, top_blk, path);
+  __shared__ uint32_t s_bins[HINT ? kHintBins : 1];
+  args_now(d, q_idx, w, keys, t0, fscore, cscore, cnt, I, top_blk, path);
+  if constexpr (HINT) arg_now(hint);
   const int b = blockIdx.y;
-  decode_scan_slab(
+  decode_scan_slab<HINT>(
       d, b, blockIdx.x, (gridDim.x + kArriveGroup - 1) / kArriveGroup, q_idx, w, keys, t0, fscore, cscore, cnt, hint,
-      sm,
+      s_bins, sm,
       [&](const SeqInfo& si) { write_unscored(d, si, b, I, top_blk, path); },
       [&](const SeqInfo& si) {
         decode_select_wg(d, si, b, fscore + (size_t)b * d.Np_cap, cscore + (size_t)b * d.nb_cap, I, top_blk, path,
@@ -988,9 +992,9 @@ __global__ __launch_bounds__(256) void k_decode_step(KDims d, int nslab, int nps
   if (x < nscan) {
     args_now(d, q_idx, w, keys, t0, fscore, cscore, cnt, I, top_blk, path);
     const int b = x / nslab;
-    decode_scan_slab(
+    decode_scan_slab<false>(
         d, b, x - b * nslab, (nslab + kArriveGroup - 1) / kArriveGroup, q_idx, w, keys, t0, fscore, cscore, cnt,
-        nullptr, sm.scan, [&](const SeqInfo& si) { step_unscored(d, si, b, nps, I, top_blk, path, sy); },
+        nullptr, nullptr, sm.scan, [&](const SeqInfo& si) { step_unscored(d, si, b, nps, I, top_blk, path, sy); },
         [&](const SeqInfo& si) {
           step_select_wg(d, si, b, nps, fscore + (size_t)b * d.Np_cap, cscore + (size_t)b * d.nb_cap, I, top_blk,
                          path, sm.scan.sel, sy);
@@ -3069,8 +3073,12 @@ hipError_t launch_decode_scan(const KDims& d, bool bf16, const void* q_idx, cons
   if (idx_mfma_ok(d, bf16)) {
     if (decode_scan_per_slab(d)) {
       // latency-bound: one workgroup per slab, rows requested before t0 is known
-      hipLaunchKernelGGL(k_decode_scan_mfma, grid, dim3(256), 0, st, d, (const uint16_t*)q_idx, w,
-                         (const uint16_t*)keys, t0, fscore, cscore, cnt, hint, I, top_blk, path);
+      if (hint)
+        hipLaunchKernelGGL(k_decode_scan_mfma<true>, grid, dim3(256), 0, st, d, (const uint16_t*)q_idx, w,
+                           (const uint16_t*)keys, t0, fscore, cscore, cnt, hint, I, top_blk, path);
+      else
+        hipLaunchKernelGGL(k_decode_scan_mfma<false>, grid, dim3(256), 0, st, d, (const uint16_t*)q_idx, w,
+                           (const uint16_t*)keys, t0, fscore, cscore, cnt, hint, I, top_blk, path);
     } else {
       // bandwidth-bound: two resident workgroups per CU share the live slabs
       hipLaunchKernelGGL(k_decode_scan_stream, dim3(512), dim3(256), 0, st, d, (const uint16_t*)q_idx, w,

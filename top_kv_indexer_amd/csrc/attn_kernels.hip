@@ -12,7 +12,7 @@
 // registers) leaves every lane with 8 scores of one head, so the online
 // softmax runs in registers; O^T += V^T P^T takes V^T from LDS with the
 // gfx950 transposing LDS read and P^T straight from the S^T registers.  Split
-// partials (m, l, O) are merged by a second kernel.
+// partials (O / l in bf16, then m and l) are merged by a second kernel.
 #include <algorithm>
 #include <type_traits>
 

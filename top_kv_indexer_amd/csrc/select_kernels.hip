@@ -2053,9 +2053,6 @@ struct TopkRegSmem {
   uint32_t hint[kHintBins];  // hinted path: the scan's coarse bin counts, summed over copies
   uint32_t few[64];          // hinted path: the keys under the k-th key's top 20 bits
 };
-// Scores of the k-th key's coarse bin ranked in LDS, in the row's place
-// (hinted path).
-constexpr int kHintCand = kTkNT * kTkR;
 
 // Rows of 8193..32768 scores, one workgroup per row, thread t holding the 32
 // consecutive scores 32t .. 32t+31 in registers.
@@ -2106,7 +2103,7 @@ __global__ __launch_bounds__(kTkNT) void k_topk_rows_reg(KDims d, const float* _
   // The scan's coarse bin counts (one query row per sequence): four lanes per
   // bin read two copies each, requested behind the row's loads; summed into
   // sm.hint once the row is in, and cleared for the next scan at the end.
-  // Plain loads and stores: the kernel boundaries order them with the scans'
+  // Plain loads and stores: the kernel boundaries order them with the scan's
   // device-scope adds.
   int* hp0 = hint ? hint + hint_slot(b, tid & 3, tid >> 2) : nullptr;
   int* hp1 = hint ? hint + hint_slot(b, (tid & 3) + 4, tid >> 2) : nullptr;

@@ -217,15 +217,6 @@ int hisa_select_prefill(const hisa_dims* d, const void* q_idx, const float* w, c
  * score every visible row, -1e30 for p >= V(t0+j), keep the top
  * k = min(topk, Np) ids.  Ignores mode and index_block.  ratio = 1 gives the
  * per-token DSA indexer.
- * Workspace: at decode (L = 1) with a bf16 64 x 128 indexer and
- * 8192 < Np_cap <= 32768 (and B * ceil(Np_cap / 64) <= 1024 or B > 1024),
- * its first B * 8 KiB hold per-sequence counts of the scores in 256 coarse
- * key bins (8 copies), which the scan adds up and the top-k reads as a hint
- * and clears.
- * Zero them once (zero-fill the workspace after allocating it); every call
- * leaves them zero.  Nonzero counts never change I_out, but they send that
- * call's top-k to its slower exact path.  Two calls that share a workspace
- * must not run at the same time; calls on one stream are ordered.
  *   I_out (B, L, topk) int32. */
 int flat_topk_select(const hisa_dims* d, const void* q_idx, const float* w, const void* keys,
                      const int32_t* t0, int32_t* I_out, void* ws, size_t ws_bytes, void* stream);

@@ -53,10 +53,8 @@ def test_workspace_sizes(lib):
     assert hisa.workspace_bytes(hisa.OP_SELECT_DECODE, dims(B=32, Np_cap=32768)) == (
         32 * 33 * 64 + 32 * 32768 * 4 + 32 * 512 * 4)
     assert hisa.workspace_bytes(hisa.OP_FLAT_TOPK, dims(L=4, Np_cap=1000)) == ((4 * 1000 * 4 + 255) // 256) * 256
-    # flat decode over 8193..32768 keys: the scan's coarse bin counts first
-    # (8 copies x 256 bins per sequence), then the scores
-    assert hisa.workspace_bytes(hisa.OP_FLAT_TOPK, dims(B=2, ratio=1, topk=2048, Np_cap=32768)) == (
-        2 * 8 * 256 * 4 + 2 * 32768 * 4)
+    # the flat top-k needs the scores only, at decode as in prefill
+    assert hisa.workspace_bytes(hisa.OP_FLAT_TOPK, dims(B=2, ratio=1, topk=2048, Np_cap=32768)) == 2 * 32768 * 4
     assert hisa.workspace_bytes(hisa.OP_FLAT_TOPK, dims(B=2, L=2, ratio=1, topk=2048, Np_cap=32768)) == 4 * 32768 * 4
     assert hisa.workspace_bytes(hisa.OP_FLAT_TOPK, dims(ratio=1, Np_cap=8192)) == 8192 * 4
     assert hisa.workspace_bytes(hisa.OP_FLAT_TOPK, dims(ratio=1, Np_cap=32768, idx_dtype=hisa.F32)) == 32768 * 4

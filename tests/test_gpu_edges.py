@@ -4,7 +4,7 @@ lists and HiSA on a long ratio-128 stream), a ratio that is not a power of
 two, value rows narrower than key rows (Dv < Dk), HiSA blocks of 8, 16 and 32
 rows on both decode scans, a 1024-sequence streaming decode scan, the dense
 fallback switch, a decode step replayed from a captured HIP graph, and the
-flat decode top-k's coarse bin counts (hint) in every state they can be in."""
+flat top-k's coarse-bin path (including samples that mislead it)."""
 import sys
 
 import numpy as np
@@ -375,63 +375,40 @@ def test_flat_topk_long_rows_decode(hisa, case):
             np.testing.assert_array_equal(v, np.arange(1000, 3048))
 
 
-# ---------------------------------------------------------------- coarse bin counts of the flat decode
 
-def hint_counts(ws, B):
-    """The flat decode's bin-count region: B x 2048 int32 counts."""
-    return ws[: B * 8 * 256 * 4].view(torch.int32).view(B, 2048)
+# ---------------------------------------------------------------- the flat top-k's coarse-bin path
 
-
-def hint_index(copy, kbin):
-    """Where copy `copy` of coarse bin `kbin` sits in a sequence's counts: the
-    16 counts of one 64-byte line are one copy's bins 16 apart."""
-    return (copy * 16 + (kbin & 15)) * 16 + (kbin >> 4)
-
-
-@pytest.mark.parametrize("case", ["ragged_b2", "misleading", "garbage", "one_coarse_bin"])
-def test_flat_decode_bin_hint(hisa, case):
-    # The flat decode scan (rows of 8193..32768 keys) counts its scores per
-    # coarse key bin at the start of the workspace, and the row top-k reads
-    # the counts as a hint, checks them against its own counts and clears
-    # them.  The ids must never depend on them: counts that add up to the row
-    # length but name the wrong bin, random garbage, and a row whose 32768
-    # scores are all equal (one coarse bin, more keys than the hinted path
-    # ranks in LDS) must all give the oracle's ids, as must a 9001-key row
-    # whose scores are all equal (ranked by the hinted path, ties by index).
-    # After every call the counts are zero and a repeated call is identical.
-    w = synth.DSA_DECODE.with_(name=f"dsa_decode_hint_{case}", B=2, t0=[32767, 9000], H=4, Dk=64, Dv=64)
+@pytest.mark.parametrize("case", ["ragged_b2", "sample_misleads", "one_coarse_bin"])
+def test_flat_topk_coarse_bin_path(hisa, case):
+    # Rows of 8193..32768 scores: the row top-k takes the coarse key bin (top
+    # 8 key bits) of the k-th key from one sample per thread (scores 0, 32,
+    # 64, ...), checks it with its own counts and moves it up or down (three
+    # tries) before falling back to the exact path.  A ragged batch (rows of
+    # 32768 and 9001 scores); samples that mislead (the best key copied onto
+    # 300 sampled rows of sequence 0, so the sample puts the k-th key in the
+    # top bin: the tries move down, then the exact path takes over); and rows
+    # whose scores are all equal (one coarse bin holds every key: 32768 and
+    # 9001 ties, the lowest 2048 ids kept).  A repeated call is identical.
+    w = synth.DSA_DECODE.with_(name=f"dsa_decode_coarse_{case}", B=2, t0=[32767, 9000], H=4, Dk=64, Dv=64)
     x, g = inputs(w, 77)
     x = dict(x)
     gk = g["keys"]
-    if case == "one_coarse_bin":
+    if case != "ragged_b2":
         keys = x["keys"].copy()
-        keys[0, :] = keys[0, 5]
-        keys[1, :] = keys[1, 7]
+        if case == "sample_misleads":
+            d0 = odims(w, x)
+            sc = oracle.scores_of(d0, x["q_idx"][0, 0], x["w"][0, 0], x["keys"][0], int(x["t0"][0]), 0,
+                                  np.arange(32768, dtype=np.int32))
+            keys[0, 0:9600:32] = x["keys"][0, int(np.argmax(sc))]
+        else:
+            keys[0, :] = keys[0, 5]
+            keys[1, :] = keys[1, 7]
         x["keys"] = keys
         gk = torch.from_numpy(keys).to("cuda").to(torch.bfloat16).contiguous()
-    d_call = hisa.selection_dims(g["q_idx"], gk, ratio=1, topk=w.topk, index_block=0, index_keep=1)
-    n = hisa.workspace_bytes(hisa.OP_FLAT_TOPK, d_call)
-    assert n == w.B * 8 * 256 * 4 + w.B * 32768 * 4
-    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
-    h = hint_counts(ws, w.B)
-    if case == "misleading":
-        # totals stay equal to the row lengths, but bin 255 (or 200) seems to hold the k-th key
-        h[0, hint_index(0, 255)] = 5000
-        h[0, hint_index(3, 0)] = -5000
-        h[1, hint_index(2, 200)] = 3000
-        h[1, hint_index(6, 17)] = -3000
-    elif case == "garbage":
-        gen = torch.Generator(device="cuda").manual_seed(5)
-        ws[: w.B * 8 * 256 * 4].copy_(torch.randint(0, 256, (w.B * 8 * 256 * 4,), dtype=torch.uint8,
-                                                     device="cuda", generator=gen))
+    say(f"[run] flat top-k, coarse-bin path: {case}")
+    I1 = hisa.flat_topk_select(g["q_idx"], g["w"], gk, g["t0"], ratio=1, topk=w.topk)
+    I2 = hisa.flat_topk_select(g["q_idx"], g["w"], gk, g["t0"], ratio=1, topk=w.topk)
     torch.cuda.synchronize()
-    say(f"[run] flat decode top-k with bin counts: {case}")
-    I1 = hisa.flat_topk_select(g["q_idx"], g["w"], gk, g["t0"], ratio=1, topk=w.topk, ws=ws)
-    torch.cuda.synchronize()
-    assert int(hint_counts(ws, w.B).abs().sum()) == 0
-    I2 = hisa.flat_topk_select(g["q_idx"], g["w"], gk, g["t0"], ratio=1, topk=w.topk, ws=ws)
-    torch.cuda.synchronize()
-    assert int(hint_counts(ws, w.B).abs().sum()) == 0
     assert torch.equal(I1, I2)
     d = odims(w, x)
     In = parity.to_np(I1)
@@ -443,3 +420,5 @@ def test_flat_decode_bin_hint(hisa, case):
         assert len(v) == w.topk and (np.diff(v) > 0).all()
         if case == "one_coarse_bin":
             np.testing.assert_array_equal(v, np.arange(w.topk))
+        if case == "sample_misleads" and b == 0:
+            assert set(range(0, 9600, 32)) <= set(v.tolist())  # the 300 copies of the best key are kept

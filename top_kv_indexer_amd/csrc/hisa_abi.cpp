@@ -127,7 +127,6 @@ int make_kdims(int op, const hisa_dims* d, KDims* k) {
 struct Layout {
   size_t total = 0;
   size_t rep = 0, rep3 = 0, cscore = 0, scores = 0, fscore = 0, partial = 0, cnt = 0, blk = 0;
-  size_t hint = 0;  // flat decode: the scan's coarse key-bin counts (flat_hint_ok)
   size_t sync = 0, sel = 0;  // decode step: its sync words, and the selection's part
   int splits = 1;
 };
@@ -214,8 +213,6 @@ Layout layout(int op, const hisa_dims* d, const KDims& k) {
       break;
     }
     case HISA_OP_FLAT_TOPK:
-      // the bin counts first: like the arrival counters, they rest at zero
-      if (hisa::flat_hint_ok(k, bf)) l.hint = take(l, hisa::flat_hint_ints(k) * sizeof(int));
       l.scores = take(l, B * L * d->Np_cap * sizeof(float));
       break;
     case HISA_OP_ATTENTION:
@@ -588,21 +585,17 @@ int flat_topk_select(const hisa_dims* d, const void* q_idx, const float* w, cons
   k.force_path = hisa::PATH_FLAT;
   float* scores = at<float>(ws, l.scores);
   hipError_t e;
-  // rows of 8193..32768 keys at decode: the scan also counts its scores per
-  // coarse key bin, which steers the row top-k
-  int* hint = hisa::flat_hint_ok(k, bf) ? at<int>(ws, l.hint) : nullptr;
   if (d->L == 1 && hisa::idx_mfma_ok(k, bf)) {
     // one query row per sequence: the decode key scan scores every row (its
     // per-sequence score rows are the (B, 1, Np_cap) layout of `scores`)
     e = timed("flat_scores", st, [&] {
-      return hisa::launch_decode_scan(k, bf, q_idx, w, keys, t0, scores, nullptr, nullptr, nullptr, nullptr, nullptr, st,
-                                      hint);
+      return hisa::launch_decode_scan(k, bf, q_idx, w, keys, t0, scores, nullptr, nullptr, nullptr, nullptr, nullptr, st);
     });
   } else {
     e = timed("flat_scores", st, [&] { return hisa::launch_flat_scores(k, bf, q_idx, w, keys, t0, scores, st); });
   }
   if (e != hipSuccess) return launch_fail(e, "flat scores");
-  e = timed("topk_rows", st, [&] { return hisa::launch_topk_rows(k, scores, t0, I_out, nullptr, st, hint); });
+  e = timed("topk_rows", st, [&] { return hisa::launch_topk_rows(k, scores, t0, I_out, nullptr, st); });
   if (e != hipSuccess) return launch_fail(e, "flat top-k");
   return HISA_OK;
 }

@@ -36,24 +36,9 @@ inline size_t decode_counter_ints(const KDims& d) {
   return (size_t)d.B * (1 + (slabs + 15) / 16) * kCntStride;
 }
 bool decode_fused_ok(const KDims& d, bool bf16);
-// Coarse key-bin counts from the flat decode scan to the row top-k (hint !=
-// NULL, flat_hint_ok): per sequence kHintCopies copies of kHintBins counts
-// (bin = top 8 bits of the order-preserving score key), flat_hint_ints(d)
-// ints in all.  The 16 counts on one 64-byte line are one copy's bins
-// 16 apart (32 octaves of score), so a slab adds to few of them and a line
-// sees about one add per slab of its copy (adds to one line are performed
-// one after another).  They must be zero before the scan; the top-k reads
-// them as a hint only (its own counts decide) and leaves them zero.
-constexpr int kHintBins = 256, kHintCopies = 8;
-inline size_t flat_hint_ints(const KDims& d) { return (size_t)d.B * kHintCopies * kHintBins; }
-__host__ __device__ inline size_t hint_slot(int b, int copy, int bin) {
-  return (size_t)b * kHintCopies * kHintBins + (size_t)(copy * 16 + (bin & 15)) * 16 + (bin >> 4);
-}
-bool flat_hint_ok(const KDims& d, bool bf16);
 hipError_t launch_decode_scan(const KDims& d, bool bf16, const void* q_idx, const float* w,
                               const void* keys, const int* t0, float* fscore, float* cscore,
-                              int* cnt, int* I, int* top_blk, int* path, hipStream_t st,
-                              int* hint = nullptr);
+                              int* cnt, int* I, int* top_blk, int* path, hipStream_t st);
 // The decode step (selection + sparse combine) of few sequences in one
 // launch up to the split partials, which launch_attention_merge (splits =
 // decode_step_splits) then combines: decode_step_ok (max_attn_wgs: attention
@@ -89,7 +74,7 @@ hipError_t launch_fine(const KDims& d, bool bf16, const void* q_idx, const float
 hipError_t launch_flat_scores(const KDims& d, bool bf16, const void* q_idx, const float* w,
                               const void* keys, const int* t0, float* scores, hipStream_t st);
 hipError_t launch_topk_rows(const KDims& d, const float* scores, const int* t0, int* I,
-                            int* path, hipStream_t st, int* hint = nullptr);
+                            int* path, hipStream_t st);
 // Selection on a caller-kept cache of f32 block means (B, nb_cap, D_i), one
 // query row (b, j) per grid row (decode, or a short verify chunk):
 // bf16 64 x 128 indexer, nb_cap <= 4096, index_keep <= 64 and

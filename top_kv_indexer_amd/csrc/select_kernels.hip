@@ -431,9 +431,8 @@ __device__ __forceinline__ void load_slab_rows(const uint16_t* kb, int slab, int
 // The block mean is linear, so q_h . rep_beta is the mean of D[h][row] over
 // the block's rows: blocks of up to 16 rows are summed inside the wave,
 // larger ones from per-wave partial sums exchanged through s_part[par].
-// Rows past Np are scored but never stored, as are blocks past nb.  Returns
-// the fine score of row slab*64 + 16*wave + (lane & 15) (lanes < 16 hold it).
-__device__ __forceinline__ float score_slab(const KDims& d, const SeqInfo& si, int b, int slab, int par,
+// Rows past Np are scored but never stored, as are blocks past nb.
+__device__ __forceinline__ void score_slab(const KDims& d, const SeqInfo& si, int b, int slab, int par,
                                            const bf16x8 (&qf)[4][4], const float (&wl)[4][4], float w_head,
                                            const bf16x8 (&kf)[4], float* fscore, float* cscore,
                                            float (*s_part)[4][64]) {
@@ -453,7 +452,7 @@ __device__ __forceinline__ float score_slab(const KDims& d, const SeqInfo& si, i
   v = sum_rows(v);
   const int r = slab * 64 + wv * 16 + c;
   if (g == 0 && r < si.Np) st_dev(fscore + (size_t)b * d.Np_cap + r, v);
-  if (si.path != PATH_HISA) return v;
+  if (si.path != PATH_HISA) return;
   const int bsz = d.index_block;
   const float inv_b = 1.f / (float)bsz;
   if (bsz <= 16) {
@@ -466,7 +465,7 @@ __device__ __forceinline__ float score_slab(const KDims& d, const SeqInfo& si, i
     cv = sum_rows(cv);
     const int beta = r / bsz;
     if (g == 0 && (c & (bsz - 1)) == 0 && beta < si.nb) st_dev(cscore + (size_t)b * d.nb_cap + beta, cv);
-    return v;
+    return;
   }
   // blocks of 32 or 64 rows: per-head sums over this wave's rows to LDS,
   // then wave j < 64 / bsz owns block j of the slab
@@ -486,7 +485,6 @@ __device__ __forceinline__ float score_slab(const KDims& d, const SeqInfo& si, i
     const int beta = (slab * 64) / bsz + wv;
     if (lane == 0 && beta < si.nb) st_dev(cscore + (size_t)b * d.nb_cap + beta, cv);
   }
-  return v;
 }
 
 // Adds n to a device-scope arrival counter that completes at `total`;
@@ -532,19 +530,15 @@ struct ScanSlabSmem {
 // parallel.  With cnt != NULL the selection is fused: select(si) runs in the
 // workgroup that completes the last group of the sequence's slabs, and
 // unscored(si) in wave 0 of slab 0 of a dense or invalid sequence.  ngmax:
-// slab-group counters per sequence.  With HINT the slab's stored scores are
-// also counted per coarse key bin (the top 8 bits of score_key; bins: LDS of
-// kHintBins words) into the sequence's bin counts `hint`, copy slab %
-// kHintCopies: one device-scope add per bin the slab holds.
-template <bool HINT, class UnscoredF, class SelectF>
+// slab-group counters per sequence.
+template <class UnscoredF, class SelectF>
 __device__ __forceinline__ void decode_scan_slab(const KDims& d, int b, int slab, int ngmax,
                                                  const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
                                                  const uint16_t* __restrict__ keys, const int* __restrict__ t0,
-                                                 float* fscore, float* cscore, int* cnt, int* hint, uint32_t* bins,
-                                                 ScanSlabSmem& sm, UnscoredF unscored, SelectF select) {
+                                                 float* fscore, float* cscore, int* cnt, ScanSlabSmem& sm,
+                                                 UnscoredF unscored, SelectF select) {
   const int lane = lane_id(), g = lane >> 4;
   const int t0b = t0[b];  // requested first, needed after the rows arrive
-  if constexpr (HINT) bins[threadIdx.x] = 0;  // ordered before the adds by the barrier below
   const uint16_t* kb = keys + (size_t)b * d.Np_cap * 128;
   bf16x8 kf[4];
   load_slab_rows(kb, slab, d.Np_cap - 1, kf);
@@ -573,16 +567,7 @@ __device__ __forceinline__ void decode_scan_slab(const KDims& d, int b, int slab
   }
   const int nslab = (si.Np + 63) / 64;
   if (slab >= nslab) return;  // uniform over the workgroup
-  const float v = score_slab(d, si, b, slab, 0, qf, wl, w_head, kf, fscore, cscore, sm.s_part);
-  if constexpr (HINT) {
-    const int r = slab * 64 + wave_id() * 16 + (lane & 15);
-    if (g == 0 && r < si.Np) atomicAdd(&bins[score_key(v) >> 24], 1u);
-    __syncthreads();
-    const uint32_t h = bins[threadIdx.x];
-    if (h)
-      __hip_atomic_fetch_add(hint + hint_slot(b, slab % kHintCopies, threadIdx.x), (int)h, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-  }
+  score_slab(d, si, b, slab, 0, qf, wl, w_head, kf, fscore, cscore, sm.s_part);
   if (!cnt) return;
   // cnt: B sequence counters, then B x ngmax group counters, kCntStride apart
   const int grp = slab / kArriveGroup, ngrp = (nslab + kArriveGroup - 1) / kArriveGroup;
@@ -598,21 +583,14 @@ __device__ __forceinline__ void decode_scan_slab(const KDims& d, int b, int slab
 
 // Latency-bound decode scan (few slabs): one workgroup per 64-row slab of one
 // sequence (decode_scan_slab); the completing workgroup of a sequence selects.
-// HINT: the flat decode's scan, which also counts its scores per coarse key
-// bin into `hint` (cnt is then NULL).
-template <bool HINT>
 __global__ __launch_bounds__(256) void k_decode_scan_mfma(
     KDims d, const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ keys,
-    const int* __restrict__ t0, float* fscore, float* cscore, int* cnt, int* hint, int* I, int* top_blk,
-    int* path) {
+    const int* __restrict__ t0, float* fscore, float* cscore, int* cnt, int* I, int* top_blk, int* path) {
   __shared__ ScanSlabSmem sm;
-  __shared__ uint32_t s_bins[HINT ? kHintBins : 1];
   args_now(d, q_idx, w, keys, t0, fscore, cscore, cnt, I, top_blk, path);
-  if constexpr (HINT) arg_now(hint);
   const int b = blockIdx.y;
-  decode_scan_slab<HINT>(
-      d, b, blockIdx.x, (gridDim.x + kArriveGroup - 1) / kArriveGroup, q_idx, w, keys, t0, fscore, cscore, cnt, hint,
-      s_bins, sm,
+  decode_scan_slab(
+      d, b, blockIdx.x, (gridDim.x + kArriveGroup - 1) / kArriveGroup, q_idx, w, keys, t0, fscore, cscore, cnt, sm,
       [&](const SeqInfo& si) { write_unscored(d, si, b, I, top_blk, path); },
       [&](const SeqInfo& si) {
         decode_select_wg(d, si, b, fscore + (size_t)b * d.Np_cap, cscore + (size_t)b * d.nb_cap, I, top_blk, path,
@@ -992,9 +970,9 @@ __global__ __launch_bounds__(256) void k_decode_step(KDims d, int nslab, int nps
   if (x < nscan) {
     args_now(d, q_idx, w, keys, t0, fscore, cscore, cnt, I, top_blk, path);
     const int b = x / nslab;
-    decode_scan_slab<false>(
+    decode_scan_slab(
         d, b, x - b * nslab, (nslab + kArriveGroup - 1) / kArriveGroup, q_idx, w, keys, t0, fscore, cscore, cnt,
-        nullptr, nullptr, sm.scan, [&](const SeqInfo& si) { step_unscored(d, si, b, nps, I, top_blk, path, sy); },
+        sm.scan, [&](const SeqInfo& si) { step_unscored(d, si, b, nps, I, top_blk, path, sy); },
         [&](const SeqInfo& si) {
           step_select_wg(d, si, b, nps, fscore + (size_t)b * d.Np_cap, cscore + (size_t)b * d.nb_cap, I, top_blk,
                          path, sm.scan.sel, sy);
@@ -2036,6 +2014,7 @@ __global__ __launch_bounds__(kTopkRowsThreads) void k_topk_rows(KDims d, int lds
 // Selected: key > kthr, or key == kthr and index <= ithr; emitted in index
 // order (ties at the threshold keep the lowest indices).
 constexpr int kTkNT = 1024, kTkR = 32, kTkBins = 2048, kTkCand = 1024;
+constexpr int kCoarseBins = 256;  // coarse key bins: the top 8 bits of score_key
 
 struct TopkRegSmem {
   float row[kTkNT * kTkR];  // the row, staged: thread t's 32 scores, 16-byte pieces XOR-swizzled
@@ -2045,25 +2024,26 @@ struct TopkRegSmem {
       float cand_s[kTkCand];
       int cand_i[kTkCand];
     };
-    uint32_t h12[4096];  // hinted path: histogram of 12 key bits
+    uint32_t h12[4096];  // coarse-bin path: histogram of 12 key bits
   };
   uint32_t wsum[16];
   float red[3][16];
   int info[8];
-  uint32_t hint[kHintBins];  // hinted path: the scan's coarse bin counts, summed over copies
-  uint32_t few[64];          // hinted path: the keys under the k-th key's top 20 bits
+  uint32_t coarse[kCoarseBins];  // coarse-bin path: the sample's counts per coarse key bin
+  uint32_t few[64];              // coarse-bin path: the keys under the k-th key's top 20 bits
 };
 
 // Rows of 8193..32768 scores, one workgroup per row, thread t holding the 32
 // consecutive scores 32t .. 32t+31 in registers.
-//  0. with the decode scan's coarse bin counts (hint): their sum must be the
-//     row's score count, and they name the bin S (top 8 key bits) holding
-//     the k-th key; one pass of two float compares per score counts the
-//     entries above S and in S (the row's own counts decide), S's scores go
-//     to LDS, a 12-bit histogram of them narrows to 20 key bits, and the few
-//     entries under those are ranked by one wave (a second 12-bit round if
-//     more than 64); ties of the k-th key are taken lowest index first.  Any
-//     check that fails leaves the row to steps 1-3;
+//  0. the coarse bin S (top 8 key bits) of the k-th key, first named by a
+//     histogram of one sample per thread (the bin of the sample at the
+//     scaled rank).  One pass of two float compares per score counts the
+//     entries above S and in S; these own counts decide, moving S one bin up
+//     or down (three tries).  S's scores go to LDS, a 12-bit histogram of
+//     them narrows to 20 key bits, and the few entries under those are
+//     ranked by one wave (a second 12-bit round if more than 64); ties of
+//     the k-th key are taken lowest index first.  If no try holds the k-th
+//     key the row goes to steps 1-3;
 //  1. range [lo, hi] of the real scores (masked ones are -1e30) and their count;
 //  2. fewer than k real scores: all of them plus the lowest-index masked ones;
 //  3. otherwise the k-th score: a histogram of one sample per thread (indices
@@ -2079,7 +2059,7 @@ struct TopkRegSmem {
 //     each thread writes its own ids.
 __global__ __launch_bounds__(kTkNT) void k_topk_rows_reg(KDims d, const float* __restrict__ scores,
                                                          const int* __restrict__ t0, int* __restrict__ I,
-                                                         int* __restrict__ path, int* __restrict__ hint) {
+                                                         int* __restrict__ path) {
   __shared__ TopkRegSmem sm;
   const int b = blockIdx.y, j = blockIdx.x;
   const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
@@ -2100,25 +2080,8 @@ __global__ __launch_bounds__(kTkNT) void k_topk_rows_reg(KDims d, const float* _
         g2lds16(srow + src, row_lds + pc * 1024);
       }
   }
-  // The scan's coarse bin counts (one query row per sequence): four lanes per
-  // bin read two copies each, requested behind the row's loads; summed into
-  // sm.hint once the row is in, and cleared for the next scan at the end.
-  // Plain loads and stores: the kernel boundaries order them with the scan's
-  // device-scope adds.
-  int* hp0 = hint ? hint + hint_slot(b, tid & 3, tid >> 2) : nullptr;
-  int* hp1 = hint ? hint + hint_slot(b, (tid & 3) + 4, tid >> 2) : nullptr;
-  int hv0 = 0, hv1 = 0;
-  if (hint) {
-    hv0 = *hp0;
-    hv1 = *hp1;
-    for (int i = tid; i < 4096; i += kTkNT) sm.h12[i] = 0;  // ordered before any add by later barriers
-  }
-  auto clear_hint = [&] {
-    if (hint) {
-      *hp0 = 0;
-      *hp1 = 0;
-    }
-  };
+  if (tid < kCoarseBins) sm.coarse[tid] = 0;  // ordered before any add by the row's barrier
+  for (int i = tid; i < 4096; i += kTkNT) sm.h12[i] = 0;  // ordered before any add by later barriers
   const SeqInfo si = seq_info(d, t0b);
   int* Irow = I + ((size_t)b * d.L + j) * d.topk;
   const bool act = flat_active(d, si);
@@ -2133,24 +2096,14 @@ __global__ __launch_bounds__(kTkNT) void k_topk_rows_reg(KDims d, const float* _
   }
   if (!act) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0: the row's LDS writes have landed
-    clear_hint();
     return;
   }
   const int n = si.Np, k = si.k;
   const int i0 = kTkR * tid;  // index of v[0]
   // absent entries (index >= n) take -inf: below every real or masked score
   float v[kTkR];
-  // the counts summed over copies into sm.hint (published by the barrier
-  // after the row's loads, or the one below)
-  auto sum_hint = [&] {
-    uint32_t h = (uint32_t)(hv0 + hv1);
-    h += __shfl_xor(h, 1);
-    h += __shfl_xor(h, 2);
-    if ((tid & 3) == 0) sm.hint[tid >> 2] = h;
-  };
   if (staged) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0 (the counts too)
-    if (hint) sum_hint();
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0
     __syncthreads();
     const float* mine = sm.row + (tid >> 3) * 8 * kTkR + (tid & 7) * kTkR;
 #pragma unroll
@@ -2164,11 +2117,10 @@ __global__ __launch_bounds__(kTkNT) void k_topk_rows_reg(KDims d, const float* _
   } else {
 #pragma unroll
     for (int q = 0; q < kTkR; ++q) v[q] = i0 + q < n ? srow[i0 + q] : -INFINITY;
-    if (hint) {
-      sum_hint();
-      __syncthreads();
-    }
   }
+  // the coarse bins of one sample per thread (index 32t)
+  if (i0 < n) atomicAdd(&sm.coarse[score_key(v[0]) >> 24], 1u);
+  __syncthreads();
   // the selection: scores with key > kthr, and those with key == kthr at
   // index <= ithr
   uint32_t kthr = 0;
@@ -2192,38 +2144,46 @@ __global__ __launch_bounds__(kTkNT) void k_topk_rows_reg(KDims d, const float* _
   };
   bool have = false;      // kthr / ithr known
   bool all_ties = false;  // every entry with key kthr is selected
-  if (hint) {
-    // 0. the scan's bin counts name the coarse bin S (top 8 key bits) of the
-    // k-th key; the row's own counts check it (the hint only steers).
-    // Every wave finds S alone: lane l holds bins 255-4l .. 252-4l
+  {
+    // 0. the coarse bin S (top 8 key bits) of the k-th key, first the bin of
+    // the sample at the same rank, scaled; the row's own counts check it and
+    // move it one bin up or down (three tries).  Every wave finds the first S
+    // alone: lane l holds bins 255-4l .. 252-4l
     uint32_t hb[4], s4 = 0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      hb[u] = sm.hint[kHintBins - 1 - 4 * lane - u];
+      hb[u] = sm.coarse[kCoarseBins - 1 - 4 * lane - u];
       s4 += hb[u];
     }
     const uint32_t inc = wave_incl_scan(s4);
-    const uint32_t htot = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+    const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+    // the rank to find among the samples (uniform; 0: none)
+    const uint32_t rt =
+        k >= 1 && tot >= 1 ? (uint32_t)min((long long)tot, max(1LL, ((long long)k * tot + n - 1) / n)) : 0u;
     int S = -1;
-    if (htot == (uint32_t)n && k >= 1) {  // then exactly one lane holds the k-th
+    if (rt >= 1) {  // then exactly one lane holds the rt-th
       int Sl = -1;
       uint32_t acc = inc - s4;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        if (acc < (uint32_t)k && acc + hb[u] >= (uint32_t)k) Sl = kHintBins - 1 - 4 * lane - u;
+        if (acc < rt && acc + hb[u] >= rt) Sl = kCoarseBins - 1 - 4 * lane - u;
         acc += hb[u];
       }
       const uint64_t hit = __ballot(Sl >= 0);
       if (hit) S = __builtin_amdgcn_readlane(Sl, (int)__builtin_ctzll(hit));
     }
     // bin 0 holds -inf and NaN keys only: left to the exact path
-    if (S >= 1) {
-      // key >= (S << 24) <=> score >= flo and key >= ((S + 1) << 24) <=>
-      // score >= fhi (the key order is the float order; no key lies past
-      // bin 255)
-      const float flo = score_of_key((uint32_t)S << 24);
-      const float fhi = S == kHintBins - 1 ? __builtin_nanf("") : score_of_key((uint32_t)(S + 1) << 24);
-      // entries at or above S (low half) and above S (high half): each <= 32768
+    bool found = false;
+    float flo = 0.f, fhi = 0.f;
+    uint32_t cex = 0;
+    int n_above = 0, n_in = 0;
+    // counts of the entries at or above S (low half) and above S (high half),
+    // each <= 32768; key >= (S << 24) <=> score >= flo and key >= ((S + 1) <<
+    // 24) <=> score >= fhi (the key order is the float order; no key lies
+    // past bin 255).  Moves S toward the k-th key unless it holds it.
+    auto classify = [&]() {
+      flo = score_of_key((uint32_t)S << 24);
+      fhi = S == kCoarseBins - 1 ? __builtin_nanf("") : score_of_key((uint32_t)(S + 1) << 24);
       uint32_t c = 0;
 #pragma unroll
       for (int q = 0; q < kTkR; ++q) {
@@ -2231,101 +2191,110 @@ __global__ __launch_bounds__(kTkNT) void k_topk_rows_reg(KDims d, const float* _
         c += v[q] >= flo ? 1u : 0u;
       }
       uint32_t ctot;
-      const uint32_t cex = block_excl_scan<kTkNT>(c, sm.wsum, &ctot);
-      const int n_above = (int)(ctot >> 16), n_in = (int)(ctot & 0xFFFFu) - n_above;
-      if (n_above < k && n_above + n_in >= k) {  // uniform: S holds the k-th key
-        // S's scores into LDS (the row's copy there is no longer read: every
-        // thread loaded its scores before the scan's barriers), then the
-        // 4096-bin histogram of their key bits 23..12
-        float* cf = sm.row;
-        int pos = (int)(cex & 0xFFFFu) - (int)(cex >> 16);
+      cex = block_excl_scan<kTkNT>(c, sm.wsum, &ctot);
+      n_above = (int)(ctot >> 16);
+      n_in = (int)(ctot & 0xFFFFu) - n_above;
+      if (n_above >= k)
+        ++S;  // uniform: the k-th key lies above S
+      else if (n_above + n_in < k)
+        --S;  // below S
+      else
+        found = true;
+    };
+#pragma unroll 1
+    for (int attempt = 0; attempt < 3 && !found && S >= 1 && S < kCoarseBins; ++attempt) classify();
+    if (found) {  // S holds the k-th key
+      // S's scores into LDS (the row's copy there is no longer read: every
+      // thread loaded its scores before the scan's barriers), then the
+      // 4096-bin histogram of their key bits 23..12
+      float* cf = sm.row;
+      int pos = (int)(cex & 0xFFFFu) - (int)(cex >> 16);
 #pragma unroll
-        for (int q = 0; q < kTkR; ++q)
-          if (v[q] >= flo && !(v[q] >= fhi)) cf[pos++] = v[q];
-        if (tid == 0) sm.info[3] = 0;
-        __syncthreads();
-        for (int i = tid; i < n_in; i += kTkNT) atomicAdd(&sm.h12[(score_key(cf[i]) >> 12) & 4095u], 1u);
-        __syncthreads();
-        int r = k - n_above;  // rank of the k-th key among S's entries, from 1
-        // the bin of h12 holding the r-th entry from the top: thread t reads
-        // (and clears) bins 4095-4t .. 4092-4t; (bin, entries above it,
-        // entries in it) come back through info[slot .. slot+2]
-        auto find12 = [&](int slot, int& T, int& above, int& m) {
-          const int top = 4095 - 4 * tid;
-          uint32_t hx[4], sx = 0;
+      for (int q = 0; q < kTkR; ++q)
+        if (v[q] >= flo && !(v[q] >= fhi)) cf[pos++] = v[q];
+      if (tid == 0) sm.info[3] = 0;
+      __syncthreads();
+      for (int i = tid; i < n_in; i += kTkNT) atomicAdd(&sm.h12[(score_key(cf[i]) >> 12) & 4095u], 1u);
+      __syncthreads();
+      int r = k - n_above;  // rank of the k-th key among S's entries, from 1
+      // the bin of h12 holding the r-th entry from the top: thread t reads
+      // (and clears) bins 4095-4t .. 4092-4t; (bin, entries above it,
+      // entries in it) come back through info[slot .. slot+2]
+      auto find12 = [&](int slot, int& T, int& above, int& m) {
+        const int top = 4095 - 4 * tid;
+        uint32_t hx[4], sx = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          hx[u] = sm.h12[top - u];
+          sm.h12[top - u] = 0;
+          sx += hx[u];
+        }
+        uint32_t tx;
+        const uint32_t ax = block_excl_scan<kTkNT>(sx, sm.wsum, &tx);
+        if (ax < (uint32_t)r && ax + sx >= (uint32_t)r) {
+          uint32_t acc = ax;
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            hx[u] = sm.h12[top - u];
-            sm.h12[top - u] = 0;
-            sx += hx[u];
-          }
-          uint32_t tx;
-          const uint32_t ax = block_excl_scan<kTkNT>(sx, sm.wsum, &tx);
-          if (ax < (uint32_t)r && ax + sx >= (uint32_t)r) {
-            uint32_t acc = ax;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              if (acc < (uint32_t)r && acc + hx[u] >= (uint32_t)r) {
-                sm.info[slot] = top - u;
-                sm.info[slot + 1] = (int)acc;
-                sm.info[slot + 2] = (int)hx[u];
-              }
-              acc += hx[u];
+            if (acc < (uint32_t)r && acc + hx[u] >= (uint32_t)r) {
+              sm.info[slot] = top - u;
+              sm.info[slot + 1] = (int)acc;
+              sm.info[slot + 2] = (int)hx[u];
             }
+            acc += hx[u];
           }
-          __syncthreads();
-          T = sm.info[slot];
-          above = sm.info[slot + 1];
-          m = sm.info[slot + 2];
-        };
-        int T, above, m;
-        find12(0, T, above, m);
-        r -= above;
-        const uint32_t pre = ((uint32_t)S << 12) | (uint32_t)T;  // top 20 bits of the k-th key
-        uint32_t kt;
-        int mt;  // entries with key kt; the r lowest-index ones are taken
-        if (m <= 64) {
-          // the few entries under pre, ranked by one wave
-          for (int i = tid; i < n_in; i += kTkNT) {
-            const uint32_t kk = score_key(cf[i]);
-            if ((kk >> 12) == pre) sm.few[atomicAdd(&sm.info[3], 1)] = kk;
-          }
-          __syncthreads();
-          if (wv == 0) {
-            const uint32_t x0 = lane < m ? sm.few[lane] : 0u;
-            int gt = 0, ge = 0;
-            for (int u = 0; u < m; ++u) {
-              const uint32_t x = sm.few[u];
-              gt += x > x0 ? 1 : 0;
-              ge += x >= x0 ? 1 : 0;
-            }
-            if (lane < m && gt < r && ge >= r) {  // every such lane holds the same key
-              sm.info[4] = (int)x0;
-              sm.info[5] = r - gt;
-              sm.info[6] = ge - gt;
-            }
-          }
-          __syncthreads();
-          kt = (uint32_t)sm.info[4];
-          r = sm.info[5];
-          mt = sm.info[6];
-        } else {
-          // many entries share the top 20 bits: one more 12-bit round
-          for (int i = tid; i < n_in; i += kTkNT) {
-            const uint32_t kk = score_key(cf[i]);
-            if ((kk >> 12) == pre) atomicAdd(&sm.h12[kk & 4095u], 1u);
-          }
-          __syncthreads();
-          int U;
-          find12(4, U, above, mt);
-          kt = (pre << 12) | (uint32_t)U;
-          r -= above;
         }
-        kthr = kt;
-        all_ties = r == mt;
-        ithr = all_ties ? n : rth_index(r, [&](int q) { return i0 + q < n && score_key(v[q]) == kt; });
-        have = true;
+        __syncthreads();
+        T = sm.info[slot];
+        above = sm.info[slot + 1];
+        m = sm.info[slot + 2];
+      };
+      int T, above, m;
+      find12(0, T, above, m);
+      r -= above;
+      const uint32_t pre = ((uint32_t)S << 12) | (uint32_t)T;  // top 20 bits of the k-th key
+      uint32_t kt;
+      int mt;  // entries with key kt; the r lowest-index ones are taken
+      if (m <= 64) {
+        // the few entries under pre, ranked by one wave
+        for (int i = tid; i < n_in; i += kTkNT) {
+          const uint32_t kk = score_key(cf[i]);
+          if ((kk >> 12) == pre) sm.few[atomicAdd(&sm.info[3], 1)] = kk;
+        }
+        __syncthreads();
+        if (wv == 0) {
+          const uint32_t x0 = lane < m ? sm.few[lane] : 0u;
+          int gt = 0, ge = 0;
+          for (int u = 0; u < m; ++u) {
+            const uint32_t x = sm.few[u];
+            gt += x > x0 ? 1 : 0;
+            ge += x >= x0 ? 1 : 0;
+          }
+          if (lane < m && gt < r && ge >= r) {  // every such lane holds the same key
+            sm.info[4] = (int)x0;
+            sm.info[5] = r - gt;
+            sm.info[6] = ge - gt;
+          }
+        }
+        __syncthreads();
+        kt = (uint32_t)sm.info[4];
+        r = sm.info[5];
+        mt = sm.info[6];
+      } else {
+        // many entries share the top 20 bits: one more 12-bit round
+        for (int i = tid; i < n_in; i += kTkNT) {
+          const uint32_t kk = score_key(cf[i]);
+          if ((kk >> 12) == pre) atomicAdd(&sm.h12[kk & 4095u], 1u);
+        }
+        __syncthreads();
+        int U;
+        find12(4, U, above, mt);
+        kt = (pre << 12) | (uint32_t)U;
+        r -= above;
       }
+      kthr = kt;
+      all_ties = r == mt;
+      ithr = all_ties ? n : rth_index(r, [&](int q) { return i0 + q < n && score_key(v[q]) == kt; });
+      have = true;
     }
   }
   if (!have) {
@@ -2534,7 +2503,6 @@ __global__ __launch_bounds__(kTkNT) void k_topk_rows_reg(KDims d, const float* _
     Irow[slot++] = i0 + q;
     m &= m - 1;
   }
-  clear_hint();
 }
 
 // The dense fallback with the indexer switched off (HiSA issue, Implementation
@@ -3052,30 +3020,16 @@ bool decode_fused_ok(const KDims& d, bool bf16) {
          d.index_keep <= kRowKeep && !big_flat;
 }
 
-// The one-slab-per-workgroup scan runs (rather than the streaming one).
-static bool decode_scan_per_slab(const KDims& d) {
-  const long long slabs = (long long)cdiv(d.Np_cap, 64) * d.B;
-  return slabs <= 1024 || d.B > kStreamMaxB;
-}
-
-bool flat_hint_ok(const KDims& d, bool bf16) {
-  return d.L == 1 && idx_mfma_ok(d, bf16) && decode_scan_per_slab(d) && d.Np_cap > 8192 && d.Np_cap <= kTkNT * kTkR;
-}
-
 hipError_t launch_decode_scan(const KDims& d, bool bf16, const void* q_idx, const float* w, const void* keys,
                               const int* t0, float* fscore, float* cscore, int* cnt, int* I, int* top_blk,
-                              int* path, hipStream_t st, int* hint) {
+                              int* path, hipStream_t st) {
   const dim3 grid(cdiv(d.Np_cap, 64), d.B);
-  if (hint && !flat_hint_ok(d, bf16)) return hipErrorInvalidValue;
   if (idx_mfma_ok(d, bf16)) {
-    if (decode_scan_per_slab(d)) {
+    const long long slabs = (long long)cdiv(d.Np_cap, 64) * d.B;
+    if (slabs <= 1024 || d.B > kStreamMaxB) {
       // latency-bound: one workgroup per slab, rows requested before t0 is known
-      if (hint)
-        hipLaunchKernelGGL(k_decode_scan_mfma<true>, grid, dim3(256), 0, st, d, (const uint16_t*)q_idx, w,
-                           (const uint16_t*)keys, t0, fscore, cscore, cnt, hint, I, top_blk, path);
-      else
-        hipLaunchKernelGGL(k_decode_scan_mfma<false>, grid, dim3(256), 0, st, d, (const uint16_t*)q_idx, w,
-                           (const uint16_t*)keys, t0, fscore, cscore, cnt, hint, I, top_blk, path);
+      hipLaunchKernelGGL(k_decode_scan_mfma, grid, dim3(256), 0, st, d, (const uint16_t*)q_idx, w,
+                         (const uint16_t*)keys, t0, fscore, cscore, cnt, I, top_blk, path);
     } else {
       // bandwidth-bound: two resident workgroups per CU share the live slabs
       hipLaunchKernelGGL(k_decode_scan_stream, dim3(512), dim3(256), 0, st, d, (const uint16_t*)q_idx, w,
@@ -3237,12 +3191,10 @@ hipError_t launch_flat_scores(const KDims& d, bool bf16, const void* q_idx, cons
   return hipGetLastError();
 }
 
-hipError_t launch_topk_rows(const KDims& d, const float* scores, const int* t0, int* I, int* path, hipStream_t st,
-                            int* hint) {
-  if (hint && (d.L != 1 || d.Np_cap <= 8192 || d.Np_cap > kTkNT * kTkR)) return hipErrorInvalidValue;
+hipError_t launch_topk_rows(const KDims& d, const float* scores, const int* t0, int* I, int* path, hipStream_t st) {
   if (d.Np_cap > 8192 && d.Np_cap <= kTkNT * kTkR) {
     // long rows: scores held in registers of a 1024-thread workgroup
-    hipLaunchKernelGGL(k_topk_rows_reg, dim3(d.L, d.B), dim3(kTkNT), 0, st, d, scores, t0, I, path, hint);
+    hipLaunchKernelGGL(k_topk_rows_reg, dim3(d.L, d.B), dim3(kTkNT), 0, st, d, scores, t0, I, path);
     return hipGetLastError();
   }
   constexpr int kLdsCap = 32768;  // 128 KiB of keys

@@ -146,11 +146,10 @@ def workspace_bytes(op: int, d: hisa_dims) -> int:
 
 # One workspace per (device, stream, op), grown on demand and reused by every
 # call of that op on that stream (calls on one stream are ordered, so they
-# never overlap).  The decode selection's arrival counters (and the flat
-# decode's coarse bin counts) start zeroed and every call leaves them zero;
-# their region grows with B and Np_cap (and the decode step's also with H,
-# topk, index_block and index_keep), so those workspaces are kept per such
-# dims as well.
+# never overlap).  The decode selection's arrival counters start zeroed and
+# every call leaves them zero; their region grows with B and Np_cap (and the
+# decode step's also with H, topk, index_block and index_keep), so those
+# workspaces are kept per such dims as well.
 _ws_cache = {}
 
 
@@ -167,9 +166,6 @@ def _workspace(op: int, d: hisa_dims, dev: torch.device, ws: Optional[torch.Tens
         key += (d.B, d.Np_cap)
     elif op == OP_DECODE_STEP:
         key += (d.B, d.Np_cap, d.H, d.topk, d.index_block, d.index_keep)
-    elif op == OP_FLAT_TOPK and d.L == 1:
-        # the decode scan's coarse bin counts rest at zero between calls
-        key += ("decode", d.B, d.Np_cap)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < n:
         buf = torch.zeros(n, dtype=torch.uint8, device=dev)

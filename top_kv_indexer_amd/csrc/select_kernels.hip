@@ -2876,25 +2876,25 @@ __global__ __launch_bounds__(256) void k_cached_step(KDims d, int nwg_c, const u
 // [floor(floor(t0 / r) / b), floor(Np / b)) (every complete block when t0 = 0),
 // rows summed in order in f32 and scaled by 1/b, as the cached decode does.
 // bf16 keys with 128 dims: one wave (workgroup) per block, spread over every
-// CU, lane l dims 2l and 2l+1; all b rows are requested before the in-order
-// sum, which is the same sum as the cached decode's (so the two give the same
-// bits).
+// CU, lane l dims 2l and 2l+1; all b rows are requested before t0 arrives
+// (block beta < nb_cap lies inside the buffer whatever t0 is), then summed in
+// order, the same sum as the cached decode's (so the two give the same bits).
 __global__ __launch_bounds__(64) void k_rep_update_bf16(KDims d, int all, const uint16_t* __restrict__ keys,
                                                         const int* __restrict__ t0, float* rep, int* zero_p,
                                                         int zero_n) {
   const int b = blockIdx.y, beta = blockIdx.x, lane = lane_id();
-  // sequence 0's workgroups also zero the arrival counters of the kernels that follow
-  if (zero_p && b == 0)
-    for (int i = blockIdx.x * 64 + lane; i < zero_n; i += gridDim.x * 64) zero_p[i] = 0;
-  const int t0b = t0[b];
-  const SeqInfo si = seq_info(d, t0b);
+  const int t0b = t0[b];  // requested first, needed once the rows' loads are out
   const int bsz = d.index_block;
-  const int first_new = all ? 0 : (int)div_ratio(d, (uint32_t)t0b) / bsz;
-  if (!si.ok || beta < first_new || beta >= si.nb) return;  // uniform over the wave
   const uint32_t* src = (const uint32_t*)(keys + ((size_t)b * d.Np_cap + (size_t)beta * bsz) * 128) + lane;
   uint32_t v[64];
 #pragma unroll
   for (int r = 0; r < 64; ++r) v[r] = r < bsz ? src[r * 64] : 0u;
+  // sequence 0's workgroups also zero the arrival counters of the kernels that follow
+  if (zero_p && b == 0)
+    for (int i = blockIdx.x * 64 + lane; i < zero_n; i += gridDim.x * 64) zero_p[i] = 0;
+  const SeqInfo si = seq_info(d, t0b);
+  const int first_new = all ? 0 : (int)div_ratio(d, (uint32_t)t0b) / bsz;
+  if (!si.ok || beta < first_new || beta >= si.nb) return;  // uniform over the wave
   float sx = 0.f, sy = 0.f;
 #pragma unroll
   for (int r = 0; r < 64; ++r)

@@ -378,7 +378,7 @@ def test_flat_topk_long_rows_decode(hisa, case):
 
 # ---------------------------------------------------------------- the flat top-k's coarse-bin path
 
-@pytest.mark.parametrize("case", ["ragged_b2", "sample_misleads", "one_coarse_bin"])
+@pytest.mark.parametrize("case", ["ragged_b2", "sample_misleads", "one_coarse_bin", "retry_one_bin"])
 def test_flat_topk_coarse_bin_path(hisa, case):
     # Rows of 8193..32768 scores: the row top-k takes the coarse key bin (top
     # 8 key bits) of the k-th key from one sample per thread (scores 0, 32,
@@ -386,14 +386,42 @@ def test_flat_topk_coarse_bin_path(hisa, case):
     # tries) before falling back to the exact path.  A ragged batch (rows of
     # 32768 and 9001 scores); samples that mislead (the best key copied onto
     # 300 sampled rows of sequence 0, so the sample puts the k-th key in the
-    # top bin: the tries move down, then the exact path takes over); and rows
+    # top bin: the tries move down, then the exact path takes over); rows
     # whose scores are all equal (one coarse bin holds every key: 32768 and
-    # 9001 ties, the lowest 2048 ids kept).  A repeated call is identical.
+    # 9001 ties, the lowest 2048 ids kept); and rows built so that the first
+    # guess is one bin too high: every head's q is one unit vector u, every
+    # head weight 1 and key row i is a_i u, so the score is about 0.71 a_i;
+    # the sampled rows and 1000 others score in [2, 8), one coarse bin, all
+    # the rest in [0.5, 2), the bin below, so the sample names the upper bin,
+    # which holds fewer than k entries, and one move down finds the k-th key.
+    # A repeated call is identical.
     w = synth.DSA_DECODE.with_(name=f"dsa_decode_coarse_{case}", B=2, t0=[32767, 9000], H=4, Dk=64, Dv=64)
     x, g = inputs(w, 77)
     x = dict(x)
     gk = g["keys"]
-    if case != "ragged_b2":
+    if case == "retry_one_bin":
+        rng = np.random.default_rng(9)
+        u = rng.standard_normal(128).astype(np.float32)
+        u /= np.linalg.norm(u)
+        q_idx = np.repeat(synth.round_bf16(u)[None, None, None, :], 64, axis=2).repeat(w.B, axis=0)
+        keys = np.empty_like(x["keys"])
+        high = []
+        for b in range(w.B):
+            n_b = int(x["Np"][b])
+            a = rng.uniform(0.8, 2.7, keys.shape[1]).astype(np.float32)
+            hi = np.zeros(keys.shape[1], dtype=bool)
+            hi[0:n_b:32] = True
+            hi[rng.choice(np.flatnonzero(~hi[:n_b]), 1000, replace=False)] = True
+            a[hi] = rng.uniform(3.0, 10.0, int(hi.sum())).astype(np.float32)
+            keys[b] = synth.round_bf16(a[:, None] * u[None, :])
+            high.append(np.flatnonzero(hi[:n_b]))
+            assert len(high[b]) < w.topk
+        x["q_idx"], x["w"], x["keys"] = q_idx.astype(np.float32), np.ones_like(x["w"]), keys
+        gq = torch.from_numpy(x["q_idx"]).to("cuda").to(torch.bfloat16).contiguous()
+        gw = torch.from_numpy(x["w"]).to("cuda")
+        gk = torch.from_numpy(keys).to("cuda").to(torch.bfloat16).contiguous()
+        g = dict(g, q_idx=gq, w=gw)
+    elif case != "ragged_b2":
         keys = x["keys"].copy()
         if case == "sample_misleads":
             d0 = odims(w, x)
@@ -422,3 +450,5 @@ def test_flat_topk_coarse_bin_path(hisa, case):
             np.testing.assert_array_equal(v, np.arange(w.topk))
         if case == "sample_misleads" and b == 0:
             assert set(range(0, 9600, 32)) <= set(v.tolist())  # the 300 copies of the best key are kept
+        if case == "retry_one_bin":
+            assert set(high[b].tolist()) <= set(v.tolist())  # every row of the upper bin, then the best below

@@ -812,8 +812,6 @@ __global__ __launch_bounds__(256) void k_attn_split64(KDims d, int splits, const
   __shared__ __align__(1024) uint16_t kv[kSplitRows * KPD];
   __shared__ __align__(16) uint16_t s_p[16 * PP];
   __shared__ float s_red[2][4][16];
-  __shared__ int s_code[kSplitRows];
-  __shared__ uint32_t s_live[2];
   args_now(d, splits, q, local_kv, pooled_kv, I, t0, part);
   // workgroup wg takes head group hg of (query row, split) pair p, with
   // wg = 8 ngrp (p / 8) + 8 hg + p % 8: the head groups of one split are 8
@@ -826,7 +824,7 @@ __global__ __launch_bounds__(256) void k_attn_split64(KDims d, int splits, const
   const int split = pair % splits, row = pair / splits, hbase = (rem >> 3) * 16;
   const int b = row / d.L, j = row - b * d.L;
   const int lane = lane_id(), wv = wave_id(), g = lane >> 4, c = lane & 15;
-  // this row's 16 heads of q (the B operand of S) and wave 0's entries of
+  // this row's 16 heads of q (the B operand of S) and the split's entries of
   // the index row, requested before t0 (nothing of theirs depends on it)
   bf16x8 qf[NS];
   {
@@ -836,34 +834,27 @@ __global__ __launch_bounds__(256) void k_attn_split64(KDims d, int splits, const
   }
   const int e = split * kSplitRows + lane;
   int id = -1;
-  if (wv == 0 && e < d.kI) id = I ? I[(size_t)row * d.kI + e] : e;
+  if (e < d.kI) id = I ? I[(size_t)row * d.kI + e] : e;
   const int T0 = t0[b];
   const RowPlan rp = row_plan(d, T0, ring_slot0(d, b, T0), j);
   // a row every live split may read (entries that take no part point at it)
   const int dummy = rp.n_loc > 0 ? -1 - rp.lbase : 0;
-  if (wv == 0) {
-    int code = dummy;
-    bool present = false;
-    if (rp.ok) {
-      if (e < d.kI) {
-        if (id >= 0 && id < rp.V) {
-          present = true;
-          code = id;
-        }
-      } else if (e - d.kI < d.window && e - d.kI < rp.n_loc) {
+  // every wave resolves all 64 entries of the split itself (lane = entry), so
+  // no wave waits on another before its gather
+  int code = dummy;
+  bool present = false;
+  if (rp.ok) {
+    if (e < d.kI) {
+      if (id >= 0 && id < rp.V) {
         present = true;
-        code = -1 - local_row(d, rp, e - d.kI);
+        code = id;
       }
-    }
-    s_code[lane] = code;
-    const uint64_t m = __ballot(present);
-    if (lane == 0) {
-      s_live[0] = (uint32_t)m;
-      s_live[1] = (uint32_t)(m >> 32);
+    } else if (e - d.kI < d.window && e - d.kI < rp.n_loc) {
+      present = true;
+      code = -1 - local_row(d, rp, e - d.kI);
     }
   }
-  lds_sync();  // the codes (q stays in flight)
-  const uint64_t live = ((uint64_t)s_live[1] << 32) | s_live[0];
+  const uint64_t live = __ballot(present);
   const bool any = live != 0;
   const uint32_t kv_lds = lds_addr(kv);
   const int kvb10 = (int)((kv_lds >> 10) & 15);
@@ -880,7 +871,7 @@ __global__ __launch_bounds__(256) void k_attn_split64(KDims d, int splits, const
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int r = 16 * wv + u;
-      const int cd = s_code[r];
+      const int cd = __builtin_amdgcn_readlane(code, r);
       const uint16_t* src = cd >= 0 ? pooled_b + (size_t)cd * DK : local_b + (size_t)(-1 - cd) * DK;
       const int x = lane ^ sw(r);
       const uint32_t dst = kv_lds + (uint32_t)(r * KPD * 2);

@@ -125,14 +125,15 @@ def test_value_narrower_than_key(hisa, bf16):
 
 # ---------------------------------------------------------------- small HiSA blocks
 
-@pytest.mark.parametrize("block,keep", [(8, 64), (16, 32), (32, 16)])
+@pytest.mark.parametrize("block,keep", [(1, 512), (2, 256), (4, 128), (8, 64), (16, 32), (32, 16)])
 @pytest.mark.parametrize("scan", ["latency", "streaming"])
 def test_decode_small_blocks(hisa, block, keep, scan):
     # index_block below 64 on the bf16 MFMA decode scans: blocks of <= 16 rows
     # are summed across the lanes of one wave, 32-row blocks across two waves.
     # index_block * index_keep = 512 = topk keeps the HiSA path.  Latency scan:
     # one sequence of 256 slabs; streaming: 5 sequences of up to 256 slabs.
-    # (Blocks of 16 and 32 rows keep the selection fused into both scans.)
+    # (Blocks of 16 and 32 rows keep the selection fused into both scans; with
+    # more than 64 kept blocks the selection runs in a launch of its own.)
     if scan == "latency":
         w = synth.FLASH_DECODE.with_(name=f"flash_b{block}", index_block=block, index_keep=keep, planted=24)
         seed = 48

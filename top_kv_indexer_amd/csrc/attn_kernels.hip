@@ -785,7 +785,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_fa(KDims d, c
 
 // Few query rows (decode, short verify chunks; K = V rows 512 or 576 wide):
 // one workgroup per (64-entry split of the row list, query row, 16 heads),
-// four waves, the whole split in one pass.  Wave 0 resolves the split's 64
+// four waves, the whole split in one pass.  Every wave resolves the split's 64
 // entries (pooled ids from I, then the local window) into row codes; wave w
 // brings rows 16w .. 16w+15 global->LDS and scores them against the 16 heads
 // (S = K q^T, 16x16x32 MFMA, lane (g, c) holding rows 16w + 4g + i of head c);
